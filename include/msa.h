@@ -1,0 +1,175 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) Memory Sparse Attention hot path.
+ *
+ * The library implements, for one upper attention layer, the four steps of MSA's
+ * inference path:
+ *   A. msa_pool        offline memory encoding: document-wise RoPE, then chunk-mean
+ *                      pooling of token-level K, V, Kr into bank rows K-bar, V-bar, Kr-bar;
+ *   B+C. msa_route_topk the router: cosine of the query's Qr against every Kr-bar row,
+ *                      mean over heads, max over query tokens, max over each document's
+ *                      rows, then the top-k documents;
+ *   D. msa_sparse_attn context assembly (selected documents' K-bar/V-bar followed by the
+ *                      query's local K/V under global RoPE) and GQA softmax attention.
+ *
+ * Sources: hysenlabs.com "EverMind-AI/MSA: routing top-k compressed documents inside
+ * attention, and where the 100M-token claim stops" (sections "Routing happens inside
+ * attention ...", "Document-wise RoPE resets every document to position zero", "Memory
+ * must be encoded offline ...", "The 100M-token setup depends on host memory ...");
+ * yeyulingfeng.com "深度分析MSA：把超长文档组织成可检索内部记忆的工程路径" (section 三,
+ * chunk compression; section 五, inference).
+ *
+ * Conventions for every call:
+ *  - Tensors are caller-owned, contiguous, row-major, and device-accessible unless a
+ *    parameter says "host".  Element type is given by `dtype` (MSA_F32 or MSA_BF16);
+ *    bf16 is the upper half of an IEEE float32.  Offsets are device arrays unless noted.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream).  The
+ *    library allocates no memory and keeps no state between calls: scratch space comes
+ *    from the caller's `workspace`.
+ *  - Arguments are validated on the host before any HIP call; a bad argument returns
+ *    MSA_ERR_INVALID_ARG or MSA_ERR_UNSUPPORTED at once, with a message in
+ *    msa_last_error().  A failed launch returns MSA_ERR_HIP.  Nothing is printed and no
+ *    exception or abort crosses the ABI.
+ *  - Device-resident offset arrays are a caller precondition (non-decreasing, every
+ *    document has >= 1 token, offsets within the tensors); they are not read on the host.
+ *  - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* msa_stream_t; /* same type as hipStream_t */
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shapes           */
+  MSA_ERR_UNSUPPORTED = 2, /* valid but not implemented (head dim, dtype, k > 1024) */
+  MSA_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace() size */
+  MSA_ERR_HIP = 4          /* a HIP call or kernel launch failed                     */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+/* Which tensors msa_pool rotates with document-wise RoPE.  The default reading rotates
+ * K only (keys carry positions; V and the routing keys Kr are left as they are). */
+enum { MSA_ROPE_K = 1u, MSA_ROPE_V = 2u, MSA_ROPE_KR = 4u };
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t msa_version(void);
+
+/* Text for a status code (static storage). */
+const char* msa_status_string(msa_status s);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* msa_last_error(void);
+
+/*
+ * msa_chunk_offsets -- host-side chunk layout of a bank (yeyulingfeng.com section 三,
+ * chunk compression: one chunk per `chunk` tokens; its worked example maps 180 tokens to
+ * 3 chunks, so a partial last chunk counts).
+ *   doc_tok_off  host [n_docs+1] token offsets of the documents, non-decreasing, with
+ *                doc_tok_off[0] == 0 and every document holding >= 1 token.
+ *   chunk_off    host [n_docs+1] output: document d owns bank rows
+ *                [chunk_off[d], chunk_off[d+1]), ceil(L_d / chunk) of them.
+ * Returns the total number of bank rows, or -1 on a bad argument (see msa_last_error).
+ */
+int64_t msa_chunk_offsets(const int64_t* doc_tok_off, int32_t n_docs, int32_t chunk,
+                          int64_t* chunk_off);
+
+/*
+ * msa_pool -- step A, offline memory encoding (hysenlabs.com "Memory must be encoded
+ * offline ...": one pass over the corpus caches chunk-pooled K, V and Kr; yeyulingfeng.com
+ * section 三: mean pooling per chunk; hysenlabs.com "Document-wise RoPE resets every
+ * document to position zero").
+ *   K, V       [n_tokens, h_kv, d]; Kr [n_tokens, h_r, d]; documents concatenated.
+ *   doc_tok_off, chunk_off   device [n_docs+1] (chunk_off as from msa_chunk_offsets).
+ *   rope_mask  MSA_ROPE_* bits: tensors rotated at their in-document position p
+ *              (restarting at 0 per document), angle p * rope_base^(-2i/d) on the pair
+ *              (i, i + d/2).
+ *   Kbar, Vbar [n_chunks, h_kv, d]; Krbar [n_chunks, h_r, d] outputs.  Row
+ *              chunk_off[doc] + j is the mean of tokens [j*chunk, min((j+1)*chunk, L)) of
+ *              the document, after rotation; means are accumulated in float32 and
+ *              rounded once to dtype.
+ *   Supported: d in {32, 64, 128}; 1 <= chunk <= 128; h_kv, h_r in [1, 64].
+ */
+msa_status msa_pool(msa_dtype dtype, int32_t n_docs, int64_t n_tokens, int64_t n_chunks,
+                    const int64_t* doc_tok_off, const int64_t* chunk_off,
+                    int32_t h_kv, int32_t h_r, int32_t d, int32_t chunk, float rope_base,
+                    uint32_t rope_mask, const void* K, const void* V, const void* Kr,
+                    void* Kbar, void* Vbar, void* Krbar, msa_stream_t stream);
+
+/* Bytes of workspace msa_route_topk needs (256-byte aligned pointer expected). */
+size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
+
+/*
+ * msa_route_topk -- steps B and C, the router (hysenlabs.com "Routing happens inside
+ * attention ...": cosine similarity of the query's routing vectors with the pooled routing
+ * keys, averaged over heads, then the maximum over the query's tokens, then top-k
+ * documents; yeyulingfeng.com section 五 step 2).
+ *   Qr         [total_q, h_r, d]; query b owns rows [q_off[b], q_off[b+1]).
+ *   q_off      device int32 [n_queries+1].
+ *   max_q_len  host-side upper bound of every query's length; it picks the kernel tile
+ *              (rows are still read from q_off, so a loose bound is only slower).
+ *   Krbar      [n_chunks, h_r, d]; chunk_off device [n_docs+1].
+ *   Scores: s(t,c) = (1/h_r) sum_h cos(Qr[t,h], Krbar[c,h]) (cos = 0 if a norm is 0),
+ *           chunk score = max_t s(t,c), document score = max over its rows.
+ *   topk_ids   device int32 [n_queries, k]: the min(k, n_docs) best documents by (score
+ *              descending, id ascending); remaining slots -1.
+ *   topk_scores device float [n_queries, k]: their scores; -inf in unused slots.
+ *   doc_scores device float [n_queries, n_docs] or NULL: every document's score.
+ *   Supported: d in {32, 64, 128}; h_r in [1, 16]; 1 <= k <= 1024.  Scores and norms
+ *   accumulate in float32; bf16 inputs with max_q_len >= 16 use MFMA tiles.
+ */
+msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                          const int32_t* q_off, int32_t max_q_len, const void* Qr,
+                          int32_t h_r, int32_t d, int32_t n_docs, int64_t n_chunks,
+                          const int64_t* chunk_off, const void* Krbar, int32_t k,
+                          int32_t* topk_ids, float* topk_scores, float* doc_scores,
+                          void* workspace, size_t workspace_bytes, msa_stream_t stream);
+
+/* Bytes of workspace msa_sparse_attn needs for these sizes. */
+size_t msa_sparse_attn_workspace(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                                 int64_t total_kv, int32_t max_q_len, int32_t hq,
+                                 int32_t h_kv, int32_t d);
+
+/*
+ * msa_sparse_attn -- step D, context assembly and sparse attention (hysenlabs.com
+ * "Routing happens inside attention ...": the selected documents' compressed K/V are
+ * joined with the query's local K/V; "Document-wise RoPE ..." second paragraph: global
+ * RoPE over the active context with the query's start shifted by the number of retrieved
+ * blocks, causal order memory -> query -> generation; "The 100M-token setup ...": content
+ * K/V may stay in host memory and be fetched when selected).
+ *   Q          [total_q, hq, d]; query b owns rows [q_off[b], q_off[b+1]).
+ *   Kloc, Vloc [total_kv, h_kv, d]; query b owns rows [kv_off[b], kv_off[b+1]) with
+ *              Lkv_b >= Lq_b; its Lq_b query tokens are the last Lq_b local tokens.
+ *              Not rotated: the call applies global RoPE itself.
+ *   topk_ids   device int32 [n_queries, k] as written by msa_route_topk (-1 = unused).
+ *   Kbar, Vbar [n_chunks, h_kv, d] bank rows, used as stored (no second rotation).
+ *   kv_source  0: Kbar/Vbar are device memory; 1: they are page-locked host memory
+ *              (hipHostMalloc / pinned) read over the host link by the kernel.
+ *   Let k_eff = number of valid ids.  Memory = rows of the selected documents in rank
+ *   order.  Local token j is rotated at global position k_eff + j; query token t is local
+ *   token Lkv - Lq + t and attends to every memory row and to local tokens <= its own.
+ *   Query head hq reads kv head hq / (hq_count / h_kv).  scale 0 means 1/sqrt(d).
+ *   O          [total_q, hq, d] output.
+ *   Supported: d in {32, 64, 128}; hq % h_kv == 0; 1 <= k <= 1024.
+ */
+msa_status msa_sparse_attn(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                           int64_t total_kv, const int32_t* q_off, const int32_t* kv_off,
+                           int32_t max_q_len, const void* Q, const void* Kloc,
+                           const void* Vloc, int32_t hq, int32_t h_kv, int32_t d,
+                           float rope_base, float scale, int32_t k, const int32_t* topk_ids,
+                           int32_t n_docs, int64_t n_chunks, const int64_t* chunk_off,
+                           const void* Kbar, const void* Vbar, int32_t kv_source, void* O,
+                           void* workspace, size_t workspace_bytes, msa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

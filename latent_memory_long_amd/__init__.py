@@ -1,0 +1,11 @@
+"""MI355X (gfx950) implementation of Memory Sparse Attention's routing + sparse-attention
+hot path: chunk-mean pooling with document-wise RoPE, the cosine router scan, top-k
+document selection, and sparse GQA attention over the selected memory plus the local
+context.  The kernels live in csrc/ and are reached through the C ABI of include/msa.h;
+``binding`` exposes the same entry points to Python.
+"""
+from .binding import (  # noqa: F401
+    MSA_BF16, MSA_F32, MSA_ROPE_K, MSA_ROPE_KR, MSA_ROPE_V, LIB_PATH, MsaError,
+    msa_chunk_offsets, msa_last_error, msa_pool, msa_route_topk, msa_route_topk_workspace,
+    msa_sparse_attn, msa_sparse_attn_workspace, msa_status_string, msa_version,
+)

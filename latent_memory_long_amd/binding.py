@@ -1,0 +1,197 @@
+"""Python binding of libmsa.so: the C entry points of include/msa.h, same names.
+
+Only argument marshalling happens here: torch tensors provide device memory, pinned host
+memory and the current stream; shapes and pointers are passed to the library, and every
+step of the path runs in its HIP kernels.  If the library is missing the import fails:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
+MSA_F32, MSA_BF16 = 0, 1
+MSA_ROPE_K, MSA_ROPE_V, MSA_ROPE_KR = 1, 2, 4
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"msa status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python -m latent_memory_long_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F, SZ, U32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                              ctypes.c_size_t, ctypes.c_uint32)
+    sig = {
+        "msa_version": (I32, []),
+        "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "msa_last_error": (ctypes.c_char_p, []),
+        "msa_chunk_offsets": (I64, [P, I32, I32, P]),
+        "msa_pool": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, I32, I32, I32, F, U32,
+                                    P, P, P, P, P, P, P]),
+        "msa_route_topk_workspace": (SZ, [I32, I32, I32]),
+        "msa_route_topk": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
+                                          P, I32, P, P, P, P, SZ, P]),
+        "msa_sparse_attn_workspace": (SZ, [ctypes.c_int, I32, I64, I64, I32, I32, I32, I32]),
+        "msa_sparse_attn": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, P, P, P, I32, I32,
+                                           I32, F, F, I32, P, I32, I64, P, P, P, I32, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != MSA_OK:
+        raise MsaError(status, lib.msa_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MSA_F32
+    if t.dtype == torch.bfloat16:
+        return MSA_BF16
+    raise MsaError(MSA_ERR_UNSUPPORTED, f"dtype {t.dtype} (need float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise MsaError(MSA_ERR_INVALID_ARG, "tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def msa_version() -> int:
+    return int(lib.msa_version())
+
+
+def msa_status_string(status: int) -> str:
+    return lib.msa_status_string(status).decode()
+
+
+def msa_last_error() -> str:
+    return lib.msa_last_error().decode()
+
+
+def msa_chunk_offsets(doc_tok_off, chunk: int = 64) -> np.ndarray:
+    """Host-side bank layout: chunk_off[N+1] (int64) from token offsets."""
+    off = np.ascontiguousarray(np.asarray(doc_tok_off, dtype=np.int64))
+    n = len(off) - 1
+    out = np.zeros(max(n + 1, 1), dtype=np.int64)
+    c = lib.msa_chunk_offsets(off.ctypes.data, n, chunk, out.ctypes.data)
+    if c < 0:
+        raise MsaError(MSA_ERR_INVALID_ARG, msa_last_error())
+    return out
+
+
+def msa_pool(K: torch.Tensor, V: torch.Tensor, Kr: torch.Tensor, doc_tok_off: torch.Tensor,
+             chunk_off: torch.Tensor, n_chunks: int, chunk: int = 64, rope_base: float = 1e6,
+             rope_mask: int = MSA_ROPE_K, out=None, stream=None):
+    """Step A.  K, V [T, h_kv, d]; Kr [T, h_r, d]; offsets int64 on the device.
+    Returns (Kbar, Vbar, Krbar) [n_chunks, h, d]."""
+    T, h_kv, d = K.shape
+    h_r = Kr.shape[1]
+    if out is None:
+        out = (torch.empty((n_chunks, h_kv, d), dtype=K.dtype, device=K.device),
+               torch.empty((n_chunks, h_kv, d), dtype=K.dtype, device=K.device),
+               torch.empty((n_chunks, h_r, d), dtype=K.dtype, device=K.device))
+    Kb, Vb, Krb = out
+    _check(lib.msa_pool(_dtype_code(K), doc_tok_off.numel() - 1, T, n_chunks, _ptr(doc_tok_off),
+                        _ptr(chunk_off), h_kv, h_r, d, chunk, rope_base, rope_mask, _ptr(K), _ptr(V),
+                        _ptr(Kr), _ptr(Kb), _ptr(Vb), _ptr(Krb), _stream(stream)))
+    return Kb, Vb, Krb
+
+
+def msa_route_topk_workspace(n_queries: int, n_docs: int, k: int) -> int:
+    return int(lib.msa_route_topk_workspace(n_queries, n_docs, k))
+
+
+def msa_route_topk(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar: torch.Tensor,
+                   chunk_off: torch.Tensor, k: int, want_doc_scores: bool = False, out=None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Steps B + C.  Qr [total_q, h_r, d]; q_off int32 [B+1]; Krbar [C, h_r, d].
+    Returns (topk_ids int32 [B,k], topk_scores f32 [B,k], doc_scores f32 [B,N] or None)."""
+    B = q_off.numel() - 1
+    N = chunk_off.numel() - 1
+    dev = Krbar.device
+    if out is None:
+        out = (torch.empty((B, k), dtype=torch.int32, device=dev),
+               torch.empty((B, k), dtype=torch.float32, device=dev),
+               torch.empty((B, N), dtype=torch.float32, device=dev) if want_doc_scores else None)
+    ids, sc, ds = out
+    need = msa_route_topk_workspace(B, N, k)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.msa_route_topk(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
+                              Krbar.shape[1], Krbar.shape[2], N, Krbar.shape[0], _ptr(chunk_off),
+                              _ptr(Krbar), k, _ptr(ids), _ptr(sc), _ptr(ds), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)))
+    return ids, sc, ds
+
+
+def msa_sparse_attn_workspace(dtype: int, n_queries: int, total_q: int, total_kv: int,
+                              max_q_len: int, hq: int, h_kv: int, d: int) -> int:
+    return int(lib.msa_sparse_attn_workspace(dtype, n_queries, total_q, total_kv, max_q_len, hq,
+                                             h_kv, d))
+
+
+def msa_sparse_attn(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Tensor, q_off: torch.Tensor,
+                    kv_off: torch.Tensor, max_q_len: int, topk_ids: torch.Tensor,
+                    chunk_off: torch.Tensor, Kbar: torch.Tensor, Vbar: torch.Tensor,
+                    rope_base: float = 1e6, scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    """Step D.  Q [total_q, hq, d]; Kloc/Vloc [total_kv, h_kv, d]; Kbar/Vbar [C, h_kv, d] on the
+    device, or in pinned host memory (then read over the host link).  Returns O."""
+    B = q_off.numel() - 1
+    total_q, hq, d = Q.shape
+    total_kv, h_kv, _ = Kloc.shape
+    k = topk_ids.shape[1]
+    N = chunk_off.numel() - 1
+    kv_source = 0 if Kbar.is_cuda else 1
+    if kv_source == 1 and not (Kbar.is_pinned() and Vbar.is_pinned()):
+        raise MsaError(MSA_ERR_INVALID_ARG, "host-resident Kbar/Vbar must be pinned")
+    dev = Q.device
+    if out is None:
+        out = torch.empty_like(Q)
+    code = _dtype_code(Q)
+    need = msa_sparse_attn_workspace(code, B, total_q, total_kv, max_q_len, hq, h_kv, d)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.msa_sparse_attn(code, B, total_q, total_kv, _ptr(q_off), _ptr(kv_off), max_q_len,
+                               _ptr(Q), _ptr(Kloc), _ptr(Vloc), hq, h_kv, d, rope_base, scale, k,
+                               _ptr(topk_ids), N, Kbar.shape[0], _ptr(chunk_off), _ptr(Kbar),
+                               _ptr(Vbar), kv_source, _ptr(out), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)))
+    return out

@@ -1,0 +1,209 @@
+// C ABI of the MSA hot path: argument validation, workspace layout, kernel launches.
+// Declarations and the contract of every entry point are in include/msa.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/msa.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status fail(msa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+msa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MSA_OK;
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool head_dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
+
+int route_path_override() {
+  const char* v = getenv("MSA_ROUTE_PATH");
+  if (!v) return 0;
+  if (!strcmp(v, "dot")) return 1;
+  if (!strcmp(v, "mfma")) return 2;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t msa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+const char* msa_status_string(msa_status s) {
+  switch (s) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_INVALID_ARG: return "invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "unsupported";
+    case MSA_ERR_WORKSPACE: return "workspace too small";
+    case MSA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+int64_t msa_chunk_offsets(const int64_t* doc_tok_off, int32_t n_docs, int32_t chunk,
+                          int64_t* chunk_off) {
+  g_last_error.clear();
+  if (!doc_tok_off || !chunk_off) { fail(MSA_ERR_INVALID_ARG, "null pointer"); return -1; }
+  if (n_docs < 1) { fail(MSA_ERR_INVALID_ARG, "n_docs must be >= 1 (got %d)", n_docs); return -1; }
+  if (chunk < 1) { fail(MSA_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", chunk); return -1; }
+  if (doc_tok_off[0] != 0) { fail(MSA_ERR_INVALID_ARG, "doc_tok_off[0] must be 0"); return -1; }
+  int64_t c = 0;
+  chunk_off[0] = 0;
+  for (int32_t d = 0; d < n_docs; ++d) {
+    const int64_t len = doc_tok_off[d + 1] - doc_tok_off[d];
+    if (len < 1) { fail(MSA_ERR_INVALID_ARG, "document %d has %lld tokens (need >= 1)", d, (long long)len); return -1; }
+    c += (len + chunk - 1) / chunk;
+    chunk_off[d + 1] = c;
+  }
+  return c;
+}
+
+msa_status msa_pool(msa_dtype dtype, int32_t n_docs, int64_t n_tokens, int64_t n_chunks,
+                    const int64_t* doc_tok_off, const int64_t* chunk_off, int32_t h_kv,
+                    int32_t h_r, int32_t d, int32_t chunk, float rope_base, uint32_t rope_mask,
+                    const void* K, const void* V, const void* Kr, void* Kbar, void* Vbar,
+                    void* Krbar, msa_stream_t stream) {
+  g_last_error.clear();
+  if (dtype != MSA_F32 && dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (n_docs < 1) return fail(MSA_ERR_INVALID_ARG, "n_docs must be >= 1 (got %d)", n_docs);
+  if (n_tokens < n_docs) return fail(MSA_ERR_INVALID_ARG, "n_tokens (%lld) < n_docs (%d): every document needs a token", (long long)n_tokens, n_docs);
+  if (n_chunks < n_docs || n_chunks > n_tokens) return fail(MSA_ERR_INVALID_ARG, "n_chunks (%lld) must lie in [n_docs, n_tokens]", (long long)n_chunks);
+  if (!doc_tok_off || !chunk_off) return fail(MSA_ERR_INVALID_ARG, "null offset array");
+  if (!K || !V || !Kr || !Kbar || !Vbar || !Krbar) return fail(MSA_ERR_INVALID_ARG, "null tensor pointer");
+  if (h_kv < 1 || h_kv > 64 || h_r < 1 || h_r > 64) return fail(MSA_ERR_UNSUPPORTED, "h_kv and h_r must lie in [1, 64] (got %d, %d)", h_kv, h_r);
+  if (!head_dim_ok(d)) return fail(MSA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (chunk < 1 || chunk > 128) return fail(MSA_ERR_UNSUPPORTED, "chunk %d not in [1, 128]", chunk);
+  if (rope_mask > 7u) return fail(MSA_ERR_INVALID_ARG, "rope_mask 0x%x has unknown bits", rope_mask);
+  if (rope_mask && !(rope_base > 0.f && isfinite(rope_base))) return fail(MSA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  msa::PoolArgs a{(int)dtype, n_docs, n_tokens, n_chunks, doc_tok_off, chunk_off, h_kv, h_r, d,
+                  chunk, rope_base, rope_mask, K, V, Kr, Kbar, Vbar, Krbar};
+  return hip_status(msa::launch_pool(a, (hipStream_t)stream), "msa_pool launch");
+}
+
+size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k) {
+  (void)k;
+  if (n_queries < 1 || n_docs < 1) return 0;
+  return msa::align256((size_t)n_queries * (size_t)n_docs * sizeof(uint32_t));
+}
+
+msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                          const int32_t* q_off, int32_t max_q_len, const void* Qr, int32_t h_r,
+                          int32_t d, int32_t n_docs, int64_t n_chunks, const int64_t* chunk_off,
+                          const void* Krbar, int32_t k, int32_t* topk_ids, float* topk_scores,
+                          float* doc_scores, void* workspace, size_t workspace_bytes,
+                          msa_stream_t stream) {
+  g_last_error.clear();
+  if (dtype != MSA_F32 && dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (n_queries < 1 || n_queries > 65535) return fail(MSA_ERR_INVALID_ARG, "n_queries %d not in [1, 65535]", n_queries);
+  if (total_q < 0 || total_q > INT32_MAX) return fail(MSA_ERR_INVALID_ARG, "total_q %lld out of range", (long long)total_q);
+  if (max_q_len < 1) return fail(MSA_ERR_INVALID_ARG, "max_q_len must be >= 1 (got %d)", max_q_len);
+  if (!q_off || (total_q > 0 && !Qr)) return fail(MSA_ERR_INVALID_ARG, "null query pointer");
+  if (h_r < 1 || h_r > 16) return fail(MSA_ERR_UNSUPPORTED, "h_r %d not in [1, 16]", h_r);
+  if (!head_dim_ok(d)) return fail(MSA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (n_docs < 1) return fail(MSA_ERR_INVALID_ARG, "n_docs must be >= 1 (got %d)", n_docs);
+  if (n_chunks < n_docs) return fail(MSA_ERR_INVALID_ARG, "n_chunks (%lld) < n_docs (%d)", (long long)n_chunks, n_docs);
+  if (!chunk_off || !Krbar) return fail(MSA_ERR_INVALID_ARG, "null bank pointer");
+  if (k < 1) return fail(MSA_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (k > 1024) return fail(MSA_ERR_UNSUPPORTED, "k %d > 1024", k);
+  if (!topk_ids || !topk_scores) return fail(MSA_ERR_INVALID_ARG, "null output pointer");
+  const size_t need = msa_route_topk_workspace(n_queries, n_docs, k);
+  if (!workspace || workspace_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  msa::RouteArgs r{(int)dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
+                   chunk_off, Krbar, (uint32_t*)workspace, route_path_override()};
+  msa_status st = hip_status(msa::launch_route_scan(r, s), "msa_route_topk scan launch");
+  if (st != MSA_OK) return st;
+  msa::TopkArgs t{n_queries, n_docs, k, (const uint32_t*)workspace, topk_ids, topk_scores, doc_scores};
+  return hip_status(msa::launch_topk(t, s), "msa_route_topk top-k launch");
+}
+
+size_t msa_sparse_attn_workspace(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                                 int64_t total_kv, int32_t max_q_len, int32_t hq, int32_t h_kv,
+                                 int32_t d) {
+  if ((dtype != MSA_F32 && dtype != MSA_BF16) || n_queries < 1 || total_q < 0 || total_kv < 0 ||
+      max_q_len < 1 || hq < 1 || h_kv < 1 || hq % h_kv || !head_dim_ok(d))
+    return 0;
+  return msa::attn_workspace_bytes((int)dtype, n_queries, total_q, total_kv, max_q_len, hq, h_kv, d);
+}
+
+msa_status msa_sparse_attn(msa_dtype dtype, int32_t n_queries, int64_t total_q, int64_t total_kv,
+                           const int32_t* q_off, const int32_t* kv_off, int32_t max_q_len,
+                           const void* Q, const void* Kloc, const void* Vloc, int32_t hq,
+                           int32_t h_kv, int32_t d, float rope_base, float scale, int32_t k,
+                           const int32_t* topk_ids, int32_t n_docs, int64_t n_chunks,
+                           const int64_t* chunk_off, const void* Kbar, const void* Vbar,
+                           int32_t kv_source, void* O, void* workspace, size_t workspace_bytes,
+                           msa_stream_t stream) {
+  g_last_error.clear();
+  if (dtype != MSA_F32 && dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (n_queries < 1 || n_queries > 65535) return fail(MSA_ERR_INVALID_ARG, "n_queries %d not in [1, 65535]", n_queries);
+  if (total_q < 0 || total_q > INT32_MAX || total_kv < total_q || total_kv > INT32_MAX)
+    return fail(MSA_ERR_INVALID_ARG, "need 0 <= total_q <= total_kv < 2^31 (got %lld, %lld)", (long long)total_q, (long long)total_kv);
+  if (max_q_len < 1) return fail(MSA_ERR_INVALID_ARG, "max_q_len must be >= 1 (got %d)", max_q_len);
+  if (!q_off || !kv_off) return fail(MSA_ERR_INVALID_ARG, "null offset array");
+  if (total_q > 0 && (!Q || !O)) return fail(MSA_ERR_INVALID_ARG, "null query/output pointer");
+  if (total_kv > 0 && (!Kloc || !Vloc)) return fail(MSA_ERR_INVALID_ARG, "null local K/V pointer");
+  if (hq < 1 || h_kv < 1) return fail(MSA_ERR_INVALID_ARG, "head counts must be >= 1 (got %d, %d)", hq, h_kv);
+  if (hq % h_kv) return fail(MSA_ERR_INVALID_ARG, "hq (%d) is not a multiple of h_kv (%d)", hq, h_kv);
+  if (!head_dim_ok(d)) return fail(MSA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (!(rope_base > 0.f && isfinite(rope_base))) return fail(MSA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  if (!isfinite(scale) || scale < 0.f) return fail(MSA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (k < 1) return fail(MSA_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (k > 1024) return fail(MSA_ERR_UNSUPPORTED, "k %d > 1024", k);
+  if (!topk_ids) return fail(MSA_ERR_INVALID_ARG, "null topk_ids");
+  if (n_docs < 1 || n_chunks < n_docs) return fail(MSA_ERR_INVALID_ARG, "need n_docs >= 1 and n_chunks >= n_docs");
+  if (!chunk_off || !Kbar || !Vbar) return fail(MSA_ERR_INVALID_ARG, "null bank pointer");
+  if (kv_source != 0 && kv_source != 1) return fail(MSA_ERR_INVALID_ARG, "kv_source must be 0 (device) or 1 (pinned host)");
+  const size_t need = msa_sparse_attn_workspace(dtype, n_queries, total_q, total_kv, max_q_len, hq, h_kv, d);
+  if (!workspace || workspace_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  const void* kb = Kbar;
+  const void* vb = Vbar;
+  if (kv_source == 1) {
+    // The bank's content rows live in page-locked host memory: use the device-side alias.
+    const void* host[2] = {Kbar, Vbar};
+    const void* dev[2] = {nullptr, nullptr};
+    for (int i = 0; i < 2; ++i) {
+      hipPointerAttribute_t attr;
+      hipError_t e = hipPointerGetAttributes(&attr, host[i]);
+      if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(MSA_ERR_INVALID_ARG, "kv_source=1 needs page-locked host memory for %s", i ? "Vbar" : "Kbar");
+      }
+      void* p = nullptr;
+      e = hipHostGetDevicePointer(&p, const_cast<void*>(host[i]), 0);
+      if (e != hipSuccess) return hip_status(e, "hipHostGetDevicePointer");
+      dev[i] = p;
+    }
+    kb = dev[0];
+    vb = dev[1];
+  }
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  msa::AttnArgs a{(int)dtype, n_queries, total_q, total_kv, q_off, kv_off, max_q_len, Q, Kloc, Vloc,
+                  hq, h_kv, d, rope_base, sc, k, topk_ids, n_docs, n_chunks, chunk_off, kb, vb, O,
+                  workspace};
+  return hip_status(msa::launch_sparse_attn(a, (hipStream_t)stream), "msa_sparse_attn launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,562 @@
+// Step D -- context assembly and sparse attention.
+//
+// hysenlabs.com "EverMind-AI/MSA: routing top-k compressed documents inside attention ...":
+//  * "Routing happens inside attention ...": the selected documents' compressed K/V are
+//    concatenated with the query's local K/V for decoding;
+//  * "Document-wise RoPE resets ..." (second paragraph): global RoPE over the active
+//    context; the query's start index is offset by k, the number of retrieved blocks, so
+//    the causal order is memory, then query, then generation;
+//  * "The 100M-token setup depends on host memory ...": content K/V may stay in host
+//    DRAM and be fetched only when selected.
+// yeyulingfeng.com "深度分析MSA ..." section 五 step 3: generation sees only the query's
+// local states and the top-k memory.
+//
+// Kernels:
+//  * rope_local: rotates Q and the local K at their global positions (k_eff + local
+//    index) into the workspace, angles in double precision, once per row.
+//  * attn_mfma (bf16): one workgroup per (query, kv head, 64 query rows, key split).  The
+//    key sequence is [rows of the selected documents in rank order ; local keys]; the
+//    workgroup maps each key of a 32-key tile to its source row (bank row of a selected
+//    document, read from HBM or over the host link from pinned memory, or a local row),
+//    stages K in LDS row-major and V transposed, and runs an online softmax in float32.
+//    S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 leaves each lane with 8 scores of one
+//    query row, which are exactly the P^T operand of O^T = V^T * P^T, so probabilities
+//    never leave registers.
+//  * attn_valu (float32): one thread per (query row, head), plain online softmax.
+//  * attn_combine: merges the per-split (max, sum, unnormalised output) triples.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int RPW = 4;          // rows per workgroup in rope_local
+constexpr int ATT_WAVES = 4;    // waves per attention workgroup (16 query rows each)
+constexpr int ATT_ROWS = ATT_WAVES * 16;
+constexpr int KT = 32;          // keys per tile
+
+struct AttnK {
+  int n_queries;
+  int64_t total_q, total_kv;
+  const int32_t *q_off, *kv_off;
+  const void *Q, *Kloc, *Vloc;
+  int hq, h_kv;
+  float rope_base, scale_log2;
+  int k;
+  const int32_t* ids;
+  const int64_t* chunk_off;
+  const void *Kbar, *Vbar;
+  void* O;
+  void* Qrot;
+  void* Krot;
+  float* part_o;
+  float* part_ml;
+  int splits;
+};
+
+__device__ __forceinline__ int find_query(const int32_t* off, int n, int64_t row) {
+  int lo = 0, hi = n;  // largest b with off[b] <= row
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int count_valid_ids(const int32_t* ids, int k) {
+  int n = 0;
+  for (int r = 0; r < k; ++r) n += ids[r] >= 0;
+  return n;
+}
+
+// ---- global RoPE of the local context --------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
+  __shared__ float cs_tab[RPW][D / 2], sn_tab[RPW][D / 2];
+  __shared__ int row_q[RPW];
+  __shared__ int64_t row_pos[RPW];
+  const bool is_q = blockIdx.x < (unsigned)nq_blocks;
+  const int64_t r0 = (int64_t)(is_q ? blockIdx.x : blockIdx.x - nq_blocks) * RPW;
+  const int64_t total = is_q ? a.total_q : a.total_kv;
+  const int heads = is_q ? a.hq : a.h_kv;
+  const T* src = (const T*)(is_q ? a.Q : a.Kloc);
+  T* dst = (T*)(is_q ? a.Qrot : a.Krot);
+  const int32_t* off = is_q ? a.q_off : a.kv_off;
+  const int tid = threadIdx.x;
+  if (tid < RPW) {
+    const int64_t r = r0 + tid;
+    int64_t pos = -1;
+    if (r < total) {
+      const int b = find_query(off, a.n_queries, r);
+      const int keff = count_valid_ids(a.ids + (int64_t)b * a.k, a.k);
+      const int64_t Lq = a.q_off[b + 1] - a.q_off[b];
+      const int64_t Lkv = a.kv_off[b + 1] - a.kv_off[b];
+      pos = is_q ? keff + (Lkv - Lq) + (r - off[b]) : keff + (r - off[b]);
+      row_q[tid] = b;
+    }
+    row_pos[tid] = pos;
+  }
+  __syncthreads();
+  for (int e = tid; e < RPW * (D / 2); e += blockDim.x) {
+    const int rr = e / (D / 2), i = e % (D / 2);
+    const double th = pow((double)a.rope_base, -2.0 * (double)i / (double)D);
+    double sn = 0.0, cs = 1.0;
+    if (row_pos[rr] >= 0) sincos((double)row_pos[rr] * th, &sn, &cs);
+    cs_tab[rr][i] = (float)cs;
+    sn_tab[rr][i] = (float)sn;
+  }
+  __syncthreads();
+  const int units = RPW * heads * (D / 8);  // unit = 4 rotation pairs
+  for (int u = tid; u < units; u += blockDim.x) {
+    const int rr = u / (heads * (D / 8));
+    const int rem = u % (heads * (D / 8));
+    const int h = rem / (D / 8), i0 = (rem % (D / 8)) * 4;
+    const int64_t r = r0 + rr;
+    if (r >= total) continue;
+    const T* p = src + (r * heads + h) * D;
+    float lo[4], hi[4], o_lo[4], o_hi[4];
+    Elem<T>::load4(p + i0, lo);
+    Elem<T>::load4(p + i0 + D / 2, hi);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float c = cs_tab[rr][i0 + q], s = sn_tab[rr][i0 + q];
+      o_lo[q] = lo[q] * c - hi[q] * s;
+      o_hi[q] = hi[q] * c + lo[q] * s;
+    }
+    T* o = dst + (r * heads + h) * D;
+    Elem<T>::store4(o + i0, o_lo);
+    Elem<T>::store4(o + i0 + D / 2, o_hi);
+  }
+}
+
+// Memory layout of one query: the selected documents' bank rows in rank order.
+struct MemMap {
+  int keff;
+  int64_t M;
+};
+
+// Fills mstart[r] (first bank row of the r-th valid document) and mpre[r] (its first key
+// index); mpre[keff] = M.  Runs on wave 0; k <= 1024.
+__device__ __forceinline__ MemMap build_memmap(const int32_t* ids, int k, const int64_t* chunk_off,
+                                               int64_t* mstart, int64_t* mpre) {
+  const int lane = threadIdx.x & 63;
+  int64_t run = 0;
+  int keff = 0;
+  for (int r0 = 0; r0 < k; r0 += 64) {
+    const int r = r0 + lane;
+    const int id = (r < k) ? ids[r] : -1;
+    const bool ok = id >= 0;
+    int64_t cnt = 0, st = 0;
+    if (ok) { st = chunk_off[id]; cnt = chunk_off[id + 1] - st; }
+    // exclusive scans of cnt and of ok over the wave
+    int64_t x = cnt;
+    int y = ok ? 1 : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t xo = __shfl_up(x, o);
+      const int yo = __shfl_up(y, o);
+      if (lane >= o) { x += xo; y += yo; }
+    }
+    if (ok) {
+      const int slot = keff + y - 1;
+      mstart[slot] = st;
+      mpre[slot] = run + x - cnt;
+    }
+    run += __shfl(x, 63);
+    keff += __shfl(y, 63);
+  }
+  if (lane == 0) mpre[keff] = run;
+  return {keff, run};
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_mfma(AttnK a) {
+  constexpr int KK = D / 32;
+  constexpr int MD = D / 16;
+  constexpr int KSTR = D + 8;   // bf16 per K row in LDS
+  constexpr int VSTR = KT + 8;  // bf16 per V^T row in LDS
+  __shared__ __align__(16) bf16_t Ks[KT * KSTR];
+  __shared__ __align__(16) bf16_t Vt[D * VSTR];
+  __shared__ int64_t mstart[1025], mpre[1025];
+  __shared__ int sh_keff;
+  __shared__ int64_t sh_M;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int cl = lane & 15, g4 = lane >> 4;
+  const int b = blockIdx.z;
+  const int g = blockIdx.y % a.h_kv;
+  const int split = blockIdx.y / a.h_kv;
+  const int G = a.hq / a.h_kv;
+  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+  const int kv0 = a.kv_off[b], Lkv = a.kv_off[b + 1] - kv0;
+  const int nrows = Lq * G;
+  const int rb = blockIdx.x * ATT_ROWS;
+  if (rb >= nrows) return;
+
+  if (w == 0) {
+    MemMap mm = build_memmap(a.ids + (int64_t)b * a.k, a.k, a.chunk_off, mstart, mpre);
+    if (lane == 0) { sh_keff = mm.keff; sh_M = mm.M; }
+  }
+  __syncthreads();
+  const int keff = sh_keff;
+  const int64_t M = sh_M;
+  const int64_t NK = M + Lkv;
+  int64_t k_lo = NK * split / a.splits, k_hi = NK * (split + 1) / a.splits;
+  // keys past the last local position any row of this block may see are never needed
+  const int t_max = min(Lq - 1, (rb + ATT_ROWS - 1) / G);
+  k_hi = min(k_hi, M + (int64_t)(Lkv - Lq + t_max + 1));
+
+  // this lane's query row (B operand of S^T), and its causal limit in key indices
+  const int row = rb + w * 16 + cl;
+  const bool row_ok = row < nrows;
+  const int t = row_ok ? row / G : 0;
+  const int hq = g * G + (row_ok ? row % G : 0);
+  const int64_t key_lim = M + (int64_t)(Lkv - Lq + t);  // last visible key index
+  bf16x8_t Qf[KK];
+  {
+    const bf16_t* qp = (const bf16_t*)a.Qrot + ((int64_t)(q0 + t) * a.hq + hq) * D + g4 * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      Qf[kk] = row_ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + kk * 32))
+                      : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+  }
+
+  f32x4_t acc[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) acc[md] = {0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const bf16_t* Kb = (const bf16_t*)a.Kbar;
+  const bf16_t* Vb = (const bf16_t*)a.Vbar;
+  const bf16_t* Kr = (const bf16_t*)a.Krot;
+  const bf16_t* Vl = (const bf16_t*)a.Vloc;
+  constexpr int UPR = D / 8;  // 16-byte units per key row
+
+  for (int64_t kt = k_lo; kt < k_hi; kt += KT) {
+    // ---- stage K (row-major) and V (transposed) for keys kt .. kt+31 ----
+    for (int u = tid; u < KT * UPR; u += blockDim.x) {
+      const int kr = u / UPR, e0 = (u % UPR) * 8;
+      const int64_t key = kt + kr;
+      uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
+      if (key < k_hi) {
+        const bf16_t *kp, *vp;
+        if (key < M) {
+          int lo = 0, hi = keff;  // rank r with mpre[r] <= key < mpre[r+1]
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (mpre[mid] <= key) lo = mid; else hi = mid;
+          }
+          const int64_t brow = mstart[lo] + (key - mpre[lo]);
+          kp = Kb + (brow * a.h_kv + g) * D + e0;
+          vp = Vb + (brow * a.h_kv + g) * D + e0;
+        } else {
+          const int64_t lrow = kv0 + (key - M);
+          kp = Kr + (lrow * a.h_kv + g) * D + e0;
+          vp = Vl + (lrow * a.h_kv + g) * D + e0;
+        }
+        kw = *reinterpret_cast<const uint4*>(kp);
+        vw = *reinterpret_cast<const uint4*>(vp);
+      }
+      *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = kw;
+      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        Vt[(e0 + 2 * q) * VSTR + kr] = (bf16_t)(vv[q] & 0xffffu);
+        Vt[(e0 + 2 * q + 1) * VSTR + kr] = (bf16_t)(vv[q] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for two 16-key halves ----
+    f32x4_t s[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      s[n] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(&Ks[(n * 16 + cl) * KSTR + kk * 32 + g4 * 8]);
+        s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), Qf[kk], s[n], 0, 0, 0);
+      }
+    }
+    // lane holds S[row cl][key kt + n*16 + g4*4 + i]
+    float mx = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = kt + n * 16 + g4 * 4 + i;
+        const bool vis = row_ok && key < k_hi && key <= key_lim;
+        s[n][i] = vis ? s[n][i] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[n][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    float alpha = 1.f;
+    float p[2][4];
+    if (m_new == -INFINITY) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[n][i] = 0.f;
+    } else {
+      alpha = exp2f(m_run - m_new);
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[n][i] = exp2f(s[n][i] - m_new);
+    }
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps += p[n][i];
+    l_run = l_run * alpha + ps;
+    // P^T operand: k-slot g4*8 + j  <->  key g4*4 + j (j < 4), 16 + g4*4 + (j-4) (j >= 4)
+    uint4 pw;
+    pw.x = f32_to_bf16(p[0][0]) | (f32_to_bf16(p[0][1]) << 16);
+    pw.y = f32_to_bf16(p[0][2]) | (f32_to_bf16(p[0][3]) << 16);
+    pw.z = f32_to_bf16(p[1][0]) | (f32_to_bf16(p[1][1]) << 16);
+    pw.w = f32_to_bf16(p[1][2]) | (f32_to_bf16(p[1][3]) << 16);
+    const bf16x8_t Pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const bf16_t* vr = &Vt[(md * 16 + cl) * VSTR];
+      const uint2 v0 = *reinterpret_cast<const uint2*>(vr + g4 * 4);
+      const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + g4 * 4);
+      const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[md][i] *= alpha;
+      acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vf, Pf, acc[md], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // row totals: the 4 lane groups of a row hold partial sums
+  float l_row = l_run + __shfl_xor(l_run, 16);
+  l_row += __shfl_xor(l_row, 32);
+  if (!row_ok) return;
+  const int64_t orow = (int64_t)(q0 + t) * a.hq + hq;
+  if (a.splits == 1) {
+    const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
+    bf16_t* o = (bf16_t*)a.O + orow * D + g4 * 4;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      float f[4] = {acc[md][0] * inv, acc[md][1] * inv, acc[md][2] * inv, acc[md][3] * inv};
+      Elem<bf16_t>::store4(o + md * 16, f);
+    }
+  } else {
+    const int64_t prow = (int64_t)split * a.total_q * a.hq + orow;
+    float* po = a.part_o + prow * D + g4 * 4;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+      *reinterpret_cast<float4*>(po + md * 16) = make_float4(acc[md][0], acc[md][1], acc[md][2], acc[md][3]);
+    if (g4 == 0) {
+      a.part_ml[prow * 2] = m_run;
+      a.part_ml[prow * 2 + 1] = l_row;
+    }
+  }
+}
+
+// ---- float32 path: one thread per (query row, head) ----------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void attn_valu(AttnK a) {
+  const int b = blockIdx.y;
+  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+  const int kv0 = a.kv_off[b], Lkv = a.kv_off[b + 1] - kv0;
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= Lq * a.hq) return;
+  const int t = r / a.hq, hq = r % a.hq;
+  const int g = hq / (a.hq / a.h_kv);
+  const T* Qr = (const T*)a.Qrot + ((int64_t)(q0 + t) * a.hq + hq) * D;
+  float q[D], acc[D];
+#pragma unroll
+  for (int e = 0; e < D; e += 8) Elem<T>::load8(Qr + e, q + e);
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  auto visit = [&](const T* kp, const T* vp) {
+    float kv[8], dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; e += 8) {
+      Elem<T>::load8(kp + e, kv);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) dot += q[e + x] * kv[x];
+    }
+    const float s = dot * a.scale_log2;
+    const float mn = fmaxf(m, s);
+    const float al = exp2f(m - mn), p = exp2f(s - mn);
+    l = l * al + p;
+#pragma unroll
+    for (int e = 0; e < D; e += 8) {
+      Elem<T>::load8(vp + e, kv);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[e + x] = acc[e + x] * al + p * kv[x];
+    }
+    m = mn;
+  };
+  const int32_t* ids = a.ids + (int64_t)b * a.k;
+  const T* Kb = (const T*)a.Kbar;
+  const T* Vb = (const T*)a.Vbar;
+  for (int rr = 0; rr < a.k; ++rr) {
+    const int id = ids[rr];
+    if (id < 0) continue;
+    for (int64_t c = a.chunk_off[id]; c < a.chunk_off[id + 1]; ++c)
+      visit(Kb + (c * a.h_kv + g) * D, Vb + (c * a.h_kv + g) * D);
+  }
+  const T* Kr = (const T*)a.Krot;
+  const T* Vl = (const T*)a.Vloc;
+  for (int j = 0; j <= Lkv - Lq + t; ++j)
+    visit(Kr + ((int64_t)(kv0 + j) * a.h_kv + g) * D, Vl + ((int64_t)(kv0 + j) * a.h_kv + g) * D);
+  T* o = (T*)a.O + ((int64_t)(q0 + t) * a.hq + hq) * D;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < D; e += 8) {
+    float f[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) f[x] = acc[e + x] * inv;
+    Elem<T>::store8(o + e, f);
+  }
+}
+
+// ---- merge of key splits -------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine(AttnK a) {
+  // one wave per output row; lane covers D/64 elements (at least one)
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = a.total_q * a.hq;
+  if (row >= rows) return;
+  float mstar = -INFINITY;
+  for (int s = 0; s < a.splits; ++s)
+    mstar = fmaxf(mstar, a.part_ml[((int64_t)s * rows + row) * 2]);
+  float L = 0.f;
+  constexpr int PER = (D + 63) / 64;
+  float o[PER];
+#pragma unroll
+  for (int x = 0; x < PER; ++x) o[x] = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    const int64_t pr = (int64_t)s * rows + row;
+    const float ms = a.part_ml[pr * 2];
+    if (ms == -INFINITY) continue;
+    const float wgt = exp2f(ms - mstar);
+    L += wgt * a.part_ml[pr * 2 + 1];
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int e = lane + 64 * x;
+      if (e < D) o[x] += wgt * a.part_o[pr * D + e];
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  bf16_t* out = (bf16_t*)a.O + row * D;
+#pragma unroll
+  for (int x = 0; x < PER; ++x) {
+    const int e = lane + 64 * x;
+    if (e < D) out[e] = (bf16_t)f32_to_bf16(o[x] * inv);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, hipStream_t s) {
+  const int nq_blocks = (int)((r.total_q + RPW - 1) / RPW);
+  const int nk_blocks = (int)((r.total_kv + RPW - 1) / RPW);
+  if (nq_blocks + nk_blocks > 0) {
+    hipLaunchKernelGGL((rope_local<T, D>), dim3(nq_blocks + nk_blocks), dim3(256), 0, s, k, nq_blocks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (r.total_q == 0) return hipSuccess;
+  if constexpr (sizeof(T) == 4) {
+    k.splits = 1;
+    dim3 grid((unsigned)((r.max_q_len * r.hq + 63) / 64), (unsigned)r.n_queries);
+    hipLaunchKernelGGL((attn_valu<T, D>), grid, dim3(64), 0, s, k);
+    return hipGetLastError();
+  } else {
+    const int G = r.hq / r.h_kv;
+    const int rblocks = (r.max_q_len * G + ATT_ROWS - 1) / ATT_ROWS;
+    dim3 grid((unsigned)rblocks, (unsigned)(r.h_kv * k.splits), (unsigned)r.n_queries);
+    hipLaunchKernelGGL((attn_mfma<D>), grid, dim3(64 * ATT_WAVES), 0, s, k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || k.splits == 1) return e;
+    const int64_t rows = r.total_q * r.hq;
+    hipLaunchKernelGGL((attn_combine<D>), dim3((unsigned)((rows * 64 + 255) / 256)), dim3(256), 0, s, k);
+    return hipGetLastError();
+  }
+}
+
+}  // namespace
+
+int attn_splits(int n_queries, int max_q_len, int hq, int h_kv) {
+  const int G = hq / h_kv;
+  const int rblocks = (max_q_len * G + ATT_ROWS - 1) / ATT_ROWS;
+  const long base = (long)n_queries * h_kv * (rblocks > 0 ? rblocks : 1);
+  long s = (256 + base - 1) / base;
+  if (s < 1) s = 1;
+  if (s > 8) s = 8;
+  return (int)s;
+}
+
+size_t attn_workspace_bytes(int dtype, int n_queries, int64_t total_q, int64_t total_kv,
+                            int max_q_len, int hq, int h_kv, int d) {
+  const size_t esz = dtype == 0 ? 4 : 2;
+  size_t bytes = align256((size_t)total_q * hq * d * esz) + align256((size_t)total_kv * h_kv * d * esz);
+  if (dtype == 1) {
+    const int s = attn_splits(n_queries, max_q_len, hq, h_kv);
+    if (s > 1) {
+      bytes += align256((size_t)s * total_q * hq * d * 4);
+      bytes += align256((size_t)s * total_q * hq * 2 * 4);
+    }
+  }
+  return bytes;
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& r, hipStream_t s) {
+  AttnK k{};
+  k.n_queries = r.n_queries;
+  k.total_q = r.total_q;
+  k.total_kv = r.total_kv;
+  k.q_off = r.q_off;
+  k.kv_off = r.kv_off;
+  k.Q = r.Q;
+  k.Kloc = r.Kloc;
+  k.Vloc = r.Vloc;
+  k.hq = r.hq;
+  k.h_kv = r.h_kv;
+  k.rope_base = r.rope_base;
+  k.scale_log2 = r.scale * 1.4426950408889634f;
+  k.k = r.k;
+  k.ids = r.ids;
+  k.chunk_off = r.chunk_off;
+  k.Kbar = r.Kbar;
+  k.Vbar = r.Vbar;
+  k.O = r.O;
+  const size_t esz = r.dtype == 0 ? 4 : 2;
+  char* ws = (char*)r.workspace;
+  k.Qrot = ws;
+  ws += align256((size_t)r.total_q * r.hq * r.d * esz);
+  k.Krot = ws;
+  ws += align256((size_t)r.total_kv * r.h_kv * r.d * esz);
+  k.splits = r.dtype == 1 ? attn_splits(r.n_queries, r.max_q_len, r.hq, r.h_kv) : 1;
+  if (k.splits > 1) {
+    k.part_o = (float*)ws;
+    ws += align256((size_t)k.splits * r.total_q * r.hq * r.d * 4);
+    k.part_ml = (float*)ws;
+  }
+  if (r.dtype == 0) {
+    switch (r.d) {
+      case 32: return launch_attn_t<float, 32>(r, k, s);
+      case 64: return launch_attn_t<float, 64>(r, k, s);
+      default: return launch_attn_t<float, 128>(r, k, s);
+    }
+  }
+  switch (r.d) {
+    case 32: return launch_attn_t<bf16_t, 32>(r, k, s);
+    case 64: return launch_attn_t<bf16_t, 64>(r, k, s);
+    default: return launch_attn_t<bf16_t, 128>(r, k, s);
+  }
+}
+
+}  // namespace msa

@@ -1,0 +1,142 @@
+// Device helpers shared by the MSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+// ---- element types -------------------------------------------------------------------
+// bf16 is carried as its 16-bit pattern: the upper half of an IEEE float32.
+typedef uint16_t bf16_t;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Unpack 8 bf16 (one 16-byte word) into floats.
+__device__ __forceinline__ void unpack8(const uint4& w, float* f) {
+  f[0] = __uint_as_float(w.x << 16); f[1] = __uint_as_float(w.x & 0xffff0000u);
+  f[2] = __uint_as_float(w.y << 16); f[3] = __uint_as_float(w.y & 0xffff0000u);
+  f[4] = __uint_as_float(w.z << 16); f[5] = __uint_as_float(w.z & 0xffff0000u);
+  f[6] = __uint_as_float(w.w << 16); f[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ void unpack4(const uint2& w, float* f) {
+  f[0] = __uint_as_float(w.x << 16); f[1] = __uint_as_float(w.x & 0xffff0000u);
+  f[2] = __uint_as_float(w.y << 16); f[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  uint4 w;
+  w.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
+  w.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
+  w.z = f32_to_bf16(f[4]) | (f32_to_bf16(f[5]) << 16);
+  w.w = f32_to_bf16(f[6]) | (f32_to_bf16(f[7]) << 16);
+  return w;
+}
+
+__device__ __forceinline__ uint2 pack4(const float* f) {
+  uint2 w;
+  w.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
+  w.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
+  return w;
+}
+
+// Load / store n contiguous elements (n = 4 or 8) as floats, for either storage type.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static void load8(const float* p, float* f) {
+    float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  __device__ __forceinline__ static void load4(const float* p, float* f) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  }
+  __device__ __forceinline__ static void store8(float* p, const float* f) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  __device__ __forceinline__ static void store4(float* p, const float* f) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static void load8(const bf16_t* p, float* f) {
+    unpack8(*reinterpret_cast<const uint4*>(p), f);
+  }
+  __device__ __forceinline__ static void load4(const bf16_t* p, float* f) {
+    unpack4(*reinterpret_cast<const uint2*>(p), f);
+  }
+  __device__ __forceinline__ static void store8(bf16_t* p, const float* f) {
+    *reinterpret_cast<uint4*>(p) = pack8(f);
+  }
+  __device__ __forceinline__ static void store4(bf16_t* p, const float* f) {
+    *reinterpret_cast<uint2*>(p) = pack4(f);
+  }
+};
+
+// ---- order-preserving score keys -------------------------------------------------------
+// Maps a float to a uint32 whose unsigned order is the float order (-0.0 folded into
+// +0.0).  Key 0 sorts below every non-NaN float and marks "no score yet".
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  if (k == 0u) return -INFINITY;  // never scored (a query with no tokens)
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ---- wave64 reductions ------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Workgroup barrier that waits only for LDS traffic, so global loads issued earlier
+// (prefetches) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Index of the document owning bank row c: the largest d with chunk_off[d] <= c, found by
+// one wave with 64-way search (a few dependent loads instead of log2(N)).  All lanes
+// return the same value.
+__device__ __forceinline__ int find_doc_wave(const int64_t* chunk_off, int n_docs, int64_t c) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n_docs;  // invariant: chunk_off[lo] <= c, answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int span = hi - lo;
+    // span <= 64: one lane per candidate; else 64 strictly increasing sample points.
+    const int p = (span <= 64) ? lo + lane : lo + (int)(((int64_t)span * lane) / 64);
+    const bool ok = (p < hi) && (chunk_off[p] <= c);
+    const uint64_t m = __ballot(ok);              // lane 0 (p = lo) is always set
+    const int best = 63 - __clzll((long long)m);  // highest lane with chunk_off[p] <= c
+    if (span <= 64) return lo + best;
+    const int pn = (best == 63) ? hi : lo + (int)(((int64_t)span * (best + 1)) / 64);
+    lo = lo + (int)(((int64_t)span * best) / 64);
+    hi = pn;
+  }
+  return lo;
+}
+
+}  // namespace msa

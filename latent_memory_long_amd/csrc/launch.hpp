@@ -1,0 +1,75 @@
+// Internal launchers: one per kernel family, defined next to the kernels.  Each one
+// assumes the C-ABI layer already validated its arguments and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct PoolArgs {
+  int dtype;  // 0 f32, 1 bf16
+  int n_docs;
+  int64_t n_tokens, n_chunks;
+  const int64_t* doc_tok_off;
+  const int64_t* chunk_off;
+  int h_kv, h_r, d, chunk;
+  float rope_base;
+  uint32_t rope_mask;
+  const void *K, *V, *Kr;
+  void *Kbar, *Vbar, *Krbar;
+};
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+
+struct RouteArgs {
+  int dtype;
+  int n_queries;
+  int64_t total_q;
+  const int32_t* q_off;
+  int max_q_len;
+  const void* Qr;
+  int h_r, d;
+  int n_docs;
+  int64_t n_chunks;
+  const int64_t* chunk_off;
+  const void* Krbar;
+  uint32_t* keys;  // [n_queries, n_docs] workspace
+  int force_path;  // 0 auto, 1 dot, 2 mfma (test hook, not in the C ABI)
+};
+hipError_t launch_route_scan(const RouteArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  int n_queries, n_docs, k;
+  const uint32_t* keys;
+  int32_t* ids;
+  float* scores;
+  float* doc_scores;  // may be null
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  int dtype;
+  int n_queries;
+  int64_t total_q, total_kv;
+  const int32_t *q_off, *kv_off;
+  int max_q_len;
+  const void *Q, *Kloc, *Vloc;
+  int hq, h_kv, d;
+  float rope_base, scale;
+  int k;
+  const int32_t* ids;
+  int n_docs;
+  int64_t n_chunks;
+  const int64_t* chunk_off;
+  const void *Kbar, *Vbar;
+  void* O;
+  void* workspace;
+};
+int attn_splits(int n_queries, int max_q_len, int hq, int h_kv);
+size_t attn_workspace_bytes(int dtype, int n_queries, int64_t total_q, int64_t total_kv,
+                            int max_q_len, int hq, int h_kv, int d);
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace msa

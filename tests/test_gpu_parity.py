@@ -1,0 +1,329 @@
+"""GPU parity of the HIP path against the CPU oracle, at sizes the oracle finishes in
+seconds that still span many tiles and ragged tails.  Every case prints its name before
+touching the GPU."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import latent_memory_long_amd as M
+from oracle import msa_oracle as O
+from synth import workloads as W
+from tests.helpers import (assert_attn_close, assert_pool_close, assert_scores_close,
+                           assert_topk_consistent, assert_topk_valid, f64, say)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _dt(dtype):
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+def _cpu_randn(shape, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32) * std
+
+
+def _route_env(path):
+    if path == "auto":
+        os.environ.pop("MSA_ROUTE_PATH", None)
+    else:
+        os.environ["MSA_ROUTE_PATH"] = path
+
+
+@pytest.fixture(autouse=True)
+def _reset_env():
+    yield
+    os.environ.pop("MSA_ROUTE_PATH", None)
+
+
+def random_bank(n_chunks_per_doc, heads, d, dtype, seed, doc_std=0.5):
+    """Pooled-looking bank: per-document offset plus noise, rows of each document
+    contiguous.  Returns (chunk_off host, tensor [C, heads, d] on the GPU)."""
+    counts = np.asarray(n_chunks_per_doc, dtype=np.int64)
+    coff = np.concatenate([[0], np.cumsum(counts)])
+    mu = _cpu_randn((len(counts), heads, d), seed, doc_std)
+    x = _cpu_randn((int(coff[-1]), heads, d), seed + 1, 0.125)
+    x += torch.repeat_interleave(mu, torch.as_tensor(counts), dim=0)
+    return coff, x.to(_dt(dtype)).to(DEV)
+
+
+def route(Qr, q_lens, Krb, coff, k, want=True):
+    q_off = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]), dtype=torch.int32, device=DEV)
+    coff_d = torch.tensor(coff, dtype=torch.int64, device=DEV)
+    ids, sc, ds = M.msa_route_topk(Qr, q_off, int(max(q_lens)), Krb, coff_d, k, want_doc_scores=want)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), sc.cpu().numpy(), (ds.cpu().numpy() if ds is not None else None)
+
+
+# ------------------------------------------------------------------------------ end to end
+
+def test_tiny_fp32_end_to_end():
+    say("case tiny_fp32 end-to-end")
+    wl = W.workload("tiny_fp32")
+    sh = wl.shape
+    lens = W.doc_lengths(wl)
+    off = W.token_offsets(lens)
+    K, V, Kr = W.gen_token_states(wl, lens, "cpu")
+    coff = M.msa_chunk_offsets(off, sh.chunk)
+    C = int(coff[-1])
+    off_d = torch.tensor(off, device=DEV)
+    coff_d = torch.tensor(coff, device=DEV)
+    Kb, Vb, Krb = M.msa_pool(K.to(DEV), V.to(DEV), Kr.to(DEV), off_d, coff_d, C, sh.chunk, sh.rope_base)
+    oK, oV, oKr, ocoff = O.pool(f64(K), f64(V), f64(Kr), off, sh.chunk, sh.rope_base, O.ROPE_K)
+    assert np.array_equal(ocoff, coff)
+    for g, o, n in ((Kb, oK, "Kbar"), (Vb, oV, "Vbar"), (Krb, oKr, "Krbar")):
+        assert_pool_close(g, o, "f32", n)
+
+    q = W.gen_queries(wl, "cpu")
+    Lq = int(q["q_len"][0])
+    ids, sc, ds = route(q["Qr"].to(DEV), q["q_len"], Krb, coff, wl.k)
+    o_ds = O.route_doc_scores(f64(q["Qr"]), [0, Lq], f64(Krb), coff)[0]
+    assert_scores_close(ds[0], o_ds, "f32", "doc scores (gpu bank)")
+    assert_topk_consistent(ids[0], sc[0], ds[0], wl.k, "topk")
+    assert_topk_valid(ids[0], o_ds, wl.k, "topk vs oracle (gpu bank)")
+    # end to end: oracle bank, oracle route
+    e2e = O.route_doc_scores(f64(q["Qr"]), [0, Lq], oKr, coff)[0]
+    assert_topk_valid(ids[0], e2e, wl.k, "topk vs oracle (oracle bank)")
+
+    q_off = torch.tensor([0, Lq], dtype=torch.int32, device=DEV)
+    kv_off = torch.tensor([0, int(q["kv_len"][0])], dtype=torch.int32, device=DEV)
+    ids_d = torch.tensor(ids, device=DEV)
+    Out = M.msa_sparse_attn(q["Q"].to(DEV), q["Kloc"].to(DEV), q["Vloc"].to(DEV), q_off, kv_off, Lq,
+                            ids_d, coff_d, Kb, Vb, rope_base=sh.rope_base)
+    torch.cuda.synchronize()
+    ref = O.sparse_attn(f64(q["Q"]), f64(q["Kloc"]), f64(q["Vloc"]), [0, Lq], [0, int(q["kv_len"][0])],
+                        ids, coff, f64(Kb), f64(Vb), sh.rope_base)
+    assert_attn_close(Out, ref, "f32", "attention (gpu bank, gpu ids)")
+    ref2 = O.sparse_attn(f64(q["Q"]), f64(q["Kloc"]), f64(q["Vloc"]), [0, Lq], [0, int(q["kv_len"][0])],
+                         ids, coff, oK, oV, sh.rope_base)
+    assert_attn_close(Out, ref2, "f32", "attention (oracle bank)")
+
+
+# ------------------------------------------------------------------------------ pooling
+
+POOL_CASES = [
+    # (name, heads kv, heads r, d, chunk, rope mask, dtype)
+    ("qwen_like", 8, 8, 128, 64, 1, "bf16"),
+    ("rope_all", 8, 8, 128, 64, 7, "bf16"),
+    ("no_rope", 8, 8, 128, 64, 0, "bf16"),
+    ("d64_chunk48", 4, 2, 64, 48, 1, "bf16"),
+    ("d32_chunk128", 2, 3, 32, 128, 5, "bf16"),
+    ("f32_d128", 2, 2, 128, 64, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", POOL_CASES, ids=[c[0] for c in POOL_CASES])
+def test_pool(case):
+    name, hkv, hr, d, chunk, mask, dtype = case
+    say(f"case pool {name}")
+    rng = np.random.default_rng(7)
+    lens = np.concatenate([[1, 63, 64, 65, 128, 129, chunk - 1, chunk + 1, 2 * chunk],
+                           rng.integers(1, 700, size=25)]).astype(np.int64)
+    lens = np.maximum(lens, 1)
+    off = W.token_offsets(lens)
+    T = int(off[-1])
+    K = _cpu_randn((T, hkv, d), 1).to(_dt(dtype))
+    V = _cpu_randn((T, hkv, d), 2).to(_dt(dtype))
+    Kr = _cpu_randn((T, hr, d), 3).to(_dt(dtype))
+    coff = M.msa_chunk_offsets(off, chunk)
+    C = int(coff[-1])
+    Kb, Vb, Krb = M.msa_pool(K.to(DEV), V.to(DEV), Kr.to(DEV), torch.tensor(off, device=DEV),
+                             torch.tensor(coff, device=DEV), C, chunk, 1e6, mask)
+    torch.cuda.synchronize()
+    oK, oV, oKr, _ = O.pool(f64(K), f64(V), f64(Kr), off, chunk, 1e6, mask)
+    for g, o, n in ((Kb, oK, "Kbar"), (Vb, oV, "Vbar"), (Krb, oKr, "Krbar")):
+        assert_pool_close(g, o, dtype, f"{name} {n}")
+
+
+def test_pool_constant_chunk_bit_exact_and_doc_restart():
+    say("case pool constant chunk / document restart")
+    d, h = 128, 8
+    v = _cpu_randn((1, h, d), 11).to(torch.bfloat16)
+    lens = np.array([64, 100, 1, 64], dtype=np.int64)
+    K = v.repeat(int(lens.sum()), 1, 1)
+    # document 3 repeats document 0's random content: identical pooled rows expected
+    rnd = _cpu_randn((64, h, d), 12).to(torch.bfloat16)
+    K[165:229] = rnd
+    K[0:64] = rnd
+    off = W.token_offsets(lens)
+    coff = M.msa_chunk_offsets(off, 64)
+    Kb, Vb, Krb = M.msa_pool(K.to(DEV), K.to(DEV), K.to(DEV), torch.tensor(off, device=DEV),
+                             torch.tensor(coff, device=DEV), int(coff[-1]), 64, 1e6, 1)
+    torch.cuda.synchronize()
+    Vb, Kb, Krb = Vb.cpu(), Kb.cpu(), Krb.cpu()
+    # constant chunks (rows 1, 2 of document 1 and document 2) pool to the value itself
+    for r in (1, 2, 3):
+        assert torch.equal(Vb[r], v[0]) and torch.equal(Krb[r], v[0])
+    assert torch.equal(Kb[3], v[0])          # single-token document: rotation at 0
+    assert torch.equal(Kb[0], Kb[4]) and torch.equal(Vb[0], Vb[4])
+
+
+# ------------------------------------------------------------------------------ routing
+
+def _chunk_counts(n_docs, seed, small_frac=0.4, hi=40):
+    rng = np.random.default_rng(seed)
+    c = rng.integers(1, hi, size=n_docs)
+    c[rng.random(n_docs) < small_frac] = 1          # many one-row documents: many per tile
+    return c
+
+
+ROUTE_CASES = [(lq, path) for lq in (1, 3, 15, 16, 17, 40, 64, 65, 100) for path in ("auto", "dot", "mfma")]
+
+
+@pytest.mark.parametrize("lq,path", ROUTE_CASES, ids=[f"lq{a}-{b}" for a, b in ROUTE_CASES])
+def test_route_bf16(lq, path):
+    say(f"case route bf16 lq={lq} path={path}")
+    _route_env(path)
+    counts = _chunk_counts(300, 5)
+    coff, Krb = random_bank(counts, 8, 128, "bf16", 20)
+    Qr = (_cpu_randn((lq, 8, 128), 21) + _cpu_randn((1, 8, 128), 22, 0.5)).to(torch.bfloat16)
+    for k in (1, 16):
+        ids, sc, ds = route(Qr.to(DEV), [lq], Krb, coff, k)
+        o = O.route_doc_scores(f64(Qr), [0, lq], f64(Krb), coff)[0]
+        assert_scores_close(ds[0], o, "bf16", f"lq{lq} {path} scores")
+        assert_topk_consistent(ids[0], sc[0], ds[0], k, "consistency")
+        assert_topk_valid(ids[0], o, k, f"lq{lq} {path} k{k}")
+
+
+@pytest.mark.parametrize("lq", [1, 8, 20])
+def test_route_fp32(lq):
+    say(f"case route fp32 lq={lq}")
+    counts = _chunk_counts(100, 6)
+    coff, Krb = random_bank(counts, 2, 32, "f32", 30)
+    Qr = _cpu_randn((lq, 2, 32), 31)
+    ids, sc, ds = route(Qr.to(DEV), [lq], Krb, coff, 5)
+    o = O.route_doc_scores(f64(Qr), [0, lq], f64(Krb), coff)[0]
+    assert_scores_close(ds[0], o, "f32", "fp32 scores")
+    assert_topk_valid(ids[0], o, 5, "fp32 topk")
+
+
+@pytest.mark.parametrize("path", ["auto", "dot", "mfma"])
+def test_route_batched(path):
+    say(f"case route batched path={path}")
+    _route_env(path)
+    counts = _chunk_counts(257, 8)
+    coff, Krb = random_bank(counts, 8, 128, "bf16", 40)
+    q_lens = [1, 7, 16, 33, 64, 130]
+    Qr = _cpu_randn((sum(q_lens), 8, 128), 41).to(torch.bfloat16)
+    ids, sc, ds = route(Qr.to(DEV), q_lens, Krb, coff, 16)
+    q_off = np.concatenate([[0], np.cumsum(q_lens)])
+    o = O.route_doc_scores(f64(Qr), q_off, f64(Krb), coff)
+    for b in range(len(q_lens)):
+        assert_scores_close(ds[b], o[b], "bf16", f"query {b}")
+        assert_topk_consistent(ids[b], sc[b], ds[b], 16, f"query {b}")
+        assert_topk_valid(ids[b], o[b], 16, f"query {b}")
+
+
+def test_route_paths_agree_and_deterministic():
+    say("case route dot vs mfma, repeatability")
+    counts = _chunk_counts(500, 9)
+    coff, Krb = random_bank(counts, 8, 128, "bf16", 50)
+    Qr = _cpu_randn((48, 8, 128), 51).to(torch.bfloat16).to(DEV)
+    _route_env("mfma")
+    a = route(Qr, [48], Krb, coff, 16)
+    b = route(Qr, [48], Krb, coff, 16)
+    _route_env("dot")
+    c = route(Qr, [48], Krb, coff, 16)
+    assert np.array_equal(a[2], b[2]) and np.array_equal(a[0], b[0])   # same bits twice
+    assert np.max(np.abs(a[2] - c[2])) < 1e-5
+
+
+def test_topk_ties_and_small_banks():
+    say("case top-k ties, k > N, single document")
+    # documents 3 and 7 duplicate documents 1 and 2: equal scores, lower id first
+    counts = np.array([2, 3, 1, 3, 4, 2, 5, 1])
+    coff, Krb = random_bank(counts, 8, 128, "bf16", 60)
+    Krb[coff[3]:coff[4]] = Krb[coff[1]:coff[2]]
+    Krb[coff[7]:coff[8]] = Krb[coff[2]:coff[3]]
+    Qr = _cpu_randn((20, 8, 128), 61).to(torch.bfloat16)
+    ids, sc, ds = route(Qr.to(DEV), [20], Krb, coff, 12)
+    assert ds[0][1] == ds[0][3] and ds[0][2] == ds[0][7]
+    order = list(ids[0][:8])
+    assert order.index(1) < order.index(3) and order.index(2) < order.index(7)
+    assert list(ids[0][8:]) == [-1] * 4 and np.all(np.isneginf(sc[0][8:]))
+    o = O.route_doc_scores(f64(Qr), [0, 20], f64(Krb), coff)[0]
+    assert_topk_valid(ids[0], o, 12, "ties")
+    coff1, Krb1 = random_bank([3], 8, 128, "bf16", 62)
+    ids1, sc1, _ = route(Qr.to(DEV), [20], Krb1, coff1, 4)
+    assert list(ids1[0]) == [0, -1, -1, -1]
+
+
+def test_route_zero_vectors():
+    say("case route zero-norm rows")
+    counts = np.array([2, 2, 2])
+    coff, Krb = random_bank(counts, 8, 128, "bf16", 70)
+    Krb[1, 3] = 0
+    Qr = _cpu_randn((16, 8, 128), 71).to(torch.bfloat16)
+    Qr[5, 2] = 0
+    ids, sc, ds = route(Qr.to(DEV), [16], Krb, coff, 3)
+    o = O.route_doc_scores(f64(Qr), [0, 16], f64(Krb), coff)[0]
+    assert np.all(np.isfinite(ds[0]))
+    assert_scores_close(ds[0], o, "bf16", "zero rows")
+
+
+# ------------------------------------------------------------------------------ attention
+
+ATTN_CASES = [
+    # (name, dtype, hq, hkv, d, q_lens, extra_kv, k)
+    ("prefill64", "bf16", 32, 8, 128, [64], 0, 16),
+    ("decode", "bf16", 32, 8, 128, [1], 40, 16),
+    ("batch_ragged", "bf16", 32, 8, 128, [1, 16, 37, 64, 130], 3, 8),
+    ("gqa2_d64", "bf16", 8, 4, 64, [20, 5], 7, 4),
+    ("d32", "bf16", 4, 2, 32, [9], 0, 3),
+    ("fp32_tiny", "f32", 4, 2, 32, [8, 3], 2, 2),
+    ("fp32_d128", "f32", 8, 2, 128, [5], 1, 3),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention(case):
+    name, dtype, hq, hkv, d, q_lens, extra, k = case
+    say(f"case attention {name}")
+    counts = _chunk_counts(60, 12, small_frac=0.2, hi=30)
+    coff, Kb = random_bank(counts, hkv, d, dtype, 80, doc_std=1.0)
+    _, Vb = random_bank(counts, hkv, d, dtype, 82, doc_std=1.0)
+    rng = np.random.default_rng(83)
+    B = len(q_lens)
+    ids = np.full((B, k), -1, dtype=np.int32)
+    for b in range(B):
+        keff = k if b % 2 == 0 else max(1, k - 2)      # some queries with unused slots
+        ids[b, :keff] = rng.choice(len(counts), size=keff, replace=False)
+    kv_lens = [q + extra for q in q_lens]
+    Q = _cpu_randn((sum(q_lens), hq, d), 84).to(_dt(dtype))
+    Kl = _cpu_randn((sum(kv_lens), hkv, d), 85).to(_dt(dtype))
+    Vl = _cpu_randn((sum(kv_lens), hkv, d), 86).to(_dt(dtype))
+    q_off = np.concatenate([[0], np.cumsum(q_lens)])
+    kv_off = np.concatenate([[0], np.cumsum(kv_lens)])
+    args = (Q.to(DEV), Kl.to(DEV), Vl.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV),
+            torch.tensor(kv_off, dtype=torch.int32, device=DEV), max(q_lens),
+            torch.tensor(ids, device=DEV), torch.tensor(coff, device=DEV))
+    out = M.msa_sparse_attn(*args, Kb, Vb, rope_base=1e6)
+    torch.cuda.synchronize()
+    ref = O.sparse_attn(f64(Q), f64(Kl), f64(Vl), q_off, kv_off, ids, coff, f64(Kb), f64(Vb), 1e6)
+    err = assert_attn_close(out, ref, dtype, name)
+    say(f"  max abs err {err:.3g}")
+    if dtype == "bf16":
+        # the same bank read from pinned host memory gives the same bits
+        out_h = M.msa_sparse_attn(*args, Kb.cpu().pin_memory(), Vb.cpu().pin_memory(), rope_base=1e6)
+        out_2 = M.msa_sparse_attn(*args, Kb, Vb, rope_base=1e6)
+        torch.cuda.synchronize()
+        assert torch.equal(out_h, out) and torch.equal(out_2, out)
+
+
+def test_attention_scale_argument():
+    say("case attention explicit scale")
+    coff, Kb = random_bank([3, 2], 2, 64, "bf16", 90)
+    _, Vb = random_bank([3, 2], 2, 64, "bf16", 91)
+    Q = _cpu_randn((4, 4, 64), 92).to(torch.bfloat16)
+    Kl = _cpu_randn((4, 2, 64), 93).to(torch.bfloat16)
+    Vl = _cpu_randn((4, 2, 64), 94).to(torch.bfloat16)
+    ids = np.array([[1, 0]], dtype=np.int32)
+    out = M.msa_sparse_attn(Q.to(DEV), Kl.to(DEV), Vl.to(DEV), torch.tensor([0, 4], dtype=torch.int32, device=DEV),
+                            torch.tensor([0, 4], dtype=torch.int32, device=DEV), 4, torch.tensor(ids, device=DEV),
+                            torch.tensor(coff, device=DEV), Kb, Vb, rope_base=1e4, scale=0.05)
+    torch.cuda.synchronize()
+    ref = O.sparse_attn(f64(Q), f64(Kl), f64(Vl), [0, 4], [0, 4], ids, coff, f64(Kb), f64(Vb), 1e4, scale=0.05)
+    assert_attn_close(out, ref, "bf16", "scale 0.05")
