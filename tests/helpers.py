@@ -36,11 +36,21 @@ def _ordered(bits: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -mag, mag)
 
 
-def assert_pool_close(gpu: torch.Tensor, oracle64: np.ndarray, dtype: str, what: str):
+POOL_ACC_ABS = 2.0 ** -20                        # float32 accumulation bound, x input RMS
+
+
+def assert_pool_close(gpu: torch.Tensor, oracle64: np.ndarray, dtype: str, what: str,
+                      input_rms: float = 1.0):
+    """bf16: within 1 ulp of the exact mean, or -- for means that cancel to near zero,
+    where a bf16 ulp is far below float32 summation error -- within 2^-20 x the RMS of
+    the pooled inputs in absolute terms.  float32: relative 1e-6 of max(|o|, rms)."""
     if dtype == "bf16":
         ref = O.f64_to_bf16_bits(oracle64)
         d = np.abs(_ordered(bf16_bits(gpu)) - _ordered(ref))
-        assert d.max(initial=0) <= 1, f"{what}: {int(d.max())} bf16 ulps apart (allowed 1)"
+        absdiff = np.abs(f64(gpu) - oracle64)
+        bad = (d > 1) & (absdiff > POOL_ACC_ABS * input_rms)
+        assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond 1 bf16 ulp and the "
+                               f"accumulation bound (max {int(d.max())} ulp, {absdiff[bad].max():.3g} abs)")
     else:
         g = f64(gpu)
         scale = max(float(np.sqrt(np.mean(oracle64 ** 2))), 1e-30)
