@@ -1,0 +1,313 @@
+"""Benchmark of the MSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bank100m_host]
+
+One step is one query through the router and the sparse attention: the routing scan of
+every bank row (msa_route_scan), top-k document selection (msa_topk), and sparse attention
+over the selected documents' pooled K/V plus the query's local K/V (msa_sparse_attn).
+On the 100M-token bank the routing keys (3.25 GB) are in HBM and the content K/V are in
+pinned host memory, read over the host link when selected.  Inputs are resident before
+the timed region starts.  The pooling step (offline memory encoding) cannot run on the
+100M-token bank itself (its token states would take 614 GB), so it is measured on the
+10M-token encode workload and reported next to the step figures.
+
+Prints one JSON line.  The CPU baseline runs the NumPy oracle on a bounded sample of the
+same bank on the host (one thread) and scales it to the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from dataclasses import replace
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import latent_memory_long_amd as M  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "routed bank tokens/s & % HBM peak; p50 route+attend latency, 100M-token bank"
+SCAN_KERNEL = "route_scan_mfma"
+
+# HBM traffic of the scan kernel per launch, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# on this workload (scaled by the counters' reading of a copy kernel of known size).  It is
+# reported only while the kernel source still has the digest it was measured with.
+TRAFFIC = None  # {"route_sha": "...", "fetch_bytes": ..., "write_bytes": ...}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def pct(a, q):
+    return float(np.percentile(np.asarray(a), q))
+
+
+def source_sha(name):
+    with open(os.path.join(ROOT, "latent_memory_long_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def make_bank(wl, dev):
+    lens = W.doc_lengths(wl)
+    off = W.token_offsets(lens)
+    coff = M.msa_chunk_offsets(off, wl.shape.chunk)
+    kv_dev = "cpu-pinned" if wl.kv_source == "host" else dev
+    log(f"bank: {len(lens)} documents, {int(coff[-1])} rows, content K/V on {kv_dev}")
+    Krb, Kb, Vb = W.gen_pooled_bank(wl, coff, dev, kv_device=kv_dev)
+    return lens, off, coff, Krb, Kb, Vb
+
+
+def make_queries(wl, dev, n):
+    qs = []
+    for i in range(n):
+        q = W.gen_queries(replace(wl, seed=wl.seed + 1 + i), dev)
+        qs.append(q)
+    return qs
+
+
+def time_pool(dev, reps=3):
+    """Pool a 10M-token bank (the batched encode workload) and time msa_pool."""
+    wl = W.workload("batch32_bank10m")
+    sh = wl.shape
+    lens = W.doc_lengths(wl)
+    off = W.token_offsets(lens)
+    coff = M.msa_chunk_offsets(off, sh.chunk)
+    C = int(coff[-1])
+    K, V, Kr = W.gen_token_states(wl, lens, dev)
+    off_d = torch.tensor(off, device=dev)
+    coff_d = torch.tensor(coff, device=dev)
+    outs = (torch.empty((C, sh.h_kv, sh.d), dtype=torch.bfloat16, device=dev),
+            torch.empty((C, sh.h_kv, sh.d), dtype=torch.bfloat16, device=dev),
+            torch.empty((C, sh.h_r, sh.d), dtype=torch.bfloat16, device=dev))
+    M.msa_pool(K, V, Kr, off_d, coff_d, C, sh.chunk, sh.rope_base, out=outs)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        M.msa_pool(K, V, Kr, off_d, coff_d, C, sh.chunk, sh.rope_base, out=outs)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    T = int(off[-1])
+    row = (2 * sh.h_kv + sh.h_r) * sh.d * 2
+    nbytes = T * row + C * row
+    t = float(np.median(ms)) / 1e3
+    del K, V, Kr, outs
+    torch.cuda.empty_cache()
+    return {"workload": "batch32_bank10m (encode stage)", "tokens": T, "bank_rows": C,
+            "ms": round(t * 1e3, 3), "tokens_per_s": T / t, "algorithmic_bytes": nbytes,
+            "gbps": nbytes / t / 1e9, "frac_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+
+
+def cpu_baseline(wl, lens, off, coff, Krb, Kb, Vb, q, target_s):
+    """The oracle, as it stands, on a bounded sample: the first documents of the bank."""
+    from threadpoolctl import threadpool_limits
+    from oracle import msa_oracle as O
+
+    Lq = int(q["q_len"][0])
+    Lkv = int(q["kv_len"][0])
+    Qr = q["Qr"][:Lq].float().cpu().double().numpy()
+    Q = q["Q"][:Lq].float().cpu().double().numpy()
+    Kl = q["Kloc"][:Lkv].float().cpu().double().numpy()
+    Vl = q["Vloc"][:Lkv].float().cpu().double().numpy()
+
+    def run(n_docs):
+        rows = int(coff[n_docs])
+        kb = Krb[:rows].float().cpu().double().numpy()
+        sub = coff[: n_docs + 1]
+        t0 = time.perf_counter()
+        ids, _, _ = O.route(Qr, [0, Lq], kb, sub, wl.k, block=16384)
+        t1 = time.perf_counter()
+        idx = np.concatenate([np.arange(sub[d], sub[d + 1]) for d in ids[0] if d >= 0])
+        Kb_s = Kb[torch.as_tensor(idx)].float().double().numpy()
+        Vb_s = Vb[torch.as_tensor(idx)].float().double().numpy()
+        # the selected documents' rows, gathered in rank order, form a compact bank
+        ids_c = np.arange(int((ids[0] >= 0).sum()), dtype=np.int32)[None]
+        lens_c = [int(sub[d + 1] - sub[d]) for d in ids[0] if d >= 0]
+        coff_c = np.concatenate([[0], np.cumsum(lens_c)])
+        t2 = time.perf_counter()
+        O.sparse_attn(Q, Kl, Vl, [0, Lq], [0, Lkv], ids_c, coff_c, Kb_s, Vb_s, wl.shape.rope_base)
+        t3 = time.perf_counter()
+        return (t1 - t0) + (t3 - t2), rows
+
+    with threadpool_limits(limits=1):
+        n0 = int(np.searchsorted(coff, 4096))
+        t_small, _ = run(max(n0, 1))
+        rows_target = int(4096 * target_s / max(t_small, 1e-3))
+        n_docs = int(min(len(lens), max(1, np.searchsorted(coff, rows_target))))
+        t, rows = run(n_docs)
+    tokens = int(off[n_docs])
+    return {"value": tokens / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"first {n_docs} of {len(lens)} documents ({rows} bank rows, {tokens} tokens) "
+                       f"of the 100M-token bank: oracle route (scan + top-k) and attention for one "
+                       f"{Lq}-token query, float64 NumPy on one host thread, {t:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bank100m_host")
+    ap.add_argument("--queries", type=int, default=8, help="distinct queries cycled by the steps")
+    ap.add_argument("--decode-steps", type=int, default=32)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pool", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sharded "
+              "multi-GPU path is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = W.workload(args.workload)
+    sh = wl.shape
+    lens, off, coff, Krb, Kb, Vb = make_bank(wl, dev)
+    N, C = len(lens), int(coff[-1])
+    T = int(off[-1])
+    coff_d = torch.tensor(coff, device=dev)
+    qs = make_queries(wl, dev, args.queries)
+    Lq = int(qs[0]["q_len"][0])
+    k = wl.k
+
+    # buffers, allocated once
+    q_off = torch.tensor([0, Lq], dtype=torch.int32, device=dev)
+    kv_off = torch.tensor([0, Lq], dtype=torch.int32, device=dev)
+    ds = torch.empty((1, N), dtype=torch.float32, device=dev)
+    ids = torch.empty((1, k), dtype=torch.int32, device=dev)
+    sc = torch.empty((1, k), dtype=torch.float32, device=dev)
+    out = torch.empty((Lq, sh.hq, sh.d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(M.msa_sparse_attn_workspace(M.MSA_BF16, 1, 200, 200, 200, sh.hq, sh.h_kv, sh.d), 256),
+                     dtype=torch.uint8, device=dev)
+    pre = [(q["Qr"][:Lq].contiguous(), q["Q"][:Lq].contiguous(), q["Kloc"][:Lq].contiguous(),
+            q["Vloc"][:Lq].contiguous()) for q in qs]
+
+    def step(i, ev):
+        Qr, Q, Kl, Vl = pre[i % len(pre)]
+        ev[0].record()
+        M.msa_route_scan(Qr, q_off, Lq, Krb, coff_d, out=ds)
+        ev[1].record()
+        M.msa_topk(ds, k, out=(ids, sc))
+        ev[2].record()
+        M.msa_sparse_attn(Q, Kl, Vl, q_off, kv_off, Lq, ids, coff_d, Kb, Vb, rope_base=sh.rope_base,
+                          out=out, workspace=ws)
+        ev[3].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for i in range(args.warmup):
+        step(i, wev)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    scan_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    topk_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    attn_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    ms_per_step = wall / args.steps * 1e3
+
+    # roofline of the scan kernel: algorithmic bytes per launch / its average duration
+    scan_bytes = C * sh.h_r * sh.d * 2 + Lq * sh.h_r * sh.d * 2 + (N + 1) * 8 + N * 4
+    scan_s = float(np.mean(scan_ms)) / 1e3
+    achieved = scan_bytes / scan_s / 1e9
+    traffic = None
+    if TRAFFIC and TRAFFIC.get("route_sha") == source_sha("route.hip"):
+        traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+
+    # decode: single-token steps after the prefill, routed again each step or reusing ids
+    dec = {}
+    if wl.decode_steps and args.decode_steps:
+        q = qs[0]
+        steps = min(args.decode_steps, wl.decode_steps)
+        M.msa_route_topk(pre[0][0], q_off, Lq, Krb, coff_d, k, out=(ids, sc, ds))
+        fixed_ids = ids.clone()
+        one = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+        routed, fixed = [], []
+        for s in range(steps):
+            r = Lq + s
+            kvo = torch.tensor([0, r + 1], dtype=torch.int32, device=dev)
+            Qr1, Q1 = q["Qr"][r:r + 1], q["Q"][r:r + 1]
+            Kl, Vl = q["Kloc"][:r + 1], q["Vloc"][:r + 1]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            M.msa_route_scan(Qr1, one, 1, Krb, coff_d, out=ds)
+            M.msa_topk(ds, k, out=(ids, sc))
+            M.msa_sparse_attn(Q1, Kl, Vl, one, kvo, 1, ids, coff_d, Kb, Vb, rope_base=sh.rope_base,
+                              out=out[:1], workspace=ws)
+            e[1].record()
+            M.msa_sparse_attn(Q1, Kl, Vl, one, kvo, 1, fixed_ids, coff_d, Kb, Vb,
+                              rope_base=sh.rope_base, out=out[:1], workspace=ws)
+            e[2].record()
+            torch.cuda.synchronize()
+            if s >= 2:
+                routed.append(e[0].elapsed_time(e[1]))
+                fixed.append(e[1].elapsed_time(e[2]))
+        dec = {"steps": steps, "routed_p50_ms": round(pct(routed, 50), 4),
+               "routed_p90_ms": round(pct(routed, 90), 4), "fixed_ids_p50_ms": round(pct(fixed, 50), 4),
+               "routed_bank_tokens_per_s": T / (pct(routed, 50) / 1e3)}
+
+    pool = None
+    if not args.no_pool:
+        del qs
+        torch.cuda.empty_cache()
+        log("pool on the 10M-token encode workload")
+        pool = time_pool(dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        q0 = W.gen_queries(replace(wl, seed=wl.seed + 1), dev)
+        cpu = cpu_baseline(wl, lens, off, coff, Krb, Kb, Vb, q0, args.cpu_seconds)
+
+    value = T / (ms_per_step / 1e3)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "bank_tokens": T, "documents": N, "bank_rows": C,
+                   "query_tokens": Lq, "k": k, "heads_q_kv_r": [sh.hq, sh.h_kv, sh.h_r],
+                   "head_dim": sh.d, "content_kv": "pinned host" if wl.kv_source == "host" else "hbm",
+                   "distinct_queries": len(pre)},
+        "latency_ms": {"route_attend_p50": round(pct(step_ms, 50), 4),
+                       "route_attend_p90": round(pct(step_ms, 90), 4),
+                       "scan_p50": round(pct(scan_ms, 50), 4), "topk_p50": round(pct(topk_ms, 50), 4),
+                       "attend_p50": round(pct(attn_ms, 50), 4)},
+        "roofline": {"kernel": SCAN_KERNEL, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
+                     "avg_launch_ms": scan_s * 1e3},
+        "scan_routed_bank_tokens_per_s": T / scan_s,
+        "decode": dec or None,
+        "pool": pool,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

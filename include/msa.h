@@ -103,7 +103,31 @@ msa_status msa_pool(msa_dtype dtype, int32_t n_docs, int64_t n_tokens, int64_t n
                     uint32_t rope_mask, const void* K, const void* V, const void* Kr,
                     void* Kbar, void* Vbar, void* Krbar, msa_stream_t stream);
 
-/* Bytes of workspace msa_route_topk needs (256-byte aligned pointer expected). */
+/*
+ * msa_route_scan -- step B alone: every document's router score.
+ *   Same inputs and score definition as msa_route_topk below;
+ *   doc_scores device float [n_queries, n_docs] output (written in full).
+ *   A query with no tokens scores -inf for every document.
+ */
+msa_status msa_route_scan(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                          const int32_t* q_off, int32_t max_q_len, const void* Qr,
+                          int32_t h_r, int32_t d, int32_t n_docs, int64_t n_chunks,
+                          const int64_t* chunk_off, const void* Krbar, float* doc_scores,
+                          msa_stream_t stream);
+
+/*
+ * msa_topk -- step C alone (github-wiki.com project 250, section 6 item 1: top-k document
+ * selection; yeyulingfeng.com section 五 step 2).
+ *   doc_scores device float [n_queries, n_docs]; finite or -inf (NaN is undefined).
+ *   topk_ids   device int32 [n_queries, k]: the min(k, n_docs) best documents by (score
+ *              descending, id ascending; -0.0 equals +0.0); remaining slots -1.
+ *   topk_scores device float [n_queries, k]: their scores; -inf in unused slots.
+ *   Supported: 1 <= k <= 1024.
+ */
+msa_status msa_topk(int32_t n_queries, int32_t n_docs, const float* doc_scores, int32_t k,
+                    int32_t* topk_ids, float* topk_scores, msa_stream_t stream);
+
+/* Bytes of workspace msa_route_topk needs when doc_scores is NULL (256-byte aligned). */
 size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
 
 /*
@@ -121,7 +145,8 @@ size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
  *   topk_ids   device int32 [n_queries, k]: the min(k, n_docs) best documents by (score
  *              descending, id ascending); remaining slots -1.
  *   topk_scores device float [n_queries, k]: their scores; -inf in unused slots.
- *   doc_scores device float [n_queries, n_docs] or NULL: every document's score.
+ *   doc_scores device float [n_queries, n_docs] or NULL: every document's score; when
+ *              NULL the scores are kept in `workspace` instead (which may be NULL otherwise).
  *   Supported: d in {32, 64, 128}; h_r in [1, 16]; 1 <= k <= 1024.  Scores and norms
  *   accumulate in float32; bf16 inputs with max_q_len >= 16 use MFMA tiles.
  */

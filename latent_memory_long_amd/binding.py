@@ -32,7 +32,7 @@ class MsaError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
-                          "python -m latent_memory_long_amd.build")
+                          "python latent_memory_long_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F, SZ, U32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                               ctypes.c_size_t, ctypes.c_uint32)
@@ -43,6 +43,9 @@ def _load() -> ctypes.CDLL:
         "msa_chunk_offsets": (I64, [P, I32, I32, P]),
         "msa_pool": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, I32, I32, I32, F, U32,
                                     P, P, P, P, P, P, P]),
+        "msa_route_scan": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
+                                          P, P, P]),
+        "msa_topk": (ctypes.c_int, [I32, I32, P, I32, P, P, P]),
         "msa_route_topk_workspace": (SZ, [I32, I32, I32]),
         "msa_route_topk": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
                                           P, I32, P, P, P, P, SZ, P]),
@@ -136,6 +139,30 @@ def msa_pool(K: torch.Tensor, V: torch.Tensor, Kr: torch.Tensor, doc_tok_off: to
     return Kb, Vb, Krb
 
 
+def msa_route_scan(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar: torch.Tensor,
+                   chunk_off: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """Step B.  Returns every document's score, float32 [B, N]."""
+    B = q_off.numel() - 1
+    N = chunk_off.numel() - 1
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float32, device=Krbar.device)
+    _check(lib.msa_route_scan(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
+                              Krbar.shape[1], Krbar.shape[2], N, Krbar.shape[0], _ptr(chunk_off),
+                              _ptr(Krbar), _ptr(out), _stream(stream)))
+    return out
+
+
+def msa_topk(doc_scores: torch.Tensor, k: int, out=None, stream=None):
+    """Step C.  doc_scores float32 [B, N] -> (ids int32 [B, k], scores float32 [B, k])."""
+    B, N = doc_scores.shape
+    if out is None:
+        out = (torch.empty((B, k), dtype=torch.int32, device=doc_scores.device),
+               torch.empty((B, k), dtype=torch.float32, device=doc_scores.device))
+    ids, sc = out
+    _check(lib.msa_topk(B, N, _ptr(doc_scores), k, _ptr(ids), _ptr(sc), _stream(stream)))
+    return ids, sc
+
+
 def msa_route_topk_workspace(n_queries: int, n_docs: int, k: int) -> int:
     return int(lib.msa_route_topk_workspace(n_queries, n_docs, k))
 
@@ -153,12 +180,14 @@ def msa_route_topk(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar:
                torch.empty((B, k), dtype=torch.float32, device=dev),
                torch.empty((B, N), dtype=torch.float32, device=dev) if want_doc_scores else None)
     ids, sc, ds = out
-    need = msa_route_topk_workspace(B, N, k)
-    ws = _workspace(need, dev, workspace)
+    ws, wsb = None, 0
+    if ds is None:
+        ws = _workspace(msa_route_topk_workspace(B, N, k), dev, workspace)
+        wsb = ws.numel() * ws.element_size()
     _check(lib.msa_route_topk(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
                               Krbar.shape[1], Krbar.shape[2], N, Krbar.shape[0], _ptr(chunk_off),
-                              _ptr(Krbar), k, _ptr(ids), _ptr(sc), _ptr(ds), _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream(stream)))
+                              _ptr(Krbar), k, _ptr(ids), _ptr(sc), _ptr(ds), _ptr(ws), wsb,
+                              _stream(stream)))
     return ids, sc, ds
 
 

@@ -1,6 +1,6 @@
 """Build libmsa.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m latent_memory_long_amd.build [-v]
+    python latent_memory_long_amd/build.py [-v]
 
 Each csrc/*.hip is compiled to an object in parallel, then linked into
 latent_memory_long_amd/libmsa.so.  Device code is built for gfx950 only.

@@ -102,16 +102,14 @@ msa_status msa_pool(msa_dtype dtype, int32_t n_docs, int64_t n_tokens, int64_t n
 size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k) {
   (void)k;
   if (n_queries < 1 || n_docs < 1) return 0;
-  return msa::align256((size_t)n_queries * (size_t)n_docs * sizeof(uint32_t));
+  return msa::align256((size_t)n_queries * (size_t)n_docs * sizeof(float));
 }
 
-msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
-                          const int32_t* q_off, int32_t max_q_len, const void* Qr, int32_t h_r,
-                          int32_t d, int32_t n_docs, int64_t n_chunks, const int64_t* chunk_off,
-                          const void* Krbar, int32_t k, int32_t* topk_ids, float* topk_scores,
-                          float* doc_scores, void* workspace, size_t workspace_bytes,
-                          msa_stream_t stream) {
-  g_last_error.clear();
+namespace {
+
+msa_status check_route(msa_dtype dtype, int32_t n_queries, int64_t total_q, const int32_t* q_off,
+                       int32_t max_q_len, const void* Qr, int32_t h_r, int32_t d, int32_t n_docs,
+                       int64_t n_chunks, const int64_t* chunk_off, const void* Krbar) {
   if (dtype != MSA_F32 && dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   if (n_queries < 1 || n_queries > 65535) return fail(MSA_ERR_INVALID_ARG, "n_queries %d not in [1, 65535]", n_queries);
   if (total_q < 0 || total_q > INT32_MAX) return fail(MSA_ERR_INVALID_ARG, "total_q %lld out of range", (long long)total_q);
@@ -122,18 +120,69 @@ msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
   if (n_docs < 1) return fail(MSA_ERR_INVALID_ARG, "n_docs must be >= 1 (got %d)", n_docs);
   if (n_chunks < n_docs) return fail(MSA_ERR_INVALID_ARG, "n_chunks (%lld) < n_docs (%d)", (long long)n_chunks, n_docs);
   if (!chunk_off || !Krbar) return fail(MSA_ERR_INVALID_ARG, "null bank pointer");
+  return MSA_OK;
+}
+
+msa_status check_topk(int32_t n_queries, int32_t n_docs, int32_t k, const int32_t* ids, const float* sc) {
+  if (n_queries < 1 || n_queries > 65535) return fail(MSA_ERR_INVALID_ARG, "n_queries %d not in [1, 65535]", n_queries);
+  if (n_docs < 1) return fail(MSA_ERR_INVALID_ARG, "n_docs must be >= 1 (got %d)", n_docs);
   if (k < 1) return fail(MSA_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
   if (k > 1024) return fail(MSA_ERR_UNSUPPORTED, "k %d > 1024", k);
-  if (!topk_ids || !topk_scores) return fail(MSA_ERR_INVALID_ARG, "null output pointer");
-  const size_t need = msa_route_topk_workspace(n_queries, n_docs, k);
-  if (!workspace || workspace_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-  if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (!ids || !sc) return fail(MSA_ERR_INVALID_ARG, "null output pointer");
+  return MSA_OK;
+}
+
+}  // namespace
+
+msa_status msa_route_scan(msa_dtype dtype, int32_t n_queries, int64_t total_q, const int32_t* q_off,
+                          int32_t max_q_len, const void* Qr, int32_t h_r, int32_t d, int32_t n_docs,
+                          int64_t n_chunks, const int64_t* chunk_off, const void* Krbar,
+                          float* doc_scores, msa_stream_t stream) {
+  g_last_error.clear();
+  msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
+                              n_chunks, chunk_off, Krbar);
+  if (st != MSA_OK) return st;
+  if (!doc_scores) return fail(MSA_ERR_INVALID_ARG, "null doc_scores");
+  msa::RouteArgs r{(int)dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
+                   chunk_off, Krbar, doc_scores, route_path_override()};
+  return hip_status(msa::launch_route_scan(r, (hipStream_t)stream), "msa_route_scan launch");
+}
+
+msa_status msa_topk(int32_t n_queries, int32_t n_docs, const float* doc_scores, int32_t k,
+                    int32_t* topk_ids, float* topk_scores, msa_stream_t stream) {
+  g_last_error.clear();
+  msa_status st = check_topk(n_queries, n_docs, k, topk_ids, topk_scores);
+  if (st != MSA_OK) return st;
+  if (!doc_scores) return fail(MSA_ERR_INVALID_ARG, "null doc_scores");
+  msa::TopkArgs t{n_queries, n_docs, k, doc_scores, topk_ids, topk_scores};
+  return hip_status(msa::launch_topk(t, (hipStream_t)stream), "msa_topk launch");
+}
+
+msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                          const int32_t* q_off, int32_t max_q_len, const void* Qr, int32_t h_r,
+                          int32_t d, int32_t n_docs, int64_t n_chunks, const int64_t* chunk_off,
+                          const void* Krbar, int32_t k, int32_t* topk_ids, float* topk_scores,
+                          float* doc_scores, void* workspace, size_t workspace_bytes,
+                          msa_stream_t stream) {
+  g_last_error.clear();
+  msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
+                              n_chunks, chunk_off, Krbar);
+  if (st != MSA_OK) return st;
+  st = check_topk(n_queries, n_docs, k, topk_ids, topk_scores);
+  if (st != MSA_OK) return st;
+  float* scores = doc_scores;
+  if (!scores) {  // document scores go to the workspace
+    const size_t need = msa_route_topk_workspace(n_queries, n_docs, k);
+    if (!workspace || workspace_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    scores = (float*)workspace;
+  }
   hipStream_t s = (hipStream_t)stream;
   msa::RouteArgs r{(int)dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
-                   chunk_off, Krbar, (uint32_t*)workspace, route_path_override()};
-  msa_status st = hip_status(msa::launch_route_scan(r, s), "msa_route_topk scan launch");
+                   chunk_off, Krbar, scores, route_path_override()};
+  st = hip_status(msa::launch_route_scan(r, s), "msa_route_topk scan launch");
   if (st != MSA_OK) return st;
-  msa::TopkArgs t{n_queries, n_docs, k, (const uint32_t*)workspace, topk_ids, topk_scores, doc_scores};
+  msa::TopkArgs t{n_queries, n_docs, k, scores, topk_ids, topk_scores};
   return hip_status(msa::launch_topk(t, s), "msa_route_topk top-k launch");
 }
 

@@ -139,4 +139,16 @@ __device__ __forceinline__ int find_doc_wave(const int64_t* chunk_off, int n_doc
   return lo;
 }
 
+// Documents [d0, d1) of part p out of P: the part starts at the first document whose first
+// bank row is >= p * C / P, so every document belongs to exactly one part and parts hold
+// nearly equal numbers of rows.  Wave-collective (all lanes must call).
+__device__ __forceinline__ int part_first_doc(const int64_t* chunk_off, int n_docs,
+                                              int64_t n_chunks, int64_t p, int64_t P) {
+  if (p <= 0) return 0;
+  if (p >= P) return n_docs;
+  const int64_t x = n_chunks * p / P;
+  const int d = find_doc_wave(chunk_off, n_docs, x);
+  return (chunk_off[d] == x) ? d : d + 1;
+}
+
 }  // namespace msa

@@ -33,17 +33,16 @@ struct RouteArgs {
   int64_t n_chunks;
   const int64_t* chunk_off;
   const void* Krbar;
-  uint32_t* keys;  // [n_queries, n_docs] workspace
-  int force_path;  // 0 auto, 1 dot, 2 mfma (test hook, not in the C ABI)
+  float* scores;   // [n_queries, n_docs] output
+  int force_path;  // 0 auto, 1 dot, 2 mfma (MSA_ROUTE_PATH environment override)
 };
 hipError_t launch_route_scan(const RouteArgs& a, hipStream_t s);
 
 struct TopkArgs {
   int n_queries, n_docs, k;
-  const uint32_t* keys;
+  const float* doc_scores;  // [n_queries, n_docs]
   int32_t* ids;
   float* scores;
-  float* doc_scores;  // may be null
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 

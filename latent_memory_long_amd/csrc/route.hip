@@ -12,8 +12,9 @@
 //   rs = 1 / (H * |Qr[t,h]|), cs = 1 / |Kb[c,h]|   (0 when the norm is 0),
 //   S(c) = max_t s(t, c),  D(d) = max_{c in d} S(c).
 //
-// D(d) is accumulated with atomicMax on order-preserving uint32 keys: max is exact and
-// commutative, so the result does not depend on the order of the atomics.
+// Work is split into document-aligned parts (each part starts at a document boundary), so
+// every document's score is produced by exactly one wave with a plain store: no atomics,
+// no initialisation pass, and the result does not depend on scheduling.
 //
 // The scan reads each bank row once (H * d * 2 bytes per row in bf16) and does
 // 2 * Lq * H * d flops on it, so it is bound by HBM bandwidth unless Lq is in the
@@ -35,59 +36,67 @@
 namespace msa {
 namespace {
 
-__global__ void fill_u32(uint32_t* p, int64_t n, uint32_t v) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
-
 struct ScanK {
   const void* Qr;
   const int32_t* q_off;
   const void* Krb;
   const int64_t* chunk_off;
-  uint32_t* keys;
+  float* scores;  // [n_queries, n_docs]
   int64_t n_chunks;
   int n_docs;
   int H;
 };
 
+__device__ __forceinline__ int64_t load_window(const int64_t* chunk_off, int n_docs, int wb) {
+  const int di = wb + 1 + (int)(threadIdx.x & 63);
+  return (di <= n_docs) ? chunk_off[di] : INT64_MAX;
+}
+
 // ------------------------------------------------------------------------------------
-// Wave-0 helper of the MFMA scan: fold 16 consecutive row scores into document maxima.
-// `win` holds chunk_off[wb + 1 + lane] (INT64_MAX past the end), a window of document
-// ends that must cover the tile; it is rebased when the tile runs past it.
+// Wave-0 helper of the MFMA scan: fold 16 consecutive row scores (lane l < 16 holds row
+// c_first + l) into document maxima.  `win` holds chunk_off[wb + 1 + lane], a window of
+// document ends that must cover the tile; it is rebased when the tile runs past it.
+// `carry` is the running maximum of document `cur_doc`, which began in an earlier tile.
+// A document's score is stored once its last row has been seen; on a later pass over the
+// same rows (query rows beyond the first block) it is combined with the stored value.
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ void fold_tile_docs(const ScanK& a, uint32_t* keys, int64_t c_first,
-                                               int64_t c_end, float s, int& cur_doc, int& wb,
-                                               int64_t& win) {
+__device__ __forceinline__ void fold_tile_docs(const ScanK& a, float* scores, int64_t c_first,
+                                               int64_t c_end, float s, bool first_pass,
+                                               int& cur_doc, int& wb, int64_t& win,
+                                               float& carry) {
   const int lane = threadIdx.x & 63;
   const int64_t c_last = min(c_first + 15, c_end - 1);
-  if (!(c_last < __shfl(win, 63))) {  // rebase the window at the tile's first document
+  const int nvalid = (int)(c_last - c_first + 1);
+  if (!(c_last < __shfl(win, 63))) {
     wb = cur_doc;
-    const int di = wb + 1 + lane;
-    win = (di <= a.n_docs) ? a.chunk_off[di] : INT64_MAX;
+    win = load_window(a.chunk_off, a.n_docs, wb);
   }
   const int64_t c = c_first + lane;
-  const bool valid = (lane < 16) && (c < c_end);
-  // document of row c: wb + #{j : win[j] <= c}  (win strictly increasing)
-  int pos = 0;
+  const bool valid = lane < nvalid;
+  int pos = 0;  // #{j : win[j] <= c}, win strictly increasing
 #pragma unroll
   for (int step = 32; step >= 1; step >>= 1) {
     const int64_t v = __shfl(win, pos + step - 1);
     if (v <= c) pos += step;
   }
   const int doc = wb + pos;
-  // segmented inclusive max over lanes 0..15 (documents are contiguous runs)
+  const int64_t doc_end = __shfl(win, pos);  // chunk_off[doc + 1]
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
+  for (int off = 1; off < 16; off <<= 1) {  // segmented inclusive max
     const float os = __shfl_up(s, off);
     const int od = __shfl_up(doc, off);
     if (lane >= off && od == doc) s = fmaxf(s, os);
   }
-  const int nd = __shfl_down(doc, 1);
-  const bool last = valid && (lane == 15 || c + 1 >= c_end || nd != doc);
-  if (last) atomicMax(keys + doc, score_key(s));
-  cur_doc = __shfl(doc, (int)(c_last - c_first));
+  if (doc == cur_doc) s = fmaxf(s, carry);
+  if (valid && c + 1 == doc_end) {  // last row of its document
+    const float v = first_pass ? s : fmaxf(s, scores[doc]);
+    scores[doc] = v;
+  }
+  const int ld = __shfl(doc, nvalid - 1);
+  const float ls = __shfl(s, nvalid - 1);
+  const int64_t lend = __shfl(doc_end, nvalid - 1);
+  if (c_last + 1 == lend) { cur_doc = ld + 1; carry = -INFINITY; }
+  else { cur_doc = ld; carry = ls; }
 }
 
 template <int MT, int D>
@@ -104,24 +113,25 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
   const int b = blockIdx.y;
   const int q0 = a.q_off[b];
   const int Lq = a.q_off[b + 1] - q0;
-  const int64_t c_begin = a.n_chunks * (int64_t)blockIdx.x / gridDim.x;
-  const int64_t c_end = a.n_chunks * ((int64_t)blockIdx.x + 1) / gridDim.x;
-  if (Lq <= 0 || c_begin >= c_end) return;
-  uint32_t* keys = a.keys + (int64_t)b * a.n_docs;
+  const int d_begin = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, blockIdx.x, gridDim.x);
+  const int d_end = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, blockIdx.x + 1, gridDim.x);
+  if (d_begin >= d_end) return;
+  float* scores = a.scores + (int64_t)b * a.n_docs;
+  if (Lq <= 0) {  // a query without tokens scores -inf everywhere
+    for (int d = d_begin + threadIdx.x; d < d_end; d += blockDim.x) scores[d] = -INFINITY;
+    return;
+  }
+  const int64_t c_begin = a.chunk_off[d_begin];
+  const int64_t c_end = a.chunk_off[d_end];
   const bf16_t* Qr = (const bf16_t*)a.Qr;
   const bf16_t* Kb = (const bf16_t*)a.Krb;
-
-  int cur_doc = find_doc_wave(a.chunk_off, a.n_docs, c_begin);
-  int wb = cur_doc;
-  int64_t win;
-  {
-    const int di = wb + 1 + lane;
-    win = (di <= a.n_docs) ? a.chunk_off[di] : INT64_MAX;
-  }
   const int64_t ntiles = (c_end - c_begin + 15) / 16;
 
   for (int rb = 0; rb < Lq; rb += ROWS) {
     const int rows = min(ROWS, Lq - rb);
+    int cur_doc = d_begin, wb = d_begin;
+    int64_t win = load_window(a.chunk_off, a.n_docs, wb);
+    float carry = -INFINITY;
     // ---- A operands: this head's query rows, and their scales ----
     bf16x8_t A[MT][KK];
     float rs[MT][4];
@@ -213,30 +223,23 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
       }
       if (w == 0 && t > 0) {
         const float s = (lane < 16) ? sc[buf ^ 1][lane] : -INFINITY;
-        fold_tile_docs(a, keys, c_begin + (t - 1) * 16, c_end, s, cur_doc, wb, win);
+        fold_tile_docs(a, scores, c_begin + (t - 1) * 16, c_end, s, rb == 0, cur_doc, wb, win, carry);
       }
       buf ^= 1;
     }
     lds_barrier();
     if (w == 0) {
       const float s = (lane < 16) ? sc[buf ^ 1][lane] : -INFINITY;
-      fold_tile_docs(a, keys, c_begin + (ntiles - 1) * 16, c_end, s, cur_doc, wb, win);
+      fold_tile_docs(a, scores, c_begin + (ntiles - 1) * 16, c_end, s, rb == 0, cur_doc, wb, win, carry);
     }
     lds_barrier();
-    // the next row block restarts at the first row of the range
-    if (rb + ROWS < Lq) {
-      cur_doc = find_doc_wave(a.chunk_off, a.n_docs, c_begin);
-      wb = cur_doc;
-      const int di = wb + 1 + lane;
-      win = (di <= a.n_docs) ? a.chunk_off[di] : INT64_MAX;
-    }
   }
 }
 
 // ------------------------------------------------------------------------------------
-// Dot-product scan.  Each wave owns a contiguous range of rows and folds row scores into
-// documents itself.  Query rows are handled in blocks of up to QB tokens held in LDS as
-// float, pre-multiplied by rs[t,h].
+// Dot-product scan.  Each wave owns a document-aligned range of rows and folds row scores
+// into documents itself.  Query rows are handled in blocks of up to QB tokens held in LDS
+// as float, pre-multiplied by rs[t,h].
 // ------------------------------------------------------------------------------------
 constexpr int QB = 16;
 constexpr int DOT_WAVES = 4;
@@ -253,12 +256,17 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
   const int Lq = a.q_off[b + 1] - q0;
   const int64_t gw = (int64_t)blockIdx.x * DOT_WAVES + w;
   const int64_t nw = (int64_t)gridDim.x * DOT_WAVES;
-  const int64_t c_begin = a.n_chunks * gw / nw;
-  const int64_t c_end = a.n_chunks * (gw + 1) / nw;
-  uint32_t* keys = a.keys + (int64_t)b * a.n_docs;
+  const int d_begin = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, gw, nw);
+  const int d_end = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, gw + 1, nw);
+  float* scores = a.scores + (int64_t)b * a.n_docs;
   const T* Qr = (const T*)a.Qr;
   const T* Kb = (const T*)a.Krb;
-  if (Lq <= 0) return;  // uniform over the workgroup
+  if (Lq <= 0) {  // uniform over the workgroup
+    for (int d = d_begin + lane; d < d_end; d += 64) scores[d] = -INFINITY;
+    return;
+  }
+  const int64_t c_begin = (d_begin < d_end) ? a.chunk_off[d_begin] : 0;
+  const int64_t c_end = (d_begin < d_end) ? a.chunk_off[d_end] : 0;
 
   for (int tb = 0; tb < Lq; tb += QB) {
     const int nt = min(QB, Lq - tb);
@@ -285,16 +293,16 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
     }
     __syncthreads();
     if (c_begin >= c_end) continue;
+    const bool first_pass = tb == 0;
 
-    int cur = find_doc_wave(a.chunk_off, a.n_docs, c_begin);
+    int cur = d_begin;
     int wb = cur;
-    int64_t win;
-    {
-      const int di = wb + 1 + lane;
-      win = (di <= a.n_docs) ? a.chunk_off[di] : INT64_MAX;
-    }
+    int64_t win = load_window(a.chunk_off, a.n_docs, wb);
     int64_t nb = __shfl(win, 0);  // end row of document `cur`
     float run = -INFINITY;
+    auto emit = [&](int doc, float v) {
+      if (lane == 0) scores[doc] = first_pass ? v : fmaxf(v, scores[doc]);
+    };
 
     float xn[4][8];
     auto load_row = [&](int64_t c, float (*x)[8]) {
@@ -346,31 +354,34 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
       }
       // fold into documents (wave-uniform control flow)
       while (c >= nb) {
-        if (lane == 0) atomicMax(keys + cur, score_key(run));
+        emit(cur, run);
         run = -INFINITY;
         ++cur;
         if (cur - wb >= 63) {
           wb = cur;
-          const int di = wb + 1 + lane;
-          win = (di <= a.n_docs) ? a.chunk_off[di] : INT64_MAX;
+          win = load_window(a.chunk_off, a.n_docs, wb);
         }
         nb = __shfl(win, cur - wb);
       }
       run = fmaxf(run, best);
     }
-    if (lane == 0) atomicMax(keys + cur, score_key(run));
+    emit(cur, run);  // the range ends at a document end
   }
+}
+
+int route_parts(int64_t n_chunks, int64_t rows_per_part) {
+  int64_t p = 2048;
+  const int64_t mx = (n_chunks + rows_per_part - 1) / rows_per_part;
+  if (p > mx) p = mx;
+  if (p < 1) p = 1;
+  return (int)p;
 }
 
 template <int D>
 hipError_t launch_mfma(const RouteArgs& r, const ScanK& k, hipStream_t s) {
   const int mt = min(4, (r.max_q_len + 15) / 16);
-  // 2 workgroups per CU on 256 CUs, several times over; every workgroup gets >= 4 tiles.
-  int64_t wgs = 2048;
-  const int64_t max_wgs = (r.n_chunks + 63) / 64;
-  if (wgs > max_wgs) wgs = max_wgs;
-  if (wgs < 1) wgs = 1;
-  dim3 grid((unsigned)wgs, (unsigned)r.n_queries);
+  // 2 workgroups per CU on 256 CUs, several times over; >= 4 tiles per workgroup.
+  dim3 grid((unsigned)route_parts(r.n_chunks, 64), (unsigned)r.n_queries);
   dim3 block(64 * r.h_r);
   switch (mt) {
     case 1: hipLaunchKernelGGL((route_scan_mfma<1, D>), grid, block, 0, s, k); break;
@@ -383,12 +394,8 @@ hipError_t launch_mfma(const RouteArgs& r, const ScanK& k, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
-  int64_t wgs = 2048;
-  const int64_t max_wgs = (r.n_chunks + 4 * DOT_WAVES - 1) / (4 * DOT_WAVES);
-  if (wgs > max_wgs) wgs = max_wgs;
-  if (wgs < 1) wgs = 1;
   const size_t lds = (size_t)QB * r.h_r * D * sizeof(float);
-  dim3 grid((unsigned)wgs, (unsigned)r.n_queries);
+  dim3 grid((unsigned)route_parts(r.n_chunks, 4 * DOT_WAVES), (unsigned)r.n_queries);
   hipLaunchKernelGGL((route_scan_dot<T, D>), grid, dim3(64 * DOT_WAVES), lds, s, k);
   return hipGetLastError();
 }
@@ -396,17 +403,7 @@ hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_route_scan(const RouteArgs& r, hipStream_t s) {
-  const int64_t nkeys = (int64_t)r.n_queries * r.n_docs;
-  {
-    int64_t blocks = (nkeys + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, r.keys, nkeys, 0u);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (r.n_chunks == 0) return hipSuccess;
-  ScanK k{r.Qr, r.q_off, r.Krbar, r.chunk_off, r.keys, r.n_chunks, r.n_docs, r.h_r};
+  ScanK k{r.Qr, r.q_off, r.Krbar, r.chunk_off, r.scores, r.n_chunks, r.n_docs, r.h_r};
   bool mfma = (r.dtype == 1) && (r.max_q_len >= 16) && (r.h_r <= 8);
   if (r.force_path == 1) mfma = false;
   if (r.force_path == 2 && r.dtype == 1 && r.h_r <= 8) mfma = true;

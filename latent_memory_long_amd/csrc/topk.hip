@@ -5,15 +5,14 @@
 // top-k memory); hysenlabs.com "... Routing happens inside attention ...".
 // Order: score descending, ties to the lower document id; k_eff = min(k, N).
 //
-// One workgroup (1024 threads) per query, working on the order-preserving uint32 score
-// keys written by the scan:
+// One workgroup (1024 threads) per query, working on order-preserving uint32 keys of the
+// float document scores (the key order is the float order, with -0.0 folded into +0.0):
 //  1. Radix select, most significant digit first (11 + 11 + 10 bits): an LDS histogram of
 //     the keys that share the digits chosen so far finds, digit by digit, the exact key T
 //     of the k_eff-th largest score and how many of the winners must be taken among keys
 //     equal to T.
 //  2. One compaction pass in id order: keys > T are all taken; keys == T are taken in id
-//     order through a block-wide prefix count until the quota is filled.  The same pass
-//     writes the optional float score of every document.
+//     order through a block-wide prefix count until the quota is filled.
 //  3. The <= 1024 winners are sorted in LDS by (key descending, id ascending) with a
 //     bitonic network on 64-bit composites key << 32 | ~id.
 // The work per query is a few reads of 4 * N bytes that stay in L2; it is latency-bound.
@@ -63,7 +62,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   const int b = blockIdx.x;
   const int N = a.n_docs;
   const int keff = min(a.k, N);
-  const uint32_t* kb = a.keys + (int64_t)b * N;
+  const float* sb = a.doc_scores + (int64_t)b * N;
 
   uint32_t prefix = 0, pmask = 0;
   uint32_t remaining = (uint32_t)keff;
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     for (uint32_t i = tid; i < 2048; i += TK_THREADS) hist[i] = 0u;
     __syncthreads();
     for (int i = tid; i < N; i += TK_THREADS) {
-      const uint32_t key = kb[i];
+      const uint32_t key = score_key(sb[i]);
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
@@ -103,8 +102,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   uint32_t eq_base = 0;
   for (int base = 0; base < N; base += TK_THREADS) {
     const int i = base + tid;
-    const uint32_t key = (i < N) ? kb[i] : 0u;
-    if (i < N && a.doc_scores) a.doc_scores[(int64_t)b * N + i] = key_score(key);
+    const uint32_t key = (i < N) ? score_key(sb[i]) : 0u;
     const bool gt = (i < N) && key > T;
     const bool eq = (i < N) && key == T;
     if (gt) {

@@ -327,3 +327,48 @@ def test_attention_scale_argument():
     torch.cuda.synchronize()
     ref = O.sparse_attn(f64(Q), f64(Kl), f64(Vl), [0, 4], [0, 4], ids, coff, f64(Kb), f64(Vb), 1e4, scale=0.05)
     assert_attn_close(out, ref, "bf16", "scale 0.05")
+
+
+# ------------------------------------------------------------------------------ steps alone
+
+@pytest.mark.parametrize("n,k", [(1, 1), (5, 8), (1000, 16), (47_000, 16), (100_003, 32), (5000, 1024)])
+def test_topk_alone_exact(n, k):
+    say(f"case top-k alone n={n} k={k}")
+    rng = np.random.default_rng(n + k)
+    sc = np.round(rng.standard_normal((3, n)), 2).astype(np.float32)   # many ties
+    sc[0, : min(n, 7)] = 0.0
+    sc[0, min(n, 7): min(n, 14)] = -0.0                                  # -0.0 ties +0.0
+    sc[2] = -np.inf
+    sc[2, n // 2] = 1.0
+    ids, top = M.msa_topk(torch.tensor(sc, device=DEV), k)
+    torch.cuda.synchronize()
+    ids, top = ids.cpu().numpy(), top.cpu().numpy()
+    keff = min(k, n)
+    for b in range(3):
+        key = np.where(sc[b] == 0, 0.0, sc[b]).astype(np.float64)
+        order = np.lexsort((np.arange(n), -key))[:keff]
+        assert np.array_equal(ids[b, :keff], order), f"row {b}"
+        assert np.array_equal(top[b, :keff], np.where(sc[b][order] == 0, 0.0, sc[b][order]))
+        assert np.all(ids[b, keff:] == -1)
+
+
+def test_route_scan_alone_and_empty_query():
+    say("case route scan alone, empty query")
+    counts = _chunk_counts(120, 13)
+    coff, Krb = random_bank(counts, 8, 128, "bf16", 100)
+    q_lens = [20, 0, 5]
+    Qr = _cpu_randn((sum(q_lens), 8, 128), 101).to(torch.bfloat16)
+    q_off = np.concatenate([[0], np.cumsum(q_lens)])
+    for path in ("auto", "dot", "mfma"):
+        _route_env(path)
+        ds = M.msa_route_scan(Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), 20, Krb,
+                              torch.tensor(coff, device=DEV))
+        ids, sc = M.msa_topk(ds, 4)
+        torch.cuda.synchronize()
+        ds = ds.cpu().numpy()
+        assert np.all(np.isneginf(ds[1])), path
+        assert list(ids[1].cpu().numpy()) == [0, 1, 2, 3]
+        o = O.route_doc_scores(f64(Qr), q_off[[0, 1]], f64(Krb), coff)[0]
+        assert_scores_close(ds[0], o, "bf16", f"{path} q0")
+        o2 = O.route_doc_scores(f64(Qr), q_off[[2, 3]] , f64(Krb), coff)[0]
+        assert_scores_close(ds[2], o2, "bf16", f"{path} q2")
