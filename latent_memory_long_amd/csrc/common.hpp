@@ -112,6 +112,80 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// ---- DPP reductions (gfx9 data-parallel primitives, no LDS traffic) ----------------------
+// dpp_ctrl codes: row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_keep(float v) {  // lanes without a source keep v
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_zero(float v) {  // lanes without a source read 0
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+// Sum over groups of N consecutive lanes (N = 2..16 dividing 16): the group's last lane
+// receives the total.
+template <int N>
+__device__ __forceinline__ float group_sum_last(float v) {
+  if (N > 1) v += dpp_zero<0x111>(v);
+  if (N > 2) v += dpp_zero<0x112>(v);
+  if (N > 4) v += dpp_zero<0x114>(v);
+  if (N > 8) v += dpp_zero<0x118>(v);
+  return v;
+}
+// Double-precision variants (the two 32-bit halves move together).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_zero(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffff), CTRL, ROW_MASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROW_MASK, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+template <int N>
+__device__ __forceinline__ double group_sum_last(double v) {
+  if (N > 1) v += dpp_zero<0x111>(v);
+  if (N > 2) v += dpp_zero<0x112>(v);
+  if (N > 4) v += dpp_zero<0x114>(v);
+  if (N > 8) v += dpp_zero<0x118>(v);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_last(double v) {
+  v = group_sum_last<16>(v);
+  v += dpp_zero<0x142, 0xa>(v);
+  v += dpp_zero<0x143, 0xc>(v);
+  return v;
+}
+
+// Sum over the whole wave; lane 63 receives the total.
+__device__ __forceinline__ float wave_sum_last(float v) {
+  v = group_sum_last<16>(v);
+  v += dpp_zero<0x142, 0xa>(v);
+  v += dpp_zero<0x143, 0xc>(v);
+  return v;
+}
+// Max over groups of 32 lanes: lanes 31 and 63 receive their half's maximum.
+__device__ __forceinline__ float half_max_last(float v) {
+  v = fmaxf(v, dpp_keep<0x111>(v));
+  v = fmaxf(v, dpp_keep<0x112>(v));
+  v = fmaxf(v, dpp_keep<0x114>(v));
+  v = fmaxf(v, dpp_keep<0x118>(v));
+  v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+  return v;
+}
+// Max over the wave, broadcast to every lane.
+__device__ __forceinline__ float wave_max_all(float v) {
+  v = half_max_last(v);
+  v = fmaxf(v, dpp_keep<0x143, 0xc>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// bf16 pair dot product accumulated in float32 (v_dot2_f32_bf16).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         c, false);
+}
+
 // Workgroup barrier that waits only for LDS traffic, so global loads issued earlier
 // (prefetches) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

@@ -22,12 +22,14 @@
 //  * route_scan_mfma (bf16, queries of >= 16 rows): one wave per routing head.  The wave
 //    keeps its head's query rows as MFMA A operands (v_mfma_f32_16x16x32_bf16, rows padded
 //    to 16) and streams 16-row tiles of its head's Kr-bar slice as B operands straight
-//    from HBM into registers, one tile ahead.  Column norms come from the same registers.
-//    The scaled per-head scores meet in LDS (double-buffered, one barrier per tile) for
-//    the head sum and token max; wave 0 then folds the 16 row scores into documents.
-//  * route_scan_dot (any dtype, short queries): one wave per row; each lane holds 8
-//    elements of the row and multiplies them with pre-scaled query vectors from LDS,
-//    reducing across the wave.
+//    from HBM into registers through a ring of three tiles (two tiles of loads stay in
+//    flight while one is computed).  Column norms come from the same registers
+//    (v_dot2_f32_bf16).  The scaled per-head scores meet in LDS (double-buffered, one
+//    barrier per tile) for the head sum and the token max (DPP reductions); row scores
+//    collect in LDS and are folded into documents once per window of rows, by all waves.
+//  * route_scan_dot (any dtype, short queries): each wave streams its own range of rows,
+//    four rows per step with the next four in flight; a lane holds 8 elements of a row,
+//    head sums and the head mean use DPP lane shifts.
 #include <math.h>
 
 #include "common.hpp"
@@ -53,51 +55,9 @@ __device__ __forceinline__ int64_t load_window(const int64_t* chunk_off, int n_d
 }
 
 // ------------------------------------------------------------------------------------
-// Wave-0 helper of the MFMA scan: fold 16 consecutive row scores (lane l < 16 holds row
-// c_first + l) into document maxima.  `win` holds chunk_off[wb + 1 + lane], a window of
-// document ends that must cover the tile; it is rebased when the tile runs past it.
-// `carry` is the running maximum of document `cur_doc`, which began in an earlier tile.
-// A document's score is stored once its last row has been seen; on a later pass over the
-// same rows (query rows beyond the first block) it is combined with the stored value.
+// MFMA scan.
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ void fold_tile_docs(const ScanK& a, float* scores, int64_t c_first,
-                                               int64_t c_end, float s, bool first_pass,
-                                               int& cur_doc, int& wb, int64_t& win,
-                                               float& carry) {
-  const int lane = threadIdx.x & 63;
-  const int64_t c_last = min(c_first + 15, c_end - 1);
-  const int nvalid = (int)(c_last - c_first + 1);
-  if (!(c_last < __shfl(win, 63))) {
-    wb = cur_doc;
-    win = load_window(a.chunk_off, a.n_docs, wb);
-  }
-  const int64_t c = c_first + lane;
-  const bool valid = lane < nvalid;
-  int pos = 0;  // #{j : win[j] <= c}, win strictly increasing
-#pragma unroll
-  for (int step = 32; step >= 1; step >>= 1) {
-    const int64_t v = __shfl(win, pos + step - 1);
-    if (v <= c) pos += step;
-  }
-  const int doc = wb + pos;
-  const int64_t doc_end = __shfl(win, pos);  // chunk_off[doc + 1]
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {  // segmented inclusive max
-    const float os = __shfl_up(s, off);
-    const int od = __shfl_up(doc, off);
-    if (lane >= off && od == doc) s = fmaxf(s, os);
-  }
-  if (doc == cur_doc) s = fmaxf(s, carry);
-  if (valid && c + 1 == doc_end) {  // last row of its document
-    const float v = first_pass ? s : fmaxf(s, scores[doc]);
-    scores[doc] = v;
-  }
-  const int ld = __shfl(doc, nvalid - 1);
-  const float ls = __shfl(s, nvalid - 1);
-  const int64_t lend = __shfl(doc_end, nvalid - 1);
-  if (c_last + 1 == lend) { cur_doc = ld + 1; carry = -INFINITY; }
-  else { cur_doc = ld; carry = ls; }
-}
+constexpr int WIN = 4096;  // rows whose scores are held in LDS before folding into documents
 
 template <int MT, int D>
 __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
@@ -105,10 +65,12 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
   constexpr int ROWS = MT * 16;       // query rows per block
   constexpr int STRIDE = ROWS + 4;    // padded LDS row (floats)
   __shared__ float red[2][8][16][STRIDE];
-  __shared__ float sc[2][16];
+  __shared__ float sc_all[WIN];
+  __shared__ float carry[2];
 
   const int H = a.H;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int w = tid >> 6, lane = tid & 63;
   const int cl = lane & 15, g = lane >> 4;
   const int b = blockIdx.y;
   const int q0 = a.q_off[b];
@@ -118,138 +80,215 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
   if (d_begin >= d_end) return;
   float* scores = a.scores + (int64_t)b * a.n_docs;
   if (Lq <= 0) {  // a query without tokens scores -inf everywhere
-    for (int d = d_begin + threadIdx.x; d < d_end; d += blockDim.x) scores[d] = -INFINITY;
+    for (int d = d_begin + tid; d < d_end; d += nthr) scores[d] = -INFINITY;
     return;
   }
   const int64_t c_begin = a.chunk_off[d_begin];
   const int64_t c_end = a.chunk_off[d_end];
   const bf16_t* Qr = (const bf16_t*)a.Qr;
   const bf16_t* Kb = (const bf16_t*)a.Krb;
-  const int64_t ntiles = (c_end - c_begin + 15) / 16;
+  int d_first = d_begin;  // document owning the window's first row
+  if (tid == 0) carry[0] = -INFINITY;
 
-  for (int rb = 0; rb < Lq; rb += ROWS) {
-    const int rows = min(ROWS, Lq - rb);
-    int cur_doc = d_begin, wb = d_begin;
-    int64_t win = load_window(a.chunk_off, a.n_docs, wb);
-    float carry = -INFINITY;
-    // ---- A operands: this head's query rows, and their scales ----
-    bf16x8_t A[MT][KK];
-    float rs[MT][4];
+  for (int64_t w0 = c_begin, wi = 0; w0 < c_end; w0 += WIN, ++wi) {
+    const int64_t w1 = min(w0 + (int64_t)WIN, c_end);
+    const int wn = (int)(w1 - w0);
+    const int64_t ntiles = (wn + 15) / 16;
+    for (int i = tid; i < wn; i += nthr) sc_all[i] = -INFINITY;
+
+    for (int rb = 0; rb < Lq; rb += ROWS) {
+      const int rows = min(ROWS, Lq - rb);
+      // ---- A operands: this head's query rows, and their scales ----
+      bf16x8_t A[MT][KK];
+      float rs[MT][4];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int r = rb + m * 16 + cl;
-      float ss = 0.f;
+      for (int m = 0; m < MT; ++m) {
+        const int r = rb + m * 16 + cl;
+        float ss = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if (r < Lq) {
-          const uint4 wq = *reinterpret_cast<const uint4*>(
-              Qr + ((int64_t)(q0 + r) * H + w) * D + kk * 32 + g * 8);
+        for (int kk = 0; kk < KK; ++kk) {
+          uint4 wq = make_uint4(0, 0, 0, 0);
+          if (r < Lq)
+            wq = *reinterpret_cast<const uint4*>(Qr + ((int64_t)(q0 + r) * H + w) * D + kk * 32 + g * 8);
           A[m][kk] = __builtin_bit_cast(bf16x8_t, wq);
-          float f[8];
-          unpack8(wq, f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-        } else {
-          A[m][kk] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+          ss = dot2_bf16(wq.x, wq.x, ss);
+          ss = dot2_bf16(wq.y, wq.y, ss);
+          ss = dot2_bf16(wq.z, wq.z, ss);
+          ss = dot2_bf16(wq.w, wq.w, ss);
         }
-      }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      const float rrow = ss > 0.f ? 1.0f / ((float)H * sqrtf(ss)) : 0.f;
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const float rrow = ss > 0.f ? 1.0f / ((float)H * sqrtf(ss)) : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rs[m][i] = __shfl(rrow, g * 4 + i);
-    }
+        for (int i = 0; i < 4; ++i) rs[m][i] = __shfl(rrow, g * 4 + i);
+      }
+      __syncthreads();  // sc_all initialised; red free from the previous block
 
-    // ---- stream 16-row tiles, one tile of loads in flight ahead ----
-    bf16x8_t Bn[KK];
-    auto load_tile = [&](int64_t t, bf16x8_t* Bf) {
-      const int64_t c = c_begin + t * 16 + cl;
-      if (c < c_end) {
+      // Tile t covers rows w0 + 16t .. +15; rows past the window are clamped to the last
+      // row (their columns are zeroed through cs = 0), so loads need no branches.
+      auto load = [&](bf16x8_t (&B)[KK], int64_t t) {
+        int64_t c = w0 + t * 16 + cl;
+        c = c < w1 ? c : w1 - 1;
         const bf16_t* p = Kb + (c * H + w) * D + g * 8;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          Bf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + kk * 32));
-      } else {
+          B[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + kk * 32));
+      };
+      auto process = [&](bf16x8_t (&B)[KK], int64_t t) {
+        const int buf = (int)(t & 1);
+        float ss = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) Bf[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-      }
-    };
-    load_tile(0, Bn);
-    int buf = 0;
-    for (int64_t t = 0; t < ntiles; ++t) {
-      bf16x8_t Bc[KK];
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) Bc[kk] = Bn[kk];
-      if (t + 1 < ntiles) load_tile(t + 1, Bn);
-
-      float ss = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        float f[8];
-        unpack8(__builtin_bit_cast(uint4, Bc[kk]), f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-      }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      const float cs = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
-
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][kk], Bc[kk], acc, 0, 0, 0);
-        // lane holds rows m*16 + g*4 + i of column cl
-        float4 v;
-        v.x = acc[0] * rs[m][0] * cs;
-        v.y = acc[1] * rs[m][1] * cs;
-        v.z = acc[2] * rs[m][2] * cs;
-        v.w = acc[3] * rs[m][3] * cs;
-        *reinterpret_cast<float4*>(&red[buf][w][cl][m * 16 + g * 4]) = v;
-      }
-      lds_barrier();
-
-      // head sum, then max over this block's query rows; wave w takes rows w, w+H, ...
-      for (int cc = w; cc < 16; cc += H) {
-        float s = -INFINITY;
-        if (lane < rows) {
-          float sum = 0.f;
-          for (int h = 0; h < H; ++h) sum += red[buf][h][cc][lane];
-          s = sum;
+        for (int kk = 0; kk < KK; ++kk) {
+          const uint4 u = __builtin_bit_cast(uint4, B[kk]);
+          ss = dot2_bf16(u.x, u.x, ss);
+          ss = dot2_bf16(u.y, u.y, ss);
+          ss = dot2_bf16(u.z, u.z, ss);
+          ss = dot2_bf16(u.w, u.w, ss);
         }
-        s = wave_max(s);
-        if (lane == 0) sc[buf][cc] = s;
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const bool valid = w0 + t * 16 + cl < w1;
+        const float cs = (valid && ss > 0.f) ? 1.0f / sqrtf(ss) : 0.f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][kk], B[kk], acc, 0, 0, 0);
+          // lane holds rows m*16 + g*4 + i of column cl
+          float4 v;
+          v.x = acc[0] * rs[m][0] * cs;
+          v.y = acc[1] * rs[m][1] * cs;
+          v.z = acc[2] * rs[m][2] * cs;
+          v.w = acc[3] * rs[m][3] * cs;
+          *reinterpret_cast<float4*>(&red[buf][w][cl][m * 16 + g * 4]) = v;
+        }
+        lds_barrier();
+        // head sum then max over query rows: thread (column c, row pair j), 32 lanes per column
+        for (int base = 0; base < 16 * 32; base += nthr) {
+          const int idx = base + tid;
+          const int c = idx >> 5, j = idx & 31;
+          float s = -INFINITY;
+          if (2 * j < rows) {
+            float s0 = 0.f, s1 = 0.f;
+            for (int h = 0; h < H; ++h) {
+              const float2 v = *reinterpret_cast<const float2*>(&red[buf][h][c][2 * j]);
+              s0 += v.x;
+              s1 += v.y;
+            }
+            s = (2 * j + 1 < rows) ? fmaxf(s0, s1) : s0;
+          }
+          s = half_max_last(s);
+          if ((lane & 31) == 31) {
+            const int64_t ci = t * 16 + c;
+            if (ci < wn) sc_all[ci] = fmaxf(sc_all[ci], s);
+          }
+        }
+      };
+
+      bf16x8_t B0[KK], B1[KK], B2[KK];
+      load(B0, 0);
+      if (ntiles > 1) load(B1, 1);
+      if (ntiles > 2) load(B2, 2);
+      for (int64_t t = 0; t < ntiles; t += 3) {
+        process(B0, t);
+        if (t + 3 < ntiles) load(B0, t + 3);
+        if (t + 1 < ntiles) {
+          process(B1, t + 1);
+          if (t + 4 < ntiles) load(B1, t + 4);
+        }
+        if (t + 2 < ntiles) {
+          process(B2, t + 2);
+          if (t + 5 < ntiles) load(B2, t + 5);
+        }
       }
-      if (w == 0 && t > 0) {
-        const float s = (lane < 16) ? sc[buf ^ 1][lane] : -INFINITY;
-        fold_tile_docs(a, scores, c_begin + (t - 1) * 16, c_end, s, rb == 0, cur_doc, wb, win, carry);
+      __syncthreads();
+    }
+
+    // ---- fold the window's row scores into documents, all waves in parallel ----
+    const int cin = (int)(wi & 1), cout = cin ^ 1;
+    int d_next = d_first;
+    for (int d = d_first + w; d < d_end; d += H) {
+      const int64_t r0 = a.chunk_off[d], r1 = a.chunk_off[d + 1];
+      if (r0 >= w1) break;
+      const int lo = (int)(max(r0, w0) - w0), hi = (int)(min(r1, w1) - w0);
+      float m = -INFINITY;
+      for (int i = lo + lane; i < hi; i += 64) m = fmaxf(m, sc_all[i]);
+      m = wave_max_all(m);
+      if (r0 < w0) m = fmaxf(m, carry[cin]);  // began in an earlier window
+      if (lane == 0) {
+        if (r1 <= w1) scores[d] = m;
+        else carry[cout] = m;                  // continues into the next window
       }
-      buf ^= 1;
     }
-    lds_barrier();
-    if (w == 0) {
-      const float s = (lane < 16) ? sc[buf ^ 1][lane] : -INFINITY;
-      fold_tile_docs(a, scores, c_begin + (ntiles - 1) * 16, c_end, s, rb == 0, cur_doc, wb, win, carry);
-    }
-    lds_barrier();
+    if (w1 < c_end) d_next = find_doc_wave(a.chunk_off, a.n_docs, w1);
+    d_first = d_next;
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------------------------
-// Dot-product scan.  Each wave owns a document-aligned range of rows and folds row scores
-// into documents itself.  Query rows are handled in blocks of up to QB tokens held in LDS
-// as float, pre-multiplied by rs[t,h].
+// Dot-product scan for short queries.  Each wave owns a document-aligned range of rows,
+// reads them four at a time with the next four in flight, and folds row scores into
+// documents itself (its documents belong to it alone).  Query rows (raw) and their
+// scales rs[t,h] wait in LDS, in blocks of up to QB tokens.
 // ------------------------------------------------------------------------------------
 constexpr int QB = 16;
 constexpr int DOT_WAVES = 4;
+constexpr int U = 4;  // rows per group
 
-template <typename T, int D>
+template <typename T>
+struct RowSlot;  // one lane's 8 elements of one 512-element slice of a row
+// bf16 rows accumulate in float (bf16 products are exact in float); float32 rows in
+// double (float products are exact in double), which keeps near-cancelling cosines of
+// float32 inputs within a few float ulps.
+template <> struct RowSlot<bf16_t> {
+  typedef float acc_t;
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float sumsq() const {
+    float s = dot2_bf16(v.x, v.x, 0.f);
+    s = dot2_bf16(v.y, v.y, s);
+    s = dot2_bf16(v.z, v.z, s);
+    return dot2_bf16(v.w, v.w, s);
+  }
+  __device__ __forceinline__ float dot(const void* q) const {
+    const uint4 w = *reinterpret_cast<const uint4*>(q);
+    float s = dot2_bf16(v.x, w.x, 0.f);
+    s = dot2_bf16(v.y, w.y, s);
+    s = dot2_bf16(v.z, w.z, s);
+    return dot2_bf16(v.w, w.w, s);
+  }
+};
+template <> struct RowSlot<float> {
+  typedef double acc_t;
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ static double d(float x) { return (double)x; }
+  __device__ __forceinline__ double sumsq() const {
+    return d(a.x) * a.x + d(a.y) * a.y + d(a.z) * a.z + d(a.w) * a.w + d(b.x) * b.x + d(b.y) * b.y +
+           d(b.z) * b.z + d(b.w) * b.w;
+  }
+  __device__ __forceinline__ double dot(const void* q) const {
+    const float4 u = reinterpret_cast<const float4*>(q)[0], w = reinterpret_cast<const float4*>(q)[1];
+    return d(a.x) * u.x + d(a.y) * u.y + d(a.z) * u.z + d(a.w) * u.w + d(b.x) * w.x + d(b.y) * w.y +
+           d(b.z) * w.z + d(b.w) * w.w;
+  }
+};
+
+template <typename T, int D, int P>
 __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
-  extern __shared__ float qs[];  // [QB][H*D]
+  extern __shared__ __align__(16) unsigned char dot_lds[];
+  constexpr int LPH = D / 8;  // lanes per head within a 512-element slice
   const int H = a.H;
   const int R = H * D;
-  const int P = (R + 511) / 512;  // 8-element slots per lane
+  // P = slices of 512 elements per row (template, 1..4)
+  typedef typename RowSlot<T>::acc_t acc_t;
+  T* qs = reinterpret_cast<T*>(dot_lds);                           // [QB][R] raw query rows
+  acc_t* rsl = reinterpret_cast<acc_t*>(dot_lds + (size_t)QB * R * sizeof(T));  // [QB][H]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.y;
   const int q0 = a.q_off[b];
@@ -267,29 +306,24 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
   }
   const int64_t c_begin = (d_begin < d_end) ? a.chunk_off[d_begin] : 0;
   const int64_t c_end = (d_begin < d_end) ? a.chunk_off[d_end] : 0;
+  const bool head_last = (lane % LPH) == LPH - 1;
 
   for (int tb = 0; tb < Lq; tb += QB) {
     const int nt = min(QB, Lq - tb);
     __syncthreads();  // previous block's readers are done with qs
-    // pre-scaled query rows: one wave per (token, head) norm
-    for (int th = w; th < nt * H; th += DOT_WAVES) {
+    for (int i = threadIdx.x; i < nt * R; i += blockDim.x) qs[i] = Qr[(int64_t)(q0 + tb) * R + i];
+    for (int th = w; th < nt * H; th += DOT_WAVES) {  // one wave per (token, head) norm
       const int t = th / H, h = th % H;
       const T* q = Qr + ((int64_t)(q0 + tb + t) * H + h) * D;
-      float ss = 0.f;
+      acc_t ss = 0;
       for (int e = lane; e < D; e += 64) {
-        float x;
+        acc_t x;
         if constexpr (sizeof(T) == 4) x = ((const float*)q)[e];
         else x = bf16_to_f32(((const bf16_t*)q)[e]);
         ss += x * x;
       }
-      ss = wave_sum(ss);
-      const float r = ss > 0.f ? 1.0f / ((float)H * sqrtf(ss)) : 0.f;
-      for (int e = lane; e < D; e += 64) {
-        float x;
-        if constexpr (sizeof(T) == 4) x = ((const float*)q)[e];
-        else x = bf16_to_f32(((const bf16_t*)q)[e]);
-        qs[t * R + h * D + e] = x * r;
-      }
+      ss = wave_sum_last(ss);
+      if (lane == 63) rsl[t * H + h] = ss > 0 ? (acc_t)1 / ((acc_t)H * sqrt(ss)) : (acc_t)0;
     }
     __syncthreads();
     if (c_begin >= c_end) continue;
@@ -300,72 +334,75 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
     int64_t win = load_window(a.chunk_off, a.n_docs, wb);
     int64_t nb = __shfl(win, 0);  // end row of document `cur`
     float run = -INFINITY;
-    auto emit = [&](int doc, float v) {
-      if (lane == 0) scores[doc] = first_pass ? v : fmaxf(v, scores[doc]);
-    };
 
-    float xn[4][8];
-    auto load_row = [&](int64_t c, float (*x)[8]) {
+    auto load = [&](RowSlot<T> (&X)[U][P], int64_t c0) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int e0 = p * 512 + lane * 8;
-        if (p < P && e0 < R && c < c_end) Elem<T>::load8(Kb + c * R + e0, x[p]);
-        else {
+      for (int u = 0; u < U; ++u) {
+        int64_t c = c0 + u;
+        c = c < c_end ? c : c_end - 1;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[p][e] = 0.f;
-        }
-      }
-    };
-    load_row(c_begin, xn);
-    for (int64_t c = c_begin; c < c_end; ++c) {
-      float x[4][8];
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[p][e] = xn[p][e];
-      if (c + 1 < c_end) load_row(c + 1, xn);
-
-      // per-head inverse norms: reduce over the D/8 lanes of a head
-      float cs[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += x[p][e] * x[p][e];
-#pragma unroll
-        for (int o = 1; o < D / 8; o <<= 1) ss += __shfl_xor(ss, o);
-        cs[p] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
-      }
-      float best = -INFINITY;
-      for (int t = 0; t < nt; ++t) {
-        float dsum = 0.f;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < P; ++p) {
           const int e0 = p * 512 + lane * 8;
-          if (p < P && e0 < R) {
-            const float4 qa = *reinterpret_cast<const float4*>(&qs[t * R + e0]);
-            const float4 qb = *reinterpret_cast<const float4*>(&qs[t * R + e0 + 4]);
-            float d0 = x[p][0] * qa.x + x[p][1] * qa.y + x[p][2] * qa.z + x[p][3] * qa.w +
-                       x[p][4] * qb.x + x[p][5] * qb.y + x[p][6] * qb.z + x[p][7] * qb.w;
-            dsum += d0 * cs[p];
+          if (e0 < R) X[u][p].load(Kb + c * R + e0);
+        }
+      }
+    };
+    auto process = [&](RowSlot<T> (&X)[U][P], int64_t c0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u;
+        if (c >= c_end) break;  // uniform
+        acc_t cs[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int e0 = p * 512 + lane * 8;
+          acc_t ss = (e0 < R) ? X[u][p].sumsq() : (acc_t)0;
+          ss = group_sum_last<LPH>(ss);  // head total on the head's last lane
+          cs[p] = (head_last && ss > 0) ? (acc_t)1 / sqrt(ss) : (acc_t)0;
+        }
+        float best = -INFINITY;
+        for (int t = 0; t < nt; ++t) {
+          acc_t contrib = 0;
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const int e0 = p * 512 + lane * 8;
+            if (e0 < R) {
+              acc_t d0 = X[u][p].dot(qs + t * R + e0);
+              d0 = group_sum_last<LPH>(d0);
+              contrib += d0 * cs[p] * rsl[t * H + e0 / D];
+            }
           }
+          contrib = wave_sum_last(contrib);
+          best = fmaxf(best, (float)contrib);
         }
-        best = fmaxf(best, wave_sum(dsum));
-      }
-      // fold into documents (wave-uniform control flow)
-      while (c >= nb) {
-        emit(cur, run);
-        run = -INFINITY;
-        ++cur;
-        if (cur - wb >= 63) {
-          wb = cur;
-          win = load_window(a.chunk_off, a.n_docs, wb);
+        best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 63));
+        // fold into documents (wave-uniform control flow)
+        while (c >= nb) {
+          if (lane == 0) scores[cur] = first_pass ? run : fmaxf(run, scores[cur]);
+          run = -INFINITY;
+          ++cur;
+          if (cur - wb >= 63) {
+            wb = cur;
+            win = load_window(a.chunk_off, a.n_docs, wb);
+          }
+          nb = __shfl(win, cur - wb);
         }
-        nb = __shfl(win, cur - wb);
+        run = fmaxf(run, best);
       }
-      run = fmaxf(run, best);
+    };
+
+    RowSlot<T> X0[U][P], X1[U][P];
+    load(X0, c_begin);
+    if (c_begin + U < c_end) load(X1, c_begin + U);
+    for (int64_t c0 = c_begin; c0 < c_end; c0 += 2 * U) {
+      process(X0, c0);
+      if (c0 + 2 * U < c_end) load(X0, c0 + 2 * U);
+      if (c0 + U < c_end) {
+        process(X1, c0 + U);
+        if (c0 + 3 * U < c_end) load(X1, c0 + 3 * U);
+      }
     }
-    emit(cur, run);  // the range ends at a document end
+    if (lane == 0) scores[cur] = first_pass ? run : fmaxf(run, scores[cur]);  // range ends at a document end
   }
 }
 
@@ -380,7 +417,6 @@ int route_parts(int64_t n_chunks, int64_t rows_per_part) {
 template <int D>
 hipError_t launch_mfma(const RouteArgs& r, const ScanK& k, hipStream_t s) {
   const int mt = min(4, (r.max_q_len + 15) / 16);
-  // 2 workgroups per CU on 256 CUs, several times over; >= 4 tiles per workgroup.
   dim3 grid((unsigned)route_parts(r.n_chunks, 64), (unsigned)r.n_queries);
   dim3 block(64 * r.h_r);
   switch (mt) {
@@ -394,9 +430,16 @@ hipError_t launch_mfma(const RouteArgs& r, const ScanK& k, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
-  const size_t lds = (size_t)QB * r.h_r * D * sizeof(float);
-  dim3 grid((unsigned)route_parts(r.n_chunks, 4 * DOT_WAVES), (unsigned)r.n_queries);
-  hipLaunchKernelGGL((route_scan_dot<T, D>), grid, dim3(64 * DOT_WAVES), lds, s, k);
+  const size_t R = (size_t)r.h_r * D;
+  const size_t lds = QB * R * sizeof(T) + QB * r.h_r * (sizeof(T) == 4 ? sizeof(double) : sizeof(float));
+  dim3 grid((unsigned)route_parts(r.n_chunks, 8 * DOT_WAVES), (unsigned)r.n_queries);
+  dim3 block(64 * DOT_WAVES);
+  switch ((R + 511) / 512) {
+    case 1: hipLaunchKernelGGL((route_scan_dot<T, D, 1>), grid, block, lds, s, k); break;
+    case 2: hipLaunchKernelGGL((route_scan_dot<T, D, 2>), grid, block, lds, s, k); break;
+    case 3: hipLaunchKernelGGL((route_scan_dot<T, D, 3>), grid, block, lds, s, k); break;
+    default: hipLaunchKernelGGL((route_scan_dot<T, D, 4>), grid, block, lds, s, k); break;
+  }
   return hipGetLastError();
 }
 
