@@ -14,11 +14,14 @@
 // Kernels:
 //  * rope_local: rotates Q and the local K at their global positions (k_eff + local
 //    index) into the workspace, angles in double precision, once per row.
-//  * attn_mfma (bf16): one workgroup per (query, kv head, 64 query rows, key split).  The
+//  * attn_mfma (bf16): one workgroup per (query, kv head, block of up to 256 query rows,
+//    key split), with one 16-row wave per row slice, so each staged K/V tile serves every
+//    query row of the kv head and every byte read over the host link is read once.  The
 //    key sequence is [rows of the selected documents in rank order ; local keys]; the
 //    workgroup maps each key of a 32-key tile to its source row (bank row of a selected
 //    document, read from HBM or over the host link from pinned memory, or a local row),
-//    stages K in LDS row-major and V transposed, and runs an online softmax in float32.
+//    stages K in LDS row-major and V transposed (double-buffered, the next tile's loads in
+//    flight during the current tile's math), and runs an online softmax in float32.
 //    S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 leaves each lane with 8 scores of one
 //    query row, which are exactly the P^T operand of O^T = V^T * P^T, so probabilities
 //    never leave registers.
@@ -33,8 +36,6 @@ namespace msa {
 namespace {
 
 constexpr int RPW = 4;          // rows per workgroup in rope_local
-constexpr int ATT_WAVES = 4;    // waves per attention workgroup (16 query rows each)
-constexpr int ATT_ROWS = ATT_WAVES * 16;
 constexpr int KT = 32;          // keys per tile
 
 struct AttnK {
@@ -171,14 +172,90 @@ __device__ __forceinline__ MemMap build_memmap(const int32_t* ids, int k, const 
   return {keff, run};
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_mfma(AttnK a) {
+// Staging of one 32-key tile: 16-byte unit u < KT*D/8 is a K unit, the rest V units.
+// Key index -> source row: a bank row of the selected document of rank r (mpre[r] <= key <
+// mpre[r+1]) while key < M, else local row key - M.
+struct TileSrc {
+  const bf16_t *Kb, *Vb, *Kr, *Vl;
+  const int64_t *mstart, *mpre;
+  int keff, hkv, g, kv0;
+  int64_t M, k_hi;
+};
+
+template <int D, int THREADS, int UPT>
+__device__ __forceinline__ void tile_fetch(const TileSrc ts, int tid, int64_t kt, uint4 (&stage)[UPT]) {
+  constexpr int UPR = D / 8;
+  constexpr int UNITS = 2 * KT * UPR;
+#pragma unroll
+  for (int j = 0; j < UPT; ++j) {
+    const int u = tid + j * THREADS;
+    uint4 wv = make_uint4(0, 0, 0, 0);
+    if (u < UNITS) {
+      const bool isv = u >= KT * UPR;
+      const int uu = isv ? u - KT * UPR : u;
+      const int kr = uu / UPR, e0 = (uu % UPR) * 8;
+      const int64_t key = kt + kr;
+      if (key < ts.k_hi) {
+        const bf16_t* p;
+        if (key < ts.M) {
+          int lo = 0, hi = ts.keff;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (ts.mpre[mid] <= key) lo = mid; else hi = mid;
+          }
+          const int64_t brow = ts.mstart[lo] + (key - ts.mpre[lo]);
+          p = (isv ? ts.Vb : ts.Kb) + (brow * ts.hkv + ts.g) * D + e0;
+        } else {
+          const int64_t lrow = ts.kv0 + (key - ts.M);
+          p = (isv ? ts.Vl : ts.Kr) + (lrow * ts.hkv + ts.g) * D + e0;
+        }
+        wv = *reinterpret_cast<const uint4*>(p);
+      }
+    }
+    stage[j] = wv;
+  }
+}
+
+template <int D, int THREADS, int UPT, int KSTR, int VSTR>
+__device__ __forceinline__ void tile_commit(int tid, const uint4 (&stage)[UPT], bf16_t* Ks, bf16_t* Vt) {
+  constexpr int UPR = D / 8;
+  constexpr int UNITS = 2 * KT * UPR;
+#pragma unroll
+  for (int j = 0; j < UPT; ++j) {
+    const int u = tid + j * THREADS;
+    if (u < UNITS) {
+      const bool isv = u >= KT * UPR;
+      const int uu = isv ? u - KT * UPR : u;
+      const int kr = uu / UPR, e0 = (uu % UPR) * 8;
+      if (!isv) {
+        *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = stage[j];
+      } else {
+        const uint32_t w0 = stage[j].x, w1 = stage[j].y, w2 = stage[j].z, w3 = stage[j].w;
+        Vt[(e0 + 0) * VSTR + kr] = (bf16_t)(w0 & 0xffffu);
+        Vt[(e0 + 1) * VSTR + kr] = (bf16_t)(w0 >> 16);
+        Vt[(e0 + 2) * VSTR + kr] = (bf16_t)(w1 & 0xffffu);
+        Vt[(e0 + 3) * VSTR + kr] = (bf16_t)(w1 >> 16);
+        Vt[(e0 + 4) * VSTR + kr] = (bf16_t)(w2 & 0xffffu);
+        Vt[(e0 + 5) * VSTR + kr] = (bf16_t)(w2 >> 16);
+        Vt[(e0 + 6) * VSTR + kr] = (bf16_t)(w3 & 0xffffu);
+        Vt[(e0 + 7) * VSTR + kr] = (bf16_t)(w3 >> 16);
+      }
+    }
+  }
+}
+
+template <int D, int NW, int MTW>
+__global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
   constexpr int KK = D / 32;
   constexpr int MD = D / 16;
   constexpr int KSTR = D + 8;   // bf16 per K row in LDS
   constexpr int VSTR = KT + 8;  // bf16 per V^T row in LDS
-  __shared__ __align__(16) bf16_t Ks[KT * KSTR];
-  __shared__ __align__(16) bf16_t Vt[D * VSTR];
+  constexpr int UNITS = 2 * KT * (D / 8);  // 16-byte K and V units of one tile
+  constexpr int THREADS = 64 * NW;
+  constexpr int UPT = (UNITS + THREADS - 1) / THREADS;
+  constexpr int ROWS = NW * MTW * 16;  // query rows per workgroup (MTW 16-row tiles per wave)
+  __shared__ __align__(16) bf16_t Ks[2][KT * KSTR];
+  __shared__ __align__(16) bf16_t Vt[2][D * VSTR];
   __shared__ int64_t mstart[1025], mpre[1025];
   __shared__ int sh_keff;
   __shared__ int64_t sh_M;
@@ -189,10 +266,11 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnK a) {
   const int g = blockIdx.y % a.h_kv;
   const int split = blockIdx.y / a.h_kv;
   const int G = a.hq / a.h_kv;
+  const int hq_n = a.hq;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int kv0 = a.kv_off[b], Lkv = a.kv_off[b + 1] - kv0;
   const int nrows = Lq * G;
-  const int rb = blockIdx.x * ATT_ROWS;
+  const int rb = blockIdx.x * ROWS;
   if (rb >= nrows) return;
 
   if (w == 0) {
@@ -205,158 +283,156 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnK a) {
   const int64_t NK = M + Lkv;
   int64_t k_lo = NK * split / a.splits, k_hi = NK * (split + 1) / a.splits;
   // keys past the last local position any row of this block may see are never needed
-  const int t_max = min(Lq - 1, (rb + ATT_ROWS - 1) / G);
+  const int t_max = min(Lq - 1, (rb + ROWS - 1) / G);
   k_hi = min(k_hi, M + (int64_t)(Lkv - Lq + t_max + 1));
+  const float scale_log2 = a.scale_log2;
 
-  // this lane's query row (B operand of S^T), and its causal limit in key indices
-  const int row = rb + w * 16 + cl;
-  const bool row_ok = row < nrows;
-  const int t = row_ok ? row / G : 0;
-  const int hq = g * G + (row_ok ? row % G : 0);
-  const int64_t key_lim = M + (int64_t)(Lkv - Lq + t);  // last visible key index
-  bf16x8_t Qf[KK];
-  {
-    const bf16_t* qp = (const bf16_t*)a.Qrot + ((int64_t)(q0 + t) * a.hq + hq) * D + g4 * 8;
+  // this lane's query rows (one per row tile; B operands of S^T) and causal limits
+  bool row_ok[MTW];
+  int t_of[MTW], hq_of[MTW];
+  int64_t key_lim[MTW];
+  bf16x8_t Qf[MTW][KK];
+#pragma unroll
+  for (int m = 0; m < MTW; ++m) {
+    const int row = rb + (w * MTW + m) * 16 + cl;
+    row_ok[m] = row < nrows;
+    t_of[m] = row_ok[m] ? row / G : 0;
+    hq_of[m] = g * G + (row_ok[m] ? row % G : 0);
+    key_lim[m] = M + (int64_t)(Lkv - Lq + t_of[m]);  // last visible key index
+    const bf16_t* qp = (const bf16_t*)a.Qrot + ((int64_t)(q0 + t_of[m]) * hq_n + hq_of[m]) * D + g4 * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      Qf[kk] = row_ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + kk * 32))
-                      : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      Qf[m][kk] = row_ok[m] ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + kk * 32))
+                            : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
   }
 
-  f32x4_t acc[MD];
+  f32x4_t acc[MTW][MD];
+  float m_run[MTW], l_run[MTW];
 #pragma unroll
-  for (int md = 0; md < MD; ++md) acc[md] = {0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int m = 0; m < MTW; ++m) {
+    m_run[m] = -INFINITY;
+    l_run[m] = 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[m][md] = {0.f, 0.f, 0.f, 0.f};
+  }
 
-  const bf16_t* Kb = (const bf16_t*)a.Kbar;
-  const bf16_t* Vb = (const bf16_t*)a.Vbar;
-  const bf16_t* Kr = (const bf16_t*)a.Krot;
-  const bf16_t* Vl = (const bf16_t*)a.Vloc;
-  constexpr int UPR = D / 8;  // 16-byte units per key row
+  TileSrc ts;
+  ts.Kb = (const bf16_t*)a.Kbar;
+  ts.Vb = (const bf16_t*)a.Vbar;
+  ts.Kr = (const bf16_t*)a.Krot;
+  ts.Vl = (const bf16_t*)a.Vloc;
+  ts.mstart = mstart;
+  ts.mpre = mpre;
+  ts.keff = keff;
+  ts.hkv = a.h_kv;
+  ts.g = g;
+  ts.kv0 = kv0;
+  ts.M = M;
+  ts.k_hi = k_hi;
+  uint4 stage[UPT];
 
-  for (int64_t kt = k_lo; kt < k_hi; kt += KT) {
-    // ---- stage K (row-major) and V (transposed) for keys kt .. kt+31 ----
-    for (int u = tid; u < KT * UPR; u += blockDim.x) {
-      const int kr = u / UPR, e0 = (u % UPR) * 8;
-      const int64_t key = kt + kr;
-      uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
-      if (key < k_hi) {
-        const bf16_t *kp, *vp;
-        if (key < M) {
-          int lo = 0, hi = keff;  // rank r with mpre[r] <= key < mpre[r+1]
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (mpre[mid] <= key) lo = mid; else hi = mid;
-          }
-          const int64_t brow = mstart[lo] + (key - mpre[lo]);
-          kp = Kb + (brow * a.h_kv + g) * D + e0;
-          vp = Vb + (brow * a.h_kv + g) * D + e0;
-        } else {
-          const int64_t lrow = kv0 + (key - M);
-          kp = Kr + (lrow * a.h_kv + g) * D + e0;
-          vp = Vl + (lrow * a.h_kv + g) * D + e0;
+  if (k_lo < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, k_lo, stage);
+  int it = 0;
+  for (int64_t kt = k_lo; kt < k_hi; kt += KT, ++it) {
+    const int buf = it & 1;
+    tile_commit<D, THREADS, UPT, KSTR, VSTR>(tid, stage, Ks[buf], Vt[buf]);
+    __syncthreads();  // tile visible; the other buffer is free again
+    if (kt + KT < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, kt + KT, stage);  // in flight during the math
+
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      // ---- S^T = K Q^T for two 16-key halves ----
+      f32x4_t s[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        s[n] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const uint4 kw = *reinterpret_cast<const uint4*>(&Ks[buf][(n * 16 + cl) * KSTR + kk * 32 + g4 * 8]);
+          s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), Qf[m][kk], s[n], 0, 0, 0);
         }
-        kw = *reinterpret_cast<const uint4*>(kp);
-        vw = *reinterpret_cast<const uint4*>(vp);
       }
-      *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = kw;
-      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        Vt[(e0 + 2 * q) * VSTR + kr] = (bf16_t)(vv[q] & 0xffffu);
-        Vt[(e0 + 2 * q + 1) * VSTR + kr] = (bf16_t)(vv[q] >> 16);
-      }
-    }
-    __syncthreads();
-
-    // ---- S^T = K Q^T for two 16-key halves ----
-    f32x4_t s[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      s[n] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(&Ks[(n * 16 + cl) * KSTR + kk * 32 + g4 * 8]);
-        s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), Qf[kk], s[n], 0, 0, 0);
-      }
-    }
-    // lane holds S[row cl][key kt + n*16 + g4*4 + i]
-    float mx = -INFINITY;
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t key = kt + n * 16 + g4 * 4 + i;
-        const bool vis = row_ok && key < k_hi && key <= key_lim;
-        s[n][i] = vis ? s[n][i] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[n][i]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    float alpha = 1.f;
-    float p[2][4];
-    if (m_new == -INFINITY) {
+      // lane holds S[row cl of tile m][key kt + n*16 + g4*4 + i]
+      float mx = -INFINITY;
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[n][i] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
+        for (int i = 0; i < 4; ++i) {
+          const int64_t key = kt + n * 16 + g4 * 4 + i;
+          const bool vis = row_ok[m] && key < k_hi && key <= key_lim[m];
+          s[n][i] = vis ? s[n][i] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, s[n][i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[m], mx);
+      float alpha = 1.f;
+      float p[2][4];
+      if (m_new == -INFINITY) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[n][i] = 0.f;
+      } else {
+        alpha = exp2f(m_run[m] - m_new);
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[n][i] = exp2f(s[n][i] - m_new);
+      }
+      m_run[m] = m_new;
+      float ps = 0.f;
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[n][i] = exp2f(s[n][i] - m_new);
+        for (int i = 0; i < 4; ++i) ps += p[n][i];
+      l_run[m] = l_run[m] * alpha + ps;
+      // P^T operand: k-slot g4*8 + j  <->  key g4*4 + j (j < 4), 16 + g4*4 + (j-4) (j >= 4)
+      uint4 pw;
+      pw.x = f32_to_bf16(p[0][0]) | (f32_to_bf16(p[0][1]) << 16);
+      pw.y = f32_to_bf16(p[0][2]) | (f32_to_bf16(p[0][3]) << 16);
+      pw.z = f32_to_bf16(p[1][0]) | (f32_to_bf16(p[1][1]) << 16);
+      pw.w = f32_to_bf16(p[1][2]) | (f32_to_bf16(p[1][3]) << 16);
+      const bf16x8_t Pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const bf16_t* vr = &Vt[buf][(md * 16 + cl) * VSTR];
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vr + g4 * 4);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + g4 * 4);
+        const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][md][i] *= alpha;
+        acc[m][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vf, Pf, acc[m][md], 0, 0, 0);
+      }
     }
-    m_run = m_new;
-    float ps = 0.f;
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ps += p[n][i];
-    l_run = l_run * alpha + ps;
-    // P^T operand: k-slot g4*8 + j  <->  key g4*4 + j (j < 4), 16 + g4*4 + (j-4) (j >= 4)
-    uint4 pw;
-    pw.x = f32_to_bf16(p[0][0]) | (f32_to_bf16(p[0][1]) << 16);
-    pw.y = f32_to_bf16(p[0][2]) | (f32_to_bf16(p[0][3]) << 16);
-    pw.z = f32_to_bf16(p[1][0]) | (f32_to_bf16(p[1][1]) << 16);
-    pw.w = f32_to_bf16(p[1][2]) | (f32_to_bf16(p[1][3]) << 16);
-    const bf16x8_t Pf = __builtin_bit_cast(bf16x8_t, pw);
-#pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      const bf16_t* vr = &Vt[(md * 16 + cl) * VSTR];
-      const uint2 v0 = *reinterpret_cast<const uint2*>(vr + g4 * 4);
-      const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + g4 * 4);
-      const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[md][i] *= alpha;
-      acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vf, Pf, acc[md], 0, 0, 0);
-    }
-    __syncthreads();
   }
 
-  // row totals: the 4 lane groups of a row hold partial sums
-  float l_row = l_run + __shfl_xor(l_run, 16);
-  l_row += __shfl_xor(l_row, 32);
-  if (!row_ok) return;
-  const int64_t orow = (int64_t)(q0 + t) * a.hq + hq;
-  if (a.splits == 1) {
-    const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
-    bf16_t* o = (bf16_t*)a.O + orow * D + g4 * 4;
 #pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      float f[4] = {acc[md][0] * inv, acc[md][1] * inv, acc[md][2] * inv, acc[md][3] * inv};
-      Elem<bf16_t>::store4(o + md * 16, f);
-    }
-  } else {
-    const int64_t prow = (int64_t)split * a.total_q * a.hq + orow;
-    float* po = a.part_o + prow * D + g4 * 4;
+  for (int m = 0; m < MTW; ++m) {
+    // row totals: the 4 lane groups of a row hold partial sums
+    float l_row = l_run[m] + __shfl_xor(l_run[m], 16);
+    l_row += __shfl_xor(l_row, 32);
+    if (!row_ok[m]) continue;
+    const int64_t orow = (int64_t)(q0 + t_of[m]) * hq_n + hq_of[m];
+    if (a.splits == 1) {
+      const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
+      bf16_t* o = (bf16_t*)a.O + orow * D + g4 * 4;
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
-      *reinterpret_cast<float4*>(po + md * 16) = make_float4(acc[md][0], acc[md][1], acc[md][2], acc[md][3]);
-    if (g4 == 0) {
-      a.part_ml[prow * 2] = m_run;
-      a.part_ml[prow * 2 + 1] = l_row;
+      for (int md = 0; md < MD; ++md) {
+        float f[4] = {acc[m][md][0] * inv, acc[m][md][1] * inv, acc[m][md][2] * inv, acc[m][md][3] * inv};
+        Elem<bf16_t>::store4(o + md * 16, f);
+      }
+    } else {
+      const int64_t prow = (int64_t)split * a.total_q * hq_n + orow;
+      float* po = a.part_o + prow * D + g4 * 4;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        *reinterpret_cast<float4*>(po + md * 16) =
+            make_float4(acc[m][md][0], acc[m][md][1], acc[m][md][2], acc[m][md][3]);
+      if (g4 == 0) {
+        a.part_ml[prow * 2] = m_run[m];
+        a.part_ml[prow * 2 + 1] = l_row;
+      }
     }
   }
 }
@@ -476,9 +552,16 @@ hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, hipStream_t s) {
     return hipGetLastError();
   } else {
     const int G = r.hq / r.h_kv;
-    const int rblocks = (r.max_q_len * G + ATT_ROWS - 1) / ATT_ROWS;
+    const int brows = attn_rows_per_block(r.max_q_len, G);
+    const int rblocks = (r.max_q_len * G + brows - 1) / brows;
     dim3 grid((unsigned)rblocks, (unsigned)(r.h_kv * k.splits), (unsigned)r.n_queries);
-    hipLaunchKernelGGL((attn_mfma<D>), grid, dim3(64 * ATT_WAVES), 0, s, k);
+    switch (brows) {
+      case 16: hipLaunchKernelGGL((attn_mfma<D, 1, 1>), grid, dim3(64), 0, s, k); break;
+      case 32: hipLaunchKernelGGL((attn_mfma<D, 2, 1>), grid, dim3(128), 0, s, k); break;
+      case 64: hipLaunchKernelGGL((attn_mfma<D, 4, 1>), grid, dim3(256), 0, s, k); break;
+      case 128: hipLaunchKernelGGL((attn_mfma<D, 8, 1>), grid, dim3(512), 0, s, k); break;
+      default: hipLaunchKernelGGL((attn_mfma<D, 8, 2>), grid, dim3(512), 0, s, k); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || k.splits == 1) return e;
     const int64_t rows = r.total_q * r.hq;
@@ -489,13 +572,26 @@ hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, hipStream_t s) {
 
 }  // namespace
 
+// Query rows per attention workgroup: every row of one (query, kv head) up to 256, so that
+// a staged K/V tile serves all the rows that need it (16 rows per wave up to 8 waves, then
+// two 16-row tiles per wave).
+int attn_rows_per_block(int max_q_len, int G) {
+  const int need = max_q_len * G;
+  int rows = 16;
+  while (rows < need && rows < 256) rows <<= 1;
+  return rows;
+}
+
+// Key splits per (query, kv head): enough workgroups in flight to keep the host link or HBM
+// busy (about 64), bounded so the partial results stay small.
 int attn_splits(int n_queries, int max_q_len, int hq, int h_kv) {
   const int G = hq / h_kv;
-  const int rblocks = (max_q_len * G + ATT_ROWS - 1) / ATT_ROWS;
+  const int rows = attn_rows_per_block(max_q_len, G);
+  const int rblocks = (max_q_len * G + rows - 1) / rows;
   const long base = (long)n_queries * h_kv * (rblocks > 0 ? rblocks : 1);
-  long s = (256 + base - 1) / base;
+  long s = (64 + base - 1) / base;
   if (s < 1) s = 1;
-  if (s > 8) s = 8;
+  if (s > 16) s = 16;
   return (int)s;
 }
 

@@ -64,6 +64,7 @@ struct AttnArgs {
   void* O;
   void* workspace;
 };
+int attn_rows_per_block(int max_q_len, int G);
 int attn_splits(int n_queries, int max_q_len, int hq, int h_kv);
 size_t attn_workspace_bytes(int dtype, int n_queries, int64_t total_q, int64_t total_kv,
                             int max_q_len, int hq, int h_kv, int d);

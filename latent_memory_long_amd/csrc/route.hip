@@ -32,6 +32,8 @@
 //    head sums and the head mean use DPP lane shifts.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -58,6 +60,7 @@ __device__ __forceinline__ int64_t load_window(const int64_t* chunk_off, int n_d
 // MFMA scan.
 // ------------------------------------------------------------------------------------
 constexpr int WIN = 4096;  // rows whose scores are held in LDS before folding into documents
+constexpr int RING = 4;    // register tile buffers per wave
 
 template <int MT, int D>
 __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
@@ -186,20 +189,18 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
         }
       };
 
-      bf16x8_t B0[KK], B1[KK], B2[KK];
-      load(B0, 0);
-      if (ntiles > 1) load(B1, 1);
-      if (ntiles > 2) load(B2, 2);
-      for (int64_t t = 0; t < ntiles; t += 3) {
-        process(B0, t);
-        if (t + 3 < ntiles) load(B0, t + 3);
-        if (t + 1 < ntiles) {
-          process(B1, t + 1);
-          if (t + 4 < ntiles) load(B1, t + 4);
-        }
-        if (t + 2 < ntiles) {
-          process(B2, t + 2);
-          if (t + 5 < ntiles) load(B2, t + 5);
+      // Ring of RING tiles: RING - 1 tiles of loads stay in flight while one is computed.
+      // Every load is issued unconditionally (tile index clamped to the last tile) so the
+      // compiler can wait for exactly the oldest tile instead of draining the queue.
+      bf16x8_t Bq[RING][KK];
+#pragma unroll
+      for (int r = 0; r < RING; ++r) load(Bq[r], min((int64_t)r, ntiles - 1));
+      for (int64_t t0 = 0; t0 < ntiles; t0 += RING) {
+#pragma unroll
+        for (int r = 0; r < RING; ++r) {
+          const int64_t t = t0 + r;
+          if (t < ntiles) process(Bq[r], t);
+          load(Bq[r], min(t + RING, ntiles - 1));
         }
       }
       __syncthreads();
@@ -327,82 +328,96 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
     }
     __syncthreads();
     if (c_begin >= c_end) continue;
-    const bool first_pass = tb == 0;
-
-    int cur = d_begin;
-    int wb = cur;
-    int64_t win = load_window(a.chunk_off, a.n_docs, wb);
-    int64_t nb = __shfl(win, 0);  // end row of document `cur`
-    float run = -INFINITY;
-
-    auto load = [&](RowSlot<T> (&X)[U][P], int64_t c0) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        int64_t c = c0 + u;
-        c = c < c_end ? c : c_end - 1;
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const int e0 = p * 512 + lane * 8;
-          if (e0 < R) X[u][p].load(Kb + c * R + e0);
+    // The first token block stores document scores; later blocks (queries longer than QB
+    // rows) combine with them.  The two cases are separate loops so the streaming loop of
+    // the common case holds no global read that would make it wait for its prefetches.
+    auto run_rows = [&](auto first_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;
+      int cur = d_begin;
+      int wb = cur;
+      int64_t win = load_window(a.chunk_off, a.n_docs, wb);
+      int64_t nb = __shfl(win, 0);  // end row of document `cur`
+      float run = -INFINITY;
+      auto emit = [&](int doc, float v) {
+        if (lane == 0) {
+          if (FIRST) scores[doc] = v;
+          else scores[doc] = fmaxf(v, scores[doc]);
         }
-      }
-    };
-    auto process = [&](RowSlot<T> (&X)[U][P], int64_t c0) {
+      };
+
+      auto load = [&](RowSlot<T> (&X)[U][P], int64_t c0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + u;
-        if (c >= c_end) break;  // uniform
-        acc_t cs[P];
+        for (int u = 0; u < U; ++u) {
+          int64_t c = c0 + u;
+          c = c < c_end ? c : c_end - 1;
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const int e0 = p * 512 + lane * 8;
-          acc_t ss = (e0 < R) ? X[u][p].sumsq() : (acc_t)0;
-          ss = group_sum_last<LPH>(ss);  // head total on the head's last lane
-          cs[p] = (head_last && ss > 0) ? (acc_t)1 / sqrt(ss) : (acc_t)0;
+          for (int p = 0; p < P; ++p) {  // lanes past the row end re-read its last 8 elements
+            const int e0 = min(p * 512 + lane * 8, R - 8);
+            X[u][p].load(Kb + c * R + e0);
+          }
         }
-        float best = -INFINITY;
-        for (int t = 0; t < nt; ++t) {
-          acc_t contrib = 0;
+      };
+      auto process = [&](RowSlot<T> (&X)[U][P], int64_t c0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t c = c0 + u;
+          if (c >= c_end) break;  // uniform
+          acc_t cs[P];
 #pragma unroll
           for (int p = 0; p < P; ++p) {
             const int e0 = p * 512 + lane * 8;
-            if (e0 < R) {
-              acc_t d0 = X[u][p].dot(qs + t * R + e0);
-              d0 = group_sum_last<LPH>(d0);
-              contrib += d0 * cs[p] * rsl[t * H + e0 / D];
+            acc_t ss = (e0 < R) ? X[u][p].sumsq() : (acc_t)0;
+            ss = group_sum_last<LPH>(ss);  // head total on the head's last lane
+            cs[p] = (head_last && ss > 0) ? (acc_t)1 / sqrt(ss) : (acc_t)0;
+          }
+          float best = -INFINITY;
+          for (int t = 0; t < nt; ++t) {
+            acc_t contrib = 0;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+              const int e0 = p * 512 + lane * 8;
+              if (e0 < R) {
+                acc_t d0 = X[u][p].dot(qs + t * R + e0);
+                d0 = group_sum_last<LPH>(d0);
+                contrib += d0 * cs[p] * rsl[t * H + e0 / D];
+              }
+            }
+            contrib = wave_sum_last(contrib);
+            best = fmaxf(best, (float)contrib);
+          }
+          best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 63));
+          // fold into documents (wave-uniform control flow)
+          while (c >= nb) {
+            emit(cur, run);
+            run = -INFINITY;
+            ++cur;
+            if (cur - wb >= 63) {
+              wb = cur;
+              win = load_window(a.chunk_off, a.n_docs, wb);
+              nb = __shfl(win, 0);
+            } else {
+              nb = __shfl(win, cur - wb);
             }
           }
-          contrib = wave_sum_last(contrib);
-          best = fmaxf(best, (float)contrib);
+          run = fmaxf(run, best);
         }
-        best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 63));
-        // fold into documents (wave-uniform control flow)
-        while (c >= nb) {
-          if (lane == 0) scores[cur] = first_pass ? run : fmaxf(run, scores[cur]);
-          run = -INFINITY;
-          ++cur;
-          if (cur - wb >= 63) {
-            wb = cur;
-            win = load_window(a.chunk_off, a.n_docs, wb);
-          }
-          nb = __shfl(win, cur - wb);
-        }
-        run = fmaxf(run, best);
-      }
-    };
+      };
 
-    RowSlot<T> X0[U][P], X1[U][P];
-    load(X0, c_begin);
-    if (c_begin + U < c_end) load(X1, c_begin + U);
-    for (int64_t c0 = c_begin; c0 < c_end; c0 += 2 * U) {
-      process(X0, c0);
-      if (c0 + 2 * U < c_end) load(X0, c0 + 2 * U);
-      if (c0 + U < c_end) {
-        process(X1, c0 + U);
-        if (c0 + 3 * U < c_end) load(X1, c0 + 3 * U);
+      // Two groups of U rows: one computed while the other is in flight.  Loads are issued
+      // unconditionally (rows clamped to the range) so waits target the oldest group only.
+      RowSlot<T> X0[U][P], X1[U][P];
+      load(X0, c_begin);
+      load(X1, c_begin + U);
+      for (int64_t c0 = c_begin; c0 < c_end; c0 += 2 * U) {
+        process(X0, c0);
+        load(X0, c0 + 2 * U);
+        if (c0 + U < c_end) process(X1, c0 + U);
+        load(X1, c0 + 3 * U);
       }
-    }
-    if (lane == 0) scores[cur] = first_pass ? run : fmaxf(run, scores[cur]);  // range ends at a document end
+      emit(cur, run);  // the range ends at a document end
+    };
+    if (tb == 0) run_rows(std::true_type{});
+    else run_rows(std::false_type{});
   }
 }
 
