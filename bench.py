@@ -189,6 +189,7 @@ def main():
     ids = torch.empty((1, k), dtype=torch.int32, device=dev)
     sc = torch.empty((1, k), dtype=torch.float32, device=dev)
     out = torch.empty((Lq, sh.hq, sh.d), dtype=torch.bfloat16, device=dev)
+    tws = torch.empty(max(M.msa_topk_workspace(1, N, k), 256), dtype=torch.uint8, device=dev)
     ws = torch.empty(max(M.msa_sparse_attn_workspace(M.MSA_BF16, 1, 200, 200, 200, sh.hq, sh.h_kv, sh.d), 256),
                      dtype=torch.uint8, device=dev)
     pre = [(q["Qr"][:Lq].contiguous(), q["Q"][:Lq].contiguous(), q["Kloc"][:Lq].contiguous(),
@@ -199,7 +200,7 @@ def main():
         ev[0].record()
         M.msa_route_scan(Qr, q_off, Lq, Krb, coff_d, out=ds)
         ev[1].record()
-        M.msa_topk(ds, k, out=(ids, sc))
+        M.msa_topk(ds, k, out=(ids, sc), workspace=tws)
         ev[2].record()
         M.msa_sparse_attn(Q, Kl, Vl, q_off, kv_off, Lq, ids, coff_d, Kb, Vb, rope_base=sh.rope_base,
                           out=out, workspace=ws)
@@ -235,7 +236,7 @@ def main():
     if wl.decode_steps and args.decode_steps:
         q = qs[0]
         steps = min(args.decode_steps, wl.decode_steps)
-        M.msa_route_topk(pre[0][0], q_off, Lq, Krb, coff_d, k, out=(ids, sc, ds))
+        M.msa_route_topk(pre[0][0], q_off, Lq, Krb, coff_d, k, out=(ids, sc, ds), workspace=tws)
         fixed_ids = ids.clone()
         one = torch.tensor([0, 1], dtype=torch.int32, device=dev)
         routed, fixed = [], []
@@ -247,7 +248,7 @@ def main():
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             e[0].record()
             M.msa_route_scan(Qr1, one, 1, Krb, coff_d, out=ds)
-            M.msa_topk(ds, k, out=(ids, sc))
+            M.msa_topk(ds, k, out=(ids, sc), workspace=tws)
             M.msa_sparse_attn(Q1, Kl, Vl, one, kvo, 1, ids, coff_d, Kb, Vb, rope_base=sh.rope_base,
                               out=out[:1], workspace=ws)
             e[1].record()

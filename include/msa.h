@@ -115,6 +115,9 @@ msa_status msa_route_scan(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                           const int64_t* chunk_off, const void* Krbar, float* doc_scores,
                           msa_stream_t stream);
 
+/* Bytes of workspace msa_topk needs (0 when none; else a 256-byte aligned buffer). */
+size_t msa_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
+
 /*
  * msa_topk -- step C alone (github-wiki.com project 250, section 6 item 1: top-k document
  * selection; yeyulingfeng.com section 五 step 2).
@@ -122,12 +125,16 @@ msa_status msa_route_scan(msa_dtype dtype, int32_t n_queries, int64_t total_q,
  *   topk_ids   device int32 [n_queries, k]: the min(k, n_docs) best documents by (score
  *              descending, id ascending; -0.0 equals +0.0); remaining slots -1.
  *   topk_scores device float [n_queries, k]: their scores; -inf in unused slots.
+ *   workspace  msa_topk_workspace() bytes (may be NULL when that is 0): candidates of
+ *              document slices, reduced in parallel before a final merge.
  *   Supported: 1 <= k <= 1024.
  */
 msa_status msa_topk(int32_t n_queries, int32_t n_docs, const float* doc_scores, int32_t k,
-                    int32_t* topk_ids, float* topk_scores, msa_stream_t stream);
+                    int32_t* topk_ids, float* topk_scores, void* workspace,
+                    size_t workspace_bytes, msa_stream_t stream);
 
-/* Bytes of workspace msa_route_topk needs when doc_scores is NULL (256-byte aligned). */
+/* Bytes of workspace msa_route_topk needs when doc_scores is NULL (256-byte aligned);
+ * with doc_scores given it needs msa_topk_workspace() bytes. */
 size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
 
 /*
@@ -146,7 +153,7 @@ size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
  *              descending, id ascending); remaining slots -1.
  *   topk_scores device float [n_queries, k]: their scores; -inf in unused slots.
  *   doc_scores device float [n_queries, n_docs] or NULL: every document's score; when
- *              NULL the scores are kept in `workspace` instead (which may be NULL otherwise).
+ *              NULL the scores are kept in `workspace` instead.
  *   Supported: d in {32, 64, 128}; h_r in [1, 16]; 1 <= k <= 1024.  Scores and norms
  *   accumulate in float32; bf16 inputs with max_q_len >= 16 use MFMA tiles.
  */

@@ -7,6 +7,6 @@ context.  The kernels live in csrc/ and are reached through the C ABI of include
 from .binding import (  # noqa: F401
     MSA_BF16, MSA_F32, MSA_ROPE_K, MSA_ROPE_KR, MSA_ROPE_V, LIB_PATH, MsaError,
     msa_chunk_offsets, msa_last_error, msa_pool, msa_route_scan, msa_route_topk,
-    msa_route_topk_workspace, msa_topk,
+    msa_route_topk_workspace, msa_topk, msa_topk_workspace,
     msa_sparse_attn, msa_sparse_attn_workspace, msa_status_string, msa_version,
 )

@@ -45,7 +45,8 @@ def _load() -> ctypes.CDLL:
                                     P, P, P, P, P, P, P]),
         "msa_route_scan": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
                                           P, P, P]),
-        "msa_topk": (ctypes.c_int, [I32, I32, P, I32, P, P, P]),
+        "msa_topk_workspace": (SZ, [I32, I32, I32]),
+        "msa_topk": (ctypes.c_int, [I32, I32, P, I32, P, P, P, SZ, P]),
         "msa_route_topk_workspace": (SZ, [I32, I32, I32]),
         "msa_route_topk": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
                                           P, I32, P, P, P, P, SZ, P]),
@@ -152,14 +153,22 @@ def msa_route_scan(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar:
     return out
 
 
-def msa_topk(doc_scores: torch.Tensor, k: int, out=None, stream=None):
+def msa_topk_workspace(n_queries: int, n_docs: int, k: int) -> int:
+    return int(lib.msa_topk_workspace(n_queries, n_docs, k))
+
+
+def msa_topk(doc_scores: torch.Tensor, k: int, out=None, workspace: Optional[torch.Tensor] = None,
+             stream=None):
     """Step C.  doc_scores float32 [B, N] -> (ids int32 [B, k], scores float32 [B, k])."""
     B, N = doc_scores.shape
     if out is None:
         out = (torch.empty((B, k), dtype=torch.int32, device=doc_scores.device),
                torch.empty((B, k), dtype=torch.float32, device=doc_scores.device))
     ids, sc = out
-    _check(lib.msa_topk(B, N, _ptr(doc_scores), k, _ptr(ids), _ptr(sc), _stream(stream)))
+    need = msa_topk_workspace(B, N, k)
+    ws = _workspace(need, doc_scores.device, workspace) if need else None
+    _check(lib.msa_topk(B, N, _ptr(doc_scores), k, _ptr(ids), _ptr(sc), _ptr(ws),
+                        need and ws.numel() * ws.element_size(), _stream(stream)))
     return ids, sc
 
 
@@ -181,8 +190,9 @@ def msa_route_topk(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar:
                torch.empty((B, N), dtype=torch.float32, device=dev) if want_doc_scores else None)
     ids, sc, ds = out
     ws, wsb = None, 0
-    if ds is None:
-        ws = _workspace(msa_route_topk_workspace(B, N, k), dev, workspace)
+    need = msa_route_topk_workspace(B, N, k) if ds is None else msa_topk_workspace(B, N, k)
+    if need:
+        ws = _workspace(need, dev, workspace)
         wsb = ws.numel() * ws.element_size()
     _check(lib.msa_route_topk(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
                               Krbar.shape[1], Krbar.shape[2], N, Krbar.shape[0], _ptr(chunk_off),

@@ -99,10 +99,15 @@ msa_status msa_pool(msa_dtype dtype, int32_t n_docs, int64_t n_tokens, int64_t n
   return hip_status(msa::launch_pool(a, (hipStream_t)stream), "msa_pool launch");
 }
 
+size_t msa_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k) {
+  if (n_queries < 1 || n_docs < 1 || k < 1 || k > 1024) return 0;
+  return msa::topk_workspace_bytes(n_queries, n_docs, k);
+}
+
 size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k) {
-  (void)k;
-  if (n_queries < 1 || n_docs < 1) return 0;
-  return msa::align256((size_t)n_queries * (size_t)n_docs * sizeof(float));
+  if (n_queries < 1 || n_docs < 1 || k < 1 || k > 1024) return 0;
+  return msa::align256((size_t)n_queries * (size_t)n_docs * sizeof(float)) +
+         msa::topk_workspace_bytes(n_queries, n_docs, k);
 }
 
 namespace {
@@ -149,13 +154,17 @@ msa_status msa_route_scan(msa_dtype dtype, int32_t n_queries, int64_t total_q, c
 }
 
 msa_status msa_topk(int32_t n_queries, int32_t n_docs, const float* doc_scores, int32_t k,
-                    int32_t* topk_ids, float* topk_scores, msa_stream_t stream) {
+                    int32_t* topk_ids, float* topk_scores, void* workspace,
+                    size_t workspace_bytes, msa_stream_t stream) {
   g_last_error.clear();
   msa_status st = check_topk(n_queries, n_docs, k, topk_ids, topk_scores);
   if (st != MSA_OK) return st;
   if (!doc_scores) return fail(MSA_ERR_INVALID_ARG, "null doc_scores");
+  const size_t need = msa_topk_workspace(n_queries, n_docs, k);
+  if (need && (!workspace || workspace_bytes < need)) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  if (need && ((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   msa::TopkArgs t{n_queries, n_docs, k, doc_scores, topk_ids, topk_scores};
-  return hip_status(msa::launch_topk(t, (hipStream_t)stream), "msa_topk launch");
+  return hip_status(msa::launch_topk(t, workspace, (hipStream_t)stream), "msa_topk launch");
 }
 
 msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
@@ -170,20 +179,20 @@ msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
   if (st != MSA_OK) return st;
   st = check_topk(n_queries, n_docs, k, topk_ids, topk_scores);
   if (st != MSA_OK) return st;
-  float* scores = doc_scores;
-  if (!scores) {  // document scores go to the workspace
-    const size_t need = msa_route_topk_workspace(n_queries, n_docs, k);
-    if (!workspace || workspace_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-    if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    scores = (float*)workspace;
-  }
+  // workspace: [document scores when doc_scores is NULL][top-k candidates]
+  const size_t score_bytes = doc_scores ? 0 : msa::align256((size_t)n_queries * n_docs * sizeof(float));
+  const size_t need = score_bytes + msa::topk_workspace_bytes(n_queries, n_docs, k);
+  if (need && (!workspace || workspace_bytes < need)) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  if (need && ((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  float* scores = doc_scores ? doc_scores : (float*)workspace;
+  void* topk_ws = need ? (void*)((char*)workspace + score_bytes) : nullptr;
   hipStream_t s = (hipStream_t)stream;
   msa::RouteArgs r{(int)dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
                    chunk_off, Krbar, scores, route_path_override()};
   st = hip_status(msa::launch_route_scan(r, s), "msa_route_topk scan launch");
   if (st != MSA_OK) return st;
   msa::TopkArgs t{n_queries, n_docs, k, scores, topk_ids, topk_scores};
-  return hip_status(msa::launch_topk(t, s), "msa_route_topk top-k launch");
+  return hip_status(msa::launch_topk(t, topk_ws, s), "msa_route_topk top-k launch");
 }
 
 size_t msa_sparse_attn_workspace(msa_dtype dtype, int32_t n_queries, int64_t total_q,

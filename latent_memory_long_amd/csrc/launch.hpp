@@ -44,7 +44,8 @@ struct TopkArgs {
   int32_t* ids;
   float* scores;
 };
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+size_t topk_workspace_bytes(int n_queries, int n_docs, int k);
+hipError_t launch_topk(const TopkArgs& a, void* workspace, hipStream_t s);
 
 struct AttnArgs {
   int dtype;
