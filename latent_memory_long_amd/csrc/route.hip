@@ -22,9 +22,9 @@
 //  * route_scan_mfma (bf16, queries of >= 16 rows): one wave per routing head.  The wave
 //    keeps its head's query rows as MFMA A operands (v_mfma_f32_16x16x32_bf16, rows padded
 //    to 16) and streams 16-row tiles of its head's Kr-bar slice as B operands straight
-//    from HBM into registers through a ring of three tiles (two tiles of loads stay in
-//    flight while one is computed).  Column norms come from the same registers
-//    (v_dot2_f32_bf16).  The scaled per-head scores meet in LDS (double-buffered, one
+//    from HBM into registers through a ring of four tiles (three tiles of loads stay in
+//    flight while one is computed).  Row norms of the tile are the diagonal of B^T B, one
+//    more MFMA chain on the same registers.  The scaled per-head scores meet in LDS (double-buffered, one
 //    barrier per tile) for the head sum and the token max (DPP reductions); row scores
 //    collect in LDS and are folded into documents once per window of rows, by all waves.
 //  * route_scan_dot (any dtype, short queries): each wave streams its own range of rows,
@@ -68,6 +68,7 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
   constexpr int ROWS = MT * 16;       // query rows per block
   constexpr int STRIDE = ROWS + 4;    // padded LDS row (floats)
   __shared__ float red[2][8][16][STRIDE];
+  __shared__ float4 csq[2][16][2];  // 1/|Kr-bar[c, h]| of the tile, [buf][c][h / 4]
   __shared__ float sc_all[WIN];
   __shared__ float carry[2];
 
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
         }
         ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
-        const float rrow = ss > 0.f ? 1.0f / ((float)H * sqrtf(ss)) : 0.f;
+        const float rrow = ss > 0.f ? __builtin_amdgcn_rsqf(ss) / (float)H : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) rs[m][i] = __shfl(rrow, g * 4 + i);
       }
@@ -139,31 +140,33 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
       };
       auto process = [&](bf16x8_t (&B)[KK], int64_t t) {
         const int buf = (int)(t & 1);
-        float ss = 0.f;
+        // Squared row norms of the tile: the diagonal of B^T B (the B registers are also the
+        // A operand of the 16 rows), exact products in float32.  The lane holding diagonal
+        // element (cl, cl) -- lane group g == cl / 4, element cl % 4 -- stores 1/|row|.
+        {
+          f32x4_t gram = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const uint4 u = __builtin_bit_cast(uint4, B[kk]);
-          ss = dot2_bf16(u.x, u.x, ss);
-          ss = dot2_bf16(u.y, u.y, ss);
-          ss = dot2_bf16(u.z, u.z, ss);
-          ss = dot2_bf16(u.w, u.w, ss);
+          for (int kk = 0; kk < KK; ++kk)
+            gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(B[kk], B[kk], gram, 0, 0, 0);
+          if (g == (cl >> 2)) {
+            const float ss = gram[cl & 3];
+            const bool valid = w0 + t * 16 + cl < w1;
+            reinterpret_cast<float*>(&csq[buf][cl][0])[w] =
+                (valid && ss > 0.f) ? __builtin_amdgcn_rsqf(ss) : 0.f;
+          }
         }
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        const bool valid = w0 + t * 16 + cl < w1;
-        const float cs = (valid && ss > 0.f) ? 1.0f / sqrtf(ss) : 0.f;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < KK; ++kk)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][kk], B[kk], acc, 0, 0, 0);
-          // lane holds rows m*16 + g*4 + i of column cl
+          // lane holds rows m*16 + g*4 + i of column cl; the column scale comes later
           float4 v;
-          v.x = acc[0] * rs[m][0] * cs;
-          v.y = acc[1] * rs[m][1] * cs;
-          v.z = acc[2] * rs[m][2] * cs;
-          v.w = acc[3] * rs[m][3] * cs;
+          v.x = acc[0] * rs[m][0];
+          v.y = acc[1] * rs[m][1];
+          v.z = acc[2] * rs[m][2];
+          v.w = acc[3] * rs[m][3];
           *reinterpret_cast<float4*>(&red[buf][w][cl][m * 16 + g * 4]) = v;
         }
         lds_barrier();
@@ -173,11 +176,13 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
           const int c = idx >> 5, j = idx & 31;
           float s = -INFINITY;
           if (2 * j < rows) {
+            const float* csc = reinterpret_cast<const float*>(&csq[buf][c][0]);
             float s0 = 0.f, s1 = 0.f;
             for (int h = 0; h < H; ++h) {
               const float2 v = *reinterpret_cast<const float2*>(&red[buf][h][c][2 * j]);
-              s0 += v.x;
-              s1 += v.y;
+              const float ch = csc[h];
+              s0 += v.x * ch;
+              s1 += v.y * ch;
             }
             s = (2 * j + 1 < rows) ? fmaxf(s0, s1) : s0;
           }
