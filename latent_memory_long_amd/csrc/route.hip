@@ -426,8 +426,8 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
   }
 }
 
-int route_parts(int64_t n_chunks, int64_t rows_per_part) {
-  int64_t p = 2048;
+int route_parts(int64_t n_chunks, int64_t rows_per_part, int64_t max_parts) {
+  int64_t p = max_parts;
   const int64_t mx = (n_chunks + rows_per_part - 1) / rows_per_part;
   if (p > mx) p = mx;
   if (p < 1) p = 1;
@@ -437,7 +437,8 @@ int route_parts(int64_t n_chunks, int64_t rows_per_part) {
 template <int D>
 hipError_t launch_mfma(const RouteArgs& r, const ScanK& k, hipStream_t s) {
   const int mt = min(4, (r.max_q_len + 15) / 16);
-  dim3 grid((unsigned)route_parts(r.n_chunks, 64), (unsigned)r.n_queries);
+  // about two workgroups per CU in turn: one 8-wave workgroup fits a CU at a time
+  dim3 grid((unsigned)route_parts(r.n_chunks, 64, 512), (unsigned)r.n_queries);
   dim3 block(64 * r.h_r);
   switch (mt) {
     case 1: hipLaunchKernelGGL((route_scan_mfma<1, D>), grid, block, 0, s, k); break;
@@ -452,7 +453,7 @@ template <typename T, int D>
 hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
   const size_t R = (size_t)r.h_r * D;
   const size_t lds = QB * R * sizeof(T) + QB * r.h_r * (sizeof(T) == 4 ? sizeof(double) : sizeof(float));
-  dim3 grid((unsigned)route_parts(r.n_chunks, 8 * DOT_WAVES), (unsigned)r.n_queries);
+  dim3 grid((unsigned)route_parts(r.n_chunks, 8 * DOT_WAVES, 2048), (unsigned)r.n_queries);
   dim3 block(64 * DOT_WAVES);
   switch ((R + 511) / 512) {
     case 1: hipLaunchKernelGGL((route_scan_dot<T, D, 1>), grid, block, lds, s, k); break;
