@@ -39,7 +39,9 @@ those readings are:
   R13 every query token sees all memory keys; local keys are causal;
   R14 GQA: query head hq uses kv head hq // (Hq / H_kv);
   R15 softmax scale 1/sqrt(D), no extras;
-  R16 bf16 values are produced by one round-to-nearest-even from float64.
+  R16 bf16 values are produced by one round-to-nearest-even from float64;
+  R25 a query with no tokens scores -inf on every document (the maximum over an empty set
+      of tokens), so its top-k is the k_eff lowest ids.
 
 Precision: every computation is float64.  Inputs given as bf16 are decoded exactly.
 """
@@ -236,7 +238,9 @@ def token_chunk_scores(Qr_q, Krbar) -> np.ndarray:
 
 
 def chunk_scores(Qr_q, Krbar) -> np.ndarray:
-    """S[c] = max over query tokens t of s[t, c] (R6)."""
+    """S[c] = max over query tokens t of s[t, c] (R6); -inf for a query with no tokens (R25)."""
+    if np.asarray(Qr_q).shape[0] == 0:
+        return np.full(np.asarray(Krbar).shape[0], -np.inf)
     return token_chunk_scores(Qr_q, Krbar).max(axis=0)
 
 

@@ -366,8 +366,9 @@ def test_route_scan_alone_and_empty_query():
         ids, sc = M.msa_topk(ds, 4)
         torch.cuda.synchronize()
         ds = ds.cpu().numpy()
-        assert np.all(np.isneginf(ds[1])), path
-        assert list(ids[1].cpu().numpy()) == [0, 1, 2, 3]
+        o1 = O.route_doc_scores(f64(Qr), q_off[[1, 2]], f64(Krb), coff)[0]
+        assert np.all(np.isneginf(ds[1])) and np.all(np.isneginf(o1)), path
+        assert list(ids[1].cpu().numpy()) == list(O.topk_docs(o1, 4)[0]) == [0, 1, 2, 3]
         o = O.route_doc_scores(f64(Qr), q_off[[0, 1]], f64(Krb), coff)[0]
         assert_scores_close(ds[0], o, "bf16", f"{path} q0")
         o2 = O.route_doc_scores(f64(Qr), q_off[[2, 3]] , f64(Krb), coff)[0]

@@ -128,3 +128,22 @@ def test_route_blocking_is_exact():
     a = O.route_doc_scores(Qr, q_off, Kb, off)
     b = O.route_doc_scores(Qr, q_off, Kb, off, block=13)
     assert np.array_equal(a, b)
+
+
+def test_empty_query_is_the_identity_of_the_token_max():
+    # Scores of a token set are the max over its tokens, so scores(A u B) = max(scores(A),
+    # scores(B)) for any split; with B empty this forces scores(empty) = -inf (R25), and the
+    # top-k of an all -inf row is the k lowest ids by the tie rule.
+    Qr, Kb, off = _tiny(28, T=5, n_chunks=(2, 1, 3, 1, 2))
+    whole = O.doc_scores_one(Qr, Kb, off)
+    for cut in range(0, 6):
+        a = O.doc_scores_one(Qr[:cut], Kb, off)
+        b = O.doc_scores_one(Qr[cut:], Kb, off)
+        assert np.array_equal(np.maximum(a, b), whole)
+    empty = O.doc_scores_one(Qr[:0], Kb, off)
+    assert np.all(np.isneginf(empty))
+    q_off = np.array([0, 2, 2, 5])                         # the middle query has no tokens
+    ids, vals, D = O.route(Qr, q_off, Kb, off, k=3)
+    assert list(ids[1]) == [0, 1, 2] and np.all(np.isneginf(vals[1]))
+    assert np.array_equal(D[0], O.doc_scores_one(Qr[:2], Kb, off))
+    assert np.array_equal(D[2], O.doc_scores_one(Qr[2:], Kb, off))
