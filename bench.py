@@ -34,13 +34,18 @@ import latent_memory_long_amd as M  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 METRIC = "routed bank tokens/s & % HBM peak; p50 route+attend latency, 100M-token bank"
 SCAN_KERNEL = "route_scan_mfma"
 
 # HBM traffic of the scan kernel per launch, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # on this workload (scaled by the counters' reading of a copy kernel of known size).  It is
 # reported only while the kernel source still has the digest it was measured with.
-TRAFFIC = None  # {"route_sha": "...", "fetch_bytes": ..., "write_bytes": ...}
+TRAFFIC = {"route_sha": "15dd6d44e0fab8f1",
+           # FETCH_SIZE 1,588,775 KiB per launch x 1.99993 (a 1 GiB copy reads 524,306 KiB)
+           "fetch_bytes": 3253767393,
+           # WRITE_SIZE 198.97 KiB per launch x 1.0 (a 1 GiB copy writes 1,048,576 KiB)
+           "write_bytes": 203744}
 
 
 def log(msg):
@@ -75,7 +80,8 @@ def make_queries(wl, dev, n):
 
 
 def time_pool(dev, reps=3):
-    """Pool a 10M-token bank (the batched encode workload) and time msa_pool."""
+    """Pool a 10M-token bank (the batched encode workload) and time msa_pool.  Returns the
+    figures and the pooled bank, which the batched route + attend stage then queries."""
     wl = W.workload("batch32_bank10m")
     sh = wl.shape
     lens = W.doc_lengths(wl)
@@ -102,11 +108,64 @@ def time_pool(dev, reps=3):
     row = (2 * sh.h_kv + sh.h_r) * sh.d * 2
     nbytes = T * row + C * row
     t = float(np.median(ms)) / 1e3
-    del K, V, Kr, outs
+    del K, V, Kr
     torch.cuda.empty_cache()
-    return {"workload": "batch32_bank10m (encode stage)", "tokens": T, "bank_rows": C,
-            "ms": round(t * 1e3, 3), "tokens_per_s": T / t, "algorithmic_bytes": nbytes,
-            "gbps": nbytes / t / 1e9, "frac_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+    fig = {"workload": "batch32_bank10m (encode stage)", "tokens": T, "bank_rows": C,
+           "ms": round(t * 1e3, 3), "tokens_per_s": T / t, "algorithmic_bytes": nbytes,
+           "gbps": nbytes / t / 1e9, "frac_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+    return fig, (wl, lens, coff, coff_d) + outs
+
+
+def time_batch(dev, bank, reps=20):
+    """Route + attend a batch of 32 queries (16-256 tokens each) against the pooled 10M-token
+    bank: one msa_route_scan over all queries, msa_topk, one msa_sparse_attn."""
+    wl, lens, coff, coff_d, Kb, Vb, Krb = bank
+    sh = wl.shape
+    N, C = len(lens), int(coff[-1])
+    q = W.gen_queries(wl, dev)
+    q_len = q["q_len"]
+    B = len(q_len)
+    q_off = np.concatenate([[0], np.cumsum(q_len)]).astype(np.int32)
+    q_off_d = torch.tensor(q_off, device=dev)
+    Qr, Q, Kl, Vl = q["Qr"], q["Q"], q["Kloc"], q["Vloc"]      # no decode rows: prefill only
+    Lmax = int(q_len.max())
+    tq = int(q_off[-1])
+    ds = torch.empty((B, N), dtype=torch.float32, device=dev)
+    ids = torch.empty((B, wl.k), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, wl.k), dtype=torch.float32, device=dev)
+    out = torch.empty_like(Q)
+    tws = torch.empty(max(M.msa_topk_workspace(B, N, wl.k), 256), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(M.msa_sparse_attn_workspace(M.MSA_BF16, B, tq, tq, Lmax, sh.hq, sh.h_kv, sh.d), 256),
+                     dtype=torch.uint8, device=dev)
+
+    def run(ev):
+        ev[0].record()
+        M.msa_route_scan(Qr, q_off_d, Lmax, Krb, coff_d, out=ds)
+        ev[1].record()
+        M.msa_topk(ds, wl.k, out=(ids, sc), workspace=tws)
+        ev[2].record()
+        M.msa_sparse_attn(Q, Kl, Vl, q_off_d, q_off_d, Lmax, ids, coff_d, Kb, Vb, rope_base=sh.rope_base,
+                          out=out, workspace=ws)
+        ev[3].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps + 2)]
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    evs = evs[2:]
+    scan = [e[0].elapsed_time(e[1]) for e in evs]
+    topk = [e[1].elapsed_time(e[2]) for e in evs]
+    attn = [e[2].elapsed_time(e[3]) for e in evs]
+    tot = [e[0].elapsed_time(e[3]) for e in evs]
+    # algorithmic scan flops: one dot product of D per (query token, bank row, routing head)
+    flops = 2.0 * tq * C * sh.h_r * sh.d
+    t_scan = float(np.mean(scan)) / 1e3
+    return {"workload": "batch32_bank10m (route + attend)", "queries": B, "query_tokens": tq,
+            "k": wl.k, "bank_rows": C, "route_attend_p50_ms": round(pct(tot, 50), 4),
+            "scan_p50_ms": round(pct(scan, 50), 4), "topk_p50_ms": round(pct(topk, 50), 4),
+            "attend_p50_ms": round(pct(attn, 50), 4), "scan_tflops": flops / t_scan / 1e12,
+            "scan_mfma_util": flops / t_scan / 1e12 / MFMA_PEAK_BF16_TFLOPS,
+            "routed_bank_tokens_per_s": B * int(np.sum(lens)) / (pct(tot, 50) / 1e3)}
 
 
 def cpu_baseline(wl, lens, off, coff, Krb, Kb, Vb, q, target_s):
@@ -141,9 +200,13 @@ def cpu_baseline(wl, lens, off, coff, Krb, Kb, Vb, q, target_s):
         return (t1 - t0) + (t3 - t2), rows
 
     with threadpool_limits(limits=1):
-        n0 = int(np.searchsorted(coff, 4096))
-        t_small, _ = run(max(n0, 1))
-        rows_target = int(4096 * target_s / max(t_small, 1e-3))
+        # two small samples fix the fixed cost (attention) and the per-row cost (routing)
+        n1 = max(int(np.searchsorted(coff, 4096)), 1)
+        n2 = max(int(np.searchsorted(coff, 32768)), n1 + 1)
+        t1, r1 = run(n1)
+        t2, r2 = run(n2)
+        per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-9)
+        rows_target = int(r1 + (target_s - t1) / per_row)
         n_docs = int(min(len(lens), max(1, np.searchsorted(coff, rows_target))))
         t, rows = run(n_docs)
     tokens = int(off[n_docs])
@@ -163,7 +226,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-pool", action="store_true")
+    ap.add_argument("--no-pool", action="store_true", help="skip the 10M-token encode and batch stages")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device to device 3 times: a kernel of known traffic "
+                         "against which hardware byte counters are scaled")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sharded "
@@ -178,6 +244,15 @@ def main():
     N, C = len(lens), int(coff[-1])
     T = int(off[-1])
     coff_d = torch.tensor(coff, device=dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {n} bytes")
+        del src, dst
     qs = make_queries(wl, dev, args.queries)
     Lq = int(qs[0]["q_len"][0])
     k = wl.k
@@ -263,12 +338,16 @@ def main():
                "routed_p90_ms": round(pct(routed, 90), 4), "fixed_ids_p50_ms": round(pct(fixed, 50), 4),
                "routed_bank_tokens_per_s": T / (pct(routed, 50) / 1e3)}
 
-    pool = None
+    pool = batch = None
     if not args.no_pool:
         del qs
         torch.cuda.empty_cache()
         log("pool on the 10M-token encode workload")
-        pool = time_pool(dev)
+        pool, bank10m = time_pool(dev)
+        log("batched route + attend: 32 queries against the pooled 10M-token bank")
+        batch = time_batch(dev, bank10m)
+        del bank10m
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -303,8 +382,10 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
                      "avg_launch_ms": scan_s * 1e3},
         "scan_routed_bank_tokens_per_s": T / scan_s,
+        "scan_mfma_util": 2.0 * Lq * C * sh.h_r * sh.d / scan_s / 1e12 / MFMA_PEAK_BF16_TFLOPS,
         "decode": dec or None,
         "pool": pool,
+        "batch": batch,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
