@@ -225,4 +225,22 @@ __device__ __forceinline__ int part_first_doc(const int64_t* chunk_off, int n_do
   return (chunk_off[d] == x) ? d : d + 1;
 }
 
+// Part and query of this workgroup in a (parts x queries) grid.  Workgroups go to the
+// eight XCDs round-robin in linear order (x fastest).  With several queries and a part
+// count divisible by 8, the linear id is remapped so that the queries of one part run on
+// the same XCD one after another: after the first reads a part's rows from HBM, the others
+// find them in that XCD's L2.  Otherwise the grid coordinates are used as they are.
+__device__ __forceinline__ void part_and_query(int& part, int& query) {
+  const unsigned P = gridDim.x, B = gridDim.y;
+  if (B == 1 || (P & 7u)) {
+    part = (int)blockIdx.x;
+    query = (int)blockIdx.y;
+    return;
+  }
+  const unsigned L = blockIdx.y * P + blockIdx.x;
+  const unsigned slot = L >> 3;  // position in this XCD's sequence
+  part = (int)((slot / B) * 8u + (L & 7u));
+  query = (int)(slot % B);
+}
+
 }  // namespace msa

@@ -76,11 +76,12 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int w = tid >> 6, lane = tid & 63;
   const int cl = lane & 15, g = lane >> 4;
-  const int b = blockIdx.y;
+  int part, b;
+  part_and_query(part, b);
   const int q0 = a.q_off[b];
   const int Lq = a.q_off[b + 1] - q0;
-  const int d_begin = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, blockIdx.x, gridDim.x);
-  const int d_end = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, blockIdx.x + 1, gridDim.x);
+  const int d_begin = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, part, gridDim.x);
+  const int d_end = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, part + 1, gridDim.x);
   if (d_begin >= d_end) return;
   float* scores = a.scores + (int64_t)b * a.n_docs;
   if (Lq <= 0) {  // a query without tokens scores -inf everywhere
@@ -296,10 +297,11 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
   T* qs = reinterpret_cast<T*>(dot_lds);                           // [QB][R] raw query rows
   acc_t* rsl = reinterpret_cast<acc_t*>(dot_lds + (size_t)QB * R * sizeof(T));  // [QB][H]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int b = blockIdx.y;
+  int part, b;
+  part_and_query(part, b);
   const int q0 = a.q_off[b];
   const int Lq = a.q_off[b + 1] - q0;
-  const int64_t gw = (int64_t)blockIdx.x * DOT_WAVES + w;
+  const int64_t gw = (int64_t)part * DOT_WAVES + w;
   const int64_t nw = (int64_t)gridDim.x * DOT_WAVES;
   const int d_begin = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, gw, nw);
   const int d_end = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, gw + 1, nw);
@@ -426,10 +428,14 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
   }
 }
 
-int route_parts(int64_t n_chunks, int64_t rows_per_part, int64_t max_parts) {
+// Parts of a scan: max_parts, fewer for small banks (at least rows_per_part rows each).
+// With several queries the count is rounded down to a multiple of 8 so that all queries
+// of a part can share one XCD (part_and_query).
+int route_parts(int64_t n_chunks, int64_t rows_per_part, int64_t max_parts, int n_queries) {
   int64_t p = max_parts;
   const int64_t mx = (n_chunks + rows_per_part - 1) / rows_per_part;
   if (p > mx) p = mx;
+  if (n_queries > 1 && p >= 8) p &= ~(int64_t)7;
   if (p < 1) p = 1;
   return (int)p;
 }
@@ -438,7 +444,7 @@ template <int D>
 hipError_t launch_mfma(const RouteArgs& r, const ScanK& k, hipStream_t s) {
   const int mt = min(4, (r.max_q_len + 15) / 16);
   // about two workgroups per CU in turn: one 8-wave workgroup fits a CU at a time
-  dim3 grid((unsigned)route_parts(r.n_chunks, 64, 512), (unsigned)r.n_queries);
+  dim3 grid((unsigned)route_parts(r.n_chunks, 64, 512, r.n_queries), (unsigned)r.n_queries);
   dim3 block(64 * r.h_r);
   switch (mt) {
     case 1: hipLaunchKernelGGL((route_scan_mfma<1, D>), grid, block, 0, s, k); break;
@@ -453,7 +459,7 @@ template <typename T, int D>
 hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
   const size_t R = (size_t)r.h_r * D;
   const size_t lds = QB * R * sizeof(T) + QB * r.h_r * (sizeof(T) == 4 ? sizeof(double) : sizeof(float));
-  dim3 grid((unsigned)route_parts(r.n_chunks, 8 * DOT_WAVES, 2048), (unsigned)r.n_queries);
+  dim3 grid((unsigned)route_parts(r.n_chunks, 8 * DOT_WAVES, 2048, r.n_queries), (unsigned)r.n_queries);
   dim3 block(64 * DOT_WAVES);
   switch ((R + 511) / 512) {
     case 1: hipLaunchKernelGGL((route_scan_dot<T, D, 1>), grid, block, lds, s, k); break;

@@ -217,6 +217,27 @@ def test_route_batched(path):
         assert_topk_valid(ids[b], o[b], 16, f"query {b}")
 
 
+@pytest.mark.parametrize("path", ["dot", "mfma"])
+def test_route_batched_parts_share_xcd(path):
+    # 4096 rows: 64 parts for the MFMA scan, 128 for the dot scan, so with several queries
+    # the workgroups take the XCD-grouped (part, query) order.
+    say(f"case route batched, XCD-grouped parts, path={path}")
+    _route_env(path)
+    counts = _chunk_counts(400, 12, hi=20)
+    counts[-1] += 4096 - int(counts.sum())
+    assert counts[-1] >= 1 and counts.sum() == 4096
+    coff, Krb = random_bank(counts, 8, 128, "bf16", 60)
+    for q_lens in ([20, 3, 48], [16] * 8, [1, 17, 2, 64, 5, 30, 16, 7, 40]):
+        Qr = _cpu_randn((sum(q_lens), 8, 128), 61 + len(q_lens)).to(torch.bfloat16)
+        ids, sc, ds = route(Qr.to(DEV), q_lens, Krb, coff, 8)
+        q_off = np.concatenate([[0], np.cumsum(q_lens)])
+        o = O.route_doc_scores(f64(Qr), q_off, f64(Krb), coff)
+        for b in range(len(q_lens)):
+            assert_scores_close(ds[b], o[b], "bf16", f"B={len(q_lens)} query {b}")
+            assert_topk_consistent(ids[b], sc[b], ds[b], 8, f"B={len(q_lens)} query {b}")
+            assert_topk_valid(ids[b], o[b], 8, f"B={len(q_lens)} query {b}")
+
+
 def test_route_paths_agree_and_deterministic():
     say("case route dot vs mfma, repeatability")
     counts = _chunk_counts(500, 9)
