@@ -7,53 +7,243 @@
 // 64-token chunk into K-bar / V-bar / Kr-bar; a partial last chunk still counts).
 //
 // Design (HBM-bound streaming read, ~6 KB per token for the Qwen3-4B-like layer):
-//  * Persistent workgroups each own a contiguous range of bank rows; every row reads its
-//    chunk's tokens once, coalesced (each token row of K, V and Kr is read by consecutive
-//    threads in 16-byte pieces).
-//  * One thread owns an 8-element "unit" of a token row: 8 consecutive elements, or for a
-//    rotated tensor 4 rotation pairs (i..i+3 together with i+d/2..i+d/2+3).  It sums its
-//    unit over the chunk's tokens in float32 registers.
+//  * The token rows are split over workgroups by bytes, each workgroup taking a contiguous
+//    range of whole chunks.  A thread owns one 8-element "unit" of a token row -- 8
+//    consecutive elements, or for a rotated tensor 4 rotation pairs (i..i+3 together with
+//    i+d/2..i+d/2+3) -- and streams its unit through the range token by token, 8 tokens
+//    per batch with the next batch's loads in flight, so the workgroup reads its range as
+//    one coalesced stream.  The sum runs in float32 registers, in token order.
+//  * Chunk and document boundaries are the same for every thread of the workgroup: when
+//    the stream reaches the end of a chunk, the chunk's mean is stored and the sum
+//    restarts.
 //  * Rotation by in-document position p = s + r (s = first position of the chunk) is split
-//    as R(s) * R(r): the token loop applies R(r) from a per-workgroup LDS table
+//    as R(s) * R(r): each token is rotated by R(r) from a per-workgroup LDS table
 //    (cos/sin of r*theta_i, r < chunk, evaluated in double precision), and R(s) is applied
 //    once to the chunk sum with double-precision angles.  Both are exact rotations, so the
 //    result is the same mean up to float32 rounding.
 //  * The mean divides by the number of real tokens with an IEEE division (a constant chunk
 //    pools to itself bit for bit), then rounds once to the storage type.
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace msa {
 namespace {
 
+// One lane's unit of one token row, as stored (converted to float when used).
+template <typename T> struct Raw;
+template <> struct Raw<bf16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load8(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load4x2(const bf16_t* lo, const bf16_t* hi) {
+    const uint2 x = *reinterpret_cast<const uint2*>(lo), y = *reinterpret_cast<const uint2*>(hi);
+    v = make_uint4(x.x, x.y, y.x, y.y);
+  }
+  __device__ __forceinline__ void get(float* f) const { unpack8(v, f); }
+};
+template <> struct Raw<float> {
+  float4 x, y;
+  __device__ __forceinline__ void load8(const float* p) {
+    x = *reinterpret_cast<const float4*>(p);
+    y = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void load4x2(const float* lo, const float* hi) {
+    x = *reinterpret_cast<const float4*>(lo);
+    y = *reinterpret_cast<const float4*>(hi);
+  }
+  __device__ __forceinline__ void get(float* f) const {
+    f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w; f[4] = y.x; f[5] = y.y; f[6] = y.z; f[7] = y.w;
+  }
+};
+
+constexpr int PT = 8;  // tokens per batch
+
+// A workgroup-uniform int64 read through the scalar cache, waited for in the same asm
+// block.  The document offsets are read this way inside the stream: the compiler cannot
+// prove that the kernel's own stores leave them alone, and a vector load there would make
+// the stream wait for every load in flight.
+__device__ __forceinline__ int64_t scalar_load_i64(const int64_t* p) {
+  int64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// First token of workgroup range w of W: token T * w / W rounded down to the start of its
+// chunk, so ranges hold whole chunks.  Also returns the document owning that token.
+// Wave-collective.
+__device__ __forceinline__ int64_t range_start(const PoolArgs& a, int64_t w, int64_t W, int& doc) {
+  if (w <= 0) { doc = 0; return 0; }
+  if (w >= W) { doc = a.n_docs; return a.n_tokens; }
+  const int64_t x = a.n_tokens * w / W;
+  doc = __builtin_amdgcn_readfirstlane(find_doc_wave(a.doc_tok_off, a.n_docs, x));
+  const int64_t t0 = a.doc_tok_off[doc];
+  return t0 + (x - t0) / a.chunk * a.chunk;
+}
+
+// State of one thread's stream.  The chunk fields are the same in every thread of the
+// workgroup: current chunk [cst, bnd) of document doc ([doc_s, doc_e)), bank row c.
+struct PoolStream {
+  float acc[8];
+  // cos / sin of s * theta_q for the current chunk start s (double); the step rotation
+  // by one chunk, chunk * theta_q
+  double rc[4], rs[4], stc[4], sts[4];
+  int64_t cst, bnd, c, doc_s, doc_e;
+  int doc;
+};
+
+// Mean of the finished chunk [cst, bnd) -> bank row c, then move to the next chunk.
+template <bool rotate, typename T>
+__device__ __forceinline__ void pool_flush(PoolStream& st, const PoolArgs& a, T* dst, int row_elems,
+                                           int e_lo, int e_hi, bool store) {
+  if constexpr (rotate) {  // R(s), s = first in-document position of the chunk (identity at s = 0)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float c32 = (float)st.rc[q], s32 = (float)st.rs[q];
+      const float x = st.acc[q], y = st.acc[4 + q];
+      st.acc[q] = x * c32 - y * s32;
+      st.acc[4 + q] = y * c32 + x * s32;
+    }
+  }
+  const float fn = (float)(st.bnd - st.cst);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) st.acc[q] = st.acc[q] / fn;
+  T* out = dst + st.c * row_elems;
+  if (store) {
+    if constexpr (rotate) {
+      Elem<T>::store4(out + e_lo, st.acc);
+      Elem<T>::store4(out + e_hi, st.acc + 4);
+    } else {
+      Elem<T>::store8(out + e_lo, st.acc);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) st.acc[q] = 0.f;
+  ++st.c;
+  st.cst = st.bnd;
+  if (st.cst == st.doc_e && st.doc + 1 < a.n_docs) {  // next document: positions restart
+    ++st.doc;
+    st.doc_s = st.doc_e;
+    st.doc_e = scalar_load_i64(a.doc_tok_off + st.doc + 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { st.rc[q] = 1.0; st.rs[q] = 0.0; }
+  } else {  // next chunk of the same document: s advances by one chunk
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double c0 = st.rc[q], s0 = st.rs[q];
+      st.rc[q] = c0 * st.stc[q] - s0 * st.sts[q];
+      st.rs[q] = s0 * st.stc[q] + c0 * st.sts[q];
+    }
+  }
+  st.bnd = min(st.cst + a.chunk, st.doc_e);
+}
+
+// Tokens t0 .. t0 + PT - 1 of this thread's unit (past the range: its last token again).
+template <bool rotate, typename T>
+__device__ __forceinline__ void pool_load(Raw<T> (&X)[PT], const T* src, int64_t t0, int64_t p1,
+                                          int row_elems, int e_lo, int e_hi) {
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    const int64_t t = min(t0 + k, p1 - 1);
+    const T* p = src + t * row_elems;
+    if constexpr (rotate) X[k].load4x2(p + e_lo, p + e_hi);
+    else X[k].load8(p + e_lo);
+  }
+}
+
+template <bool rotate, typename T>
+__device__ __forceinline__ void pool_batch(PoolStream& st, const Raw<T> (&X)[PT], int64_t t0, int64_t p1,
+                                           const PoolArgs& a, T* dst, int row_elems, int e_lo, int e_hi,
+                                           bool store, const float* rope_tab, int half, int i0) {
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    const int64_t t = t0 + k;
+    if (t >= p1) break;  // uniform
+    if (t == st.bnd) pool_flush<rotate>(st, a, dst, row_elems, e_lo, e_hi, store);
+    float v[8];
+    X[k].get(v);
+    if constexpr (rotate) {
+      const int r = (int)(t - st.cst);
+      const float4 cs = *reinterpret_cast<const float4*>(rope_tab + r * half + i0);
+      const float4 sn = *reinterpret_cast<const float4*>(rope_tab + a.chunk * half + r * half + i0);
+      const float cq[4] = {cs.x, cs.y, cs.z, cs.w}, sq[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x = v[q], y = v[4 + q];
+        st.acc[q] += x * cq[q] - y * sq[q];
+        st.acc[4 + q] += y * cq[q] + x * sq[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) st.acc[q] += v[q];
+    }
+  }
+}
+
+// The stream of one thread's unit through token range [p0, p1) (whole chunks, starting in
+// document doc0).
+template <bool rotate, typename T, int D>
+__device__ __forceinline__ void pool_stream(const PoolArgs& a, const T* src, T* dst, int64_t p0, int64_t p1,
+                                            int doc0, int row_elems, int e_lo, int e_hi, int i0, bool valid,
+                                            const float* rope_tab) {
+  PoolStream st;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) st.acc[q] = 0.f;
+  st.doc = doc0;
+  st.doc_s = a.doc_tok_off[doc0];
+  st.doc_e = a.doc_tok_off[doc0 + 1];
+  st.cst = p0;
+  st.bnd = min(p0 + a.chunk, st.doc_e);
+  st.c = a.chunk_off[doc0] + (p0 - st.doc_s) / a.chunk;
+  // R(s) of the first chunk, and the one-chunk step, in double precision
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    st.rc[q] = 1.0; st.rs[q] = 0.0; st.stc[q] = 1.0; st.sts[q] = 0.0;
+    if constexpr (rotate) {
+      const double th = pow((double)a.rope_base, -2.0 * (double)(i0 + q) / (double)D);
+      sincos((double)(p0 - st.doc_s) * th, &st.rs[q], &st.rc[q]);
+      sincos((double)a.chunk * th, &st.sts[q], &st.stc[q]);
+    }
+  }
+
+  // Two batches: one summed while the other is in flight.  Loads are unconditional
+  // (clamped to the range) so each wait targets the older batch only.
+  Raw<T> X0[PT], X1[PT];
+  pool_load<rotate>(X0, src, p0, p1, row_elems, e_lo, e_hi);
+  pool_load<rotate>(X1, src, p0 + PT, p1, row_elems, e_lo, e_hi);
+  for (int64_t t0 = p0; t0 < p1; t0 += 2 * PT) {
+    pool_batch<rotate>(st, X0, t0, p1, a, dst, row_elems, e_lo, e_hi, valid, rope_tab, D / 2, i0);
+    pool_load<rotate>(X0, src, t0 + 2 * PT, p1, row_elems, e_lo, e_hi);
+    if (t0 + PT < p1)
+      pool_batch<rotate>(st, X1, t0 + PT, p1, a, dst, row_elems, e_lo, e_hi, valid, rope_tab, D / 2, i0);
+    pool_load<rotate>(X1, src, t0 + 3 * PT, p1, row_elems, e_lo, e_hi);
+  }
+  pool_flush<rotate>(st, a, dst, row_elems, e_lo, e_hi, valid);  // the range ends at a chunk end
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(512) void pool_kernel(PoolArgs a) {
   extern __shared__ float rope_tab[];  // [chunk][D/2] cos, then [chunk][D/2] sin
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int units_per_head = D / 8;
-  const int n_units = (2 * a.h_kv + a.h_r) * units_per_head;
-  const int u = blockIdx.y * blockDim.x + tid;
   const int half = D / 2;
-
-  // Which tensor / head / piece this thread owns.
-  int tensor = 0, head = 0, piece = 0, heads = a.h_kv;
-  const T* src = nullptr;
-  T* dst = nullptr;
-  bool valid = u < n_units;
-  if (valid) {
-    int v = u;
-    if (v < a.h_kv * units_per_head) {
-      tensor = 0; heads = a.h_kv; src = (const T*)a.K; dst = (T*)a.Kbar;
-    } else if ((v -= a.h_kv * units_per_head) < a.h_kv * units_per_head) {
-      tensor = 1; heads = a.h_kv; src = (const T*)a.V; dst = (T*)a.Vbar;
-    } else {
-      v -= a.h_kv * units_per_head;
-      tensor = 2; heads = a.h_r; src = (const T*)a.Kr; dst = (T*)a.Krbar;
-    }
-    head = v / units_per_head;
-    piece = v % units_per_head;
-  }
-  const bool rotate = valid && ((a.rope_mask >> tensor) & 1u);
+  // Waves are assigned whole to one tensor (K, then V, then Kr; each tensor's units padded
+  // to a whole number of waves), so the tensor, its pointers and whether it is rotated are
+  // the same across a wave.
+  const int nk = a.h_kv * units_per_head, nr = a.h_r * units_per_head;
+  const int wk = (nk + 63) / 64, wr = (nr + 63) / 64;
+  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.y * (blockDim.x >> 6) + (tid >> 6));
+  int tensor, first;  // first unit of this wave within its tensor
+  if (gw < wk) { tensor = 0; first = gw * 64; }
+  else if (gw < 2 * wk) { tensor = 1; first = (gw - wk) * 64; }
+  else { tensor = 2; first = (gw - 2 * wk) * 64; }
+  const int n_t = tensor == 2 ? nr : nk;
+  const bool valid = gw < 2 * wk + wr && first + lane < n_t;
+  const int unit = min(first + lane, n_t - 1);  // lanes past the tensor load its last unit
+  const T* src = tensor == 0 ? (const T*)a.K : tensor == 1 ? (const T*)a.V : (const T*)a.Kr;
+  T* dst = tensor == 0 ? (T*)a.Kbar : tensor == 1 ? (T*)a.Vbar : (T*)a.Krbar;
+  const int heads = tensor == 2 ? a.h_r : a.h_kv;
+  const int head = unit / units_per_head, piece = unit % units_per_head;
+  const bool rotate = (a.rope_mask >> tensor) & 1u;  // uniform
   // Element offsets of the unit inside one token row of its tensor.
   const int e_lo = head * D + (rotate ? piece * 4 : piece * 8);
   const int e_hi = e_lo + half;  // second half of the rotation pairs
@@ -73,109 +263,27 @@ __global__ __launch_bounds__(512) void pool_kernel(PoolArgs a) {
   }
   __syncthreads();
 
-  const int64_t c_begin = a.n_chunks * (int64_t)blockIdx.x / gridDim.x;
-  const int64_t c_end = a.n_chunks * ((int64_t)blockIdx.x + 1) / gridDim.x;
-  if (c_begin >= c_end) return;
-  // Every lane of every wave takes part in the search (it votes across the wave).
-  int doc = find_doc_wave(a.chunk_off, a.n_docs, c_begin);
-  if (!valid) return;
+  // Token range [p0, p1) of this workgroup; every lane takes part in the searches.
+  int doc0, doc1;
+  const int64_t p0 = range_start(a, blockIdx.x, gridDim.x, doc0);
+  const int64_t p1 = range_start(a, (int64_t)blockIdx.x + 1, gridDim.x, doc1);
+  if (p0 >= p1 || gw >= 2 * wk + wr) return;
 
-  double theta[4];
-  if (rotate) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) theta[q] = pow((double)a.rope_base, -2.0 * (double)(i0 + q) / (double)D);
-  }
-
-  int64_t doc_c0 = a.chunk_off[doc], doc_c1 = a.chunk_off[doc + 1];
-  int64_t doc_t0 = a.doc_tok_off[doc], doc_t1 = a.doc_tok_off[doc + 1];
-
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    while (c >= doc_c1) {  // advance to the document owning row c
-      ++doc;
-      doc_c0 = doc_c1;
-      doc_c1 = a.chunk_off[doc + 1];
-      doc_t0 = doc_t1;
-      doc_t1 = a.doc_tok_off[doc + 1];
-    }
-    const int64_t j = c - doc_c0;                     // chunk index inside the document
-    const int64_t tok0 = doc_t0 + j * a.chunk;
-    const int n = (int)min((int64_t)a.chunk, doc_t1 - tok0);
-    const T* base = src + tok0 * row_elems;
-
-    float acc[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-
-    for (int r0 = 0; r0 < n; r0 += 8) {
-      float v[8][8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (r0 + t < n) {
-          const T* p = base + (int64_t)(r0 + t) * row_elems;
-          if (rotate) {
-            Elem<T>::load4(p + e_lo, v[t]);
-            Elem<T>::load4(p + e_hi, v[t] + 4);
-          } else {
-            Elem<T>::load8(p + e_lo, v[t]);
-          }
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (r0 + t < n) {
-          if (rotate) {
-            const float* cs = rope_tab + (r0 + t) * half + i0;
-            const float* sn = rope_tab + a.chunk * half + (r0 + t) * half + i0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float x = v[t][q], y = v[t][4 + q];
-              acc[q] += x * cs[q] - y * sn[q];
-              acc[4 + q] += y * cs[q] + x * sn[q];
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc[q] += v[t][q];
-          }
-        }
-      }
-    }
-
-    if (rotate && j > 0) {  // R(s), s = first in-document position of the chunk
-      const double s = (double)(j * a.chunk);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        double sn, cs;
-        sincos(s * theta[q], &sn, &cs);
-        const float c32 = (float)cs, s32 = (float)sn;
-        const float x = acc[q], y = acc[4 + q];
-        acc[q] = x * c32 - y * s32;
-        acc[4 + q] = y * c32 + x * s32;
-      }
-    }
-    const float fn = (float)n;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = acc[q] / fn;
-
-    T* out = dst + c * row_elems;
-    if (rotate) {
-      Elem<T>::store4(out + e_lo, acc);
-      Elem<T>::store4(out + e_hi, acc + 4);
-    } else {
-      Elem<T>::store8(out + e_lo, acc);
-    }
-  }
+  if (rotate) pool_stream<true, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab);
+  else pool_stream<false, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab);
 }
 
 template <typename T, int D>
 hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
-  const int n_units = (2 * a.h_kv + a.h_r) * (D / 8);
-  int threads = ((n_units + 63) / 64) * 64;
-  if (threads > 512) threads = 512;
-  const int ygroups = (n_units + threads - 1) / threads;
-  // Enough workgroups to fill 256 CUs several times over, never more than one per row.
-  int64_t wgs = 1024 / ygroups;
-  if (wgs < 256) wgs = 256;
+  const int nk = a.h_kv * (D / 8), nr = a.h_r * (D / 8);
+  const int waves = 2 * ((nk + 63) / 64) + (nr + 63) / 64;  // whole waves per tensor
+  int wpg = waves < 8 ? waves : 8;                          // waves per workgroup
+  const int ygroups = (waves + wpg - 1) / wpg;
+  const int threads = 64 * wpg;
+  // Token ranges: several per CU, each at least a few chunks long.
+  int64_t wgs = 2048 / ygroups;
   if (wgs > a.n_chunks) wgs = a.n_chunks;
+  if (wgs < 1) wgs = 1;
   const size_t lds = a.rope_mask ? (size_t)a.chunk * D * sizeof(float) : 0;
   dim3 grid((unsigned)wgs, (unsigned)ygroups);
   hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(threads), lds, s, a);
