@@ -154,8 +154,9 @@ size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
  *   topk_scores device float [n_queries, k]: their scores; -inf in unused slots.
  *   doc_scores device float [n_queries, n_docs] or NULL: every document's score; when
  *              NULL the scores are kept in `workspace` instead.
- *   Supported: d in {32, 64, 128}; h_r in [1, 16]; 1 <= k <= 1024.  Scores and norms
- *   accumulate in float32; bf16 inputs with max_q_len >= 16 use MFMA tiles.
+ *   Supported: d in {32, 64, 128}; h_r in [1, 16]; 1 <= k <= 1024.  bf16 inputs with
+ *   h_r <= 8 run on MFMA tiles (exact bf16 products, float32 sums); other bf16 inputs sum
+ *   in float32 and float32 inputs in double.
  */
 msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                           const int32_t* q_off, int32_t max_q_len, const void* Qr,

@@ -19,7 +19,8 @@
 // The scan reads each bank row once (H * d * 2 bytes per row in bf16) and does
 // 2 * Lq * H * d flops on it, so it is bound by HBM bandwidth unless Lq is in the
 // hundreds.  Two kernels:
-//  * route_scan_mfma (bf16, queries of >= 16 rows): one wave per routing head.  The wave
+//  * route_scan_mfma (bf16, up to 8 routing heads, any query length): one wave per routing
+//    head, a pass per 64 query rows.  The wave
 //    keeps its head's query rows as MFMA A operands (v_mfma_f32_16x16x32_bf16, rows padded
 //    to 16) and streams 16-row tiles of its head's Kr-bar slice as B operands straight
 //    from HBM into registers through a ring of four tiles (three tiles of loads stay in
@@ -27,9 +28,9 @@
 //    more MFMA chain on the same registers.  The scaled per-head scores meet in LDS (double-buffered, one
 //    barrier per tile) for the head sum and the token max (DPP reductions); row scores
 //    collect in LDS and are folded into documents once per window of rows, by all waves.
-//  * route_scan_dot (any dtype, short queries): each wave streams its own range of rows,
-//    four rows per step with the next four in flight; a lane holds 8 elements of a row,
-//    head sums and the head mean use DPP lane shifts.
+//  * route_scan_dot (float32, or more than 8 routing heads): each wave streams its own
+//    range of rows, four rows per step with the next four in flight; a lane holds 8
+//    elements of a row, head sums and the head mean use DPP lane shifts.
 #include <math.h>
 
 #include <type_traits>
@@ -474,7 +475,9 @@ hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
 
 hipError_t launch_route_scan(const RouteArgs& r, hipStream_t s) {
   ScanK k{r.Qr, r.q_off, r.Krbar, r.chunk_off, r.scores, r.n_chunks, r.n_docs, r.h_r};
-  bool mfma = (r.dtype == 1) && (r.max_q_len >= 16) && (r.h_r <= 8);
+  // bf16: the MFMA scan at any query length (a short query pads its 16-row tile; the
+  // scan stays bound by the bank read and beats the dot-product scan even for one row).
+  bool mfma = (r.dtype == 1) && (r.h_r <= 8);
   if (r.force_path == 1) mfma = false;
   if (r.force_path == 2 && r.dtype == 1 && r.h_r <= 8) mfma = true;
   if (mfma) {
