@@ -41,9 +41,9 @@ SCAN_KERNEL = "route_scan_mfma"
 # HBM traffic of the scan kernel per launch, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # on this workload (scaled by the counters' reading of a copy kernel of known size).  It is
 # reported only while the kernel source still has the digest it was measured with.
-TRAFFIC = {"route_sha": "15dd6d44e0fab8f1",
-           # FETCH_SIZE 1,588,775 KiB per launch x 1.99993 (a 1 GiB copy reads 524,306 KiB)
-           "fetch_bytes": 3253767393,
+TRAFFIC = {"route_sha": "2d598e117809066d",
+           # FETCH_SIZE 1,588,779 KiB per launch x 1.99993 (a 1 GiB copy reads 524,306 KiB)
+           "fetch_bytes": 3253704763,
            # WRITE_SIZE 198.97 KiB per launch x 1.0 (a 1 GiB copy writes 1,048,576 KiB)
            "write_bytes": 203744}
 
@@ -168,6 +168,61 @@ def time_batch(dev, bank, reps=20):
             "routed_bank_tokens_per_s": B * int(np.sum(lens)) / (pct(tot, 50) / 1e3)}
 
 
+def time_banks(dev, reps=50):
+    """Route + attend one 64-token query against the 1M- and 10M-token banks (drawn pooled,
+    everything in HBM).  The 1M bank's routing keys (33 MB) stay in the last-level cache
+    between steps; the 10M bank (325 MB) is timed warm (back to back) and cold (a 1 GiB
+    buffer is rewritten between steps)."""
+    out = {}
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    for name in ("bank1m", "bank10m_needles"):
+        wl = W.workload(name)
+        sh = wl.shape
+        lens = W.doc_lengths(wl)
+        off = W.token_offsets(lens)
+        coff = M.msa_chunk_offsets(off, sh.chunk)
+        N, C, T = len(lens), int(coff[-1]), int(off[-1])
+        Krb, Kb, Vb = W.gen_pooled_bank(wl, coff, dev)
+        coff_d = torch.tensor(coff, device=dev)
+        q = W.gen_queries(wl, dev)
+        Lq = int(q["q_len"][0])
+        q_off = torch.tensor([0, Lq], dtype=torch.int32, device=dev)
+        Qr, Q, Kl, Vl = (q[x][:Lq].contiguous() for x in ("Qr", "Q", "Kloc", "Vloc"))
+        ds = torch.empty((1, N), dtype=torch.float32, device=dev)
+        ids = torch.empty((1, wl.k), dtype=torch.int32, device=dev)
+        sc = torch.empty((1, wl.k), dtype=torch.float32, device=dev)
+        o = torch.empty_like(Q)
+        tws = torch.empty(max(M.msa_topk_workspace(1, N, wl.k), 256), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(M.msa_sparse_attn_workspace(M.MSA_BF16, 1, Lq, Lq, Lq, sh.hq, sh.h_kv, sh.d), 256),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            M.msa_route_scan(Qr, q_off, Lq, Krb, coff_d, out=ds)
+            M.msa_topk(ds, wl.k, out=(ids, sc), workspace=tws)
+            M.msa_sparse_attn(Q, Kl, Vl, q_off, q_off, Lq, ids, coff_d, Kb, Vb, rope_base=sh.rope_base,
+                              out=o, workspace=ws)
+
+        res = {"bank_tokens": T, "bank_rows": C, "documents": N, "krbar_mb": round(C * sh.h_r * sh.d * 2 / 1e6, 1)}
+        for mode in ("warm", "cold") if name != "bank1m" else ("warm",):
+            ms = []
+            for i in range(reps + 3):
+                if mode == "cold":
+                    flush.fill_(i & 255)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                step()
+                e1.record()
+                torch.cuda.synchronize()
+                if i >= 3:
+                    ms.append(e0.elapsed_time(e1))
+            p50 = pct(ms, 50)
+            res[mode] = {"route_attend_p50_ms": round(p50, 4), "routed_bank_tokens_per_s": T / (p50 / 1e3)}
+        out[name] = res
+        del Krb, Kb, Vb
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, lens, off, coff, Krb, Kb, Vb, q, target_s):
     """The oracle, as it stands, on a bounded sample: the first documents of the bank."""
     from threadpoolctl import threadpool_limits
@@ -197,6 +252,7 @@ def cpu_baseline(wl, lens, off, coff, Krb, Kb, Vb, q, target_s):
         t2 = time.perf_counter()
         O.sparse_attn(Q, Kl, Vl, [0, Lq], [0, Lkv], ids_c, coff_c, Kb_s, Vb_s, wl.shape.rope_base)
         t3 = time.perf_counter()
+        run.parts = (t1 - t0, t3 - t2)
         return (t1 - t0) + (t3 - t2), rows
 
     with threadpool_limits(limits=1):
@@ -209,11 +265,33 @@ def cpu_baseline(wl, lens, off, coff, Krb, Kb, Vb, q, target_s):
         rows_target = int(r1 + (target_s - t1) / per_row)
         n_docs = int(min(len(lens), max(1, np.searchsorted(coff, rows_target))))
         t, rows = run(n_docs)
+        t_route, t_attn = run.parts
+        pool = cpu_pool_sample()
     tokens = int(off[n_docs])
     return {"value": tokens / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": (f"first {n_docs} of {len(lens)} documents ({rows} bank rows, {tokens} tokens) "
                        f"of the 100M-token bank: oracle route (scan + top-k) and attention for one "
-                       f"{Lq}-token query, float64 NumPy on one host thread, {t:.1f} s")}
+                       f"{Lq}-token query, float64 NumPy on one host thread, {t:.1f} s"),
+            "route_tokens_per_s": tokens / t_route, "route_s": round(t_route, 3),
+            "attend_s": round(t_attn, 3), "pool": pool}
+
+
+def cpu_pool_sample(n_docs=64):
+    """The oracle's pooling on the first documents of the 10M-token encode workload (token
+    states drawn on the host with the same recipe), in tokens/s."""
+    from oracle import msa_oracle as O
+
+    wl = W.workload("batch32_bank10m")
+    lens = W.doc_lengths(wl)[:n_docs]
+    off = W.token_offsets(lens)
+    K, V, Kr = W.gen_token_states(wl, lens, "cpu")
+    K64, V64, Kr64 = (x.float().double().numpy() for x in (K, V, Kr))
+    t0 = time.perf_counter()
+    O.pool(K64, V64, Kr64, off, wl.shape.chunk, wl.shape.rope_base, O.ROPE_K)
+    t = time.perf_counter() - t0
+    T = int(off[-1])
+    return {"value": T / t, "unit": "tokens/s", "sample": f"first {n_docs} documents ({T} tokens) of "
+            f"the 10M-token encode workload, {t:.1f} s"}
 
 
 def main():
@@ -338,6 +416,10 @@ def main():
                "routed_p90_ms": round(pct(routed, 90), 4), "fixed_ids_p50_ms": round(pct(fixed, 50), 4),
                "routed_bank_tokens_per_s": T / (pct(routed, 50) / 1e3)}
 
+    banks = None
+    if not args.no_pool:
+        log("1M- and 10M-token banks")
+        banks = time_banks(dev)
     pool = batch = None
     if not args.no_pool:
         del qs
@@ -384,6 +466,7 @@ def main():
         "scan_routed_bank_tokens_per_s": T / scan_s,
         "scan_mfma_util": 2.0 * Lq * C * sh.h_r * sh.d / scan_s / 1e12 / MFMA_PEAK_BF16_TFLOPS,
         "decode": dec or None,
+        "banks": banks,
         "pool": pool,
         "batch": batch,
         "cpu_baseline": cpu,
