@@ -19,8 +19,10 @@
 //  * Rotation by in-document position p = s + r (s = first position of the chunk) is split
 //    as R(s) * R(r): each token is rotated by R(r) from a per-workgroup LDS table
 //    (cos/sin of r*theta_i, r < chunk, evaluated in double precision), and R(s) is applied
-//    once to the chunk sum with double-precision angles.  Both are exact rotations, so the
-//    result is the same mean up to float32 rounding.
+//    once to the chunk sum.  R(s) is kept in double precision and advanced by R(chunk) from
+//    chunk to chunk of a document (identity at its start), so every row is computed the
+//    same way whatever range holds it.  Both are rotations, so the result is the same mean
+//    up to float32 rounding.
 //  * The mean divides by the number of real tokens with an IEEE division (a constant chunk
 //    pools to itself bit for bit), then rounds once to the storage type.
 
@@ -194,14 +196,25 @@ __device__ __forceinline__ void pool_stream(const PoolArgs& a, const T* src, T* 
   st.cst = p0;
   st.bnd = min(p0 + a.chunk, st.doc_e);
   st.c = a.chunk_off[doc0] + (p0 - st.doc_s) / a.chunk;
-  // R(s) of the first chunk, and the one-chunk step, in double precision
+  // The one-chunk step rotation, and R(s) of the first chunk reached by that same recurrence
+  // from the document's start, so a row's value does not depend on where ranges begin
+  // (pooling documents in several calls, or with another grid, gives the same bits).
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     st.rc[q] = 1.0; st.rs[q] = 0.0; st.stc[q] = 1.0; st.sts[q] = 0.0;
     if constexpr (rotate) {
       const double th = pow((double)a.rope_base, -2.0 * (double)(i0 + q) / (double)D);
-      sincos((double)(p0 - st.doc_s) * th, &st.rs[q], &st.rc[q]);
       sincos((double)a.chunk * th, &st.sts[q], &st.stc[q]);
+    }
+  }
+  if constexpr (rotate) {
+    for (int64_t j = (p0 - st.doc_s) / a.chunk; j > 0; --j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double c0 = st.rc[q], s0 = st.rs[q];
+        st.rc[q] = c0 * st.stc[q] - s0 * st.sts[q];
+        st.rs[q] = s0 * st.stc[q] + c0 * st.sts[q];
+      }
     }
   }
 

@@ -161,6 +161,44 @@ def test_pool_constant_chunk_bit_exact_and_doc_restart():
     assert torch.equal(Kb[0], Kb[4]) and torch.equal(Vb[0], Vb[4])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pool_append_equals_pool_at_once(dtype):
+    # A bank grown by appending documents (msa_pool on the new documents, writing after the
+    # existing rows) holds the same bits as the bank pooled in one call, and routes the same.
+    say(f"case pool append {dtype}")
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, 900, size=60).astype(np.int64)
+    cut = 23
+    off = W.token_offsets(lens)
+    T = int(off[-1])
+    h, d = 8, 128
+    K = _cpu_randn((T, h, d), 31).to(_dt(dtype)).to(DEV)
+    V = _cpu_randn((T, h, d), 32).to(_dt(dtype)).to(DEV)
+    Kr = _cpu_randn((T, h, d), 33, 1.0).to(_dt(dtype)).to(DEV)
+    coff = M.msa_chunk_offsets(off, 64)
+    C = int(coff[-1])
+    whole = M.msa_pool(K, V, Kr, torch.tensor(off, device=DEV), torch.tensor(coff, device=DEV), C)
+    # first the documents before `cut`, then the rest appended after their rows
+    offA, offB = off[:cut + 1], off[cut:] - off[cut]
+    coffA, coffB = M.msa_chunk_offsets(offA, 64), M.msa_chunk_offsets(offB, 64)
+    CA = int(coffA[-1])
+    bank = tuple(torch.empty_like(x) for x in whole)
+    M.msa_pool(K[:off[cut]], V[:off[cut]], Kr[:off[cut]], torch.tensor(offA, device=DEV),
+               torch.tensor(coffA, device=DEV), CA, out=tuple(x[:CA] for x in bank))
+    tB = slice(int(off[cut]), T)
+    M.msa_pool(K[tB], V[tB], Kr[tB], torch.tensor(offB, device=DEV), torch.tensor(coffB, device=DEV),
+               C - CA, out=tuple(x[CA:] for x in bank))
+    torch.cuda.synchronize()
+    assert np.array_equal(np.concatenate([coffA, CA + coffB[1:]]), coff)
+    for x, y, n in zip(whole, bank, ("Kbar", "Vbar", "Krbar")):
+        assert torch.equal(x, y), f"{dtype} {n}: appended bank differs"
+    if dtype == "bf16":
+        Qr = _cpu_randn((40, h, d), 34).to(torch.bfloat16).to(DEV)
+        a = route(Qr, [40], whole[2], coff, 8)
+        b = route(Qr, [40], bank[2], coff, 8)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+
+
 # ------------------------------------------------------------------------------ routing
 
 def _chunk_counts(n_docs, seed, small_frac=0.4, hi=40):
