@@ -370,6 +370,11 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # bytes the attention reads over the host link: K-bar and V-bar rows of the selected
+    # documents (the last step's selection; the cycled queries select alike)
+    sel = [int(d) for d in ids[0].cpu().numpy() if d >= 0]
+    mem_rows = int(sum(coff[d + 1] - coff[d] for d in sel))
+    host_bytes = mem_rows * sh.h_kv * sh.d * 2 * 2
     scan_ms = [e[0].elapsed_time(e[1]) for e in evs]
     topk_ms = [e[1].elapsed_time(e[2]) for e in evs]
     attn_ms = [e[2].elapsed_time(e[3]) for e in evs]
@@ -463,6 +468,9 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
                      "avg_launch_ms": scan_s * 1e3},
+        "attend_memory": {"rows": mem_rows, "kv_bytes": host_bytes,
+                          "source": "pinned host" if wl.kv_source == "host" else "hbm",
+                          "gbps_at_p50": host_bytes / (pct(attn_ms, 50) / 1e3) / 1e9},
         "scan_routed_bank_tokens_per_s": T / scan_s,
         "scan_mfma_util": 2.0 * Lq * C * sh.h_r * sh.d / scan_s / 1e12 / MFMA_PEAK_BF16_TFLOPS,
         "decode": dec or None,

@@ -41,7 +41,14 @@ those readings are:
   R15 softmax scale 1/sqrt(D), no extras;
   R16 bf16 values are produced by one round-to-nearest-even from float64;
   R25 a query with no tokens scores -inf on every document (the maximum over an empty set
-      of tokens), so its top-k is the k_eff lowest ids.
+      of tokens), so its top-k is the k_eff lowest ids;
+  R26 backward of step D: the gradient of sum(dO * O) through the same computation
+      (softmax, GQA, global RoPE of the local context); memory rows' gradients are summed
+      into bank-shaped arrays over every query that selected them;
+  R27 backward of the router: a document score is one maximum over (query token, bank
+      row), so its gradient reaches only the maximising pair -- the first in row-major
+      order over (bank row, token) -- through that pair's head-mean of cosines; a zero
+      vector has cosine 0 and gets no gradient.
 
 Precision: every computation is float64.  Inputs given as bf16 are decoded exactly.
 """
@@ -65,6 +72,7 @@ __all__ = [
     "head_cosines", "token_chunk_scores", "chunk_scores", "doc_scores_one", "route_doc_scores",
     "topk_docs", "route",
     "assemble_memory", "sparse_attention_one", "sparse_attn",
+    "sparse_attention_backward_one", "sparse_attn_backward", "route_backward",
 ]
 
 
@@ -385,3 +393,127 @@ def sparse_attn(Q, Kloc, Vloc, q_off, kv_off, ids, chunk_off, Kbar, Vbar, base: 
             Q[q_off[b]:q_off[b + 1]], Kloc[kv_off[b]:kv_off[b + 1]],
             Vloc[kv_off[b]:kv_off[b + 1]], Km, Vm, keff, base, scale)
     return out
+
+
+# ---------------------------------------------------------------------------------------
+# Backward of step D and of the router (training: [yeyulingfeng] section 四 -- the
+# language-model loss reaches Q, K/V and Q_r/K_r through the selected memory, and a routing
+# auxiliary loss supervises the document scores; [github-wiki] section 6 item 1 -- the
+# layer stays differentiable end to end).  Readings R26, R27.
+# ---------------------------------------------------------------------------------------
+
+def sparse_attention_backward_one(Q_b, Kloc_b, Vloc_b, Kmem, Vmem, k_eff: int, base: float, dO_b,
+                                  scale: float | None = None):
+    """Gradients of L = sum(dO_b * O_b), O_b = sparse_attention_one(...), with respect to
+    Q_b, Kloc_b, Vloc_b (un-rotated inputs), Kmem and Vmem: a tuple of float64 arrays of
+    their shapes.  Per query head: dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dO O)),
+    dQ~ = scale dS K, dK~ = scale dS^T Q~; the rotations of Q and the local K are undone by
+    rotating the gradient by the negative angle; kv head g sums over its query heads."""
+    Q_b = np.asarray(Q_b, dtype=np.float64)
+    Kl = np.asarray(Kloc_b, dtype=np.float64)
+    Vl = np.asarray(Vloc_b, dtype=np.float64)
+    Km = np.asarray(Kmem, dtype=np.float64)
+    Vm = np.asarray(Vmem, dtype=np.float64)
+    dO = np.asarray(dO_b, dtype=np.float64)
+    Lq, Hq, D = Q_b.shape
+    Lkv, Hkv, _ = Kl.shape
+    M = Km.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    G = Hq // Hkv
+    qpos = k_eff + (Lkv - Lq) + np.arange(Lq)
+    kpos = k_eff + np.arange(Lkv)
+    Qr_ = rope_rotate(Q_b, qpos, base)
+    Klr = rope_rotate(Kl, kpos, base)
+    mask = np.arange(Lkv)[None, :] <= ((Lkv - Lq) + np.arange(Lq))[:, None]
+    dQr = np.zeros_like(Qr_)
+    dKall = np.zeros((M + Lkv, Hkv, D))
+    dVall = np.zeros((M + Lkv, Hkv, D))
+    for hq in range(Hq):
+        g = hq // G
+        keys = np.concatenate([Km[:, g, :], Klr[:, g, :]], axis=0)
+        vals = np.concatenate([Vm[:, g, :], Vl[:, g, :]], axis=0)
+        logits = scale * (Qr_[:, hq, :] @ keys.T)
+        logits[:, M:][~mask] = -np.inf
+        logits -= logits.max(axis=1, keepdims=True)
+        p = np.exp(logits)
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ vals
+        do = dO[:, hq, :]
+        dVall[:, g, :] += p.T @ do
+        dp = do @ vals.T
+        ds = p * (dp - np.sum(do * o, axis=1, keepdims=True))
+        dQr[:, hq, :] = scale * (ds @ keys)
+        dKall[:, g, :] += scale * (ds.T @ Qr_[:, hq, :])
+    dQ = rope_rotate(dQr, -qpos, base)
+    dKl = rope_rotate(dKall[M:], -kpos, base)
+    return dQ, dKl, dVall[M:], dKall[:M], dVall[:M]
+
+
+def sparse_attn_backward(Q, Kloc, Vloc, q_off, kv_off, ids, chunk_off, Kbar, Vbar, base: float, dO,
+                         scale: float | None = None):
+    """Backward of step D for every query: (dQ, dKloc, dVloc, dKbar, dVbar), float64, with
+    dKbar / dVbar shaped like the bank and summed over the queries that selected a row."""
+    q_off = np.asarray(q_off, dtype=np.int64)
+    kv_off = np.asarray(kv_off, dtype=np.int64)
+    coff = np.asarray(chunk_off, dtype=np.int64)
+    ids = np.asarray(ids)
+    dQ = np.zeros(np.asarray(Q).shape)
+    dKl = np.zeros(np.asarray(Kloc).shape)
+    dVl = np.zeros(np.asarray(Vloc).shape)
+    dKb = np.zeros(np.asarray(Kbar).shape)
+    dVb = np.zeros(np.asarray(Vbar).shape)
+    for b in range(len(q_off) - 1):
+        Km, Vm = assemble_memory(ids[b], chunk_off, Kbar, Vbar)
+        keff = int(np.sum(ids[b] >= 0))
+        q0, q1, k0, k1 = q_off[b], q_off[b + 1], kv_off[b], kv_off[b + 1]
+        gq, gk, gv, gkm, gvm = sparse_attention_backward_one(
+            Q[q0:q1], Kloc[k0:k1], Vloc[k0:k1], Km, Vm, keff, base, dO[q0:q1], scale)
+        dQ[q0:q1] = gq
+        dKl[k0:k1] = gk
+        dVl[k0:k1] = gv
+        idx = np.concatenate([np.arange(coff[d], coff[d + 1]) for d in ids[b] if d >= 0]
+                             + [np.zeros(0, dtype=np.int64)])
+        np.add.at(dKb, idx, gkm)
+        np.add.at(dVb, idx, gvm)
+    return dQ, dKl, dVl, dKb, dVb
+
+
+def route_backward(Qr, q_off, Krbar, chunk_off, dD):
+    """Gradients of L = sum(dD * D) with D = route_doc_scores(Qr, q_off, Krbar, chunk_off),
+    with respect to Qr and Krbar (R27): (dQr, dKrbar), float64.  For query b and document d
+    with dD[b, d] != 0, the maximising pair (t*, c*) receives
+        dQr[t*, h]    += dD[b, d] / H * (khat - cos_h qhat) / |q|
+        dKrbar[c*, h] += dD[b, d] / H * (qhat - cos_h khat) / |k|
+    with qhat, khat the unit vectors of Qr[t*, h] and Krbar[c*, h] (no gradient to a zero
+    vector)."""
+    Qr = np.asarray(Qr, dtype=np.float64)
+    Kb = np.asarray(Krbar, dtype=np.float64)
+    q_off = np.asarray(q_off, dtype=np.int64)
+    coff = np.asarray(chunk_off, dtype=np.int64)
+    dD = np.asarray(dD, dtype=np.float64)
+    H = Qr.shape[1]
+    dQr = np.zeros_like(Qr)
+    dKb = np.zeros_like(Kb)
+    for b in range(len(q_off) - 1):
+        Qb = Qr[q_off[b]:q_off[b + 1]]
+        if len(Qb) == 0:
+            continue
+        for d in range(len(coff) - 1):
+            gd = dD[b, d]
+            if gd == 0:
+                continue
+            s = token_chunk_scores(Qb, Kb[coff[d]:coff[d + 1]])        # [T, rows]
+            j = int(np.argmax(s.T))                                     # row-major over (row, t)
+            c = int(coff[d] + j // s.shape[0])
+            t = int(j % s.shape[0])
+            for h in range(H):
+                q, k = Qb[t, h], Kb[c, h]
+                nq, nk = np.linalg.norm(q), np.linalg.norm(k)
+                if nq == 0 or nk == 0:
+                    continue
+                qh, kh = q / nq, k / nk
+                cs = float(qh @ kh)
+                dQr[q_off[b] + t, h] += gd / H * (kh - cs * qh) / nq
+                dKb[c, h] += gd / H * (qh - cs * kh) / nk
+    return dQr, dKb
