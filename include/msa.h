@@ -201,6 +201,41 @@ msa_status msa_sparse_attn(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                            const void* Kbar, const void* Vbar, int32_t kv_source, void* O,
                            void* workspace, size_t workspace_bytes, msa_stream_t stream);
 
+/* Bytes of workspace msa_sparse_attn_backward needs for these sizes (0 if unsupported). */
+size_t msa_sparse_attn_backward_workspace(int64_t total_q, int64_t total_kv, int32_t hq,
+                                          int32_t h_kv, int32_t d);
+
+/*
+ * msa_sparse_attn_backward -- gradients of step D for training (yeyulingfeng.com section
+ * 四: the language-model loss reaches Q, K/V and the routing keys through the selected
+ * memory; github-wiki.com project 250, section 6 item 1: the layer stays differentiable end
+ * to end).  For L = sum(dO * O), O = msa_sparse_attn(...) with the same arguments:
+ *   The first 23 arguments are those of msa_sparse_attn (same meaning, same layout).
+ *   O          [total_q, hq, d]: the forward output for these inputs.
+ *   dO         [total_q, hq, d]: dL/dO.
+ *   dQ         device float [total_q, hq, d], overwritten: dL/dQ (the un-rotated input).
+ *   dKloc      device float [total_kv, h_kv, d], overwritten: dL/dKloc (un-rotated input).
+ *   dVloc      device float [total_kv, h_kv, d], overwritten: dL/dVloc.
+ *   dKbar, dVbar device float [n_chunks, h_kv, d], ADDED TO: the gradients of the selected
+ *              documents' bank rows (rows nobody selected are left as they are); the caller
+ *              zeroes them once.  A row selected by several queries receives the sum of
+ *              their shares; those additions are atomic, so their order (and the last bits
+ *              of such rows) can vary from run to run.  Every other output is deterministic.
+ *   Supported: dtype MSA_BF16; d in {64, 128}; 1 <= k <= 1024.  Products in bf16 on MFMA,
+ *   sums and softmax statistics in float32.  Kbar/Vbar may be pinned host memory
+ *   (kv_source 1); the gradient arrays are device memory.
+ */
+msa_status msa_sparse_attn_backward(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                                    int64_t total_kv, const int32_t* q_off, const int32_t* kv_off,
+                                    int32_t max_q_len, const void* Q, const void* Kloc,
+                                    const void* Vloc, int32_t hq, int32_t h_kv, int32_t d,
+                                    float rope_base, float scale, int32_t k,
+                                    const int32_t* topk_ids, int32_t n_docs, int64_t n_chunks,
+                                    const int64_t* chunk_off, const void* Kbar, const void* Vbar,
+                                    int32_t kv_source, const void* O, const void* dO, float* dQ,
+                                    float* dKloc, float* dVloc, float* dKbar, float* dVbar,
+                                    void* workspace, size_t workspace_bytes, msa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

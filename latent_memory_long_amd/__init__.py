@@ -9,4 +9,5 @@ from .binding import (  # noqa: F401
     msa_chunk_offsets, msa_last_error, msa_pool, msa_route_scan, msa_route_topk,
     msa_route_topk_workspace, msa_topk, msa_topk_workspace,
     msa_sparse_attn, msa_sparse_attn_workspace, msa_status_string, msa_version,
+    msa_sparse_attn_backward, msa_sparse_attn_backward_workspace,
 )

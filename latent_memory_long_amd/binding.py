@@ -53,6 +53,10 @@ def _load() -> ctypes.CDLL:
         "msa_sparse_attn_workspace": (SZ, [ctypes.c_int, I32, I64, I64, I32, I32, I32, I32]),
         "msa_sparse_attn": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, P, P, P, I32, I32,
                                            I32, F, F, I32, P, I32, I64, P, P, P, I32, P, P, SZ, P]),
+        "msa_sparse_attn_backward_workspace": (SZ, [I64, I64, I32, I32, I32]),
+        "msa_sparse_attn_backward": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, P, P, P, I32,
+                                                    I32, I32, F, F, I32, P, I32, I64, P, P, P, I32, P, P,
+                                                    P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -234,3 +238,46 @@ def msa_sparse_attn(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Tensor, q_o
                                _ptr(Vbar), kv_source, _ptr(out), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
     return out
+
+
+def msa_sparse_attn_backward_workspace(total_q: int, total_kv: int, hq: int, h_kv: int, d: int) -> int:
+    return int(lib.msa_sparse_attn_backward_workspace(total_q, total_kv, hq, h_kv, d))
+
+
+def msa_sparse_attn_backward(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Tensor, q_off: torch.Tensor,
+                             kv_off: torch.Tensor, max_q_len: int, topk_ids: torch.Tensor,
+                             chunk_off: torch.Tensor, Kbar: torch.Tensor, Vbar: torch.Tensor,
+                             O: torch.Tensor, dO: torch.Tensor, rope_base: float = 1e6, scale: float = 0.0,
+                             dbank: Optional[tuple] = None, out: Optional[tuple] = None,
+                             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of step D.  Returns (dQ, dKloc, dVloc, dKbar, dVbar), float32.  dKbar / dVbar
+    ([n_chunks, h_kv, d] on the device) are added to: pass `dbank` to accumulate into your
+    own arrays, else zero-filled ones are made."""
+    B = q_off.numel() - 1
+    total_q, hq, d = Q.shape
+    total_kv, h_kv, _ = Kloc.shape
+    k = topk_ids.shape[1]
+    N = chunk_off.numel() - 1
+    C = Kbar.shape[0]
+    kv_source = 0 if Kbar.is_cuda else 1
+    if kv_source == 1 and not (Kbar.is_pinned() and Vbar.is_pinned()):
+        raise MsaError(MSA_ERR_INVALID_ARG, "host-resident Kbar/Vbar must be pinned")
+    dev = Q.device
+    f32 = torch.float32
+    if out is None:
+        out = (torch.empty((total_q, hq, d), dtype=f32, device=dev),
+               torch.empty((total_kv, h_kv, d), dtype=f32, device=dev),
+               torch.empty((total_kv, h_kv, d), dtype=f32, device=dev))
+    if dbank is None:
+        dbank = (torch.zeros((C, h_kv, d), dtype=f32, device=dev), torch.zeros((C, h_kv, d), dtype=f32, device=dev))
+    dQ, dKl, dVl = out
+    dKb, dVb = dbank
+    need = msa_sparse_attn_backward_workspace(total_q, total_kv, hq, h_kv, d)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.msa_sparse_attn_backward(_dtype_code(Q), B, total_q, total_kv, _ptr(q_off), _ptr(kv_off),
+                                        max_q_len, _ptr(Q), _ptr(Kloc), _ptr(Vloc), hq, h_kv, d, rope_base,
+                                        scale, k, _ptr(topk_ids), N, C, _ptr(chunk_off), _ptr(Kbar),
+                                        _ptr(Vbar), kv_source, _ptr(O), _ptr(dO), _ptr(dQ), _ptr(dKl),
+                                        _ptr(dVl), _ptr(dKb), _ptr(dVb), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
+    return dQ, dKl, dVl, dKb, dVb

@@ -195,6 +195,27 @@ msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
   return hip_status(msa::launch_topk(t, topk_ws, s), "msa_route_topk top-k launch");
 }
 
+// The bank's content rows live in page-locked host memory: the device-side aliases.
+static msa_status host_bank_alias(const void* Kbar, const void* Vbar, const void** kb, const void** vb) {
+  const void* host[2] = {Kbar, Vbar};
+  const void* dev[2] = {nullptr, nullptr};
+  for (int i = 0; i < 2; ++i) {
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, host[i]);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return fail(MSA_ERR_INVALID_ARG, "kv_source=1 needs page-locked host memory for %s", i ? "Vbar" : "Kbar");
+    }
+    void* p = nullptr;
+    e = hipHostGetDevicePointer(&p, const_cast<void*>(host[i]), 0);
+    if (e != hipSuccess) return hip_status(e, "hipHostGetDevicePointer");
+    dev[i] = p;
+  }
+  *kb = dev[0];
+  *vb = dev[1];
+  return MSA_OK;
+}
+
 size_t msa_sparse_attn_workspace(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                                  int64_t total_kv, int32_t max_q_len, int32_t hq, int32_t h_kv,
                                  int32_t d) {
@@ -239,29 +260,73 @@ msa_status msa_sparse_attn(msa_dtype dtype, int32_t n_queries, int64_t total_q, 
   const void* kb = Kbar;
   const void* vb = Vbar;
   if (kv_source == 1) {
-    // The bank's content rows live in page-locked host memory: use the device-side alias.
-    const void* host[2] = {Kbar, Vbar};
-    const void* dev[2] = {nullptr, nullptr};
-    for (int i = 0; i < 2; ++i) {
-      hipPointerAttribute_t attr;
-      hipError_t e = hipPointerGetAttributes(&attr, host[i]);
-      if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
-        (void)hipGetLastError();
-        return fail(MSA_ERR_INVALID_ARG, "kv_source=1 needs page-locked host memory for %s", i ? "Vbar" : "Kbar");
-      }
-      void* p = nullptr;
-      e = hipHostGetDevicePointer(&p, const_cast<void*>(host[i]), 0);
-      if (e != hipSuccess) return hip_status(e, "hipHostGetDevicePointer");
-      dev[i] = p;
-    }
-    kb = dev[0];
-    vb = dev[1];
+    const msa_status st = host_bank_alias(Kbar, Vbar, &kb, &vb);
+    if (st != MSA_OK) return st;
   }
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   msa::AttnArgs a{(int)dtype, n_queries, total_q, total_kv, q_off, kv_off, max_q_len, Q, Kloc, Vloc,
                   hq, h_kv, d, rope_base, sc, k, topk_ids, n_docs, n_chunks, chunk_off, kb, vb, O,
                   workspace};
   return hip_status(msa::launch_sparse_attn(a, (hipStream_t)stream), "msa_sparse_attn launch");
+}
+
+size_t msa_sparse_attn_backward_workspace(int64_t total_q, int64_t total_kv, int32_t hq, int32_t h_kv,
+                                          int32_t d) {
+  if (total_q < 0 || total_kv < 0 || hq < 1 || h_kv < 1 || hq % h_kv || (d != 64 && d != 128)) return 0;
+  return msa::attn_bwd_workspace_bytes(total_q, total_kv, hq, h_kv, d);
+}
+
+msa_status msa_sparse_attn_backward(msa_dtype dtype, int32_t n_queries, int64_t total_q, int64_t total_kv,
+                                    const int32_t* q_off, const int32_t* kv_off, int32_t max_q_len,
+                                    const void* Q, const void* Kloc, const void* Vloc, int32_t hq,
+                                    int32_t h_kv, int32_t d, float rope_base, float scale, int32_t k,
+                                    const int32_t* topk_ids, int32_t n_docs, int64_t n_chunks,
+                                    const int64_t* chunk_off, const void* Kbar, const void* Vbar,
+                                    int32_t kv_source, const void* O, const void* dO, float* dQ,
+                                    float* dKloc, float* dVloc, float* dKbar, float* dVbar,
+                                    void* workspace, size_t workspace_bytes, msa_stream_t stream) {
+  g_last_error.clear();
+  if (dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "the backward supports bf16 only (dtype %d)", (int)dtype);
+  if (n_queries < 1 || n_queries > 65535) return fail(MSA_ERR_INVALID_ARG, "n_queries %d not in [1, 65535]", n_queries);
+  if (total_q < 0 || total_q > INT32_MAX || total_kv < total_q || total_kv > INT32_MAX)
+    return fail(MSA_ERR_INVALID_ARG, "need 0 <= total_q <= total_kv < 2^31 (got %lld, %lld)", (long long)total_q, (long long)total_kv);
+  if (max_q_len < 1) return fail(MSA_ERR_INVALID_ARG, "max_q_len must be >= 1 (got %d)", max_q_len);
+  if (!q_off || !kv_off) return fail(MSA_ERR_INVALID_ARG, "null offset array");
+  if (total_q > 0 && (!Q || !O || !dO || !dQ)) return fail(MSA_ERR_INVALID_ARG, "null query-side pointer");
+  if (total_kv > 0 && (!Kloc || !Vloc || !dKloc || !dVloc)) return fail(MSA_ERR_INVALID_ARG, "null local K/V pointer");
+  if (hq < 1 || h_kv < 1) return fail(MSA_ERR_INVALID_ARG, "head counts must be >= 1 (got %d, %d)", hq, h_kv);
+  if (hq % h_kv) return fail(MSA_ERR_INVALID_ARG, "hq (%d) is not a multiple of h_kv (%d)", hq, h_kv);
+  if (d != 64 && d != 128) return fail(MSA_ERR_UNSUPPORTED, "the backward supports head dim 64 or 128 (got %d)", d);
+  if (!(rope_base > 0.f && isfinite(rope_base))) return fail(MSA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  if (!isfinite(scale) || scale < 0.f) return fail(MSA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (k < 1) return fail(MSA_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (k > 1024) return fail(MSA_ERR_UNSUPPORTED, "k %d > 1024", k);
+  if (!topk_ids) return fail(MSA_ERR_INVALID_ARG, "null topk_ids");
+  if (n_docs < 1 || n_chunks < n_docs) return fail(MSA_ERR_INVALID_ARG, "need n_docs >= 1 and n_chunks >= n_docs");
+  if (!chunk_off || !Kbar || !Vbar || !dKbar || !dVbar) return fail(MSA_ERR_INVALID_ARG, "null bank pointer");
+  if (kv_source != 0 && kv_source != 1) return fail(MSA_ERR_INVALID_ARG, "kv_source must be 0 (device) or 1 (pinned host)");
+  const size_t need = msa_sparse_attn_backward_workspace(total_q, total_kv, hq, h_kv, d);
+  if (!workspace || workspace_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const void* kb = Kbar;
+  const void* vb = Vbar;
+  if (kv_source == 1) {
+    const msa_status st = host_bank_alias(Kbar, Vbar, &kb, &vb);
+    if (st != MSA_OK) return st;
+  }
+  msa::AttnBwdArgs a{};
+  a.f = msa::AttnArgs{(int)dtype, n_queries, total_q, total_kv, q_off, kv_off, max_q_len, Q, Kloc, Vloc,
+                      hq, h_kv, d, rope_base, scale, k, topk_ids, n_docs, n_chunks, chunk_off, kb, vb,
+                      nullptr, workspace};
+  a.O = O;
+  a.dO = dO;
+  a.dQ = dQ;
+  a.dKloc = dKloc;
+  a.dVloc = dVloc;
+  a.dKbar = dKbar;
+  a.dVbar = dVbar;
+  a.workspace = workspace;
+  return hip_status(msa::launch_sparse_attn_backward(a, (hipStream_t)stream), "msa_sparse_attn_backward launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,223 @@
+// Pieces shared by the sparse-attention forward (attn.hip) and backward (attn_bwd.hip):
+// the kernel argument block, the global RoPE of the local context, the memory map of a
+// query's selected documents and the staging of 32-key tiles.
+#pragma once
+
+#include <math.h>
+
+#include "common.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int RPW = 4;          // rows per workgroup in rope_local
+constexpr int KT = 32;          // keys per tile
+
+struct AttnK {
+  int n_queries;
+  int64_t total_q, total_kv;
+  const int32_t *q_off, *kv_off;
+  const void *Q, *Kloc, *Vloc;
+  int hq, h_kv;
+  float rope_base, scale_log2;
+  int k;
+  const int32_t* ids;
+  const int64_t* chunk_off;
+  const void *Kbar, *Vbar;
+  void* O;
+  void* Qrot;
+  void* Krot;
+  float* part_o;
+  float* part_ml;
+  int splits;
+};
+
+__device__ __forceinline__ int find_query(const int32_t* off, int n, int64_t row) {
+  int lo = 0, hi = n;  // largest b with off[b] <= row
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int count_valid_ids(const int32_t* ids, int k) {
+  int n = 0;
+  for (int r = 0; r < k; ++r) n += ids[r] >= 0;
+  return n;
+}
+
+// ---- global RoPE of the local context --------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
+  __shared__ float cs_tab[RPW][D / 2], sn_tab[RPW][D / 2];
+  __shared__ int row_q[RPW];
+  __shared__ int64_t row_pos[RPW];
+  const bool is_q = blockIdx.x < (unsigned)nq_blocks;
+  const int64_t r0 = (int64_t)(is_q ? blockIdx.x : blockIdx.x - nq_blocks) * RPW;
+  const int64_t total = is_q ? a.total_q : a.total_kv;
+  const int heads = is_q ? a.hq : a.h_kv;
+  const T* src = (const T*)(is_q ? a.Q : a.Kloc);
+  T* dst = (T*)(is_q ? a.Qrot : a.Krot);
+  const int32_t* off = is_q ? a.q_off : a.kv_off;
+  const int tid = threadIdx.x;
+  if (tid < RPW) {
+    const int64_t r = r0 + tid;
+    int64_t pos = -1;
+    if (r < total) {
+      const int b = find_query(off, a.n_queries, r);
+      const int keff = count_valid_ids(a.ids + (int64_t)b * a.k, a.k);
+      const int64_t Lq = a.q_off[b + 1] - a.q_off[b];
+      const int64_t Lkv = a.kv_off[b + 1] - a.kv_off[b];
+      pos = is_q ? keff + (Lkv - Lq) + (r - off[b]) : keff + (r - off[b]);
+      row_q[tid] = b;
+    }
+    row_pos[tid] = pos;
+  }
+  __syncthreads();
+  for (int e = tid; e < RPW * (D / 2); e += blockDim.x) {
+    const int rr = e / (D / 2), i = e % (D / 2);
+    const double th = pow((double)a.rope_base, -2.0 * (double)i / (double)D);
+    double sn = 0.0, cs = 1.0;
+    if (row_pos[rr] >= 0) sincos((double)row_pos[rr] * th, &sn, &cs);
+    cs_tab[rr][i] = (float)cs;
+    sn_tab[rr][i] = (float)sn;
+  }
+  __syncthreads();
+  const int units = RPW * heads * (D / 8);  // unit = 4 rotation pairs
+  for (int u = tid; u < units; u += blockDim.x) {
+    const int rr = u / (heads * (D / 8));
+    const int rem = u % (heads * (D / 8));
+    const int h = rem / (D / 8), i0 = (rem % (D / 8)) * 4;
+    const int64_t r = r0 + rr;
+    if (r >= total) continue;
+    const T* p = src + (r * heads + h) * D;
+    float lo[4], hi[4], o_lo[4], o_hi[4];
+    Elem<T>::load4(p + i0, lo);
+    Elem<T>::load4(p + i0 + D / 2, hi);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float c = cs_tab[rr][i0 + q], s = sn_tab[rr][i0 + q];
+      o_lo[q] = lo[q] * c - hi[q] * s;
+      o_hi[q] = hi[q] * c + lo[q] * s;
+    }
+    T* o = dst + (r * heads + h) * D;
+    Elem<T>::store4(o + i0, o_lo);
+    Elem<T>::store4(o + i0 + D / 2, o_hi);
+  }
+}
+
+// Memory layout of one query: the selected documents' bank rows in rank order.
+struct MemMap {
+  int keff;
+  int64_t M;
+};
+
+// Fills mstart[r] (first bank row of the r-th valid document) and mpre[r] (its first key
+// index); mpre[keff] = M.  Runs on wave 0; k <= 1024.
+__device__ __forceinline__ MemMap build_memmap(const int32_t* ids, int k, const int64_t* chunk_off,
+                                               int64_t* mstart, int64_t* mpre) {
+  const int lane = threadIdx.x & 63;
+  int64_t run = 0;
+  int keff = 0;
+  for (int r0 = 0; r0 < k; r0 += 64) {
+    const int r = r0 + lane;
+    const int id = (r < k) ? ids[r] : -1;
+    const bool ok = id >= 0;
+    int64_t cnt = 0, st = 0;
+    if (ok) { st = chunk_off[id]; cnt = chunk_off[id + 1] - st; }
+    // exclusive scans of cnt and of ok over the wave
+    int64_t x = cnt;
+    int y = ok ? 1 : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t xo = __shfl_up(x, o);
+      const int yo = __shfl_up(y, o);
+      if (lane >= o) { x += xo; y += yo; }
+    }
+    if (ok) {
+      const int slot = keff + y - 1;
+      mstart[slot] = st;
+      mpre[slot] = run + x - cnt;
+    }
+    run += __shfl(x, 63);
+    keff += __shfl(y, 63);
+  }
+  if (lane == 0) mpre[keff] = run;
+  return {keff, run};
+}
+
+// Staging of one 32-key tile: 16-byte unit u < KT*D/8 is a K unit, the rest V units.
+// Key index -> source row: a bank row of the selected document of rank r (mpre[r] <= key <
+// mpre[r+1]) while key < M, else local row key - M.
+struct TileSrc {
+  const bf16_t *Kb, *Vb, *Kr, *Vl;
+  const int64_t *mstart, *mpre;
+  int keff, hkv, g, kv0;
+  int64_t M, k_hi;
+};
+
+template <int D, int THREADS, int UPT>
+__device__ __forceinline__ void tile_fetch(const TileSrc ts, int tid, int64_t kt, uint4 (&stage)[UPT]) {
+  constexpr int UPR = D / 8;
+  constexpr int UNITS = 2 * KT * UPR;
+#pragma unroll
+  for (int j = 0; j < UPT; ++j) {
+    const int u = tid + j * THREADS;
+    uint4 wv = make_uint4(0, 0, 0, 0);
+    if (u < UNITS) {
+      const bool isv = u >= KT * UPR;
+      const int uu = isv ? u - KT * UPR : u;
+      const int kr = uu / UPR, e0 = (uu % UPR) * 8;
+      const int64_t key = kt + kr;
+      if (key < ts.k_hi) {
+        const bf16_t* p;
+        if (key < ts.M) {
+          int lo = 0, hi = ts.keff;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (ts.mpre[mid] <= key) lo = mid; else hi = mid;
+          }
+          const int64_t brow = ts.mstart[lo] + (key - ts.mpre[lo]);
+          p = (isv ? ts.Vb : ts.Kb) + (brow * ts.hkv + ts.g) * D + e0;
+        } else {
+          const int64_t lrow = ts.kv0 + (key - ts.M);
+          p = (isv ? ts.Vl : ts.Kr) + (lrow * ts.hkv + ts.g) * D + e0;
+        }
+        wv = *reinterpret_cast<const uint4*>(p);
+      }
+    }
+    stage[j] = wv;
+  }
+}
+
+template <int D, int THREADS, int UPT, int KSTR, int VSTR>
+__device__ __forceinline__ void tile_commit(int tid, const uint4 (&stage)[UPT], bf16_t* Ks, bf16_t* Vt) {
+  constexpr int UPR = D / 8;
+  constexpr int UNITS = 2 * KT * UPR;
+#pragma unroll
+  for (int j = 0; j < UPT; ++j) {
+    const int u = tid + j * THREADS;
+    if (u < UNITS) {
+      const bool isv = u >= KT * UPR;
+      const int uu = isv ? u - KT * UPR : u;
+      const int kr = uu / UPR, e0 = (uu % UPR) * 8;
+      if (!isv) {
+        *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = stage[j];
+      } else {
+        const uint32_t w0 = stage[j].x, w1 = stage[j].y, w2 = stage[j].z, w3 = stage[j].w;
+        Vt[(e0 + 0) * VSTR + kr] = (bf16_t)(w0 & 0xffffu);
+        Vt[(e0 + 1) * VSTR + kr] = (bf16_t)(w0 >> 16);
+        Vt[(e0 + 2) * VSTR + kr] = (bf16_t)(w1 & 0xffffu);
+        Vt[(e0 + 3) * VSTR + kr] = (bf16_t)(w1 >> 16);
+        Vt[(e0 + 4) * VSTR + kr] = (bf16_t)(w2 & 0xffffu);
+        Vt[(e0 + 5) * VSTR + kr] = (bf16_t)(w2 >> 16);
+        Vt[(e0 + 6) * VSTR + kr] = (bf16_t)(w3 & 0xffffu);
+        Vt[(e0 + 7) * VSTR + kr] = (bf16_t)(w3 >> 16);
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace msa

@@ -71,6 +71,17 @@ size_t attn_workspace_bytes(int dtype, int n_queries, int64_t total_q, int64_t t
                             int max_q_len, int hq, int h_kv, int d);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
 
+struct AttnBwdArgs {
+  AttnArgs f;        // the forward call's arguments (f.O unused)
+  const void* O;     // forward output
+  const void* dO;    // gradient of the loss with respect to O
+  float *dQ, *dKloc, *dVloc;  // overwritten
+  float *dKbar, *dVbar;       // accumulated
+  void* workspace;
+};
+size_t attn_bwd_workspace_bytes(int64_t total_q, int64_t total_kv, int hq, int h_kv, int d);
+hipError_t launch_sparse_attn_backward(const AttnBwdArgs& a, hipStream_t s);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace msa

@@ -127,9 +127,36 @@ def test_attn_validation(kw, code):
     assert lib.msa_last_error().decode()
 
 
+def _attn_bwd(**kw):
+    a = dict(dtype=1, B=1, tq=64, tkv=64, q_off=FAKE, kv_off=FAKE, maxq=64, Q=FAKE, Kl=FAKE, Vl=FAKE,
+             hq=32, h_kv=8, d=128, base=1e6, scale=0.0, k=16, ids=FAKE, N=10, C=20, coff=FAKE,
+             Kb=FAKE, Vb=FAKE, src=0, O=FAKE, dO=FAKE, dQ=FAKE, dKl=FAKE, dVl=FAKE, dKb=FAKE, dVb=FAKE,
+             ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.msa_sparse_attn_backward(
+        a["dtype"], a["B"], a["tq"], a["tkv"], a["q_off"], a["kv_off"], a["maxq"], a["Q"], a["Kl"], a["Vl"],
+        a["hq"], a["h_kv"], a["d"], a["base"], a["scale"], a["k"], a["ids"], a["N"], a["C"], a["coff"],
+        a["Kb"], a["Vb"], a["src"], a["O"], a["dO"], a["dQ"], a["dKl"], a["dVl"], a["dKb"], a["dVb"],
+        a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(tkv=10), INVALID),
+    (dict(hq=30), INVALID), (dict(k=2048), UNSUPPORTED), (dict(src=2), INVALID),
+    (dict(wsb=100), WORKSPACE), (dict(dO=None), INVALID), (dict(dKb=None), INVALID),
+    (dict(dKl=None), INVALID), (dict(O=None), INVALID), (dict(C=3), INVALID),
+])
+def test_attn_backward_validation(kw, code):
+    assert _attn_bwd(**kw) == code
+    assert lib.msa_last_error().decode()
+
+
 def test_workspace_sizes():
     assert m.msa_route_topk_workspace(1, 47000, 16) >= 47000 * 4
     assert m.msa_route_topk_workspace(0, 10, 1) == 0
     a = m.msa_sparse_attn_workspace(1, 1, 64, 64, 64, 32, 8, 128)
     assert a >= 64 * 32 * 128 * 2 + 64 * 8 * 128 * 2
     assert m.msa_sparse_attn_workspace(1, 1, 64, 64, 64, 30, 8, 128) == 0
+    b = m.msa_sparse_attn_backward_workspace(64, 64, 32, 8, 128)
+    assert b >= 64 * 32 * 128 * 2 + 64 * 8 * 128 * 2 + 2 * 64 * 32 * 4
+    assert m.msa_sparse_attn_backward_workspace(64, 64, 32, 8, 32) == 0
