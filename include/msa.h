@@ -165,6 +165,39 @@ msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                           int32_t* topk_ids, float* topk_scores, float* doc_scores,
                           void* workspace, size_t workspace_bytes, msa_stream_t stream);
 
+/* Bytes of workspace msa_route_backward needs for these sizes (0 if unsupported). */
+size_t msa_route_backward_workspace(int32_t n_queries, int32_t n_docs, int64_t n_chunks,
+                                    int32_t h_r);
+
+/*
+ * msa_route_backward -- gradient of the router for training (yeyulingfeng.com section 四:
+ * an auxiliary routing loss on the document scores, whose gradient reaches the routing
+ * projections through Qr and the pooled routing keys Krbar).  For L = sum(dD * S), S the
+ * document scores msa_route_scan returns for the same arguments:
+ *   The first 12 arguments are those of msa_route_scan (same meaning, same layout).
+ *   dD         device float [n_queries, n_docs]: dL/dS (0 entries cost nothing).
+ *   dQr        device float [total_q, h_r, d], overwritten: dL/dQr.
+ *   dKrbar     device float [n_chunks, h_r, d], ADDED TO (the caller zeroes it once).
+ *   A document score is one maximum, so its gradient reaches one (token, row) pair: the
+ *   first row of the document (in bank order) with the largest row score, then the first
+ *   token (in query order) with the largest score on that row.  For that pair and each
+ *   head h with nonzero vectors q, k and cosine c:
+ *     dQr[t,h] += g/h_r * (k/|k| - c q/|q|) / |q|,  dKrbar[row,h] += g/h_r * (q/|q| - c k/|k|) / |k|.
+ *   Heads with a zero vector get nothing; a query with no tokens gets nothing.  When two
+ *   pairs tie the choice follows the forward kernel's float32 scores, so a near-tie can
+ *   resolve differently from a float64 computation.  Row gradients shared by several
+ *   queries are added atomically (their last bits can vary from run to run).
+ *   workspace  msa_route_backward_workspace() bytes, 256-byte aligned: the scan's document
+ *              and row scores plus one record per (query, document).
+ *   Supported: as msa_route_scan (d in {32, 64, 128}; h_r in [1, 16]).
+ */
+msa_status msa_route_backward(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                              const int32_t* q_off, int32_t max_q_len, const void* Qr,
+                              int32_t h_r, int32_t d, int32_t n_docs, int64_t n_chunks,
+                              const int64_t* chunk_off, const void* Krbar, const float* dD,
+                              float* dQr, float* dKrbar, void* workspace,
+                              size_t workspace_bytes, msa_stream_t stream);
+
 /* Bytes of workspace msa_sparse_attn needs for these sizes. */
 size_t msa_sparse_attn_workspace(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                                  int64_t total_kv, int32_t max_q_len, int32_t hq,

@@ -57,6 +57,9 @@ def _load() -> ctypes.CDLL:
         "msa_sparse_attn_backward": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, P, P, P, I32,
                                                     I32, I32, F, F, I32, P, I32, I64, P, P, P, I32, P, P,
                                                     P, P, P, P, P, P, SZ, P]),
+        "msa_route_backward_workspace": (SZ, [I32, I32, I64, I32]),
+        "msa_route_backward": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
+                                              P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -281,3 +284,30 @@ def msa_sparse_attn_backward(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Te
                                         _ptr(dVl), _ptr(dKb), _ptr(dVb), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)))
     return dQ, dKl, dVl, dKb, dVb
+
+
+def msa_route_backward_workspace(n_queries: int, n_docs: int, n_chunks: int, h_r: int) -> int:
+    return int(lib.msa_route_backward_workspace(n_queries, n_docs, n_chunks, h_r))
+
+
+def msa_route_backward(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar: torch.Tensor,
+                       chunk_off: torch.Tensor, dD: torch.Tensor, dKrbar: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None):
+    """Backward of step B for a loss on the document scores.  dD float32 [B, N] on the
+    device.  Returns (dQr, dKrbar), float32; dKrbar is added to (pass your own array to
+    accumulate, else a zero-filled one is made)."""
+    B = q_off.numel() - 1
+    N = chunk_off.numel() - 1
+    C, h_r, d = Krbar.shape
+    dev = Krbar.device
+    if out is None:
+        out = torch.empty((Qr.shape[0], h_r, d), dtype=torch.float32, device=dev)
+    if dKrbar is None:
+        dKrbar = torch.zeros((C, h_r, d), dtype=torch.float32, device=dev)
+    need = msa_route_backward_workspace(B, N, C, h_r)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.msa_route_backward(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr), h_r,
+                                  d, N, C, _ptr(chunk_off), _ptr(Krbar), _ptr(dD), _ptr(out), _ptr(dKrbar),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out, dKrbar

@@ -195,6 +195,29 @@ msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
   return hip_status(msa::launch_topk(t, topk_ws, s), "msa_route_topk top-k launch");
 }
 
+size_t msa_route_backward_workspace(int32_t n_queries, int32_t n_docs, int64_t n_chunks, int32_t h_r) {
+  if (n_queries < 1 || n_docs < 1 || n_chunks < n_docs || h_r < 1 || h_r > 16) return 0;
+  return msa::route_bwd_workspace_bytes(n_queries, n_docs, n_chunks, h_r);
+}
+
+msa_status msa_route_backward(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                              const int32_t* q_off, int32_t max_q_len, const void* Qr, int32_t h_r,
+                              int32_t d, int32_t n_docs, int64_t n_chunks, const int64_t* chunk_off,
+                              const void* Krbar, const float* dD, float* dQr, float* dKrbar,
+                              void* workspace, size_t workspace_bytes, msa_stream_t stream) {
+  g_last_error.clear();
+  msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
+                              n_chunks, chunk_off, Krbar);
+  if (st != MSA_OK) return st;
+  if (!dD || !dKrbar || (total_q > 0 && !dQr)) return fail(MSA_ERR_INVALID_ARG, "null gradient pointer");
+  const size_t need = msa_route_backward_workspace(n_queries, n_docs, n_chunks, h_r);
+  if (!workspace || workspace_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  msa::RouteBwdArgs r{(int)dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
+                      chunk_off, Krbar, dD, dQr, dKrbar, workspace};
+  return hip_status(msa::launch_route_backward(r, (hipStream_t)stream), "msa_route_backward launch");
+}
+
 // The bank's content rows live in page-locked host memory: the device-side aliases.
 static msa_status host_bank_alias(const void* Kbar, const void* Vbar, const void** kb, const void** vb) {
   const void* host[2] = {Kbar, Vbar};

@@ -35,8 +35,29 @@ struct RouteArgs {
   const void* Krbar;
   float* scores;   // [n_queries, n_docs] output
   int force_path;  // 0 auto, 1 dot, 2 mfma (MSA_ROUTE_PATH environment override)
+  float* row_scores = nullptr;  // [n_queries, n_chunks] or null: per-row max over tokens
 };
 hipError_t launch_route_scan(const RouteArgs& a, hipStream_t s);
+
+struct RouteBwdArgs {
+  int dtype;
+  int n_queries;
+  int64_t total_q;
+  const int32_t* q_off;
+  int max_q_len;
+  const void* Qr;
+  int h_r, d;
+  int n_docs;
+  int64_t n_chunks;
+  const int64_t* chunk_off;
+  const void* Krbar;
+  const float* dD;  // [n_queries, n_docs] gradient of the loss with respect to the scores
+  float* dQr;       // [total_q, h_r, d] overwritten
+  float* dKrbar;    // [n_chunks, h_r, d] added to
+  void* workspace;
+};
+size_t route_bwd_workspace_bytes(int n_queries, int n_docs, int64_t n_chunks, int h_r);
+hipError_t launch_route_backward(const RouteBwdArgs& a, hipStream_t s);
 
 struct TopkArgs {
   int n_queries, n_docs, k;

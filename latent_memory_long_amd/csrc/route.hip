@@ -46,7 +46,8 @@ struct ScanK {
   const int32_t* q_off;
   const void* Krb;
   const int64_t* chunk_off;
-  float* scores;  // [n_queries, n_docs]
+  float* scores;      // [n_queries, n_docs]
+  float* row_scores;  // [n_queries, n_chunks] or null: max over the query's tokens per bank row
   int64_t n_chunks;
   int n_docs;
   int H;
@@ -212,6 +213,9 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
       }
       __syncthreads();
     }
+
+    if (a.row_scores)
+      for (int i = tid; i < wn; i += nthr) a.row_scores[(int64_t)b * a.n_chunks + w0 + i] = sc_all[i];
 
     // ---- fold the window's row scores into documents, all waves in parallel ----
     const int cin = (int)(wi & 1), cout = cin ^ 1;
@@ -394,6 +398,10 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
             best = fmaxf(best, (float)contrib);
           }
           best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 63));
+          if (a.row_scores && lane == 0) {
+            float* rsc = a.row_scores + (int64_t)b * a.n_chunks + c;
+            *rsc = FIRST ? best : fmaxf(best, *rsc);
+          }
           // fold into documents (wave-uniform control flow)
           while (c >= nb) {
             emit(cur, run);
@@ -474,7 +482,7 @@ hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_route_scan(const RouteArgs& r, hipStream_t s) {
-  ScanK k{r.Qr, r.q_off, r.Krbar, r.chunk_off, r.scores, r.n_chunks, r.n_docs, r.h_r};
+  ScanK k{r.Qr, r.q_off, r.Krbar, r.chunk_off, r.scores, r.row_scores, r.n_chunks, r.n_docs, r.h_r};
   // bf16: the MFMA scan at any query length (a short query pads its 16-row tile; the
   // scan stays bound by the bank read and beats the dot-product scan even for one row).
   bool mfma = (r.dtype == 1) && (r.h_r <= 8);

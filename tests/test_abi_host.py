@@ -151,6 +151,26 @@ def test_attn_backward_validation(kw, code):
     assert lib.msa_last_error().decode()
 
 
+def _route_bwd(**kw):
+    a = dict(dtype=1, B=2, tq=8, q_off=FAKE, maxq=4, Qr=FAKE, h_r=4, d=128, N=10, C=20, coff=FAKE,
+             Krb=FAKE, dD=FAKE, dQr=FAKE, dKrb=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.msa_route_backward(a["dtype"], a["B"], a["tq"], a["q_off"], a["maxq"], a["Qr"], a["h_r"], a["d"],
+                                  a["N"], a["C"], a["coff"], a["Krb"], a["dD"], a["dQr"], a["dKrb"], a["ws"],
+                                  a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), UNSUPPORTED), (dict(h_r=17), UNSUPPORTED), (dict(d=100), UNSUPPORTED),
+    (dict(C=3), INVALID), (dict(B=0), INVALID), (dict(maxq=0), INVALID), (dict(dD=None), INVALID),
+    (dict(dKrb=None), INVALID), (dict(dQr=None), INVALID), (dict(wsb=100), WORKSPACE),
+    (dict(ws=None), WORKSPACE), (dict(ws=ctypes.c_void_p(0x1010)), INVALID),
+])
+def test_route_backward_validation(kw, code):
+    assert _route_bwd(**kw) == code
+    assert lib.msa_last_error().decode()
+
+
 def test_workspace_sizes():
     assert m.msa_route_topk_workspace(1, 47000, 16) >= 47000 * 4
     assert m.msa_route_topk_workspace(0, 10, 1) == 0
@@ -160,3 +180,6 @@ def test_workspace_sizes():
     b = m.msa_sparse_attn_backward_workspace(64, 64, 32, 8, 128)
     assert b >= 64 * 32 * 128 * 2 + 64 * 8 * 128 * 2 + 2 * 64 * 32 * 4
     assert m.msa_sparse_attn_backward_workspace(64, 64, 32, 8, 32) == 0
+    c = m.msa_route_backward_workspace(2, 10, 20, 4)
+    assert c >= 2 * 10 * 4 + 2 * 20 * 4 + 2 * 10 * (4 + 8) + 2 * 2 * 10 * 4 * 4
+    assert m.msa_route_backward_workspace(2, 10, 5, 4) == 0 and m.msa_route_backward_workspace(2, 10, 20, 17) == 0
