@@ -160,12 +160,60 @@ def time_batch(dev, bank, reps=20):
     # algorithmic scan flops: one dot product of D per (query token, bank row, routing head)
     flops = 2.0 * tq * C * sh.h_r * sh.d
     t_scan = float(np.mean(scan)) / 1e3
-    return {"workload": "batch32_bank10m (route + attend)", "queries": B, "query_tokens": tq,
-            "k": wl.k, "bank_rows": C, "route_attend_p50_ms": round(pct(tot, 50), 4),
-            "scan_p50_ms": round(pct(scan, 50), 4), "topk_p50_ms": round(pct(topk, 50), 4),
-            "attend_p50_ms": round(pct(attn, 50), 4), "scan_tflops": flops / t_scan / 1e12,
-            "scan_mfma_util": flops / t_scan / 1e12 / MFMA_PEAK_BF16_TFLOPS,
-            "routed_bank_tokens_per_s": B * int(np.sum(lens)) / (pct(tot, 50) / 1e3)}
+    fig = {"workload": "batch32_bank10m (route + attend)", "queries": B, "query_tokens": tq,
+           "k": wl.k, "bank_rows": C, "route_attend_p50_ms": round(pct(tot, 50), 4),
+           "scan_p50_ms": round(pct(scan, 50), 4), "topk_p50_ms": round(pct(topk, 50), 4),
+           "attend_p50_ms": round(pct(attn, 50), 4), "scan_tflops": flops / t_scan / 1e12,
+           "scan_mfma_util": flops / t_scan / 1e12 / MFMA_PEAK_BF16_TFLOPS,
+           "routed_bank_tokens_per_s": B * int(np.sum(lens)) / (pct(tot, 50) / 1e3)}
+
+    # ---- training step of the same batch: the attention's and the router's backward ----
+    dO = torch.randn(Q.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
+                     dtype=torch.float32).to(torch.bfloat16)
+    dD = torch.randn((B, N), generator=torch.Generator(device=dev).manual_seed(8), device=dev)
+    f32 = torch.float32
+    gq = (torch.empty(Q.shape, dtype=f32, device=dev), torch.empty(Kl.shape, dtype=f32, device=dev),
+          torch.empty(Vl.shape, dtype=f32, device=dev))
+    gb = (torch.zeros((C, sh.h_kv, sh.d), dtype=f32, device=dev), torch.zeros((C, sh.h_kv, sh.d), dtype=f32, device=dev))
+    bws = torch.empty(max(M.msa_sparse_attn_backward_workspace(tq, tq, sh.hq, sh.h_kv, sh.d), 256),
+                      dtype=torch.uint8, device=dev)
+    dQr = torch.empty(Qr.shape, dtype=f32, device=dev)
+    dKr = torch.zeros(Krb.shape, dtype=f32, device=dev)
+    rws = torch.empty(max(M.msa_route_backward_workspace(B, N, C, sh.h_r), 256), dtype=torch.uint8, device=dev)
+
+    def run_bwd(ev):
+        ev[0].record()
+        M.msa_sparse_attn_backward(Q, Kl, Vl, q_off_d, q_off_d, Lmax, ids, coff_d, Kb, Vb, out, dO,
+                                   rope_base=sh.rope_base, dbank=gb, out=gq, workspace=bws)
+        ev[1].record()
+        M.msa_route_backward(Qr, q_off_d, Lmax, Krb, coff_d, dD, dKrbar=dKr, out=dQr, workspace=rws)
+        ev[2].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 2)]
+    for e in evs:
+        run_bwd(e)
+    torch.cuda.synchronize()
+    evs = evs[2:]
+    abwd = [e[0].elapsed_time(e[1]) for e in evs]
+    rbwd = [e[1].elapsed_time(e[2]) for e in evs]
+    # algorithmic attention flops: (query, key) pairs x heads x d, 4 per pair forward and
+    # 10 per pair backward (S recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q)
+    sel = ids.cpu().numpy()
+    pairs = 0
+    for b in range(B):
+        m = int(sum(coff[d + 1] - coff[d] for d in sel[b] if d >= 0))
+        L = int(q_len[b])
+        pairs += L * m + L * (L + 1) // 2
+    bflops = 10.0 * pairs * sh.hq * sh.d
+    t_abwd = pct(abwd, 50) / 1e3
+    bwd = {"workload": "batch32_bank10m (training backward)", "attend_pairs": pairs,
+           "attend_backward_p50_ms": round(pct(abwd, 50), 4),
+           "attend_backward_tflops": bflops / t_abwd / 1e12,
+           "attend_backward_mfma_util": bflops / t_abwd / 1e12 / MFMA_PEAK_BF16_TFLOPS,
+           "attend_forward_tflops": 0.4 * bflops / (pct(attn, 50) / 1e3) / 1e12,
+           "route_backward_p50_ms": round(pct(rbwd, 50), 4),
+           "route_backward_over_scan": pct(rbwd, 50) / pct(scan, 50)}
+    return fig, bwd
 
 
 def time_banks(dev, reps=50):
@@ -425,14 +473,14 @@ def main():
     if not args.no_pool:
         log("1M- and 10M-token banks")
         banks = time_banks(dev)
-    pool = batch = None
+    pool = batch = backward = None
     if not args.no_pool:
         del qs
         torch.cuda.empty_cache()
         log("pool on the 10M-token encode workload")
         pool, bank10m = time_pool(dev)
-        log("batched route + attend: 32 queries against the pooled 10M-token bank")
-        batch = time_batch(dev, bank10m)
+        log("batched route + attend and its backward: 32 queries against the pooled 10M-token bank")
+        batch, backward = time_batch(dev, bank10m)
         del bank10m
         torch.cuda.empty_cache()
 
@@ -477,6 +525,7 @@ def main():
         "banks": banks,
         "pool": pool,
         "batch": batch,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -36,6 +36,7 @@ struct RouteArgs {
   float* scores;   // [n_queries, n_docs] output
   int force_path;  // 0 auto, 1 dot, 2 mfma (MSA_ROUTE_PATH environment override)
   float* row_scores = nullptr;  // [n_queries, n_chunks] or null: per-row max over tokens
+  int32_t* row_arg = nullptr;   // with row_scores: the first token reaching each row's max
 };
 hipError_t launch_route_scan(const RouteArgs& a, hipStream_t s);
 

@@ -48,6 +48,7 @@ struct ScanK {
   const int64_t* chunk_off;
   float* scores;      // [n_queries, n_docs]
   float* row_scores;  // [n_queries, n_chunks] or null: max over the query's tokens per bank row
+  int32_t* row_arg;   // [n_queries, n_chunks], with row_scores: the first token reaching it
   int64_t n_chunks;
   int n_docs;
   int H;
@@ -64,7 +65,9 @@ __device__ __forceinline__ int64_t load_window(const int64_t* chunk_off, int n_d
 constexpr int WIN = 4096;  // rows whose scores are held in LDS before folding into documents
 constexpr int RING = 4;    // register tile buffers per wave
 
-template <int MT, int D>
+// ARG: also write every row's score and the first query token reaching it (row_scores,
+// row_arg), for the router's backward; the forward instantiation carries none of it.
+template <int MT, int D, bool ARG>
 __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
   constexpr int KK = D / 32;          // 32-wide k steps per head
   constexpr int ROWS = MT * 16;       // query rows per block
@@ -72,6 +75,7 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
   __shared__ float red[2][8][16][STRIDE];
   __shared__ float4 csq[2][16][2];  // 1/|Kr-bar[c, h]| of the tile, [buf][c][h / 4]
   __shared__ float sc_all[WIN];
+  __shared__ int arg_all[ARG ? WIN : 1];
   __shared__ float carry[2];
 
   const int H = a.H;
@@ -178,6 +182,7 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
           const int idx = base + tid;
           const int c = idx >> 5, j = idx & 31;
           float s = -INFINITY;
+          int ri = 2 * j;  // ARG: the lane's first maximising row
           if (2 * j < rows) {
             const float* csc = reinterpret_cast<const float*>(&csq[buf][c][0]);
             float s0 = 0.f, s1 = 0.f;
@@ -188,11 +193,31 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
               s1 += v.y * ch;
             }
             s = (2 * j + 1 < rows) ? fmaxf(s0, s1) : s0;
+            if (ARG && 2 * j + 1 < rows && s1 > s0) ri = 2 * j + 1;
           }
-          s = half_max_last(s);
-          if ((lane & 31) == 31) {
-            const int64_t ci = t * 16 + c;
-            if (ci < wn) sc_all[ci] = fmaxf(sc_all[ci], s);
+          if constexpr (ARG) {
+            // the column's max, then the lowest lane (lowest rows) holding it
+            const float sl = s;
+            s = half_max_last(s);
+            const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 31));
+            const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
+            const uint64_t hit = __ballot(sl == ((lane < 32) ? mx : mh));
+            const uint32_t half = (lane < 32) ? (uint32_t)hit : (uint32_t)(hit >> 32);
+            const int src = (lane & 32) + (half ? __builtin_ctz(half) : 0);
+            const int rfirst = __shfl(ri, src, 64);
+            if ((lane & 31) == 31) {
+              const int64_t ci = t * 16 + c;
+              if (ci < wn && s > sc_all[ci]) {  // strictly greater: an earlier block keeps a tie
+                sc_all[ci] = s;
+                arg_all[ci] = rb + rfirst;
+              }
+            }
+          } else {
+            s = half_max_last(s);
+            if ((lane & 31) == 31) {
+              const int64_t ci = t * 16 + c;
+              if (ci < wn) sc_all[ci] = fmaxf(sc_all[ci], s);
+            }
           }
         }
       };
@@ -214,8 +239,12 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
       __syncthreads();
     }
 
-    if (a.row_scores)
-      for (int i = tid; i < wn; i += nthr) a.row_scores[(int64_t)b * a.n_chunks + w0 + i] = sc_all[i];
+    if constexpr (ARG) {
+      for (int i = tid; i < wn; i += nthr) {
+        a.row_scores[(int64_t)b * a.n_chunks + w0 + i] = sc_all[i];
+        a.row_arg[(int64_t)b * a.n_chunks + w0 + i] = arg_all[i];
+      }
+    }
 
     // ---- fold the window's row scores into documents, all waves in parallel ----
     const int cin = (int)(wi & 1), cout = cin ^ 1;
@@ -383,6 +412,7 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
             cs[p] = (head_last && ss > 0) ? (acc_t)1 / sqrt(ss) : (acc_t)0;
           }
           float best = -INFINITY;
+          int arg = 0;  // first maximising token (lane 63)
           for (int t = 0; t < nt; ++t) {
             acc_t contrib = 0;
 #pragma unroll
@@ -395,12 +425,19 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
               }
             }
             contrib = wave_sum_last(contrib);
+            if ((float)contrib > best) arg = t;
             best = fmaxf(best, (float)contrib);
           }
           best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 63));
-          if (a.row_scores && lane == 0) {
-            float* rsc = a.row_scores + (int64_t)b * a.n_chunks + c;
-            *rsc = FIRST ? best : fmaxf(best, *rsc);
+          if (a.row_scores) {
+            arg = __builtin_amdgcn_readlane(arg, 63);
+            if (lane == 0) {
+              float* rsc = a.row_scores + (int64_t)b * a.n_chunks + c;
+              if (FIRST || best > *rsc) {  // an earlier token block keeps a tie
+                *rsc = best;
+                a.row_arg[(int64_t)b * a.n_chunks + c] = tb + arg;
+              }
+            }
           }
           // fold into documents (wave-uniform control flow)
           while (c >= nb) {
@@ -455,11 +492,20 @@ hipError_t launch_mfma(const RouteArgs& r, const ScanK& k, hipStream_t s) {
   // about two workgroups per CU in turn: one 8-wave workgroup fits a CU at a time
   dim3 grid((unsigned)route_parts(r.n_chunks, 64, 512, r.n_queries), (unsigned)r.n_queries);
   dim3 block(64 * r.h_r);
+  if (k.row_scores) {
+    switch (mt) {
+      case 1: hipLaunchKernelGGL((route_scan_mfma<1, D, true>), grid, block, 0, s, k); break;
+      case 2: hipLaunchKernelGGL((route_scan_mfma<2, D, true>), grid, block, 0, s, k); break;
+      case 3: hipLaunchKernelGGL((route_scan_mfma<3, D, true>), grid, block, 0, s, k); break;
+      default: hipLaunchKernelGGL((route_scan_mfma<4, D, true>), grid, block, 0, s, k); break;
+    }
+    return hipGetLastError();
+  }
   switch (mt) {
-    case 1: hipLaunchKernelGGL((route_scan_mfma<1, D>), grid, block, 0, s, k); break;
-    case 2: hipLaunchKernelGGL((route_scan_mfma<2, D>), grid, block, 0, s, k); break;
-    case 3: hipLaunchKernelGGL((route_scan_mfma<3, D>), grid, block, 0, s, k); break;
-    default: hipLaunchKernelGGL((route_scan_mfma<4, D>), grid, block, 0, s, k); break;
+    case 1: hipLaunchKernelGGL((route_scan_mfma<1, D, false>), grid, block, 0, s, k); break;
+    case 2: hipLaunchKernelGGL((route_scan_mfma<2, D, false>), grid, block, 0, s, k); break;
+    case 3: hipLaunchKernelGGL((route_scan_mfma<3, D, false>), grid, block, 0, s, k); break;
+    default: hipLaunchKernelGGL((route_scan_mfma<4, D, false>), grid, block, 0, s, k); break;
   }
   return hipGetLastError();
 }
@@ -482,7 +528,7 @@ hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_route_scan(const RouteArgs& r, hipStream_t s) {
-  ScanK k{r.Qr, r.q_off, r.Krbar, r.chunk_off, r.scores, r.row_scores, r.n_chunks, r.n_docs, r.h_r};
+  ScanK k{r.Qr, r.q_off, r.Krbar, r.chunk_off, r.scores, r.row_scores, r.row_arg, r.n_chunks, r.n_docs, r.h_r};
   // bf16: the MFMA scan at any query length (a short query pads its 16-row tile; the
   // scan stays bound by the bank read and beats the dot-product scan even for one row).
   bool mfma = (r.dtype == 1) && (r.h_r <= 8);

@@ -10,10 +10,11 @@
 // (no gradient for a head whose query or key vector is zero).
 //
 // Kernels:
-//  * the forward scan (route.hip), writing each bank row's max over the query's tokens;
-//  * route_bwd_pair: one wave per (query, document): the maximising row, the maximising
-//    token on it, the key gradient (added atomically: a row can be the maximiser for several
-//    queries), and a record (t*, row, per-head cosine and 1/|k|) for the query gradient;
+//  * the forward scan (route.hip), writing each bank row's max over the query's tokens and
+//    the first token reaching it;
+//  * route_bwd_pair: one wave per (query, document): the maximising row, its token, the key
+//    gradient (added atomically: a row can be the maximiser for several queries), and a
+//    record (t*, row, per-head cosine and 1/|k|) for the query gradient;
 //  * route_bwd_dq: one workgroup per (query, token) (strided when a query is longer than the
 //    grid): gathers the records that name the
 //    token (filtered a block of documents at a time through LDS) and writes its gradient
@@ -33,6 +34,7 @@ struct RouteBwdK {
   const int64_t* chunk_off;
   const float* dD;          // [B, N]
   const float* row_scores;  // [B, C]
+  const int32_t* row_arg;   // [B, C]
   float* dQr;               // [total_q, H, D]
   float* dKrb;              // [C, H, D], added to
   int32_t* tstar;           // [B, N]: maximising token (query-local), -1 if no gradient
@@ -58,12 +60,13 @@ __global__ __launch_bounds__(256) void route_bwd_pair(RouteBwdK a) {
   const float gd = a.dD[rec];
   const int64_t c0 = a.chunk_off[d];
   const int nc = (int)(a.chunk_off[d + 1] - c0);
+  const float* rs = a.row_scores + (int64_t)b * a.n_chunks + c0;
   // maximising row: the first with the largest row score
   float best = -INFINITY;
   int bc = nc;
   if (gd != 0.f && Lq > 0) {
     for (int c = lane; c < nc; c += 64) {
-      const float v = a.row_scores[(int64_t)b * a.n_chunks + c0 + c];
+      const float v = rs[c];
       if (v > best) { best = v; bc = c; }  // c ascending: a tie keeps the first
     }
   }
@@ -79,64 +82,29 @@ __global__ __launch_bounds__(256) void route_bwd_pair(RouteBwdK a) {
   }
   const int H = a.H;
   const int64_t cs = c0 + bc;
-  const T* Q = (const T*)a.Qr;
-  const T* K = (const T*)a.Krb + cs * H * D;
-  // the row's squared key norms, per head, known to every lane
-  float kn2[16];
-  for (int h = 0; h < H; ++h) {
-    float acc = 0.f;
-    for (int e = lane; e < D; e += 64) {
-      const float x = ld(K, h * D + e);
-      acc += x * x;
-    }
-    kn2[h] = wave_sum(acc);
-  }
-  // maximising token on that row: lanes take tokens, the first with the largest score wins
-  float tb = -INFINITY;
-  int tt = Lq;
-  for (int t = lane; t < Lq; t += 64) {
-    const T* q = Q + (int64_t)(q0 + t) * H * D;
-    float s = 0.f;
-    for (int h = 0; h < H; ++h) {
-      float dot = 0.f, qn = 0.f;
-      for (int e = 0; e < D; ++e) {
-        const float x = ld(q, h * D + e);
-        dot += x * ld(K, h * D + e);
-        qn += x * x;
-      }
-      if (qn > 0.f && kn2[h] > 0.f) s += dot / (sqrtf(qn) * sqrtf(kn2[h]));
-    }
-    if (s > tb) { tb = s; tt = t; }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(tb, o, 64);
-    const int ot = __shfl_xor(tt, o, 64);
-    if (ov > tb || (ov == tb && ot < tt)) { tb = ov; tt = ot; }
-  }
-  if (tt >= Lq) {  // no finite token score (non-finite inputs)
-    if (lane == 0) a.tstar[rec] = -1;
-    return;
-  }
-  // gradient of the pair, head by head, lanes over elements
-  const T* q = Q + (int64_t)(q0 + tt) * H * D;
+  const int ts = a.row_arg[(int64_t)b * a.n_chunks + cs];  // the scan's first maximising token
+  const T* q = (const T*)a.Qr + (int64_t)(q0 + ts) * H * D;
+  const T* k = (const T*)a.Krb + cs * H * D;
   float* dk = a.dKrb + cs * H * D;
   const float gH = gd / (float)H;
+  // gradient of the pair, head by head, lanes over elements
   for (int h = 0; h < H; ++h) {
-    float dot = 0.f, qn = 0.f;
+    float dot = 0.f, qn = 0.f, kn = 0.f;
     for (int e = lane; e < D; e += 64) {
-      const float x = ld(q, h * D + e);
-      dot += x * ld(K, h * D + e);
+      const float x = ld(q, h * D + e), y = ld(k, h * D + e);
+      dot += x * y;
       qn += x * x;
+      kn += y * y;
     }
     dot = wave_sum(dot);
     qn = wave_sum(qn);
-    const bool ok = qn > 0.f && kn2[h] > 0.f;
-    const float iq = ok ? 1.f / sqrtf(qn) : 0.f, ik = ok ? 1.f / sqrtf(kn2[h]) : 0.f;
+    kn = wave_sum(kn);
+    const bool ok = qn > 0.f && kn > 0.f;
+    const float iq = ok ? 1.f / sqrtf(qn) : 0.f, ik = ok ? 1.f / sqrtf(kn) : 0.f;
     const float cosv = dot * iq * ik;
     if (ok) {
       for (int e = lane; e < D; e += 64)
-        atomicAdd(dk + h * D + e, gH * (ld(q, h * D + e) * iq - cosv * ld(K, h * D + e) * ik) * ik);
+        atomicAdd(dk + h * D + e, gH * (ld(q, h * D + e) * iq - cosv * ld(k, h * D + e) * ik) * ik);
     }
     if (lane == 0) {
       a.cosv[rec * H + h] = cosv;
@@ -144,24 +112,24 @@ __global__ __launch_bounds__(256) void route_bwd_pair(RouteBwdK a) {
     }
   }
   if (lane == 0) {
-    a.tstar[rec] = tt;
+    a.tstar[rec] = ts;
     a.cstar[rec] = cs;
   }
 }
 
 constexpr int DQ_THREADS = 256;
-constexpr int DQ_BLOCK = 256;  // documents filtered per step in route_bwd_dq
+constexpr int DQ_BLOCK = DQ_THREADS;  // documents filtered per step in route_bwd_dq
 
 template <typename T, int D>
 __global__ __launch_bounds__(DQ_THREADS) void route_bwd_dq(RouteBwdK a) {
   constexpr int EPT = (16 * D) / DQ_THREADS;  // elements per thread at the largest head count
   __shared__ int match[DQ_BLOCK];
-  __shared__ int n_match;
+  __shared__ int wave_hits[DQ_THREADS / 64];
   __shared__ float qn_s[16];
   const int b = blockIdx.y;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int H = a.H, n_el = H * D;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int t = blockIdx.x; t < Lq; t += gridDim.x) {
     const T* q = (const T*)a.Qr + (int64_t)(q0 + t) * n_el;
     const T* K = (const T*)a.Krb;
@@ -178,11 +146,21 @@ __global__ __launch_bounds__(DQ_THREADS) void route_bwd_dq(RouteBwdK a) {
     for (int j = 0; j < EPT; ++j) acc1[j] = acc2[j] = 0.f;
     const int32_t* ts = a.tstar + (int64_t)b * a.n_docs;
     for (int d0 = 0; d0 < a.n_docs; d0 += DQ_BLOCK) {
-      if (tid == 0) n_match = 0;
+      // the block's documents whose maximum sits on token t, listed in document order
+      // (a fixed summation order: the result does not depend on scheduling)
+      const int dd = d0 + tid;
+      const bool hit = dd < a.n_docs && ts[dd] == t;
+      const uint64_t bal = __ballot(hit);
+      if (lane == 0) wave_hits[wv] = __popcll(bal);
       __syncthreads();
-      if (tid < DQ_BLOCK && d0 + tid < a.n_docs && ts[d0 + tid] == t) match[atomicAdd(&n_match, 1)] = d0 + tid;
+      int base = 0, nm = 0;
+#pragma unroll
+      for (int i = 0; i < DQ_THREADS / 64; ++i) {
+        base += (i < wv) ? wave_hits[i] : 0;
+        nm += wave_hits[i];
+      }
+      if (hit) match[base + __popcll(bal & ((1ull << lane) - 1))] = dd;
       __syncthreads();
-      const int nm = n_match;
       for (int m = 0; m < nm; ++m) {
         const int64_t rec = (int64_t)b * a.n_docs + match[m];
         const float g = a.dD[rec];
@@ -230,7 +208,7 @@ hipError_t launch_t(const RouteBwdArgs& r, const RouteBwdK& k, hipStream_t s) {
 
 size_t route_bwd_workspace_bytes(int n_queries, int n_docs, int64_t n_chunks, int h_r) {
   const size_t bn = (size_t)n_queries * n_docs;
-  return align256(bn * 4) + align256((size_t)n_queries * n_chunks * 4) + align256(bn * 4) +
+  return align256(bn * 4) + 2 * align256((size_t)n_queries * n_chunks * 4) + align256(bn * 4) +
          align256(bn * 8) + 2 * align256(bn * h_r * 4);
 }
 
@@ -240,6 +218,8 @@ hipError_t launch_route_backward(const RouteBwdArgs& r, hipStream_t s) {
   float* scores = (float*)ws;
   ws += align256(bn * 4);
   float* rows = (float*)ws;
+  ws += align256((size_t)r.n_queries * r.n_chunks * 4);
+  int32_t* rarg = (int32_t*)ws;
   ws += align256((size_t)r.n_queries * r.n_chunks * 4);
   RouteBwdK k{};
   k.tstar = (int32_t*)ws;
@@ -253,6 +233,7 @@ hipError_t launch_route_backward(const RouteBwdArgs& r, hipStream_t s) {
   RouteArgs f{r.dtype, r.n_queries, r.total_q, r.q_off, r.max_q_len, r.Qr, r.h_r, r.d, r.n_docs,
               r.n_chunks, r.chunk_off, r.Krbar, scores, 0};
   f.row_scores = rows;
+  f.row_arg = rarg;
   hipError_t e = launch_route_scan(f, s);
   if (e != hipSuccess) return e;
   k.Qr = r.Qr;
@@ -261,6 +242,7 @@ hipError_t launch_route_backward(const RouteBwdArgs& r, hipStream_t s) {
   k.chunk_off = r.chunk_off;
   k.dD = r.dD;
   k.row_scores = rows;
+  k.row_arg = rarg;
   k.dQr = r.dQr;
   k.dKrb = r.dKrbar;
   k.n_chunks = r.n_chunks;

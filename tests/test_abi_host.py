@@ -181,5 +181,5 @@ def test_workspace_sizes():
     assert b >= 64 * 32 * 128 * 2 + 64 * 8 * 128 * 2 + 2 * 64 * 32 * 4
     assert m.msa_sparse_attn_backward_workspace(64, 64, 32, 8, 32) == 0
     c = m.msa_route_backward_workspace(2, 10, 20, 4)
-    assert c >= 2 * 10 * 4 + 2 * 20 * 4 + 2 * 10 * (4 + 8) + 2 * 2 * 10 * 4 * 4
+    assert c >= 2 * 10 * 4 + 2 * 2 * 20 * 4 + 2 * 10 * (4 + 8) + 2 * 2 * 10 * 4 * 4
     assert m.msa_route_backward_workspace(2, 10, 5, 4) == 0 and m.msa_route_backward_workspace(2, 10, 20, 17) == 0
