@@ -12,8 +12,9 @@ Sources (the web pages this project is built from; cited by page and section):
   to position zero", "Memory must be encoded offline before a query can reach it",
   "The 100M-token setup depends on host memory as well as two GPUs".
 * [yeyulingfeng] yeyulingfeng.com, "深度分析MSA：把超长文档组织成可检索内部记忆的工程路径",
-  sections 三 (how documents become memory: chunk compression) and 五 (inference:
-  routing retrieval, local generation).
+  sections 三 (how documents become memory: chunk compression), 四 (training: the
+  language-model loss and the routing auxiliary loss) and 五 (inference: routing
+  retrieval, local generation).
 * [github-wiki] github-wiki.com project 250, "MSA 记忆稀疏注意力框架 ...",
   section 6 (implementation features).
 
@@ -48,7 +49,13 @@ those readings are:
   R27 backward of the router: a document score is one maximum over (query token, bank
       row), so its gradient reaches only the maximising pair -- the first in row-major
       order over (bank row, token) -- through that pair's head-mean of cosines; a zero
-      vector has cosine 0 and gets no gradient.
+      vector has cosine 0 and gets no gradient;
+  R28 the routing auxiliary loss supervises the document scores S in one of the two forms
+      the training section names, on logits z = S / temperature, averaged over queries:
+      BCE: the mean over documents of binary cross-entropy with logits against labels y
+      in [0, 1]; InfoNCE: -log of the label-weighted share of softmax(z) (y >= 0; one
+      positive gives the usual cross-entropy).  A query with a non-finite score (a query
+      without tokens) or, for InfoNCE, without a positive label contributes nothing.
 
 Precision: every computation is float64.  Inputs given as bf16 are decoded exactly.
 """
@@ -73,6 +80,7 @@ __all__ = [
     "topk_docs", "route",
     "assemble_memory", "sparse_attention_one", "sparse_attn",
     "sparse_attention_backward_one", "sparse_attn_backward", "route_backward",
+    "AUX_BCE", "AUX_INFONCE", "route_aux_loss",
 ]
 
 
@@ -517,3 +525,58 @@ def route_backward(Qr, q_off, Krbar, chunk_off, dD):
                 dQr[q_off[b] + t, h] += gd / H * (kh - cs * qh) / nq
                 dKb[c, h] += gd / H * (qh - cs * kh) / nk
     return dQr, dKb
+
+
+# ---------------------------------------------------------------------------------------
+# Routing auxiliary loss ([yeyulingfeng] section 四, training signal 2: the document scores
+# are supervised, commonly with BCE or InfoNCE).  Reading R28.
+# ---------------------------------------------------------------------------------------
+
+AUX_BCE = 0
+AUX_INFONCE = 1
+
+
+def _softplus(z):
+    """log(1 + e^z), evaluated without overflow."""
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def _sigmoid(z):
+    e = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def route_aux_loss(kind: int, scores, labels, temperature: float = 1.0):
+    """Per-query losses l[b] and the gradient dD = dL/dS of L = mean_b l[b] (R28), float64.
+
+    BCE:     l[b] = (1/N) sum_d [softplus(z) - y z],   dl/dz = (sigmoid(z) - y) / N
+    InfoNCE: l[b] = log sum_d e^z - log sum_d y e^z,   dl/dz = softmax(z) - y e^z / sum y e^z
+    with z = S[b] / temperature; a skipped query has l[b] = 0 and a zero gradient row."""
+    S = np.asarray(scores, dtype=np.float64)
+    Y = np.asarray(labels, dtype=np.float64)
+    B, N = S.shape
+    loss = np.zeros(B)
+    dD = np.zeros((B, N))
+    for b in range(B):
+        if not np.all(np.isfinite(S[b])):
+            continue
+        z = S[b] / temperature
+        y = Y[b]
+        if kind == AUX_BCE:
+            loss[b] = float(np.mean(_softplus(z) - y * z))
+            dz = (_sigmoid(z) - y) / N
+        elif kind == AUX_INFONCE:
+            if not np.any(y > 0):
+                continue
+            # each log-sum-exp shifted by its own maximum, so neither sum underflows
+            m = z.max()
+            mp = z[y > 0].max()
+            e, ep = np.exp(z - m), np.zeros_like(z)
+            ep[y > 0] = np.exp(z[y > 0] - mp)
+            tot, pos = e.sum(), (y * ep).sum()
+            loss[b] = float((m + np.log(tot)) - (mp + np.log(pos)))
+            dz = e / tot - y * ep / pos
+        else:
+            raise ValueError(f"unknown loss kind {kind}")
+        dD[b] = dz / temperature / B
+    return loss, dD
