@@ -198,6 +198,27 @@ msa_status msa_route_backward(msa_dtype dtype, int32_t n_queries, int64_t total_
                               float* dQr, float* dKrbar, void* workspace,
                               size_t workspace_bytes, msa_stream_t stream);
 
+/* Loss forms of msa_route_aux_loss. */
+enum { MSA_AUX_BCE = 0, MSA_AUX_INFONCE = 1 };
+
+/*
+ * msa_route_aux_loss -- the routing auxiliary loss (yeyulingfeng.com section 四: the document
+ * scores are supervised directly, commonly with BCE or InfoNCE, to train retrieval), with
+ * its gradient, ready for msa_route_backward.  With z = doc_scores[b] / temperature:
+ *   MSA_AUX_BCE:     loss[b] = mean over documents of softplus(z) - y z  (y in [0, 1])
+ *   MSA_AUX_INFONCE: loss[b] = log sum_d e^z_d - log sum_d y_d e^z_d     (y >= 0; a single
+ *                    positive label gives the usual cross-entropy)
+ *   doc_scores, labels  device float [n_queries, n_docs] (scores as msa_route_scan writes).
+ *   loss       device float [n_queries]: the per-query losses (the total is their mean).
+ *   dD         device float [n_queries, n_docs]: d(mean of loss)/d(doc_scores).
+ *   A query with a non-finite score (a query without tokens) or, for InfoNCE, without a
+ *   positive label gets loss 0 and a zero gradient row.  Sums run in double in a fixed
+ *   order; each log-sum-exp is shifted by its own maximum.
+ */
+msa_status msa_route_aux_loss(int32_t kind, int32_t n_queries, int32_t n_docs,
+                              const float* doc_scores, const float* labels, float temperature,
+                              float* loss, float* dD, msa_stream_t stream);
+
 /* Bytes of workspace msa_sparse_attn needs for these sizes. */
 size_t msa_sparse_attn_workspace(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                                  int64_t total_kv, int32_t max_q_len, int32_t hq,

@@ -11,4 +11,5 @@ from .binding import (  # noqa: F401
     msa_sparse_attn, msa_sparse_attn_workspace, msa_status_string, msa_version,
     msa_sparse_attn_backward, msa_sparse_attn_backward_workspace,
     msa_route_backward, msa_route_backward_workspace,
+    MSA_AUX_BCE, MSA_AUX_INFONCE, msa_route_aux_loss,
 )

@@ -57,6 +57,7 @@ def _load() -> ctypes.CDLL:
         "msa_sparse_attn_backward": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, P, P, P, I32,
                                                     I32, I32, F, F, I32, P, I32, I64, P, P, P, I32, P, P,
                                                     P, P, P, P, P, P, SZ, P]),
+        "msa_route_aux_loss": (ctypes.c_int, [I32, I32, I32, P, P, F, P, P, P]),
         "msa_route_backward_workspace": (SZ, [I32, I32, I64, I32]),
         "msa_route_backward": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
                                               P, P, P, P, P, SZ, P]),
@@ -311,3 +312,21 @@ def msa_route_backward(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Kr
                                   d, N, C, _ptr(chunk_off), _ptr(Krbar), _ptr(dD), _ptr(out), _ptr(dKrbar),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out, dKrbar
+
+
+MSA_AUX_BCE = 0
+MSA_AUX_INFONCE = 1
+
+
+def msa_route_aux_loss(doc_scores: torch.Tensor, labels: torch.Tensor, kind: int = MSA_AUX_BCE,
+                       temperature: float = 1.0, out: Optional[tuple] = None, stream=None):
+    """Routing auxiliary loss on float32 [B, N] document scores and labels (device).
+    Returns (per-query loss [B], dL/dS [B, N]) for L = the mean of the per-query losses."""
+    B, N = doc_scores.shape
+    if out is None:
+        out = (torch.empty(B, dtype=torch.float32, device=doc_scores.device),
+               torch.empty((B, N), dtype=torch.float32, device=doc_scores.device))
+    loss, dD = out
+    _check(lib.msa_route_aux_loss(kind, B, N, _ptr(doc_scores), _ptr(labels), temperature, _ptr(loss),
+                                  _ptr(dD), _stream(stream)))
+    return loss, dD

@@ -218,6 +218,18 @@ msa_status msa_route_backward(msa_dtype dtype, int32_t n_queries, int64_t total_
   return hip_status(msa::launch_route_backward(r, (hipStream_t)stream), "msa_route_backward launch");
 }
 
+msa_status msa_route_aux_loss(int32_t kind, int32_t n_queries, int32_t n_docs, const float* doc_scores,
+                              const float* labels, float temperature, float* loss, float* dD,
+                              msa_stream_t stream) {
+  g_last_error.clear();
+  if (kind != MSA_AUX_BCE && kind != MSA_AUX_INFONCE) return fail(MSA_ERR_UNSUPPORTED, "unknown loss kind %d", kind);
+  if (n_queries < 1 || n_docs < 1) return fail(MSA_ERR_INVALID_ARG, "need n_queries >= 1 and n_docs >= 1 (got %d, %d)", n_queries, n_docs);
+  if (!(temperature > 0.f && isfinite(temperature))) return fail(MSA_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  if (!doc_scores || !labels || !loss || !dD) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  msa::AuxArgs a{kind, n_queries, n_docs, doc_scores, labels, temperature, loss, dD};
+  return hip_status(msa::launch_aux_loss(a, (hipStream_t)stream), "msa_route_aux_loss launch");
+}
+
 // The bank's content rows live in page-locked host memory: the device-side aliases.
 static msa_status host_bank_alias(const void* Kbar, const void* Vbar, const void** kb, const void** vb) {
   const void* host[2] = {Kbar, Vbar};

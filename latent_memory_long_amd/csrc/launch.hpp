@@ -104,6 +104,19 @@ struct AttnBwdArgs {
 size_t attn_bwd_workspace_bytes(int64_t total_q, int64_t total_kv, int hq, int h_kv, int d);
 hipError_t launch_sparse_attn_backward(const AttnBwdArgs& a, hipStream_t s);
 
+constexpr int AUX_BCE = 0;
+constexpr int AUX_INFONCE = 1;
+struct AuxArgs {
+  int kind;  // AUX_BCE or AUX_INFONCE
+  int n_queries, n_docs;
+  const float* scores;  // [n_queries, n_docs]
+  const float* labels;  // [n_queries, n_docs]
+  float temperature;
+  float* loss;          // [n_queries]
+  float* dD;            // [n_queries, n_docs]
+};
+hipError_t launch_aux_loss(const AuxArgs& a, hipStream_t s);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace msa

@@ -171,6 +171,22 @@ def test_route_backward_validation(kw, code):
     assert lib.msa_last_error().decode()
 
 
+def _aux(**kw):
+    a = dict(kind=0, B=2, N=10, S=FAKE, Y=FAKE, tau=1.0, loss=FAKE, dD=FAKE)
+    a.update(kw)
+    return lib.msa_route_aux_loss(a["kind"], a["B"], a["N"], a["S"], a["Y"], a["tau"], a["loss"], a["dD"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kind=2), UNSUPPORTED), (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(tau=0.0), INVALID),
+    (dict(tau=float("inf")), INVALID), (dict(S=None), INVALID), (dict(Y=None), INVALID),
+    (dict(loss=None), INVALID), (dict(dD=None), INVALID),
+])
+def test_aux_loss_validation(kw, code):
+    assert _aux(**kw) == code
+    assert lib.msa_last_error().decode()
+
+
 def test_workspace_sizes():
     assert m.msa_route_topk_workspace(1, 47000, 16) >= 47000 * 4
     assert m.msa_route_topk_workspace(0, 10, 1) == 0

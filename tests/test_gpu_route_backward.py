@@ -130,3 +130,70 @@ def test_route_backward_empty_query():
     counts = np.random.default_rng(4).integers(1, 6, size=20)
     got, ref, kept = _run([6, 0, 3], counts, 4, 64, "bf16", seed=91)
     _check(got, ref, "empty")
+
+
+# ------------------------------------------------------------------ routing auxiliary loss
+
+AUX_RTOL = 1e-6   # double sums, one rounding to float32 at the end
+
+
+def _aux_case(kind, B, N, seed, tau):
+    rng = np.random.default_rng(seed)
+    S = rng.uniform(-1, 1, size=(B, N)).astype(np.float32)
+    if kind == O.AUX_BCE:
+        Y = rng.random((B, N)).astype(np.float32)
+    else:
+        Y = (rng.random((B, N)) < 0.05).astype(np.float32)
+        Y[:, 0] = 1.0
+    return S, Y
+
+
+@pytest.mark.parametrize("kind", [O.AUX_BCE, O.AUX_INFONCE], ids=["bce", "infonce"])
+@pytest.mark.parametrize("B,N,tau", [(1, 1, 1.0), (3, 7, 0.1), (32, 4747, 0.05), (2, 47343, 1.0)])
+def test_aux_loss(kind, B, N, tau):
+    say(f"case routing aux loss kind={kind} B={B} N={N} tau={tau}")
+    S, Y = _aux_case(kind, B, N, B * 1000 + N, tau)
+    if B > 1:
+        S[1, N // 2] = -np.inf          # a query without tokens: skipped
+    if kind == O.AUX_INFONCE and B > 2:
+        Y[2] = 0.0                      # no positive label: skipped
+    loss, dD = M.msa_route_aux_loss(torch.tensor(S, device=DEV), torch.tensor(Y, device=DEV), kind, tau)
+    torch.cuda.synchronize()
+    rl, rd = O.route_aux_loss(kind, S.astype(np.float64), Y.astype(np.float64), tau)
+    gl, gd = f64(loss), f64(dD)
+    assert np.all(np.abs(gl - rl) <= AUX_RTOL * np.abs(rl) + 1e-12), (gl, rl)
+    err = np.abs(gd - rd) - (AUX_RTOL * np.abs(rd) + 1e-12)
+    assert err.max() <= 0, float(np.abs(gd - rd).max())
+    if B > 1:
+        assert gl[1] == 0 and not gd[1].any()
+
+
+def test_route_training_chain():
+    # scan -> auxiliary loss -> router backward on the GPU against the same chain in the
+    # oracle, on data whose maximising (token, row) pairs are all well separated
+    say("case router training chain: scan, InfoNCE, backward")
+    H, D = 8, 128
+    q_lens, counts = [1, 3, 2], np.array([2, 1, 4, 3, 1, 2, 5, 1])
+    q_off = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    coff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    Kb = _randn((int(coff[-1]), H, D), 518).to(torch.bfloat16)   # seed chosen for separated maxima
+    Qr = _randn((int(q_off[-1]), H, D), 519).to(torch.bfloat16)
+    for b in range(len(q_lens)):
+        for d in range(len(counts)):
+            s = np.sort(O.token_chunk_scores(f64(Qr)[q_off[b]:q_off[b + 1]],
+                                             f64(Kb)[coff[d]:coff[d + 1]]).ravel())[::-1]
+            assert s.size == 1 or s[0] - s[1] >= GAP, (b, d)
+    Y = np.zeros((len(q_lens), len(counts)), dtype=np.float32)
+    Y[[0, 1, 2], [3, 0, 6]] = 1.0
+    qo = torch.tensor(q_off, dtype=torch.int32, device=DEV)
+    co = torch.tensor(coff, dtype=torch.int64, device=DEV)
+    Qd, Kd = Qr.to(DEV), Kb.to(DEV)
+    S = M.msa_route_scan(Qd, qo, max(q_lens), Kd, co)
+    loss, dD = M.msa_route_aux_loss(S, torch.tensor(Y, device=DEV), M.MSA_AUX_INFONCE, 0.1)
+    dQr, dK = M.msa_route_backward(Qd, qo, max(q_lens), Kd, co, dD)
+    torch.cuda.synchronize()
+    rS = O.route_doc_scores(f64(Qr), q_off, f64(Kb), coff)
+    rl, rd = O.route_aux_loss(O.AUX_INFONCE, rS, Y.astype(np.float64), 0.1)
+    rq, rk = O.route_backward(f64(Qr), q_off, f64(Kb), coff, rd)
+    assert np.allclose(f64(loss), rl, rtol=1e-4, atol=1e-6)
+    _check((f64(dQr), f64(dK)), (rq, rk), "chain")
