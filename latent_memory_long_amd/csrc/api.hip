@@ -37,6 +37,7 @@ int route_path_override() {
   if (!v) return 0;
   if (!strcmp(v, "dot")) return 1;
   if (!strcmp(v, "mfma")) return 2;
+  if (!strcmp(v, "batch")) return 3;
   return 0;
 }
 

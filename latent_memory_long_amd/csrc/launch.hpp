@@ -34,11 +34,13 @@ struct RouteArgs {
   const int64_t* chunk_off;
   const void* Krbar;
   float* scores;   // [n_queries, n_docs] output
-  int force_path;  // 0 auto, 1 dot, 2 mfma (MSA_ROUTE_PATH environment override)
+  int force_path;  // 0 auto, 1 dot, 2 mfma, 3 batch (MSA_ROUTE_PATH environment override)
   float* row_scores = nullptr;  // [n_queries, n_chunks] or null: per-row max over tokens
   int32_t* row_arg = nullptr;   // with row_scores: the first token reaching each row's max
 };
 hipError_t launch_route_scan(const RouteArgs& a, hipStream_t s);
+bool route_batch_supported(const RouteArgs& a);
+hipError_t launch_route_scan_batch(const RouteArgs& a, hipStream_t s);
 
 struct RouteBwdArgs {
   int dtype;

@@ -527,10 +527,17 @@ hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
 
 }  // namespace
 
+// Query rows from which the batched scan (route_batch.hip) takes over.  Below it the scan
+// is bound by the bank read and the streaming kernels above are as fast or faster (10M-
+// token bank: 64 rows 94 us streaming vs 98 us batched; 128 rows 164 vs 128 us).
+constexpr int64_t BATCH_MIN_ROWS = 128;
+
 hipError_t launch_route_scan(const RouteArgs& r, hipStream_t s) {
   ScanK k{r.Qr, r.q_off, r.Krbar, r.chunk_off, r.scores, r.row_scores, r.row_arg, r.n_chunks, r.n_docs, r.h_r};
   // bf16: the MFMA scan at any query length (a short query pads its 16-row tile; the
   // scan stays bound by the bank read and beats the dot-product scan even for one row).
+  if (route_batch_supported(r) && (r.force_path == 3 || (r.force_path == 0 && r.total_q >= BATCH_MIN_ROWS)))
+    return launch_route_scan_batch(r, s);
   bool mfma = (r.dtype == 1) && (r.h_r <= 8);
   if (r.force_path == 1) mfma = false;
   if (r.force_path == 2 && r.dtype == 1 && r.h_r <= 8) mfma = true;

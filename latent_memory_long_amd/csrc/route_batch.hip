@@ -1,0 +1,326 @@
+// Step B for a batch of queries -- the router's scan of many queries in one pass.
+//
+// hysenlabs.com "EverMind-AI/MSA: routing top-k compressed documents inside attention ...",
+// section "Routing happens inside attention ...": a document's relevance is the cosine of
+// the query's routing vectors with the pooled routing keys, averaged over heads and
+// maximised over the query's tokens; yeyulingfeng.com "深度分析MSA ..." section 五 step 2.
+// The scores are those of route.hip:
+//   s(t, c) = sum_h dot(Qr[t,h], Kb[c,h]) * rs[t,h] * cs[c,h],
+//   rs = 1 / (H |Qr[t,h]|), cs = 1 / |Kb[c,h]|   (0 for a zero vector),
+//   document score = max over its rows c and the query's tokens t.
+//
+// With many query rows the scan is a matrix product (query rows x bank rows, inner length
+// H x 128) with a per-head scale and a max epilogue, so it is laid out for the matrix
+// cores rather than for the bank read:
+//  * Each wave keeps 16 bank rows of 8 heads (32 rows of 4 heads) in registers as MFMA B
+//    operands for the whole launch, with their per-head 1/|k|: 128 registers, so two
+//    waves share a SIMD.  A workgroup is eight such waves and covers 128 (256) bank
+//    rows; the bank is read from HBM once.
+//  * Every query of the batch, padded to 16-row tiles, streams past those registers
+//    through LDS in stages of two tiles (32 rows, all heads), double-buffered: the next
+//    stage's rows are loaded into registers while the current stage is multiplied, then
+//    written to LDS with their per-head 1/(H |q|).  LDS rows are padded by 32 bytes: a
+//    16-byte LDS read is served 32 lanes at a time, and the MFMA operand pattern (16
+//    rows x 2 column groups per 32 lanes) then touches 32 distinct 16-byte slots.
+//  * v_mfma_f32_16x16x32_bf16 products (exact bf16 products, float32 sums) of all heads
+//    go to separate accumulators first, then are scaled by rs and cs in float32 and
+//    summed over heads in registers: no head exchange through LDS.  The tile's maximum
+//    over its valid query rows is folded into a running maximum per bank row while the
+//    tiles belong to one query.
+//  * When the query changes, each bank row's maximum is reduced over the rows of its
+//    document inside the wave (a segmented max over lanes) and merged into the document
+//    score with an integer atomic max/min on the float bits, after a fill of -inf.  The
+//    maximum does not depend on the order of the merges.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int BD = 128;               // head dim
+constexpr int BWAVES = 8;             // waves per workgroup, two per SIMD
+constexpr int SQ = 32;                // query rows per stage: two 16-row tiles
+constexpr int KS = BD / 32;           // 32-wide k steps per head
+constexpr int BTHREADS = BWAVES * 64;
+
+// 16-row bank tiles per wave: 128 registers of B operands whatever the head count
+template <int H> constexpr int bank_tiles() { return 8 / H; }
+template <int H> constexpr int bank_rows_per_group() { return BWAVES * bank_tiles<H>() * 16; }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+struct BatchK {
+  const bf16_t* Qr;
+  const int32_t* q_off;
+  const bf16_t* Krb;
+  const int64_t* chunk_off;
+  float* scores;  // [n_queries, n_docs], filled with -inf first
+  int64_t n_chunks;
+  int n_docs;
+  int n_queries;
+};
+
+// A 16-row tile of one query (wave-uniform): query b (n_queries when past the end),
+// first token t0, query length lq, first row of the query in Qr.
+struct Tile {
+  int b, t0, lq, off;
+};
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ Tile query_start(const BatchK& a, int b) {
+  Tile t{b, 0, 0, 0};
+  while (t.b < a.n_queries) {
+    t.off = uni(a.q_off[t.b]);
+    t.lq = uni(a.q_off[t.b + 1]) - t.off;
+    if (t.lq > 0) break;
+    ++t.b;
+  }
+  return t;
+}
+
+__device__ __forceinline__ Tile next_tile(const BatchK& a, const Tile& t) {
+  if (t.b >= a.n_queries) return t;
+  if (t.t0 + 16 < t.lq) return Tile{t.b, t.t0 + 16, t.lq, t.off};
+  return query_start(a, t.b + 1);
+}
+
+// Float max through integer atomics: non-negative floats order like their int bits,
+// negative ones reversely like their unsigned bits.  The target starts at -inf.
+__device__ __forceinline__ void atomic_max_f32(float* p, float v) {
+  if (!(v == v)) return;
+  if (__float_as_int(v) >= 0) atomicMax(reinterpret_cast<int*>(p), __float_as_int(v));
+  else atomicMin(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
+template <int H>
+__global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
+  constexpr int BNT = bank_tiles<H>();
+  constexpr int BROWS = bank_rows_per_group<H>();
+  constexpr int HD = H * BD;
+  constexpr int RS = HD + 16;           // LDS row stride in elements (32 B of padding)
+  constexpr int CPR = HD / 8;           // 16-byte chunks per query row
+  constexpr int CPT = SQ * CPR / BTHREADS;  // chunks per thread per stage
+  static_assert(CPT * BTHREADS == SQ * CPR, "stage chunks must split evenly");
+  __shared__ __align__(16) bf16_t Abuf[2][SQ * RS];
+  __shared__ __align__(16) float rsb[2][H][SQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cl = lane & 15, g = lane >> 4;
+  const int64_t C = a.n_chunks;
+  const int64_t base = (int64_t)blockIdx.x * BROWS + w * (BNT * 16);
+  const bool has_rows = base < C;  // wave-uniform
+
+  // ---- this wave's bank rows: B operands, 1/|k| per head, document of each column ----
+  bf16x8_t Bt[BNT][H][KS];
+  float cs[BNT][H];
+  int doc[BNT];
+#pragma unroll
+  for (int j = 0; j < BNT; ++j) {
+    int64_t c = base + j * 16 + cl;
+    const bool valid = c < C;
+    c = valid ? c : C - 1;
+    const bf16_t* p = a.Krb + c * HD + g * 8;
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        Bt[j][h][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + h * BD + ks * 32));
+    // the norms read the rows a second time (from cache), so the B operands have no use
+    // but the matrix products and may live in accumulation registers
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + h * BD + ks * 32));
+        ss = dot2_bf16(v.x, v.x, ss);
+        ss = dot2_bf16(v.y, v.y, ss);
+        ss = dot2_bf16(v.z, v.z, ss);
+        ss = dot2_bf16(v.w, v.w, ss);
+      }
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      cs[j][h] = (valid && ss > 0.f) ? __builtin_amdgcn_rsqf(ss) : 0.f;
+    }
+    doc[j] = -1;
+  }
+  if (has_rows) {
+    int d = find_doc_wave(a.chunk_off, a.n_docs, base);
+#pragma unroll
+    for (int j = 0; j < BNT; ++j) {
+      const int64_t c = base + j * 16 + cl;
+      if (c < C) {
+        while (a.chunk_off[d + 1] <= c) ++d;
+        doc[j] = d;
+      }
+    }
+  }
+
+  // ---- query stages ----
+  // Chunk i of a thread is 16 bytes of row (tid + i * BTHREADS) / CPR of the stage.  Rows
+  // past a query's end are not loaded; their LDS rows are zero and masked out later.
+  uint4 stage_regs[CPT];
+  auto load_stage = [&](const Tile& t0, const Tile& t1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int q = tid + i * BTHREADS;
+      const int row = q / CPR, cr = q % CPR;
+      const Tile& t = (row < 16) ? t0 : t1;
+      const int tok = t.t0 + (row & 15);
+      stage_regs[i] = make_uint4(0, 0, 0, 0);
+      if (t.b < a.n_queries && tok < t.lq)
+        stage_regs[i] = *reinterpret_cast<const uint4*>(a.Qr + (int64_t)(t.off + tok) * HD + cr * 8);
+    }
+  };
+  auto commit_stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int q = tid + i * BTHREADS;
+      const int row = q / CPR, cr = q % CPR;
+      const uint4 v = stage_regs[i];
+      *reinterpret_cast<uint4*>(&Abuf[buf][row * RS + cr * 8]) = v;
+      float ss = dot2_bf16(v.x, v.x, 0.f);
+      ss = dot2_bf16(v.y, v.y, ss);
+      ss = dot2_bf16(v.z, v.z, ss);
+      ss = dot2_bf16(v.w, v.w, ss);
+      ss = group_sum_last<16>(ss);  // the 16 chunks of one (row, head)
+      if ((lane & 15) == 15) rsb[buf][cr / (BD / 8)][row] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) / (float)H : 0.f;
+    }
+  };
+
+  float run[BNT];  // running max of each bank row over the current query's tiles
+  int run_b = -1;
+#pragma unroll
+  for (int j = 0; j < BNT; ++j) run[j] = -INFINITY;
+
+  auto flush = [&]() __attribute__((always_inline)) {
+    float* sc = a.scores + (int64_t)run_b * a.n_docs;
+#pragma unroll
+    for (int j = 0; j < BNT; ++j) {
+      // segmented max over the 16 columns of the tile, runs = documents
+      float v = run[j];
+      const int d = doc[j];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float ov = __shfl_up(v, o, 16);
+        const int od = __shfl_up(d, o, 16);
+        if (cl >= o && od == d) v = fmaxf(v, ov);
+      }
+      const int dn = __shfl_down(d, 1, 16);
+      const bool last = (cl == 15) || dn != d;
+      if (lane < 16 && d >= 0 && last) atomic_max_f32(sc + d, v);
+    }
+  };
+
+  auto compute_tile = [&](const Tile& t, int buf, int tt) __attribute__((always_inline)) {
+    const bf16_t* arow = &Abuf[buf][(tt * 16 + cl) * RS + g * 8];
+    f32x4_t acc[H][BNT];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      bf16x8_t A[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) A[ks] = *reinterpret_cast<const bf16x8_t*>(arow + h * BD + ks * 32);
+#pragma unroll
+      for (int j = 0; j < BNT; ++j) {
+        acc[h][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], Bt[j][h][ks], acc[h][j], 0, 0, 0);
+      }
+    }
+    float tot[BNT][4];
+#pragma unroll
+    for (int j = 0; j < BNT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tot[j][i] = 0.f;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const float4 r4 = *reinterpret_cast<const float4*>(&rsb[buf][h][tt * 16 + g * 4]);
+#pragma unroll
+      for (int j = 0; j < BNT; ++j) {
+        const float c = cs[j][h];
+        tot[j][0] += acc[h][j][0] * r4.x * c;
+        tot[j][1] += acc[h][j][1] * r4.y * c;
+        tot[j][2] += acc[h][j][2] * r4.z * c;
+        tot[j][3] += acc[h][j][3] * r4.w * c;
+      }
+    }
+    // max over the tile's valid query rows (rows g*4 + i of column cl)
+    const int nv = t.lq - t.t0;
+    float m[BNT];
+#pragma unroll
+    for (int j = 0; j < BNT; ++j) {
+      float x = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x = (g * 4 + i < nv) ? fmaxf(x, tot[j][i]) : x;
+      x = fmaxf(x, __shfl_xor(x, 16, 64));
+      x = fmaxf(x, __shfl_xor(x, 32, 64));
+      m[j] = x;
+    }
+    if (t.b != run_b) {
+      if (run_b >= 0) flush();
+      run_b = t.b;
+#pragma unroll
+      for (int j = 0; j < BNT; ++j) run[j] = m[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < BNT; ++j) run[j] = fmaxf(run[j], m[j]);
+    }
+  };
+
+  Tile t0 = query_start(a, 0);
+  Tile t1 = next_tile(a, t0);
+  if (t0.b >= a.n_queries) return;  // no query has tokens (uniform over the grid)
+  load_stage(t0, t1);
+  commit_stage(0);
+  __syncthreads();
+  int cur = 0;
+  while (t0.b < a.n_queries) {
+    const Tile n0 = next_tile(a, t1);
+    const Tile n1 = next_tile(a, n0);
+    const bool more = n0.b < a.n_queries;
+    if (more) load_stage(n0, n1);  // in flight during the products
+    if (has_rows) {
+      compute_tile(t0, cur, 0);
+      if (t1.b < a.n_queries) compute_tile(t1, cur, 1);
+    }
+    if (more) commit_stage(cur ^ 1);
+    __syncthreads();
+    t0 = n0;
+    t1 = n1;
+    cur ^= 1;
+  }
+  if (has_rows && run_b >= 0) flush();
+}
+
+__global__ void fill_neg_inf(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = -INFINITY;
+}
+
+}  // namespace
+
+bool route_batch_supported(const RouteArgs& r) {
+  return r.dtype == 1 && r.d == BD && (r.h_r == 4 || r.h_r == 8) && r.row_scores == nullptr;
+}
+
+hipError_t launch_route_scan_batch(const RouteArgs& r, hipStream_t s) {
+  BatchK k{(const bf16_t*)r.Qr, r.q_off, (const bf16_t*)r.Krbar, r.chunk_off, r.scores, r.n_chunks,
+           r.n_docs, r.n_queries};
+  const int64_t n = (int64_t)r.n_queries * r.n_docs;
+  hipLaunchKernelGGL(fill_neg_inf, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256), 0, s,
+                     r.scores, n);
+  if (r.h_r == 8) {
+    const dim3 grid((unsigned)((r.n_chunks + bank_rows_per_group<8>() - 1) / bank_rows_per_group<8>()));
+    hipLaunchKernelGGL((route_scan_batch<8>), grid, dim3(BTHREADS), 0, s, k);
+  } else {
+    const dim3 grid((unsigned)((r.n_chunks + bank_rows_per_group<4>() - 1) / bank_rows_per_group<4>()));
+    hipLaunchKernelGGL((route_scan_batch<4>), grid, dim3(BTHREADS), 0, s, k);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

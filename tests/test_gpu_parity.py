@@ -208,7 +208,7 @@ def _chunk_counts(n_docs, seed, small_frac=0.4, hi=40):
     return c
 
 
-ROUTE_CASES = [(lq, path) for lq in (1, 3, 15, 16, 17, 40, 64, 65, 100) for path in ("auto", "dot", "mfma")]
+ROUTE_CASES = [(lq, path) for lq in (1, 3, 15, 16, 17, 40, 64, 65, 100) for path in ("auto", "dot", "mfma", "batch")]
 
 
 @pytest.mark.parametrize("lq,path", ROUTE_CASES, ids=[f"lq{a}-{b}" for a, b in ROUTE_CASES])
@@ -238,7 +238,7 @@ def test_route_fp32(lq):
     assert_topk_valid(ids[0], o, 5, "fp32 topk")
 
 
-@pytest.mark.parametrize("path", ["auto", "dot", "mfma"])
+@pytest.mark.parametrize("path", ["auto", "dot", "mfma", "batch"])
 def test_route_batched(path):
     say(f"case route batched path={path}")
     _route_env(path)
@@ -255,7 +255,7 @@ def test_route_batched(path):
         assert_topk_valid(ids[b], o[b], 16, f"query {b}")
 
 
-@pytest.mark.parametrize("path", ["dot", "mfma"])
+@pytest.mark.parametrize("path", ["dot", "mfma", "batch"])
 def test_route_batched_parts_share_xcd(path):
     # 4096 rows: 64 parts for the MFMA scan, 128 for the dot scan, so with several queries
     # the workgroups take the XCD-grouped (part, query) order.
@@ -288,6 +288,38 @@ def test_route_paths_agree_and_deterministic():
     c = route(Qr, [48], Krb, coff, 16)
     assert np.array_equal(a[2], b[2]) and np.array_equal(a[0], b[0])   # same bits twice
     assert np.max(np.abs(a[2] - c[2])) < 1e-5
+    _route_env("batch")
+    d = route(Qr, [48], Krb, coff, 16)
+    e = route(Qr, [48], Krb, coff, 16)
+    assert np.array_equal(d[2], e[2]) and np.array_equal(d[0], e[0])   # atomics merge a max: same bits
+    assert np.max(np.abs(a[2] - d[2])) < 1e-5
+
+
+@pytest.mark.parametrize("heads", [8, 4])
+@pytest.mark.parametrize("n_rows", [1, 37, 128, 129, 300])
+def test_route_batch_kernel_edges(heads, n_rows):
+    # banks smaller than one workgroup's 128 rows, exactly one, one more; documents that
+    # cross wave and workgroup boundaries; queries of 1, 0, 16, 17 and 33 tokens
+    say(f"case batched scan edges heads={heads} rows={n_rows}")
+    _route_env("batch")
+    rng = np.random.default_rng(n_rows)
+    counts = []
+    while sum(counts) < n_rows:
+        counts.append(int(min(rng.integers(1, 40), n_rows - sum(counts))))
+    coff, Krb = random_bank(np.array(counts), heads, 128, "bf16", 70 + n_rows)
+    q_lens = [1, 0, 16, 17, 33]
+    Qr = _cpu_randn((sum(q_lens), heads, 128), 71).to(torch.bfloat16)
+    q_off = np.concatenate([[0], np.cumsum(q_lens)])
+    ds = M.msa_route_scan(Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), 33, Krb,
+                          torch.tensor(coff, device=DEV))
+    torch.cuda.synchronize()
+    ds = ds.cpu().numpy()
+    o = O.route_doc_scores(f64(Qr), q_off, f64(Krb), coff)
+    for b in range(len(q_lens)):
+        if q_lens[b] == 0:
+            assert np.all(np.isneginf(ds[b]))
+        else:
+            assert_scores_close(ds[b], o[b], "bf16", f"rows {n_rows} query {b}")
 
 
 def test_topk_ties_and_small_banks():
@@ -418,7 +450,7 @@ def test_route_scan_alone_and_empty_query():
     q_lens = [20, 0, 5]
     Qr = _cpu_randn((sum(q_lens), 8, 128), 101).to(torch.bfloat16)
     q_off = np.concatenate([[0], np.cumsum(q_lens)])
-    for path in ("auto", "dot", "mfma"):
+    for path in ("auto", "dot", "mfma", "batch"):
         _route_env(path)
         ds = M.msa_route_scan(Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), 20, Krb,
                               torch.tensor(coff, device=DEV))
