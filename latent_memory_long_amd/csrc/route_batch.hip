@@ -22,9 +22,10 @@
 //    written to LDS with their per-head 1/(H |q|).  LDS rows are padded by 32 bytes: a
 //    16-byte LDS read is served 32 lanes at a time, and the MFMA operand pattern (16
 //    rows x 2 column groups per 32 lanes) then touches 32 distinct 16-byte slots.
-//  * v_mfma_f32_16x16x32_bf16 products (exact bf16 products, float32 sums) of all heads
-//    go to separate accumulators first, then are scaled by rs and cs in float32 and
-//    summed over heads in registers: no head exchange through LDS.  The tile's maximum
+//  * v_mfma_f32_16x16x32_bf16 products (exact bf16 products, float32 sums) are scaled by
+//    rs and cs in float32 and summed over heads in registers, as a pipeline over heads
+//    (one head's products, the next head's LDS reads and the previous head's scaling in
+//    flight together): no head exchange through LDS.  The tile's maximum
 //    over its valid query rows is folded into a running maximum per bank row while the
 //    tiles belong to one query.
 //  * When the query changes, each bank row's maximum is reduced over the rows of its
@@ -57,6 +58,8 @@ struct BatchK {
   const bf16_t* Krb;
   const int64_t* chunk_off;
   float* scores;  // [n_queries, n_docs], filled with -inf first
+  float* row_scores;  // ARG: [n_queries, n_chunks] every bank row's max over the tokens
+  int32_t* row_arg;   // ARG: [n_queries, n_chunks] the first token reaching it
   int64_t n_chunks;
   int n_docs;
   int n_queries;
@@ -95,7 +98,9 @@ __device__ __forceinline__ void atomic_max_f32(float* p, float v) {
   else atomicMin(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
 }
 
-template <int H>
+// ARG: also record every bank row's score and the first query token reaching it (for the
+// router's backward); the document scores are then left to the caller's -inf fill.
+template <int H, bool ARG>
 __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
   constexpr int BNT = bank_tiles<H>();
   constexpr int BROWS = bank_rows_per_group<H>();
@@ -160,19 +165,22 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
   }
 
   // ---- query stages ----
-  // Chunk i of a thread is 16 bytes of row (tid + i * BTHREADS) / CPR of the stage.  Rows
-  // past a query's end are not loaded; their LDS rows are zero and masked out later.
+  // Chunk i of a thread is 16 bytes of row (tid + i * BTHREADS) / CPR of the stage: the
+  // first CPT / 2 chunks lie in rows 0..15 (the first tile), the others in rows 16..31.
+  // A row past its query's end re-reads the tile's last row: its scores are masked out
+  // before any maximum.
+  static_assert(BTHREADS % CPR == 0 && CPT % 2 == 0, "a chunk index must pick one tile");
   uint4 stage_regs[CPT];
   auto load_stage = [&](const Tile& t0, const Tile& t1) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
+      const Tile& t = (i < CPT / 2) ? t0 : t1;
+      if (t.b >= a.n_queries) continue;  // uniform: no such tile
       const int q = tid + i * BTHREADS;
-      const int row = q / CPR, cr = q % CPR;
-      const Tile& t = (row < 16) ? t0 : t1;
-      const int tok = t.t0 + (row & 15);
-      stage_regs[i] = make_uint4(0, 0, 0, 0);
-      if (t.b < a.n_queries && tok < t.lq)
-        stage_regs[i] = *reinterpret_cast<const uint4*>(a.Qr + (int64_t)(t.off + tok) * HD + cr * 8);
+      const int row = (q / CPR) & 15, cr = q % CPR;
+      const char* tb = reinterpret_cast<const char*>(a.Qr + (int64_t)(t.off + t.t0) * HD);  // uniform
+      const uint32_t off = (uint32_t)(min(row, t.lq - t.t0 - 1) * (HD * 2) + cr * 16);
+      stage_regs[i] = *reinterpret_cast<const uint4*>(tb + off);
     }
   };
   auto commit_stage = [&](int buf) __attribute__((always_inline)) {
@@ -192,11 +200,26 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
   };
 
   float run[BNT];  // running max of each bank row over the current query's tiles
+  int run_arg[BNT];  // ARG: the query-local token of that maximum
   int run_b = -1;
 #pragma unroll
-  for (int j = 0; j < BNT; ++j) run[j] = -INFINITY;
+  for (int j = 0; j < BNT; ++j) {
+    run[j] = -INFINITY;
+    run_arg[j] = 0;
+  }
 
   auto flush = [&]() __attribute__((always_inline)) {
+    if constexpr (ARG) {
+#pragma unroll
+      for (int j = 0; j < BNT; ++j) {
+        const int64_t c = base + j * 16 + cl;
+        if (lane < 16 && c < C) {
+          a.row_scores[(int64_t)run_b * C + c] = run[j];
+          a.row_arg[(int64_t)run_b * C + c] = run_arg[j];
+        }
+      }
+      return;
+    }
     float* sc = a.scores + (int64_t)run_b * a.n_docs;
 #pragma unroll
     for (int j = 0; j < BNT; ++j) {
@@ -217,57 +240,106 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
 
   auto compute_tile = [&](const Tile& t, int buf, int tt) __attribute__((always_inline)) {
     const bf16_t* arow = &Abuf[buf][(tt * 16 + cl) * RS + g * 8];
-    f32x4_t acc[H][BNT];
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      bf16x8_t A[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) A[ks] = *reinterpret_cast<const bf16x8_t*>(arow + h * BD + ks * 32);
-#pragma unroll
-      for (int j = 0; j < BNT; ++j) {
-        acc[h][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], Bt[j][h][ks], acc[h][j], 0, 0, 0);
-      }
-    }
+    const float* rrow = &rsb[buf][0][tt * 16 + g * 4];
     float tot[BNT][4];
 #pragma unroll
     for (int j = 0; j < BNT; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tot[j][i] = 0.f;
+    // Software pipeline over heads: head h's products run while head h + 1's operands
+    // load from LDS and head h - 1's products are scaled into the total.
+    bf16x8_t A[2][KS];
+    float4 r4[2];
+    f32x4_t acc[2][BNT];
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
-      const float4 r4 = *reinterpret_cast<const float4*>(&rsb[buf][h][tt * 16 + g * 4]);
+    for (int ks = 0; ks < KS; ++ks) A[0][ks] = *reinterpret_cast<const bf16x8_t*>(arow + ks * 32);
+    r4[0] = *reinterpret_cast<const float4*>(rrow);
 #pragma unroll
-      for (int j = 0; j < BNT; ++j) {
-        const float c = cs[j][h];
-        tot[j][0] += acc[h][j][0] * r4.x * c;
-        tot[j][1] += acc[h][j][1] * r4.y * c;
-        tot[j][2] += acc[h][j][2] * r4.z * c;
-        tot[j][3] += acc[h][j][3] * r4.w * c;
+    for (int h = 0; h <= H; ++h) {
+      const int cur = h & 1, prv = cur ^ 1;
+      const float4 rr = r4[prv];  // head h - 1's row scales, read before the slot refills
+      if (h + 1 < H) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          A[prv][ks] = *reinterpret_cast<const bf16x8_t*>(arow + (h + 1) * BD + ks * 32);
+        r4[prv] = *reinterpret_cast<const float4*>(rrow + (h + 1) * SQ);
+      }
+      if (h < H) {
+#pragma unroll
+        for (int j = 0; j < BNT; ++j) {
+          acc[cur][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc[cur][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[cur][ks], Bt[j][h][ks], acc[cur][j], 0, 0, 0);
+        }
+      }
+      if (h > 0) {
+#pragma unroll
+        for (int j = 0; j < BNT; ++j) {
+          const float c = cs[j][h - 1];
+          tot[j][0] += acc[prv][j][0] * rr.x * c;
+          tot[j][1] += acc[prv][j][1] * rr.y * c;
+          tot[j][2] += acc[prv][j][2] * rr.z * c;
+          tot[j][3] += acc[prv][j][3] * rr.w * c;
+        }
       }
     }
     // max over the tile's valid query rows (rows g*4 + i of column cl)
     const int nv = t.lq - t.t0;
     float m[BNT];
+    int mi[BNT];  // ARG: the first row reaching it
 #pragma unroll
     for (int j = 0; j < BNT; ++j) {
       float x = -INFINITY;
+      int xi = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x = (g * 4 + i < nv) ? fmaxf(x, tot[j][i]) : x;
-      x = fmaxf(x, __shfl_xor(x, 16, 64));
-      x = fmaxf(x, __shfl_xor(x, 32, 64));
+      for (int i = 0; i < 4; ++i) {
+        if (ARG) {
+          if (g * 4 + i < nv && tot[j][i] > x) {
+            x = tot[j][i];
+            xi = g * 4 + i;
+          }
+        } else {
+          x = (g * 4 + i < nv) ? fmaxf(x, tot[j][i]) : x;
+        }
+      }
+      if constexpr (ARG) {
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+          const float ox = __shfl_xor(x, o, 64);
+          const int oi = __shfl_xor(xi, o, 64);
+          if (ox > x || (ox == x && oi < xi)) {
+            x = ox;
+            xi = oi;
+          }
+        }
+      } else {
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        x = fmaxf(x, __shfl_xor(x, 32, 64));
+      }
       m[j] = x;
+      mi[j] = t.t0 + xi;
     }
     if (t.b != run_b) {
       if (run_b >= 0) flush();
       run_b = t.b;
 #pragma unroll
-      for (int j = 0; j < BNT; ++j) run[j] = m[j];
+      for (int j = 0; j < BNT; ++j) {
+        run[j] = m[j];
+        run_arg[j] = mi[j];
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < BNT; ++j) run[j] = fmaxf(run[j], m[j]);
+      for (int j = 0; j < BNT; ++j) {
+        if (ARG) {
+          if (m[j] > run[j]) {  // strictly: an earlier tile keeps a tie
+            run[j] = m[j];
+            run_arg[j] = mi[j];
+          }
+        } else {
+          run[j] = fmaxf(run[j], m[j]);
+        }
+      }
     }
   };
 
@@ -304,23 +376,26 @@ __global__ void fill_neg_inf(float* p, int64_t n) {
 }  // namespace
 
 bool route_batch_supported(const RouteArgs& r) {
-  return r.dtype == 1 && r.d == BD && (r.h_r == 4 || r.h_r == 8) && r.row_scores == nullptr;
+  return r.dtype == 1 && r.d == BD && (r.h_r == 4 || r.h_r == 8);
+}
+
+template <int H>
+hipError_t launch_h(const RouteArgs& r, const BatchK& k, hipStream_t s) {
+  const dim3 grid((unsigned)((r.n_chunks + bank_rows_per_group<H>() - 1) / bank_rows_per_group<H>()));
+  if (k.row_scores) hipLaunchKernelGGL((route_scan_batch<H, true>), grid, dim3(BTHREADS), 0, s, k);
+  else hipLaunchKernelGGL((route_scan_batch<H, false>), grid, dim3(BTHREADS), 0, s, k);
+  return hipGetLastError();
 }
 
 hipError_t launch_route_scan_batch(const RouteArgs& r, hipStream_t s) {
-  BatchK k{(const bf16_t*)r.Qr, r.q_off, (const bf16_t*)r.Krbar, r.chunk_off, r.scores, r.n_chunks,
-           r.n_docs, r.n_queries};
+  BatchK k{(const bf16_t*)r.Qr, r.q_off, (const bf16_t*)r.Krbar, r.chunk_off, r.scores, r.row_scores,
+           r.row_arg, r.n_chunks, r.n_docs, r.n_queries};
+  // -inf: the value of an empty maximum (documents without rows, queries without tokens,
+  // and, with row scores, every document: the router's backward reads the rows only)
   const int64_t n = (int64_t)r.n_queries * r.n_docs;
   hipLaunchKernelGGL(fill_neg_inf, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256), 0, s,
                      r.scores, n);
-  if (r.h_r == 8) {
-    const dim3 grid((unsigned)((r.n_chunks + bank_rows_per_group<8>() - 1) / bank_rows_per_group<8>()));
-    hipLaunchKernelGGL((route_scan_batch<8>), grid, dim3(BTHREADS), 0, s, k);
-  } else {
-    const dim3 grid((unsigned)((r.n_chunks + bank_rows_per_group<4>() - 1) / bank_rows_per_group<4>()));
-    hipLaunchKernelGGL((route_scan_batch<4>), grid, dim3(BTHREADS), 0, s, k);
-  }
-  return hipGetLastError();
+  return r.h_r == 8 ? launch_h<8>(r, k, s) : launch_h<4>(r, k, s);
 }
 
 }  // namespace msa

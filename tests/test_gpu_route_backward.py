@@ -98,6 +98,8 @@ CASES = [
     ("bf16_h8_d64_mfma", [3, 17], 8, 64, "bf16", "mfma"),
     ("f32_h16_d32", [2, 9, 1], 16, 32, "f32", "auto"),
     ("bf16_h16_d128", [5, 12], 16, 128, "bf16", "auto"),
+    ("bf16_h8_d128_batch", [3, 40, 130], 8, 128, "bf16", "batch"),
+    ("bf16_h4_d128_batch", [1, 7, 40], 4, 128, "bf16", "batch"),
 ]
 
 
