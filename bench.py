@@ -216,6 +216,72 @@ def time_batch(dev, bank, reps=20):
     return fig, bwd
 
 
+def time_layers(dev, reps=20):
+    """One 64-token query routed and attended in each of 18 upper layers, every layer with
+    its own 10M-token bank (K-bar, V-bar, Kr-bar all in HBM: 17.5 GB).  The step runs the
+    layers in order, eagerly and as one captured HIP graph."""
+    wl = W.workload("layers18_bank10m")
+    sh = wl.shape
+    lens = W.doc_lengths(wl)
+    coff = M.msa_chunk_offsets(W.token_offsets(lens), sh.chunk)
+    N, C, L, k = len(lens), int(coff[-1]), wl.n_layers, wl.k
+    lq = 64
+    banks = [W.gen_pooled_bank(W.layer(wl, l), coff, dev) for l in range(L)]
+    qs = [W.gen_queries(W.layer(wl, l), dev, lq_override=[lq]) for l in range(L)]
+    q_off = torch.tensor([0, lq], dtype=torch.int32, device=dev)
+    coff_d = torch.tensor(coff, device=dev)
+    ds = torch.empty((L, 1, N), dtype=torch.float32, device=dev)
+    ids = torch.empty((L, 1, k), dtype=torch.int32, device=dev)
+    sc = torch.empty((L, 1, k), dtype=torch.float32, device=dev)
+    out = torch.empty((L, lq, sh.hq, sh.d), dtype=torch.bfloat16, device=dev)
+    tws = torch.empty(max(M.msa_topk_workspace(1, N, k), 256), dtype=torch.uint8, device=dev)
+    aws = torch.empty(max(M.msa_sparse_attn_workspace(M.MSA_BF16, 1, lq, lq, lq, sh.hq, sh.h_kv, sh.d), 256),
+                      dtype=torch.uint8, device=dev)
+
+    def step():
+        for l in range(L):
+            Krb, Kb, Vb = banks[l]
+            q = qs[l]
+            M.msa_route_scan(q["Qr"], q_off, lq, Krb, coff_d, out=ds[l])
+            M.msa_topk(ds[l], k, out=(ids[l], sc[l]), workspace=tws)
+            M.msa_sparse_attn(q["Q"], q["Kloc"], q["Vloc"], q_off, q_off, lq, ids[l], coff_d, Kb, Vb,
+                              rope_base=sh.rope_base, out=out[l], workspace=aws)
+
+    def timed(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+    eager = timed(step)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.synchronize()
+    replay = timed(graph.replay)
+    scan_bytes = L * C * sh.h_r * sh.d * 2
+    t = pct(replay, 50) / 1e3
+    del banks, qs, graph
+    torch.cuda.empty_cache()
+    return {"workload": "layers18_bank10m", "layers": L, "bank_tokens_per_layer": int(lens.sum()),
+            "bank_rows": C, "documents": N, "query_tokens": lq, "k": k, "banks_gb_in_hbm": round(3 * scan_bytes / 1e9, 2),
+            "eager_step_p50_ms": round(pct(eager, 50), 4), "graph_step_p50_ms": round(pct(replay, 50), 4),
+            "graph_per_layer_ms": round(pct(replay, 50) / L, 4),
+            "routed_bank_tokens_per_s": L * int(lens.sum()) / t,
+            "krbar_gbps_over_step": scan_bytes / t / 1e9}
+
+
 def time_banks(dev, reps=50):
     """Route + attend one 64-token query against the 1M- and 10M-token banks (drawn pooled,
     everything in HBM).  The 1M bank's routing keys (33 MB) stay in the last-level cache
@@ -353,6 +419,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pool", action="store_true", help="skip the 10M-token encode and batch stages")
+    ap.add_argument("--no-layers", action="store_true", help="skip the 18-layer stage")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device 3 times: a kernel of known traffic "
                          "against which hardware byte counters are scaled")
@@ -473,7 +540,7 @@ def main():
     if not args.no_pool:
         log("1M- and 10M-token banks")
         banks = time_banks(dev)
-    pool = batch = backward = None
+    pool = batch = backward = layers = None
     if not args.no_pool:
         del qs
         torch.cuda.empty_cache()
@@ -483,6 +550,9 @@ def main():
         batch, backward = time_batch(dev, bank10m)
         del bank10m
         torch.cuda.empty_cache()
+    if not args.no_layers:
+        log("18 routed layers, a 10M-token bank each, eager and graph-captured")
+        layers = time_layers(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -526,6 +596,7 @@ def main():
         "pool": pool,
         "batch": batch,
         "backward": backward,
+        "layers": layers,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

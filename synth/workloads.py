@@ -22,7 +22,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "LayerShape", "Workload", "WORKLOADS", "workload",
+    "LayerShape", "Workload", "WORKLOADS", "workload", "layer",
     "doc_lengths", "token_offsets", "gen_token_states", "gen_queries", "plant_needles",
     "gen_pooled_bank", "torch_gen", "STREAM",
 ]
@@ -60,6 +60,7 @@ class Workload:
     kv_source: str = "hbm"       # where K-bar / V-bar live: "hbm" or "host" (pinned)
     pooled_direct: bool = False  # bank drawn already pooled (token level would not fit)
     decode_steps: int = 0        # single-token steps after the prefill query
+    n_layers: int = 1            # routed layers, each with its own bank and query tensors
     seed: int = 0
 
 
@@ -78,6 +79,11 @@ WORKLOADS = {
     "bank100m_host": Workload("bank100m_host", "bf16", QWEN3_4B_LIKE, ("loguniform", 200, 8000),
                               bank_tokens=100_000_000, doc_offset_std=0.5, q_offset_std=0.5,
                               kv_source="host", pooled_direct=True, decode_steps=32),
+    # 18 routed (upper) layers of a 36-layer Qwen3-4B-like model over one 10M-token corpus:
+    # a bank per layer, all resident in HBM, one 64-token query routed in every layer.
+    "layers18_bank10m": Workload("layers18_bank10m", "bf16", QWEN3_4B_LIKE, ("loguniform", 200, 8000),
+                                 bank_tokens=10_000_000, doc_offset_std=0.5, q_offset_std=0.5,
+                                 pooled_direct=True, n_layers=18),
     # Encode 10M tokens, then a batch of 32 queries of 16-256 tokens, k = 32.
     "batch32_bank10m": Workload("batch32_bank10m", "bf16", QWEN3_4B_LIKE,
                                 ("loguniform", 200, 8000), bank_tokens=10_000_000,
@@ -89,6 +95,14 @@ WORKLOADS = {
 def workload(name: str, **overrides) -> Workload:
     """A named workload, optionally with fields replaced (e.g. a smaller bank)."""
     return replace(WORKLOADS[name], **overrides) if overrides else WORKLOADS[name]
+
+
+def layer(wl: Workload, l: int) -> Workload:
+    """The tensor streams of routed layer l.  Every layer sees the same documents and
+    query lengths: take those from the base workload (``doc_lengths(wl)``, and pass the
+    base query lengths to ``gen_queries`` as ``lq_override``), and draw layer l's banks and
+    query tensors from ``layer(wl, l)``."""
+    return replace(wl, seed=wl.seed + 1000 * (l + 1))
 
 
 # Independent generator streams, one per tensor.
