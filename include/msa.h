@@ -50,7 +50,8 @@ typedef enum {
   MSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shapes           */
   MSA_ERR_UNSUPPORTED = 2, /* valid but not implemented (head dim, dtype, k > 1024) */
   MSA_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace() size */
-  MSA_ERR_HIP = 4          /* a HIP call or kernel launch failed                     */
+  MSA_ERR_HIP = 4,         /* a HIP call or kernel launch failed                     */
+  MSA_ERR_IO = 5           /* a bank file could not be written, read or verified     */
 } msa_status;
 
 typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
@@ -218,6 +219,46 @@ enum { MSA_AUX_BCE = 0, MSA_AUX_INFONCE = 1 };
 msa_status msa_route_aux_loss(int32_t kind, int32_t n_queries, int32_t n_docs,
                               const float* doc_scores, const float* labels, float temperature,
                               float* loss, float* dD, msa_stream_t stream);
+
+/*
+ * Bank persistence (hysenlabs.com "Memory must be encoded offline before a query can reach
+ * it": the corpus is encoded once and later queries read the result; yeyulingfeng.com
+ * section 三 part 3: the bank holds K-bar / V-bar / Kr-bar for every layer).  A bank file
+ * stores the document and row offsets and, for each routed layer, Kr-bar, K-bar and V-bar,
+ * each section with a checksum.  All pointers are host memory (pageable or pinned); the
+ * caller copies to and from the device.  Failures return MSA_ERR_IO (open, write or read
+ * error, not a bank file, truncated, checksum mismatch) or MSA_ERR_INVALID_ARG.
+ */
+typedef struct {
+  int32_t dtype;      /* msa_dtype of the tensors */
+  int32_t n_layers;   /* routed layers, one Kr-bar / K-bar / V-bar each */
+  int32_t n_docs;
+  int32_t h_kv, h_r, d;
+  int32_t chunk;      /* tokens per bank row, as given to msa_chunk_offsets / msa_pool */
+  uint32_t rope_mask; /* as given to msa_pool (recorded, not interpreted) */
+  float rope_base;    /* as given to msa_pool (recorded, not interpreted) */
+  int32_t reserved;   /* 0 */
+  int64_t n_tokens;   /* doc_tok_off[n_docs] */
+  int64_t n_chunks;   /* chunk_off[n_docs] = C */
+} msa_bank_info;
+
+/* Writes a bank: doc_tok_off / chunk_off [n_docs+1] (chunk_off must follow the chunking
+ * rule of msa_chunk_offsets for info->chunk), and for layer l the arrays Krbar[l]
+ * [C, h_r, d], Kbar[l] and Vbar[l] [C, h_kv, d] of info->dtype.  Overwrites `path`. */
+msa_status msa_bank_save(const char* path, const msa_bank_info* info, const int64_t* doc_tok_off,
+                         const int64_t* chunk_off, const void* const* Krbar,
+                         const void* const* Kbar, const void* const* Vbar);
+
+/* Reads a bank file's header, to size the buffers of msa_bank_load. */
+msa_status msa_bank_read_info(const char* path, msa_bank_info* info);
+
+/* Reads a bank into caller buffers sized for `expect` (the file must describe the same
+ * bank: dtype, layers, documents, heads, head dim, chunk and sizes), verifying every
+ * section's checksum and the offsets' chunking rule.  On failure the buffers' contents
+ * are unspecified. */
+msa_status msa_bank_load(const char* path, const msa_bank_info* expect, int64_t* doc_tok_off,
+                         int64_t* chunk_off, void* const* Krbar, void* const* Kbar,
+                         void* const* Vbar);
 
 /* Bytes of workspace msa_sparse_attn needs for these sizes. */
 size_t msa_sparse_attn_workspace(msa_dtype dtype, int32_t n_queries, int64_t total_q,

@@ -12,4 +12,5 @@ from .binding import (  # noqa: F401
     msa_sparse_attn_backward, msa_sparse_attn_backward_workspace,
     msa_route_backward, msa_route_backward_workspace,
     MSA_AUX_BCE, MSA_AUX_INFONCE, msa_route_aux_loss,
+    MSA_ERR_IO, msa_bank_save, msa_bank_read_info, msa_bank_load,
 )

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
-MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
+MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP, MSA_ERR_IO = range(6)
 MSA_F32, MSA_BF16 = 0, 1
 MSA_ROPE_K, MSA_ROPE_V, MSA_ROPE_KR = 1, 2, 4
 
@@ -27,6 +27,14 @@ class MsaError(RuntimeError):
         super().__init__(f"msa status {status}: {message}")
         self.status = status
         self.message = message
+
+
+class BankInfo(ctypes.Structure):
+    """msa_bank_info of include/msa.h."""
+    _fields_ = [("dtype", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("n_docs", ctypes.c_int32),
+                ("h_kv", ctypes.c_int32), ("h_r", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("rope_mask", ctypes.c_uint32), ("rope_base", ctypes.c_float),
+                ("reserved", ctypes.c_int32), ("n_tokens", ctypes.c_int64), ("n_chunks", ctypes.c_int64)]
 
 
 def _load() -> ctypes.CDLL:
@@ -58,6 +66,9 @@ def _load() -> ctypes.CDLL:
                                                     I32, I32, F, F, I32, P, I32, I64, P, P, P, I32, P, P,
                                                     P, P, P, P, P, P, SZ, P]),
         "msa_route_aux_loss": (ctypes.c_int, [I32, I32, I32, P, P, F, P, P, P]),
+        "msa_bank_save": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(BankInfo), P, P, P, P, P]),
+        "msa_bank_read_info": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(BankInfo)]),
+        "msa_bank_load": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(BankInfo), P, P, P, P, P]),
         "msa_route_backward_workspace": (SZ, [I32, I32, I64, I32]),
         "msa_route_backward": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
                                               P, P, P, P, P, SZ, P]),
@@ -330,3 +341,60 @@ def msa_route_aux_loss(doc_scores: torch.Tensor, labels: torch.Tensor, kind: int
     _check(lib.msa_route_aux_loss(kind, B, N, _ptr(doc_scores), _ptr(labels), temperature, _ptr(loss),
                                   _ptr(dD), _stream(stream)))
     return loss, dD
+
+
+def _info_dict(info: BankInfo) -> dict:
+    return {f: getattr(info, f) for f, _ in BankInfo._fields_ if f != "reserved"}
+
+
+def msa_bank_save(path: str, doc_tok_off, chunk_off, layers, chunk: int = 64, rope_base: float = 1e6,
+                  rope_mask: int = 1):
+    """Writes a bank file.  layers: [(Krbar, Kbar, Vbar), ...] one tuple per routed layer,
+    tensors on any device (copied to host memory for the write)."""
+    dto = np.ascontiguousarray(doc_tok_off, dtype=np.int64)
+    cho = np.ascontiguousarray(chunk_off, dtype=np.int64)
+    Kr0, K0, _ = layers[0]
+    host = [tuple(t.detach().contiguous().cpu() for t in trio) for trio in layers]
+    info = BankInfo(_dtype_code(Kr0), len(layers), len(dto) - 1, K0.shape[1], Kr0.shape[1], Kr0.shape[2], chunk,
+                    rope_mask, rope_base, 0, int(dto[-1]), int(cho[-1]))
+    arr = lambda i: (ctypes.c_void_p * len(host))(*[h[i].data_ptr() for h in host])
+    _check(lib.msa_bank_save(os.fsencode(path), ctypes.byref(info), dto.ctypes.data, cho.ctypes.data, arr(0), arr(1),
+                             arr(2)))
+
+
+def msa_bank_read_info(path: str) -> dict:
+    info = BankInfo()
+    _check(lib.msa_bank_read_info(os.fsencode(path), ctypes.byref(info)))
+    return _info_dict(info)
+
+
+def msa_bank_load(path: str, device=None, kv_device=None):
+    """Reads a bank file.  Returns (doc_tok_off, chunk_off, layers, info): offsets as NumPy
+    int64 arrays, layers as [(Krbar, Kbar, Vbar), ...].  Kr-bar goes to ``device`` and K-bar /
+    V-bar to ``kv_device`` (default: ``device``; "cpu-pinned" for page-locked host memory);
+    None keeps a tensor in host memory."""
+    info = BankInfo()
+    _check(lib.msa_bank_read_info(os.fsencode(path), ctypes.byref(info)))
+    dt = torch.float32 if info.dtype == MSA_F32 else torch.bfloat16
+    C, L = info.n_chunks, info.n_layers
+    kvdev = device if kv_device is None else kv_device
+    # host buffers are page-locked when they feed a device copy or are asked for as such
+    kr = [torch.empty((C, info.h_r, info.d), dtype=dt, pin_memory=device is not None) for _ in range(L)]
+    kv = [tuple(torch.empty((C, info.h_kv, info.d), dtype=dt, pin_memory=kvdev is not None) for _ in range(2))
+          for _ in range(L)]
+    dto = np.empty(info.n_docs + 1, dtype=np.int64)
+    cho = np.empty(info.n_docs + 1, dtype=np.int64)
+    arr = lambda ts: (ctypes.c_void_p * L)(*[t.data_ptr() for t in ts])
+    _check(lib.msa_bank_load(os.fsencode(path), ctypes.byref(info), dto.ctypes.data, cho.ctypes.data, arr(kr),
+                             arr([k for k, _ in kv]), arr([v for _, v in kv])))
+    layers = []
+    for l in range(L):
+        Kr = kr[l].to(device, non_blocking=True) if device is not None else kr[l]
+        if kvdev is None or kvdev == "cpu-pinned":
+            K, V = kv[l]
+        else:
+            K, V = kv[l][0].to(kvdev, non_blocking=True), kv[l][1].to(kvdev, non_blocking=True)
+        layers.append((Kr, K, V))
+    if device is not None or (kvdev is not None and kvdev != "cpu-pinned"):
+        torch.cuda.synchronize()
+    return dto, cho, layers, _info_dict(info)

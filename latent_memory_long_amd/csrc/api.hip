@@ -10,8 +10,7 @@
 
 #include "../../include/msa.h"
 #include "launch.hpp"
-
-namespace {
+#include "status.hpp"
 
 thread_local std::string g_last_error;
 
@@ -24,6 +23,8 @@ msa_status fail(msa_status s, const char* fmt, ...) {
   g_last_error = buf;
   return s;
 }
+
+namespace {
 
 msa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return MSA_OK;
@@ -54,6 +55,7 @@ const char* msa_status_string(msa_status s) {
     case MSA_ERR_UNSUPPORTED: return "unsupported";
     case MSA_ERR_WORKSPACE: return "workspace too small";
     case MSA_ERR_HIP: return "HIP error";
+    case MSA_ERR_IO: return "file error";
   }
   return "unknown status";
 }

@@ -1,0 +1,85 @@
+"""A bank kept on disk and grown by appending documents: pool part of a corpus on the GPU,
+save it, load it into device and pinned host memory, pool the remaining documents after
+its rows, save and load again.  The result must equal, bit for bit, the bank pooled from
+the whole corpus in one call, and route and attend the same."""
+import numpy as np
+import pytest
+import torch
+
+import latent_memory_long_amd as M
+from synth import workloads as W
+from tests.helpers import say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _pool_layers(wl, lens, n_layers):
+    """Token states of every layer and their banks pooled in one call."""
+    off = W.token_offsets(lens)
+    coff = M.msa_chunk_offsets(off, wl.shape.chunk)
+    states, banks = [], []
+    for l in range(n_layers):
+        K, V, Kr = W.gen_token_states(W.layer(wl, l), lens, DEV)
+        states.append((K, V, Kr))
+        Kb, Vb, Krb = M.msa_pool(K, V, Kr, torch.tensor(off, device=DEV), torch.tensor(coff, device=DEV),
+                                 int(coff[-1]), wl.shape.chunk, wl.shape.rope_base)
+        banks.append((Krb, Kb, Vb))
+    return off, coff, states, banks
+
+
+def test_saved_bank_grows_by_appending(tmp_path):
+    say("case bank file: pool, save, load, append, save, load")
+    wl = W.workload("bank1m", bank_tokens=None, n_docs=70, len_dist=("loguniform", 30, 1500))
+    lens = W.doc_lengths(wl)
+    L, cut = 2, 41
+    off, coff, states, whole = _pool_layers(wl, lens, L)
+    torch.cuda.synchronize()
+    # the first `cut` documents, pooled and saved
+    offA = off[:cut + 1]
+    coffA = M.msa_chunk_offsets(offA, 64)
+    CA = int(coffA[-1])
+    partA = []
+    for K, V, Kr in states:
+        Kb, Vb, Krb = M.msa_pool(K[:offA[-1]], V[:offA[-1]], Kr[:offA[-1]], torch.tensor(offA, device=DEV),
+                                 torch.tensor(coffA, device=DEV), CA)
+        partA.append((Krb, Kb, Vb))
+    path = str(tmp_path / "bank.msab")
+    M.msa_bank_save(path, offA, coffA, partA)
+    # load it back, grow the arrays, pool the other documents after the existing rows
+    dto, cho, loaded, info = M.msa_bank_load(path, device=DEV)
+    assert np.array_equal(dto, offA) and np.array_equal(cho, coffA) and info["n_layers"] == L
+    offB = off[cut:] - off[cut]
+    coffB = M.msa_chunk_offsets(offB, 64)
+    C = CA + int(coffB[-1])
+    grown = []
+    for (Krb, Kb, Vb), (K, V, Kr) in zip(loaded, states):
+        big = [torch.empty((C,) + tuple(x.shape[1:]), dtype=x.dtype, device=DEV) for x in (Kb, Vb, Krb)]
+        for b, x in zip(big, (Kb, Vb, Krb)):
+            b[:CA].copy_(x)
+        t = slice(int(off[cut]), int(off[-1]))
+        M.msa_pool(K[t], V[t], Kr[t], torch.tensor(offB, device=DEV), torch.tensor(coffB, device=DEV), C - CA,
+                   out=tuple(b[CA:] for b in big))
+        grown.append((big[2], big[0], big[1]))
+    coff_g = np.concatenate([coffA, CA + coffB[1:]])
+    assert np.array_equal(coff_g, coff)
+    path2 = str(tmp_path / "bank2.msab")
+    M.msa_bank_save(path2, off, coff_g, grown)
+    # the grown bank, loaded with the content K/V in pinned host memory
+    dto2, cho2, final, _ = M.msa_bank_load(path2, device=DEV, kv_device="cpu-pinned")
+    assert np.array_equal(dto2, off) and np.array_equal(cho2, coff)
+    for (a_kr, a_k, a_v), (b_kr, b_k, b_v) in zip(whole, final):
+        assert b_k.is_pinned() and b_kr.is_cuda
+        assert torch.equal(a_kr, b_kr) and torch.equal(a_k.cpu(), b_k) and torch.equal(a_v.cpu(), b_v)
+    # routing and attention on the loaded bank match the in-memory one
+    q = W.gen_queries(wl, DEV, lq_override=[24])
+    q_off = torch.tensor([0, 24], dtype=torch.int32, device=DEV)
+    coff_d = torch.tensor(coff, device=DEV)
+    for (Krb, Kb, Vb), (lKrb, lKb, lVb) in zip(whole, final):
+        ids_a, sc_a = M.msa_route_topk(q["Qr"], q_off, 24, Krb, coff_d, 8)[:2]
+        ids_b, sc_b = M.msa_route_topk(q["Qr"], q_off, 24, lKrb, coff_d, 8)[:2]
+        assert torch.equal(ids_a, ids_b) and torch.equal(sc_a, sc_b)
+        o_a = M.msa_sparse_attn(q["Q"], q["Kloc"], q["Vloc"], q_off, q_off, 24, ids_a, coff_d, Kb, Vb)
+        o_b = M.msa_sparse_attn(q["Q"], q["Kloc"], q["Vloc"], q_off, q_off, 24, ids_b, coff_d, lKb, lVb)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b)
