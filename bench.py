@@ -41,9 +41,9 @@ SCAN_KERNEL = "route_scan_mfma"
 # HBM traffic of the scan kernel per launch, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # on this workload (scaled by the counters' reading of a copy kernel of known size).  It is
 # reported only while the kernel source still has the digest it was measured with.
-TRAFFIC = {"route_sha": "2d598e117809066d",
-           # FETCH_SIZE 1,588,779 KiB per launch x 1.99993 (a 1 GiB copy reads 524,306 KiB)
-           "fetch_bytes": 3253704763,
+TRAFFIC = {"route_sha": "87e317c342c9b9bb",
+           # FETCH_SIZE 1,588,783 KiB per launch x 1.99995 (a 1 GiB copy reads 524,302 KiB)
+           "fetch_bytes": 3253741422,
            # WRITE_SIZE 198.97 KiB per launch x 1.0 (a 1 GiB copy writes 1,048,576 KiB)
            "write_bytes": 203744}
 
