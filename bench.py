@@ -5,6 +5,10 @@
 One step is one query through the router and the sparse attention: the routing scan of
 every bank row (msa_route_scan), top-k document selection (msa_topk), and sparse attention
 over the selected documents' pooled K/V plus the query's local K/V (msa_sparse_attn).
+The timed steps run one query at a time.  A second run, reported apart as serving
+throughput, keeps --inflight queries in flight on separate streams (default 3), so one
+query's top-k and host-link-bound attention overlap other queries' HBM-bound scans, as
+concurrent requests do on a serving GPU.
 On the 100M-token bank the routing keys (3.25 GB) are in HBM and the content K/V are in
 pinned host memory, read over the host link when selected.  Inputs are resident before
 the timed region starts.  The pooling step (offline memory encoding) cannot run on the
@@ -415,6 +419,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bank100m_host")
     ap.add_argument("--queries", type=int, default=8, help="distinct queries cycled by the steps")
+    ap.add_argument("--inflight", type=int, default=3,
+                    help="queries in flight on separate streams for the extra serving-throughput run (1: none)")
     ap.add_argument("--decode-steps", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -450,41 +456,64 @@ def main():
     Lq = int(qs[0]["q_len"][0])
     k = wl.k
 
-    # buffers, allocated once
+    # buffers, allocated once per in-flight query slot
     q_off = torch.tensor([0, Lq], dtype=torch.int32, device=dev)
     kv_off = torch.tensor([0, Lq], dtype=torch.int32, device=dev)
-    ds = torch.empty((1, N), dtype=torch.float32, device=dev)
-    ids = torch.empty((1, k), dtype=torch.int32, device=dev)
-    sc = torch.empty((1, k), dtype=torch.float32, device=dev)
-    out = torch.empty((Lq, sh.hq, sh.d), dtype=torch.bfloat16, device=dev)
-    tws = torch.empty(max(M.msa_topk_workspace(1, N, k), 256), dtype=torch.uint8, device=dev)
-    ws = torch.empty(max(M.msa_sparse_attn_workspace(M.MSA_BF16, 1, 200, 200, 200, sh.hq, sh.h_kv, sh.d), 256),
-                     dtype=torch.uint8, device=dev)
+
+    def slot_buffers():
+        return {"ds": torch.empty((1, N), dtype=torch.float32, device=dev),
+                "ids": torch.empty((1, k), dtype=torch.int32, device=dev),
+                "sc": torch.empty((1, k), dtype=torch.float32, device=dev),
+                "out": torch.empty((Lq, sh.hq, sh.d), dtype=torch.bfloat16, device=dev),
+                "tws": torch.empty(max(M.msa_topk_workspace(1, N, k), 256), dtype=torch.uint8, device=dev),
+                "ws": torch.empty(max(M.msa_sparse_attn_workspace(M.MSA_BF16, 1, 200, 200, 200, sh.hq, sh.h_kv,
+                                                                  sh.d), 256), dtype=torch.uint8, device=dev)}
+
     pre = [(q["Qr"][:Lq].contiguous(), q["Q"][:Lq].contiguous(), q["Kloc"][:Lq].contiguous(),
             q["Vloc"][:Lq].contiguous()) for q in qs]
 
-    def step(i, ev):
-        Qr, Q, Kl, Vl = pre[i % len(pre)]
-        ev[0].record()
-        M.msa_route_scan(Qr, q_off, Lq, Krb, coff_d, out=ds)
-        ev[1].record()
-        M.msa_topk(ds, k, out=(ids, sc), workspace=tws)
-        ev[2].record()
-        M.msa_sparse_attn(Q, Kl, Vl, q_off, kv_off, Lq, ids, coff_d, Kb, Vb, rope_base=sh.rope_base,
-                          out=out, workspace=ws)
-        ev[3].record()
+    def run(n_slots, steps):
+        """`steps` timed steps, query i on stream i mod n_slots (default priority).  With one
+        slot the queries run one at a time.  With several, queries are in flight together
+        as concurrent requests are on a serving GPU: one query's top-k and host-link-bound
+        attention overlap other queries' HBM-bound scans, and scans overlap one another.
+        Per-step events are recorded on the step's own stream."""
+        streams = [torch.cuda.current_stream()] if n_slots == 1 else [torch.cuda.Stream() for _ in range(n_slots)]
+        slots = [slot_buffers() for _ in range(n_slots)]
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    wev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    for i in range(args.warmup):
-        step(i, wev)
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+        def step(i, ev):
+            Qr, Q, Kl, Vl = pre[i % len(pre)]
+            st, b = streams[i % n_slots], slots[i % n_slots]
+            ev[0].record(st)
+            M.msa_route_scan(Qr, q_off, Lq, Krb, coff_d, out=b["ds"], stream=st)
+            ev[1].record(st)
+            M.msa_topk(b["ds"], k, out=(b["ids"], b["sc"]), workspace=b["tws"], stream=st)
+            ev[2].record(st)
+            M.msa_sparse_attn(Q, Kl, Vl, q_off, kv_off, Lq, b["ids"], coff_d, Kb, Vb, rope_base=sh.rope_base,
+                              out=b["out"], workspace=b["ws"], stream=st)
+            ev[3].record(st)
+
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        wev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for i in range(args.warmup):
+            step(i, wev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, evs, slots[(steps - 1) % n_slots]["ids"]
+
+    log(f"timing {args.steps} steps, one query at a time")
+    wall, evs, ids = run(1, args.steps)
+    serving = None
+    if args.inflight > 1:
+        log(f"serving throughput: {args.steps} steps with {args.inflight} queries in flight")
+        wall_n, _, _ = run(args.inflight, args.steps)
+        t_n = wall_n / args.steps
+        serving = {"queries_in_flight": args.inflight, "ms_per_step": t_n * 1e3, "tokens_per_s": T / t_n,
+                   "krbar_tb_per_s": C * sh.h_r * sh.d * 2 / t_n / 1e12}
     # bytes the attention reads over the host link: K-bar and V-bar rows of the selected
     # documents (the last step's selection; the cycled queries select alike)
     sel = [int(d) for d in ids[0].cpu().numpy() if d >= 0]
@@ -503,6 +532,13 @@ def main():
     traffic = None
     if TRAFFIC and TRAFFIC.get("route_sha") == source_sha("route.hip"):
         traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+    out = torch.empty((Lq, sh.hq, sh.d), dtype=torch.bfloat16, device=dev)
+    ds = torch.empty((1, N), dtype=torch.float32, device=dev)
+    sc = torch.empty((1, k), dtype=torch.float32, device=dev)
+    ids = torch.empty((1, k), dtype=torch.int32, device=dev)
+    tws = torch.empty(max(M.msa_topk_workspace(1, N, k), 256), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(M.msa_sparse_attn_workspace(M.MSA_BF16, 1, 200, 200, 200, sh.hq, sh.h_kv, sh.d), 256),
+                     dtype=torch.uint8, device=dev)
 
     # decode: single-token steps after the prefill, routed again each step or reusing ids
     dec = {}
@@ -582,6 +618,7 @@ def main():
                        "route_attend_p90": round(pct(step_ms, 90), 4),
                        "scan_p50": round(pct(scan_ms, 50), 4), "topk_p50": round(pct(topk_ms, 50), 4),
                        "attend_p50": round(pct(attn_ms, 50), 4)},
+        "serving": serving,
         "roofline": {"kernel": SCAN_KERNEL, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
