@@ -34,9 +34,16 @@ namespace {
 
 // One lane's unit of one token row, as stored (converted to float when used).
 template <typename T> struct Raw;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 template <> struct Raw<bf16_t> {
   uint4 v;
-  __device__ __forceinline__ void load8(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  // Token rows are read once: the non-temporal hint keeps them from displacing other lines
+  // (10.8 ms instead of 11.7 ms for the 10M-token encode; on the rotated K's 8-byte halves
+  // it was slower, so those keep ordinary loads).
+  __device__ __forceinline__ void load8(const bf16_t* p) {
+    v = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+  }
   __device__ __forceinline__ void load4x2(const bf16_t* lo, const bf16_t* hi) {
     const uint2 x = *reinterpret_cast<const uint2*>(lo), y = *reinterpret_cast<const uint2*>(hi);
     v = make_uint4(x.x, x.y, y.x, y.y);
