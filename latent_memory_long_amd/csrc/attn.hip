@@ -181,10 +181,10 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
       l_run[m] = l_run[m] * alpha + ps;
       // P^T operand: k-slot g4*8 + j  <->  key g4*4 + j (j < 4), 16 + g4*4 + (j-4) (j >= 4)
       uint4 pw;
-      pw.x = f32_to_bf16(p[0][0]) | (f32_to_bf16(p[0][1]) << 16);
-      pw.y = f32_to_bf16(p[0][2]) | (f32_to_bf16(p[0][3]) << 16);
-      pw.z = f32_to_bf16(p[1][0]) | (f32_to_bf16(p[1][1]) << 16);
-      pw.w = f32_to_bf16(p[1][2]) | (f32_to_bf16(p[1][3]) << 16);
+      pw.x = f32x2_to_bf16x2(p[0][0], p[0][1]);
+      pw.y = f32x2_to_bf16x2(p[0][2], p[0][3]);
+      pw.z = f32x2_to_bf16x2(p[1][0], p[1][1]);
+      pw.w = f32x2_to_bf16x2(p[1][2], p[1][3]);
       const bf16x8_t Pf = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
       for (int md = 0; md < MD; ++md) {

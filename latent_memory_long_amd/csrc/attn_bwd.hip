@@ -126,7 +126,7 @@ __device__ __forceinline__ void bwd_commit(int tid, const uint4 (&stage)[UPT], b
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return f32x2_to_bf16x2(lo, hi);
 }
 
 template <int D, int NW, int MTW>

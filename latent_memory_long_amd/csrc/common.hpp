@@ -15,12 +15,18 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// float32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+// float32 -> bf16, round to nearest, ties to even (NaN stays NaN): gfx950 converts in
+// hardware, two values per v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// two floats -> packed bf16 pair (a in the low half)
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Unpack 8 bf16 (one 16-byte word) into floats.
@@ -38,17 +44,17 @@ __device__ __forceinline__ void unpack4(const uint2& w, float* f) {
 
 __device__ __forceinline__ uint4 pack8(const float* f) {
   uint4 w;
-  w.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
-  w.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
-  w.z = f32_to_bf16(f[4]) | (f32_to_bf16(f[5]) << 16);
-  w.w = f32_to_bf16(f[6]) | (f32_to_bf16(f[7]) << 16);
+  w.x = f32x2_to_bf16x2(f[0], f[1]);
+  w.y = f32x2_to_bf16x2(f[2], f[3]);
+  w.z = f32x2_to_bf16x2(f[4], f[5]);
+  w.w = f32x2_to_bf16x2(f[6], f[7]);
   return w;
 }
 
 __device__ __forceinline__ uint2 pack4(const float* f) {
   uint2 w;
-  w.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
-  w.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
+  w.x = f32x2_to_bf16x2(f[0], f[1]);
+  w.y = f32x2_to_bf16x2(f[2], f[3]);
   return w;
 }
 
@@ -180,7 +186,6 @@ __device__ __forceinline__ float wave_max_all(float v) {
 }
 
 // bf16 pair dot product accumulated in float32 (v_dot2_f32_bf16).
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
                                          c, false);
