@@ -108,6 +108,9 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
     for (int md = 0; md < MD; ++md) acc[m][md] = {0.f, 0.f, 0.f, 0.f};
   }
 
+  // the smallest causal limit over the block's rows (its first row's)
+  const int64_t key_lim_min = M + (int64_t)(Lkv - Lq + rb / G);
+
   TileSrc ts;
   ts.Kb = (const bf16_t*)a.Kbar;
   ts.Vb = (const bf16_t*)a.Vbar;
@@ -121,16 +124,12 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
   ts.kv0 = kv0;
   ts.M = M;
   ts.k_hi = k_hi;
-  uint4 stage[UPT];
-
-  if (k_lo < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, k_lo, stage);
-  int it = 0;
-  for (int64_t kt = k_lo; kt < k_hi; kt += KT, ++it) {
-    const int buf = it & 1;
-    tile_commit<D, THREADS, UPT, KSTR, VSTR>(tid, stage, Ks[buf], Vt[buf]);
-    __syncthreads();  // tile visible; the other buffer is free again
-    if (kt + KT < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, kt + KT, stage);  // in flight during the math
-
+  // Two tiles of loads in flight: register stages A and B take turns (a tile is fetched
+  // two tiles ahead of its use), so the gather latency spans two tiles of math.
+  uint4 stA[UPT], stB[UPT];
+  auto tile_math = [&](int buf, int64_t kt) __attribute__((always_inline)) {
+    // every key of the tile is visible to every row of the block: no masking needed
+    const bool full_tile = kt + KT <= k_hi && kt + KT - 1 <= key_lim_min && rb + ROWS <= nrows;
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       // ---- S^T = K Q^T for two 16-key halves ----
@@ -144,17 +143,25 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
           s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), Qf[m][kk], s[n], 0, 0, 0);
         }
       }
-      // lane holds S[row cl of tile m][key kt + n*16 + g4*4 + i]
+      // lane holds S[row cl of tile m][key kt + n*16 + g4*4 + i]; the running max is kept
+      // on the raw scores (scale_log2 > 0 keeps their order), scaled inside the exponent
       float mx = -INFINITY;
+      if (full_tile) {
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t key = kt + n * 16 + g4 * 4 + i;
-          const bool vis = row_ok[m] && key < k_hi && key <= key_lim[m];
-          s[n][i] = vis ? s[n][i] * scale_log2 : -INFINITY;
-          mx = fmaxf(mx, s[n][i]);
-        }
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[n][i]);
+      } else {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t key = kt + n * 16 + g4 * 4 + i;
+            const bool vis = row_ok[m] && key < k_hi && key <= key_lim[m];
+            s[n][i] = vis ? s[n][i] : -INFINITY;
+            mx = fmaxf(mx, s[n][i]);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run[m], mx);
@@ -166,11 +173,12 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) p[n][i] = 0.f;
       } else {
-        alpha = exp2f(m_run[m] - m_new);
+        const float mb = m_new * scale_log2;
+        alpha = exp2f(m_run[m] * scale_log2 - mb);
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[n][i] = exp2f(s[n][i] - m_new);
+          for (int i = 0; i < 4; ++i) p[n][i] = exp2f(fmaf(s[n][i], scale_log2, -mb));
       }
       m_run[m] = m_new;
       float ps = 0.f;
@@ -186,17 +194,36 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
       pw.z = f32x2_to_bf16x2(p[1][0], p[1][1]);
       pw.w = f32x2_to_bf16x2(p[1][2], p[1][3]);
       const bf16x8_t Pf = __builtin_bit_cast(bf16x8_t, pw);
+      // the output columns are rescaled only when some row's maximum moved (alpha != 1)
+      const bool rescale = __ballot(alpha != 1.f) != 0;
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
         const bf16_t* vr = &Vt[buf][(md * 16 + cl) * VSTR];
         const uint2 v0 = *reinterpret_cast<const uint2*>(vr + g4 * 4);
         const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + g4 * 4);
         const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        if (rescale) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][md][i] *= alpha;
+          for (int i = 0; i < 4; ++i) acc[m][md][i] *= alpha;
+        }
         acc[m][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vf, Pf, acc[m][md], 0, 0, 0);
       }
     }
+  };
+  if (k_lo < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, k_lo, stA);
+  if (k_lo + KT < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, k_lo + KT, stB);
+  for (int64_t kt = k_lo; kt < k_hi;) {
+    tile_commit<D, THREADS, UPT, KSTR, VSTR>(tid, stA, Ks[0], Vt[0]);
+    __syncthreads();  // tile visible; the other buffer is free again
+    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, kt + 2 * KT, stA);
+    tile_math(0, kt);
+    kt += KT;
+    if (kt >= k_hi) break;
+    tile_commit<D, THREADS, UPT, KSTR, VSTR>(tid, stB, Ks[1], Vt[1]);
+    __syncthreads();
+    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, kt + 2 * KT, stB);
+    tile_math(1, kt);
+    kt += KT;
   }
 
 #pragma unroll
@@ -222,7 +249,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
         *reinterpret_cast<float4*>(po + md * 16) =
             make_float4(acc[m][md][0], acc[m][md][1], acc[m][md][2], acc[m][md][3]);
       if (g4 == 0) {
-        a.part_ml[prow * 2] = m_run[m];
+        a.part_ml[prow * 2] = m_run[m] * scale_log2;  // the combine works on scaled maxima
         a.part_ml[prow * 2 + 1] = l_row;
       }
     }
