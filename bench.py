@@ -141,6 +141,7 @@ def time_batch(dev, bank, reps=20):
     tws = torch.empty(max(M.msa_topk_workspace(B, N, wl.k), 256), dtype=torch.uint8, device=dev)
     ws = torch.empty(max(M.msa_sparse_attn_workspace(M.MSA_BF16, B, tq, tq, Lmax, sh.hq, sh.h_kv, sh.d), 256),
                      dtype=torch.uint8, device=dev)
+    lse = torch.empty((tq, sh.hq), dtype=torch.float32, device=dev)   # kept for the backward
 
     def run(ev):
         ev[0].record()
@@ -149,7 +150,7 @@ def time_batch(dev, bank, reps=20):
         M.msa_topk(ds, wl.k, out=(ids, sc), workspace=tws)
         ev[2].record()
         M.msa_sparse_attn(Q, Kl, Vl, q_off_d, q_off_d, Lmax, ids, coff_d, Kb, Vb, rope_base=sh.rope_base,
-                          out=out, workspace=ws)
+                          out=out, workspace=ws, lse=lse)
         ev[3].record()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps + 2)]
@@ -188,7 +189,7 @@ def time_batch(dev, bank, reps=20):
     def run_bwd(ev):
         ev[0].record()
         M.msa_sparse_attn_backward(Q, Kl, Vl, q_off_d, q_off_d, Lmax, ids, coff_d, Kb, Vb, out, dO,
-                                   rope_base=sh.rope_base, dbank=gb, out=gq, workspace=bws)
+                                   rope_base=sh.rope_base, dbank=gb, out=gq, workspace=bws, lse=lse)
         ev[1].record()
         M.msa_route_backward(Qr, q_off_d, Lmax, Krb, coff_d, dD, dKrbar=dKr, out=dQr, workspace=rws)
         ev[2].record()
@@ -211,7 +212,7 @@ def time_batch(dev, bank, reps=20):
     bflops = 10.0 * pairs * sh.hq * sh.d
     t_abwd = pct(abwd, 50) / 1e3
     bwd = {"workload": "batch32_bank10m (training backward)", "attend_pairs": pairs,
-           "attend_backward_p50_ms": round(pct(abwd, 50), 4),
+           "attend_backward_p50_ms": round(pct(abwd, 50), 4), "attend_backward_lse": "from the forward",
            "attend_backward_tflops": bflops / t_abwd / 1e12,
            "attend_backward_mfma_util": bflops / t_abwd / 1e12 / MFMA_PEAK_BF16_TFLOPS,
            "attend_forward_tflops": 0.4 * bflops / (pct(attn, 50) / 1e3) / 1e12,

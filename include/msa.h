@@ -285,6 +285,9 @@ size_t msa_sparse_attn_workspace(msa_dtype dtype, int32_t n_queries, int64_t tot
  *   token Lkv - Lq + t and attends to every memory row and to local tokens <= its own.
  *   Query head hq reads kv head hq / (hq_count / h_kv).  scale 0 means 1/sqrt(d).
  *   O          [total_q, hq, d] output.
+ *   lse        optional (NULL: not written) device float [total_q, hq], output: the natural
+ *              log of each row's softmax normaliser, ln sum_j exp(scale * q . k_j) over the
+ *              keys the row sees.  msa_sparse_attn_backward takes it to skip recomputing it.
  *   Supported: d in {32, 64, 128}; hq % h_kv == 0; 1 <= k <= 1024.
  */
 msa_status msa_sparse_attn(msa_dtype dtype, int32_t n_queries, int64_t total_q,
@@ -294,7 +297,8 @@ msa_status msa_sparse_attn(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                            float rope_base, float scale, int32_t k, const int32_t* topk_ids,
                            int32_t n_docs, int64_t n_chunks, const int64_t* chunk_off,
                            const void* Kbar, const void* Vbar, int32_t kv_source, void* O,
-                           void* workspace, size_t workspace_bytes, msa_stream_t stream);
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           msa_stream_t stream);
 
 /* Bytes of workspace msa_sparse_attn_backward needs for these sizes (0 if unsupported). */
 size_t msa_sparse_attn_backward_workspace(int64_t total_q, int64_t total_kv, int32_t hq,
@@ -307,6 +311,8 @@ size_t msa_sparse_attn_backward_workspace(int64_t total_q, int64_t total_kv, int
  * to end).  For L = sum(dO * O), O = msa_sparse_attn(...) with the same arguments:
  *   The first 23 arguments are those of msa_sparse_attn (same meaning, same layout).
  *   O          [total_q, hq, d]: the forward output for these inputs.
+ *   lse        optional [total_q, hq]: the forward's lse output for these inputs; NULL
+ *              recomputes it (one more pass over the keys).
  *   dO         [total_q, hq, d]: dL/dO.
  *   dQ         device float [total_q, hq, d], overwritten: dL/dQ (the un-rotated input).
  *   dKloc      device float [total_kv, h_kv, d], overwritten: dL/dKloc (un-rotated input).
@@ -327,7 +333,8 @@ msa_status msa_sparse_attn_backward(msa_dtype dtype, int32_t n_queries, int64_t 
                                     float rope_base, float scale, int32_t k,
                                     const int32_t* topk_ids, int32_t n_docs, int64_t n_chunks,
                                     const int64_t* chunk_off, const void* Kbar, const void* Vbar,
-                                    int32_t kv_source, const void* O, const void* dO, float* dQ,
+                                    int32_t kv_source, const void* O, const float* lse,
+                                    const void* dO, float* dQ,
                                     float* dKloc, float* dVloc, float* dKbar, float* dVbar,
                                     void* workspace, size_t workspace_bytes, msa_stream_t stream);
 

@@ -60,11 +60,11 @@ def _load() -> ctypes.CDLL:
                                           P, I32, P, P, P, P, SZ, P]),
         "msa_sparse_attn_workspace": (SZ, [ctypes.c_int, I32, I64, I64, I32, I32, I32, I32]),
         "msa_sparse_attn": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, P, P, P, I32, I32,
-                                           I32, F, F, I32, P, I32, I64, P, P, P, I32, P, P, SZ, P]),
+                                           I32, F, F, I32, P, I32, I64, P, P, P, I32, P, P, P, SZ, P]),
         "msa_sparse_attn_backward_workspace": (SZ, [I64, I64, I32, I32, I32]),
         "msa_sparse_attn_backward": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, P, P, P, I32,
                                                     I32, I32, F, F, I32, P, I32, I64, P, P, P, I32, P, P,
-                                                    P, P, P, P, P, P, SZ, P]),
+                                                    P, P, P, P, P, P, P, SZ, P]),
         "msa_route_aux_loss": (ctypes.c_int, [I32, I32, I32, P, P, F, P, P, P]),
         "msa_bank_save": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(BankInfo), P, P, P, P, P]),
         "msa_bank_read_info": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(BankInfo)]),
@@ -230,9 +230,12 @@ def msa_sparse_attn(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Tensor, q_o
                     kv_off: torch.Tensor, max_q_len: int, topk_ids: torch.Tensor,
                     chunk_off: torch.Tensor, Kbar: torch.Tensor, Vbar: torch.Tensor,
                     rope_base: float = 1e6, scale: float = 0.0, out: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None):
+                    workspace: Optional[torch.Tensor] = None, stream=None,
+                    lse: Optional[torch.Tensor] = None):
     """Step D.  Q [total_q, hq, d]; Kloc/Vloc [total_kv, h_kv, d]; Kbar/Vbar [C, h_kv, d] on the
-    device, or in pinned host memory (then read over the host link).  Returns O."""
+    device, or in pinned host memory (then read over the host link).  Returns O.  Pass a
+    float32 [total_q, hq] device tensor as `lse` to also get each row's log-sum-exp (natural
+    log), which msa_sparse_attn_backward can reuse."""
     B = q_off.numel() - 1
     total_q, hq, d = Q.shape
     total_kv, h_kv, _ = Kloc.shape
@@ -245,14 +248,20 @@ def msa_sparse_attn(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Tensor, q_o
     if out is None:
         out = torch.empty_like(Q)
     code = _dtype_code(Q)
+    _check_lse(lse, total_q, hq)
     need = msa_sparse_attn_workspace(code, B, total_q, total_kv, max_q_len, hq, h_kv, d)
     ws = _workspace(need, dev, workspace)
     _check(lib.msa_sparse_attn(code, B, total_q, total_kv, _ptr(q_off), _ptr(kv_off), max_q_len,
                                _ptr(Q), _ptr(Kloc), _ptr(Vloc), hq, h_kv, d, rope_base, scale, k,
                                _ptr(topk_ids), N, Kbar.shape[0], _ptr(chunk_off), _ptr(Kbar),
-                               _ptr(Vbar), kv_source, _ptr(out), _ptr(ws),
+                               _ptr(Vbar), kv_source, _ptr(out), _ptr(lse), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
     return out
+
+
+def _check_lse(lse: Optional[torch.Tensor], total_q: int, hq: int):
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (total_q, hq) or not lse.is_cuda):
+        raise MsaError(MSA_ERR_INVALID_ARG, f"lse must be a float32 device tensor of shape ({total_q}, {hq})")
 
 
 def msa_sparse_attn_backward_workspace(total_q: int, total_kv: int, hq: int, h_kv: int, d: int) -> int:
@@ -264,10 +273,12 @@ def msa_sparse_attn_backward(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Te
                              chunk_off: torch.Tensor, Kbar: torch.Tensor, Vbar: torch.Tensor,
                              O: torch.Tensor, dO: torch.Tensor, rope_base: float = 1e6, scale: float = 0.0,
                              dbank: Optional[tuple] = None, out: Optional[tuple] = None,
-                             workspace: Optional[torch.Tensor] = None, stream=None):
+                             workspace: Optional[torch.Tensor] = None, stream=None,
+                             lse: Optional[torch.Tensor] = None):
     """Backward of step D.  Returns (dQ, dKloc, dVloc, dKbar, dVbar), float32.  dKbar / dVbar
     ([n_chunks, h_kv, d] on the device) are added to: pass `dbank` to accumulate into your
-    own arrays, else zero-filled ones are made."""
+    own arrays, else zero-filled ones are made.  `lse`: the forward's log-sum-exp output for
+    the same inputs, which saves recomputing it."""
     B = q_off.numel() - 1
     total_q, hq, d = Q.shape
     total_kv, h_kv, _ = Kloc.shape
@@ -287,12 +298,14 @@ def msa_sparse_attn_backward(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Te
         dbank = (torch.zeros((C, h_kv, d), dtype=f32, device=dev), torch.zeros((C, h_kv, d), dtype=f32, device=dev))
     dQ, dKl, dVl = out
     dKb, dVb = dbank
+    _check_lse(lse, total_q, hq)
     need = msa_sparse_attn_backward_workspace(total_q, total_kv, hq, h_kv, d)
     ws = _workspace(need, dev, workspace)
     _check(lib.msa_sparse_attn_backward(_dtype_code(Q), B, total_q, total_kv, _ptr(q_off), _ptr(kv_off),
                                         max_q_len, _ptr(Q), _ptr(Kloc), _ptr(Vloc), hq, h_kv, d, rope_base,
                                         scale, k, _ptr(topk_ids), N, C, _ptr(chunk_off), _ptr(Kbar),
-                                        _ptr(Vbar), kv_source, _ptr(O), _ptr(dO), _ptr(dQ), _ptr(dKl),
+                                        _ptr(Vbar), kv_source, _ptr(O), _ptr(lse), _ptr(dO), _ptr(dQ),
+                                        _ptr(dKl),
                                         _ptr(dVl), _ptr(dKb), _ptr(dVb), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)))
     return dQ, dKl, dVl, dKb, dVb

@@ -269,8 +269,8 @@ msa_status msa_sparse_attn(msa_dtype dtype, int32_t n_queries, int64_t total_q, 
                            int32_t h_kv, int32_t d, float rope_base, float scale, int32_t k,
                            const int32_t* topk_ids, int32_t n_docs, int64_t n_chunks,
                            const int64_t* chunk_off, const void* Kbar, const void* Vbar,
-                           int32_t kv_source, void* O, void* workspace, size_t workspace_bytes,
-                           msa_stream_t stream) {
+                           int32_t kv_source, void* O, float* lse, void* workspace,
+                           size_t workspace_bytes, msa_stream_t stream) {
   g_last_error.clear();
   if (dtype != MSA_F32 && dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   if (n_queries < 1 || n_queries > 65535) return fail(MSA_ERR_INVALID_ARG, "n_queries %d not in [1, 65535]", n_queries);
@@ -304,7 +304,7 @@ msa_status msa_sparse_attn(msa_dtype dtype, int32_t n_queries, int64_t total_q, 
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   msa::AttnArgs a{(int)dtype, n_queries, total_q, total_kv, q_off, kv_off, max_q_len, Q, Kloc, Vloc,
                   hq, h_kv, d, rope_base, sc, k, topk_ids, n_docs, n_chunks, chunk_off, kb, vb, O,
-                  workspace};
+                  lse, workspace};
   return hip_status(msa::launch_sparse_attn(a, (hipStream_t)stream), "msa_sparse_attn launch");
 }
 
@@ -320,7 +320,8 @@ msa_status msa_sparse_attn_backward(msa_dtype dtype, int32_t n_queries, int64_t 
                                     int32_t h_kv, int32_t d, float rope_base, float scale, int32_t k,
                                     const int32_t* topk_ids, int32_t n_docs, int64_t n_chunks,
                                     const int64_t* chunk_off, const void* Kbar, const void* Vbar,
-                                    int32_t kv_source, const void* O, const void* dO, float* dQ,
+                                    int32_t kv_source, const void* O, const float* lse,
+                                    const void* dO, float* dQ,
                                     float* dKloc, float* dVloc, float* dKbar, float* dVbar,
                                     void* workspace, size_t workspace_bytes, msa_stream_t stream) {
   g_last_error.clear();
@@ -355,8 +356,9 @@ msa_status msa_sparse_attn_backward(msa_dtype dtype, int32_t n_queries, int64_t 
   msa::AttnBwdArgs a{};
   a.f = msa::AttnArgs{(int)dtype, n_queries, total_q, total_kv, q_off, kv_off, max_q_len, Q, Kloc, Vloc,
                       hq, h_kv, d, rope_base, scale, k, topk_ids, n_docs, n_chunks, chunk_off, kb, vb,
-                      nullptr, workspace};
+                      nullptr, nullptr, workspace};
   a.O = O;
+  a.lse = lse;
   a.dO = dO;
   a.dQ = dQ;
   a.dKloc = dKloc;

@@ -234,6 +234,8 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
     if (!row_ok[m]) continue;
     const int64_t orow = (int64_t)(q0 + t_of[m]) * hq_n + hq_of[m];
     if (a.splits == 1) {
+      if (a.lse != nullptr && g4 == 0)
+        a.lse[orow] = l_row > 0.f ? (m_run[m] * scale_log2 + log2f(l_row)) * LN2 : -INFINITY;
       const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
       bf16_t* o = (bf16_t*)a.O + orow * D + g4 * 4;
 #pragma unroll
@@ -307,6 +309,7 @@ __global__ __launch_bounds__(64) void attn_valu(AttnK a) {
   for (int j = 0; j <= Lkv - Lq + t; ++j)
     visit(Kr + ((int64_t)(kv0 + j) * a.h_kv + g) * D, Vl + ((int64_t)(kv0 + j) * a.h_kv + g) * D);
   T* o = (T*)a.O + ((int64_t)(q0 + t) * a.hq + hq) * D;
+  if (a.lse != nullptr) a.lse[(int64_t)(q0 + t) * a.hq + hq] = l > 0.f ? (m + log2f(l)) * LN2 : -INFINITY;
   const float inv = 1.0f / l;
 #pragma unroll
   for (int e = 0; e < D; e += 8) {
@@ -346,6 +349,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnK a) {
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
+  if (a.lse != nullptr && lane == 0) a.lse[row] = L > 0.f ? (mstar + log2f(L)) * LN2 : -INFINITY;
   bf16_t* out = (bf16_t*)a.O + row * D;
 #pragma unroll
   for (int x = 0; x < PER; ++x) {
@@ -441,13 +445,14 @@ hipError_t launch_sparse_attn(const AttnArgs& r, hipStream_t s) {
   k.hq = r.hq;
   k.h_kv = r.h_kv;
   k.rope_base = r.rope_base;
-  k.scale_log2 = r.scale * 1.4426950408889634f;
+  k.scale_log2 = r.scale * LOG2E;
   k.k = r.k;
   k.ids = r.ids;
   k.chunk_off = r.chunk_off;
   k.Kbar = r.Kbar;
   k.Vbar = r.Vbar;
   k.O = r.O;
+  k.lse = r.lse;
   const size_t esz = r.dtype == 0 ? 4 : 2;
   char* ws = (char*)r.workspace;
   k.Qrot = ws;

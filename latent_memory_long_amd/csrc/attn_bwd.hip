@@ -13,15 +13,18 @@
 //
 // Kernels (bf16 inputs, float32 gradients, MFMA with float32 accumulation):
 //  * rope_local (shared with the forward): rotated Q and local K into the workspace.
-//  * bwd_dq: one workgroup per (query, kv head, block of query rows), like the forward.  A
-//    first pass over the key tiles recomputes each row's log-sum-exp; a second computes
-//    S^T = K Q~^T, P^T, dP^T = V dO^T and dS^T in registers and accumulates
-//    dQ~^T = K^T dS^T.  It stores the rows' log-sum-exp and rowsum(dO O) for bwd_dkv.
-//  * bwd_dkv: workgroups over blocks of keys of a (query, kv head); each wave owns a
-//    16-key tile and walks all query rows of the kv head in 16-row tiles staged in LDS.
-//    S = Q~ K^T leaves every lane with 4 probabilities of one key, which are exactly the
-//    A operand of the 16x16x16 products dV += P^T dO and dK += dS^T Q~, so nothing is
-//    transposed in registers.
+//  * bwd_dq: one workgroup per (query, kv head, block of query rows), like the forward.
+//    Unless the forward's per-row log-sum-exp is passed in, a first pass over the key tiles
+//    recomputes it; the second computes S^T = K Q~^T, P^T, dP^T = V dO^T and dS^T in
+//    registers and accumulates dQ~^T = K^T dS^T, reading K^T straight from the row-major
+//    key tile with gfx950's transposing LDS load.  It stores the rows' log-sum-exp and
+//    rowsum(dO O) for bwd_dkv.
+//  * bwd_dkv: workgroups over blocks of keys of a (query, kv head); each wave keeps one
+//    16-key tile of K and V in registers and walks all query rows of the kv head in 32-row
+//    stages (Q~ and dO staged in LDS one stage ahead through registers).  S = Q~ K^T leaves
+//    every lane with probabilities of one key over 4 rows of each 16-row half, which are the
+//    A operand of the 16x16x32 products dV += P^T dO and dK += dS^T Q~; their B operands are
+//    read transposed from the row-major stage.
 //  * rope_unrotate: turns dQ and the local dK back to the un-rotated inputs, in place.
 #include <math.h>
 
@@ -45,6 +48,7 @@ struct BwdK {
   float* dVb;      // [n_chunks, h_kv, D], accumulated
   float* lse;      // [total_q * hq]: log2 of sum_k 2^(s * scale_log2)
   float* drow;     // [total_q * hq]: rowsum(dO * O)
+  const float* lse_in;  // optional: the forward's per-row log-sum-exp (natural log)
   float scale;     // softmax scale (natural)
   int kblocks;     // bwd_dkv workgroups per (query, kv head)
 };
@@ -71,56 +75,47 @@ __device__ __forceinline__ int64_t key_row(const int64_t* mstart, const int64_t*
 }
 
 // ---- dQ and the row statistics -----------------------------------------------------
-// Tile staging: K row-major (A of S^T), K transposed (A of dQ^T), V row-major (A of dP^T).
+// Tile staging: K and V row-major (A operands of S^T and dP^T; dQ^T reads K transposed).
+// Stage slot j < UPK holds K unit tid + j*THREADS of the tile, slot UPK + j the V unit of
+// the same key and elements, so each key's source row is located once.
+template <int D, int THREADS>
+constexpr int bwd_upk() { return (KT * (D / 8) + THREADS - 1) / THREADS; }
+
 template <int D, int THREADS, int UPT, bool WITHV>
 __device__ __forceinline__ void bwd_fetch(const TileSrc ts, int tid, int64_t kt, uint4 (&stage)[UPT]) {
   constexpr int UPR = D / 8;
-  constexpr int UNITS = (WITHV ? 2 : 1) * KT * UPR;
+  constexpr int UPK = bwd_upk<D, THREADS>();
 #pragma unroll
-  for (int j = 0; j < UPT; ++j) {
+  for (int j = 0; j < UPK; ++j) {
     const int u = tid + j * THREADS;
-    uint4 wv = make_uint4(0, 0, 0, 0);
-    if (u < UNITS) {
-      const bool isv = u >= KT * UPR;
-      const int uu = isv ? u - KT * UPR : u;
-      const int kr = uu / UPR, e0 = (uu % UPR) * 8;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
+    if (u < KT * UPR) {
+      const int kr = u / UPR, e0 = (u % UPR) * 8;
       const int64_t key = kt + kr;
       if (key < ts.k_hi) {
         bool bank;
         int64_t row;
-        const int64_t off = key_row(ts.mstart, ts.mpre, ts.keff, ts.M, key, ts.kv0, ts.hkv, ts.g, D, bank, row);
-        const bf16_t* p = bank ? (isv ? ts.Vb : ts.Kb) : (isv ? ts.Vl : ts.Kr);
-        wv = *reinterpret_cast<const uint4*>(p + off + e0);
+        const int64_t off = key_row(ts.mstart, ts.mpre, ts.keff, ts.M, key, ts.kv0, ts.hkv, ts.g, D, bank, row) + e0;
+        kv = *reinterpret_cast<const uint4*>((bank ? ts.Kb : ts.Kr) + off);
+        if (WITHV) vv = *reinterpret_cast<const uint4*>((bank ? ts.Vb : ts.Vl) + off);
       }
     }
-    stage[j] = wv;
+    stage[j] = kv;
+    if (WITHV) stage[UPK + j] = vv;
   }
 }
 
-template <int D, int THREADS, int UPT, int KSTR, int TSTR, bool WITHV>
-__device__ __forceinline__ void bwd_commit(int tid, const uint4 (&stage)[UPT], bf16_t* Ks, bf16_t* Kt, bf16_t* Vs) {
+template <int D, int THREADS, int UPT, int KSTR, bool WITHV>
+__device__ __forceinline__ void bwd_commit(int tid, const uint4 (&stage)[UPT], bf16_t* Ks, bf16_t* Vs) {
   constexpr int UPR = D / 8;
-  constexpr int UNITS = (WITHV ? 2 : 1) * KT * UPR;
+  constexpr int UPK = bwd_upk<D, THREADS>();
 #pragma unroll
-  for (int j = 0; j < UPT; ++j) {
+  for (int j = 0; j < UPK; ++j) {
     const int u = tid + j * THREADS;
-    if (u < UNITS) {
-      const bool isv = u >= KT * UPR;
-      const int uu = isv ? u - KT * UPR : u;
-      const int kr = uu / UPR, e0 = (uu % UPR) * 8;
-      if (isv) {
-        *reinterpret_cast<uint4*>(&Vs[kr * KSTR + e0]) = stage[j];
-      } else {
-        *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = stage[j];
-        if (WITHV) {
-          const uint32_t w[4] = {stage[j].x, stage[j].y, stage[j].z, stage[j].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            Kt[(e0 + 2 * q) * TSTR + kr] = (bf16_t)(w[q] & 0xffffu);
-            Kt[(e0 + 2 * q + 1) * TSTR + kr] = (bf16_t)(w[q] >> 16);
-          }
-        }
-      }
+    if (u < KT * UPR) {
+      const int kr = u / UPR, e0 = (u % UPR) * 8;
+      *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = stage[j];
+      if (WITHV) *reinterpret_cast<uint4*>(&Vs[kr * KSTR + e0]) = stage[UPK + j];
     }
   }
 }
@@ -129,19 +124,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32x2_to_bf16x2(lo, hi);
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane L
+// names 4 consecutive 16-bit elements E[L][0..3]; lane i receives E[i/4 + 4j][i%4] for
+// j = 0..3.  Pointing lane L at row r0 + L/4, column c0 + 4*(L%4) of a row-major tile thus
+// hands lane i the column c0 + i over rows r0 .. r0+3: the k-contiguous B operand of a
+// product that sums over rows.
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 template <int D, int NW, int MTW>
 __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
   const AttnK& a = bk.f;
   constexpr int KK = D / 32;
   constexpr int MD = D / 16;
-  constexpr int KSTR = D + 8;
-  constexpr int TSTR = KT + 8;
+  constexpr int KSTR = D + 16;  // 32 bytes of padding: row and transposed reads are conflict-free
   constexpr int THREADS = 64 * NW;
-  constexpr int UPT = (2 * KT * (D / 8) + THREADS - 1) / THREADS;
+  constexpr int UPT = 2 * bwd_upk<D, THREADS>();
   constexpr int ROWS = NW * MTW * 16;
   __shared__ __align__(16) bf16_t Ks[2][KT * KSTR];
   __shared__ __align__(16) bf16_t Vs[2][KT * KSTR];
-  __shared__ __align__(16) bf16_t Kt[2][D * TSTR];
   __shared__ int64_t mstart[1025], mpre[1025];
   __shared__ int sh_keff;
   __shared__ int64_t sh_M;
@@ -218,11 +223,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
   ts.kv0 = kv0;
   ts.M = M;
   ts.k_hi = k_hi;
-  uint4 stage[UPT];
+
+  // the smallest causal limit over the block's rows (its first row's)
+  const int64_t key_lim_min = M + (int64_t)(Lkv - Lq + rb / G);
 
   // S^T for row tile m and key tile kt from Ks: s[n][i] = logit (log2 units) of key
-  // kt + n*16 + g4*4 + i for row cl, -inf where not visible
+  // kt + n*16 + g4*4 + i for row cl, -inf where not visible.  A tile whose keys every row
+  // of the block sees skips the masks.
   auto logits = [&](const bf16_t* ks, int m, int64_t kt, float (&s)[2][4]) __attribute__((always_inline)) {
+    const bool full = kt + KT <= k_hi && kt + KT - 1 <= key_lim_min && rb + ROWS <= nrows;
+    // limits relative to kt, clamped into int range: visible iff rel < hi_rel && rel <= lim_rel
+    const int hi_rel = (int)(k_hi - kt < KT ? k_hi - kt : KT);
+    const int64_t lr = key_lim[m] - kt;
+    const int lim_rel = row_ok[m] ? (int)(lr < -1 ? -1 : (lr > KT ? KT : lr)) : -1;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -233,59 +246,81 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t key = kt + n * 16 + g4 * 4 + i;
-        s[n][i] = (row_ok[m] && key < k_hi && key <= key_lim[m]) ? acc[i] * sl2 : -INFINITY;
+        const int rel = n * 16 + g4 * 4 + i;
+        s[n][i] = (full || (rel < hi_rel && rel <= lim_rel)) ? acc[i] * sl2 : -INFINITY;
       }
     }
   };
 
-  // ---- pass 1: log-sum-exp of every row ----
-  float m_run[MTW], l_run[MTW];
+  // Two tiles of loads in flight: register stages A and B take turns.
+  uint4 stA[UPT], stB[UPT];
+  // ---- pass 1: log-sum-exp of every row (log2 units), unless the forward's is given ----
+  float lse[MTW];
+  if (bk.lse_in == nullptr) {
+    float m_run[MTW], l_run[MTW];
 #pragma unroll
-  for (int m = 0; m < MTW; ++m) { m_run[m] = -INFINITY; l_run[m] = 0.f; }
-  if (0 < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, 0, stage);
-  int it = 0;
-  for (int64_t kt = 0; kt < k_hi; kt += KT, ++it) {
-    const int buf = it & 1;
-    bwd_commit<D, THREADS, UPT, KSTR, TSTR, false>(tid, stage, Ks[buf], Kt[buf], Vs[buf]);
-    __syncthreads();
-    if (kt + KT < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, kt + KT, stage);
+    for (int m = 0; m < MTW; ++m) { m_run[m] = -INFINITY; l_run[m] = 0.f; }
+    auto lse_math = [&](int buf, int64_t kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < MTW; ++m) {
-      float s[2][4];
-      logits(Ks[buf], m, kt, s);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[n][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[m], mx);
-      if (m_new != -INFINITY) {
-        float ps = 0.f;
+      for (int m = 0; m < MTW; ++m) {
+        float s[2][4];
+        logits(Ks[buf], m, kt, s);
+        float mx = -INFINITY;
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ps += exp2f(s[n][i] - m_new);
-        l_run[m] = l_run[m] * exp2f(m_run[m] - m_new) + ps;
-        m_run[m] = m_new;
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[n][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[m], mx);
+        if (m_new != -INFINITY) {
+          float ps = 0.f;
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ps += exp2f(s[n][i] - m_new);
+          l_run[m] = l_run[m] * exp2f(m_run[m] - m_new) + ps;
+          m_run[m] = m_new;
+        }
       }
+    };
+    if (0 < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, 0, stA);
+    if (KT < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, KT, stB);
+    for (int64_t kt = 0; kt < k_hi;) {
+      bwd_commit<D, THREADS, UPT, KSTR, false>(tid, stA, Ks[0], Vs[0]);
+      __syncthreads();
+      if (kt + 2 * KT < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, kt + 2 * KT, stA);
+      lse_math(0, kt);
+      kt += KT;
+      if (kt >= k_hi) break;
+      bwd_commit<D, THREADS, UPT, KSTR, false>(tid, stB, Ks[1], Vs[1]);
+      __syncthreads();
+      if (kt + 2 * KT < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, kt + 2 * KT, stB);
+      lse_math(1, kt);
+      kt += KT;
+    }
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      float l = l_run[m] + __shfl_xor(l_run[m], 16);
+      l += __shfl_xor(l, 32);
+      lse[m] = (l > 0.f) ? m_run[m] + log2f(l) : INFINITY;  // a row with no visible key: P = 0
+    }
+    __syncthreads();  // the stage buffers are reused
+  } else {
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      const float v = row_ok[m] ? bk.lse_in[(int64_t)(q0 + t_of[m]) * a.hq + hq_of[m]] : -INFINITY;
+      lse[m] = v > -INFINITY ? v * LOG2E : INFINITY;
     }
   }
-  float lse[MTW];
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {
-    float l = l_run[m] + __shfl_xor(l_run[m], 16);
-    l += __shfl_xor(l, 32);
-    lse[m] = (l > 0.f) ? m_run[m] + log2f(l) : INFINITY;  // a row with no visible key: P = 0
     if (row_ok[m] && g4 == 0) {
       const int64_t orow = (int64_t)(q0 + t_of[m]) * a.hq + hq_of[m];
       bk.lse[orow] = lse[m];
       bk.drow[orow] = drow[m];
     }
   }
-  __syncthreads();  // the stage buffers are reused
 
   // ---- pass 2: dQ~^T = K^T dS^T ----
   f32x4_t acc[MTW][MD];
@@ -293,13 +328,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
   for (int m = 0; m < MTW; ++m)
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[m][md] = {0.f, 0.f, 0.f, 0.f};
-  if (0 < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, 0, stage);
-  it = 0;
-  for (int64_t kt = 0; kt < k_hi; kt += KT, ++it) {
-    const int buf = it & 1;
-    bwd_commit<D, THREADS, UPT, KSTR, TSTR, true>(tid, stage, Ks[buf], Kt[buf], Vs[buf]);
-    __syncthreads();
-    if (kt + KT < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, kt + KT, stage);
+  auto dq_math = [&](int buf, int64_t kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       float s[2][4];
@@ -328,13 +357,29 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
       const bf16x8_t dSf = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
-        const bf16_t* kr = &Kt[buf][(md * 16 + cl) * TSTR];
-        const uint2 k0 = *reinterpret_cast<const uint2*>(kr + g4 * 4);
-        const uint2 k1 = *reinterpret_cast<const uint2*>(kr + 16 + g4 * 4);
+        // A operand K^T: element md*16 + cl over keys g4*4 .. +3 and 16 + g4*4 .. +3
+        const bf16_t* kr = &Ks[buf][(g4 * 4 + (cl >> 2)) * KSTR + md * 16 + (cl & 3) * 4];
+        const uint2 k0 = lds_read_tr16(kr);
+        const uint2 k1 = lds_read_tr16(kr + 16 * KSTR);
         const bf16x8_t Kf = __builtin_bit_cast(bf16x8_t, make_uint4(k0.x, k0.y, k1.x, k1.y));
         acc[m][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf, dSf, acc[m][md], 0, 0, 0);
       }
     }
+  };
+  if (0 < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, 0, stA);
+  if (KT < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, KT, stB);
+  for (int64_t kt = 0; kt < k_hi;) {
+    bwd_commit<D, THREADS, UPT, KSTR, true>(tid, stA, Ks[0], Vs[0]);
+    __syncthreads();
+    if (kt + 2 * KT < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stA);
+    dq_math(0, kt);
+    kt += KT;
+    if (kt >= k_hi) break;
+    bwd_commit<D, THREADS, UPT, KSTR, true>(tid, stB, Ks[1], Vs[1]);
+    __syncthreads();
+    if (kt + 2 * KT < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stB);
+    dq_math(1, kt);
+    kt += KT;
   }
 
   // lane holds dQ~^T[d = md*16 + g4*4 + i][row cl]; natural-scale gradient = scale * acc
@@ -350,18 +395,23 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
 }
 
 // ---- dK and dV --------------------------------------------------------------------------
-constexpr int DKV_NW = 4;  // waves per workgroup, one 16-key tile each per round
+constexpr int DKV_NW = 4;   // waves per workgroup
+constexpr int DKV_NT = 1;   // 16-key tiles per wave
+constexpr int DKV_RS = 32;  // query rows per LDS stage (two 16-row tiles)
 
 template <int D>
 __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
   const AttnK& a = bk.f;
   constexpr int KK = D / 32;
   constexpr int MD = D / 16;
-  constexpr int QSTR = D + 8;   // bf16 per staged row (row-major)
-  constexpr int RSTR = 16 + 8;  // bf16 per staged column (transposed)
-  __shared__ __align__(16) bf16_t Qs[16 * QSTR], dOs[16 * QSTR];
-  __shared__ __align__(16) bf16_t Qt[D * RSTR], dOt[D * RSTR];
-  __shared__ float lse_s[16], drow_s[16];
+  constexpr int STR = D + 16;  // bf16 per staged row: 32 bytes of padding keep the reads conflict-free
+  constexpr int UPR = D / 8;   // 16-byte units per row
+  constexpr int THREADS = 64 * DKV_NW;
+  constexpr int UNITS = DKV_RS * UPR;  // 16-byte units per array per stage
+  constexpr int UPT = (UNITS + THREADS - 1) / THREADS;
+  constexpr int KEYS = DKV_NW * DKV_NT * 16;  // keys per workgroup round
+  __shared__ __align__(16) bf16_t Qs[2][DKV_RS * STR], dOs[2][DKV_RS * STR];
+  __shared__ __align__(16) float lse_s[2][DKV_RS], drow_s[2][DKV_RS];
   __shared__ int64_t mstart[1025], mpre[1025];
   __shared__ int sh_keff;
   __shared__ int64_t sh_M;
@@ -373,7 +423,7 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int kv0 = a.kv_off[b], Lkv = a.kv_off[b + 1] - kv0;
   const int nrows = Lq * G;
-  const int nrt = (nrows + 15) / 16;
+  const int nst = (nrows + DKV_RS - 1) / DKV_RS;
 
   if (w == 0) {
     MemMap mm = build_memmap(a.ids + (int64_t)b * a.k, a.k, a.chunk_off, mstart, mpre);
@@ -383,132 +433,187 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
   const int keff = sh_keff;
   const int64_t M = sh_M;
   const int64_t NK = M + Lkv;
-  const int64_t ntile = (NK + 15) / 16;
-  const int64_t tile0 = ntile * blockIdx.x / bk.kblocks, tile1 = ntile * (blockIdx.x + 1) / bk.kblocks;
+  const int64_t nchunk = (NK + KEYS - 1) / KEYS;
+  const int64_t c0 = nchunk * blockIdx.x / bk.kblocks, c1 = nchunk * (blockIdx.x + 1) / bk.kblocks;
   const float sl2 = a.scale_log2;
   const bf16_t* Kb = (const bf16_t*)a.Kbar;
   const bf16_t* Vb = (const bf16_t*)a.Vbar;
   const bf16_t* Kr = (const bf16_t*)a.Krot;
   const bf16_t* Vl = (const bf16_t*)a.Vloc;
+  const bf16_t* Qg = (const bf16_t*)a.Qrot;
+  const bf16_t* dOg = (const bf16_t*)bk.dO;
 
-  for (int64_t r0 = tile0; r0 < tile1; r0 += DKV_NW) {
-    const int64_t tile = r0 + w;  // this wave's key tile in this round
-    const bool active = tile < tile1;
-    // B operands of S = Q~ K^T and dP = dO V^T: lane (cl, g4) holds key tile*16 + cl,
-    // elements kk*32 + g4*8 .. + 8
-    bf16x8_t Kf[KK], Vf[KK];
-    const int64_t mykey = tile * 16 + cl;
-    bool mybank = false;
-    int64_t myrow = 0;
-    {
+  // Stage `st` (query rows st*32 .. +31, row = t*G + j for token t and query head g*G + j)
+  // is read into registers one stage ahead and written to LDS buffer st & 1.
+  uint4 pq[UPT], pd[UPT];
+  float pl = INFINITY, pr = 0.f;
+  auto fetch = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      const int u = tid + j * THREADS;
+      const int rr = u / UPR, e0 = (u % UPR) * 8;
+      const int row = st * DKV_RS + rr;
+      pq[j] = pd[j] = make_uint4(0, 0, 0, 0);
+      if ((UNITS % THREADS == 0 || u < UNITS) && row < nrows) {
+        const int64_t ro = ((int64_t)(q0 + row / G) * a.hq + g * G + row % G) * D + e0;
+        pq[j] = *reinterpret_cast<const uint4*>(Qg + ro);
+        pd[j] = *reinterpret_cast<const uint4*>(dOg + ro);
+      }
+    }
+    if (tid < DKV_RS) {
+      const int row = st * DKV_RS + tid;
+      pl = INFINITY;  // rows past the end: P = 0
+      pr = 0.f;
+      if (row < nrows) {
+        const int64_t orow = (int64_t)(q0 + row / G) * a.hq + g * G + row % G;
+        pl = bk.lse[orow];
+        pr = bk.drow[orow];
+      }
+    }
+  };
+  auto commit = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      const int u = tid + j * THREADS;
+      const int rr = u / UPR, e0 = (u % UPR) * 8;
+      if (UNITS % THREADS != 0 && u >= UNITS) break;
+      *reinterpret_cast<uint4*>(&Qs[buf][rr * STR + e0]) = pq[j];
+      *reinterpret_cast<uint4*>(&dOs[buf][rr * STR + e0]) = pd[j];
+    }
+    if (tid < DKV_RS) {
+      lse_s[buf][tid] = pl;
+      drow_s[buf][tid] = pr;
+    }
+  };
+
+  for (int64_t c = c0; c < c1; ++c) {
+    // this wave's keys: c*KEYS + (w*NT + nt)*16 + 0..15.  B operands of S = Q~ K^T and
+    // dP = dO V^T: lane (cl, g4) holds key base + cl, elements kk*32 + g4*8 .. +8.
+    bf16x8_t Kf[DKV_NT][KK], Vf[DKV_NT][KK];
+    int rowmin[DKV_NT];  // key base + cl is visible to rows >= rowmin (causal on local keys)
+#pragma unroll
+    for (int nt = 0; nt < DKV_NT; ++nt) {
+      const int64_t key = c * KEYS + (w * DKV_NT + nt) * 16 + cl;
       uint4 kz[KK], vz[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) kz[kk] = vz[kk] = make_uint4(0, 0, 0, 0);
-      if (active && mykey < NK) {
-        const int64_t off = key_row(mstart, mpre, keff, M, mykey, kv0, a.h_kv, g, D, mybank, myrow);
-        const bf16_t* kp = (mybank ? Kb : Kr) + off + g4 * 8;
-        const bf16_t* vp = (mybank ? Vb : Vl) + off + g4 * 8;
+      rowmin[nt] = 0;
+      if (key < NK) {
+        bool bank;
+        int64_t row;
+        const int64_t off = key_row(mstart, mpre, keff, M, key, kv0, a.h_kv, g, D, bank, row);
+        const bf16_t* kp = (bank ? Kb : Kr) + off + g4 * 8;
+        const bf16_t* vp = (bank ? Vb : Vl) + off + g4 * 8;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           kz[kk] = *reinterpret_cast<const uint4*>(kp + kk * 32);
           vz[kk] = *reinterpret_cast<const uint4*>(vp + kk * 32);
         }
+        // local key i = key - M is visible to token t when i <= Lkv - Lq + t
+        if (!bank) {
+          const int64_t tmin = (key - M) - (Lkv - Lq);
+          rowmin[nt] = tmin > 0 ? (int)tmin * G : 0;
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        Kf[kk] = __builtin_bit_cast(bf16x8_t, kz[kk]);
-        Vf[kk] = __builtin_bit_cast(bf16x8_t, vz[kk]);
+        Kf[nt][kk] = __builtin_bit_cast(bf16x8_t, kz[kk]);
+        Vf[nt][kk] = __builtin_bit_cast(bf16x8_t, vz[kk]);
       }
     }
-    f32x4_t dK[MD], dV[MD];
+    f32x4_t dK[DKV_NT][MD], dV[DKV_NT][MD];
 #pragma unroll
-    for (int md = 0; md < MD; ++md) dK[md] = dV[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // the local index past which this tile's keys are invisible to row t: key - M <= Lkv - Lq + t
-    for (int rt = 0; rt < nrt; ++rt) {
-      __syncthreads();  // the previous row tile's readers are done
-      // stage rows rt*16 .. +15 (row = t * G + j: token t, query head g*G + j)
-      for (int u = tid; u < 16 * (D / 8); u += 64 * DKV_NW) {
-        const int rr = u / (D / 8), e0 = (u % (D / 8)) * 8;
-        const int row = rt * 16 + rr;
-        uint4 qv = make_uint4(0, 0, 0, 0), dv = qv;
-        if (row < nrows) {
-          const int64_t ro = ((int64_t)(q0 + row / G) * a.hq + g * G + row % G) * D + e0;
-          qv = *reinterpret_cast<const uint4*>((const bf16_t*)a.Qrot + ro);
-          dv = *reinterpret_cast<const uint4*>((const bf16_t*)bk.dO + ro);
+    for (int nt = 0; nt < DKV_NT; ++nt)
+#pragma unroll
+      for (int md = 0; md < MD; ++md) dK[nt][md] = dV[nt][md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (nst > 0) fetch(0);
+    for (int st = 0; st < nst; ++st) {
+      const int buf = st & 1;
+      commit(buf);
+      __syncthreads();  // stage st is visible, and every wave is done with stage st-2 (this buffer)
+      if (st + 1 < nst) fetch(st + 1);
+      const bf16_t* qs = Qs[buf];
+      const bf16_t* ds_ = dOs[buf];
+      // P and dS of this wave's keys over the stage's 32 rows, packed as the A operands
+      // (key cl, k-slot g4*8 + j) of the 16x16x32 products; k-slot g4*8 + j is row
+      // g4*4 + j for j < 4 and 16 + g4*4 + (j - 4) for j >= 4.
+      uint32_t pw[DKV_NT][4], sw[DKV_NT][4];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        f32x4_t sacc[DKV_NT], dpacc[DKV_NT];
+#pragma unroll
+        for (int nt = 0; nt < DKV_NT; ++nt) sacc[nt] = dpacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const uint4 qa = *reinterpret_cast<const uint4*>(&qs[(sub * 16 + cl) * STR + kk * 32 + g4 * 8]);
+          const uint4 da = *reinterpret_cast<const uint4*>(&ds_[(sub * 16 + cl) * STR + kk * 32 + g4 * 8]);
+#pragma unroll
+          for (int nt = 0; nt < DKV_NT; ++nt) {
+            sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa), Kf[nt][kk], sacc[nt], 0, 0, 0);
+            dpacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, da), Vf[nt][kk], dpacc[nt], 0, 0, 0);
+          }
         }
-        *reinterpret_cast<uint4*>(&Qs[rr * QSTR + e0]) = qv;
-        *reinterpret_cast<uint4*>(&dOs[rr * QSTR + e0]) = dv;
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w}, dw[4] = {dv.x, dv.y, dv.z, dv.w};
+        // lane holds rows sub*16 + g4*4 + i of key cl
+        const float4 L4 = *reinterpret_cast<const float4*>(&lse_s[buf][sub * 16 + g4 * 4]);
+        const float4 R4 = *reinterpret_cast<const float4*>(&drow_s[buf][sub * 16 + g4 * 4]);
+        const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Rr[4] = {R4.x, R4.y, R4.z, R4.w};
+        const int row0 = st * DKV_RS + sub * 16 + g4 * 4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          Qt[(e0 + 2 * q) * RSTR + rr] = (bf16_t)(qw[q] & 0xffffu);
-          Qt[(e0 + 2 * q + 1) * RSTR + rr] = (bf16_t)(qw[q] >> 16);
-          dOt[(e0 + 2 * q) * RSTR + rr] = (bf16_t)(dw[q] & 0xffffu);
-          dOt[(e0 + 2 * q + 1) * RSTR + rr] = (bf16_t)(dw[q] >> 16);
+        for (int nt = 0; nt < DKV_NT; ++nt) {
+          float p[4], dsv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[i] = row0 + i >= rowmin[nt] ? exp2f(fmaf(sacc[nt][i], sl2, -Lr[i])) : 0.f;
+            dsv[i] = p[i] * (dpacc[nt][i] - Rr[i]);
+          }
+          pw[nt][sub * 2] = pack_bf16x2(p[0], p[1]);
+          pw[nt][sub * 2 + 1] = pack_bf16x2(p[2], p[3]);
+          sw[nt][sub * 2] = pack_bf16x2(dsv[0], dsv[1]);
+          sw[nt][sub * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
         }
       }
-      if (tid < 16) {
-        const int row = rt * 16 + tid;
-        float l = INFINITY, d = 0.f;
-        if (row < nrows) {
-          const int64_t orow = (int64_t)(q0 + row / G) * a.hq + g * G + row % G;
-          l = bk.lse[orow];
-          d = bk.drow[orow];
-        }
-        lse_s[tid] = l;
-        drow_s[tid] = d;
-      }
-      __syncthreads();
-      if (!active) continue;
-      // S = Q~ K^T and dP = dO V^T: lane holds rows g4*4 + i of key cl
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      // dV += P^T dO and dK += dS^T Q~: B operand (element md*16 + cl, k-slots g4*8 .. +8)
+      // read transposed from the row-major stage, rows g4*4 .. +3 and 16 + g4*4 .. +3
+      const int trow = g4 * 4 + (cl >> 2), tcol = (cl & 3) * 4;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint4 qw = *reinterpret_cast<const uint4*>(&Qs[cl * QSTR + kk * 32 + g4 * 8]);
-        const uint4 dw = *reinterpret_cast<const uint4*>(&dOs[cl * QSTR + kk * 32 + g4 * 8]);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qw), Kf[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, dw), Vf[kk], dp, 0, 0, 0);
+      for (int md = 0; md < MD; ++md) {
+        const uint2 d0 = lds_read_tr16(&ds_[trow * STR + md * 16 + tcol]);
+        const uint2 d1 = lds_read_tr16(&ds_[(16 + trow) * STR + md * 16 + tcol]);
+        const uint2 q0v = lds_read_tr16(&qs[trow * STR + md * 16 + tcol]);
+        const uint2 q1v = lds_read_tr16(&qs[(16 + trow) * STR + md * 16 + tcol]);
+        const bf16x8_t dOb = __builtin_bit_cast(bf16x8_t, make_uint4(d0.x, d0.y, d1.x, d1.y));
+        const bf16x8_t Qb = __builtin_bit_cast(bf16x8_t, make_uint4(q0v.x, q0v.y, q1v.x, q1v.y));
+#pragma unroll
+        for (int nt = 0; nt < DKV_NT; ++nt) {
+          const bf16x8_t Pa = __builtin_bit_cast(bf16x8_t, make_uint4(pw[nt][0], pw[nt][1], pw[nt][2], pw[nt][3]));
+          const bf16x8_t Sa = __builtin_bit_cast(bf16x8_t, make_uint4(sw[nt][0], sw[nt][1], sw[nt][2], sw[nt][3]));
+          dV[nt][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pa, dOb, dV[nt][md], 0, 0, 0);
+          dK[nt][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Sa, Qb, dK[nt][md], 0, 0, 0);
+        }
       }
-      float p[4], ds[4];
+    }
+    __syncthreads();  // the stage buffers are free for the next round
+    // lane holds dK / dV of key base + g4*4 + i at element md*16 + cl
+#pragma unroll
+    for (int nt = 0; nt < DKV_NT; ++nt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rr = g4 * 4 + i;
-        const int row = rt * 16 + rr;
-        const int t = row / G;
-        const bool vis = row < nrows && mykey < NK && (mykey < M || mykey - M <= (int64_t)(Lkv - Lq + t));
-        p[i] = vis ? exp2f(s[i] * sl2 - lse_s[rr]) : 0.f;
-        ds[i] = p[i] * (dp[i] - drow_s[rr]);
-      }
-      // A operands: P^T and dS^T of this lane's key cl over rows g4*4 .. +3
-      const bf16x4_t Pa = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
-      const bf16x4_t Sa = __builtin_bit_cast(bf16x4_t, make_uint2(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])));
+        const int64_t key = c * KEYS + (w * DKV_NT + nt) * 16 + g4 * 4 + i;
+        if (key >= NK) continue;
+        bool bank;
+        int64_t row;
+        const int64_t off = key_row(mstart, mpre, keff, M, key, kv0, a.h_kv, g, D, bank, row) + cl;
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        // B operands: dO and Q~ at element md*16 + cl over rows g4*4 .. +3
-        const bf16x4_t dOb = __builtin_bit_cast(bf16x4_t, *reinterpret_cast<const uint2*>(&dOt[(md * 16 + cl) * RSTR + g4 * 4]));
-        const bf16x4_t Qb = __builtin_bit_cast(bf16x4_t, *reinterpret_cast<const uint2*>(&Qt[(md * 16 + cl) * RSTR + g4 * 4]));
-        dV[md] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Pa, dOb, dV[md], 0, 0, 0);
-        dK[md] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Sa, Qb, dK[md], 0, 0, 0);
-      }
-    }
-    if (!active) continue;
-    // lane holds dK / dV of key tile*16 + g4*4 + i at element md*16 + cl
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t key = tile * 16 + g4 * 4 + i;
-      if (key >= NK) continue;
-      bool bank;
-      int64_t row;
-      const int64_t off = key_row(mstart, mpre, keff, M, key, kv0, a.h_kv, g, D, bank, row) + cl;
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const float gk = dK[md][i] * bk.scale, gv = dV[md][i];
-        if (bank) {
-          atomicAdd(bk.dKb + off + md * 16, gk);
-          atomicAdd(bk.dVb + off + md * 16, gv);
-        } else {
-          bk.dKl[off + md * 16] = gk;
-          bk.dVl[off + md * 16] = gv;
+        for (int md = 0; md < MD; ++md) {
+          const float gk = dK[nt][md][i] * bk.scale, gv = dV[nt][md][i];
+          if (bank) {
+            atomicAdd(bk.dKb + off + md * 16, gk);
+            atomicAdd(bk.dVb + off + md * 16, gv);
+          } else {
+            bk.dKl[off + md * 16] = gk;
+            bk.dVl[off + md * 16] = gv;
+          }
         }
       }
     }
@@ -588,7 +693,7 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
   k.f.h_kv = f.h_kv;
   k.f.rope_base = f.rope_base;
   const float scale = f.scale > 0.f ? f.scale : 1.0f / sqrtf((float)D);
-  k.f.scale_log2 = scale * 1.4426950408889634f;
+  k.f.scale_log2 = scale * LOG2E;
   k.f.k = f.k;
   k.f.ids = f.ids;
   k.f.chunk_off = f.chunk_off;
@@ -603,6 +708,7 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
   ws += align256((size_t)f.total_q * f.hq * 4);
   k.drow = (float*)ws;
   k.O = r.O;
+  k.lse_in = r.lse;
   k.dO = r.dO;
   k.dQ = r.dQ;
   k.dKl = r.dKloc;

@@ -30,6 +30,7 @@ struct AttnK {
   float* part_o;
   float* part_ml;
   int splits;
+  float* lse;  // optional per-row log-sum-exp output (natural log)
 };
 
 __device__ __forceinline__ int find_query(const int32_t* off, int n, int64_t row) {

@@ -6,6 +6,9 @@
 
 namespace msa {
 
+constexpr float LN2 = 0.69314718055994531f;    // ln 2: log2-domain values to natural log
+constexpr float LOG2E = 1.44269504088896341f;  // log2 e: natural log to log2 domain
+
 // ---- element types -------------------------------------------------------------------
 // bf16 is carried as its 16-bit pattern: the upper half of an IEEE float32.
 typedef uint16_t bf16_t;

@@ -87,6 +87,7 @@ struct AttnArgs {
   const int64_t* chunk_off;
   const void *Kbar, *Vbar;
   void* O;
+  float* lse;        // optional [total_q * hq]: natural-log log-sum-exp of each row's logits
   void* workspace;
 };
 int attn_rows_per_block(int max_q_len, int G);
@@ -98,6 +99,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
 struct AttnBwdArgs {
   AttnArgs f;        // the forward call's arguments (f.O unused)
   const void* O;     // forward output
+  const float* lse;  // optional: the forward's log-sum-exp per row (else recomputed)
   const void* dO;    // gradient of the loss with respect to O
   float *dQ, *dKloc, *dVloc;  // overwritten
   float *dKbar, *dVbar;       // accumulated

@@ -345,7 +345,7 @@ def assemble_memory(ids_b, chunk_off, Kbar, Vbar):
 
 
 def sparse_attention_one(Q_b, Kloc_b, Vloc_b, Kmem, Vmem, k_eff: int, base: float,
-                         scale: float | None = None) -> np.ndarray:
+                         scale: float | None = None, with_lse: bool = False):
     """Attention of one query's tokens over [memory ; causal local context].
 
     Q_b: [Lq, Hq, D]; Kloc_b, Vloc_b: [Lkv, H_kv, D] (Lkv >= Lq; the query's tokens are
@@ -353,6 +353,8 @@ def sparse_attention_one(Q_b, Kloc_b, Vloc_b, Kmem, Vmem, k_eff: int, base: floa
     Local token j is rotated at global position k_eff + j (R12), memory keys are used as
     pooled (R11); query token t is local token Lkv - Lq + t and sees every memory key and
     local keys j <= Lkv - Lq + t (R13).  kv head of hq = hq // (Hq/H_kv) (R14).
+    with_lse also returns [Lq, Hq]: the natural log of each row's softmax normaliser,
+    log sum_j exp(logit_j) over the keys the row sees (what a backward pass reuses).
     """
     Q_b = np.asarray(Q_b, dtype=np.float64)
     Kl = np.asarray(Kloc_b, dtype=np.float64)
@@ -370,17 +372,21 @@ def sparse_attention_one(Q_b, Kloc_b, Vloc_b, Kmem, Vmem, k_eff: int, base: floa
     qpos = (Lkv - Lq) + np.arange(Lq)
     mask = np.arange(Lkv)[None, :] <= qpos[:, None]           # [Lq, Lkv]
     out = np.zeros((Lq, Hq, D), dtype=np.float64)
+    lse = np.zeros((Lq, Hq), dtype=np.float64)
     for hq in range(Hq):
         g = hq // G
         keys = np.concatenate([Kmem[:, g, :], Klr[:, g, :]], axis=0)   # [M+Lkv, D]
         vals = np.concatenate([Vmem[:, g, :], Vl[:, g, :]], axis=0)
         logits = scale * (Qr_[:, hq, :] @ keys.T)                       # [Lq, M+Lkv]
         logits[:, M:][~mask] = -np.inf
-        logits -= logits.max(axis=1, keepdims=True)
+        mx = logits.max(axis=1, keepdims=True)
+        logits -= mx
         p = np.exp(logits)
-        p /= p.sum(axis=1, keepdims=True)
+        z = p.sum(axis=1, keepdims=True)
+        lse[:, hq] = (mx + np.log(z))[:, 0]
+        p /= z
         out[:, hq, :] = p @ vals
-    return out
+    return (out, lse) if with_lse else out
 
 
 def sparse_attn(Q, Kloc, Vloc, q_off, kv_off, ids, chunk_off, Kbar, Vbar, base: float,
@@ -400,6 +406,23 @@ def sparse_attn(Q, Kloc, Vloc, q_off, kv_off, ids, chunk_off, Kbar, Vbar, base: 
         out[q_off[b]:q_off[b + 1]] = sparse_attention_one(
             Q[q_off[b]:q_off[b + 1]], Kloc[kv_off[b]:kv_off[b + 1]],
             Vloc[kv_off[b]:kv_off[b + 1]], Km, Vm, keff, base, scale)
+    return out
+
+
+def sparse_attn_lse(Q, Kloc, Vloc, q_off, kv_off, ids, chunk_off, Kbar, Vbar, base: float,
+                    scale: float | None = None) -> np.ndarray:
+    """Each row's log-sum-exp of its logits over the keys it sees, [total_q, Hq] float64
+    (natural log), as returned alongside O by sparse_attention_one."""
+    q_off = np.asarray(q_off, dtype=np.int64)
+    kv_off = np.asarray(kv_off, dtype=np.int64)
+    ids = np.asarray(ids)
+    out = np.zeros(np.asarray(Q).shape[:2], dtype=np.float64)
+    for b in range(len(q_off) - 1):
+        Km, Vm = assemble_memory(ids[b], chunk_off, Kbar, Vbar)
+        keff = int(np.sum(ids[b] >= 0))
+        out[q_off[b]:q_off[b + 1]] = sparse_attention_one(
+            Q[q_off[b]:q_off[b + 1]], Kloc[kv_off[b]:kv_off[b + 1]],
+            Vloc[kv_off[b]:kv_off[b + 1]], Km, Vm, keff, base, scale, with_lse=True)[1]
     return out
 
 

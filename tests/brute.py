@@ -86,14 +86,16 @@ def topk_brute(scores, k):
     return by_rank[:keff] + [-1] * (k - keff)
 
 
-def attention_brute(Q, Kloc, Vloc, Kmem, Vmem, k_eff, base, scale=None):
+def attention_brute(Q, Kloc, Vloc, Kmem, Vmem, k_eff, base, scale=None, with_lse=False):
     """Explicit loops: rotate local query/keys at k_eff + local index, softmax over
-    every memory key and the causal local keys, weighted sum of values."""
+    every memory key and the causal local keys, weighted sum of values.  with_lse also
+    returns each row's log of the softmax normaliser, log sum_j exp(logit_j)."""
     Lq, Hq, D = len(Q), len(Q[0]), len(Q[0][0])
     Lkv, Hkv = len(Kloc), len(Kloc[0])
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     out = [[[0.0] * D for _ in range(Hq)] for _ in range(Lq)]
+    lse = [[0.0] * Hq for _ in range(Lq)]
     for t in range(Lq):
         i = Lkv - Lq + t
         for hq in range(Hq):
@@ -110,6 +112,7 @@ def attention_brute(Q, Kloc, Vloc, Kmem, Vmem, k_eff, base, scale=None):
             mx = max(logits)
             w = [math.exp(x - mx) for x in logits]
             z = sum(w)
+            lse[t][hq] = mx + math.log(z)
             for e in range(D):
                 out[t][hq][e] = sum(w[n] * vals[n][e] for n in range(len(w))) / z
-    return out
+    return (out, lse) if with_lse else out

@@ -107,12 +107,12 @@ def test_route_validation(kw, code):
 def _attn(**kw):
     a = dict(dtype=1, B=1, tq=64, tkv=64, q_off=FAKE, kv_off=FAKE, maxq=64, Q=FAKE, Kl=FAKE, Vl=FAKE,
              hq=32, h_kv=8, d=128, base=1e6, scale=0.0, k=16, ids=FAKE, N=10, C=20, coff=FAKE,
-             Kb=FAKE, Vb=FAKE, src=0, O=FAKE, ws=FAKE, wsb=1 << 30)
+             Kb=FAKE, Vb=FAKE, src=0, O=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return lib.msa_sparse_attn(a["dtype"], a["B"], a["tq"], a["tkv"], a["q_off"], a["kv_off"], a["maxq"],
                                a["Q"], a["Kl"], a["Vl"], a["hq"], a["h_kv"], a["d"], a["base"], a["scale"],
                                a["k"], a["ids"], a["N"], a["C"], a["coff"], a["Kb"], a["Vb"], a["src"],
-                               a["O"], a["ws"], a["wsb"], None)
+                               a["O"], a["lse"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -130,13 +130,13 @@ def test_attn_validation(kw, code):
 def _attn_bwd(**kw):
     a = dict(dtype=1, B=1, tq=64, tkv=64, q_off=FAKE, kv_off=FAKE, maxq=64, Q=FAKE, Kl=FAKE, Vl=FAKE,
              hq=32, h_kv=8, d=128, base=1e6, scale=0.0, k=16, ids=FAKE, N=10, C=20, coff=FAKE,
-             Kb=FAKE, Vb=FAKE, src=0, O=FAKE, dO=FAKE, dQ=FAKE, dKl=FAKE, dVl=FAKE, dKb=FAKE, dVb=FAKE,
-             ws=FAKE, wsb=1 << 30)
+             Kb=FAKE, Vb=FAKE, src=0, O=FAKE, lse=None, dO=FAKE, dQ=FAKE, dKl=FAKE, dVl=FAKE, dKb=FAKE,
+             dVb=FAKE, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return lib.msa_sparse_attn_backward(
         a["dtype"], a["B"], a["tq"], a["tkv"], a["q_off"], a["kv_off"], a["maxq"], a["Q"], a["Kl"], a["Vl"],
         a["hq"], a["h_kv"], a["d"], a["base"], a["scale"], a["k"], a["ids"], a["N"], a["C"], a["coff"],
-        a["Kb"], a["Vb"], a["src"], a["O"], a["dO"], a["dQ"], a["dKl"], a["dVl"], a["dKb"], a["dVb"],
+        a["Kb"], a["Vb"], a["src"], a["O"], a["lse"], a["dO"], a["dQ"], a["dKl"], a["dVl"], a["dKb"], a["dVb"],
         a["ws"], a["wsb"], None)
 
 

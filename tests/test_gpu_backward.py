@@ -23,14 +23,23 @@ DEV = "cuda"
 GRAD_RTOL = 2.0 ** -6
 GRAD_ATOL = 1e-4
 
+# The forward's per-row log-sum-exp: the GPU's logits use the rotated Q and local K rounded
+# to bf16 (unit roundoff u = 2^-8 each), so every logit is off by at most
+# scale * 2u * |q| * |k| (Cauchy-Schwarz), and so is the log-sum-exp; float32 sums and
+# exp2/log2 add about 1e-4 at most at these sizes.
+LSE_U = 2.0 ** -8
+LSE_ATOL = 1e-4
+
 
 def _randn(shape, seed, std=1.0):
     g = torch.Generator().manual_seed(seed)
     return (torch.randn(shape, generator=g) * std).to(torch.bfloat16)
 
 
-def _case(q_lens, extra_kv, hq, h_kv, d, counts, ids, seed, host=False):
-    """Runs the GPU forward then backward, and the oracle backward, on one batch."""
+def _case(q_lens, extra_kv, hq, h_kv, d, counts, ids, seed, host=False, use_lse=False):
+    """Runs the GPU forward then backward, and the oracle backward, on one batch.  With
+    use_lse the forward also returns each row's log-sum-exp, which the backward reuses; it
+    is checked against the oracle's here."""
     B = len(q_lens)
     kv_lens = [q + e for q, e in zip(q_lens, extra_kv)]
     q_off = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
@@ -49,14 +58,35 @@ def _case(q_lens, extra_kv, hq, h_kv, d, counts, ids, seed, host=False):
     Kb_d = Kb.pin_memory() if host else Kb.to(DEV)
     Vb_d = Vb.pin_memory() if host else Vb.to(DEV)
     Qd, Kld, Vld = Q.to(DEV), Kl.to(DEV), Vl.to(DEV)
+    lse = torch.full((int(q_off[-1]), hq), float("nan"), device=DEV) if use_lse else None
     Out = M.msa_sparse_attn(Qd, Kld, Vld, args["q_off"], args["kv_off"], args["max_q_len"], ids_t,
-                            args["chunk_off"], Kb_d, Vb_d, rope_base=1e6)
+                            args["chunk_off"], Kb_d, Vb_d, rope_base=1e6, lse=lse)
     grads = M.msa_sparse_attn_backward(Qd, Kld, Vld, args["q_off"], args["kv_off"], args["max_q_len"], ids_t,
-                                       args["chunk_off"], Kb_d, Vb_d, Out, dO.to(DEV), rope_base=1e6)
+                                       args["chunk_off"], Kb_d, Vb_d, Out, dO.to(DEV), rope_base=1e6, lse=lse)
     torch.cuda.synchronize()
+    if use_lse:
+        _check_lse(lse, Q, Kl, Kb, q_off, kv_off, np.asarray(ids), coff, d)
     ref = O.sparse_attn_backward(f64(Q), f64(Kl), f64(Vl), q_off, kv_off, np.asarray(ids), coff, f64(Kb),
                                  f64(Vb), 1e6, f64(dO))
     return grads, ref, coff
+
+
+def _check_lse(lse, Q, Kl, Kb, q_off, kv_off, ids, coff, d):
+    ref = O.sparse_attn_lse(f64(Q), f64(Kl), f64(Kl), q_off, kv_off, ids, coff, f64(Kb), f64(Kb), 1e6)
+    got = lse.cpu().double().numpy()
+    assert np.all(np.isfinite(got)), "lse: non-finite or unwritten rows"
+    # per-row bound: the row's |q| times the largest |k| of its query's keys
+    qn = np.linalg.norm(f64(Q), axis=-1)
+    G = Q.shape[1] // Kl.shape[1]
+    for b in range(len(q_off) - 1):
+        rows = [r for dd in ids[b] if dd >= 0 for r in range(int(coff[dd]), int(coff[dd + 1]))]
+        kn = np.linalg.norm(f64(Kl)[kv_off[b]:kv_off[b + 1]], axis=-1).max(axis=0)
+        if rows:
+            kn = np.maximum(kn, np.linalg.norm(f64(Kb)[rows], axis=-1).max(axis=0))
+        tol = 2 * LSE_U / np.sqrt(d) * qn[q_off[b]:q_off[b + 1]] * np.repeat(kn, G)[None, :] + LSE_ATOL
+        err = np.abs(got[q_off[b]:q_off[b + 1]] - ref[q_off[b]:q_off[b + 1]])
+        say(f"  lse query {b}: max err {err.max():.3g}, smallest bound {tol.min():.3g}")
+        assert np.all(err <= tol), f"lse query {b}: max err {err.max():.3g}"
 
 
 def _check(grads, ref, what):
@@ -78,14 +108,19 @@ CASES = [
     ("gqa2_d64_ragged", [5, 33, 17], [0, 2, 40], 8, 4, 64, [4, 1, 9, 30, 2, 6, 3],
      [[2, 4, -1], [4, 0, 3], [6, 5, 4]]),
     ("few_docs_k_gt_n", [20], [3], 16, 4, 128, [2, 5], [[1, 0, -1, -1]]),
+    # 8 queries x 8 kv heads fill the GPU without splitting the keys: the forward writes O
+    # and the log-sum-exp straight from the attention kernel instead of the split merge
+    ("batch8_unsplit", [12, 3, 20, 7, 1, 16, 9, 5], [0, 4, 0, 2, 30, 0, 1, 0], 32, 8, 128,
+     [3, 8, 1, 5, 12, 2, 6], [[0, 4], [2, 1], [6, 5], [3, -1], [4, 0], [1, 2], [5, 6], [0, 3]]),
 ]
 
 
+@pytest.mark.parametrize("use_lse", [False, True], ids=["recompute_lse", "forward_lse"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_attention_backward(case):
+def test_attention_backward(case, use_lse):
     name, q_lens, extra, hq, h_kv, d, counts, ids = case
-    say(f"case attention backward {name}")
-    grads, ref, coff = _case(q_lens, extra, hq, h_kv, d, counts, ids, seed=len(name))
+    say(f"case attention backward {name} lse {'from the forward' if use_lse else 'recomputed'}")
+    grads, ref, coff = _case(q_lens, extra, hq, h_kv, d, counts, ids, seed=len(name), use_lse=use_lse)
     _check(grads, ref, name)
     # bank rows no query selected keep their (zero) initial value
     used = set(int(x) for row in ids for x in row if x >= 0)
@@ -97,5 +132,31 @@ def test_attention_backward(case):
 
 def test_attention_backward_host_bank():
     say("case attention backward, bank content in pinned host memory")
-    grads, ref, coff = _case([16, 9], [4, 0], 16, 4, 128, [6, 3, 11, 2], [[2, 0], [2, 3]], seed=77, host=True)
+    grads, ref, coff = _case([16, 9], [4, 0], 16, 4, 128, [6, 3, 11, 2], [[2, 0], [2, 3]], seed=77, host=True,
+                             use_lse=True)
     _check(grads, ref, "host bank")
+
+
+def test_forward_lse_fp32():
+    say("case forward log-sum-exp, float32 inputs")
+    rng = np.random.default_rng(90)
+    q_lens, kv_lens, hq, h_kv, d = [6, 2], [9, 2], 8, 2, 64
+    q_off = np.array([0, 6, 8], dtype=np.int32)
+    kv_off = np.array([0, 9, 11], dtype=np.int32)
+    coff = np.array([0, 3, 4, 9], dtype=np.int64)
+    Q = torch.tensor(rng.standard_normal((8, hq, d)), dtype=torch.float32)
+    Kl = torch.tensor(rng.standard_normal((11, h_kv, d)), dtype=torch.float32)
+    Vl = torch.tensor(rng.standard_normal((11, h_kv, d)), dtype=torch.float32)
+    Kb = torch.tensor(rng.standard_normal((9, h_kv, d)) * 0.6, dtype=torch.float32)
+    Vb = torch.tensor(rng.standard_normal((9, h_kv, d)), dtype=torch.float32)
+    ids = np.array([[2, 0], [1, -1]], dtype=np.int32)
+    lse = torch.full((8, hq), float("nan"), device=DEV)
+    M.msa_sparse_attn(Q.to(DEV), Kl.to(DEV), Vl.to(DEV), torch.tensor(q_off, device=DEV),
+                      torch.tensor(kv_off, device=DEV), max(q_lens), torch.tensor(ids, device=DEV),
+                      torch.tensor(coff, device=DEV), Kb.to(DEV), Vb.to(DEV), rope_base=1e6, lse=lse)
+    torch.cuda.synchronize()
+    ref = O.sparse_attn_lse(f64(Q), f64(Kl), f64(Vl), q_off, kv_off, ids, coff, f64(Kb), f64(Vb), 1e6)
+    # float32 rotation and dot products: errors of order 1e-6 relative to |q||k| / sqrt(d)
+    err = float(np.max(np.abs(lse.cpu().double().numpy() - ref)))
+    say(f"  fp32 lse max err {err:.3g}")
+    assert err < 1e-4

@@ -108,3 +108,53 @@ def test_sparse_attn_multi_query_offsets():
     Km, Vm = O.assemble_memory(ids[1], coff, Kb, Vb)
     ref = O.sparse_attention_one(Q[2:3], Kl[4:6], Vl[4:6], Km, Vm, 1, 1e6)
     np.testing.assert_allclose(out[2:3], ref, atol=0)
+
+
+def test_lse_matches_brute_force():
+    # each row's log-sum-exp of its logits against the explicit-loop attention
+    rng = np.random.default_rng(34)
+    Lq, Lkv, Hq, Hkv, D, M = 3, 6, 4, 2, 8, 5
+    Q = rng.standard_normal((Lq, Hq, D))
+    Kl, Vl = rng.standard_normal((Lkv, Hkv, D)), rng.standard_normal((Lkv, Hkv, D))
+    Km, Vm = rng.standard_normal((M, Hkv, D)), rng.standard_normal((M, Hkv, D))
+    out, lse = O.sparse_attention_one(Q, Kl, Vl, Km, Vm, 3, 1e4, with_lse=True)
+    ref_out, ref_lse = brute.attention_brute(Q, Kl, Vl, Km, Vm, 3, 1e4, with_lse=True)
+    np.testing.assert_allclose(lse, np.array(ref_lse), atol=1e-12)
+    np.testing.assert_allclose(out, np.array(ref_out), atol=1e-12)
+
+
+def test_lse_closed_forms():
+    rng = np.random.default_rng(35)
+    D = 16
+    empty = np.zeros((0, 1, D))
+    # one query token that sees only its own key: query and key are rotated by the same
+    # angles, so the single logit, and hence the log-sum-exp, is scale * q . k
+    Q = rng.standard_normal((1, 2, D))
+    Kl, Vl = rng.standard_normal((1, 1, D)), rng.standard_normal((1, 1, D))
+    _, lse = O.sparse_attention_one(Q, Kl, Vl, empty, empty, 7, 1e6, with_lse=True)
+    for h in range(2):
+        assert abs(lse[0, h] - float(Q[0, h] @ Kl[0, 0]) / np.sqrt(D)) < 1e-12
+    # all keys zero: every logit is 0, so the log-sum-exp is log(number of visible keys)
+    Lq, Lkv, M = 3, 5, 4
+    Q = rng.standard_normal((Lq, 1, D))
+    _, lse = O.sparse_attention_one(Q, np.zeros((Lkv, 1, D)), rng.standard_normal((Lkv, 1, D)),
+                                    np.zeros((M, 1, D)), rng.standard_normal((M, 1, D)), 2, 1e6, with_lse=True)
+    for t in range(Lq):
+        assert abs(lse[t, 0] - np.log(M + Lkv - Lq + t + 1)) < 1e-12
+
+
+def test_sparse_attn_lse_per_query():
+    # the batched form equals the per-query one, memory assembled from each query's ids
+    rng = np.random.default_rng(36)
+    q_len, kv_len, Hq, Hkv, D = [2, 3], [4, 3], 4, 2, 8
+    q_off, kv_off = np.array([0, 2, 5]), np.array([0, 4, 7])
+    coff = np.array([0, 2, 3, 6])
+    Q = rng.standard_normal((5, Hq, D))
+    Kl, Vl = rng.standard_normal((7, Hkv, D)), rng.standard_normal((7, Hkv, D))
+    Kb, Vb = rng.standard_normal((6, Hkv, D)), rng.standard_normal((6, Hkv, D))
+    ids = np.array([[2, -1], [0, 1]])
+    got = O.sparse_attn_lse(Q, Kl, Vl, q_off, kv_off, ids, coff, Kb, Vb, 1e6)
+    for b, rows in enumerate(([3, 4, 5], [0, 1, 2])):
+        _, ref = brute.attention_brute(Q[q_off[b]:q_off[b + 1]], Kl[kv_off[b]:kv_off[b + 1]],
+                                       Vl[kv_off[b]:kv_off[b + 1]], Kb[rows], Vb[rows], 1 + b, 1e6, with_lse=True)
+        np.testing.assert_allclose(got[q_off[b]:q_off[b + 1]], np.array(ref), atol=1e-12)
