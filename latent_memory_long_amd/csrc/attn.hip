@@ -20,11 +20,12 @@
 //    key sequence is [rows of the selected documents in rank order ; local keys]; the
 //    workgroup maps each key of a 32-key tile to its source row (bank row of a selected
 //    document, read from HBM or over the host link from pinned memory, or a local row),
-//    stages K in LDS row-major and V transposed (double-buffered, the next tile's loads in
-//    flight during the current tile's math), and runs an online softmax in float32.
+//    stages K and V in LDS row-major (double-buffered, the next two tiles' loads in flight
+//    during the current tile's math), and runs an online softmax in float32.
 //    S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 leaves each lane with 8 scores of one
 //    query row, which are exactly the P^T operand of O^T = V^T * P^T, so probabilities
-//    never leave registers.
+//    never leave registers; V^T comes from the row-major tile through gfx950's
+//    transposing LDS load.
 //  * attn_valu (float32): one thread per (query row, head), plain online softmax.
 //  * attn_combine: merges the per-split (max, sum, unnormalised output) triples.
 #include <math.h>
@@ -40,14 +41,13 @@ template <int D, int NW, int MTW>
 __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
   constexpr int KK = D / 32;
   constexpr int MD = D / 16;
-  constexpr int KSTR = D + 8;   // bf16 per K row in LDS
-  constexpr int VSTR = KT + 8;  // bf16 per V^T row in LDS
-  constexpr int UNITS = 2 * KT * (D / 8);  // 16-byte K and V units of one tile
+  constexpr int KSTR = D + 16;  // bf16 per K / V row in LDS: 32 bytes of padding keep the
+                                // row reads and the transposed reads conflict-free
   constexpr int THREADS = 64 * NW;
-  constexpr int UPT = (UNITS + THREADS - 1) / THREADS;
+  constexpr int UPT = 2 * tile_upk<D, THREADS>();
   constexpr int ROWS = NW * MTW * 16;  // query rows per workgroup (MTW 16-row tiles per wave)
   __shared__ __align__(16) bf16_t Ks[2][KT * KSTR];
-  __shared__ __align__(16) bf16_t Vt[2][D * VSTR];
+  __shared__ __align__(16) bf16_t Vs[2][KT * KSTR];
   __shared__ int64_t mstart[1025], mpre[1025];
   __shared__ int sh_keff;
   __shared__ int64_t sh_M;
@@ -198,9 +198,10 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
       const bool rescale = __ballot(alpha != 1.f) != 0;
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
-        const bf16_t* vr = &Vt[buf][(md * 16 + cl) * VSTR];
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vr + g4 * 4);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + g4 * 4);
+        // A operand V^T: element md*16 + cl over keys g4*4 .. +3 and 16 + g4*4 .. +3
+        const bf16_t* vr = &Vs[buf][(g4 * 4 + (cl >> 2)) * KSTR + md * 16 + (cl & 3) * 4];
+        const uint2 v0 = lds_read_tr16(vr);
+        const uint2 v1 = lds_read_tr16(vr + 16 * KSTR);
         const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
         if (rescale) {
 #pragma unroll
@@ -210,18 +211,18 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
       }
     }
   };
-  if (k_lo < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, k_lo, stA);
-  if (k_lo + KT < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, k_lo + KT, stB);
+  if (k_lo < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, k_lo, stA);
+  if (k_lo + KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, k_lo + KT, stB);
   for (int64_t kt = k_lo; kt < k_hi;) {
-    tile_commit<D, THREADS, UPT, KSTR, VSTR>(tid, stA, Ks[0], Vt[0]);
+    tile_commit<D, THREADS, UPT, KSTR, true>(tid, stA, Ks[0], Vs[0]);
     __syncthreads();  // tile visible; the other buffer is free again
-    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, kt + 2 * KT, stA);
+    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stA);
     tile_math(0, kt);
     kt += KT;
     if (kt >= k_hi) break;
-    tile_commit<D, THREADS, UPT, KSTR, VSTR>(tid, stB, Ks[1], Vt[1]);
+    tile_commit<D, THREADS, UPT, KSTR, true>(tid, stB, Ks[1], Vs[1]);
     __syncthreads();
-    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT>(ts, tid, kt + 2 * KT, stB);
+    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stB);
     tile_math(1, kt);
     kt += KT;
   }

@@ -35,8 +35,6 @@
 namespace msa {
 namespace {
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-
 struct BwdK {
   AttnK f;         // forward arguments; f.Qrot / f.Krot are the rotated copies
   const void* O;   // forward output [total_q, hq, D]
@@ -53,87 +51,11 @@ struct BwdK {
   int kblocks;     // bwd_dkv workgroups per (query, kv head)
 };
 
-// Source row of key `key` of a query: a bank row of the document of rank r (mpre[r] <=
-// key < mpre[r+1]) while key < M, else local row key - M.  Returns the row's element
-// offset for kv head g and whether it is a bank row.
-__device__ __forceinline__ int64_t key_row(const int64_t* mstart, const int64_t* mpre, int keff, int64_t M,
-                                           int64_t key, int kv0, int hkv, int g, int D, bool& bank,
-                                           int64_t& row) {
-  if (key < M) {
-    int lo = 0, hi = keff;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (mpre[mid] <= key) lo = mid; else hi = mid;
-    }
-    row = mstart[lo] + (key - mpre[lo]);
-    bank = true;
-  } else {
-    row = kv0 + (key - M);
-    bank = false;
-  }
-  return (row * hkv + g) * D;
-}
-
 // ---- dQ and the row statistics -----------------------------------------------------
-// Tile staging: K and V row-major (A operands of S^T and dP^T; dQ^T reads K transposed).
-// Stage slot j < UPK holds K unit tid + j*THREADS of the tile, slot UPK + j the V unit of
-// the same key and elements, so each key's source row is located once.
-template <int D, int THREADS>
-constexpr int bwd_upk() { return (KT * (D / 8) + THREADS - 1) / THREADS; }
-
-template <int D, int THREADS, int UPT, bool WITHV>
-__device__ __forceinline__ void bwd_fetch(const TileSrc ts, int tid, int64_t kt, uint4 (&stage)[UPT]) {
-  constexpr int UPR = D / 8;
-  constexpr int UPK = bwd_upk<D, THREADS>();
-#pragma unroll
-  for (int j = 0; j < UPK; ++j) {
-    const int u = tid + j * THREADS;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-    if (u < KT * UPR) {
-      const int kr = u / UPR, e0 = (u % UPR) * 8;
-      const int64_t key = kt + kr;
-      if (key < ts.k_hi) {
-        bool bank;
-        int64_t row;
-        const int64_t off = key_row(ts.mstart, ts.mpre, ts.keff, ts.M, key, ts.kv0, ts.hkv, ts.g, D, bank, row) + e0;
-        kv = *reinterpret_cast<const uint4*>((bank ? ts.Kb : ts.Kr) + off);
-        if (WITHV) vv = *reinterpret_cast<const uint4*>((bank ? ts.Vb : ts.Vl) + off);
-      }
-    }
-    stage[j] = kv;
-    if (WITHV) stage[UPK + j] = vv;
-  }
-}
-
-template <int D, int THREADS, int UPT, int KSTR, bool WITHV>
-__device__ __forceinline__ void bwd_commit(int tid, const uint4 (&stage)[UPT], bf16_t* Ks, bf16_t* Vs) {
-  constexpr int UPR = D / 8;
-  constexpr int UPK = bwd_upk<D, THREADS>();
-#pragma unroll
-  for (int j = 0; j < UPK; ++j) {
-    const int u = tid + j * THREADS;
-    if (u < KT * UPR) {
-      const int kr = u / UPR, e0 = (u % UPR) * 8;
-      *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = stage[j];
-      if (WITHV) *reinterpret_cast<uint4*>(&Vs[kr * KSTR + e0]) = stage[UPK + j];
-    }
-  }
-}
+// K and V tiles are staged row-major (A operands of S^T and dP^T); dQ^T reads K transposed.
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32x2_to_bf16x2(lo, hi);
-}
-
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane L
-// names 4 consecutive 16-bit elements E[L][0..3]; lane i receives E[i/4 + 4j][i%4] for
-// j = 0..3.  Pointing lane L at row r0 + L/4, column c0 + 4*(L%4) of a row-major tile thus
-// hands lane i the column c0 + i over rows r0 .. r0+3: the k-contiguous B operand of a
-// product that sums over rows.
-__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-  return __builtin_bit_cast(uint2, v);
 }
 
 template <int D, int NW, int MTW>
@@ -143,7 +65,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
   constexpr int MD = D / 16;
   constexpr int KSTR = D + 16;  // 32 bytes of padding: row and transposed reads are conflict-free
   constexpr int THREADS = 64 * NW;
-  constexpr int UPT = 2 * bwd_upk<D, THREADS>();
+  constexpr int UPT = 2 * tile_upk<D, THREADS>();
   constexpr int ROWS = NW * MTW * 16;
   __shared__ __align__(16) bf16_t Ks[2][KT * KSTR];
   __shared__ __align__(16) bf16_t Vs[2][KT * KSTR];
@@ -284,18 +206,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
         }
       }
     };
-    if (0 < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, 0, stA);
-    if (KT < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, KT, stB);
+    if (0 < k_hi) tile_fetch<D, THREADS, UPT, false>(ts, tid, 0, stA);
+    if (KT < k_hi) tile_fetch<D, THREADS, UPT, false>(ts, tid, KT, stB);
     for (int64_t kt = 0; kt < k_hi;) {
-      bwd_commit<D, THREADS, UPT, KSTR, false>(tid, stA, Ks[0], Vs[0]);
+      tile_commit<D, THREADS, UPT, KSTR, false>(tid, stA, Ks[0], Vs[0]);
       __syncthreads();
-      if (kt + 2 * KT < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, kt + 2 * KT, stA);
+      if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, false>(ts, tid, kt + 2 * KT, stA);
       lse_math(0, kt);
       kt += KT;
       if (kt >= k_hi) break;
-      bwd_commit<D, THREADS, UPT, KSTR, false>(tid, stB, Ks[1], Vs[1]);
+      tile_commit<D, THREADS, UPT, KSTR, false>(tid, stB, Ks[1], Vs[1]);
       __syncthreads();
-      if (kt + 2 * KT < k_hi) bwd_fetch<D, THREADS, UPT, false>(ts, tid, kt + 2 * KT, stB);
+      if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, false>(ts, tid, kt + 2 * KT, stB);
       lse_math(1, kt);
       kt += KT;
     }
@@ -366,18 +288,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
       }
     }
   };
-  if (0 < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, 0, stA);
-  if (KT < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, KT, stB);
+  if (0 < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, 0, stA);
+  if (KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, KT, stB);
   for (int64_t kt = 0; kt < k_hi;) {
-    bwd_commit<D, THREADS, UPT, KSTR, true>(tid, stA, Ks[0], Vs[0]);
+    tile_commit<D, THREADS, UPT, KSTR, true>(tid, stA, Ks[0], Vs[0]);
     __syncthreads();
-    if (kt + 2 * KT < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stA);
+    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stA);
     dq_math(0, kt);
     kt += KT;
     if (kt >= k_hi) break;
-    bwd_commit<D, THREADS, UPT, KSTR, true>(tid, stB, Ks[1], Vs[1]);
+    tile_commit<D, THREADS, UPT, KSTR, true>(tid, stB, Ks[1], Vs[1]);
     __syncthreads();
-    if (kt + 2 * KT < k_hi) bwd_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stB);
+    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stB);
     dq_math(1, kt);
     kt += KT;
   }

@@ -148,9 +148,9 @@ __device__ __forceinline__ MemMap build_memmap(const int32_t* ids, int k, const 
   return {keff, run};
 }
 
-// Staging of one 32-key tile: 16-byte unit u < KT*D/8 is a K unit, the rest V units.
-// Key index -> source row: a bank row of the selected document of rank r (mpre[r] <= key <
-// mpre[r+1]) while key < M, else local row key - M.
+// Staging of one 32-key tile, K and V row-major.  Key index -> source row: a bank row of
+// the selected document of rank r (mpre[r] <= key < mpre[r+1]) while key < M, else local
+// row key - M.
 struct TileSrc {
   const bf16_t *Kb, *Vb, *Kr, *Vl;
   const int64_t *mstart, *mpre;
@@ -158,66 +158,81 @@ struct TileSrc {
   int64_t M, k_hi;
 };
 
-template <int D, int THREADS, int UPT>
+// Source row of key `key` of a query; returns the row's element offset for kv head g and
+// whether it is a bank row.
+__device__ __forceinline__ int64_t key_row(const int64_t* mstart, const int64_t* mpre, int keff, int64_t M,
+                                           int64_t key, int kv0, int hkv, int g, int D, bool& bank,
+                                           int64_t& row) {
+  if (key < M) {
+    int lo = 0, hi = keff;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (mpre[mid] <= key) lo = mid; else hi = mid;
+    }
+    row = mstart[lo] + (key - mpre[lo]);
+    bank = true;
+  } else {
+    row = kv0 + (key - M);
+    bank = false;
+  }
+  return (row * hkv + g) * D;
+}
+
+// 16-byte K units of a tile per thread; stage slot j < UPK holds K unit tid + j*THREADS,
+// slot UPK + j the V unit of the same key and elements, so each key's row is located once.
+template <int D, int THREADS>
+constexpr int tile_upk() { return (KT * (D / 8) + THREADS - 1) / THREADS; }
+
+template <int D, int THREADS, int UPT, bool WITHV>
 __device__ __forceinline__ void tile_fetch(const TileSrc ts, int tid, int64_t kt, uint4 (&stage)[UPT]) {
   constexpr int UPR = D / 8;
-  constexpr int UNITS = 2 * KT * UPR;
+  constexpr int UPK = tile_upk<D, THREADS>();
+  static_assert(UPT >= (WITHV ? 2 : 1) * UPK, "stage too small");
 #pragma unroll
-  for (int j = 0; j < UPT; ++j) {
+  for (int j = 0; j < UPK; ++j) {
     const int u = tid + j * THREADS;
-    uint4 wv = make_uint4(0, 0, 0, 0);
-    if (u < UNITS) {
-      const bool isv = u >= KT * UPR;
-      const int uu = isv ? u - KT * UPR : u;
-      const int kr = uu / UPR, e0 = (uu % UPR) * 8;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
+    if (u < KT * UPR) {
+      const int kr = u / UPR, e0 = (u % UPR) * 8;
       const int64_t key = kt + kr;
       if (key < ts.k_hi) {
-        const bf16_t* p;
-        if (key < ts.M) {
-          int lo = 0, hi = ts.keff;
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (ts.mpre[mid] <= key) lo = mid; else hi = mid;
-          }
-          const int64_t brow = ts.mstart[lo] + (key - ts.mpre[lo]);
-          p = (isv ? ts.Vb : ts.Kb) + (brow * ts.hkv + ts.g) * D + e0;
-        } else {
-          const int64_t lrow = ts.kv0 + (key - ts.M);
-          p = (isv ? ts.Vl : ts.Kr) + (lrow * ts.hkv + ts.g) * D + e0;
-        }
-        wv = *reinterpret_cast<const uint4*>(p);
+        bool bank;
+        int64_t row;
+        const int64_t off = key_row(ts.mstart, ts.mpre, ts.keff, ts.M, key, ts.kv0, ts.hkv, ts.g, D, bank, row) + e0;
+        kv = *reinterpret_cast<const uint4*>((bank ? ts.Kb : ts.Kr) + off);
+        if (WITHV) vv = *reinterpret_cast<const uint4*>((bank ? ts.Vb : ts.Vl) + off);
       }
     }
-    stage[j] = wv;
+    stage[j] = kv;
+    if (WITHV) stage[UPK + j] = vv;
   }
 }
 
-template <int D, int THREADS, int UPT, int KSTR, int VSTR>
-__device__ __forceinline__ void tile_commit(int tid, const uint4 (&stage)[UPT], bf16_t* Ks, bf16_t* Vt) {
+template <int D, int THREADS, int UPT, int KSTR, bool WITHV>
+__device__ __forceinline__ void tile_commit(int tid, const uint4 (&stage)[UPT], bf16_t* Ks, bf16_t* Vs) {
   constexpr int UPR = D / 8;
-  constexpr int UNITS = 2 * KT * UPR;
+  constexpr int UPK = tile_upk<D, THREADS>();
 #pragma unroll
-  for (int j = 0; j < UPT; ++j) {
+  for (int j = 0; j < UPK; ++j) {
     const int u = tid + j * THREADS;
-    if (u < UNITS) {
-      const bool isv = u >= KT * UPR;
-      const int uu = isv ? u - KT * UPR : u;
-      const int kr = uu / UPR, e0 = (uu % UPR) * 8;
-      if (!isv) {
-        *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = stage[j];
-      } else {
-        const uint32_t w0 = stage[j].x, w1 = stage[j].y, w2 = stage[j].z, w3 = stage[j].w;
-        Vt[(e0 + 0) * VSTR + kr] = (bf16_t)(w0 & 0xffffu);
-        Vt[(e0 + 1) * VSTR + kr] = (bf16_t)(w0 >> 16);
-        Vt[(e0 + 2) * VSTR + kr] = (bf16_t)(w1 & 0xffffu);
-        Vt[(e0 + 3) * VSTR + kr] = (bf16_t)(w1 >> 16);
-        Vt[(e0 + 4) * VSTR + kr] = (bf16_t)(w2 & 0xffffu);
-        Vt[(e0 + 5) * VSTR + kr] = (bf16_t)(w2 >> 16);
-        Vt[(e0 + 6) * VSTR + kr] = (bf16_t)(w3 & 0xffffu);
-        Vt[(e0 + 7) * VSTR + kr] = (bf16_t)(w3 >> 16);
-      }
+    if (u < KT * UPR) {
+      const int kr = u / UPR, e0 = (u % UPR) * 8;
+      *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = stage[j];
+      if (WITHV) *reinterpret_cast<uint4*>(&Vs[kr * KSTR + e0]) = stage[UPK + j];
     }
   }
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane L
+// names 4 consecutive 16-bit elements E[L][0..3]; lane i receives E[i/4 + 4j][i%4] for
+// j = 0..3.  Pointing lane L at row r0 + L/4, column c0 + 4*(L%4) of a row-major tile thus
+// hands lane i the column c0 + i over rows r0 .. r0+3: the k-contiguous operand of a
+// product that sums over the tile's rows.
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(uint2, v);
 }
 
 }  // namespace
