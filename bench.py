@@ -185,13 +185,23 @@ def time_batch(dev, bank, reps=20):
     dQr = torch.empty(Qr.shape, dtype=f32, device=dev)
     dKr = torch.zeros(Krb.shape, dtype=f32, device=dev)
     rws = torch.empty(max(M.msa_route_backward_workspace(B, N, C, sh.h_r), 256), dtype=torch.uint8, device=dev)
+    # a training step's forward scan keeps every bank row's best token for the backward
+    rows = (torch.empty((B, C), dtype=torch.float32, device=dev), torch.empty((B, C), dtype=torch.int32, device=dev))
+    ds_rows = torch.empty_like(ds)
+    ev_rows = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps + 2)]
+    for e in ev_rows:
+        e[0].record()
+        M.msa_route_scan(Qr, q_off_d, Lmax, Krb, coff_d, out=ds_rows, rows=rows)
+        e[1].record()
+    torch.cuda.synchronize()
+    scan_rows = [e[0].elapsed_time(e[1]) for e in ev_rows[2:]]
 
     def run_bwd(ev):
         ev[0].record()
         M.msa_sparse_attn_backward(Q, Kl, Vl, q_off_d, q_off_d, Lmax, ids, coff_d, Kb, Vb, out, dO,
                                    rope_base=sh.rope_base, dbank=gb, out=gq, workspace=bws, lse=lse)
         ev[1].record()
-        M.msa_route_backward(Qr, q_off_d, Lmax, Krb, coff_d, dD, dKrbar=dKr, out=dQr, workspace=rws)
+        M.msa_route_backward(Qr, q_off_d, Lmax, Krb, coff_d, dD, dKrbar=dKr, out=dQr, workspace=rws, rows=rows)
         ev[2].record()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 2)]
@@ -216,7 +226,8 @@ def time_batch(dev, bank, reps=20):
            "attend_backward_tflops": bflops / t_abwd / 1e12,
            "attend_backward_mfma_util": bflops / t_abwd / 1e12 / MFMA_PEAK_BF16_TFLOPS,
            "attend_forward_tflops": 0.4 * bflops / (pct(attn, 50) / 1e3) / 1e12,
-           "route_backward_p50_ms": round(pct(rbwd, 50), 4),
+           "scan_with_rows_p50_ms": round(pct(scan_rows, 50), 4),
+           "route_backward_p50_ms": round(pct(rbwd, 50), 4), "route_backward_rows": "from the forward scan",
            "route_backward_over_scan": pct(rbwd, 50) / pct(scan, 50)}
     return fig, bwd
 

@@ -109,12 +109,18 @@ msa_status msa_pool(msa_dtype dtype, int32_t n_docs, int64_t n_tokens, int64_t n
  *   Same inputs and score definition as msa_route_topk below;
  *   doc_scores device float [n_queries, n_docs] output (written in full).
  *   A query with no tokens scores -inf for every document.
+ *   row_scores, row_arg  optional (both or neither; NULL: not written), for training:
+ *              device float / int32 [n_queries, n_chunks].  row_scores[b, c] is bank row
+ *              c's largest token score for query b (-inf for a query with no tokens), and
+ *              row_arg[b, c] the first token (index within the query) reaching it, defined
+ *              where row_scores is finite.  A document's score is the largest of its rows'.
+ *              msa_route_backward takes them to skip its own scan.
  */
 msa_status msa_route_scan(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                           const int32_t* q_off, int32_t max_q_len, const void* Qr,
                           int32_t h_r, int32_t d, int32_t n_docs, int64_t n_chunks,
                           const int64_t* chunk_off, const void* Krbar, float* doc_scores,
-                          msa_stream_t stream);
+                          float* row_scores, int32_t* row_arg, msa_stream_t stream);
 
 /* Bytes of workspace msa_topk needs (0 when none; else a 256-byte aligned buffer). */
 size_t msa_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
@@ -177,6 +183,8 @@ size_t msa_route_backward_workspace(int32_t n_queries, int32_t n_docs, int64_t n
  * document scores msa_route_scan returns for the same arguments:
  *   The first 12 arguments are those of msa_route_scan (same meaning, same layout).
  *   dD         device float [n_queries, n_docs]: dL/dS (0 entries cost nothing).
+ *   row_scores, row_arg  optional (both or neither): msa_route_scan's row outputs for the
+ *              same arguments; NULL runs that scan again (into the workspace).
  *   dQr        device float [total_q, h_r, d], overwritten: dL/dQr.
  *   dKrbar     device float [n_chunks, h_r, d], ADDED TO (the caller zeroes it once).
  *   A document score is one maximum, so its gradient reaches one (token, row) pair: the
@@ -196,8 +204,9 @@ msa_status msa_route_backward(msa_dtype dtype, int32_t n_queries, int64_t total_
                               const int32_t* q_off, int32_t max_q_len, const void* Qr,
                               int32_t h_r, int32_t d, int32_t n_docs, int64_t n_chunks,
                               const int64_t* chunk_off, const void* Krbar, const float* dD,
-                              float* dQr, float* dKrbar, void* workspace,
-                              size_t workspace_bytes, msa_stream_t stream);
+                              const float* row_scores, const int32_t* row_arg, float* dQr,
+                              float* dKrbar, void* workspace, size_t workspace_bytes,
+                              msa_stream_t stream);
 
 /* Loss forms of msa_route_aux_loss. */
 enum { MSA_AUX_BCE = 0, MSA_AUX_INFONCE = 1 };

@@ -52,7 +52,7 @@ def _load() -> ctypes.CDLL:
         "msa_pool": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, I32, I32, I32, F, U32,
                                     P, P, P, P, P, P, P]),
         "msa_route_scan": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
-                                          P, P, P]),
+                                          P, P, P, P, P]),
         "msa_topk_workspace": (SZ, [I32, I32, I32]),
         "msa_topk": (ctypes.c_int, [I32, I32, P, I32, P, P, P, SZ, P]),
         "msa_route_topk_workspace": (SZ, [I32, I32, I32]),
@@ -71,7 +71,7 @@ def _load() -> ctypes.CDLL:
         "msa_bank_load": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(BankInfo), P, P, P, P, P]),
         "msa_route_backward_workspace": (SZ, [I32, I32, I64, I32]),
         "msa_route_backward": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
-                                              P, P, P, P, P, SZ, P]),
+                                              P, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -160,16 +160,30 @@ def msa_pool(K: torch.Tensor, V: torch.Tensor, Kr: torch.Tensor, doc_tok_off: to
 
 
 def msa_route_scan(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar: torch.Tensor,
-                   chunk_off: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
-    """Step B.  Returns every document's score, float32 [B, N]."""
+                   chunk_off: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None,
+                   rows: Optional[tuple] = None):
+    """Step B.  Returns every document's score, float32 [B, N].  For training pass `rows` =
+    (float32 [B, C], int32 [B, C]) device tensors to also get each bank row's best token
+    score and the first token reaching it, which msa_route_backward can reuse."""
     B = q_off.numel() - 1
     N = chunk_off.numel() - 1
     if out is None:
         out = torch.empty((B, N), dtype=torch.float32, device=Krbar.device)
     _check(lib.msa_route_scan(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
                               Krbar.shape[1], Krbar.shape[2], N, Krbar.shape[0], _ptr(chunk_off),
-                              _ptr(Krbar), _ptr(out), _stream(stream)))
+                              _ptr(Krbar), _ptr(out), *_rows(rows, B, Krbar.shape[0]), _stream(stream)))
     return out
+
+
+def _rows(rows: Optional[tuple], B: int, C: int):
+    """Pointers of a (row scores, row args) pair, checked, or two nulls."""
+    if rows is None:
+        return None, None
+    rs, ra = rows
+    if (rs.dtype != torch.float32 or ra.dtype != torch.int32 or tuple(rs.shape) != (B, C)
+            or tuple(ra.shape) != (B, C) or not (rs.is_cuda and ra.is_cuda)):
+        raise MsaError(MSA_ERR_INVALID_ARG, f"rows must be float32 and int32 device tensors of shape ({B}, {C})")
+    return _ptr(rs), _ptr(ra)
 
 
 def msa_topk_workspace(n_queries: int, n_docs: int, k: int) -> int:
@@ -318,10 +332,11 @@ def msa_route_backward_workspace(n_queries: int, n_docs: int, n_chunks: int, h_r
 def msa_route_backward(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar: torch.Tensor,
                        chunk_off: torch.Tensor, dD: torch.Tensor, dKrbar: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                       stream=None):
+                       stream=None, rows: Optional[tuple] = None):
     """Backward of step B for a loss on the document scores.  dD float32 [B, N] on the
     device.  Returns (dQr, dKrbar), float32; dKrbar is added to (pass your own array to
-    accumulate, else a zero-filled one is made)."""
+    accumulate, else a zero-filled one is made).  `rows`: msa_route_scan's row outputs for
+    the same inputs, which saves scanning the bank again."""
     B = q_off.numel() - 1
     N = chunk_off.numel() - 1
     C, h_r, d = Krbar.shape
@@ -333,7 +348,8 @@ def msa_route_backward(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Kr
     need = msa_route_backward_workspace(B, N, C, h_r)
     ws = _workspace(need, dev, workspace)
     _check(lib.msa_route_backward(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr), h_r,
-                                  d, N, C, _ptr(chunk_off), _ptr(Krbar), _ptr(dD), _ptr(out), _ptr(dKrbar),
+                                  d, N, C, _ptr(chunk_off), _ptr(Krbar), _ptr(dD), *_rows(rows, B, C),
+                                  _ptr(out), _ptr(dKrbar),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out, dKrbar
 

@@ -145,14 +145,19 @@ msa_status check_topk(int32_t n_queries, int32_t n_docs, int32_t k, const int32_
 msa_status msa_route_scan(msa_dtype dtype, int32_t n_queries, int64_t total_q, const int32_t* q_off,
                           int32_t max_q_len, const void* Qr, int32_t h_r, int32_t d, int32_t n_docs,
                           int64_t n_chunks, const int64_t* chunk_off, const void* Krbar,
-                          float* doc_scores, msa_stream_t stream) {
+                          float* doc_scores, float* row_scores, int32_t* row_arg,
+                          msa_stream_t stream) {
   g_last_error.clear();
   msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
                               n_chunks, chunk_off, Krbar);
   if (st != MSA_OK) return st;
   if (!doc_scores) return fail(MSA_ERR_INVALID_ARG, "null doc_scores");
+  if ((row_scores == nullptr) != (row_arg == nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "row_scores and row_arg go together (both or neither)");
   msa::RouteArgs r{(int)dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
                    chunk_off, Krbar, doc_scores, route_path_override()};
+  r.row_scores = row_scores;
+  r.row_arg = row_arg;
   return hip_status(msa::launch_route_scan(r, (hipStream_t)stream), "msa_route_scan launch");
 }
 
@@ -206,18 +211,23 @@ size_t msa_route_backward_workspace(int32_t n_queries, int32_t n_docs, int64_t n
 msa_status msa_route_backward(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                               const int32_t* q_off, int32_t max_q_len, const void* Qr, int32_t h_r,
                               int32_t d, int32_t n_docs, int64_t n_chunks, const int64_t* chunk_off,
-                              const void* Krbar, const float* dD, float* dQr, float* dKrbar,
-                              void* workspace, size_t workspace_bytes, msa_stream_t stream) {
+                              const void* Krbar, const float* dD, const float* row_scores,
+                              const int32_t* row_arg, float* dQr, float* dKrbar, void* workspace,
+                              size_t workspace_bytes, msa_stream_t stream) {
   g_last_error.clear();
   msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
                               n_chunks, chunk_off, Krbar);
   if (st != MSA_OK) return st;
   if (!dD || !dKrbar || (total_q > 0 && !dQr)) return fail(MSA_ERR_INVALID_ARG, "null gradient pointer");
+  if ((row_scores == nullptr) != (row_arg == nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "row_scores and row_arg go together (both or neither)");
   const size_t need = msa_route_backward_workspace(n_queries, n_docs, n_chunks, h_r);
   if (!workspace || workspace_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   if (((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   msa::RouteBwdArgs r{(int)dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
                       chunk_off, Krbar, dD, dQr, dKrbar, workspace};
+  r.row_scores = row_scores;
+  r.row_arg = row_arg;
   return hip_status(msa::launch_route_backward(r, (hipStream_t)stream), "msa_route_backward launch");
 }
 

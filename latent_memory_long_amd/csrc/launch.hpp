@@ -39,6 +39,7 @@ struct RouteArgs {
   int32_t* row_arg = nullptr;   // with row_scores: the first token reaching each row's max
 };
 hipError_t launch_route_scan(const RouteArgs& a, hipStream_t s);
+hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t s);
 bool route_batch_supported(const RouteArgs& a);
 hipError_t launch_route_scan_batch(const RouteArgs& a, hipStream_t s);
 
@@ -58,6 +59,8 @@ struct RouteBwdArgs {
   float* dQr;       // [total_q, h_r, d] overwritten
   float* dKrbar;    // [n_chunks, h_r, d] added to
   void* workspace;
+  const float* row_scores = nullptr;  // optional: the forward scan's row outputs (else rescanned)
+  const int32_t* row_arg = nullptr;
 };
 size_t route_bwd_workspace_bytes(int n_queries, int n_docs, int64_t n_chunks, int h_r);
 hipError_t launch_route_backward(const RouteBwdArgs& a, hipStream_t s);

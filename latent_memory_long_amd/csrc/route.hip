@@ -525,6 +525,23 @@ hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Each document's score as the largest of its rows' scores (-inf for a document without
+// rows): one wave per (query, document).
+__global__ __launch_bounds__(256) void docs_from_rows(const float* rows, const int64_t* chunk_off, float* scores,
+                                                      int n_docs, int64_t n_chunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (n >= n_docs) return;
+  const int64_t c0 = chunk_off[n], c1 = chunk_off[n + 1];
+  const float* r = rows + (int64_t)b * n_chunks;
+  float m = -INFINITY;
+  for (int64_t c = c0 + lane; c < c1; c += 64) m = fmaxf(m, r[c]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) scores[(int64_t)b * n_docs + n] = m;
+}
+
 }  // namespace
 
 // Query rows from which the batched scan (route_batch.hip) takes over.  Below it the scan
@@ -532,7 +549,7 @@ hipError_t launch_dot(const RouteArgs& r, const ScanK& k, hipStream_t s) {
 // token bank: 64 rows 94 us streaming vs 98 us batched; 128 rows 164 vs 128 us).
 constexpr int64_t BATCH_MIN_ROWS = 128;
 
-hipError_t launch_route_scan(const RouteArgs& r, hipStream_t s) {
+static hipError_t launch_scan_paths(const RouteArgs& r, hipStream_t s) {
   ScanK k{r.Qr, r.q_off, r.Krbar, r.chunk_off, r.scores, r.row_scores, r.row_arg, r.n_chunks, r.n_docs, r.h_r};
   // bf16: the MFMA scan at any query length (a short query pads its 16-row tile; the
   // scan stays bound by the bank read and beats the dot-product scan even for one row).
@@ -560,6 +577,20 @@ hipError_t launch_route_scan(const RouteArgs& r, hipStream_t s) {
     case 64: return launch_dot<bf16_t, 64>(r, k, s);
     default: return launch_dot<bf16_t, 128>(r, k, s);
   }
+}
+
+// With row outputs the rows start at -inf (a query without tokens leaves them so), the
+// scan writes each row's maximum and first maximising token, and the document scores are
+// then taken as their rows' maxima: the same floats the scan maximises, so they equal the
+// scores of a scan without row outputs.
+hipError_t launch_route_scan(const RouteArgs& r, hipStream_t s) {
+  if (r.row_scores == nullptr) return launch_scan_paths(r, s);
+  hipError_t e = launch_fill_neg_inf(r.row_scores, (int64_t)r.n_queries * r.n_chunks, s);
+  if (e == hipSuccess) e = launch_scan_paths(r, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(docs_from_rows, dim3((unsigned)((r.n_docs + 3) / 4), (unsigned)r.n_queries), dim3(256), 0, s,
+                     r.row_scores, r.chunk_off, r.scores, r.n_docs, r.n_chunks);
+  return hipGetLastError();
 }
 
 }  // namespace msa

@@ -375,6 +375,14 @@ __global__ void fill_neg_inf(float* p, int64_t n) {
 
 }  // namespace
 
+// A fill kernel rather than a memset, so that the call can be captured in a graph.
+hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_neg_inf, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256), 0, s,
+                     p, n);
+  return hipGetLastError();
+}
+
 bool route_batch_supported(const RouteArgs& r) {
   return r.dtype == 1 && r.d == BD && (r.h_r == 4 || r.h_r == 8);
 }
@@ -392,9 +400,8 @@ hipError_t launch_route_scan_batch(const RouteArgs& r, hipStream_t s) {
            r.row_arg, r.n_chunks, r.n_docs, r.n_queries};
   // -inf: the value of an empty maximum (documents without rows, queries without tokens,
   // and, with row scores, every document: the router's backward reads the rows only)
-  const int64_t n = (int64_t)r.n_queries * r.n_docs;
-  hipLaunchKernelGGL(fill_neg_inf, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256), 0, s,
-                     r.scores, n);
+  const hipError_t e = launch_fill_neg_inf(r.scores, (int64_t)r.n_queries * r.n_docs, s);
+  if (e != hipSuccess) return e;
   return r.h_r == 8 ? launch_h<8>(r, k, s) : launch_h<4>(r, k, s);
 }
 

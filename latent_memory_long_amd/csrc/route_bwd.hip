@@ -229,20 +229,28 @@ hipError_t launch_route_backward(const RouteBwdArgs& r, hipStream_t s) {
   k.cosv = (float*)ws;
   ws += align256(bn * r.h_r * 4);
   k.kinv = (float*)ws;
-  // the forward scan, keeping every row's max over the query's tokens
-  RouteArgs f{r.dtype, r.n_queries, r.total_q, r.q_off, r.max_q_len, r.Qr, r.h_r, r.d, r.n_docs,
-              r.n_chunks, r.chunk_off, r.Krbar, scores, 0};
-  f.row_scores = rows;
-  f.row_arg = rarg;
-  hipError_t e = launch_route_scan(f, s);
-  if (e != hipSuccess) return e;
+  const float* row_scores = rows;
+  const int32_t* row_arg = rarg;
+  if (r.row_scores != nullptr) {
+    // the forward scan's rows, passed in
+    row_scores = r.row_scores;
+    row_arg = r.row_arg;
+  } else {
+    // the forward scan again, keeping every row's max over the query's tokens
+    RouteArgs f{r.dtype, r.n_queries, r.total_q, r.q_off, r.max_q_len, r.Qr, r.h_r, r.d, r.n_docs,
+                r.n_chunks, r.chunk_off, r.Krbar, scores, 0};
+    f.row_scores = rows;
+    f.row_arg = rarg;
+    const hipError_t e = launch_route_scan(f, s);
+    if (e != hipSuccess) return e;
+  }
   k.Qr = r.Qr;
   k.q_off = r.q_off;
   k.Krb = r.Krbar;
   k.chunk_off = r.chunk_off;
   k.dD = r.dD;
-  k.row_scores = rows;
-  k.row_arg = rarg;
+  k.row_scores = row_scores;
+  k.row_arg = row_arg;
   k.dQr = r.dQr;
   k.dKrb = r.dKrbar;
   k.n_chunks = r.n_chunks;

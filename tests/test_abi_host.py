@@ -153,18 +153,19 @@ def test_attn_backward_validation(kw, code):
 
 def _route_bwd(**kw):
     a = dict(dtype=1, B=2, tq=8, q_off=FAKE, maxq=4, Qr=FAKE, h_r=4, d=128, N=10, C=20, coff=FAKE,
-             Krb=FAKE, dD=FAKE, dQr=FAKE, dKrb=FAKE, ws=FAKE, wsb=1 << 30)
+             Krb=FAKE, dD=FAKE, rs=None, ra=None, dQr=FAKE, dKrb=FAKE, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return lib.msa_route_backward(a["dtype"], a["B"], a["tq"], a["q_off"], a["maxq"], a["Qr"], a["h_r"], a["d"],
-                                  a["N"], a["C"], a["coff"], a["Krb"], a["dD"], a["dQr"], a["dKrb"], a["ws"],
-                                  a["wsb"], None)
+                                  a["N"], a["C"], a["coff"], a["Krb"], a["dD"], a["rs"], a["ra"], a["dQr"],
+                                  a["dKrb"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=2), UNSUPPORTED), (dict(h_r=17), UNSUPPORTED), (dict(d=100), UNSUPPORTED),
     (dict(C=3), INVALID), (dict(B=0), INVALID), (dict(maxq=0), INVALID), (dict(dD=None), INVALID),
     (dict(dKrb=None), INVALID), (dict(dQr=None), INVALID), (dict(wsb=100), WORKSPACE),
-    (dict(ws=None), WORKSPACE), (dict(ws=ctypes.c_void_p(0x1010)), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws=ctypes.c_void_p(0x1010)), INVALID), (dict(rs=FAKE), INVALID),
+    (dict(ra=FAKE), INVALID),
 ])
 def test_route_backward_validation(kw, code):
     assert _route_bwd(**kw) == code
@@ -199,3 +200,10 @@ def test_workspace_sizes():
     c = m.msa_route_backward_workspace(2, 10, 20, 4)
     assert c >= 2 * 10 * 4 + 2 * 2 * 20 * 4 + 2 * 10 * (4 + 8) + 2 * 2 * 10 * 4 * 4
     assert m.msa_route_backward_workspace(2, 10, 5, 4) == 0 and m.msa_route_backward_workspace(2, 10, 20, 17) == 0
+
+
+def test_route_scan_rows_go_together():
+    # row scores without row args (or the reverse) is refused before anything runs
+    for rs, ra in ((FAKE, None), (None, FAKE)):
+        assert lib.msa_route_scan(1, 2, 8, FAKE, 4, FAKE, 4, 128, 10, 20, FAKE, FAKE, FAKE, rs, ra, None) == INVALID
+        assert "together" in lib.msa_last_error().decode()

@@ -15,7 +15,7 @@ import torch
 
 import latent_memory_long_amd as M
 from oracle import msa_oracle as O
-from tests.helpers import f64, say
+from tests.helpers import SCORE_FLOOR, SCORE_RTOL, assert_scores_close, f64, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -52,7 +52,14 @@ def _mask_near_ties(Qr64, q_off, Kb64, coff, dD):
     return kept
 
 
-def _run(q_lens, counts, H, D, dtype, seed, path="auto", zero_heads=False, dKinit=False):
+def _scan_rows(Qr_d, q_off_d, max_q_len, Kb_d, coff_d, B, N, C):
+    """The forward scan with its row outputs: (doc scores, row scores, row args)."""
+    rows = (torch.empty((B, C), dtype=torch.float32, device=DEV), torch.empty((B, C), dtype=torch.int32, device=DEV))
+    ds = M.msa_route_scan(Qr_d, q_off_d, max_q_len, Kb_d, coff_d, rows=rows)
+    return ds, rows
+
+
+def _run(q_lens, counts, H, D, dtype, seed, path="auto", zero_heads=False, dKinit=False, use_rows=False):
     torch_dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     q_off = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
     coff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
@@ -72,10 +79,10 @@ def _run(q_lens, counts, H, D, dtype, seed, path="auto", zero_heads=False, dKini
         os.environ["MSA_ROUTE_PATH"] = path
     init = _randn((C, H, D), seed + 4) if dKinit else torch.zeros((C, H, D))
     dK = init.to(DEV)
-    dQr, dK = M.msa_route_backward(Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV),
-                                   int(max(max(q_lens), 1)), Kb.to(DEV),
-                                   torch.tensor(coff, dtype=torch.int64, device=DEV),
-                                   torch.tensor(dD, dtype=torch.float32, device=DEV), dKrbar=dK)
+    args = (Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), int(max(max(q_lens), 1)), Kb.to(DEV),
+            torch.tensor(coff, dtype=torch.int64, device=DEV))
+    rows = _scan_rows(*args, B, N, C)[1] if use_rows else None
+    dQr, dK = M.msa_route_backward(*args, torch.tensor(dD, dtype=torch.float32, device=DEV), dKrbar=dK, rows=rows)
     torch.cuda.synchronize()
     rq, rk = O.route_backward(f64(Qr), q_off, f64(Kb), coff, dD)
     rk = rk + init.double().numpy()
@@ -103,12 +110,14 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("use_rows", [False, True], ids=["rescan", "forward_rows"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_route_backward(case):
+def test_route_backward(case, use_rows):
     name, q_lens, H, D, dtype, path = case
-    say(f"case route backward {name}")
+    say(f"case route backward {name}, rows {'from the forward scan' if use_rows else 'rescanned'}")
     counts = np.random.default_rng(len(name)).integers(1, 13, size=37)
-    got, ref, kept = _run(q_lens, counts, H, D, dtype, seed=len(name) * 7, path=path, zero_heads=True)
+    got, ref, kept = _run(q_lens, counts, H, D, dtype, seed=len(name) * 7, path=path, zero_heads=True,
+                          use_rows=use_rows)
     assert kept >= len(q_lens) * 37 // 3, kept
     _check(got, ref, name)
     # rows no maximum reached keep their initial (zero) value
@@ -130,8 +139,50 @@ def test_route_backward_empty_query():
     # a query with no tokens contributes nothing, whatever dL/dS holds for it
     say("case route backward with an empty query")
     counts = np.random.default_rng(4).integers(1, 6, size=20)
-    got, ref, kept = _run([6, 0, 3], counts, 4, 64, "bf16", seed=91)
-    _check(got, ref, "empty")
+    for use_rows in (False, True):
+        got, ref, kept = _run([6, 0, 3], counts, 4, 64, "bf16", seed=91, use_rows=use_rows)
+        _check(got, ref, "empty")
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_scan_row_outputs(case):
+    # every bank row's best token score and the first token reaching it, from each scan path;
+    # the document scores come out bit-identical to a scan without row outputs
+    name, q_lens, H, D, dtype, path = case
+    say(f"case scan row outputs {name}")
+    q_lens = list(q_lens) + [0]                      # and a query without tokens
+    counts = np.random.default_rng(len(name) + 1).integers(1, 13, size=31)
+    torch_dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q_off = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    coff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    B, N, C = len(q_lens), len(counts), int(coff[-1])
+    Kb = _randn((C, H, D), len(name) + 5).to(torch_dt)
+    Qr = _randn((int(q_off[-1]), H, D), len(name) + 6).to(torch_dt)
+    if path != "auto":
+        os.environ["MSA_ROUTE_PATH"] = path
+    args = (Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), int(max(q_lens)), Kb.to(DEV),
+            torch.tensor(coff, dtype=torch.int64, device=DEV))
+    ds_rows, (rs, ra) = _scan_rows(*args, B, N, C)
+    ds = M.msa_route_scan(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(ds_rows, ds), "document scores differ with row outputs"
+    rs, ra = rs.cpu().numpy(), ra.cpu().numpy()
+    assert np.all(rs[B - 1] == -np.inf), "rows of a query without tokens"
+    Q64, K64 = f64(Qr), f64(Kb)
+    for b in range(B - 1):
+        ts = O.token_chunk_scores(Q64[q_off[b]:q_off[b + 1]], K64)          # [Lq, C]
+        best = ts.max(axis=0)
+        assert_scores_close(rs[b], best, dtype, f"{name} query {b} row scores")
+        assert np.all((ra[b] >= 0) & (ra[b] < q_lens[b])), f"{name} query {b}: row arg out of range"
+        # the chosen token reaches the row's maximum up to the scores' error; where the best
+        # token leads the runner-up by more than that, it is the oracle's first maximum
+        picked = ts[ra[b], np.arange(C)]
+        tol = SCORE_RTOL[dtype] * np.maximum(np.abs(best), SCORE_FLOOR)
+        assert np.all(best - picked <= 2 * tol), f"{name} query {b}: row arg misses the maximum"
+        if q_lens[b] > 1:
+            srt = np.sort(ts, axis=0)
+            clear = srt[-1] - srt[-2] > 2 * tol
+            assert np.array_equal(ra[b][clear], np.argmax(ts, axis=0)[clear]), f"{name} query {b}: row arg"
 
 
 # ------------------------------------------------------------------ routing auxiliary loss
