@@ -29,8 +29,13 @@
  *    MSA_ERR_INVALID_ARG or MSA_ERR_UNSUPPORTED at once, with a message in
  *    msa_last_error().  A failed launch returns MSA_ERR_HIP.  Nothing is printed and no
  *    exception or abort crosses the ABI.
- *  - Device-resident offset arrays are a caller precondition (non-decreasing, every
- *    document has >= 1 token, offsets within the tensors); they are not read on the host.
+ *  - Device-resident offset arrays and selected ids are a caller precondition (offsets
+ *    start at 0, never decrease and end at the stated totals, every document has >= 1
+ *    token and >= 1 bank row, every query has <= max_q_len tokens and at least as many
+ *    local tokens, ids lie in [-1, n_docs)); they are not read on the host.  With the
+ *    environment variable MSA_DEBUG_VALIDATE=1, every entry point copies them to the host
+ *    first (synchronising `stream`) and returns MSA_ERR_INVALID_ARG, naming the first bad
+ *    entry, before any kernel runs.
  *  - Results are deterministic: the same inputs give the same bits.
  */
 #ifndef MSA_H

@@ -13,4 +13,5 @@ from .binding import (  # noqa: F401
     msa_route_backward, msa_route_backward_workspace,
     MSA_AUX_BCE, MSA_AUX_INFONCE, msa_route_aux_loss,
     MSA_ERR_IO, msa_bank_save, msa_bank_read_info, msa_bank_load,
+    MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP,
 )

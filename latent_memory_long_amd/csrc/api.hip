@@ -97,6 +97,11 @@ msa_status msa_pool(msa_dtype dtype, int32_t n_docs, int64_t n_tokens, int64_t n
   if (chunk < 1 || chunk > 128) return fail(MSA_ERR_UNSUPPORTED, "chunk %d not in [1, 128]", chunk);
   if (rope_mask > 7u) return fail(MSA_ERR_INVALID_ARG, "rope_mask 0x%x has unknown bits", rope_mask);
   if (rope_mask && !(rope_base > 0.f && isfinite(rope_base))) return fail(MSA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  if (msa::debug_validate_enabled()) {
+    const msa_status v = msa::debug_validate_pool(n_docs, n_tokens, n_chunks, chunk, doc_tok_off, chunk_off,
+                                                  (hipStream_t)stream);
+    if (v != MSA_OK) return v;
+  }
   msa::PoolArgs a{(int)dtype, n_docs, n_tokens, n_chunks, doc_tok_off, chunk_off, h_kv, h_r, d,
                   chunk, rope_base, rope_mask, K, V, Kr, Kbar, Vbar, Krbar};
   return hip_status(msa::launch_pool(a, (hipStream_t)stream), "msa_pool launch");
@@ -131,6 +136,17 @@ msa_status check_route(msa_dtype dtype, int32_t n_queries, int64_t total_q, cons
   return MSA_OK;
 }
 
+// check_route, then (MSA_DEBUG_VALIDATE=1) the device offsets
+msa_status check_route_all(msa_dtype dtype, int32_t n_queries, int64_t total_q, const int32_t* q_off,
+                           int32_t max_q_len, const void* Qr, int32_t h_r, int32_t d, int32_t n_docs,
+                           int64_t n_chunks, const int64_t* chunk_off, const void* Krbar, msa_stream_t stream) {
+  const msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
+                                    chunk_off, Krbar);
+  if (st != MSA_OK || !msa::debug_validate_enabled()) return st;
+  return msa::debug_validate_route(n_queries, total_q, q_off, max_q_len, n_docs, n_chunks, chunk_off,
+                                   (hipStream_t)stream);
+}
+
 msa_status check_topk(int32_t n_queries, int32_t n_docs, int32_t k, const int32_t* ids, const float* sc) {
   if (n_queries < 1 || n_queries > 65535) return fail(MSA_ERR_INVALID_ARG, "n_queries %d not in [1, 65535]", n_queries);
   if (n_docs < 1) return fail(MSA_ERR_INVALID_ARG, "n_docs must be >= 1 (got %d)", n_docs);
@@ -148,8 +164,8 @@ msa_status msa_route_scan(msa_dtype dtype, int32_t n_queries, int64_t total_q, c
                           float* doc_scores, float* row_scores, int32_t* row_arg,
                           msa_stream_t stream) {
   g_last_error.clear();
-  msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
-                              n_chunks, chunk_off, Krbar);
+  msa_status st = check_route_all(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
+                                  n_chunks, chunk_off, Krbar, stream);
   if (st != MSA_OK) return st;
   if (!doc_scores) return fail(MSA_ERR_INVALID_ARG, "null doc_scores");
   if ((row_scores == nullptr) != (row_arg == nullptr))
@@ -182,8 +198,8 @@ msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                           float* doc_scores, void* workspace, size_t workspace_bytes,
                           msa_stream_t stream) {
   g_last_error.clear();
-  msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
-                              n_chunks, chunk_off, Krbar);
+  msa_status st = check_route_all(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
+                                  n_chunks, chunk_off, Krbar, stream);
   if (st != MSA_OK) return st;
   st = check_topk(n_queries, n_docs, k, topk_ids, topk_scores);
   if (st != MSA_OK) return st;
@@ -215,8 +231,8 @@ msa_status msa_route_backward(msa_dtype dtype, int32_t n_queries, int64_t total_
                               const int32_t* row_arg, float* dQr, float* dKrbar, void* workspace,
                               size_t workspace_bytes, msa_stream_t stream) {
   g_last_error.clear();
-  msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
-                              n_chunks, chunk_off, Krbar);
+  msa_status st = check_route_all(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs,
+                                  n_chunks, chunk_off, Krbar, stream);
   if (st != MSA_OK) return st;
   if (!dD || !dKrbar || (total_q > 0 && !dQr)) return fail(MSA_ERR_INVALID_ARG, "null gradient pointer");
   if ((row_scores == nullptr) != (row_arg == nullptr))
@@ -311,6 +327,11 @@ msa_status msa_sparse_attn(msa_dtype dtype, int32_t n_queries, int64_t total_q, 
     const msa_status st = host_bank_alias(Kbar, Vbar, &kb, &vb);
     if (st != MSA_OK) return st;
   }
+  if (msa::debug_validate_enabled()) {
+    const msa_status v = msa::debug_validate_attn(n_queries, total_q, total_kv, q_off, kv_off, max_q_len, k,
+                                                  topk_ids, n_docs, n_chunks, chunk_off, (hipStream_t)stream);
+    if (v != MSA_OK) return v;
+  }
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   msa::AttnArgs a{(int)dtype, n_queries, total_q, total_kv, q_off, kv_off, max_q_len, Q, Kloc, Vloc,
                   hq, h_kv, d, rope_base, sc, k, topk_ids, n_docs, n_chunks, chunk_off, kb, vb, O,
@@ -362,6 +383,11 @@ msa_status msa_sparse_attn_backward(msa_dtype dtype, int32_t n_queries, int64_t 
   if (kv_source == 1) {
     const msa_status st = host_bank_alias(Kbar, Vbar, &kb, &vb);
     if (st != MSA_OK) return st;
+  }
+  if (msa::debug_validate_enabled()) {
+    const msa_status v = msa::debug_validate_attn(n_queries, total_q, total_kv, q_off, kv_off, max_q_len, k,
+                                                  topk_ids, n_docs, n_chunks, chunk_off, (hipStream_t)stream);
+    if (v != MSA_OK) return v;
   }
   msa::AttnBwdArgs a{};
   a.f = msa::AttnArgs{(int)dtype, n_queries, total_q, total_kv, q_off, kv_off, max_q_len, Q, Kloc, Vloc,
