@@ -45,11 +45,11 @@ SCAN_KERNEL = "route_scan_mfma"
 # HBM traffic of the scan kernel per launch, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # on this workload (scaled by the counters' reading of a copy kernel of known size).  It is
 # reported only while the kernel source still has the digest it was measured with.
-TRAFFIC = {"route_sha": "87e317c342c9b9bb",
-           # FETCH_SIZE 1,588,783 KiB per launch x 1.99995 (a 1 GiB copy reads 524,302 KiB)
-           "fetch_bytes": 3253741422,
-           # WRITE_SIZE 198.97 KiB per launch x 1.0 (a 1 GiB copy writes 1,048,576 KiB)
-           "write_bytes": 203744}
+TRAFFIC = {"route_sha": "2cef6de018561b38",
+           # FETCH_SIZE 1,588,751 KiB per launch x 1.99995 (a 1 GiB copy reads 524,302 KiB)
+           "fetch_bytes": 3253675913,
+           # WRITE_SIZE 199.12 KiB per launch x 1.0 (a 1 GiB copy writes 1,048,576 KiB)
+           "write_bytes": 203899}
 
 
 def log(msg):
