@@ -484,7 +484,7 @@ def main():
     pre = [(q["Qr"][:Lq].contiguous(), q["Q"][:Lq].contiguous(), q["Kloc"][:Lq].contiguous(),
             q["Vloc"][:Lq].contiguous()) for q in qs]
 
-    def run(n_slots, steps):
+    def run(n_slots, steps, sync_each=False):
         """`steps` timed steps, query i on stream i mod n_slots (default priority).  With one
         slot the queries run one at a time.  With several, queries are in flight together
         as concurrent requests are on a serving GPU: one query's top-k and host-link-bound
@@ -510,6 +510,14 @@ def main():
         for i in range(args.warmup):
             step(i, wev)
         torch.cuda.synchronize()
+        if sync_each:  # host wall time of a step that waits for its own result
+            host = []
+            for i in range(steps):
+                t0 = time.perf_counter()
+                step(i, evs[i])
+                torch.cuda.synchronize()
+                host.append((time.perf_counter() - t0) * 1e3)
+            return host
         t0 = time.perf_counter()
         for i in range(steps):
             step(i, evs[i])
@@ -519,6 +527,7 @@ def main():
 
     log(f"timing {args.steps} steps, one query at a time")
     wall, evs, ids = run(1, args.steps)
+    host_sync_ms = run(1, min(args.steps, 50), sync_each=True)
     serving = None
     if args.inflight > 1:
         log(f"serving throughput: {args.steps} steps with {args.inflight} queries in flight")
@@ -629,7 +638,8 @@ def main():
         "latency_ms": {"route_attend_p50": round(pct(step_ms, 50), 4),
                        "route_attend_p90": round(pct(step_ms, 90), 4),
                        "scan_p50": round(pct(scan_ms, 50), 4), "topk_p50": round(pct(topk_ms, 50), 4),
-                       "attend_p50": round(pct(attn_ms, 50), 4)},
+                       "attend_p50": round(pct(attn_ms, 50), 4),
+                       "route_attend_host_sync_p50": round(pct(host_sync_ms, 50), 4)},
         "serving": serving,
         "roofline": {"kernel": SCAN_KERNEL, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
