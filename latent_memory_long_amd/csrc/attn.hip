@@ -124,9 +124,8 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
   ts.kv0 = kv0;
   ts.M = M;
   ts.k_hi = k_hi;
-  // Two tiles of loads in flight: register stages A and B take turns (a tile is fetched
-  // two tiles ahead of its use), so the gather latency spans two tiles of math.
-  uint4 stA[UPT], stB[UPT];
+  // The gathers run TILE_RING tiles ahead of the math (tile_pipeline; two when a stage
+  // takes many registers per thread).
   auto tile_math = [&](int buf, int64_t kt) __attribute__((always_inline)) {
     // every key of the tile is visible to every row of the block: no masking needed
     const bool full_tile = kt + KT <= k_hi && kt + KT - 1 <= key_lim_min && rb + ROWS <= nrows;
@@ -174,11 +173,11 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
           for (int i = 0; i < 4; ++i) p[n][i] = 0.f;
       } else {
         const float mb = m_new * scale_log2;
-        alpha = exp2f(m_run[m] * scale_log2 - mb);
+        alpha = exp2_hw(m_run[m] * scale_log2 - mb);
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[n][i] = exp2f(fmaf(s[n][i], scale_log2, -mb));
+          for (int i = 0; i < 4; ++i) p[n][i] = exp2_hw(fmaf(s[n][i], scale_log2, -mb));
       }
       m_run[m] = m_new;
       float ps = 0.f;
@@ -211,21 +210,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
       }
     }
   };
-  if (k_lo < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, k_lo, stA);
-  if (k_lo + KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, k_lo + KT, stB);
-  for (int64_t kt = k_lo; kt < k_hi;) {
-    tile_commit<D, THREADS, UPT, KSTR, true>(tid, stA, Ks[0], Vs[0]);
-    __syncthreads();  // tile visible; the other buffer is free again
-    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stA);
-    tile_math(0, kt);
-    kt += KT;
-    if (kt >= k_hi) break;
-    tile_commit<D, THREADS, UPT, KSTR, true>(tid, stB, Ks[1], Vs[1]);
-    __syncthreads();
-    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stB);
-    tile_math(1, kt);
-    kt += KT;
-  }
+  tile_pipeline<(UPT <= 4 ? TILE_RING : 2), D, THREADS, UPT, KSTR, true>(ts, tid, k_lo, k_hi, Ks[0], Ks[1], Vs[0], Vs[1], tile_math);
 
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {

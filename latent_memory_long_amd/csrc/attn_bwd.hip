@@ -174,8 +174,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
     }
   };
 
-  // Two tiles of loads in flight: register stages A and B take turns.
-  uint4 stA[UPT], stB[UPT];
   // ---- pass 1: log-sum-exp of every row (log2 units), unless the forward's is given ----
   float lse[MTW];
   if (bk.lse_in == nullptr) {
@@ -200,27 +198,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
 #pragma unroll
           for (int n = 0; n < 2; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ps += exp2f(s[n][i] - m_new);
-          l_run[m] = l_run[m] * exp2f(m_run[m] - m_new) + ps;
+            for (int i = 0; i < 4; ++i) ps += exp2_hw(s[n][i] - m_new);
+          l_run[m] = l_run[m] * exp2_hw(m_run[m] - m_new) + ps;
           m_run[m] = m_new;
         }
       }
     };
-    if (0 < k_hi) tile_fetch<D, THREADS, UPT, false>(ts, tid, 0, stA);
-    if (KT < k_hi) tile_fetch<D, THREADS, UPT, false>(ts, tid, KT, stB);
-    for (int64_t kt = 0; kt < k_hi;) {
-      tile_commit<D, THREADS, UPT, KSTR, false>(tid, stA, Ks[0], Vs[0]);
-      __syncthreads();
-      if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, false>(ts, tid, kt + 2 * KT, stA);
-      lse_math(0, kt);
-      kt += KT;
-      if (kt >= k_hi) break;
-      tile_commit<D, THREADS, UPT, KSTR, false>(tid, stB, Ks[1], Vs[1]);
-      __syncthreads();
-      if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, false>(ts, tid, kt + 2 * KT, stB);
-      lse_math(1, kt);
-      kt += KT;
-    }
+    tile_pipeline<(UPT <= 4 ? TILE_RING : 2), D, THREADS, UPT, KSTR, false>(ts, tid, 0, k_hi, Ks[0], Ks[1], Vs[0], Vs[1], lse_math);
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       float l = l_run[m] + __shfl_xor(l_run[m], 16);
@@ -266,7 +250,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(s[n][i] - lse[m]);  // 0 where not visible (s = -inf)
+          const float p = exp2_hw(s[n][i] - lse[m]);  // 0 where not visible (s = -inf)
           ds[n][i] = p * (dp[i] - drow[m]);
         }
       }
@@ -288,21 +272,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
       }
     }
   };
-  if (0 < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, 0, stA);
-  if (KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, KT, stB);
-  for (int64_t kt = 0; kt < k_hi;) {
-    tile_commit<D, THREADS, UPT, KSTR, true>(tid, stA, Ks[0], Vs[0]);
-    __syncthreads();
-    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stA);
-    dq_math(0, kt);
-    kt += KT;
-    if (kt >= k_hi) break;
-    tile_commit<D, THREADS, UPT, KSTR, true>(tid, stB, Ks[1], Vs[1]);
-    __syncthreads();
-    if (kt + 2 * KT < k_hi) tile_fetch<D, THREADS, UPT, true>(ts, tid, kt + 2 * KT, stB);
-    dq_math(1, kt);
-    kt += KT;
-  }
+  tile_pipeline<(UPT <= 4 ? TILE_RING : 2), D, THREADS, UPT, KSTR, true>(ts, tid, 0, k_hi, Ks[0], Ks[1], Vs[0], Vs[1], dq_math);
 
   // lane holds dQ~^T[d = md*16 + g4*4 + i][row cl]; natural-scale gradient = scale * acc
 #pragma unroll
@@ -486,7 +456,7 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
           float p[4], dsv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p[i] = row0 + i >= rowmin[nt] ? exp2f(fmaf(sacc[nt][i], sl2, -Lr[i])) : 0.f;
+            p[i] = row0 + i >= rowmin[nt] ? exp2_hw(fmaf(sacc[nt][i], sl2, -Lr[i])) : 0.f;
             dsv[i] = p[i] * (dpacc[nt][i] - Rr[i]);
           }
           pw[nt][sub * 2] = pack_bf16x2(p[0], p[1]);

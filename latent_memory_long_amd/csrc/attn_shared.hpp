@@ -223,6 +223,35 @@ __device__ __forceinline__ void tile_commit(int tid, const uint4 (&stage)[UPT], 
   }
 }
 
+// The key loop of the attention kernels: tiles k_lo, k_lo + KT, ... below k_hi are gathered
+// into a ring of RING register stages, RING tiles ahead of their use, and written to the LDS
+// buffer of their parity just before their math (RING even: a tile's buffer alternates).
+// One barrier per tile: a wave writes tile i's buffer only after every wave has passed tile
+// i-1's barrier, hence finished tile i-2's math on that buffer.  (The barrier waits for the
+// LDS traffic only; the gathers of the tiles ahead stay in flight across it.)
+constexpr int TILE_RING = 4;
+
+template <int RING, int D, int THREADS, int UPT, int KSTR, bool WITHV, typename F>
+__device__ __forceinline__ void tile_pipeline(const TileSrc& ts, int tid, int64_t k_lo, int64_t k_hi,
+                                              bf16_t* Ks0, bf16_t* Ks1, bf16_t* Vs0, bf16_t* Vs1, F&& math) {
+  static_assert(RING % 2 == 0, "tiles alternate between two LDS buffers");
+  uint4 st[RING][UPT];
+#pragma unroll
+  for (int r = 0; r < RING; ++r)
+    if (k_lo + r * KT < k_hi) tile_fetch<D, THREADS, UPT, WITHV>(ts, tid, k_lo + r * KT, st[r]);
+  for (int64_t k0 = k_lo; k0 < k_hi; k0 += RING * KT) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const int64_t kt = k0 + r * KT;
+      if (kt >= k_hi) break;  // uniform
+      tile_commit<D, THREADS, UPT, KSTR, WITHV>(tid, st[r], (r & 1) ? Ks1 : Ks0, (r & 1) ? Vs1 : Vs0);
+      __syncthreads();
+      if (kt + RING * KT < k_hi) tile_fetch<D, THREADS, UPT, WITHV>(ts, tid, kt + RING * KT, st[r]);
+      math(r & 1, kt);
+    }
+  }
+}
+
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane L
 // names 4 consecutive 16-bit elements E[L][0..3]; lane i receives E[i/4 + 4j][i%4] for
 // j = 0..3.  Pointing lane L at row r0 + L/4, column c0 + 4*(L%4) of a row-major tile thus

@@ -9,6 +9,11 @@ namespace msa {
 constexpr float LN2 = 0.69314718055994531f;    // ln 2: log2-domain values to natural log
 constexpr float LOG2E = 1.44269504088896341f;  // log2 e: natural log to log2 domain
 
+// 2^x on the hardware's v_exp_f32 (about 1 ulp), without the library's rescaling for results
+// below 2^-126: softmax weights that small only ever round to zero or a denormal, which no
+// sum notices.  exp2_hw(-inf) = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---- element types -------------------------------------------------------------------
 // bf16 is carried as its 16-bit pattern: the upper half of an IEEE float32.
 typedef uint16_t bf16_t;
