@@ -259,3 +259,92 @@ def test_batch32_bank10m_full():
         check_route_sample(Qr[q_off[b]:q_off[b + 1]], Krb, coff, ds[b], ids_h[b], wl.k,
                            sample_docs(len(lens), 10 + b)[:25] + list(ids_h[b]), f"batch query {b}")
     attn_check(q, ids, coff, Kb, Vb, sh.rope_base, sorted(set([0, longest])), "batch32")
+
+
+def test_batch32_bank10m_training_full():
+    """The training backward of the 32-query batch over the 10M-token bank, in the bench's
+    launch configuration (forward log-sum-exp and scan rows reused).  One sampled query
+    carries the only nonzero dO and dL/dS, so every gradient it produces (its dQ and local
+    dK/dV rows, the bank rows of its documents, its dQr rows and the maximising rows' dKrbar)
+    can be checked against the oracle run on that query alone, and every other query's
+    gradients must be exactly zero."""
+    say("case full-size batch32_bank10m training backward, one sampled query")
+    wl = W.workload("batch32_bank10m")
+    sh = wl.shape
+    lens = W.doc_lengths(wl)
+    coff = M.msa_chunk_offsets(W.token_offsets(lens), sh.chunk)
+    N, C = len(lens), int(coff[-1])
+    Krb, Kb, Vb = W.gen_pooled_bank(wl, coff, DEV)
+    coff_d = torch.tensor(coff, device=DEV)
+    q = W.gen_queries(wl, DEV)
+    q_len = q["q_len"]
+    B = len(q_len)
+    q_off = np.concatenate([[0], np.cumsum(q_len)]).astype(np.int32)
+    q_off_d = torch.tensor(q_off, device=DEV)
+    Lmax = int(q_len.max())
+    Qr, Q, Kl, Vl = q["Qr"], q["Q"], q["Kloc"], q["Vloc"]
+    tq = int(q_off[-1])
+    # forward: scan with row outputs, top-k, attention with log-sum-exp
+    rows = (torch.empty((B, C), dtype=torch.float32, device=DEV), torch.empty((B, C), dtype=torch.int32, device=DEV))
+    ds = M.msa_route_scan(Qr, q_off_d, Lmax, Krb, coff_d, rows=rows)
+    ids, sc = M.msa_topk(ds, wl.k)
+    lse = torch.empty((tq, sh.hq), dtype=torch.float32, device=DEV)
+    out = M.msa_sparse_attn(Q, Kl, Vl, q_off_d, q_off_d, Lmax, ids, coff_d, Kb, Vb, rope_base=sh.rope_base, lse=lse)
+    b = 7
+    r0, r1 = int(q_off[b]), int(q_off[b + 1])
+    g = torch.Generator(device=DEV).manual_seed(11)
+    dO = torch.zeros_like(Q)
+    dO[r0:r1] = torch.randn((r1 - r0,) + tuple(Q.shape[1:]), generator=g, device=DEV).to(torch.bfloat16)
+    # dL/dS on sampled documents of query b whose best (token, row) pair is clear of the runner-up
+    Qb64 = f64(Qr[r0:r1])
+    cand = sample_docs(N, 21)[:30]
+    keep = []
+    for d in cand:
+        s = np.sort(O.token_chunk_scores(Qb64, f64(Krb[int(coff[d]):int(coff[d + 1])])).ravel())[::-1]
+        if s.size == 1 or s[0] - s[1] >= 5e-3:
+            keep.append(d)
+    assert len(keep) >= 10, keep
+    dD = torch.zeros((B, N), dtype=torch.float32, device=DEV)
+    dvals = torch.randn(len(keep), generator=torch.Generator().manual_seed(12))
+    dD[b, torch.tensor(keep, device=DEV)] = dvals.to(DEV)
+    f32 = torch.float32
+    dKb, dVb = torch.zeros(Kb.shape, dtype=f32, device=DEV), torch.zeros(Vb.shape, dtype=f32, device=DEV)
+    gq = M.msa_sparse_attn_backward(Q, Kl, Vl, q_off_d, q_off_d, Lmax, ids, coff_d, Kb, Vb, out, dO,
+                                    rope_base=sh.rope_base, dbank=(dKb, dVb), lse=lse)
+    dKr = torch.zeros(Krb.shape, dtype=f32, device=DEV)
+    dQr, _ = M.msa_route_backward(Qr, q_off_d, Lmax, Krb, coff_d, dD, dKrbar=dKr, rows=rows)
+    torch.cuda.synchronize()
+    # every other query: exactly zero gradients
+    for t in (gq[0], gq[1], gq[2], dQr):
+        assert torch.count_nonzero(t[:r0]) == 0 and torch.count_nonzero(t[r1:]) == 0
+    # attention backward of query b against the oracle on its own compact bank
+    sel = [int(d) for d in ids[b].cpu().numpy() if d >= 0]
+    idx = np.concatenate([np.arange(coff[d], coff[d + 1]) for d in sel])
+    cnt = [int(coff[d + 1] - coff[d]) for d in sel]
+    coff_c = np.concatenate([[0], np.cumsum(cnt)])
+    idx_d = torch.as_tensor(idx, device=DEV)
+    L = r1 - r0
+    ref = O.sparse_attn_backward(f64(Q[r0:r1]), f64(Kl[r0:r1]), f64(Vl[r0:r1]), [0, L], [0, L],
+                                 np.arange(len(sel), dtype=np.int32)[None], coff_c, f64(Kb[idx_d]), f64(Vb[idx_d]),
+                                 sh.rope_base, f64(dO[r0:r1]))
+    got = (gq[0][r0:r1], gq[1][r0:r1], gq[2][r0:r1], dKb[idx_d], dVb[idx_d])
+    for gg, oo, n in zip(got, ref, ("dQ", "dKloc", "dVloc", "dKbar", "dVbar")):
+        gg = f64(gg)
+        top = float(np.max(np.abs(oo)))
+        err = float(np.max(np.abs(gg - oo)))
+        say(f"  query {b} {n}: max err {err:.3g}, oracle max {top:.3g}")
+        assert err <= 2.0 ** -6 * top + 1e-4, n
+    # router backward of query b on the sampled documents
+    cnt_r = [int(coff[d + 1] - coff[d]) for d in keep]
+    coff_r = np.concatenate([[0], np.cumsum(cnt_r)])
+    idx_r = torch.as_tensor(np.concatenate([np.arange(coff[d], coff[d + 1]) for d in keep]), device=DEV)
+    rq, rk = O.route_backward(Qb64, [0, L], f64(Krb[idx_r]), coff_r, dvals.double().numpy()[None])
+    for gg, oo, n in ((f64(dQr[r0:r1]), rq, "dQr"), (f64(dKr[idx_r]), rk, "dKrbar")):
+        top = float(np.max(np.abs(oo)))
+        err = float(np.max(np.abs(gg - oo)))
+        say(f"  query {b} {n}: max err {err:.3g}, oracle max {top:.3g}")
+        assert err <= 1e-4 * top + 1e-7, n
+    # rows of the bank no sampled document owns get no router gradient
+    mask = torch.ones(C, dtype=torch.bool, device=DEV)
+    mask[idx_r] = False
+    assert torch.count_nonzero(dKr[mask]) == 0
