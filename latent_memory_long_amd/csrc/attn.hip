@@ -20,8 +20,9 @@
 //    key sequence is [rows of the selected documents in rank order ; local keys]; the
 //    workgroup maps each key of a 32-key tile to its source row (bank row of a selected
 //    document, read from HBM or over the host link from pinned memory, or a local row),
-//    stages K and V in LDS row-major (double-buffered, the next two tiles' loads in flight
-//    during the current tile's math), and runs an online softmax in float32.
+//    stages K and V in LDS row-major (double-buffered, the gathers of the next tiles in
+//    flight during the current tile's math: tile_pipeline), and runs an online softmax in
+//    float32.
 //    S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 leaves each lane with 8 scores of one
 //    query row, which are exactly the P^T operand of O^T = V^T * P^T, so probabilities
 //    never leave registers; V^T comes from the row-major tile through gfx950's
