@@ -443,8 +443,8 @@ def main():
                          "against which hardware byte counters are scaled")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sharded "
-              "multi-GPU path is not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "sharded multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     dev = "cuda:0"
