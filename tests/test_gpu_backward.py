@@ -108,6 +108,9 @@ CASES = [
     ("gqa2_d64_ragged", [5, 33, 17], [0, 2, 40], 8, 4, 64, [4, 1, 9, 30, 2, 6, 3],
      [[2, 4, -1], [4, 0, 3], [6, 5, 4]]),
     ("few_docs_k_gt_n", [20], [3], 16, 4, 128, [2, 5], [[1, 0, -1, -1]]),
+    # dQ row blocks of 32 and 64 query rows (2 and 4 waves)
+    ("rows32_d128", [8], [2], 32, 8, 128, [4, 9, 2], [[2, 0]]),
+    ("rows64_d128", [16, 5], [0, 3], 32, 8, 128, [4, 9, 2, 6], [[3, 1], [0, 2]]),
     # 8 queries x 8 kv heads fill the GPU without splitting the keys: the forward writes O
     # and the log-sum-exp straight from the attention kernel instead of the split merge
     ("batch8_unsplit", [12, 3, 20, 7, 1, 16, 9, 5], [0, 4, 0, 2, 30, 0, 1, 0], 32, 8, 128,

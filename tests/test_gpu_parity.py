@@ -363,6 +363,10 @@ ATTN_CASES = [
     ("decode", "bf16", 32, 8, 128, [1], 40, 16),
     ("batch_ragged", "bf16", 32, 8, 128, [1, 16, 37, 64, 130], 3, 8),
     ("gqa2_d64", "bf16", 8, 4, 64, [20, 5], 7, 4),
+    # row blocks of 32, 64 and 128 query rows (2, 4 and 8 waves of one 16-row tile)
+    ("rows32_d128", "bf16", 32, 8, 128, [8], 5, 6),
+    ("rows64_d128", "bf16", 32, 8, 128, [16, 3], 2, 6),
+    ("rows128_d128", "bf16", 32, 8, 128, [32, 7], 0, 6),
     ("d32", "bf16", 4, 2, 32, [9], 0, 3),
     ("fp32_tiny", "f32", 4, 2, 32, [8, 3], 2, 2),
     ("fp32_d128", "f32", 8, 2, 128, [5], 1, 3),
