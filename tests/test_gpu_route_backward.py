@@ -250,3 +250,17 @@ def test_route_training_chain():
     rq, rk = O.route_backward(f64(Qr), q_off, f64(Kb), coff, rd)
     assert np.allclose(f64(loss), rl, rtol=1e-4, atol=1e-6)
     _check((f64(dQr), f64(dK)), (rq, rk), "chain")
+
+
+def test_route_backward_many_queries_shared_rows():
+    # 1,032 queries over 6 short documents: every bank row maximises many queries' scores, so
+    # its gradient gathers hundreds of atomic additions.  The query gradient has a fixed
+    # summation order: two runs give the same bits.
+    say("case route backward, 1032 queries sharing 6 documents' rows, run twice")
+    counts = np.array([1, 3, 2, 4, 1, 2])
+    q_lens = [1] * 1030 + [3, 2]
+    got, ref, kept = _run(q_lens, counts, 4, 64, "bf16", seed=92)
+    assert kept >= len(q_lens) * len(counts) // 3, kept
+    _check(got, ref, "shared rows")
+    again, _, _ = _run(q_lens, counts, 4, 64, "bf16", seed=92)
+    assert np.array_equal(got[0], again[0]), "dQr differs between two identical runs"
