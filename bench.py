@@ -45,11 +45,11 @@ SCAN_KERNEL = "route_scan_mfma"
 # HBM traffic of the scan kernel per launch, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # on this workload (scaled by the counters' reading of a copy kernel of known size).  It is
 # reported only while the kernel source still has the digest it was measured with.
-TRAFFIC = {"route_sha": "2cef6de018561b38",
-           # FETCH_SIZE 1,588,747 KiB per launch x 1.99995 (a 1 GiB copy reads 524,302 KiB)
-           "fetch_bytes": 3253666031,
-           # WRITE_SIZE 199.03 KiB per launch x 1.0 (a 1 GiB copy writes 1,048,576 KiB)
-           "write_bytes": 203808}
+TRAFFIC = {"route_sha": "00e317962530e847",
+           # FETCH_SIZE 1,588,789 KiB per launch x 1.99995 (a 1 GiB copy reads 524,301 KiB)
+           "fetch_bytes": 3253751574,
+           # WRITE_SIZE 199.22 KiB per launch x 1.0 (a 1 GiB copy writes 1,048,576 KiB)
+           "write_bytes": 204000}
 
 
 def log(msg):
