@@ -104,6 +104,48 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+_FLOAT = (torch.float32, torch.bfloat16)
+
+
+def _need(t, name: str, dtype=None, shape=None):
+    """Refuse a tensor argument whose dtype, shape or layout does not match what the C entry
+    point will read through its pointer (a wrong integer width there would be read as
+    garbage offsets).  ``dtype`` is one dtype or a tuple of allowed ones; ``shape`` a tuple
+    whose None entries match any size."""
+    if not isinstance(t, torch.Tensor):
+        raise MsaError(MSA_ERR_INVALID_ARG, f"{name} must be a torch tensor (got {type(t).__name__})")
+    allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+    if dtype is not None and t.dtype not in allowed:
+        raise MsaError(MSA_ERR_INVALID_ARG, f"{name} has dtype {t.dtype}, need {' or '.join(map(str, allowed))}")
+    if shape is not None:
+        bad = t.dim() != len(shape) or any(w is not None and int(n) != int(w) for n, w in zip(t.shape, shape))
+        if bad:
+            want = "(" + ", ".join("*" if w is None else str(int(w)) for w in shape) + ")"
+            raise MsaError(MSA_ERR_INVALID_ARG, f"{name} has shape {tuple(t.shape)}, need {want}")
+    if not t.is_contiguous():
+        raise MsaError(MSA_ERR_INVALID_ARG, f"{name} must be contiguous")
+    return t
+
+
+def _same_device(*named, pinned_ok=()):
+    """Every named tensor on one GPU; those listed in ``pinned_ok`` may instead be in
+    page-locked host memory.  None entries are skipped."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.is_cuda:
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise MsaError(MSA_ERR_INVALID_ARG, f"{name} is on {t.device}, other arguments on {dev}")
+        elif name in pinned_ok and t.is_pinned():
+            continue
+        else:
+            where = "a device tensor or pinned host memory" if name in pinned_ok else "a device tensor"
+            raise MsaError(MSA_ERR_INVALID_ARG, f"{name} must be {where}")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -111,8 +153,11 @@ def _stream(stream) -> Optional[int]:
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
-    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
-        return ws
+    if ws is not None:
+        _need(ws, "workspace")
+        _same_device(("workspace", ws))
+        if ws.numel() * ws.element_size() >= nbytes:
+            return ws
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
@@ -146,13 +191,23 @@ def msa_pool(K: torch.Tensor, V: torch.Tensor, Kr: torch.Tensor, doc_tok_off: to
              rope_mask: int = MSA_ROPE_K, out=None, stream=None):
     """Step A.  K, V [T, h_kv, d]; Kr [T, h_r, d]; offsets int64 on the device.
     Returns (Kbar, Vbar, Krbar) [n_chunks, h, d]."""
+    _need(K, "K", _FLOAT, (None, None, None))
     T, h_kv, d = K.shape
+    _need(V, "V", K.dtype, (T, h_kv, d))
+    _need(Kr, "Kr", K.dtype, (T, None, d))
     h_r = Kr.shape[1]
+    _need(doc_tok_off, "doc_tok_off", torch.int64, (None,))
+    _need(chunk_off, "chunk_off", torch.int64, (doc_tok_off.numel(),))
     if out is None:
         out = (torch.empty((n_chunks, h_kv, d), dtype=K.dtype, device=K.device),
                torch.empty((n_chunks, h_kv, d), dtype=K.dtype, device=K.device),
                torch.empty((n_chunks, h_r, d), dtype=K.dtype, device=K.device))
     Kb, Vb, Krb = out
+    _need(Kb, "Kbar", K.dtype, (n_chunks, h_kv, d))
+    _need(Vb, "Vbar", K.dtype, (n_chunks, h_kv, d))
+    _need(Krb, "Krbar", K.dtype, (n_chunks, h_r, d))
+    _same_device(("K", K), ("V", V), ("Kr", Kr), ("doc_tok_off", doc_tok_off), ("chunk_off", chunk_off),
+                 ("Kbar", Kb), ("Vbar", Vb), ("Krbar", Krb))
     _check(lib.msa_pool(_dtype_code(K), doc_tok_off.numel() - 1, T, n_chunks, _ptr(doc_tok_off),
                         _ptr(chunk_off), h_kv, h_r, d, chunk, rope_base, rope_mask, _ptr(K), _ptr(V),
                         _ptr(Kr), _ptr(Kb), _ptr(Vb), _ptr(Krb), _stream(stream)))
@@ -165,14 +220,28 @@ def msa_route_scan(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar:
     """Step B.  Returns every document's score, float32 [B, N].  For training pass `rows` =
     (float32 [B, C], int32 [B, C]) device tensors to also get each bank row's best token
     score and the first token reaching it, which msa_route_backward can reuse."""
-    B = q_off.numel() - 1
-    N = chunk_off.numel() - 1
+    B, N = _route_inputs(Qr, q_off, Krbar, chunk_off)
     if out is None:
         out = torch.empty((B, N), dtype=torch.float32, device=Krbar.device)
+    _need(out, "doc_scores", torch.float32, (B, N))
+    _route_devices(Qr, q_off, Krbar, chunk_off, ("doc_scores", out))
     _check(lib.msa_route_scan(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
                               Krbar.shape[1], Krbar.shape[2], N, Krbar.shape[0], _ptr(chunk_off),
                               _ptr(Krbar), _ptr(out), *_rows(rows, B, Krbar.shape[0]), _stream(stream)))
     return out
+
+
+def _route_inputs(Qr, q_off, Krbar, chunk_off):
+    """Checks of the router's inputs; returns (queries, documents)."""
+    _need(Krbar, "Krbar", _FLOAT, (None, None, None))
+    _need(Qr, "Qr", Krbar.dtype, (None, Krbar.shape[1], Krbar.shape[2]))
+    _need(q_off, "q_off", torch.int32, (None,))
+    _need(chunk_off, "chunk_off", torch.int64, (None,))
+    return q_off.numel() - 1, chunk_off.numel() - 1
+
+
+def _route_devices(Qr, q_off, Krbar, chunk_off, *outputs):
+    _same_device(("Krbar", Krbar), ("Qr", Qr), ("q_off", q_off), ("chunk_off", chunk_off), *outputs)
 
 
 def _rows(rows: Optional[tuple], B: int, C: int):
@@ -193,11 +262,15 @@ def msa_topk_workspace(n_queries: int, n_docs: int, k: int) -> int:
 def msa_topk(doc_scores: torch.Tensor, k: int, out=None, workspace: Optional[torch.Tensor] = None,
              stream=None):
     """Step C.  doc_scores float32 [B, N] -> (ids int32 [B, k], scores float32 [B, k])."""
+    _need(doc_scores, "doc_scores", torch.float32, (None, None))
     B, N = doc_scores.shape
     if out is None:
         out = (torch.empty((B, k), dtype=torch.int32, device=doc_scores.device),
                torch.empty((B, k), dtype=torch.float32, device=doc_scores.device))
     ids, sc = out
+    _need(ids, "topk_ids", torch.int32, (B, k))
+    _need(sc, "topk_scores", torch.float32, (B, k))
+    _same_device(("doc_scores", doc_scores), ("topk_ids", ids), ("topk_scores", sc))
     need = msa_topk_workspace(B, N, k)
     ws = _workspace(need, doc_scores.device, workspace) if need else None
     _check(lib.msa_topk(B, N, _ptr(doc_scores), k, _ptr(ids), _ptr(sc), _ptr(ws),
@@ -214,14 +287,18 @@ def msa_route_topk(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar:
                    workspace: Optional[torch.Tensor] = None, stream=None):
     """Steps B + C.  Qr [total_q, h_r, d]; q_off int32 [B+1]; Krbar [C, h_r, d].
     Returns (topk_ids int32 [B,k], topk_scores f32 [B,k], doc_scores f32 [B,N] or None)."""
-    B = q_off.numel() - 1
-    N = chunk_off.numel() - 1
+    B, N = _route_inputs(Qr, q_off, Krbar, chunk_off)
     dev = Krbar.device
     if out is None:
         out = (torch.empty((B, k), dtype=torch.int32, device=dev),
                torch.empty((B, k), dtype=torch.float32, device=dev),
                torch.empty((B, N), dtype=torch.float32, device=dev) if want_doc_scores else None)
     ids, sc, ds = out
+    _need(ids, "topk_ids", torch.int32, (B, k))
+    _need(sc, "topk_scores", torch.float32, (B, k))
+    if ds is not None:
+        _need(ds, "doc_scores", torch.float32, (B, N))
+    _route_devices(Qr, q_off, Krbar, chunk_off, ("topk_ids", ids), ("topk_scores", sc), ("doc_scores", ds))
     ws, wsb = None, 0
     need = msa_route_topk_workspace(B, N, k) if ds is None else msa_topk_workspace(B, N, k)
     if need:
@@ -250,17 +327,16 @@ def msa_sparse_attn(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Tensor, q_o
     device, or in pinned host memory (then read over the host link).  Returns O.  Pass a
     float32 [total_q, hq] device tensor as `lse` to also get each row's log-sum-exp (natural
     log), which msa_sparse_attn_backward can reuse."""
-    B = q_off.numel() - 1
+    B, N, k, kv_source = _attn_inputs(Q, Kloc, Vloc, q_off, kv_off, topk_ids, chunk_off, Kbar, Vbar)
     total_q, hq, d = Q.shape
     total_kv, h_kv, _ = Kloc.shape
-    k = topk_ids.shape[1]
-    N = chunk_off.numel() - 1
-    kv_source = 0 if Kbar.is_cuda else 1
-    if kv_source == 1 and not (Kbar.is_pinned() and Vbar.is_pinned()):
-        raise MsaError(MSA_ERR_INVALID_ARG, "host-resident Kbar/Vbar must be pinned")
     dev = Q.device
     if out is None:
         out = torch.empty_like(Q)
+    _need(out, "O", Q.dtype, tuple(Q.shape))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (total_q, hq))
+    _attn_devices(Q, Kloc, Vloc, q_off, kv_off, topk_ids, chunk_off, Kbar, Vbar, ("O", out), ("lse", lse))
     code = _dtype_code(Q)
     _check_lse(lse, total_q, hq)
     need = msa_sparse_attn_workspace(code, B, total_q, total_kv, max_q_len, hq, h_kv, d)
@@ -271,6 +347,33 @@ def msa_sparse_attn(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Tensor, q_o
                                _ptr(Vbar), kv_source, _ptr(out), _ptr(lse), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
     return out
+
+
+def _attn_inputs(Q, Kloc, Vloc, q_off, kv_off, topk_ids, chunk_off, Kbar, Vbar):
+    """Checks of the attention's inputs; returns (queries, documents, k, kv_source)."""
+    _need(Q, "Q", _FLOAT, (None, None, None))
+    total_q, hq, d = Q.shape
+    _need(Kloc, "Kloc", Q.dtype, (None, None, d))
+    _need(Vloc, "Vloc", Q.dtype, tuple(Kloc.shape))
+    h_kv = Kloc.shape[1]
+    _need(q_off, "q_off", torch.int32, (None,))
+    B = q_off.numel() - 1
+    _need(kv_off, "kv_off", torch.int32, (B + 1,))
+    _need(topk_ids, "topk_ids", torch.int32, (B, None))
+    _need(chunk_off, "chunk_off", torch.int64, (None,))
+    _need(Kbar, "Kbar", Q.dtype, (None, h_kv, d))
+    _need(Vbar, "Vbar", Q.dtype, tuple(Kbar.shape))
+    kv_source = 0 if Kbar.is_cuda else 1
+    return B, chunk_off.numel() - 1, topk_ids.shape[1], kv_source
+
+
+def _attn_devices(Q, Kloc, Vloc, q_off, kv_off, topk_ids, chunk_off, Kbar, Vbar, *outputs):
+    """Every tensor on one GPU, the bank's content rows there too or both in pinned host memory."""
+    if Kbar.is_cuda != Vbar.is_cuda:
+        raise MsaError(MSA_ERR_INVALID_ARG, "Kbar and Vbar must both be on the device or both in pinned host memory")
+    _same_device(("Q", Q), ("Kloc", Kloc), ("Vloc", Vloc), ("q_off", q_off), ("kv_off", kv_off),
+                 ("topk_ids", topk_ids), ("chunk_off", chunk_off), ("Kbar", Kbar), ("Vbar", Vbar), *outputs,
+                 pinned_ok=("Kbar", "Vbar"))
 
 
 def _check_lse(lse: Optional[torch.Tensor], total_q: int, hq: int):
@@ -293,15 +396,12 @@ def msa_sparse_attn_backward(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Te
     ([n_chunks, h_kv, d] on the device) are added to: pass `dbank` to accumulate into your
     own arrays, else zero-filled ones are made.  `lse`: the forward's log-sum-exp output for
     the same inputs, which saves recomputing it."""
-    B = q_off.numel() - 1
+    B, N, k, kv_source = _attn_inputs(Q, Kloc, Vloc, q_off, kv_off, topk_ids, chunk_off, Kbar, Vbar)
     total_q, hq, d = Q.shape
     total_kv, h_kv, _ = Kloc.shape
-    k = topk_ids.shape[1]
-    N = chunk_off.numel() - 1
     C = Kbar.shape[0]
-    kv_source = 0 if Kbar.is_cuda else 1
-    if kv_source == 1 and not (Kbar.is_pinned() and Vbar.is_pinned()):
-        raise MsaError(MSA_ERR_INVALID_ARG, "host-resident Kbar/Vbar must be pinned")
+    _need(O, "O", Q.dtype, tuple(Q.shape))
+    _need(dO, "dO", Q.dtype, tuple(Q.shape))
     dev = Q.device
     f32 = torch.float32
     if out is None:
@@ -312,6 +412,16 @@ def msa_sparse_attn_backward(Q: torch.Tensor, Kloc: torch.Tensor, Vloc: torch.Te
         dbank = (torch.zeros((C, h_kv, d), dtype=f32, device=dev), torch.zeros((C, h_kv, d), dtype=f32, device=dev))
     dQ, dKl, dVl = out
     dKb, dVb = dbank
+    f32 = torch.float32
+    _need(dQ, "dQ", f32, (total_q, hq, d))
+    _need(dKl, "dKloc", f32, (total_kv, h_kv, d))
+    _need(dVl, "dVloc", f32, (total_kv, h_kv, d))
+    _need(dKb, "dKbar", f32, (C, h_kv, d))
+    _need(dVb, "dVbar", f32, (C, h_kv, d))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (total_q, hq))
+    _attn_devices(Q, Kloc, Vloc, q_off, kv_off, topk_ids, chunk_off, Kbar, Vbar, ("O", O), ("dO", dO),
+                  ("dQ", dQ), ("dKloc", dKl), ("dVloc", dVl), ("dKbar", dKb), ("dVbar", dVb), ("lse", lse))
     _check_lse(lse, total_q, hq)
     need = msa_sparse_attn_backward_workspace(total_q, total_kv, hq, h_kv, d)
     ws = _workspace(need, dev, workspace)
@@ -337,14 +447,17 @@ def msa_route_backward(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Kr
     device.  Returns (dQr, dKrbar), float32; dKrbar is added to (pass your own array to
     accumulate, else a zero-filled one is made).  `rows`: msa_route_scan's row outputs for
     the same inputs, which saves scanning the bank again."""
-    B = q_off.numel() - 1
-    N = chunk_off.numel() - 1
+    B, N = _route_inputs(Qr, q_off, Krbar, chunk_off)
     C, h_r, d = Krbar.shape
     dev = Krbar.device
     if out is None:
         out = torch.empty((Qr.shape[0], h_r, d), dtype=torch.float32, device=dev)
     if dKrbar is None:
         dKrbar = torch.zeros((C, h_r, d), dtype=torch.float32, device=dev)
+    _need(dD, "dD", torch.float32, (B, N))
+    _need(out, "dQr", torch.float32, (Qr.shape[0], h_r, d))
+    _need(dKrbar, "dKrbar", torch.float32, (C, h_r, d))
+    _route_devices(Qr, q_off, Krbar, chunk_off, ("dD", dD), ("dQr", out), ("dKrbar", dKrbar))
     need = msa_route_backward_workspace(B, N, C, h_r)
     ws = _workspace(need, dev, workspace)
     _check(lib.msa_route_backward(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr), h_r,
@@ -362,11 +475,16 @@ def msa_route_aux_loss(doc_scores: torch.Tensor, labels: torch.Tensor, kind: int
                        temperature: float = 1.0, out: Optional[tuple] = None, stream=None):
     """Routing auxiliary loss on float32 [B, N] document scores and labels (device).
     Returns (per-query loss [B], dL/dS [B, N]) for L = the mean of the per-query losses."""
+    _need(doc_scores, "doc_scores", torch.float32, (None, None))
     B, N = doc_scores.shape
+    _need(labels, "labels", torch.float32, (B, N))
     if out is None:
         out = (torch.empty(B, dtype=torch.float32, device=doc_scores.device),
                torch.empty((B, N), dtype=torch.float32, device=doc_scores.device))
     loss, dD = out
+    _need(loss, "loss", torch.float32, (B,))
+    _need(dD, "dD", torch.float32, (B, N))
+    _same_device(("doc_scores", doc_scores), ("labels", labels), ("loss", loss), ("dD", dD))
     _check(lib.msa_route_aux_loss(kind, B, N, _ptr(doc_scores), _ptr(labels), temperature, _ptr(loss),
                                   _ptr(dD), _stream(stream)))
     return loss, dD

@@ -3,9 +3,9 @@
 // hysenlabs.com "EverMind-AI/MSA: routing top-k compressed documents inside attention ...":
 //  * "Routing happens inside attention ...": the selected documents' compressed K/V are
 //    concatenated with the query's local K/V for decoding;
-//  * "Document-wise RoPE resets ..." (second paragraph): global RoPE over the active
-//    context; the query's start index is offset by k, the number of retrieved blocks, so
-//    the causal order is memory, then query, then generation;
+//  * "Document-wise RoPE resets ..." (second paragraph): positions over the active context
+//    are global; local tokens sit at positions k_eff + j, after the k_eff selected
+//    documents, and every key is visible in the order memory, query, generated tokens;
 //  * "The 100M-token setup depends on host memory ...": content K/V may stay in host
 //    DRAM and be fetched only when selected.
 // yeyulingfeng.com "深度分析MSA ..." section 五 step 3: generation sees only the query's

@@ -1,7 +1,10 @@
 """Comparison helpers for the GPU parity tests (tolerances as stated in the design notes)."""
 from __future__ import annotations
 
+import concurrent.futures
+import os
 import sys
+import time
 
 import numpy as np
 import torch
@@ -103,3 +106,59 @@ def assert_attn_close(gpu: torch.Tensor, oracle64: np.ndarray, dtype: str, what:
     assert np.all(np.isfinite(g[rows])), f"{what}: non-finite output"
     assert err.max(initial=0) <= ATTN_ATOL[dtype], f"{what}: max abs err {err.max():.3g}"
     return float(err.max(initial=0))
+
+
+def host_threads() -> int:
+    """Host threads for oracle work: the cores this process may run on, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def doc_groups(coff: np.ndarray, block: int):
+    """Consecutive document ranges [d0, d1) of about ``block`` bank rows each (a document
+    larger than the block is a group of its own)."""
+    coff = np.asarray(coff, dtype=np.int64)
+    N = len(coff) - 1
+    out, d0 = [], 0
+    while d0 < N:
+        d1 = int(np.searchsorted(coff, coff[d0] + block, side="right")) - 1
+        d1 = min(max(d1, d0 + 1), N)
+        out.append((d0, d1))
+        d0 = d1
+    return out
+
+
+def oracle_doc_scores_all(Qr: torch.Tensor, q_off, Krb: torch.Tensor, coff, block: int = 8192,
+                          what: str = "") -> np.ndarray:
+    """The oracle's score of every document for every query, [B, N] float64.
+
+    Each group of whole documents is scored by the unchanged oracle (``doc_scores_one``
+    on its rows, from an exact float64 copy of the bank), so the result equals one call
+    of ``route_doc_scores`` on the whole bank.  The groups run on host threads: NumPy
+    leaves the interpreter lock while it evaluates the oracle's products.  Prints its
+    progress, since a 100M-token bank takes tens of seconds."""
+    q_off = np.asarray(q_off, dtype=np.int64)
+    coff = np.asarray(coff, dtype=np.int64)
+    B, N = len(q_off) - 1, len(coff) - 1
+    Kh = Krb.detach().cpu()
+    Qs = [f64(Qr[int(q_off[b]):int(q_off[b + 1])]) for b in range(B)]
+    groups = doc_groups(coff, block)
+    out = np.empty((B, N), dtype=np.float64)
+
+    def work(g):
+        d0, d1 = g
+        sub = Kh[int(coff[d0]):int(coff[d1])].float().double().numpy()
+        loc = coff[d0:d1 + 1] - coff[d0]
+        for b in range(B):
+            out[b, d0:d1] = O.doc_scores_one(Qs[b], sub, loc)
+        return d1 - d0
+
+    t0 = time.time()
+    nthr = host_threads()
+    done, next_mark = 0, 0.1
+    with concurrent.futures.ThreadPoolExecutor(nthr) as ex:
+        for n in ex.map(work, groups):
+            done += n
+            if done >= next_mark * N:
+                say(f"  oracle scores {what}: {done}/{N} documents, {time.time() - t0:.1f} s, {nthr} threads")
+                next_mark += 0.1
+    return out

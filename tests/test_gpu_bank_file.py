@@ -1,14 +1,19 @@
 """A bank kept on disk and grown by appending documents: pool part of a corpus on the GPU,
 save it, load it into device and pinned host memory, pool the remaining documents after
 its rows, save and load again.  The result must equal, bit for bit, the bank pooled from
-the whole corpus in one call, and route and attend the same."""
+the whole corpus in one call, and route and attend the same.  The reloaded bank is also
+checked against the oracle: its rows against the oracle's pooling of documents on both
+sides of the cut, and routing and attention on it (content rows read from pinned host
+memory) against the oracle's."""
 import numpy as np
 import pytest
 import torch
 
 import latent_memory_long_amd as M
+from oracle import msa_oracle as O
 from synth import workloads as W
-from tests.helpers import say
+from tests.helpers import (assert_attn_close, assert_pool_close, assert_scores_close, assert_topk_consistent,
+                           assert_topk_valid, f64, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -83,3 +88,28 @@ def test_saved_bank_grows_by_appending(tmp_path):
         o_b = M.msa_sparse_attn(q["Q"], q["Kloc"], q["Vloc"], q_off, q_off, 24, ids_b, coff_d, lKb, lVb)
         torch.cuda.synchronize()
         assert torch.equal(o_a, o_b)
+    # the reloaded, grown bank against the oracle
+    sh = wl.shape
+    for l, ((K, V, Kr), (lKrb, lKb, lVb)) in enumerate(zip(states, final)):
+        for d in (0, cut - 2, cut - 1, cut, cut + 1, len(lens) - 1):
+            t0, t1 = int(off[d]), int(off[d + 1])
+            c0, c1 = int(coff[d]), int(coff[d + 1])
+            oK, oV, oKr, _ = O.pool(f64(K[t0:t1]), f64(V[t0:t1]), f64(Kr[t0:t1]), [0, t1 - t0], sh.chunk,
+                                    sh.rope_base, O.ROPE_K)
+            rms = max(1.0, float(np.sqrt(np.mean(f64(K[t0:t1]) ** 2))))
+            for g, o, n in ((lKb[c0:c1], oK, "Kbar"), (lVb[c0:c1], oV, "Vbar"), (lKrb[c0:c1], oKr, "Krbar")):
+                assert_pool_close(g, o, "bf16", f"layer {l} doc {d} {n} (side {'A' if d < cut else 'B'})",
+                                  input_rms=rms)
+        ids, sc, ds = M.msa_route_topk(q["Qr"], q_off, 24, lKrb, coff_d, 8, want_doc_scores=True)
+        out = M.msa_sparse_attn(q["Q"], q["Kloc"], q["Vloc"], q_off, q_off, 24, ids, coff_d, lKb, lVb,
+                                rope_base=sh.rope_base)
+        torch.cuda.synchronize()
+        ids_h, ds_h = ids.cpu().numpy(), ds.cpu().numpy()
+        o_ds = O.route_doc_scores(f64(q["Qr"]), [0, 24], f64(lKrb), coff)[0]
+        assert_scores_close(ds_h[0], o_ds, "bf16", f"layer {l} reloaded bank scores")
+        assert_topk_consistent(ids_h[0], sc.cpu().numpy()[0], ds_h[0], 8, f"layer {l} reloaded bank top-k")
+        assert_topk_valid(ids_h[0], o_ds, 8, f"layer {l} reloaded bank top-k vs the oracle")
+        ref = O.sparse_attn(f64(q["Q"]), f64(q["Kloc"]), f64(q["Vloc"]), [0, 24], [0, 24], ids_h, coff,
+                            f64(lKb), f64(lVb), sh.rope_base)
+        err = assert_attn_close(out, ref, "bf16", f"layer {l} attention on the reloaded pinned-host bank")
+        say(f"  layer {l}: reloaded bank matches the oracle (attention max abs err {err:.3g})")

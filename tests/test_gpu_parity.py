@@ -11,7 +11,7 @@ import latent_memory_long_amd as M
 from oracle import msa_oracle as O
 from synth import workloads as W
 from tests.helpers import (assert_attn_close, assert_pool_close, assert_scores_close,
-                           assert_topk_consistent, assert_topk_valid, f64, say)
+                           assert_topk_consistent, assert_topk_valid, f64, oracle_doc_scores_all, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -320,6 +320,81 @@ def test_route_batch_kernel_edges(heads, n_rows):
             assert np.all(np.isneginf(ds[b]))
         else:
             assert_scores_close(ds[b], o[b], "bf16", f"rows {n_rows} query {b}")
+
+
+def _scan_parts(coff, parts):
+    """Host copy of the streaming scan's document-aligned split: part p starts at the first
+    document whose first row is at or after p * C / P."""
+    C = int(coff[-1])
+    starts = [int(np.searchsorted(coff, C * p // parts, side="left")) for p in range(parts)] + [len(coff) - 1]
+    return [(starts[p], starts[p + 1]) for p in range(parts)]
+
+
+WIN_ROWS = 4096   # rows of one LDS score window of the streaming MFMA scan
+
+
+@pytest.mark.parametrize("h_r", [1, 2])
+@pytest.mark.parametrize("with_rows", [False, True], ids=["scores", "rows"])
+def test_route_scan_window_carry(h_r, with_rows):
+    # A bank of 1.1M rows: each of the scan's 256 parts holds more than one 4,096-row score
+    # window, so documents cross window boundaries and their running maximum is carried
+    # from one window to the next.  One document of 9,000 rows spans three windows.
+    say(f"case route scan window carry h_r={h_r} rows={with_rows}")
+    _route_env("mfma")
+    rng = np.random.default_rng(300 + h_r)
+    counts = rng.integers(1, 48, size=46_000)
+    counts[[100, 20_000, 30_000, 45_000]] = [9000, 8193, 4097, 4096]
+    counts[-1] += max(0, 1_100_000 - int(counts.sum()))
+    coff, Krb = random_bank(counts, h_r, 32, "bf16", 310 + h_r)
+    C = int(coff[-1])
+    # the launch takes 256 parts here: check on the host that the carry is reached
+    parts = _scan_parts(coff, 256)
+    crossing, three = 0, 0
+    for d0, d1 in parts:
+        base = int(coff[d0])
+        w_first = (coff[d0:d1] - base) // WIN_ROWS
+        w_last = (coff[d0 + 1:d1 + 1] - 1 - base) // WIN_ROWS
+        crossing += int(np.sum(w_last > w_first))
+        three += int(np.sum(w_last - w_first >= 2))
+    assert crossing >= 200 and three >= 1, (crossing, three)
+    say(f"  {len(counts)} docs, {C} rows; {crossing} documents cross a window, {three} span three")
+    q_lens = [64, 5]
+    Qr = (_cpu_randn((sum(q_lens), h_r, 32), 320) + _cpu_randn((1, h_r, 32), 321, 0.5)).to(torch.bfloat16)
+    q_off = np.concatenate([[0], np.cumsum(q_lens)])
+    q_off_d = torch.tensor(q_off, dtype=torch.int32, device=DEV)
+    coff_d = torch.tensor(coff, device=DEV)
+    rows = None
+    if with_rows:
+        rows = (torch.empty((2, C), dtype=torch.float32, device=DEV), torch.empty((2, C), dtype=torch.int32, device=DEV))
+    # one call per query (a single query keeps the plain part order), then both together
+    per_q = []
+    for b in range(2):
+        one = torch.tensor([0, q_lens[b]], dtype=torch.int32, device=DEV)
+        per_q.append(M.msa_route_scan(Qr[q_off[b]:q_off[b + 1]].to(DEV), one, q_lens[b], Krb, coff_d).cpu().numpy()[0])
+    Qr_d = Qr.to(DEV)
+    ds = M.msa_route_scan(Qr_d, q_off_d, max(q_lens), Krb, coff_d, rows=rows)
+    ids, sc = M.msa_topk(ds, 16)
+    torch.cuda.synchronize()
+    ds, ids, sc = ds.cpu().numpy(), ids.cpu().numpy(), sc.cpu().numpy()
+    o = oracle_doc_scores_all(Qr, q_off, Krb, coff, block=65536, what="window carry")
+    for b in range(2):
+        assert_scores_close(per_q[b], o[b], "bf16", f"query {b} alone, every document")
+        assert_scores_close(ds[b], o[b], "bf16", f"query {b} batched, every document")
+        assert_topk_consistent(ids[b], sc[b], ds[b], 16, f"query {b}")
+        assert_topk_valid(ids[b], o[b], 16, f"query {b}")
+    if with_rows:
+        rs, ra = rows[0].cpu().numpy(), rows[1].cpu().numpy()
+        big = [int(x) for x in np.nonzero(counts >= 4096)[0]]
+        for b in range(2):
+            Qb = f64(Qr[q_off[b]:q_off[b + 1]])
+            for d in big:
+                r0, r1 = int(coff[d]), int(coff[d + 1])
+                o_rows = O.token_chunk_scores(Qb, f64(Krb[r0:r1]))          # [Lq, rows]
+                assert_scores_close(rs[b, r0:r1], o_rows.max(axis=0), "bf16", f"query {b} doc {d} row scores")
+                # the recorded token reaches its row's maximum within twice the score bar
+                got = o_rows[ra[b, r0:r1], np.arange(r1 - r0)]
+                best = o_rows.max(axis=0)
+                assert np.all(best - got <= 2 * 2e-3 * np.maximum(np.abs(best), 1e-3)), f"query {b} doc {d} row tokens"
 
 
 def test_topk_ties_and_small_banks():
