@@ -71,8 +71,9 @@ def make_bank(wl, dev):
     coff = M.msa_chunk_offsets(off, wl.shape.chunk)
     kv_dev = "cpu-pinned" if wl.kv_source == "host" else dev
     log(f"bank: {len(lens)} documents, {int(coff[-1])} rows, content K/V on {kv_dev}")
-    Krb, Kb, Vb = W.gen_pooled_bank(wl, coff, dev, kv_device=kv_dev)
-    return lens, off, coff, Krb, Kb, Vb
+    Krb_rows, Kb, Vb = W.gen_pooled_bank(wl, coff, dev, kv_device=kv_dev)
+    Krb = M.RouteKeys.from_rows(Krb_rows)   # the routing keys in the library's bank layout
+    return lens, off, coff, Krb, Krb_rows, Kb, Vb
 
 
 def make_queries(wl, dev, n):
@@ -97,7 +98,7 @@ def time_pool(dev, reps=3):
     coff_d = torch.tensor(coff, device=dev)
     outs = (torch.empty((C, sh.h_kv, sh.d), dtype=torch.bfloat16, device=dev),
             torch.empty((C, sh.h_kv, sh.d), dtype=torch.bfloat16, device=dev),
-            torch.empty((C, sh.h_r, sh.d), dtype=torch.bfloat16, device=dev))
+            M.RouteKeys.empty(C, sh.h_r, sh.d, torch.bfloat16, dev))
     M.msa_pool(K, V, Kr, off_d, coff_d, C, sh.chunk, sh.rope_base, out=outs)
     torch.cuda.synchronize()
     ms = []
@@ -242,7 +243,11 @@ def time_layers(dev, reps=20):
     coff = M.msa_chunk_offsets(W.token_offsets(lens), sh.chunk)
     N, C, L, k = len(lens), int(coff[-1]), wl.n_layers, wl.k
     lq = 64
-    banks = [W.gen_pooled_bank(W.layer(wl, l), coff, dev) for l in range(L)]
+    banks = []
+    for l in range(L):
+        Krb, Kb, Vb = W.gen_pooled_bank(W.layer(wl, l), coff, dev)
+        banks.append((M.RouteKeys.from_rows(Krb), Kb, Vb))
+        del Krb
     qs = [W.gen_queries(W.layer(wl, l), dev, lq_override=[lq]) for l in range(L)]
     q_off = torch.tensor([0, lq], dtype=torch.int32, device=dev)
     coff_d = torch.tensor(coff, device=dev)
@@ -313,6 +318,7 @@ def time_banks(dev, reps=50):
         coff = M.msa_chunk_offsets(off, sh.chunk)
         N, C, T = len(lens), int(coff[-1]), int(off[-1])
         Krb, Kb, Vb = W.gen_pooled_bank(wl, coff, dev)
+        Krb = M.RouteKeys.from_rows(Krb)
         coff_d = torch.tensor(coff, device=dev)
         q = W.gen_queries(wl, dev)
         Lq = int(q["q_len"][0])
@@ -451,7 +457,7 @@ def main():
     torch.cuda.set_device(0)
     wl = W.workload(args.workload)
     sh = wl.shape
-    lens, off, coff, Krb, Kb, Vb = make_bank(wl, dev)
+    lens, off, coff, Krb, Krb_rows, Kb, Vb = make_bank(wl, dev)
     N, C = len(lens), int(coff[-1])
     T = int(off[-1])
     coff_d = torch.tensor(coff, device=dev)
@@ -615,7 +621,7 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         q0 = W.gen_queries(replace(wl, seed=wl.seed + 1), dev)
-        cpu = cpu_baseline(wl, lens, off, coff, Krb, Kb, Vb, q0, args.cpu_seconds)
+        cpu = cpu_baseline(wl, lens, off, coff, Krb_rows, Kb, Vb, q0, args.cpu_seconds)
 
     value = T / (ms_per_step / 1e3)
     line = {

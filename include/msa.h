@@ -65,6 +65,38 @@ typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
  * K only (keys carry positions; V and the routing keys Kr are left as they are). */
 enum { MSA_ROPE_K = 1u, MSA_ROPE_V = 2u, MSA_ROPE_KR = 4u };
 
+/*
+ * Routing-key bank layout (hysenlabs.com "The 100M-token setup depends on host memory as
+ * well as two GPUs": the routing keys stay resident in GPU memory and every query scores
+ * all of them, so they are stored the way the scan reads them).  Every Krbar argument of
+ * this library uses this layout:
+ *  - MSA_BF16: rows in tiles of 16.  Tile T holds bank rows 16T..16T+15 as h_r * (d/32)
+ *    blocks of 512 elements, in (head h, 32-dimension slice s) order.  In block (h, s),
+ *    element (row 16T + r, head h, dim 32s + 8g + j), r < 16, g < 4, j < 8, sits at
+ *    position (16g + r) * 8 + j: each block is the B operand of a 16x16x32 matrix-core
+ *    product, one contiguous 1 KB load.  A bank of C rows occupies ceil(C/16) whole tiles;
+ *    the rows past C in the last tile are padding: they are read but no result depends on
+ *    their contents (msa_krbar_pack writes them as zero, msa_pool leaves them alone).
+ *  - MSA_F32: row-major [C, h_r, d].
+ * The gradient dKrbar of msa_route_backward is float32 row-major [C, h_r, d] in every case.
+ */
+
+/* Elements of Krbar storage for a bank of n_chunks rows: 16 * ceil(n_chunks/16) * h_r * d
+ * for MSA_BF16, n_chunks * h_r * d for MSA_F32; -1 on a bad argument (d in {32, 64, 128},
+ * h_r in [1, 64], n_chunks >= 0). */
+int64_t msa_krbar_elems(msa_dtype dtype, int64_t n_chunks, int32_t h_r, int32_t d);
+
+/* Row-major routing keys `rows` [n_chunks, h_r, d] (device) -> the bank layout `Krbar`
+ * (device, msa_krbar_elems() elements, padding rows written as zero).  The buffers must not
+ * overlap.  Asynchronous on `stream`. */
+msa_status msa_krbar_pack(msa_dtype dtype, int64_t n_chunks, int32_t h_r, int32_t d,
+                          const void* rows, void* Krbar, msa_stream_t stream);
+
+/* The bank layout `Krbar` -> row-major `rows` [n_chunks, h_r, d] (both device, not
+ * overlapping).  Asynchronous on `stream`. */
+msa_status msa_krbar_unpack(msa_dtype dtype, int64_t n_chunks, int32_t h_r, int32_t d,
+                            const void* Krbar, void* rows, msa_stream_t stream);
+
 /* Library version, major*10000 + minor*100 + patch. */
 int32_t msa_version(void);
 
@@ -93,14 +125,20 @@ int64_t msa_chunk_offsets(const int64_t* doc_tok_off, int32_t n_docs, int32_t ch
  * section 三: mean pooling per chunk; hysenlabs.com "Document-wise RoPE resets every
  * document to position zero").
  *   K, V       [n_tokens, h_kv, d]; Kr [n_tokens, h_r, d]; documents concatenated.
- *   doc_tok_off, chunk_off   device [n_docs+1] (chunk_off as from msa_chunk_offsets).
+ *   doc_tok_off device [n_docs+1], starting at 0.
+ *   chunk_off  device [n_docs+1]: document d's first bank row, with the row counts of
+ *              msa_chunk_offsets.  It may start past row 0: the documents are then written
+ *              after the rows a bank already holds (a bank grown by appending documents
+ *              holds the same bits as one pooled at once).
+ *   n_chunks   rows written, chunk_off[n_docs] - chunk_off[0].
  *   rope_mask  MSA_ROPE_* bits: tensors rotated at their in-document position p
  *              (restarting at 0 per document), angle p * rope_base^(-2i/d) on the pair
  *              (i, i + d/2).
- *   Kbar, Vbar [n_chunks, h_kv, d]; Krbar [n_chunks, h_r, d] outputs.  Row
- *              chunk_off[doc] + j is the mean of tokens [j*chunk, min((j+1)*chunk, L)) of
- *              the document, after rotation; means are accumulated in float32 and
- *              rounded once to dtype.
+ *   Kbar, Vbar [rows, h_kv, d] row-major; Krbar in the routing-key bank layout (above),
+ *              outputs holding at least chunk_off[n_docs] rows.  Row chunk_off[doc] + j is
+ *              the mean of tokens [j*chunk, min((j+1)*chunk, L)) of the document, after
+ *              rotation; means are accumulated in float32 and rounded once to dtype.  Only
+ *              rows chunk_off[0] .. chunk_off[n_docs] - 1 are written.
  *   Supported: d in {32, 64, 128}; 1 <= chunk <= 128; h_kv, h_r in [1, 64].
  */
 msa_status msa_pool(msa_dtype dtype, int32_t n_docs, int64_t n_tokens, int64_t n_chunks,
@@ -158,7 +196,8 @@ size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
  *   q_off      device int32 [n_queries+1].
  *   max_q_len  host-side upper bound of every query's length; it picks the kernel tile
  *              (rows are still read from q_off, so a loose bound is only slower).
- *   Krbar      [n_chunks, h_r, d]; chunk_off device [n_docs+1].
+ *   Krbar      n_chunks rows of h_r heads, in the routing-key bank layout (above);
+ *              chunk_off device [n_docs+1], starting at 0.
  *   Scores: s(t,c) = (1/h_r) sum_h cos(Qr[t,h], Krbar[c,h]) (cos = 0 if a norm is 0),
  *           chunk score = max_t s(t,c), document score = max over its rows.
  *   topk_ids   device int32 [n_queries, k]: the min(k, n_docs) best documents by (score
@@ -167,8 +206,8 @@ size_t msa_route_topk_workspace(int32_t n_queries, int32_t n_docs, int32_t k);
  *   doc_scores device float [n_queries, n_docs] or NULL: every document's score; when
  *              NULL the scores are kept in `workspace` instead.
  *   Supported: d in {32, 64, 128}; h_r in [1, 16]; 1 <= k <= 1024.  bf16 inputs with
- *   h_r <= 8 run on MFMA tiles (exact bf16 products, float32 sums); other bf16 inputs sum
- *   in float32 and float32 inputs in double.
+ *   h_r <= 8 run on matrix-core tiles (exact bf16 products, float32 sums); other bf16
+ *   inputs sum in float32 and float32 inputs in double.
  */
 msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                           const int32_t* q_off, int32_t max_q_len, const void* Qr,
@@ -191,7 +230,8 @@ size_t msa_route_backward_workspace(int32_t n_queries, int32_t n_docs, int64_t n
  *   row_scores, row_arg  optional (both or neither): msa_route_scan's row outputs for the
  *              same arguments; NULL runs that scan again (into the workspace).
  *   dQr        device float [total_q, h_r, d], overwritten: dL/dQr.
- *   dKrbar     device float [n_chunks, h_r, d], ADDED TO (the caller zeroes it once).
+ *   dKrbar     device float [n_chunks, h_r, d] row-major, ADDED TO (the caller zeroes it
+ *              once).
  *   A document score is one maximum, so its gradient reaches one (token, row) pair: the
  *   first row of the document (in bank order) with the largest row score, then the first
  *   token (in query order) with the largest score on that row.  For that pair and each
@@ -258,7 +298,8 @@ typedef struct {
 
 /* Writes a bank: doc_tok_off / chunk_off [n_docs+1] (chunk_off must follow the chunking
  * rule of msa_chunk_offsets for info->chunk), and for layer l the arrays Krbar[l]
- * [C, h_r, d], Kbar[l] and Vbar[l] [C, h_kv, d] of info->dtype.  Overwrites `path`. */
+ * (msa_krbar_elems() elements in the routing-key bank layout), Kbar[l] and Vbar[l]
+ * [C, h_kv, d] of info->dtype.  Overwrites `path`. */
 msa_status msa_bank_save(const char* path, const msa_bank_info* info, const int64_t* doc_tok_off,
                          const int64_t* chunk_off, const void* const* Krbar,
                          const void* const* Kbar, const void* const* Vbar);

@@ -49,6 +49,9 @@ def _load() -> ctypes.CDLL:
         "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "msa_last_error": (ctypes.c_char_p, []),
         "msa_chunk_offsets": (I64, [P, I32, I32, P]),
+        "msa_krbar_elems": (I64, [ctypes.c_int, I64, I32, I32]),
+        "msa_krbar_pack": (ctypes.c_int, [ctypes.c_int, I64, I32, I32, P, P, P]),
+        "msa_krbar_unpack": (ctypes.c_int, [ctypes.c_int, I64, I32, I32, P, P, P]),
         "msa_pool": (ctypes.c_int, [ctypes.c_int, I32, I64, I64, P, P, I32, I32, I32, I32, F, U32,
                                     P, P, P, P, P, P, P]),
         "msa_route_scan": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
@@ -161,6 +164,139 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+# ----------------------------------------------------------------------------- routing keys
+
+class RouteKeys:
+    """The routing keys Kr-bar of a bank (n_chunks rows of h_r heads of dim d), in the
+    library's bank layout (include/msa.h, "Routing-key bank layout"): bf16 keys in tiles of
+    16 rows laid out as matrix-core operands, float32 keys row-major.  ``data`` is a flat
+    tensor of msa_krbar_elems() elements; it is not indexable by row -- ``rows()`` returns
+    the keys as a row-major [n_chunks, h_r, d] tensor, ``from_rows()`` builds the layout
+    from one."""
+
+    __slots__ = ("data", "n_chunks", "h_r", "d")
+
+    def __init__(self, data: torch.Tensor, n_chunks: int, h_r: int, d: int):
+        n_chunks, h_r, d = int(n_chunks), int(h_r), int(d)
+        _need(data, "RouteKeys data", _FLOAT)
+        _need(data, "RouteKeys data", _FLOAT, (msa_krbar_elems(_dtype_code(data), n_chunks, h_r, d),))
+        self.data, self.n_chunks, self.h_r, self.d = data, n_chunks, h_r, d
+
+    @property
+    def dtype(self):
+        return self.data.dtype
+
+    @property
+    def device(self):
+        return self.data.device
+
+    @property
+    def is_cuda(self):
+        return self.data.is_cuda
+
+    @property
+    def shape(self):
+        """The logical shape (n_chunks, h_r, d)."""
+        return (self.n_chunks, self.h_r, self.d)
+
+    @staticmethod
+    def empty(n_chunks: int, h_r: int, d: int, dtype=torch.bfloat16, device="cuda", pin_memory: bool = False,
+              zero: bool = False):
+        """Storage for n_chunks rows; ``zero`` fills it with zeros (padding rows included, so
+        banks pooled into it compare equal bit for bit)."""
+        n = msa_krbar_elems(_dtype_code_of(dtype), n_chunks, h_r, d)
+        make = torch.zeros if zero else torch.empty
+        if pin_memory:
+            return RouteKeys(make(n, dtype=dtype, pin_memory=True), n_chunks, h_r, d)
+        return RouteKeys(make(n, dtype=dtype, device=device), n_chunks, h_r, d)
+
+    @staticmethod
+    def from_rows(rows: torch.Tensor, stream=None) -> "RouteKeys":
+        """Routing keys from a row-major [n_chunks, h_r, d] device tensor (msa_krbar_pack)."""
+        _need(rows, "rows", _FLOAT, (None, None, None))
+        _same_device(("rows", rows))
+        C, h_r, d = rows.shape
+        keys = RouteKeys.empty(C, h_r, d, rows.dtype, rows.device)
+        msa_krbar_pack(rows, keys, stream)
+        return keys
+
+    def rows(self, stream=None) -> torch.Tensor:
+        """The keys as a new row-major [n_chunks, h_r, d] tensor on the same device
+        (msa_krbar_unpack)."""
+        out = torch.empty(self.shape, dtype=self.dtype, device=self.device)
+        msa_krbar_unpack(self, out, stream)
+        return out
+
+    def to(self, device, non_blocking: bool = False) -> "RouteKeys":
+        return RouteKeys(self.data.to(device, non_blocking=non_blocking), self.n_chunks, self.h_r, self.d)
+
+    def cpu(self) -> "RouteKeys":
+        return self.to("cpu")
+
+    def clone(self) -> "RouteKeys":
+        return RouteKeys(self.data.clone(), self.n_chunks, self.h_r, self.d)
+
+    def grown(self, n_chunks: int) -> "RouteKeys":
+        """A copy with room for n_chunks >= self.n_chunks rows: the existing rows keep their
+        place, so msa_pool can write new documents after them (offsets starting at the old
+        row count)."""
+        if n_chunks < self.n_chunks:
+            raise MsaError(MSA_ERR_INVALID_ARG, f"cannot shrink routing keys from {self.n_chunks} to {n_chunks} rows")
+        out = RouteKeys.empty(n_chunks, self.h_r, self.d, self.dtype, self.device, zero=True)
+        out.data[: self.data.numel()].copy_(self.data)
+        return out
+
+    def equal(self, other: "RouteKeys") -> bool:
+        return (isinstance(other, RouteKeys) and self.shape == other.shape and self.dtype == other.dtype
+                and torch.equal(self.data, other.data))
+
+    def __repr__(self):
+        return f"RouteKeys(n_chunks={self.n_chunks}, h_r={self.h_r}, d={self.d}, dtype={self.dtype}, device={self.device})"
+
+
+def _dtype_code_of(dtype) -> int:
+    if dtype == torch.float32:
+        return MSA_F32
+    if dtype == torch.bfloat16:
+        return MSA_BF16
+    raise MsaError(MSA_ERR_UNSUPPORTED, f"dtype {dtype} (need float32 or bfloat16)")
+
+
+def _keys(K, name: str = "Krbar") -> RouteKeys:
+    """Routing keys as a RouteKeys: float32 keys may also be a row-major [C, h_r, d] tensor."""
+    if isinstance(K, RouteKeys):
+        return K
+    if isinstance(K, torch.Tensor) and K.dtype == torch.float32 and K.dim() == 3 and K.is_contiguous():
+        return RouteKeys(K.view(-1), K.shape[0], K.shape[1], K.shape[2])
+    raise MsaError(MSA_ERR_INVALID_ARG, f"{name} must be a RouteKeys (bf16 keys are stored in the tiled bank "
+                                        f"layout; RouteKeys.from_rows packs row-major keys), or for float32 a "
+                                        f"[C, h_r, d] tensor")
+
+
+def msa_krbar_elems(dtype: int, n_chunks: int, h_r: int, d: int) -> int:
+    """Elements of routing-key storage for a bank of n_chunks rows."""
+    n = int(lib.msa_krbar_elems(dtype, n_chunks, h_r, d))
+    if n < 0:
+        raise MsaError(MSA_ERR_INVALID_ARG, msa_last_error())
+    return n
+
+
+def msa_krbar_pack(rows: torch.Tensor, keys: RouteKeys, stream=None):
+    """Row-major [n_chunks, h_r, d] -> the bank layout (padding rows written as zero)."""
+    _need(rows, "rows", keys.dtype, keys.shape)
+    _same_device(("rows", rows), ("keys", keys.data))
+    _check(lib.msa_krbar_pack(_dtype_code(rows), keys.n_chunks, keys.h_r, keys.d, _ptr(rows), _ptr(keys.data),
+                              _stream(stream)))
+
+
+def msa_krbar_unpack(keys: RouteKeys, rows: torch.Tensor, stream=None):
+    """The bank layout -> row-major [n_chunks, h_r, d]."""
+    _need(rows, "rows", keys.dtype, keys.shape)
+    _same_device(("rows", rows), ("keys", keys.data))
+    _check(lib.msa_krbar_unpack(_dtype_code(rows), keys.n_chunks, keys.h_r, keys.d, _ptr(keys.data), _ptr(rows),
+                                _stream(stream)))
+
+
 # ----------------------------------------------------------------------------- entry points
 
 def msa_version() -> int:
@@ -189,8 +325,11 @@ def msa_chunk_offsets(doc_tok_off, chunk: int = 64) -> np.ndarray:
 def msa_pool(K: torch.Tensor, V: torch.Tensor, Kr: torch.Tensor, doc_tok_off: torch.Tensor,
              chunk_off: torch.Tensor, n_chunks: int, chunk: int = 64, rope_base: float = 1e6,
              rope_mask: int = MSA_ROPE_K, out=None, stream=None):
-    """Step A.  K, V [T, h_kv, d]; Kr [T, h_r, d]; offsets int64 on the device.
-    Returns (Kbar, Vbar, Krbar) [n_chunks, h, d]."""
+    """Step A.  K, V [T, h_kv, d]; Kr [T, h_r, d]; offsets int64 on the device; n_chunks the
+    rows written.  Returns (Kbar, Vbar [rows, h_kv, d], Krbar RouteKeys).  chunk_off gives
+    each document's first bank row: to grow a bank, pass it as ``out`` (its K-bar / V-bar
+    and RouteKeys sized for the grown bank, e.g. RouteKeys.grown) with offsets that start
+    at the rows it already holds."""
     _need(K, "K", _FLOAT, (None, None, None))
     T, h_kv, d = K.shape
     _need(V, "V", K.dtype, (T, h_kv, d))
@@ -201,16 +340,19 @@ def msa_pool(K: torch.Tensor, V: torch.Tensor, Kr: torch.Tensor, doc_tok_off: to
     if out is None:
         out = (torch.empty((n_chunks, h_kv, d), dtype=K.dtype, device=K.device),
                torch.empty((n_chunks, h_kv, d), dtype=K.dtype, device=K.device),
-               torch.empty((n_chunks, h_r, d), dtype=K.dtype, device=K.device))
+               RouteKeys.empty(n_chunks, h_r, d, K.dtype, K.device, zero=True))
     Kb, Vb, Krb = out
-    _need(Kb, "Kbar", K.dtype, (n_chunks, h_kv, d))
-    _need(Vb, "Vbar", K.dtype, (n_chunks, h_kv, d))
-    _need(Krb, "Krbar", K.dtype, (n_chunks, h_r, d))
+    Krb = _keys(Krb)
+    _need(Kb, "Kbar", K.dtype, (None, h_kv, d))
+    _need(Vb, "Vbar", K.dtype, (Kb.shape[0], h_kv, d))
+    if Krb.dtype != K.dtype or Krb.h_r != h_r or Krb.d != d or Krb.n_chunks != Kb.shape[0] or Kb.shape[0] < n_chunks:
+        raise MsaError(MSA_ERR_INVALID_ARG, f"bank buffers hold {Kb.shape[0]} K-bar rows and {Krb} for {n_chunks} "
+                                            f"rows of h_r={h_r}, d={d}, {K.dtype}")
     _same_device(("K", K), ("V", V), ("Kr", Kr), ("doc_tok_off", doc_tok_off), ("chunk_off", chunk_off),
-                 ("Kbar", Kb), ("Vbar", Vb), ("Krbar", Krb))
+                 ("Kbar", Kb), ("Vbar", Vb), ("Krbar", Krb.data))
     _check(lib.msa_pool(_dtype_code(K), doc_tok_off.numel() - 1, T, n_chunks, _ptr(doc_tok_off),
                         _ptr(chunk_off), h_kv, h_r, d, chunk, rope_base, rope_mask, _ptr(K), _ptr(V),
-                        _ptr(Kr), _ptr(Kb), _ptr(Vb), _ptr(Krb), _stream(stream)))
+                        _ptr(Kr), _ptr(Kb), _ptr(Vb), _ptr(Krb.data), _stream(stream)))
     return Kb, Vb, Krb
 
 
@@ -220,28 +362,28 @@ def msa_route_scan(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar:
     """Step B.  Returns every document's score, float32 [B, N].  For training pass `rows` =
     (float32 [B, C], int32 [B, C]) device tensors to also get each bank row's best token
     score and the first token reaching it, which msa_route_backward can reuse."""
+    Krbar = _keys(Krbar)
     B, N = _route_inputs(Qr, q_off, Krbar, chunk_off)
     if out is None:
         out = torch.empty((B, N), dtype=torch.float32, device=Krbar.device)
     _need(out, "doc_scores", torch.float32, (B, N))
     _route_devices(Qr, q_off, Krbar, chunk_off, ("doc_scores", out))
-    _check(lib.msa_route_scan(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
-                              Krbar.shape[1], Krbar.shape[2], N, Krbar.shape[0], _ptr(chunk_off),
-                              _ptr(Krbar), _ptr(out), *_rows(rows, B, Krbar.shape[0]), _stream(stream)))
+    _check(lib.msa_route_scan(_dtype_code(Krbar.data), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
+                              Krbar.h_r, Krbar.d, N, Krbar.n_chunks, _ptr(chunk_off),
+                              _ptr(Krbar.data), _ptr(out), *_rows(rows, B, Krbar.n_chunks), _stream(stream)))
     return out
 
 
-def _route_inputs(Qr, q_off, Krbar, chunk_off):
+def _route_inputs(Qr, q_off, Krbar: RouteKeys, chunk_off):
     """Checks of the router's inputs; returns (queries, documents)."""
-    _need(Krbar, "Krbar", _FLOAT, (None, None, None))
-    _need(Qr, "Qr", Krbar.dtype, (None, Krbar.shape[1], Krbar.shape[2]))
+    _need(Qr, "Qr", Krbar.dtype, (None, Krbar.h_r, Krbar.d))
     _need(q_off, "q_off", torch.int32, (None,))
     _need(chunk_off, "chunk_off", torch.int64, (None,))
     return q_off.numel() - 1, chunk_off.numel() - 1
 
 
-def _route_devices(Qr, q_off, Krbar, chunk_off, *outputs):
-    _same_device(("Krbar", Krbar), ("Qr", Qr), ("q_off", q_off), ("chunk_off", chunk_off), *outputs)
+def _route_devices(Qr, q_off, Krbar: RouteKeys, chunk_off, *outputs):
+    _same_device(("Krbar", Krbar.data), ("Qr", Qr), ("q_off", q_off), ("chunk_off", chunk_off), *outputs)
 
 
 def _rows(rows: Optional[tuple], B: int, C: int):
@@ -285,8 +427,9 @@ def msa_route_topk_workspace(n_queries: int, n_docs: int, k: int) -> int:
 def msa_route_topk(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar: torch.Tensor,
                    chunk_off: torch.Tensor, k: int, want_doc_scores: bool = False, out=None,
                    workspace: Optional[torch.Tensor] = None, stream=None):
-    """Steps B + C.  Qr [total_q, h_r, d]; q_off int32 [B+1]; Krbar [C, h_r, d].
+    """Steps B + C.  Qr [total_q, h_r, d]; q_off int32 [B+1]; Krbar the bank's RouteKeys.
     Returns (topk_ids int32 [B,k], topk_scores f32 [B,k], doc_scores f32 [B,N] or None)."""
+    Krbar = _keys(Krbar)
     B, N = _route_inputs(Qr, q_off, Krbar, chunk_off)
     dev = Krbar.device
     if out is None:
@@ -304,9 +447,9 @@ def msa_route_topk(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar:
     if need:
         ws = _workspace(need, dev, workspace)
         wsb = ws.numel() * ws.element_size()
-    _check(lib.msa_route_topk(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
-                              Krbar.shape[1], Krbar.shape[2], N, Krbar.shape[0], _ptr(chunk_off),
-                              _ptr(Krbar), k, _ptr(ids), _ptr(sc), _ptr(ds), _ptr(ws), wsb,
+    _check(lib.msa_route_topk(_dtype_code(Krbar.data), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
+                              Krbar.h_r, Krbar.d, N, Krbar.n_chunks, _ptr(chunk_off),
+                              _ptr(Krbar.data), k, _ptr(ids), _ptr(sc), _ptr(ds), _ptr(ws), wsb,
                               _stream(stream)))
     return ids, sc, ds
 
@@ -447,6 +590,7 @@ def msa_route_backward(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Kr
     device.  Returns (dQr, dKrbar), float32; dKrbar is added to (pass your own array to
     accumulate, else a zero-filled one is made).  `rows`: msa_route_scan's row outputs for
     the same inputs, which saves scanning the bank again."""
+    Krbar = _keys(Krbar)
     B, N = _route_inputs(Qr, q_off, Krbar, chunk_off)
     C, h_r, d = Krbar.shape
     dev = Krbar.device
@@ -460,8 +604,8 @@ def msa_route_backward(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Kr
     _route_devices(Qr, q_off, Krbar, chunk_off, ("dD", dD), ("dQr", out), ("dKrbar", dKrbar))
     need = msa_route_backward_workspace(B, N, C, h_r)
     ws = _workspace(need, dev, workspace)
-    _check(lib.msa_route_backward(_dtype_code(Krbar), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr), h_r,
-                                  d, N, C, _ptr(chunk_off), _ptr(Krbar), _ptr(dD), *_rows(rows, B, C),
+    _check(lib.msa_route_backward(_dtype_code(Krbar.data), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr), h_r,
+                                  d, N, C, _ptr(chunk_off), _ptr(Krbar.data), _ptr(dD), *_rows(rows, B, C),
                                   _ptr(out), _ptr(dKrbar),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out, dKrbar
@@ -497,12 +641,19 @@ def _info_dict(info: BankInfo) -> dict:
 def msa_bank_save(path: str, doc_tok_off, chunk_off, layers, chunk: int = 64, rope_base: float = 1e6,
                   rope_mask: int = 1):
     """Writes a bank file.  layers: [(Krbar, Kbar, Vbar), ...] one tuple per routed layer,
-    tensors on any device (copied to host memory for the write)."""
+    Krbar a RouteKeys (or a float32 [C, h_r, d] tensor), on any device (copied to host
+    memory for the write)."""
     dto = np.ascontiguousarray(doc_tok_off, dtype=np.int64)
     cho = np.ascontiguousarray(chunk_off, dtype=np.int64)
-    Kr0, K0, _ = layers[0]
-    host = [tuple(t.detach().contiguous().cpu() for t in trio) for trio in layers]
-    info = BankInfo(_dtype_code(Kr0), len(layers), len(dto) - 1, K0.shape[1], Kr0.shape[1], Kr0.shape[2], chunk,
+    host = []
+    for l, (Kr, K, V) in enumerate(layers):
+        Kr = _keys(Kr, f"layer {l} Krbar")
+        if Kr.n_chunks != int(cho[-1]) or K.shape[0] != int(cho[-1]) or V.shape != K.shape:
+            raise MsaError(MSA_ERR_INVALID_ARG, f"layer {l}: {Kr}, K-bar {tuple(K.shape)}, V-bar {tuple(V.shape)} "
+                                                f"for {int(cho[-1])} bank rows")
+        host.append((Kr.data.detach().cpu(), K.detach().contiguous().cpu(), V.detach().contiguous().cpu()))
+    Kr0, K0 = _keys(layers[0][0]), layers[0][1]
+    info = BankInfo(_dtype_code(Kr0.data), len(layers), len(dto) - 1, K0.shape[1], Kr0.h_r, Kr0.d, chunk,
                     rope_mask, rope_base, 0, int(dto[-1]), int(cho[-1]))
     arr = lambda i: (ctypes.c_void_p * len(host))(*[h[i].data_ptr() for h in host])
     _check(lib.msa_bank_save(os.fsencode(path), ctypes.byref(info), dto.ctypes.data, cho.ctypes.data, arr(0), arr(1),
@@ -517,7 +668,7 @@ def msa_bank_read_info(path: str) -> dict:
 
 def msa_bank_load(path: str, device=None, kv_device=None):
     """Reads a bank file.  Returns (doc_tok_off, chunk_off, layers, info): offsets as NumPy
-    int64 arrays, layers as [(Krbar, Kbar, Vbar), ...].  Kr-bar goes to ``device`` and K-bar /
+    int64 arrays, layers as [(Krbar RouteKeys, Kbar, Vbar), ...].  Kr-bar goes to ``device`` and K-bar /
     V-bar to ``kv_device`` (default: ``device``; "cpu-pinned" for page-locked host memory);
     None keeps a tensor in host memory."""
     info = BankInfo()
@@ -526,13 +677,14 @@ def msa_bank_load(path: str, device=None, kv_device=None):
     C, L = info.n_chunks, info.n_layers
     kvdev = device if kv_device is None else kv_device
     # host buffers are page-locked when they feed a device copy or are asked for as such
-    kr = [torch.empty((C, info.h_r, info.d), dtype=dt, pin_memory=device is not None) for _ in range(L)]
+    kr = [RouteKeys.empty(C, info.h_r, info.d, dt, "cpu", pin_memory=device is not None) for _ in range(L)]
     kv = [tuple(torch.empty((C, info.h_kv, info.d), dtype=dt, pin_memory=kvdev is not None) for _ in range(2))
           for _ in range(L)]
     dto = np.empty(info.n_docs + 1, dtype=np.int64)
     cho = np.empty(info.n_docs + 1, dtype=np.int64)
     arr = lambda ts: (ctypes.c_void_p * L)(*[t.data_ptr() for t in ts])
-    _check(lib.msa_bank_load(os.fsencode(path), ctypes.byref(info), dto.ctypes.data, cho.ctypes.data, arr(kr),
+    _check(lib.msa_bank_load(os.fsencode(path), ctypes.byref(info), dto.ctypes.data, cho.ctypes.data,
+                             arr([k.data for k in kr]),
                              arr([k for k, _ in kv]), arr([v for _, v in kv])))
     layers = []
     for l in range(L):

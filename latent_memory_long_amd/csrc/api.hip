@@ -80,6 +80,44 @@ int64_t msa_chunk_offsets(const int64_t* doc_tok_off, int32_t n_docs, int32_t ch
   return c;
 }
 
+int64_t msa_krbar_elems(msa_dtype dtype, int64_t n_chunks, int32_t h_r, int32_t d) {
+  g_last_error.clear();
+  if (dtype != MSA_F32 && dtype != MSA_BF16) { fail(MSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype); return -1; }
+  if (n_chunks < 0 || h_r < 1 || h_r > 64 || !head_dim_ok(d)) {
+    fail(MSA_ERR_INVALID_ARG, "need n_chunks >= 0, h_r in [1, 64], d in {32, 64, 128} (got %lld, %d, %d)",
+         (long long)n_chunks, h_r, d);
+    return -1;
+  }
+  return msa::krbar_elems((int)dtype, n_chunks, h_r, d);
+}
+
+namespace {
+msa_status krbar_convert_call(bool pack, msa_dtype dtype, int64_t n_chunks, int32_t h_r, int32_t d, const void* src,
+                              void* dst, msa_stream_t stream) {
+  g_last_error.clear();
+  if (dtype != MSA_F32 && dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (n_chunks < 0 || h_r < 1 || h_r > 64 || !head_dim_ok(d))
+    return fail(MSA_ERR_INVALID_ARG, "need n_chunks >= 0, h_r in [1, 64], d in {32, 64, 128} (got %lld, %d, %d)",
+                (long long)n_chunks, h_r, d);
+  if (n_chunks == 0) return MSA_OK;
+  if (!src || !dst) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (src == dst) return fail(MSA_ERR_INVALID_ARG, "source and destination must not overlap");
+  const hipError_t e = pack ? msa::launch_krbar_pack((int)dtype, n_chunks, h_r, d, src, dst, (hipStream_t)stream)
+                            : msa::launch_krbar_unpack((int)dtype, n_chunks, h_r, d, src, dst, (hipStream_t)stream);
+  return hip_status(e, pack ? "msa_krbar_pack launch" : "msa_krbar_unpack launch");
+}
+}  // namespace
+
+msa_status msa_krbar_pack(msa_dtype dtype, int64_t n_chunks, int32_t h_r, int32_t d, const void* rows, void* Krbar,
+                          msa_stream_t stream) {
+  return krbar_convert_call(true, dtype, n_chunks, h_r, d, rows, Krbar, stream);
+}
+
+msa_status msa_krbar_unpack(msa_dtype dtype, int64_t n_chunks, int32_t h_r, int32_t d, const void* Krbar,
+                            void* rows, msa_stream_t stream) {
+  return krbar_convert_call(false, dtype, n_chunks, h_r, d, Krbar, rows, stream);
+}
+
 msa_status msa_pool(msa_dtype dtype, int32_t n_docs, int64_t n_tokens, int64_t n_chunks,
                     const int64_t* doc_tok_off, const int64_t* chunk_off, int32_t h_kv,
                     int32_t h_r, int32_t d, int32_t chunk, float rope_base, uint32_t rope_mask,

@@ -10,7 +10,8 @@
 //
 // File layout (little-endian):
 //   "MSABANK1" | FileHeader (64 bytes) | doc_tok_off int64[N+1] | chunk_off int64[N+1] |
-//   for each layer: Kr-bar [C, h_r, d], K-bar [C, h_kv, d], V-bar [C, h_kv, d] (dtype) |
+//   for each layer: Kr-bar in the routing-key bank layout (msa_krbar_elems elements: 16-row
+//   tiles for bf16, row-major for float32), K-bar [C, h_kv, d], V-bar [C, h_kv, d] (dtype) |
 //   checksums uint64[2 + 3 L] (one per section above, in order) | "MSABEND1"
 // The checksum of a section is FNV-1a over its 64-bit little-endian words in four
 // interleaved lanes (word i goes to lane i mod 4; a zero-padded tail word), the lanes then
@@ -28,7 +29,7 @@ namespace {
 
 constexpr char MAGIC[8] = {'M', 'S', 'A', 'B', 'A', 'N', 'K', '1'};
 constexpr char END_MAGIC[8] = {'M', 'S', 'A', 'B', 'E', 'N', 'D', '1'};
-constexpr uint32_t FORMAT_VERSION = 1;
+constexpr uint32_t FORMAT_VERSION = 2;  // 2: bf16 Kr-bar in tiles of 16 rows
 constexpr size_t IO_BLOCK = size_t(16) << 20;
 
 struct FileHeader {
@@ -95,7 +96,9 @@ msa_status check_info(const msa_bank_info* in) {
   if (in->dtype != MSA_F32 && in->dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "unknown dtype %d", in->dtype);
   if (in->n_layers < 1 || in->n_layers > 1024) return fail(MSA_ERR_INVALID_ARG, "n_layers %d not in [1, 1024]", in->n_layers);
   if (in->n_docs < 1) return fail(MSA_ERR_INVALID_ARG, "n_docs must be >= 1 (got %d)", in->n_docs);
-  if (in->h_kv < 1 || in->h_r < 1 || in->d < 1) return fail(MSA_ERR_INVALID_ARG, "head counts and head dim must be >= 1");
+  if (in->h_kv < 1 || in->h_kv > 64 || in->h_r < 1 || in->h_r > 64)
+    return fail(MSA_ERR_INVALID_ARG, "head counts must lie in [1, 64] (got %d, %d)", in->h_kv, in->h_r);
+  if (in->d != 32 && in->d != 64 && in->d != 128) return fail(MSA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", in->d);
   if (in->chunk < 1) return fail(MSA_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", in->chunk);
   if (in->n_chunks < in->n_docs || in->n_tokens < in->n_chunks)
     return fail(MSA_ERR_INVALID_ARG, "need n_docs <= n_chunks <= n_tokens (got %d, %lld, %lld)", in->n_docs,
@@ -185,7 +188,8 @@ msa_status msa_bank_save(const char* path, const msa_bank_info* info, const int6
     if (!Krbar[l] || !Kbar[l] || !Vbar[l]) return fail(MSA_ERR_INVALID_ARG, "null tensor for layer %d", l);
   const size_t esz = elem_bytes(info->dtype);
   const size_t C = (size_t)info->n_chunks;
-  const size_t kr_bytes = C * info->h_r * info->d * esz, kv_bytes = C * info->h_kv * info->d * esz;
+  const size_t kr_bytes = (size_t)msa_krbar_elems((msa_dtype)info->dtype, info->n_chunks, info->h_r, info->d) * esz;
+  const size_t kv_bytes = C * info->h_kv * info->d * esz;
   const size_t off_bytes = ((size_t)info->n_docs + 1) * sizeof(int64_t);
   File out;
   out.f = fopen(path, "wb");
@@ -238,7 +242,8 @@ msa_status msa_bank_load(const char* path, const msa_bank_info* expect, int64_t*
     if (!Krbar[l] || !Kbar[l] || !Vbar[l]) return fail(MSA_ERR_INVALID_ARG, "null tensor for layer %d", l);
   const size_t esz = elem_bytes(info.dtype);
   const size_t C = (size_t)info.n_chunks;
-  const size_t kr_bytes = C * info.h_r * info.d * esz, kv_bytes = C * info.h_kv * info.d * esz;
+  const size_t kr_bytes = (size_t)msa_krbar_elems((msa_dtype)info.dtype, info.n_chunks, info.h_r, info.d) * esz;
+  const size_t kv_bytes = C * info.h_kv * info.d * esz;
   const size_t off_bytes = ((size_t)info.n_docs + 1) * sizeof(int64_t);
   std::vector<uint64_t> got(2 + 3 * (size_t)info.n_layers), want(got.size());
   bool ok = read_section(in.f, doc_tok_off, off_bytes, &got[0]) && read_section(in.f, chunk_off, off_bytes, &got[1]);

@@ -100,6 +100,26 @@ template <> struct Elem<bf16_t> {
   }
 };
 
+// ---- routing-key bank layout ------------------------------------------------------------
+// bf16 routing keys (Kr-bar) are stored in tiles of 16 bank rows, laid out for the matrix
+// cores: tile T holds rows 16T..16T+15 as H x (D/32) blocks of 512 elements, in (head,
+// 32-dim slice) order.  Block (h, s) is the B operand of v_mfma_f32_16x16x32_bf16 for head
+// h, dims 32s..32s+31 of the tile's rows: lane l = 16 g + r holds the 8 elements of dims
+// 32s + 8g .. 32s + 8g + 7 of row 16T + r.  A bank of C rows occupies ceil(C/16) whole
+// tiles; the rows past C in the last tile are padding (zero when the library writes them).
+// Each 1 KB block is one contiguous load instruction of a wave, and a tile is 16 rows of
+// every head in one contiguous run.  float32 routing keys stay row-major [C, H, D].
+__host__ __device__ __forceinline__ int64_t kr_tiles(int64_t n_rows) { return (n_rows + 15) >> 4; }
+
+// Element offset of element i = h * D + e of bank row c in the tiled layout.  Elements
+// i .. i+7 with i % 8 == 0 are contiguous.
+template <int D>
+__device__ __forceinline__ int64_t kr_tiled(int64_t c, int i, int H) {
+  const int h = i / D, e = i % D;
+  return (c >> 4) * ((int64_t)16 * H * D) + (int64_t)((h * (D / 32) + (e >> 5)) << 9) +
+         (((((e & 31) >> 3) << 4) | (int)(c & 15)) << 3) + (e & 7);
+}
+
 // ---- order-preserving score keys -------------------------------------------------------
 // Maps a float to a uint32 whose unsigned order is the float order (-0.0 folded into
 // +0.0).  Key 0 sorts below every non-NaN float and marks "no score yet".

@@ -124,6 +124,14 @@ struct AuxArgs {
 };
 hipError_t launch_aux_loss(const AuxArgs& a, hipStream_t s);
 
+// Conversion of routing keys between row-major [n_chunks, h_r, d] and the bank layout
+// (tiled for bf16, row-major for float32): pack writes the layout's padding rows as zero.
+int64_t krbar_elems(int dtype, int64_t n_chunks, int h_r, int d);
+hipError_t launch_krbar_pack(int dtype, int64_t n_chunks, int h_r, int d, const void* rows, void* krbar,
+                             hipStream_t s);
+hipError_t launch_krbar_unpack(int dtype, int64_t n_chunks, int h_r, int d, const void* krbar, void* rows,
+                               hipStream_t s);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace msa

@@ -25,6 +25,10 @@
 //    up to float32 rounding.
 //  * The mean divides by the number of real tokens with an IEEE division (a constant chunk
 //    pools to itself bit for bit), then rounds once to the storage type.
+//  * Row c of document d's chunk j is chunk_off[d] + j: offsets that start past 0 write new
+//    documents after the rows a bank already holds.  bf16 routing keys are written in the
+//    tiled layout of common.hpp (each thread's 8- or 4-element unit stays one contiguous
+//    store); only the rows of the given documents are written.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -98,10 +102,12 @@ struct PoolStream {
   double rc[4], rs[4], stc[4], sts[4];
   int64_t cst, bnd, c, doc_s, doc_e;
   int doc;
+  bool tiled;  // destination is a bf16 routing-key bank in the tiled layout
+  int heads;   // heads of the destination tensor
 };
 
 // Mean of the finished chunk [cst, bnd) -> bank row c, then move to the next chunk.
-template <bool rotate, typename T>
+template <bool rotate, typename T, int D>
 __device__ __forceinline__ void pool_flush(PoolStream& st, const PoolArgs& a, T* dst, int row_elems,
                                            int e_lo, int e_hi, bool store) {
   if constexpr (rotate) {  // R(s), s = first in-document position of the chunk (identity at s = 0)
@@ -116,13 +122,19 @@ __device__ __forceinline__ void pool_flush(PoolStream& st, const PoolArgs& a, T*
   const float fn = (float)(st.bnd - st.cst);
 #pragma unroll
   for (int q = 0; q < 8; ++q) st.acc[q] = st.acc[q] / fn;
-  T* out = dst + st.c * row_elems;
+  // the unit's place in the row: row-major, or (bf16 routing keys) its 16-byte slot of the
+  // row's tile, where 4 or 8 consecutive elements of one head stay contiguous
+  int64_t o_lo = st.c * row_elems + e_lo, o_hi = st.c * row_elems + e_hi;
+  if (st.tiled) {
+    o_lo = kr_tiled<D>(st.c, e_lo, st.heads);
+    o_hi = kr_tiled<D>(st.c, e_hi, st.heads);
+  }
   if (store) {
     if constexpr (rotate) {
-      Elem<T>::store4(out + e_lo, st.acc);
-      Elem<T>::store4(out + e_hi, st.acc + 4);
+      Elem<T>::store4(dst + o_lo, st.acc);
+      Elem<T>::store4(dst + o_hi, st.acc + 4);
     } else {
-      Elem<T>::store8(out + e_lo, st.acc);
+      Elem<T>::store8(dst + o_lo, st.acc);
     }
   }
 #pragma unroll
@@ -159,7 +171,7 @@ __device__ __forceinline__ void pool_load(Raw<T> (&X)[PT], const T* src, int64_t
   }
 }
 
-template <bool rotate, typename T>
+template <bool rotate, typename T, int D>
 __device__ __forceinline__ void pool_batch(PoolStream& st, const Raw<T> (&X)[PT], int64_t t0, int64_t p1,
                                            const PoolArgs& a, T* dst, int row_elems, int e_lo, int e_hi,
                                            bool store, const float* rope_tab, int half, int i0) {
@@ -167,7 +179,7 @@ __device__ __forceinline__ void pool_batch(PoolStream& st, const Raw<T> (&X)[PT]
   for (int k = 0; k < PT; ++k) {
     const int64_t t = t0 + k;
     if (t >= p1) break;  // uniform
-    if (t == st.bnd) pool_flush<rotate>(st, a, dst, row_elems, e_lo, e_hi, store);
+    if (t == st.bnd) pool_flush<rotate, T, D>(st, a, dst, row_elems, e_lo, e_hi, store);
     float v[8];
     X[k].get(v);
     if constexpr (rotate) {
@@ -193,8 +205,10 @@ __device__ __forceinline__ void pool_batch(PoolStream& st, const Raw<T> (&X)[PT]
 template <bool rotate, typename T, int D>
 __device__ __forceinline__ void pool_stream(const PoolArgs& a, const T* src, T* dst, int64_t p0, int64_t p1,
                                             int doc0, int row_elems, int e_lo, int e_hi, int i0, bool valid,
-                                            const float* rope_tab) {
+                                            const float* rope_tab, bool tiled) {
   PoolStream st;
+  st.tiled = tiled;
+  st.heads = row_elems / D;
 #pragma unroll
   for (int q = 0; q < 8; ++q) st.acc[q] = 0.f;
   st.doc = doc0;
@@ -231,13 +245,13 @@ __device__ __forceinline__ void pool_stream(const PoolArgs& a, const T* src, T* 
   pool_load<rotate>(X0, src, p0, p1, row_elems, e_lo, e_hi);
   pool_load<rotate>(X1, src, p0 + PT, p1, row_elems, e_lo, e_hi);
   for (int64_t t0 = p0; t0 < p1; t0 += 2 * PT) {
-    pool_batch<rotate>(st, X0, t0, p1, a, dst, row_elems, e_lo, e_hi, valid, rope_tab, D / 2, i0);
+    pool_batch<rotate, T, D>(st, X0, t0, p1, a, dst, row_elems, e_lo, e_hi, valid, rope_tab, D / 2, i0);
     pool_load<rotate>(X0, src, t0 + 2 * PT, p1, row_elems, e_lo, e_hi);
     if (t0 + PT < p1)
-      pool_batch<rotate>(st, X1, t0 + PT, p1, a, dst, row_elems, e_lo, e_hi, valid, rope_tab, D / 2, i0);
+      pool_batch<rotate, T, D>(st, X1, t0 + PT, p1, a, dst, row_elems, e_lo, e_hi, valid, rope_tab, D / 2, i0);
     pool_load<rotate>(X1, src, t0 + 3 * PT, p1, row_elems, e_lo, e_hi);
   }
-  pool_flush<rotate>(st, a, dst, row_elems, e_lo, e_hi, valid);  // the range ends at a chunk end
+  pool_flush<rotate, T, D>(st, a, dst, row_elems, e_lo, e_hi, valid);  // the range ends at a chunk end
 }
 
 template <typename T, int D>
@@ -289,8 +303,9 @@ __global__ __launch_bounds__(512) void pool_kernel(PoolArgs a) {
   const int64_t p1 = range_start(a, (int64_t)blockIdx.x + 1, gridDim.x, doc1);
   if (p0 >= p1 || gw >= 2 * wk + wr) return;
 
-  if (rotate) pool_stream<true, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab);
-  else pool_stream<false, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab);
+  const bool tiled = tensor == 2 && sizeof(T) == 2;  // bf16 routing keys: tiled bank layout
+  if (rotate) pool_stream<true, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab, tiled);
+  else pool_stream<false, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab, tiled);
 }
 
 template <typename T, int D>

@@ -19,18 +19,22 @@
 // The scan reads each bank row once (H * d * 2 bytes per row in bf16) and does
 // 2 * Lq * H * d flops on it, so it is bound by HBM bandwidth unless Lq is in the
 // hundreds.  Two kernels:
-//  * route_scan_mfma (bf16, up to 8 routing heads, any query length): one wave per routing
-//    head, a pass per 64 query rows.  The wave
-//    keeps its head's query rows as MFMA A operands (v_mfma_f32_16x16x32_bf16, rows padded
-//    to 16) and streams 16-row tiles of its head's Kr-bar slice as B operands straight
-//    from HBM into registers through a ring of four tiles (three tiles of loads stay in
-//    flight while one is computed).  Row norms of the tile are the diagonal of B^T B, one
-//    more MFMA chain on the same registers.  The scaled per-head scores meet in LDS (double-buffered, one
-//    barrier per tile) for the head sum and the token max (DPP reductions); row scores
-//    collect in LDS and are folded into documents once per window of rows, by all waves.
-//  * route_scan_dot (float32, or more than 8 routing heads): each wave streams its own
-//    range of rows, four rows per step with the next four in flight; a lane holds 8
-//    elements of a row, head sums and the head mean use DPP lane shifts.
+//  * route_scan_mfma (bf16 banks in the tiled layout of common.hpp, up to 8 routing heads,
+//    any query length, a pass per 64 query rows): eight waves per part.  Each wave owns
+//    whole 16-row tiles (its part's tiles w, w + 8, ...) and computes every head of them,
+//    so waves never wait for one another inside a window.  The query rows of every head
+//    sit in LDS as MFMA A operands (v_mfma_f32_16x16x32_bf16) with their 1/(H |q|); a
+//    tile's head blocks stream from HBM straight into registers as B operands, one 1 KB
+//    contiguous load per instruction, through a ring of four (tile, head) blocks with the
+//    non-temporal hint.  Row norms are the diagonal of B^T B (one more MFMA chain on the
+//    same registers), broadcast to the column's lanes; scaled head products are summed in
+//    registers, and the maximum over the query's tokens is reduced across the column's
+//    lanes.  Row scores collect in one of two LDS windows of rows, folded into documents
+//    by all waves once per window.
+//  * route_scan_dot (float32 banks, row-major; bf16 banks with more than 8 routing heads,
+//    tiled): each wave streams its own range of rows, four rows per step with the next
+//    four in flight; a lane holds 8 elements of a row, head sums and the head mean use DPP
+//    lane shifts.
 #include <math.h>
 
 #include <type_traits>
@@ -60,22 +64,28 @@ __device__ __forceinline__ int64_t load_window(const int64_t* chunk_off, int n_d
 }
 
 // ------------------------------------------------------------------------------------
-// MFMA scan.
+// MFMA scan of a bf16 bank in the tiled layout.
 // ------------------------------------------------------------------------------------
-constexpr int WIN = 4096;  // rows whose scores are held in LDS before folding into documents
-constexpr int RING = 4;    // register tile buffers per wave
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+// Bank tiles are read once: the non-temporal hint streams them past the caches (measured on
+// the 100M-token bank: a plain read of this pattern reaches 76% of peak, with the hint 86%).
+__device__ __forceinline__ bf16x8_t load_nt(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
 
-// ARG: also write every row's score and the first query token reaching it (row_scores,
-// row_arg), for the router's backward; the forward instantiation carries none of it.
+constexpr int SCAN_WAVES = 8;  // waves per workgroup of the MFMA scan
+constexpr int SCAN_RING = 4;   // (tile, head) blocks of loads per wave: three in flight during one
 template <int MT, int D, bool ARG>
 __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
-  constexpr int KK = D / 32;          // 32-wide k steps per head
-  constexpr int ROWS = MT * 16;       // query rows per block
-  constexpr int STRIDE = ROWS + 4;    // padded LDS row (floats)
-  __shared__ float red[2][8][16][STRIDE];
-  __shared__ float4 csq[2][16][2];  // 1/|Kr-bar[c, h]| of the tile, [buf][c][h / 4]
-  __shared__ float sc_all[WIN];
-  __shared__ int arg_all[ARG ? WIN : 1];
+  constexpr int KK = D / 32;
+  constexpr int HMAX = 8;
+  constexpr int WINR = ARG ? 1024 : 2048;  // rows per score window (two windows in LDS)
+  constexpr int WTILES = WINR / 16;
+  constexpr int R = SCAN_RING;
+  __shared__ __align__(16) bf16_t Aq[HMAX * MT * KK * 512];
+  __shared__ __align__(16) float rsq_t[HMAX][MT * 16];
+  __shared__ float scw_all[2][WINR];
+  __shared__ int ag_all[ARG ? 2 : 1][ARG ? WINR : 1];
   __shared__ float carry[2];
 
   const int H = a.H;
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
   const int d_end = part_first_doc(a.chunk_off, a.n_docs, a.n_chunks, part + 1, gridDim.x);
   if (d_begin >= d_end) return;
   float* scores = a.scores + (int64_t)b * a.n_docs;
-  if (Lq <= 0) {  // a query without tokens scores -inf everywhere
+  if (Lq <= 0) {
     for (int d = d_begin + tid; d < d_end; d += nthr) scores[d] = -INFINITY;
     return;
   }
@@ -98,173 +108,191 @@ __global__ __launch_bounds__(512) void route_scan_mfma(ScanK a) {
   const int64_t c_end = a.chunk_off[d_end];
   const bf16_t* Qr = (const bf16_t*)a.Qr;
   const bf16_t* Kb = (const bf16_t*)a.Krb;
-  int d_first = d_begin;  // document owning the window's first row
-  if (tid == 0) carry[0] = -INFINITY;
+  const int64_t tile_elems = (int64_t)16 * H * D;
+  const int64_t T_begin = c_begin >> 4;
+  const int ntiles = (int)(((c_end + 15) >> 4) - T_begin);
+  const int nwin = (ntiles + WTILES - 1) / WTILES;
+  const int n_my = ntiles > w ? (ntiles - w + 7) / 8 : 0;   // this wave's tiles: w, w + 8, ...
+  const int n_steps = n_my * H;                              // one step per (tile, head)
 
-  for (int64_t w0 = c_begin, wi = 0; w0 < c_end; w0 += WIN, ++wi) {
-    const int64_t w1 = min(w0 + (int64_t)WIN, c_end);
-    const int wn = (int)(w1 - w0);
-    const int64_t ntiles = (wn + 15) / 16;
-    for (int i = tid; i < wn; i += nthr) sc_all[i] = -INFINITY;
-
-    for (int rb = 0; rb < Lq; rb += ROWS) {
-      const int rows = min(ROWS, Lq - rb);
-      // ---- A operands: this head's query rows, and their scales ----
-      bf16x8_t A[MT][KK];
-      float rs[MT][4];
+  for (int rb = 0; rb < Lq; rb += MT * 16) {
+    const int rows = min(MT * 16, Lq - rb);
+    __syncthreads();  // the previous pass is done with Aq
+    for (int u = tid; u < H * MT * KK * 64; u += nthr) {
+      const int L = u & 63;
+      int rest = u >> 6;
+      const int kk = rest % KK;
+      rest /= KK;
+      const int m = rest % MT, h = rest / MT;
+      const int t = rb + m * 16 + (L & 15);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (t < Lq) v = *reinterpret_cast<const uint4*>(Qr + ((int64_t)(q0 + t) * H + h) * D + kk * 32 + (L >> 4) * 8);
+      *reinterpret_cast<uint4*>(&Aq[(size_t)u * 8]) = v;
+    }
+    for (int u = tid; u < H * MT * 16; u += nthr) {
+      const int h = u / (MT * 16), tl = u - h * (MT * 16);
+      const int t = rb + tl;
+      float rr = 0.f;
+      if (t < Lq) {
+        const bf16_t* q = Qr + ((int64_t)(q0 + t) * H + h) * D;
+        float sg[4];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int r = rb + m * 16 + cl;
-        float ss = 0.f;
+        for (int gg = 0; gg < 4; ++gg) {
+          float ss = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          uint4 wq = make_uint4(0, 0, 0, 0);
-          if (r < Lq)
-            wq = *reinterpret_cast<const uint4*>(Qr + ((int64_t)(q0 + r) * H + w) * D + kk * 32 + g * 8);
-          A[m][kk] = __builtin_bit_cast(bf16x8_t, wq);
-          ss = dot2_bf16(wq.x, wq.x, ss);
-          ss = dot2_bf16(wq.y, wq.y, ss);
-          ss = dot2_bf16(wq.z, wq.z, ss);
-          ss = dot2_bf16(wq.w, wq.w, ss);
+          for (int kk = 0; kk < KK; ++kk) {
+            const uint4 wq = *reinterpret_cast<const uint4*>(q + kk * 32 + gg * 8);
+            ss = dot2_bf16(wq.x, wq.x, ss);
+            ss = dot2_bf16(wq.y, wq.y, ss);
+            ss = dot2_bf16(wq.z, wq.z, ss);
+            ss = dot2_bf16(wq.w, wq.w, ss);
+          }
+          sg[gg] = ss;
         }
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        const float rrow = ss > 0.f ? __builtin_amdgcn_rsqf(ss) / (float)H : 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rs[m][i] = __shfl(rrow, g * 4 + i);
+        const float ss = (sg[0] + sg[1]) + (sg[2] + sg[3]);
+        rr = ss > 0.f ? __builtin_amdgcn_rsqf(ss) / (float)H : 0.f;
       }
-      __syncthreads();  // sc_all initialised; red free from the previous block
+      rsq_t[h][tl] = rr;
+    }
+    __syncthreads();
 
-      // Tile t covers rows w0 + 16t .. +15; rows past the window are clamped to the last
-      // row (their columns are zeroed through cs = 0), so loads need no branches.
-      auto load = [&](bf16x8_t (&B)[KK], int64_t t) {
-        int64_t c = w0 + t * 16 + cl;
-        c = c < w1 ? c : w1 - 1;
-        const bf16_t* p = Kb + (c * H + w) * D + g * 8;
+    // Loads are issued unconditionally, with the tile clamped into the part's tiles (a wave
+    // without tiles of its own, in a part of fewer than eight tiles, reads the part's last
+    // tile), so the compiler waits for exactly the oldest ring slot instead of draining the
+    // queue.
+    const int64_t T_last = T_begin + ntiles - 1;
+    auto load = [&](bf16x8_t (&B)[KK], int k, int h) {
+      const int64_t T = min(T_begin + w + (int64_t)max(k, 0) * 8, T_last);
+      const bf16_t* p = Kb + T * tile_elems + (int64_t)h * (KK * 512) + lane * 8;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          B[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + kk * 32));
-      };
-      auto process = [&](bf16x8_t (&B)[KK], int64_t t) {
-        const int buf = (int)(t & 1);
-        // Squared row norms of the tile: the diagonal of B^T B (the B registers are also the
-        // A operand of the 16 rows), exact products in float32.  The lane holding diagonal
-        // element (cl, cl) -- lane group g == cl / 4, element cl % 4 -- stores 1/|row|.
-        {
-          f32x4_t gram = {0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < KK; ++kk) B[kk] = load_nt(p + kk * 512);
+    };
+    bf16x8_t B[R][KK];
+    // load position (lk, lh) runs R steps ahead of the processing position (pk, ph)
+    int lk = 0, lh = 0;
+    auto advance = [&](int& k, int& h) {
+      if (++h == H) { h = 0; ++k; }
+    };
+    auto clamp_load = [&](bf16x8_t (&Bx)[KK]) {
+      const bool in = lk < n_my;
+      load(Bx, in ? lk : n_my - 1, in ? lh : H - 1);
+      advance(lk, lh);
+    };
+    // prologue: slot r's loads in slot order (the loop waits for the oldest slot only if
+    // the loads entering it are pending in the same order as on its back edge)
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(B[kk], B[kk], gram, 0, 0, 0);
-          if (g == (cl >> 2)) {
-            const float ss = gram[cl & 3];
-            const bool valid = w0 + t * 16 + cl < w1;
-            reinterpret_cast<float*>(&csq[buf][cl][0])[w] =
-                (valid && ss > 0.f) ? __builtin_amdgcn_rsqf(ss) : 0.f;
-          }
-        }
+    for (int r = 0; r < R; ++r) {
+      clamp_load(B[r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    int pk = 0, ph = 0;
+    float total[MT][4];
+    int d_first = d_begin;
+    int st = 0;
+    for (int wi = 0; wi < nwin; ++wi) {
+      const int64_t base_row = (T_begin + (int64_t)wi * WTILES) * 16;
+      const int64_t w0 = max(c_begin, base_row);
+      const int64_t w1 = min(c_end, base_row + (int64_t)WINR);
+      float* scw = scw_all[wi & 1];
+      int* agw = ag_all[ARG ? (wi & 1) : 0];
+      const int s_end = min(n_steps, (wi + 1) * (WTILES / 8) * H);
+      for (; st < s_end; st += R) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < R; ++r) {
+          if (st + r < s_end) {
+            const int h = ph;
+            if (h == 0) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][kk], B[kk], acc, 0, 0, 0);
-          // lane holds rows m*16 + g*4 + i of column cl; the column scale comes later
-          float4 v;
-          v.x = acc[0] * rs[m][0];
-          v.y = acc[1] * rs[m][1];
-          v.z = acc[2] * rs[m][2];
-          v.w = acc[3] * rs[m][3];
-          *reinterpret_cast<float4*>(&red[buf][w][cl][m * 16 + g * 4]) = v;
-        }
-        lds_barrier();
-        // head sum then max over query rows: thread (column c, row pair j), 32 lanes per column
-        for (int base = 0; base < 16 * 32; base += nthr) {
-          const int idx = base + tid;
-          const int c = idx >> 5, j = idx & 31;
-          float s = -INFINITY;
-          int ri = 2 * j;  // ARG: the lane's first maximising row
-          if (2 * j < rows) {
-            const float* csc = reinterpret_cast<const float*>(&csq[buf][c][0]);
-            float s0 = 0.f, s1 = 0.f;
-            for (int h = 0; h < H; ++h) {
-              const float2 v = *reinterpret_cast<const float2*>(&red[buf][h][c][2 * j]);
-              const float ch = csc[h];
-              s0 += v.x * ch;
-              s1 += v.y * ch;
+              for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) total[m][i] = 0.f;
             }
-            s = (2 * j + 1 < rows) ? fmaxf(s0, s1) : s0;
-            if (ARG && 2 * j + 1 < rows && s1 > s0) ri = 2 * j + 1;
-          }
-          if constexpr (ARG) {
-            // the column's max, then the lowest lane (lowest rows) holding it
-            const float sl = s;
-            s = half_max_last(s);
-            const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 31));
-            const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
-            const uint64_t hit = __ballot(sl == ((lane < 32) ? mx : mh));
-            const uint32_t half = (lane < 32) ? (uint32_t)hit : (uint32_t)(hit >> 32);
-            const int src = (lane & 32) + (half ? __builtin_ctz(half) : 0);
-            const int rfirst = __shfl(ri, src, 64);
-            if ((lane & 31) == 31) {
-              const int64_t ci = t * 16 + c;
-              if (ci < wn && s > sc_all[ci]) {  // strictly greater: an earlier block keeps a tie
-                sc_all[ci] = s;
-                arg_all[ci] = rb + rfirst;
+            // 1/|k| of each column (bank row) for this head: Gram diagonal, broadcast from
+            // the lane holding element (cl, cl) to the column's four lanes
+            f32x4_t gram = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+              gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(B[r][kk], B[r][kk], gram, 0, 0, 0);
+            const int e = cl & 3;
+            const float dg = e == 0 ? gram[0] : e == 1 ? gram[1] : e == 2 ? gram[2] : gram[3];
+            const float nrm = __shfl(dg, (cl >> 2) * 16 + cl, 64);
+            const float cs = nrm > 0.f ? __builtin_amdgcn_rsqf(nrm) : 0.f;
+            const bf16_t* Ah = Aq + (size_t)h * (MT * KK * 512) + lane * 8;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int kk = 0; kk < KK; ++kk) {
+                const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(Ah + (m * KK + kk) * 512);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[r][kk], acc, 0, 0, 0);
+              }
+              const float4 rv = *reinterpret_cast<const float4*>(&rsq_t[h][m * 16 + g * 4]);
+              total[m][0] = fmaf(acc[0] * rv.x, cs, total[m][0]);
+              total[m][1] = fmaf(acc[1] * rv.y, cs, total[m][1]);
+              total[m][2] = fmaf(acc[2] * rv.z, cs, total[m][2]);
+              total[m][3] = fmaf(acc[3] * rv.w, cs, total[m][3]);
+            }
+            if (h == H - 1) {
+              // the column's maximum over the block's valid tokens (ARG: first token reaching it)
+              float best = -INFINITY;
+              int bt = 0;
+#pragma unroll
+              for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int tl = m * 16 + g * 4 + i;
+                  if (tl < rows && total[m][i] > best) {
+                    best = total[m][i];
+                    bt = tl;
+                  }
+                }
+#pragma unroll
+              for (int o = 16; o < 64; o <<= 1) {
+                const float ob = __shfl_xor(best, o, 64);
+                if constexpr (ARG) {
+                  const int ot = __shfl_xor(bt, o, 64);
+                  if (ob > best || (ob == best && ot < bt)) bt = ot;
+                }
+                best = fmaxf(best, ob);
+              }
+              const int64_t row = (T_begin + w + (int64_t)pk * 8) * 16 + cl;
+              if (g == 0 && row >= w0 && row < w1) {
+                scw[row - base_row] = best;
+                if constexpr (ARG) agw[row - base_row] = rb + bt;
               }
             }
-          } else {
-            s = half_max_last(s);
-            if ((lane & 31) == 31) {
-              const int64_t ci = t * 16 + c;
-              if (ci < wn) sc_all[ci] = fmaxf(sc_all[ci], s);
-            }
+            advance(pk, ph);
+          }
+          clamp_load(B[r]);
+        }
+      }
+      lds_barrier();  // every wave's row scores of this window are in LDS
+      if constexpr (ARG) {
+        for (int64_t r = w0 + tid; r < w1; r += nthr) {
+          const float v = scw[r - base_row];
+          const int64_t o = (int64_t)b * a.n_chunks + r;
+          if (rb == 0 || v > a.row_scores[o]) {  // an earlier block keeps a tie
+            a.row_scores[o] = v;
+            a.row_arg[o] = agw[r - base_row];
           }
         }
-      };
-
-      // Ring of RING tiles: RING - 1 tiles of loads stay in flight while one is computed.
-      // Every load is issued unconditionally (tile index clamped to the last tile) so the
-      // compiler can wait for exactly the oldest tile instead of draining the queue.
-      bf16x8_t Bq[RING][KK];
-#pragma unroll
-      for (int r = 0; r < RING; ++r) load(Bq[r], min((int64_t)r, ntiles - 1));
-      for (int64_t t0 = 0; t0 < ntiles; t0 += RING) {
-#pragma unroll
-        for (int r = 0; r < RING; ++r) {
-          const int64_t t = t0 + r;
-          if (t < ntiles) process(Bq[r], t);
-          load(Bq[r], min(t + RING, ntiles - 1));
+      }
+      const int cin = wi & 1, cout = cin ^ 1;
+      for (int d = d_first + w; d < d_end; d += SCAN_WAVES) {
+        const int64_t r0 = a.chunk_off[d], r1 = a.chunk_off[d + 1];
+        if (r0 >= w1) break;
+        const int lo = (int)(max(r0, w0) - base_row), hi = (int)(min(r1, w1) - base_row);
+        float m = -INFINITY;
+        for (int i = lo + lane; i < hi; i += 64) m = fmaxf(m, scw[i]);
+        m = wave_max_all(m);
+        if (r0 < w0) m = fmaxf(m, carry[cin]);
+        if (lane == 0) {
+          if (r1 <= w1) scores[d] = (rb == 0) ? m : fmaxf(m, scores[d]);
+          else carry[cout] = m;
         }
       }
-      __syncthreads();
+      if (w1 < c_end) d_first = find_doc_wave(a.chunk_off, a.n_docs, w1);
     }
-
-    if constexpr (ARG) {
-      for (int i = tid; i < wn; i += nthr) {
-        a.row_scores[(int64_t)b * a.n_chunks + w0 + i] = sc_all[i];
-        a.row_arg[(int64_t)b * a.n_chunks + w0 + i] = arg_all[i];
-      }
-    }
-
-    // ---- fold the window's row scores into documents, all waves in parallel ----
-    const int cin = (int)(wi & 1), cout = cin ^ 1;
-    int d_next = d_first;
-    for (int d = d_first + w; d < d_end; d += H) {
-      const int64_t r0 = a.chunk_off[d], r1 = a.chunk_off[d + 1];
-      if (r0 >= w1) break;
-      const int lo = (int)(max(r0, w0) - w0), hi = (int)(min(r1, w1) - w0);
-      float m = -INFINITY;
-      for (int i = lo + lane; i < hi; i += 64) m = fmaxf(m, sc_all[i]);
-      m = wave_max_all(m);
-      if (r0 < w0) m = fmaxf(m, carry[cin]);  // began in an earlier window
-      if (lane == 0) {
-        if (r1 <= w1) scores[d] = m;
-        else carry[cout] = m;                  // continues into the next window
-      }
-    }
-    if (w1 < c_end) d_next = find_doc_wave(a.chunk_off, a.n_docs, w1);
-    d_first = d_next;
-    __syncthreads();
   }
 }
 
@@ -394,7 +422,8 @@ __global__ __launch_bounds__(256) void route_scan_dot(ScanK a) {
 #pragma unroll
           for (int p = 0; p < P; ++p) {  // lanes past the row end re-read its last 8 elements
             const int e0 = min(p * 512 + lane * 8, R - 8);
-            X[u][p].load(Kb + c * R + e0);
+            if constexpr (sizeof(T) == 2) X[u][p].load(Kb + kr_tiled<D>(c, e0, H));  // bf16: tiled bank
+            else X[u][p].load(Kb + c * R + e0);
           }
         }
       };
@@ -489,10 +518,10 @@ int route_parts(int64_t n_chunks, int64_t rows_per_part, int64_t max_parts, int 
 template <int D>
 hipError_t launch_mfma(const RouteArgs& r, const ScanK& k, hipStream_t s) {
   const int mt = min(4, (r.max_q_len + 15) / 16);
-  // one part per CU: a workgroup's LDS (about 87 KB) and registers leave room for one per CU,
-  // so 256 parts run in a single round (measured 0.8% faster than 512 parts in two rounds)
+  // one part per CU: a workgroup's LDS (the query operands of every head, up to 146 KB) leaves
+  // room for one per CU, so 256 parts run in a single round
   dim3 grid((unsigned)route_parts(r.n_chunks, 64, 256, r.n_queries), (unsigned)r.n_queries);
-  dim3 block(64 * r.h_r);
+  dim3 block(64 * SCAN_WAVES);
   if (k.row_scores) {
     switch (mt) {
       case 1: hipLaunchKernelGGL((route_scan_mfma<1, D, true>), grid, block, 0, s, k); break;

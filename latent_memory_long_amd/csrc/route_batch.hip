@@ -14,7 +14,8 @@
 // cores rather than for the bank read:
 //  * Each wave keeps 16 bank rows of 8 heads (32 rows of 4 heads) in registers as MFMA B
 //    operands for the whole launch, with their per-head 1/|k|: 128 registers, so two
-//    waves share a SIMD.  A workgroup is eight such waves and covers 128 (256) bank
+//    waves share a SIMD.  The bank is in the tiled layout (common.hpp): each B operand is
+//    one contiguous 1 KB block of a 16-row tile.  A workgroup is eight such waves and covers 128 (256) bank
 //    rows; the bank is read from HBM once.
 //  * Every query of the batch, padded to 16-row tiles, streams past those registers
 //    through LDS in stages of two tiles (32 rows, all heads), double-buffered: the next
@@ -122,17 +123,19 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
   bf16x8_t Bt[BNT][H][KS];
   float cs[BNT][H];
   int doc[BNT];
+  const int64_t last_tile = kr_tiles(C) - 1;
 #pragma unroll
   for (int j = 0; j < BNT; ++j) {
-    int64_t c = base + j * 16 + cl;
+    // tile of rows base + 16 j ..: one 1 KB block per (head, 32-dim slice), lane l holding
+    // its B operand slot (columns past the bank are padding, masked through doc = -1)
+    const int64_t c = base + j * 16 + cl;
     const bool valid = c < C;
-    c = valid ? c : C - 1;
-    const bf16_t* p = a.Krb + c * HD + g * 8;
+    const bf16_t* p = a.Krb + min((base >> 4) + j, last_tile) * (16 * HD) + lane * 8;
 #pragma unroll
     for (int h = 0; h < H; ++h)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        Bt[j][h][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + h * BD + ks * 32));
+        Bt[j][h][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + (h * KS + ks) * 512));
     // the norms read the rows a second time (from cache), so the B operands have no use
     // but the matrix products and may live in accumulation registers
 #pragma unroll
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
       float ss = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + h * BD + ks * 32));
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + (h * KS + ks) * 512));
         ss = dot2_bf16(v.x, v.x, ss);
         ss = dot2_bf16(v.y, v.y, ss);
         ss = dot2_bf16(v.z, v.z, ss);

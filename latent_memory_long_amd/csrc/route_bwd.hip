@@ -36,7 +36,7 @@ struct RouteBwdK {
   const float* row_scores;  // [B, C]
   const int32_t* row_arg;   // [B, C]
   float* dQr;               // [total_q, H, D]
-  float* dKrb;              // [C, H, D], added to
+  float* dKrb;              // [C, H, D] row-major, added to
   int32_t* tstar;           // [B, N]: maximising token (query-local), -1 if no gradient
   int64_t* cstar;           // [B, N]: maximising row
   float* cosv;              // [B, N, H]
@@ -48,6 +48,14 @@ struct RouteBwdK {
 template <typename T> __device__ __forceinline__ float ld(const T* p, int64_t i);
 template <> __device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
 template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+// Element i = h * D + e of routing-key row c: bf16 banks are in the tiled layout of
+// common.hpp, float32 banks row-major.
+template <typename T, int D>
+__device__ __forceinline__ float ld_key(const T* K, int64_t c, int i, int H) {
+  if constexpr (sizeof(T) == 2) return bf16_to_f32(K[kr_tiled<D>(c, i, H)]);
+  else return K[c * (int64_t)H * D + i];
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void route_bwd_pair(RouteBwdK a) {
@@ -84,14 +92,14 @@ __global__ __launch_bounds__(256) void route_bwd_pair(RouteBwdK a) {
   const int64_t cs = c0 + bc;
   const int ts = a.row_arg[(int64_t)b * a.n_chunks + cs];  // the scan's first maximising token
   const T* q = (const T*)a.Qr + (int64_t)(q0 + ts) * H * D;
-  const T* k = (const T*)a.Krb + cs * H * D;
-  float* dk = a.dKrb + cs * H * D;
+  const T* K = (const T*)a.Krb;
+  float* dk = a.dKrb + cs * H * D;  // the gradient is row-major in every dtype
   const float gH = gd / (float)H;
   // gradient of the pair, head by head, lanes over elements
   for (int h = 0; h < H; ++h) {
     float dot = 0.f, qn = 0.f, kn = 0.f;
     for (int e = lane; e < D; e += 64) {
-      const float x = ld(q, h * D + e), y = ld(k, h * D + e);
+      const float x = ld(q, h * D + e), y = ld_key<T, D>(K, cs, h * D + e, H);
       dot += x * y;
       qn += x * x;
       kn += y * y;
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(256) void route_bwd_pair(RouteBwdK a) {
     const float cosv = dot * iq * ik;
     if (ok) {
       for (int e = lane; e < D; e += 64)
-        atomicAdd(dk + h * D + e, gH * (ld(q, h * D + e) * iq - cosv * ld(k, h * D + e) * ik) * ik);
+        atomicAdd(dk + h * D + e, gH * (ld(q, h * D + e) * iq - cosv * ld_key<T, D>(K, cs, h * D + e, H) * ik) * ik);
     }
     if (lane == 0) {
       a.cosv[rec * H + h] = cosv;
@@ -164,13 +172,13 @@ __global__ __launch_bounds__(DQ_THREADS) void route_bwd_dq(RouteBwdK a) {
       for (int m = 0; m < nm; ++m) {
         const int64_t rec = (int64_t)b * a.n_docs + match[m];
         const float g = a.dD[rec];
-        const T* k = K + a.cstar[rec] * n_el;
+        const int64_t kc = a.cstar[rec];
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
           const int i = tid + j * DQ_THREADS;
           if (i < n_el) {
             const int h = i / D;
-            acc1[j] += g * ld(k, i) * a.kinv[rec * H + h];
+            acc1[j] += g * ld_key<T, D>(K, kc, i, H) * a.kinv[rec * H + h];
             acc2[j] += g * a.cosv[rec * H + h];
           }
         }

@@ -31,11 +31,16 @@ msa_status fetch(const T* dev, size_t n, std::vector<T>& out, hipStream_t s, con
   return MSA_OK;
 }
 
-// off[0] == 0, off[n] == total, and each entry at least `min_len` past the previous one.
+// off[0] == first (any first >= 0 when first < 0), off[n] == off[0] + total, and each entry
+// at least `min_len` past the previous one.
 template <typename T>
-msa_status check_offsets(const std::vector<T>& off, int64_t total, int64_t min_len, const char* what) {
+msa_status check_offsets(const std::vector<T>& off, int64_t total, int64_t min_len, const char* what,
+                         int64_t first = 0) {
   const size_t n = off.size() - 1;
-  if (off[0] != 0) return fail(MSA_ERR_INVALID_ARG, "%s[0] is %lld, not 0", what, (long long)off[0]);
+  if (first >= 0 && (int64_t)off[0] != first)
+    return fail(MSA_ERR_INVALID_ARG, "%s[0] is %lld, not %lld", what, (long long)off[0], (long long)first);
+  if (off[0] < 0) return fail(MSA_ERR_INVALID_ARG, "%s[0] is %lld, negative", what, (long long)off[0]);
+  total += (int64_t)off[0];
   for (size_t i = 0; i < n; ++i)
     if ((int64_t)off[i + 1] - (int64_t)off[i] < min_len)
       return fail(MSA_ERR_INVALID_ARG, "%s[%zu] = %lld after %lld: entries must grow by at least %lld", what,
@@ -45,11 +50,12 @@ msa_status check_offsets(const std::vector<T>& off, int64_t total, int64_t min_l
   return MSA_OK;
 }
 
+// first = -1: the offsets may start past row 0 (pooling after the rows a bank holds)
 msa_status check_chunk_off(const int64_t* chunk_off, int32_t n_docs, int64_t n_chunks, hipStream_t s,
-                           std::vector<int64_t>& co) {
+                           std::vector<int64_t>& co, int64_t first = 0) {
   msa_status st = fetch(chunk_off, (size_t)n_docs + 1, co, s, "chunk_off");
   if (st != MSA_OK) return st;
-  return check_offsets(co, n_chunks, 1, "chunk_off");  // every document has >= 1 row
+  return check_offsets(co, n_chunks, 1, "chunk_off", first);  // every document has >= 1 row
 }
 
 msa_status check_queries(const int32_t* q_off, int32_t n_queries, int64_t total_q, int32_t max_q_len,
@@ -71,7 +77,7 @@ msa_status debug_validate_pool(int32_t n_docs, int64_t n_tokens, int64_t n_chunk
   std::vector<int64_t> to, co;
   msa_status st = fetch(doc_tok_off, (size_t)n_docs + 1, to, s, "doc_tok_off");
   if (st == MSA_OK) st = check_offsets(to, n_tokens, 1, "doc_tok_off");  // every document has >= 1 token
-  if (st == MSA_OK) st = check_chunk_off(chunk_off, n_docs, n_chunks, s, co);
+  if (st == MSA_OK) st = check_chunk_off(chunk_off, n_docs, n_chunks, s, co, -1);
   if (st != MSA_OK) return st;
   for (int32_t d = 0; d < n_docs; ++d) {
     const int64_t want = (to[d + 1] - to[d] + chunk - 1) / chunk;

@@ -9,6 +9,7 @@ import time
 import numpy as np
 import torch
 
+import latent_memory_long_amd as M
 from oracle import msa_oracle as O
 
 # floating-point bars
@@ -24,13 +25,23 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def f64(t: torch.Tensor) -> np.ndarray:
-    """Exact float64 copy of a float32 / bf16 tensor (device or host)."""
-    return t.detach().float().cpu().double().numpy()
+def key_rows(t):
+    """Routing keys as a row-major [C, h_r, d] tensor (RouteKeys are unpacked on the GPU)."""
+    return t.rows() if isinstance(t, M.RouteKeys) else t
 
 
-def bf16_bits(t: torch.Tensor) -> np.ndarray:
-    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+def as_keys(t):
+    """Routing keys in the library's bank layout, from a row-major [C, h_r, d] tensor."""
+    return t if isinstance(t, M.RouteKeys) else M.RouteKeys.from_rows(t)
+
+
+def f64(t) -> np.ndarray:
+    """Exact float64 copy of a float32 / bf16 tensor (device or host) or of RouteKeys' rows."""
+    return key_rows(t).detach().float().cpu().double().numpy()
+
+
+def bf16_bits(t) -> np.ndarray:
+    return key_rows(t).detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def _ordered(bits: np.ndarray) -> np.ndarray:
@@ -139,7 +150,7 @@ def oracle_doc_scores_all(Qr: torch.Tensor, q_off, Krb: torch.Tensor, coff, bloc
     q_off = np.asarray(q_off, dtype=np.int64)
     coff = np.asarray(coff, dtype=np.int64)
     B, N = len(q_off) - 1, len(coff) - 1
-    Kh = Krb.detach().cpu()
+    Kh = key_rows(Krb).detach().cpu()
     Qs = [f64(Qr[int(q_off[b]):int(q_off[b + 1])]) for b in range(B)]
     groups = doc_groups(coff, block)
     out = np.empty((B, N), dtype=np.float64)

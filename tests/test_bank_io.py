@@ -13,16 +13,29 @@ from latent_memory_long_amd.binding import MsaError  # noqa: E402
 IO, INVALID = 5, 1
 
 
+def _kr_elems(dtype, C, h_r=3, d=32):
+    return M.msa_krbar_elems(0 if dtype == torch.float32 else 1, C, h_r, d)
+
+
 def _bank(seed, n_docs=23, layers=2, dtype=torch.bfloat16, h_kv=2, h_r=3, d=32, chunk=64):
+    """Random bank contents (the files store bytes; routing keys as RouteKeys storage of the
+    bank layout's size: 16-row tiles for bf16)."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(1, 300, size=n_docs)
     dto = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     cho = M.msa_chunk_offsets(dto, chunk)
     C = int(cho[-1])
     g = torch.Generator().manual_seed(seed)
-    trio = lambda: (torch.randn((C, h_r, d), generator=g).to(dtype), torch.randn((C, h_kv, d), generator=g).to(dtype),
-                    torch.randn((C, h_kv, d), generator=g).to(dtype))
+    keys = lambda: M.RouteKeys(torch.randn(_kr_elems(dtype, C, h_r, d), generator=g).to(dtype), C, h_r, d)
+    trio = lambda: (keys(), torch.randn((C, h_kv, d), generator=g).to(dtype), torch.randn((C, h_kv, d), generator=g).to(dtype))
     return dto, cho, [trio() for _ in range(layers)]
+
+
+def _same(x, y):
+    if isinstance(x, M.RouteKeys):
+        return x.shape == y.shape and _same(x.data, y.data)
+    return x.dtype == y.dtype and torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                                              y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
 
 
 @pytest.mark.parametrize("dtype,layers", [(torch.bfloat16, 1), (torch.bfloat16, 3), (torch.float32, 2)])
@@ -38,12 +51,14 @@ def test_round_trip(tmp_path, dtype, layers):
     assert np.array_equal(d2, dto) and np.array_equal(c2, cho)
     for a, b in zip(L, L2):
         for x, y in zip(a, b):
-            assert x.dtype == y.dtype and torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
-                                                      y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
-    # the file size is exactly header + sections + checksums + end mark
+            assert _same(x, y)
+    # the file size is exactly header + sections + checksums + end mark; bf16 routing keys
+    # fill whole 16-row tiles
     esz = 4 if dtype == torch.float32 else 2
     C, n = int(cho[-1]), len(dto)
-    expect = 8 + 64 + 2 * n * 8 + layers * C * (3 + 2 + 2) * 32 * esz + (2 + 3 * layers) * 8 + 8
+    kr = _kr_elems(dtype, C)
+    assert kr == (C if dtype == torch.float32 else (C + 15) // 16 * 16) * 3 * 32
+    expect = 8 + 64 + 2 * n * 8 + layers * (kr + C * (2 + 2) * 32) * esz + (2 + 3 * layers) * 8 + 8
     assert os.path.getsize(path) == expect
 
 
@@ -62,9 +77,9 @@ def test_every_section_is_checked(tmp_path):
     starts = [72, 72 + n * 8]                       # the two offset arrays
     pos = 72 + 2 * n * 8
     for _ in range(2):
-        for heads in (3, 2, 2):                     # Kr-bar, K-bar, V-bar
+        for n_el in (_kr_elems(torch.bfloat16, C), C * 2 * 32, C * 2 * 32):   # Kr-bar, K-bar, V-bar
             starts.append(pos)
-            pos += C * heads * 32 * 2
+            pos += n_el * 2
     names = ["doc_tok_off", "chunk_off"] + [f"layer {l} {t}" for l in range(2) for t in ("Kr-bar", "K-bar", "V-bar")]
     for start, name in zip(starts, names):
         bad = bytearray(blob)
@@ -100,7 +115,7 @@ def test_truncated_foreign_and_mismatched_files(tmp_path):
 def test_save_rejects_offsets_that_break_the_chunking_rule(tmp_path):
     dto, cho, L = _bank(4)
     bad = cho.copy()
-    bad[5:] += 1                                     # document 4 claims an extra row
+    bad[5] += 1                                      # document 4 claims a row of document 5
     with pytest.raises(MsaError) as e:
         M.msa_bank_save(str(tmp_path / "b.msab"), dto, bad, L)
     assert e.value.status == INVALID and "rows for" in str(e.value)

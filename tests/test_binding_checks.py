@@ -14,9 +14,14 @@ def z(shape, dt):
     return torch.zeros(shape, dtype=dt)
 
 
+def keys(C=6, h_r=2, d=32, dt=bf):
+    """Routing keys of C rows in the bank layout (host storage: the checks never reach it)."""
+    return m.RouteKeys(z((m.msa_krbar_elems(1 if dt == bf else 0, C, h_r, d),), dt), C, h_r, d)
+
+
 def route_args(**over):
     a = dict(Qr=z((4, 2, 32), bf), q_off=torch.tensor([0, 4], dtype=i32), max_q_len=4,
-             Krbar=z((6, 2, 32), bf), chunk_off=torch.tensor([0, 2, 6], dtype=i64))
+             Krbar=keys(), chunk_off=torch.tensor([0, 2, 6], dtype=i64))
     a.update(over)
     return a
 
@@ -43,7 +48,8 @@ def refused(fn, kw, text):
     (dict(Qr=z((4, 2, 32), f32)), "Qr has dtype"),
     (dict(Qr=z((4, 3, 32), bf)), "Qr has shape"),
     (dict(Qr=z((4, 2, 64), bf)), "Qr has shape"),
-    (dict(Krbar=z((6, 2, 32), torch.float16), Qr=z((4, 2, 32), torch.float16)), "Krbar has dtype"),
+    (dict(Krbar=z((6, 2, 32), bf)), "Krbar must be a RouteKeys"),
+    (dict(Krbar=keys(dt=f32)), "Qr has dtype"),
     (dict(Qr=z((2, 4, 32), bf).transpose(0, 1)), "Qr must be contiguous"),
     (dict(), "must be a device tensor"),
 ])
@@ -52,6 +58,21 @@ def test_route_refusals(over, text):
     kw = route_args(**over)
     kw["k"] = 2
     refused(m.msa_route_topk, kw, text)
+
+
+def test_route_keys_refusals():
+    with pytest.raises(MsaError) as e:
+        m.RouteKeys(z((6 * 2 * 32,), bf), 6, 2, 32)        # row count, not whole 16-row tiles
+    assert "RouteKeys data has shape" in e.value.message
+    with pytest.raises(MsaError) as e:
+        m.RouteKeys(z((16 * 2 * 32,), torch.float16), 6, 2, 32)
+    assert "RouteKeys data has dtype" in e.value.message
+    assert m.msa_krbar_elems(1, 17, 2, 32) == 32 * 2 * 32 and m.msa_krbar_elems(0, 17, 2, 32) == 17 * 2 * 32
+    assert keys(17).shape == (17, 2, 32) and keys(17).data.numel() == 32 * 64
+    with pytest.raises(MsaError):
+        m.msa_krbar_elems(1, 5, 2, 48)                        # head dim outside {32, 64, 128}
+    # a float32 bank may also be a plain row-major tensor
+    refused(m.msa_route_scan, route_args(Qr=z((4, 2, 32), f32), Krbar=z((6, 2, 32), f32)), "must be a device tensor")
 
 
 def test_route_output_refusals():
@@ -103,3 +124,12 @@ def test_topk_and_loss_refusals():
     refused(m.msa_route_aux_loss, dict(doc_scores=z((2, 5), f32), labels=z((2, 4), f32)), "labels has shape")
     kw = route_args(dD=z((1, 2), f64 := torch.float64))
     refused(m.msa_route_backward, kw, "dD has dtype")
+
+
+def test_pool_output_refusals():
+    K = z((10, 2, 32), bf)
+    base = dict(K=K, V=z((10, 2, 32), bf), Kr=z((10, 1, 32), bf), doc_tok_off=torch.tensor([0, 4, 10], dtype=i64),
+                chunk_off=torch.tensor([0, 1, 2], dtype=i64), n_chunks=2)
+    refused(m.msa_pool, {**base, "out": (z((2, 2, 32), bf), z((2, 2, 32), bf), z((2, 1, 32), bf))},
+            "Krbar must be a RouteKeys")
+    refused(m.msa_pool, {**base, "out": (z((2, 2, 32), bf), z((2, 2, 32), bf), keys(3, 1, 32))}, "bank buffers hold")

@@ -13,7 +13,7 @@ import latent_memory_long_amd as M
 from oracle import msa_oracle as O
 from synth import workloads as W
 from tests.helpers import (assert_attn_close, assert_pool_close, assert_scores_close, assert_topk_consistent,
-                           assert_topk_valid, f64, say)
+                           assert_topk_valid, f64, key_rows, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -59,13 +59,15 @@ def test_saved_bank_grows_by_appending(tmp_path):
     C = CA + int(coffB[-1])
     grown = []
     for (Krb, Kb, Vb), (K, V, Kr) in zip(loaded, states):
-        big = [torch.empty((C,) + tuple(x.shape[1:]), dtype=x.dtype, device=DEV) for x in (Kb, Vb, Krb)]
-        for b, x in zip(big, (Kb, Vb, Krb)):
+        big = [torch.empty((C,) + tuple(x.shape[1:]), dtype=x.dtype, device=DEV) for x in (Kb, Vb)]
+        for b, x in zip(big, (Kb, Vb)):
             b[:CA].copy_(x)
+        keys = Krb.grown(C)
         t = slice(int(off[cut]), int(off[-1]))
-        M.msa_pool(K[t], V[t], Kr[t], torch.tensor(offB, device=DEV), torch.tensor(coffB, device=DEV), C - CA,
-                   out=tuple(b[CA:] for b in big))
-        grown.append((big[2], big[0], big[1]))
+        # offsets that start at the CA rows the bank holds: the new rows go after them
+        M.msa_pool(K[t], V[t], Kr[t], torch.tensor(offB, device=DEV), torch.tensor(coffB + CA, device=DEV), C - CA,
+                   out=(big[0], big[1], keys))
+        grown.append((keys, big[0], big[1]))
     coff_g = np.concatenate([coffA, CA + coffB[1:]])
     assert np.array_equal(coff_g, coff)
     path2 = str(tmp_path / "bank2.msab")
@@ -75,7 +77,7 @@ def test_saved_bank_grows_by_appending(tmp_path):
     assert np.array_equal(dto2, off) and np.array_equal(cho2, coff)
     for (a_kr, a_k, a_v), (b_kr, b_k, b_v) in zip(whole, final):
         assert b_k.is_pinned() and b_kr.is_cuda
-        assert torch.equal(a_kr, b_kr) and torch.equal(a_k.cpu(), b_k) and torch.equal(a_v.cpu(), b_v)
+        assert a_kr.equal(b_kr) and torch.equal(a_k.cpu(), b_k) and torch.equal(a_v.cpu(), b_v)
     # routing and attention on the loaded bank match the in-memory one
     q = W.gen_queries(wl, DEV, lq_override=[24])
     q_off = torch.tensor([0, 24], dtype=torch.int32, device=DEV)
@@ -91,13 +93,14 @@ def test_saved_bank_grows_by_appending(tmp_path):
     # the reloaded, grown bank against the oracle
     sh = wl.shape
     for l, ((K, V, Kr), (lKrb, lKb, lVb)) in enumerate(zip(states, final)):
+        kr_rows = key_rows(lKrb)
         for d in (0, cut - 2, cut - 1, cut, cut + 1, len(lens) - 1):
             t0, t1 = int(off[d]), int(off[d + 1])
             c0, c1 = int(coff[d]), int(coff[d + 1])
             oK, oV, oKr, _ = O.pool(f64(K[t0:t1]), f64(V[t0:t1]), f64(Kr[t0:t1]), [0, t1 - t0], sh.chunk,
                                     sh.rope_base, O.ROPE_K)
             rms = max(1.0, float(np.sqrt(np.mean(f64(K[t0:t1]) ** 2))))
-            for g, o, n in ((lKb[c0:c1], oK, "Kbar"), (lVb[c0:c1], oV, "Vbar"), (lKrb[c0:c1], oKr, "Krbar")):
+            for g, o, n in ((lKb[c0:c1], oK, "Kbar"), (lVb[c0:c1], oV, "Vbar"), (kr_rows[c0:c1], oKr, "Krbar")):
                 assert_pool_close(g, o, "bf16", f"layer {l} doc {d} {n} (side {'A' if d < cut else 'B'})",
                                   input_rms=rms)
         ids, sc, ds = M.msa_route_topk(q["Qr"], q_off, 24, lKrb, coff_d, 8, want_doc_scores=True)

@@ -17,7 +17,7 @@ import torch
 import latent_memory_long_amd as M
 from oracle import msa_oracle as O
 from synth import workloads as W
-from tests.helpers import (assert_attn_close, assert_pool_close,
+from tests.helpers import (as_keys, assert_attn_close, assert_pool_close, key_rows,
                            assert_scores_close, assert_topk_consistent, assert_topk_valid, f64,
                            oracle_doc_scores_all, say)
 
@@ -42,6 +42,7 @@ def sample_docs(n_docs, seed, extra=()):
 
 def check_pool_sample(K, V, Kr, off, coff, Kb, Vb, Krb, docs, chunk, base, what):
     """Pool the sampled documents with the oracle and compare their bank rows."""
+    Krb = key_rows(Krb)
     for d in docs:
         t0, t1 = int(off[d]), int(off[d + 1])
         c0, c1 = int(coff[d]), int(coff[d + 1])
@@ -184,13 +185,16 @@ def test_bank100m_host_full():
     lens = W.doc_lengths(wl)
     off = W.token_offsets(lens)
     coff = M.msa_chunk_offsets(off, sh.chunk)
-    Krb, Kb, Vb = W.gen_pooled_bank(wl, coff, DEV, kv_device="cpu-pinned")
+    Krb_rows, Kb, Vb = W.gen_pooled_bank(wl, coff, DEV, kv_device="cpu-pinned")
     assert Kb.is_pinned() and not Kb.is_cuda
+    Krb = as_keys(Krb_rows)
+    Krb_rows = Krb_rows.cpu()   # the oracle's copy of the rows, in host memory
+    torch.cuda.empty_cache()
     q = W.gen_queries(wl, DEV)
     Qr, q_off, ids, sc, ds = run_route(q, coff, Krb, wl.k)
     ids_h = ids.cpu().numpy()[0]
     assert_topk_consistent(ids_h, sc[0], ds[0], wl.k, "bank100m")
-    o = oracle_doc_scores_all(Qr, q_off, Krb, coff, what="bank100m")[0]
+    o = oracle_doc_scores_all(Qr, q_off, Krb_rows, coff, what="bank100m")[0]
     err = assert_scores_close(ds[0], o, "bf16", "bank100m every document score")
     assert_topk_valid(ids_h, o, wl.k, "bank100m top-k vs the oracle's ranking")
     say(f"  bank100m: {len(lens)} docs, {int(coff[-1])} rows; every score, max rel err {err:.3g}")
@@ -211,7 +215,7 @@ def test_bank100m_host_full():
         i1 = ids1.cpu().numpy()[0]
         d1 = ds1.cpu().numpy()[0]
         assert_topk_consistent(i1, sc1.cpu().numpy()[0], d1, wl.k, f"decode {s}")
-        o1 = oracle_doc_scores_all(q["Qr"][r:r + 1], [0, 1], Krb, coff, what=f"decode {s}")[0]
+        o1 = oracle_doc_scores_all(q["Qr"][r:r + 1], [0, 1], Krb_rows, coff, what=f"decode {s}")[0]
         assert_scores_close(d1, o1, "bf16", f"decode {s} every document score")
         assert_topk_valid(i1, o1, wl.k, f"decode {s} top-k vs the oracle's ranking")
         sel = [int(d) for d in i1 if d >= 0]
@@ -251,7 +255,7 @@ def test_batch32_bank10m_full():
     picked = sorted(picked)
     sub_rows = [Qr[q_off[b]:q_off[b + 1]] for b in picked]
     sub_off = np.concatenate([[0], np.cumsum([int(q_off[b + 1] - q_off[b]) for b in picked])])
-    o = oracle_doc_scores_all(torch.cat(sub_rows), sub_off, Krb, coff, what="batch32")
+    o = oracle_doc_scores_all(torch.cat(sub_rows), sub_off, Krb.rows(), coff, what="batch32")
     for i, b in enumerate(picked):
         err = assert_scores_close(ds[b], o[i], "bf16", f"batch query {b} every document score")
         assert_topk_valid(ids_h[b], o[i], wl.k, f"batch query {b} top-k vs the oracle's ranking")
@@ -272,7 +276,8 @@ def test_batch32_bank10m_training_full():
     lens = W.doc_lengths(wl)
     coff = M.msa_chunk_offsets(W.token_offsets(lens), sh.chunk)
     N, C = len(lens), int(coff[-1])
-    Krb, Kb, Vb = W.gen_pooled_bank(wl, coff, DEV)
+    Krb_rows, Kb, Vb = W.gen_pooled_bank(wl, coff, DEV)
+    Krb = as_keys(Krb_rows)
     coff_d = torch.tensor(coff, device=DEV)
     q = W.gen_queries(wl, DEV)
     q_len = q["q_len"]
@@ -298,7 +303,7 @@ def test_batch32_bank10m_training_full():
     cand = sample_docs(N, 21)[:30]
     keep = []
     for d in cand:
-        s = np.sort(O.token_chunk_scores(Qb64, f64(Krb[int(coff[d]):int(coff[d + 1])])).ravel())[::-1]
+        s = np.sort(O.token_chunk_scores(Qb64, f64(Krb_rows[int(coff[d]):int(coff[d + 1])])).ravel())[::-1]
         if s.size == 1 or s[0] - s[1] >= 5e-3:
             keep.append(d)
     assert len(keep) >= 10, keep
@@ -336,7 +341,7 @@ def test_batch32_bank10m_training_full():
     cnt_r = [int(coff[d + 1] - coff[d]) for d in keep]
     coff_r = np.concatenate([[0], np.cumsum(cnt_r)])
     idx_r = torch.as_tensor(np.concatenate([np.arange(coff[d], coff[d + 1]) for d in keep]), device=DEV)
-    rq, rk = O.route_backward(Qb64, [0, L], f64(Krb[idx_r]), coff_r, dvals.double().numpy()[None])
+    rq, rk = O.route_backward(Qb64, [0, L], f64(Krb_rows[idx_r]), coff_r, dvals.double().numpy()[None])
     for gg, oo, n in ((f64(dQr[r0:r1]), rq, "dQr"), (f64(dKr[idx_r]), rk, "dKrbar")):
         top = float(np.max(np.abs(oo)))
         err = float(np.max(np.abs(gg - oo)))

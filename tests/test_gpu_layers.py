@@ -11,7 +11,7 @@ import torch
 import latent_memory_long_amd as M
 from oracle import msa_oracle as O
 from synth import workloads as W
-from tests.helpers import (assert_attn_close, assert_scores_close, assert_topk_consistent,
+from tests.helpers import (as_keys, assert_attn_close, assert_scores_close, assert_topk_consistent,
                            assert_topk_valid, f64, say)
 
 pytestmark = pytest.mark.gpu
@@ -26,7 +26,8 @@ def _layers(n_layers, n_docs, lq, seed=5):
     banks, queries = [], []
     for l in range(n_layers):
         wl_l = W.layer(wl, l)
-        banks.append(W.gen_pooled_bank(wl_l, coff, DEV))
+        Krb, Kb, Vb = W.gen_pooled_bank(wl_l, coff, DEV)
+        banks.append((as_keys(Krb), Kb, Vb))
         queries.append(W.gen_queries(wl_l, DEV, lq_override=[lq]))
     return wl, coff, banks, queries
 

@@ -10,8 +10,9 @@ import torch
 import latent_memory_long_amd as M
 from oracle import msa_oracle as O
 from synth import workloads as W
-from tests.helpers import (assert_attn_close, assert_pool_close, assert_scores_close,
-                           assert_topk_consistent, assert_topk_valid, f64, oracle_doc_scores_all, say)
+from tests.helpers import (as_keys, assert_attn_close, assert_pool_close, assert_scores_close,
+                           assert_topk_consistent, assert_topk_valid, f64, key_rows, oracle_doc_scores_all,
+                           say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -41,7 +42,8 @@ def _reset_env():
 
 def random_bank(n_chunks_per_doc, heads, d, dtype, seed, doc_std=0.5):
     """Pooled-looking bank: per-document offset plus noise, rows of each document
-    contiguous.  Returns (chunk_off host, tensor [C, heads, d] on the GPU)."""
+    contiguous.  Returns (chunk_off host, row-major tensor [C, heads, d] on the GPU); routing
+    calls take it through as_keys (the library's bank layout)."""
     counts = np.asarray(n_chunks_per_doc, dtype=np.int64)
     coff = np.concatenate([[0], np.cumsum(counts)])
     mu = _cpu_randn((len(counts), heads, d), seed, doc_std)
@@ -53,7 +55,7 @@ def random_bank(n_chunks_per_doc, heads, d, dtype, seed, doc_std=0.5):
 def route(Qr, q_lens, Krb, coff, k, want=True):
     q_off = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]), dtype=torch.int32, device=DEV)
     coff_d = torch.tensor(coff, dtype=torch.int64, device=DEV)
-    ids, sc, ds = M.msa_route_topk(Qr, q_off, int(max(q_lens)), Krb, coff_d, k, want_doc_scores=want)
+    ids, sc, ds = M.msa_route_topk(Qr, q_off, int(max(q_lens)), as_keys(Krb), coff_d, k, want_doc_scores=want)
     torch.cuda.synchronize()
     return ids.cpu().numpy(), sc.cpu().numpy(), (ds.cpu().numpy() if ds is not None else None)
 
@@ -153,7 +155,7 @@ def test_pool_constant_chunk_bit_exact_and_doc_restart():
     Kb, Vb, Krb = M.msa_pool(K.to(DEV), K.to(DEV), K.to(DEV), torch.tensor(off, device=DEV),
                              torch.tensor(coff, device=DEV), int(coff[-1]), 64, 1e6, 1)
     torch.cuda.synchronize()
-    Vb, Kb, Krb = Vb.cpu(), Kb.cpu(), Krb.cpu()
+    Vb, Kb, Krb = Vb.cpu(), Kb.cpu(), Krb.rows().cpu()
     # constant chunks (rows 1, 2 of document 1 and document 2) pool to the value itself
     for r in (1, 2, 3):
         assert torch.equal(Vb[r], v[0]) and torch.equal(Krb[r], v[0])
@@ -163,8 +165,9 @@ def test_pool_constant_chunk_bit_exact_and_doc_restart():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_pool_append_equals_pool_at_once(dtype):
-    # A bank grown by appending documents (msa_pool on the new documents, writing after the
-    # existing rows) holds the same bits as the bank pooled in one call, and routes the same.
+    # A bank grown by appending documents (msa_pool on the new documents with offsets that
+    # start after the existing rows) holds the same bits as the bank pooled in one call, and
+    # routes the same.
     say(f"case pool append {dtype}")
     rng = np.random.default_rng(21)
     lens = rng.integers(1, 900, size=60).astype(np.int64)
@@ -178,20 +181,24 @@ def test_pool_append_equals_pool_at_once(dtype):
     coff = M.msa_chunk_offsets(off, 64)
     C = int(coff[-1])
     whole = M.msa_pool(K, V, Kr, torch.tensor(off, device=DEV), torch.tensor(coff, device=DEV), C)
-    # first the documents before `cut`, then the rest appended after their rows
+    # first the documents before `cut`, then the rest pooled into the same bank after their
+    # rows (offsets that start at the rows the bank already holds)
     offA, offB = off[:cut + 1], off[cut:] - off[cut]
-    coffA, coffB = M.msa_chunk_offsets(offA, 64), M.msa_chunk_offsets(offB, 64)
+    coffA = M.msa_chunk_offsets(offA, 64)
     CA = int(coffA[-1])
-    bank = tuple(torch.empty_like(x) for x in whole)
-    M.msa_pool(K[:off[cut]], V[:off[cut]], Kr[:off[cut]], torch.tensor(offA, device=DEV),
-               torch.tensor(coffA, device=DEV), CA, out=tuple(x[:CA] for x in bank))
+    coffB = M.msa_chunk_offsets(offB, 64) + CA
+    partA = M.msa_pool(K[:off[cut]], V[:off[cut]], Kr[:off[cut]], torch.tensor(offA, device=DEV),
+                       torch.tensor(coffA, device=DEV), CA)
+    bank = (torch.empty_like(whole[0]), torch.empty_like(whole[1]), partA[2].grown(C))
+    bank[0][:CA].copy_(partA[0])
+    bank[1][:CA].copy_(partA[1])
     tB = slice(int(off[cut]), T)
     M.msa_pool(K[tB], V[tB], Kr[tB], torch.tensor(offB, device=DEV), torch.tensor(coffB, device=DEV),
-               C - CA, out=tuple(x[CA:] for x in bank))
+               C - CA, out=bank)
     torch.cuda.synchronize()
-    assert np.array_equal(np.concatenate([coffA, CA + coffB[1:]]), coff)
-    for x, y, n in zip(whole, bank, ("Kbar", "Vbar", "Krbar")):
-        assert torch.equal(x, y), f"{dtype} {n}: appended bank differs"
+    assert np.array_equal(np.concatenate([coffA, coffB[1:]]), coff)
+    assert torch.equal(whole[0], bank[0]) and torch.equal(whole[1], bank[1]), f"{dtype}: appended K-bar/V-bar differ"
+    assert whole[2].equal(bank[2]), f"{dtype}: appended routing keys differ (padding included)"
     if dtype == "bf16":
         Qr = _cpu_randn((40, h, d), 34).to(torch.bfloat16).to(DEV)
         a = route(Qr, [40], whole[2], coff, 8)
@@ -310,7 +317,7 @@ def test_route_batch_kernel_edges(heads, n_rows):
     q_lens = [1, 0, 16, 17, 33]
     Qr = _cpu_randn((sum(q_lens), heads, 128), 71).to(torch.bfloat16)
     q_off = np.concatenate([[0], np.cumsum(q_lens)])
-    ds = M.msa_route_scan(Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), 33, Krb,
+    ds = M.msa_route_scan(Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), 33, as_keys(Krb),
                           torch.tensor(coff, device=DEV))
     torch.cuda.synchronize()
     ds = ds.cpu().numpy()
@@ -367,12 +374,13 @@ def test_route_scan_window_carry(h_r, with_rows):
     if with_rows:
         rows = (torch.empty((2, C), dtype=torch.float32, device=DEV), torch.empty((2, C), dtype=torch.int32, device=DEV))
     # one call per query (a single query keeps the plain part order), then both together
+    keys = as_keys(Krb)
     per_q = []
     for b in range(2):
         one = torch.tensor([0, q_lens[b]], dtype=torch.int32, device=DEV)
-        per_q.append(M.msa_route_scan(Qr[q_off[b]:q_off[b + 1]].to(DEV), one, q_lens[b], Krb, coff_d).cpu().numpy()[0])
+        per_q.append(M.msa_route_scan(Qr[q_off[b]:q_off[b + 1]].to(DEV), one, q_lens[b], keys, coff_d).cpu().numpy()[0])
     Qr_d = Qr.to(DEV)
-    ds = M.msa_route_scan(Qr_d, q_off_d, max(q_lens), Krb, coff_d, rows=rows)
+    ds = M.msa_route_scan(Qr_d, q_off_d, max(q_lens), keys, coff_d, rows=rows)
     ids, sc = M.msa_topk(ds, 16)
     torch.cuda.synchronize()
     ds, ids, sc = ds.cpu().numpy(), ids.cpu().numpy(), sc.cpu().numpy()
@@ -531,7 +539,7 @@ def test_route_scan_alone_and_empty_query():
     q_off = np.concatenate([[0], np.cumsum(q_lens)])
     for path in ("auto", "dot", "mfma", "batch"):
         _route_env(path)
-        ds = M.msa_route_scan(Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), 20, Krb,
+        ds = M.msa_route_scan(Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), 20, as_keys(Krb),
                               torch.tensor(coff, device=DEV))
         ids, sc = M.msa_topk(ds, 4)
         torch.cuda.synchronize()

@@ -15,7 +15,7 @@ import torch
 
 import latent_memory_long_amd as M
 from oracle import msa_oracle as O
-from tests.helpers import SCORE_FLOOR, SCORE_RTOL, assert_scores_close, f64, say
+from tests.helpers import SCORE_FLOOR, SCORE_RTOL, as_keys, assert_scores_close, f64, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -79,7 +79,7 @@ def _run(q_lens, counts, H, D, dtype, seed, path="auto", zero_heads=False, dKini
         os.environ["MSA_ROUTE_PATH"] = path
     init = _randn((C, H, D), seed + 4) if dKinit else torch.zeros((C, H, D))
     dK = init.to(DEV)
-    args = (Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), int(max(max(q_lens), 1)), Kb.to(DEV),
+    args = (Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), int(max(max(q_lens), 1)), as_keys(Kb.to(DEV)),
             torch.tensor(coff, dtype=torch.int64, device=DEV))
     rows = _scan_rows(*args, B, N, C)[1] if use_rows else None
     dQr, dK = M.msa_route_backward(*args, torch.tensor(dD, dtype=torch.float32, device=DEV), dKrbar=dK, rows=rows)
@@ -160,7 +160,7 @@ def test_scan_row_outputs(case):
     Qr = _randn((int(q_off[-1]), H, D), len(name) + 6).to(torch_dt)
     if path != "auto":
         os.environ["MSA_ROUTE_PATH"] = path
-    args = (Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), int(max(q_lens)), Kb.to(DEV),
+    args = (Qr.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV), int(max(q_lens)), as_keys(Kb.to(DEV)),
             torch.tensor(coff, dtype=torch.int64, device=DEV))
     ds_rows, (rs, ra) = _scan_rows(*args, B, N, C)
     ds = M.msa_route_scan(*args)
@@ -240,7 +240,7 @@ def test_route_training_chain():
     Y[[0, 1, 2], [3, 0, 6]] = 1.0
     qo = torch.tensor(q_off, dtype=torch.int32, device=DEV)
     co = torch.tensor(coff, dtype=torch.int64, device=DEV)
-    Qd, Kd = Qr.to(DEV), Kb.to(DEV)
+    Qd, Kd = Qr.to(DEV), as_keys(Kb.to(DEV))
     S = M.msa_route_scan(Qd, qo, max(q_lens), Kd, co)
     loss, dD = M.msa_route_aux_loss(S, torch.tensor(Y, device=DEV), M.MSA_AUX_INFONCE, 0.1)
     dQr, dK = M.msa_route_backward(Qd, qo, max(q_lens), Kd, co, dD)

@@ -12,7 +12,7 @@ import torch
 
 import latent_memory_long_amd as M
 from synth import workloads as W
-from tests.helpers import say
+from tests.helpers import as_keys, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -26,7 +26,8 @@ class TrainStep:
         coff = M.msa_chunk_offsets(W.token_offsets(lens), sh.chunk)
         self.N, self.C = len(lens), int(coff[-1])
         self.coff = torch.tensor(coff, device=DEV)
-        self.Krb, self.Kb, self.Vb = W.gen_pooled_bank(wl, coff, DEV)
+        Krb, self.Kb, self.Vb = W.gen_pooled_bank(wl, coff, DEV)
+        self.Krb = as_keys(Krb)
         q = W.gen_queries(wl, DEV)
         self.q = q
         q_len = q["q_len"]

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import latent_memory_long_amd as M
-from tests.helpers import say
+from tests.helpers import as_keys, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -66,7 +66,7 @@ def test_valid_inputs_unchanged(validate, monkeypatch):
     o = M.msa_sparse_attn(Q, Kl, Vl, q_off, kv_off, 6, ids, _i64(coff), off_[0], off_[1])
     torch.cuda.synchronize()
     for a, b in zip(on + (ids_on, sc_on, ds_on, o_on), off_ + (ids, sc, ds, o)):
-        assert torch.equal(a, b)
+        assert a.equal(b) if isinstance(a, M.RouteKeys) else torch.equal(a, b)
 
 
 def test_pool_offsets_refused(validate):
@@ -86,7 +86,7 @@ def test_pool_offsets_refused(validate):
 def test_route_offsets_refused(validate):
     say("case validation: bad routing offsets")
     lens, off, coff, K, V, Kr = _setup()
-    Krb = _rand((int(coff[-1]), 4, 64), 8)
+    Krb = as_keys(_rand((int(coff[-1]), 4, 64), 8))
     Qr = _rand((9, 4, 64), 9)
     # a query longer than max_q_len
     _refused(lambda: M.msa_route_scan(Qr, _i32([0, 6, 9]), 4, Krb, _i64(coff)), "more than max_q_len 4")
