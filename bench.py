@@ -45,11 +45,11 @@ SCAN_KERNEL = "route_scan_mfma"
 # HBM traffic of the scan kernel per launch, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # on this workload (scaled by the counters' reading of a copy kernel of known size).  It is
 # reported only while the kernel source still has the digest it was measured with.
-TRAFFIC = {"route_sha": "00e317962530e847",
-           # FETCH_SIZE 1,588,789 KiB per launch x 1.99995 (a 1 GiB copy reads 524,301 KiB)
-           "fetch_bytes": 3253751574,
-           # WRITE_SIZE 199.22 KiB per launch x 1.0 (a 1 GiB copy writes 1,048,576 KiB)
-           "write_bytes": 204000}
+TRAFFIC = {"route_sha": "8980c242f2a1ffd2",
+           # FETCH_SIZE 1,594,751 KiB per launch x 1.99993 (a 1 GiB copy reads 524,306 KiB)
+           "fetch_bytes": 3265940121,
+           # WRITE_SIZE 214.8 KiB per launch x 1.0 (a 1 GiB copy writes 1,048,576 KiB)
+           "write_bytes": 219968}
 
 
 def log(msg):
@@ -462,13 +462,17 @@ def main():
     T = int(off[-1])
     coff_d = torch.tensor(coff, device=dev)
     if args.copy_calibration:
+        # kernels of known traffic for scaling hardware byte counters: a device-to-device
+        # copy (the runtime's copy kernel) and an elementwise kernel (read n, write n bytes)
         n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log(f"copy calibration: 3 copies of {n} bytes")
+        log(f"copy calibration: 3 copies and 3 elementwise negations of {n} bytes")
         del src, dst
     qs = make_queries(wl, dev, args.queries)
     Lq = int(qs[0]["q_len"][0])

@@ -337,15 +337,26 @@ def _scan_parts(coff, parts):
     return [(starts[p], starts[p + 1]) for p in range(parts)]
 
 
-WIN_ROWS = 4096   # rows of one LDS score window of the streaming MFMA scan
+def _window_crossings(coff, parts, win_rows):
+    """Documents whose rows cross a score window of the MFMA scan (windows of win_rows rows
+    from the first 16-row tile of each part), and those spanning three windows or more."""
+    crossing, three = 0, 0
+    for d0, d1 in parts:
+        base = (int(coff[d0]) // 16) * 16
+        w_first = (coff[d0:d1] - base) // win_rows
+        w_last = (coff[d0 + 1:d1 + 1] - 1 - base) // win_rows
+        crossing += int(np.sum(w_last > w_first))
+        three += int(np.sum(w_last - w_first >= 2))
+    return crossing, three
 
 
 @pytest.mark.parametrize("h_r", [1, 2])
 @pytest.mark.parametrize("with_rows", [False, True], ids=["scores", "rows"])
 def test_route_scan_window_carry(h_r, with_rows):
-    # A bank of 1.1M rows: each of the scan's 256 parts holds more than one 4,096-row score
-    # window, so documents cross window boundaries and their running maximum is carried
-    # from one window to the next.  One document of 9,000 rows spans three windows.
+    # A bank of 1.1M rows: each of the scan's 256 parts holds several score windows (2,048
+    # rows, 1,024 with row outputs), so documents cross window boundaries and their running
+    # maximum is carried from one window to the next.  Documents of 4,096 to 9,000 rows
+    # span three windows or more.
     say(f"case route scan window carry h_r={h_r} rows={with_rows}")
     _route_env("mfma")
     rng = np.random.default_rng(300 + h_r)
@@ -355,16 +366,9 @@ def test_route_scan_window_carry(h_r, with_rows):
     coff, Krb = random_bank(counts, h_r, 32, "bf16", 310 + h_r)
     C = int(coff[-1])
     # the launch takes 256 parts here: check on the host that the carry is reached
-    parts = _scan_parts(coff, 256)
-    crossing, three = 0, 0
-    for d0, d1 in parts:
-        base = int(coff[d0])
-        w_first = (coff[d0:d1] - base) // WIN_ROWS
-        w_last = (coff[d0 + 1:d1 + 1] - 1 - base) // WIN_ROWS
-        crossing += int(np.sum(w_last > w_first))
-        three += int(np.sum(w_last - w_first >= 2))
-    assert crossing >= 200 and three >= 1, (crossing, three)
-    say(f"  {len(counts)} docs, {C} rows; {crossing} documents cross a window, {three} span three")
+    crossing, three = _window_crossings(coff, _scan_parts(coff, 256), 1024 if with_rows else 2048)
+    assert crossing >= 200 and three >= 4, (crossing, three)
+    say(f"  {len(counts)} docs, {C} rows; {crossing} documents cross a window, {three} span three or more")
     q_lens = [64, 5]
     Qr = (_cpu_randn((sum(q_lens), h_r, 32), 320) + _cpu_randn((1, h_r, 32), 321, 0.5)).to(torch.bfloat16)
     q_off = np.concatenate([[0], np.cumsum(q_lens)])
