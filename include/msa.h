@@ -216,6 +216,29 @@ msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                           int32_t* topk_ids, float* topk_scores, float* doc_scores,
                           void* workspace, size_t workspace_bytes, msa_stream_t stream);
 
+/* Scratch that msa_route_topk_noalloc holds per device (16 MiB). */
+#define MSA_ROUTE_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * msa_route_topk_noalloc -- msa_route_topk for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments and results, without a workspace.  Its scratch (the document scores when
+ * doc_scores is NULL, and the top-k candidates; msa_route_topk_workspace() bytes, or
+ * msa_topk_workspace() bytes with doc_scores given) lives in a device array of
+ * MSA_ROUTE_TOPK_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends; larger inputs return MSA_ERR_WORKSPACE.  Nothing is allocated
+ * (no hipMalloc/hipFree); the array's device address is looked up on the first call on a
+ * device.  Every call on a device shares that device's array and leaves its contents
+ * behind: calls that overlap on one device (other streams or threads) race.  The debug
+ * validation of MSA_DEBUG_VALIDATE is not run here (it copies offsets into host buffers).
+ */
+msa_status msa_route_topk_noalloc(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                                  const int32_t* q_off, int32_t max_q_len, const void* Qr,
+                                  int32_t h_r, int32_t d, int32_t n_docs, int64_t n_chunks,
+                                  const int64_t* chunk_off, const void* Krbar, int32_t k,
+                                  int32_t* topk_ids, float* topk_scores, float* doc_scores,
+                                  msa_stream_t stream);
+
 /* Bytes of workspace msa_route_backward needs for these sizes (0 if unsupported). */
 size_t msa_route_backward_workspace(int32_t n_queries, int32_t n_docs, int64_t n_chunks,
                                     int32_t h_r);

@@ -15,4 +15,5 @@ from .binding import (  # noqa: F401
     MSA_ERR_IO, msa_bank_save, msa_bank_read_info, msa_bank_load,
     MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP,
     RouteKeys, msa_krbar_elems, msa_krbar_pack, msa_krbar_unpack,
+    msa_route_topk_noalloc, MSA_ROUTE_TOPK_NOALLOC_SCRATCH_BYTES,
 )

@@ -59,6 +59,8 @@ def _load() -> ctypes.CDLL:
         "msa_topk_workspace": (SZ, [I32, I32, I32]),
         "msa_topk": (ctypes.c_int, [I32, I32, P, I32, P, P, P, SZ, P]),
         "msa_route_topk_workspace": (SZ, [I32, I32, I32]),
+        "msa_route_topk_noalloc": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
+                                                  P, I32, P, P, P, P]),
         "msa_route_topk": (ctypes.c_int, [ctypes.c_int, I32, I64, P, I32, P, I32, I32, I32, I64, P,
                                           P, I32, P, P, P, P, SZ, P]),
         "msa_sparse_attn_workspace": (SZ, [ctypes.c_int, I32, I64, I64, I32, I32, I32, I32]),
@@ -451,6 +453,33 @@ def msa_route_topk(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar:
                               Krbar.h_r, Krbar.d, N, Krbar.n_chunks, _ptr(chunk_off),
                               _ptr(Krbar.data), k, _ptr(ids), _ptr(sc), _ptr(ds), _ptr(ws), wsb,
                               _stream(stream)))
+    return ids, sc, ds
+
+
+MSA_ROUTE_TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def msa_route_topk_noalloc(Qr: torch.Tensor, q_off: torch.Tensor, max_q_len: int, Krbar, chunk_off: torch.Tensor,
+                           k: int, want_doc_scores: bool = False, out=None, stream=None):
+    """msa_route_topk without a workspace: the library's per-device scratch array serves
+    instead (MSA_ROUTE_TOPK_NOALLOC_SCRATCH_BYTES; larger inputs raise MSA_ERR_WORKSPACE).
+    Pass `out` = (topk_ids, topk_scores, doc_scores or None) to allocate nothing here either."""
+    Krbar = _keys(Krbar)
+    B, N = _route_inputs(Qr, q_off, Krbar, chunk_off)
+    dev = Krbar.device
+    if out is None:
+        out = (torch.empty((B, k), dtype=torch.int32, device=dev),
+               torch.empty((B, k), dtype=torch.float32, device=dev),
+               torch.empty((B, N), dtype=torch.float32, device=dev) if want_doc_scores else None)
+    ids, sc, ds = out
+    _need(ids, "topk_ids", torch.int32, (B, k))
+    _need(sc, "topk_scores", torch.float32, (B, k))
+    if ds is not None:
+        _need(ds, "doc_scores", torch.float32, (B, N))
+    _route_devices(Qr, q_off, Krbar, chunk_off, ("topk_ids", ids), ("topk_scores", sc), ("doc_scores", ds))
+    _check(lib.msa_route_topk_noalloc(_dtype_code(Krbar.data), B, Qr.shape[0], _ptr(q_off), max_q_len, _ptr(Qr),
+                                      Krbar.h_r, Krbar.d, N, Krbar.n_chunks, _ptr(chunk_off), _ptr(Krbar.data), k,
+                                      _ptr(ids), _ptr(sc), _ptr(ds), _stream(stream)))
     return ids, sc, ds
 
 

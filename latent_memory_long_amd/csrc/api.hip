@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/msa.h"
@@ -229,6 +230,38 @@ msa_status msa_topk(int32_t n_queries, int32_t n_docs, const float* doc_scores, 
   return hip_status(msa::launch_topk(t, workspace, (hipStream_t)stream), "msa_topk launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// msa_route_topk after validation, with a workspace of at least route_topk_need() bytes.
+msa_status route_topk_run(msa_dtype dtype, int32_t n_queries, int64_t total_q, const int32_t* q_off,
+                          int32_t max_q_len, const void* Qr, int32_t h_r, int32_t d, int32_t n_docs,
+                          int64_t n_chunks, const int64_t* chunk_off, const void* Krbar, int32_t k,
+                          int32_t* topk_ids, float* topk_scores, float* doc_scores, void* workspace,
+                          msa_stream_t stream) {
+  // workspace: [document scores when doc_scores is NULL][top-k candidates]
+  const size_t score_bytes = doc_scores ? 0 : msa::align256((size_t)n_queries * n_docs * sizeof(float));
+  float* scores = doc_scores ? doc_scores : (float*)workspace;
+  void* topk_ws = msa::topk_workspace_bytes(n_queries, n_docs, k) ? (void*)((char*)workspace + score_bytes) : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  msa::RouteArgs r{(int)dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
+                   chunk_off, Krbar, scores, route_path_override()};
+  msa_status st = hip_status(msa::launch_route_scan(r, s), "msa_route_topk scan launch");
+  if (st != MSA_OK) return st;
+  msa::TopkArgs t{n_queries, n_docs, k, scores, topk_ids, topk_scores};
+  return hip_status(msa::launch_topk(t, topk_ws, s), "msa_route_topk top-k launch");
+}
+
+size_t route_topk_need(int32_t n_queries, int32_t n_docs, int32_t k, const float* doc_scores) {
+  const size_t score_bytes = doc_scores ? 0 : msa::align256((size_t)n_queries * n_docs * sizeof(float));
+  return score_bytes + msa::topk_workspace_bytes(n_queries, n_docs, k);
+}
+
+}  // namespace
+
+extern "C" {
+
 msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                           const int32_t* q_off, int32_t max_q_len, const void* Qr, int32_t h_r,
                           int32_t d, int32_t n_docs, int64_t n_chunks, const int64_t* chunk_off,
@@ -241,20 +274,77 @@ msa_status msa_route_topk(msa_dtype dtype, int32_t n_queries, int64_t total_q,
   if (st != MSA_OK) return st;
   st = check_topk(n_queries, n_docs, k, topk_ids, topk_scores);
   if (st != MSA_OK) return st;
-  // workspace: [document scores when doc_scores is NULL][top-k candidates]
-  const size_t score_bytes = doc_scores ? 0 : msa::align256((size_t)n_queries * n_docs * sizeof(float));
-  const size_t need = score_bytes + msa::topk_workspace_bytes(n_queries, n_docs, k);
+  const size_t need = route_topk_need(n_queries, n_docs, k, doc_scores);
   if (need && (!workspace || workspace_bytes < need)) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   if (need && ((uintptr_t)workspace & 255u) != 0) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  float* scores = doc_scores ? doc_scores : (float*)workspace;
-  void* topk_ws = need ? (void*)((char*)workspace + score_bytes) : nullptr;
-  hipStream_t s = (hipStream_t)stream;
-  msa::RouteArgs r{(int)dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks,
-                   chunk_off, Krbar, scores, route_path_override()};
-  st = hip_status(msa::launch_route_scan(r, s), "msa_route_topk scan launch");
+  return route_topk_run(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks, chunk_off, Krbar,
+                        k, topk_ids, topk_scores, doc_scores, need ? workspace : nullptr, stream);
+}
+
+}  // extern "C"
+
+// ---- the router without allocation -----------------------------------------------------
+// msa_route_topk_noalloc keeps its scratch (document scores when the caller passes none, and
+// the top-k candidates) in a file-scope device array instead of a caller workspace.  Each
+// device holds its own copy of the array for the life of the process; in host code the
+// array's name is only a handle, so its device address is looked up once per device and
+// kept.  Calls that overlap on one device share the array and race.
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = MSA_ROUTE_TOPK_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's scratch address (looked up with that device current, on its first use).
+msa_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(MSA_ERR_UNSUPPORTED, "device %d: the library tracks devices 0..%d", dev, MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress of the scratch array");
+    if (!p) return fail(MSA_ERR_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_route_topk_noalloc(msa_dtype dtype, int32_t n_queries, int64_t total_q,
+                                  const int32_t* q_off, int32_t max_q_len, const void* Qr, int32_t h_r,
+                                  int32_t d, int32_t n_docs, int64_t n_chunks, const int64_t* chunk_off,
+                                  const void* Krbar, int32_t k, int32_t* topk_ids, float* topk_scores,
+                                  float* doc_scores, msa_stream_t stream) {
+  g_last_error.clear();
+  // host checks only: the opt-in debug validation copies offsets into host buffers
+  msa_status st = check_route(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks, chunk_off,
+                              Krbar);
   if (st != MSA_OK) return st;
-  msa::TopkArgs t{n_queries, n_docs, k, scores, topk_ids, topk_scores};
-  return hip_status(msa::launch_topk(t, topk_ws, s), "msa_route_topk top-k launch");
+  st = check_topk(n_queries, n_docs, k, topk_ids, topk_scores);
+  if (st != MSA_OK) return st;
+  const size_t need = route_topk_need(n_queries, n_docs, k, doc_scores);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(MSA_ERR_WORKSPACE,
+                "%d queries x %d documents need %zu bytes of scratch, more than the %zu this entry point holds "
+                "(pass doc_scores, or call msa_route_topk with a workspace)",
+                n_queries, n_docs, need, NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need) {
+    st = scratch_address(&ws);
+    if (st != MSA_OK) return st;
+  }
+  return route_topk_run(dtype, n_queries, total_q, q_off, max_q_len, Qr, h_r, d, n_docs, n_chunks, chunk_off, Krbar,
+                        k, topk_ids, topk_scores, doc_scores, ws, stream);
 }
 
 size_t msa_route_backward_workspace(int32_t n_queries, int32_t n_docs, int64_t n_chunks, int32_t h_r) {
