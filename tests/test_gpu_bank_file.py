@@ -13,7 +13,7 @@ import latent_memory_long_amd as M
 from oracle import msa_oracle as O
 from synth import workloads as W
 from tests.helpers import (assert_attn_close, assert_pool_close, assert_scores_close, assert_topk_consistent,
-                           assert_topk_valid, f64, key_rows, say)
+                           assert_topk_valid, f64, key_rows, pool_error_bound, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -97,12 +97,12 @@ def test_saved_bank_grows_by_appending(tmp_path):
         for d in (0, cut - 2, cut - 1, cut, cut + 1, len(lens) - 1):
             t0, t1 = int(off[d]), int(off[d + 1])
             c0, c1 = int(coff[d]), int(coff[d + 1])
-            oK, oV, oKr, _ = O.pool(f64(K[t0:t1]), f64(V[t0:t1]), f64(Kr[t0:t1]), [0, t1 - t0], sh.chunk,
-                                    sh.rope_base, O.ROPE_K)
-            rms = max(1.0, float(np.sqrt(np.mean(f64(K[t0:t1]) ** 2))))
-            for g, o, n in ((lKb[c0:c1], oK, "Kbar"), (lVb[c0:c1], oV, "Vbar"), (kr_rows[c0:c1], oKr, "Krbar")):
+            xs = (f64(K[t0:t1]), f64(V[t0:t1]), f64(Kr[t0:t1]))
+            oK, oV, oKr, _ = O.pool(*xs, [0, t1 - t0], sh.chunk, sh.rope_base, O.ROPE_K)
+            for g, o, x, rot, n in ((lKb[c0:c1], oK, xs[0], True, "Kbar"), (lVb[c0:c1], oV, xs[1], False, "Vbar"),
+                                    (kr_rows[c0:c1], oKr, xs[2], False, "Krbar")):
                 assert_pool_close(g, o, "bf16", f"layer {l} doc {d} {n} (side {'A' if d < cut else 'B'})",
-                                  input_rms=rms)
+                                  pool_error_bound(x, [0, t1 - t0], sh.chunk, rot))
         ids, sc, ds = M.msa_route_topk(q["Qr"], q_off, 24, lKrb, coff_d, 8, want_doc_scores=True)
         out = M.msa_sparse_attn(q["Q"], q["Kloc"], q["Vloc"], q_off, q_off, 24, ids, coff_d, lKb, lVb,
                                 rope_base=sh.rope_base)

@@ -17,7 +17,7 @@ import torch
 import latent_memory_long_amd as M
 from oracle import msa_oracle as O
 from synth import workloads as W
-from tests.helpers import (as_keys, assert_attn_close, assert_pool_close, key_rows,
+from tests.helpers import (as_keys, assert_attn_close, assert_pool_close, key_rows, pool_error_bound,
                            assert_scores_close, assert_topk_consistent, assert_topk_valid, f64,
                            oracle_doc_scores_all, say)
 
@@ -46,11 +46,11 @@ def check_pool_sample(K, V, Kr, off, coff, Kb, Vb, Krb, docs, chunk, base, what)
     for d in docs:
         t0, t1 = int(off[d]), int(off[d + 1])
         c0, c1 = int(coff[d]), int(coff[d + 1])
-        oK, oV, oKr, _ = O.pool(f64(K[t0:t1]), f64(V[t0:t1]), f64(Kr[t0:t1]), [0, t1 - t0], chunk, base,
-                                O.ROPE_K)
-        rms = float(np.sqrt(np.mean(f64(K[t0:t1]) ** 2)))
-        for g, o, n in ((Kb[c0:c1], oK, "Kbar"), (Vb[c0:c1], oV, "Vbar"), (Krb[c0:c1], oKr, "Krbar")):
-            assert_pool_close(g, o, "bf16", f"{what} doc {d} {n}", input_rms=max(rms, 1.0))
+        xs = (f64(K[t0:t1]), f64(V[t0:t1]), f64(Kr[t0:t1]))
+        oK, oV, oKr, _ = O.pool(*xs, [0, t1 - t0], chunk, base, O.ROPE_K)
+        for g, o, x, rot, n in ((Kb[c0:c1], oK, xs[0], True, "Kbar"), (Vb[c0:c1], oV, xs[1], False, "Vbar"),
+                                (Krb[c0:c1], oKr, xs[2], False, "Krbar")):
+            assert_pool_close(g, o, "bf16", f"{what} doc {d} {n}", pool_error_bound(x, [0, t1 - t0], chunk, rot))
 
 
 def token_bank(wl, needle_q=None):

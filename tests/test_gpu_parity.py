@@ -12,7 +12,7 @@ from oracle import msa_oracle as O
 from synth import workloads as W
 from tests.helpers import (as_keys, assert_attn_close, assert_pool_close, assert_scores_close,
                            assert_topk_consistent, assert_topk_valid, f64, key_rows, oracle_doc_scores_all,
-                           say)
+                           pool_error_bound, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -76,8 +76,8 @@ def test_tiny_fp32_end_to_end():
     Kb, Vb, Krb = M.msa_pool(K.to(DEV), V.to(DEV), Kr.to(DEV), off_d, coff_d, C, sh.chunk, sh.rope_base)
     oK, oV, oKr, ocoff = O.pool(f64(K), f64(V), f64(Kr), off, sh.chunk, sh.rope_base, O.ROPE_K)
     assert np.array_equal(ocoff, coff)
-    for g, o, n in ((Kb, oK, "Kbar"), (Vb, oV, "Vbar"), (Krb, oKr, "Krbar")):
-        assert_pool_close(g, o, "f32", n)
+    for g, o, x, rot, n in ((Kb, oK, K, True, "Kbar"), (Vb, oV, V, False, "Vbar"), (Krb, oKr, Kr, False, "Krbar")):
+        assert_pool_close(g, o, "f32", n, pool_error_bound(f64(x), off, sh.chunk, rot))
 
     q = W.gen_queries(wl, "cpu")
     Lq = int(q["q_len"][0])
@@ -136,8 +136,9 @@ def test_pool(case):
                              torch.tensor(coff, device=DEV), C, chunk, 1e6, mask)
     torch.cuda.synchronize()
     oK, oV, oKr, _ = O.pool(f64(K), f64(V), f64(Kr), off, chunk, 1e6, mask)
-    for g, o, n in ((Kb, oK, "Kbar"), (Vb, oV, "Vbar"), (Krb, oKr, "Krbar")):
-        assert_pool_close(g, o, dtype, f"{name} {n}")
+    for g, o, x, bit, n in ((Kb, oK, K, 1, "Kbar"), (Vb, oV, V, 2, "Vbar"), (Krb, oKr, Kr, 4, "Krbar")):
+        r = assert_pool_close(g, o, dtype, f"{name} {n}", pool_error_bound(f64(x), off, chunk, bool(mask & bit)))
+        say(f"  {name} {n}: largest error {r:.3f} of the bound")
 
 
 def test_pool_constant_chunk_bit_exact_and_doc_restart():
