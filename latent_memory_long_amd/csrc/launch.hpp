@@ -18,6 +18,8 @@ struct PoolArgs {
   uint32_t rope_mask;
   const void *K, *V, *Kr;
   void *Kbar, *Vbar, *Krbar;
+  int stage_waves = 0;   // set by the launcher: LDS staging of tiled routing keys
+  int stage_offset = 0;
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 

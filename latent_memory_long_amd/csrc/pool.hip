@@ -7,8 +7,8 @@
 // 64-token chunk into K-bar / V-bar / Kr-bar; a partial last chunk still counts).
 //
 // Design (HBM-bound streaming read, ~6 KB per token for the Qwen3-4B-like layer):
-//  * The token rows are split over workgroups by bytes, each workgroup taking a contiguous
-//    range of whole chunks.  A thread owns one 8-element "unit" of a token row -- 8
+//  * The token rows are split over workgroups by bank rows, each workgroup taking a
+//    contiguous range of whole chunks.  A thread owns one 8-element "unit" of a token row -- 8
 //    consecutive elements, or for a rotated tensor 4 rotation pairs (i..i+3 together with
 //    i+d/2..i+d/2+3) -- and streams its unit through the range token by token, 8 tokens
 //    per batch with the next batch's loads in flight, so the workgroup reads its range as
@@ -27,8 +27,12 @@
 //    pools to itself bit for bit), then rounds once to the storage type.
 //  * Row c of document d's chunk j is chunk_off[d] + j: offsets that start past 0 write new
 //    documents after the rows a bank already holds.  bf16 routing keys are written in the
-//    tiled layout of common.hpp (each thread's 8- or 4-element unit stays one contiguous
-//    store); only the rows of the given documents are written.
+//    tiled layout of common.hpp: workgroup ranges start on multiples of 16 rows, and each
+//    routing-key wave collects 8 consecutive rows in its own 8 KB of LDS, then writes them
+//    as whole 128-byte lines of the tile (16-byte stores per thread scattered over the
+//    tile cost 8% of the pass; this leaves about 1%).  Rows of a group of 8 that a range
+//    shares with the previous bank contents or ends inside go straight out.  Only the rows
+//    of the given documents are written.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -81,16 +85,23 @@ __device__ __forceinline__ int64_t scalar_load_i64(const int64_t* p) {
   return v;
 }
 
-// First token of workgroup range w of W: token T * w / W rounded down to the start of its
-// chunk, so ranges hold whole chunks.  Also returns the document owning that token.
-// Wave-collective.
+// First token of workgroup range w of W.  Range boundaries fall on bank rows that are
+// multiples of 16 (whole tiles of the routing keys; ranges hold whole chunks), spread evenly
+// over the rows written.  Also returns the document owning that token.  Wave-collective.
 __device__ __forceinline__ int64_t range_start(const PoolArgs& a, int64_t w, int64_t W, int& doc) {
   if (w <= 0) { doc = 0; return 0; }
   if (w >= W) { doc = a.n_docs; return a.n_tokens; }
-  const int64_t x = a.n_tokens * w / W;
-  doc = __builtin_amdgcn_readfirstlane(find_doc_wave(a.doc_tok_off, a.n_docs, x));
-  const int64_t t0 = a.doc_tok_off[doc];
-  return t0 + (x - t0) / a.chunk * a.chunk;
+  const int64_t r0 = a.chunk_off[0];
+  const int64_t r = (r0 + a.n_chunks * w / W) & ~(int64_t)15;
+  if (r <= r0) { doc = 0; return 0; }
+  doc = __builtin_amdgcn_readfirstlane(find_doc_wave(a.chunk_off, a.n_docs, r));
+  return a.doc_tok_off[doc] + (r - a.chunk_off[doc]) * a.chunk;
+}
+
+// Bank row of token p, the first token of a chunk of document doc (doc == n_docs: the end).
+__device__ __forceinline__ int64_t row_of(const PoolArgs& a, int64_t p, int doc) {
+  if (doc >= a.n_docs) return a.chunk_off[a.n_docs];
+  return a.chunk_off[doc] + (p - a.doc_tok_off[doc]) / a.chunk;
 }
 
 // State of one thread's stream.  The chunk fields are the same in every thread of the
@@ -104,6 +115,12 @@ struct PoolStream {
   int doc;
   bool tiled;  // destination is a bf16 routing-key bank in the tiled layout
   int heads;   // heads of the destination tensor
+  // Tiled destination staged in LDS, 8 rows at a time (null: stores go straight out).  A
+  // wave's 64 units of a row are 16 whole 512-element blocks of a tile (first_blk ..), so
+  // 8 rows of them fill 16 x 4 whole 128-byte lines of the tile.
+  bf16_t* stage;          // this wave's staging region in LDS
+  int first_blk, n_blk;   // the wave's blocks of a tile row
+  int64_t row0, row1;     // bank rows of the workgroup's range
 };
 
 // Mean of the finished chunk [cst, bnd) -> bank row c, then move to the next chunk.
@@ -124,17 +141,54 @@ __device__ __forceinline__ void pool_flush(PoolStream& st, const PoolArgs& a, T*
   for (int q = 0; q < 8; ++q) st.acc[q] = st.acc[q] / fn;
   // the unit's place in the row: row-major, or (bf16 routing keys) its 16-byte slot of the
   // row's tile, where 4 or 8 consecutive elements of one head stay contiguous
-  int64_t o_lo = st.c * row_elems + e_lo, o_hi = st.c * row_elems + e_hi;
-  if (st.tiled) {
-    o_lo = kr_tiled<D>(st.c, e_lo, st.heads);
-    o_hi = kr_tiled<D>(st.c, e_hi, st.heads);
-  }
-  if (store) {
-    if constexpr (rotate) {
-      Elem<T>::store4(dst + o_lo, st.acc);
-      Elem<T>::store4(dst + o_hi, st.acc + 4);
+  const int64_t grp = st.c & ~(int64_t)7;  // the row's group of 8 rows
+  if constexpr (sizeof(T) == 2) {
+    if (st.stage != nullptr && grp >= st.row0 && grp + 8 <= st.row1) {  // uniform
+      // staged: the group's 8 rows leave together, as whole 128-byte lines of the tile
+      const int r = (int)(st.c & 7);
+      // region element offset of element e of row r: piece (block e/32 of the wave's, group
+      // (e%32)/8, row r), then e%8
+      auto region = [&](int e) { return (((e >> 5) - st.first_blk) * 4 + ((e >> 3) & 3)) * 64 + r * 8 + (e & 7); };
+      if (store) {
+        if constexpr (rotate) {
+          Elem<T>::store4((T*)st.stage + region(e_lo), st.acc);
+          Elem<T>::store4((T*)st.stage + region(e_hi), st.acc + 4);
+        } else {
+          Elem<T>::store8((T*)st.stage + region(e_lo), st.acc);
+        }
+      }
+      if (r == 7) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's staged rows are in LDS
+        const int lane = threadIdx.x & 63;
+        T* tile = dst + (grp >> 4) * ((int64_t)16 * row_elems);
+#pragma unroll 1
+        for (int p = lane; p < st.n_blk * 32; p += 64) {  // 16-byte piece p: block p/32, group (p/8)%4, row p%8
+          const int slot = (st.first_blk + (p >> 5)) * 64 + ((p >> 3) & 3) * 16 + (int)(grp & 15) + (p & 7);
+          *reinterpret_cast<uint4*>(tile + slot * 8) = *reinterpret_cast<const uint4*>((const T*)st.stage + p * 8);
+        }
+      }
     } else {
-      Elem<T>::store8(dst + o_lo, st.acc);
+      const int64_t o_lo = st.tiled ? kr_tiled<D>(st.c, e_lo, st.heads) : st.c * row_elems + e_lo;
+      const int64_t o_hi = st.tiled ? kr_tiled<D>(st.c, e_hi, st.heads) : st.c * row_elems + e_hi;
+      if (store) {
+        if constexpr (rotate) {
+          Elem<T>::store4(dst + o_lo, st.acc);
+          Elem<T>::store4(dst + o_hi, st.acc + 4);
+        } else {
+          Elem<T>::store8(dst + o_lo, st.acc);
+        }
+      }
+    }
+  } else {
+    (void)grp;
+    const int64_t o_lo = st.c * row_elems + e_lo, o_hi = st.c * row_elems + e_hi;
+    if (store) {
+      if constexpr (rotate) {
+        Elem<T>::store4(dst + o_lo, st.acc);
+        Elem<T>::store4(dst + o_hi, st.acc + 4);
+      } else {
+        Elem<T>::store8(dst + o_lo, st.acc);
+      }
     }
   }
 #pragma unroll
@@ -205,10 +259,16 @@ __device__ __forceinline__ void pool_batch(PoolStream& st, const Raw<T> (&X)[PT]
 template <bool rotate, typename T, int D>
 __device__ __forceinline__ void pool_stream(const PoolArgs& a, const T* src, T* dst, int64_t p0, int64_t p1,
                                             int doc0, int row_elems, int e_lo, int e_hi, int i0, bool valid,
-                                            const float* rope_tab, bool tiled) {
+                                            const float* rope_tab, bool tiled, bf16_t* stage, int first_unit,
+                                            int n_units, int64_t row0, int64_t row1) {
   PoolStream st;
   st.tiled = tiled;
   st.heads = row_elems / D;
+  st.stage = stage;
+  st.row0 = __builtin_amdgcn_readfirstlane(row0);
+  st.row1 = __builtin_amdgcn_readfirstlane(row1);
+  st.first_blk = first_unit / 4;
+  st.n_blk = (n_units + 3) / 4;
 #pragma unroll
   for (int q = 0; q < 8; ++q) st.acc[q] = 0.f;
   st.doc = doc0;
@@ -284,6 +344,14 @@ __global__ __launch_bounds__(512) void pool_kernel(PoolArgs a) {
   const int i0 = piece * 4;      // first pair index when rotating
   const int row_elems = heads * D;
 
+  // LDS: the table below, then (bf16 routing keys) 8 KB of staging per routing-key wave
+  bf16_t* stage = nullptr;
+  if (sizeof(T) == 2 && tensor == 2 && a.stage_waves > 0) {
+    const int kr_first = max(2 * wk, (int)blockIdx.y * (int)(blockDim.x >> 6));  // first routing-key wave here
+    stage = reinterpret_cast<bf16_t*>(reinterpret_cast<unsigned char*>(rope_tab) + a.stage_offset) +
+            (size_t)(gw - kr_first) * (8 * 64 * 8);
+  }
+
   // Per-workgroup table of R(r): angles r * theta_i, r < chunk, in double precision.
   if (a.rope_mask) {
     for (int e = tid; e < a.chunk * half; e += blockDim.x) {
@@ -304,8 +372,14 @@ __global__ __launch_bounds__(512) void pool_kernel(PoolArgs a) {
   if (p0 >= p1 || gw >= 2 * wk + wr) return;
 
   const bool tiled = tensor == 2 && sizeof(T) == 2;  // bf16 routing keys: tiled bank layout
-  if (rotate) pool_stream<true, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab, tiled);
-  else pool_stream<false, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab, tiled);
+  const int64_t row0 = row_of(a, p0, doc0), row1 = row_of(a, p1, doc1);
+  const int n_units = min(64, n_t - first);
+  if (rotate)
+    pool_stream<true, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab, tiled, stage, first,
+                            n_units, row0, row1);
+  else
+    pool_stream<false, T, D>(a, src, dst, p0, p1, doc0, row_elems, e_lo, e_hi, i0, valid, rope_tab, tiled, stage, first,
+                             n_units, row0, row1);
 }
 
 template <typename T, int D>
@@ -315,13 +389,32 @@ hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
   int wpg = waves < 8 ? waves : 8;                          // waves per workgroup
   const int ygroups = (waves + wpg - 1) / wpg;
   const int threads = 64 * wpg;
-  // Token ranges: several per CU, each at least a few chunks long.
+  // Token ranges: several per CU, each of whole 16-row tiles (a few chunks at least).
   int64_t wgs = 2048 / ygroups;
-  if (wgs > a.n_chunks) wgs = a.n_chunks;
+  const int64_t tiles = (a.n_chunks + 15) / 16 + 1;
+  if (wgs > tiles) wgs = tiles;
   if (wgs < 1) wgs = 1;
-  const size_t lds = a.rope_mask ? (size_t)a.chunk * D * sizeof(float) : 0;
+  PoolArgs k = a;
+  size_t lds = a.rope_mask ? (size_t)a.chunk * D * sizeof(float) : 0;
+  k.stage_waves = 0;
+  k.stage_offset = 0;
+  if (sizeof(T) == 2) {
+    // routing-key waves of the workgroup holding the most of them: 8 KB of staging each
+    const int wk = (nk + 63) / 64, wr = (nr + 63) / 64;
+    int most = 0;
+    for (int y = 0; y < ygroups; ++y) {
+      const int lo = y * wpg > 2 * wk ? y * wpg : 2 * wk, hi = (y + 1) * wpg < 2 * wk + wr ? (y + 1) * wpg : 2 * wk + wr;
+      if (hi - lo > most) most = hi - lo;
+    }
+    const size_t off = (lds + 15) & ~(size_t)15;
+    if (most <= 8 && off + (size_t)most * 8 * 64 * 16 <= 64 * 1024) {
+      k.stage_offset = (int)off;
+      k.stage_waves = most;
+      lds = (size_t)k.stage_offset + (size_t)most * 8 * 64 * 16;
+    }
+  }
   dim3 grid((unsigned)wgs, (unsigned)ygroups);
-  hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(threads), lds, s, a);
+  hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(threads), lds, s, k);
   return hipGetLastError();
 }
 
