@@ -38,32 +38,92 @@
 namespace msa {
 namespace {
 
+// Key -> source row of a query's keys [rows of the selected documents in rank order ;
+// local rows], as a table in LDS for TCH consecutive keys of the workgroup's range (a
+// chunk): entry >= 0 is a bank row, ~entry a local row.  Two chunk slots alternate.  The
+// lookups are branch-free (binary lifting over the document starts, keff <= 1024), so no
+// control flow sits between the loads in flight.
+constexpr int TCH = 16 * KT;
+
+template <int THREADS>
+__device__ __forceinline__ void fwd_build_chunk(int* tab, int tid, int64_t key0, const int64_t* mstart,
+                                                const int64_t* mpre, int keff, int64_t M, int kv0) {
+  for (int i = tid; i < TCH; i += THREADS) {
+    const int64_t key = key0 + i;
+    int lo = 0;  // largest rank t <= keff with mpre[t] <= key (mpre[keff] = M)
+#pragma unroll
+    for (int step = 1024; step > 0; step >>= 1) {
+      const int t = min(lo + step, keff);
+      lo = mpre[t] <= key ? t : lo;
+    }
+    tab[i] = lo < keff ? (int)(mstart[lo] + (key - mpre[lo])) : ~(int)(kv0 + (key - M));
+  }
+}
+
+// One 32-key tile of K and V for kv head g into registers (tile offset rel from the range
+// start k_lo).  The loads are unconditional -- keys past the range re-read its last key and
+// are zeroed when the tile is written to LDS -- so that the wait for the oldest tile of the
+// ring can count the younger tiles' loads as still in flight.
+template <int D, int THREADS, int UPK>
+__device__ __forceinline__ void fwd_fetch(const AttnK& a, int g, int tid, int rel, int n_keys, const int* ktab,
+                                          uint4 (&st)[2 * UPK]) {
+  constexpr int UPR = D / 8;
+#pragma unroll
+  for (int j = 0; j < UPK; ++j) {
+    const int u = min(tid + j * THREADS, KT * UPR - 1);  // threads past the tile repeat its last unit
+    const int kc = min(rel + u / UPR, n_keys - 1);
+    const int v = ktab[((kc / TCH) & 1) * TCH + kc % TCH];
+    const bool bank = v >= 0;
+    const int64_t off = ((int64_t)(bank ? v : ~v) * a.h_kv + g) * D + (u % UPR) * 8;
+    st[j] = *reinterpret_cast<const uint4*>((const bf16_t*)(bank ? a.Kbar : a.Krot) + off);
+    st[UPK + j] = *reinterpret_cast<const uint4*>((const bf16_t*)(bank ? a.Vbar : a.Vloc) + off);
+  }
+}
+
+// Workgroup -> (kv pair, row block, key split).  Workgroups reach the eight XCDs round-robin
+// in linear order; the row blocks and splits of one (query, kv head) pair are placed on one
+// XCD back to back, so the selected K-bar / V-bar rows that all of them gather come from HBM
+// once and from that XCD's L2 after.
+__device__ __forceinline__ bool fwd_place(int n_pairs, int nsub, int& pair, int& sub) {
+  const int L = (int)blockIdx.x;
+  pair = (L >> 3) / nsub * 8 + (L & 7);
+  sub = (L >> 3) % nsub;
+  return pair < n_pairs;
+}
+
 template <int D, int NW, int MTW>
-__global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
+__global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a, int nsub) {
   constexpr int KK = D / 32;
   constexpr int MD = D / 16;
   constexpr int KSTR = D + 16;  // bf16 per K / V row in LDS: 32 bytes of padding keep the
                                 // row reads and the transposed reads conflict-free
   constexpr int THREADS = 64 * NW;
-  constexpr int UPT = 2 * tile_upk<D, THREADS>();
+  constexpr int UPK = (KT * (D / 8) + THREADS - 1) / THREADS;  // 16-byte units per thread per tile
+  constexpr int RING = UPK <= 2 ? 4 : 2;                       // tiles in flight
   constexpr int ROWS = NW * MTW * 16;  // query rows per workgroup (MTW 16-row tiles per wave)
+  // Lazy rescaling: a row's reference maximum moves only when its scores exceed it by more
+  // than 2^LAZY in the exponent (probabilities stay below 2^LAZY: exact in float32 and bf16).
+  constexpr float LAZY = 8.f;
   __shared__ __align__(16) bf16_t Ks[2][KT * KSTR];
   __shared__ __align__(16) bf16_t Vs[2][KT * KSTR];
   __shared__ int64_t mstart[1025], mpre[1025];
+  __shared__ __align__(16) bf16_t sink[8];
+  __shared__ int ktab[2 * TCH];
   __shared__ int sh_keff;
   __shared__ int64_t sh_M;
 
+  int pair, sub;
+  if (!fwd_place(a.n_queries * a.h_kv, nsub, pair, sub)) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int cl = lane & 15, g4 = lane >> 4;
-  const int b = blockIdx.z;
-  const int g = blockIdx.y % a.h_kv;
-  const int split = blockIdx.y / a.h_kv;
+  const int b = pair / a.h_kv, g = pair % a.h_kv;
+  const int split = sub % a.splits;
   const int G = a.hq / a.h_kv;
   const int hq_n = a.hq;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int kv0 = a.kv_off[b], Lkv = a.kv_off[b + 1] - kv0;
   const int nrows = Lq * G;
-  const int rb = blockIdx.x * ROWS;
+  const int rb = (sub / a.splits) * ROWS;
   if (rb >= nrows) return;
 
   if (w == 0) {
@@ -78,16 +138,22 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
   // keys past the last local position any row of this block may see are never needed
   const int t_max = min(Lq - 1, (rb + ROWS - 1) / G);
   k_hi = min(k_hi, M + (int64_t)(Lkv - Lq + t_max + 1));
-  const float scale_log2 = a.scale_log2;
+  const float sc = a.scale_log2;
+
+  // this wave's rows: MTW 16-row tiles from wr0; a wave with none skips the math
+  const int wr0 = rb + w * MTW * 16;
+  const bool wave_rows = wr0 < nrows;
+  // every key below this one is visible to every row of the wave
+  const int64_t key_lim_w = M + (int64_t)(Lkv - Lq + min(wr0, nrows - 1) / G);
 
   // this lane's query rows (one per row tile; B operands of S^T) and causal limits
-  bool row_ok[MTW];
   int t_of[MTW], hq_of[MTW];
+  bool row_ok[MTW];
   int64_t key_lim[MTW];
   bf16x8_t Qf[MTW][KK];
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {
-    const int row = rb + (w * MTW + m) * 16 + cl;
+    const int row = wr0 + m * 16 + cl;
     row_ok[m] = row < nrows;
     t_of[m] = row_ok[m] ? row / G : 0;
     hq_of[m] = g * G + (row_ok[m] ? row % G : 0);
@@ -100,118 +166,137 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
   }
 
   f32x4_t acc[MTW][MD];
-  float m_run[MTW], l_run[MTW];
+  float m_ref[MTW], l_run[MTW];  // reference maximum (raw score) and partial sum of the lane
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {
-    m_run[m] = -INFINITY;
+    m_ref[m] = -INFINITY;
     l_run[m] = 0.f;
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[m][md] = {0.f, 0.f, 0.f, 0.f};
   }
 
-  // the smallest causal limit over the block's rows (its first row's)
-  const int64_t key_lim_min = M + (int64_t)(Lkv - Lq + rb / G);
-
-  TileSrc ts;
-  ts.Kb = (const bf16_t*)a.Kbar;
-  ts.Vb = (const bf16_t*)a.Vbar;
-  ts.Kr = (const bf16_t*)a.Krot;
-  ts.Vl = (const bf16_t*)a.Vloc;
-  ts.mstart = mstart;
-  ts.mpre = mpre;
-  ts.keff = keff;
-  ts.hkv = a.h_kv;
-  ts.g = g;
-  ts.kv0 = kv0;
-  ts.M = M;
-  ts.k_hi = k_hi;
-  // The gathers run TILE_RING tiles ahead of the math (tile_pipeline; two when a stage
-  // takes many registers per thread).
   auto tile_math = [&](int buf, int64_t kt) __attribute__((always_inline)) {
-    // every key of the tile is visible to every row of the block: no masking needed
-    const bool full_tile = kt + KT <= k_hi && kt + KT - 1 <= key_lim_min && rb + ROWS <= nrows;
+    // ---- S^T = K Q^T: each K operand read once for all of the wave's row tiles ----
+    f32x4_t s[MTW][2];
 #pragma unroll
-    for (int m = 0; m < MTW; ++m) {
-      // ---- S^T = K Q^T for two 16-key halves ----
-      f32x4_t s[2];
+    for (int m = 0; m < MTW; ++m) s[m][0] = s[m][1] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        s[n] = {0.f, 0.f, 0.f, 0.f};
+        const bf16x8_t kw =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&Ks[buf][(n * 16 + cl) * KSTR + kk * 32 + g4 * 8]));
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const uint4 kw = *reinterpret_cast<const uint4*>(&Ks[buf][(n * 16 + cl) * KSTR + kk * 32 + g4 * 8]);
-          s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), Qf[m][kk], s[n], 0, 0, 0);
-        }
+        for (int m = 0; m < MTW; ++m) s[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw, Qf[m][kk], s[m][n], 0, 0, 0);
       }
-      // lane holds S[row cl of tile m][key kt + n*16 + g4*4 + i]; the running max is kept
-      // on the raw scores (scale_log2 > 0 keeps their order), scaled inside the exponent
-      float mx = -INFINITY;
-      if (full_tile) {
+    // lane holds S[row cl of tile m][key kt + n*16 + g4*4 + i]
+    const bool masked = kt + KT > k_hi || kt + KT - 1 > key_lim_w;  // uniform
+    bf16x8_t Pf[MTW];
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[n][i]);
-      } else {
+    for (int m = 0; m < MTW; ++m) {
+      if (masked) {
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int64_t key = kt + n * 16 + g4 * 4 + i;
-            const bool vis = row_ok[m] && key < k_hi && key <= key_lim[m];
-            s[n][i] = vis ? s[n][i] : -INFINITY;
-            mx = fmaxf(mx, s[n][i]);
+            s[m][n][i] = (key < k_hi && key <= key_lim[m]) ? s[m][n][i] : -INFINITY;
           }
       }
+      float mx = fmaxf(fmaxf(fmaxf(s[m][0][0], s[m][0][1]), fmaxf(s[m][0][2], s[m][0][3])),
+                       fmaxf(fmaxf(s[m][1][0], s[m][1][1]), fmaxf(s[m][1][2], s[m][1][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[m], mx);
-      float alpha = 1.f;
-      float p[2][4];
-      if (m_new == -INFINITY) {
+      // the running maximum is kept on raw scores (sc > 0 keeps their order)
+      if (__ballot(mx * sc - m_ref[m] * sc > LAZY) != 0) {  // also the first visible key of a row
+        const float m_new = fmaxf(m_ref[m], mx);
+        const float alpha = m_ref[m] == -INFINITY ? 0.f : exp2_hw(m_ref[m] * sc - m_new * sc);
+        m_ref[m] = m_new;
+        l_run[m] *= alpha;
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int md = 0; md < MD; ++md)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[n][i] = 0.f;
-      } else {
-        const float mb = m_new * scale_log2;
-        alpha = exp2_hw(m_run[m] * scale_log2 - mb);
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[n][i] = exp2_hw(fmaf(s[n][i], scale_log2, -mb));
+          for (int i = 0; i < 4; ++i) acc[m][md][i] *= alpha;
       }
-      m_run[m] = m_new;
-      float ps = 0.f;
+      const float mb = m_ref[m] == -INFINITY ? 0.f : m_ref[m] * sc;
+      float p[2][4];
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ps += p[n][i];
-      l_run[m] = l_run[m] * alpha + ps;
+        for (int i = 0; i < 4; ++i) p[n][i] = exp2_hw(fmaf(s[m][n][i], sc, -mb));
       // P^T operand: k-slot g4*8 + j  <->  key g4*4 + j (j < 4), 16 + g4*4 + (j-4) (j >= 4)
       uint4 pw;
       pw.x = f32x2_to_bf16x2(p[0][0], p[0][1]);
       pw.y = f32x2_to_bf16x2(p[0][2], p[0][3]);
       pw.z = f32x2_to_bf16x2(p[1][0], p[1][1]);
       pw.w = f32x2_to_bf16x2(p[1][2], p[1][3]);
-      const bf16x8_t Pf = __builtin_bit_cast(bf16x8_t, pw);
-      // the output columns are rescaled only when some row's maximum moved (alpha != 1)
-      const bool rescale = __ballot(alpha != 1.f) != 0;
+      Pf[m] = __builtin_bit_cast(bf16x8_t, pw);
+      // the denominator sums the same rounded probabilities that weight V, so the output is
+      // a weighted mean whatever the rounding (with a stale reference maximum no weight is
+      // exactly 1)
+      auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
+      auto hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
+      l_run[m] += ((lo(pw.x) + hi(pw.x)) + (lo(pw.y) + hi(pw.y))) + ((lo(pw.z) + hi(pw.z)) + (lo(pw.w) + hi(pw.w)));
+    }
+    // ---- O^T += V^T P^T: each V^T operand read once for all row tiles ----
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        // A operand V^T: element md*16 + cl over keys g4*4 .. +3 and 16 + g4*4 .. +3
-        const bf16_t* vr = &Vs[buf][(g4 * 4 + (cl >> 2)) * KSTR + md * 16 + (cl & 3) * 4];
-        const uint2 v0 = lds_read_tr16(vr);
-        const uint2 v1 = lds_read_tr16(vr + 16 * KSTR);
-        const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
-        if (rescale) {
+    for (int md = 0; md < MD; ++md) {
+      // A operand V^T: element md*16 + cl over keys g4*4 .. +3 and 16 + g4*4 .. +3
+      const bf16_t* vr = &Vs[buf][(g4 * 4 + (cl >> 2)) * KSTR + md * 16 + (cl & 3) * 4];
+      const uint2 v0 = lds_read_tr16(vr);
+      const uint2 v1 = lds_read_tr16(vr + 16 * KSTR);
+      const bf16x8_t Vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][md][i] *= alpha;
-        }
-        acc[m][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vf, Pf, acc[m][md], 0, 0, 0);
-      }
+      for (int m = 0; m < MTW; ++m) acc[m][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vf, Pf[m], acc[m][md], 0, 0, 0);
     }
   };
-  tile_pipeline<(UPT <= 4 ? TILE_RING : 2), D, THREADS, UPT, KSTR, true>(ts, tid, k_lo, k_hi, Ks[0], Ks[1], Vs[0], Vs[1], tile_math);
+
+  // ---- the key loop: gathers RING tiles ahead of the math; one barrier per tile ----
+  // A tile's LDS buffer alternates; a wave writes tile i's buffer only after every wave has
+  // passed tile i-1's barrier, hence finished tile i-2's math on that buffer.
+  if (k_lo < k_hi) {  // uniform; an empty key split still writes its (empty) partial rows
+    const int n_keys = (int)(k_hi - k_lo);  // < 2^31: bank rows and local rows are int32
+    fwd_build_chunk<THREADS>(ktab, tid, k_lo, mstart, mpre, keff, M, kv0);
+    __syncthreads();
+    uint4 st[RING][2 * UPK];
+#pragma unroll
+    for (int r = 0; r < RING; ++r) fwd_fetch<D, THREADS, UPK>(a, g, tid, r * KT, n_keys, ktab, st[r]);
+    // chunk 1 goes to the other slot; its first use comes many barriers later
+    fwd_build_chunk<THREADS>(ktab + TCH, tid, k_lo + TCH, mstart, mpre, keff, M, kv0);
+    for (int t0 = 0; t0 < n_keys; t0 += RING * KT) {
+#pragma unroll
+      for (int r = 0; r < RING; ++r) {
+        const int rel = t0 + r * KT;  // this tile's first key, relative to k_lo
+        bf16_t* Kd = Ks[r & 1];
+        bf16_t* Vd = Vs[r & 1];
+#pragma unroll
+        for (int j = 0; j < UPK; ++j) {
+          // without branches (a branch here would make the compiler drain the ring): units
+          // past the tile go to a sink
+          const int u = tid + j * THREADS;
+          const bool unit = (KT * (D / 8)) % THREADS == 0 || u < KT * (D / 8);
+          const int kr = u / (D / 8), e0 = (u % (D / 8)) * 8;
+          const uint32_t in = rel + kr < n_keys ? ~0u : 0u;  // keys past the range: zeros
+          const uint4 kv = st[r][j], vv = st[r][UPK + j];
+          *reinterpret_cast<uint4*>(unit ? &Kd[kr * KSTR + e0] : &sink[0]) =
+              make_uint4(kv.x & in, kv.y & in, kv.z & in, kv.w & in);
+          *reinterpret_cast<uint4*>(unit ? &Vd[kr * KSTR + e0] : &sink[0]) =
+              make_uint4(vv.x & in, vv.y & in, vv.z & in, vv.w & in);
+        }
+        __syncthreads();
+        const int relf = rel + RING * KT;  // the tile fetched now
+        fwd_fetch<D, THREADS, UPK>(a, g, tid, relf, n_keys, ktab, st[r]);
+        // entering chunk c: chunk c+1 replaces chunk c-1, whose last fetch came before the
+        // barrier above (uniform branch, LDS only)
+        if (relf % TCH == 0 && relf + TCH < n_keys)
+          fwd_build_chunk<THREADS>(ktab + ((relf / TCH + 1) & 1) * TCH, tid, k_lo + relf + TCH, mstart, mpre, keff,
+                                   M, kv0);
+        // the ring runs in whole groups of RING tiles, with no exit inside a group (an exit
+        // there makes the compiler drain the ring): tiles past the range only skip the math
+        if (wave_rows && rel < n_keys) tile_math(r & 1, k_lo + rel);
+      }
+    }
+  }
 
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {
@@ -222,7 +307,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
     const int64_t orow = (int64_t)(q0 + t_of[m]) * hq_n + hq_of[m];
     if (a.splits == 1) {
       if (a.lse != nullptr && g4 == 0)
-        a.lse[orow] = l_row > 0.f ? (m_run[m] * scale_log2 + log2f(l_row)) * LN2 : -INFINITY;
+        a.lse[orow] = l_row > 0.f ? (m_ref[m] * sc + log2f(l_row)) * LN2 : -INFINITY;
       const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
       bf16_t* o = (bf16_t*)a.O + orow * D + g4 * 4;
 #pragma unroll
@@ -238,7 +323,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a) {
         *reinterpret_cast<float4*>(po + md * 16) =
             make_float4(acc[m][md][0], acc[m][md][1], acc[m][md][2], acc[m][md][3]);
       if (g4 == 0) {
-        a.part_ml[prow * 2] = m_run[m] * scale_log2;  // the combine works on scaled maxima
+        a.part_ml[prow * 2] = m_ref[m] == -INFINITY ? -INFINITY : m_ref[m] * sc;  // scaled maxima
         a.part_ml[prow * 2 + 1] = l_row;
       }
     }
@@ -364,13 +449,16 @@ hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, hipStream_t s) {
     const int G = r.hq / r.h_kv;
     const int brows = attn_rows_per_block(r.max_q_len, G);
     const int rblocks = (r.max_q_len * G + brows - 1) / brows;
-    dim3 grid((unsigned)rblocks, (unsigned)(r.h_kv * k.splits), (unsigned)r.n_queries);
+    const int nsub = rblocks * k.splits;
+    const int n_pairs = r.n_queries * r.h_kv;
+    const dim3 grid((unsigned)(((n_pairs + 7) / 8) * 8 * nsub));
+    // 16-row tiles: two per wave (each K / V operand serves both) from 32 rows up
     switch (brows) {
-      case 16: hipLaunchKernelGGL((attn_mfma<D, 1, 1>), grid, dim3(64), 0, s, k); break;
-      case 32: hipLaunchKernelGGL((attn_mfma<D, 2, 1>), grid, dim3(128), 0, s, k); break;
-      case 64: hipLaunchKernelGGL((attn_mfma<D, 4, 1>), grid, dim3(256), 0, s, k); break;
-      case 128: hipLaunchKernelGGL((attn_mfma<D, 8, 1>), grid, dim3(512), 0, s, k); break;
-      default: hipLaunchKernelGGL((attn_mfma<D, 8, 2>), grid, dim3(512), 0, s, k); break;
+      case 16: hipLaunchKernelGGL((attn_mfma<D, 1, 1>), grid, dim3(64), 0, s, k, nsub); break;
+      case 32: hipLaunchKernelGGL((attn_mfma<D, 1, 2>), grid, dim3(64), 0, s, k, nsub); break;
+      case 64: hipLaunchKernelGGL((attn_mfma<D, 2, 2>), grid, dim3(128), 0, s, k, nsub); break;
+      case 128: hipLaunchKernelGGL((attn_mfma<D, 4, 2>), grid, dim3(256), 0, s, k, nsub); break;
+      default: hipLaunchKernelGGL((attn_mfma<D, 8, 2>), grid, dim3(512), 0, s, k, nsub); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || k.splits == 1) return e;
