@@ -12,21 +12,22 @@
 // local states and the top-k memory.
 //
 // Kernels:
-//  * rope_local: rotates Q and the local K at their global positions (k_eff + local
-//    index) into the workspace, angles in double precision, once per row.
-//  * attn_mfma (bf16): one workgroup per (query, kv head, block of up to 256 query rows,
-//    key split), with one 16-row wave per row slice, so each staged K/V tile serves every
-//    query row of the kv head and every byte read over the host link is read once.  The
-//    key sequence is [rows of the selected documents in rank order ; local keys]; the
-//    workgroup maps each key of a 32-key tile to its source row (bank row of a selected
-//    document, read from HBM or over the host link from pinned memory, or a local row),
-//    stages K and V in LDS row-major (double-buffered, the gathers of the next tiles in
-//    flight during the current tile's math: tile_pipeline), and runs an online softmax in
-//    float32.
+//  * rope_local: rotates the local K (and for float32 also Q) at their global positions
+//    (k_eff + local index) into the workspace, angles in double precision, once per row.
+//  * rope_table (bf16): cos / sin of every position a row or local key can take, from
+//    double-precision angles; attn_mfma rotates Q with it while loading its operands.
+//  * attn_mfma (bf16): one workgroup per (query, kv head, block of query rows, key split);
+//    each wave holds one or two 16-row tiles of query rows, so each staged K/V tile serves
+//    every row of the block.  The key sequence is [rows of the selected documents in rank
+//    order ; local keys]; a branch-free table in LDS maps each key to its source row (bank
+//    row of a selected document, read from HBM or over the host link from pinned memory, or
+//    a local row).  K and V are staged in LDS row-major, double-buffered, with the gathers
+//    of the next tiles in flight during the current tile's math.  The softmax runs in
+//    float32 with a lazily moved reference maximum.
 //    S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 leaves each lane with 8 scores of one
 //    query row, which are exactly the P^T operand of O^T = V^T * P^T, so probabilities
 //    never leave registers; V^T comes from the row-major tile through gfx950's
-//    transposing LDS load.
+//    transposing LDS load, and each K / V operand read serves both row tiles of a wave.
 //  * attn_valu (float32): one thread per (query row, head), plain online softmax.
 //  * attn_combine: merges the per-split (max, sum, unnormalised output) triples.
 #include <math.h>
@@ -72,12 +73,22 @@ __device__ __forceinline__ void fwd_fetch(const AttnK& a, int g, int tid, int re
   for (int j = 0; j < UPK; ++j) {
     const int u = min(tid + j * THREADS, KT * UPR - 1);  // threads past the tile repeat its last unit
     const int kc = min(rel + u / UPR, n_keys - 1);
-    const int v = ktab[((kc / TCH) & 1) * TCH + kc % TCH];
+    const int v = ktab[(((unsigned)kc / TCH) & 1) * TCH + (unsigned)kc % TCH];
     const bool bank = v >= 0;
     const int64_t off = ((int64_t)(bank ? v : ~v) * a.h_kv + g) * D + (u % UPR) * 8;
     st[j] = *reinterpret_cast<const uint4*>((const bf16_t*)(bank ? a.Kbar : a.Krot) + off);
     st[UPK + j] = *reinterpret_cast<const uint4*>((const bf16_t*)(bank ? a.Vbar : a.Vloc) + off);
   }
+}
+
+// Maximum over the four lanes cl, cl + 16, cl + 32, cl + 48 (the 16-lane rows of a wave):
+// gfx950's permlane swaps exchange odd and even rows, then the two halves, so each lane
+// holds its own value in one result and its partner's in the other.
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Workgroup -> (kv pair, row block, key split).  Workgroups reach the eight XCDs round-robin
@@ -92,17 +103,18 @@ __device__ __forceinline__ bool fwd_place(int n_pairs, int nsub, int& pair, int&
 }
 
 template <int D, int NW, int MTW>
-__global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a, int nsub) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma(AttnK a, int nsub) {
   constexpr int KK = D / 32;
   constexpr int MD = D / 16;
   constexpr int KSTR = D + 16;  // bf16 per K / V row in LDS: 32 bytes of padding keep the
                                 // row reads and the transposed reads conflict-free
   constexpr int THREADS = 64 * NW;
   constexpr int UPK = (KT * (D / 8) + THREADS - 1) / THREADS;  // 16-byte units per thread per tile
-  constexpr int RING = UPK <= 2 ? 4 : 2;                       // tiles in flight
+  constexpr int RING = UPK == 1 ? 4 : 2;                       // tiles in flight
   constexpr int ROWS = NW * MTW * 16;  // query rows per workgroup (MTW 16-row tiles per wave)
-  // Lazy rescaling: a row's reference maximum moves only when its scores exceed it by more
-  // than 2^LAZY in the exponent (probabilities stay below 2^LAZY: exact in float32 and bf16).
+  // Lazy rescaling: a row's reference maximum moves only when a score exceeds it by more
+  // than LAZY in the base-2 exponent, so probabilities stay below 2^LAZY (far inside the
+  // float32 and bf16 ranges) and most tiles rescale nothing.
   constexpr float LAZY = 8.f;
   __shared__ __align__(16) bf16_t Ks[2][KT * KSTR];
   __shared__ __align__(16) bf16_t Vs[2][KT * KSTR];
@@ -146,7 +158,9 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a, int nsub) {
   // every key below this one is visible to every row of the wave
   const int64_t key_lim_w = M + (int64_t)(Lkv - Lq + min(wr0, nrows - 1) / G);
 
-  // this lane's query rows (one per row tile; B operands of S^T) and causal limits
+  // this lane's query rows (one per row tile; B operands of S^T) and causal limits.  Q is
+  // rotated here to its global position keff + (Lkv - Lq) + t: each lane also loads the
+  // pair partners (d +- D/2) of its 8 elements and takes cos / sin from the table.
   int t_of[MTW], hq_of[MTW];
   bool row_ok[MTW];
   int64_t key_lim[MTW];
@@ -158,22 +172,52 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a, int nsub) {
     t_of[m] = row_ok[m] ? row / G : 0;
     hq_of[m] = g * G + (row_ok[m] ? row % G : 0);
     key_lim[m] = M + (int64_t)(Lkv - Lq + t_of[m]);  // last visible key index
-    const bf16_t* qp = (const bf16_t*)a.Qrot + ((int64_t)(q0 + t_of[m]) * hq_n + hq_of[m]) * D + g4 * 8;
+    const bf16_t* qp = (const bf16_t*)a.Q + ((int64_t)(q0 + t_of[m]) * hq_n + hq_of[m]) * D;
+    const int64_t pos = (int64_t)keff + (Lkv - Lq) + t_of[m];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      Qf[m][kk] = row_ok[m] ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + kk * 32))
-                            : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+    for (int kk = 0; kk < KK; ++kk) {
+      const int d0 = kk * 32 + g4 * 8;                 // first of the lane's 8 elements
+      const bool low = d0 < D / 2;                     // x_i (else x_{i+D/2})
+      const int i0 = low ? d0 : d0 - D / 2;            // first pair index
+      float x[8], y[8], o[8];
+      Elem<bf16_t>::load8(qp + d0, x);
+      Elem<bf16_t>::load8(qp + (low ? d0 + D / 2 : i0), y);
+      const float* cp = a.rtab + pos * (D / 2) + i0;
+      const float* sp = cp + a.n_pos * (D / 2);
+      const float4 c0 = *reinterpret_cast<const float4*>(cp), c1 = *reinterpret_cast<const float4*>(cp + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(sp), s1 = *reinterpret_cast<const float4*>(sp + 4);
+      const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = low ? rot_lo(x[j], y[j], c[j], sn[j]) : rot_hi(y[j], x[j], c[j], sn[j]);
+      uint4 w;
+      w.x = f32x2_to_bf16x2(o[0], o[1]);
+      w.y = f32x2_to_bf16x2(o[2], o[3]);
+      w.z = f32x2_to_bf16x2(o[4], o[5]);
+      w.w = f32x2_to_bf16x2(o[6], o[7]);
+      Qf[m][kk] = __builtin_bit_cast(bf16x8_t, row_ok[m] ? w : make_uint4(0, 0, 0, 0));
+    }
   }
 
   f32x4_t acc[MTW][MD];
-  float m_ref[MTW], l_run[MTW];  // reference maximum (raw score) and partial sum of the lane
+  // Row sums of the probabilities come from the matrix cores: a ones operand in place of V^T
+  // gives every lane of a row the sum over the tile's keys of the same rounded values that
+  // weight V, accumulated in float32 (so the output is a weighted mean whatever the
+  // rounding; with a stale reference maximum no weight is exactly 1).
+  f32x4_t lsum[MTW];
+  // reference maximum (raw score), its scaled value, and the rescale threshold
+  float m_ref[MTW], mb[MTW], thr[MTW];
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {
     m_ref[m] = -INFINITY;
-    l_run[m] = 0.f;
+    mb[m] = 0.f;
+    thr[m] = -INFINITY;
+    lsum[m] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[m][md] = {0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  const float lazy_raw = LAZY / sc;  // the threshold in raw score units (sc > 0)
 
   auto tile_math = [&](int buf, int64_t kt) __attribute__((always_inline)) {
     // ---- S^T = K Q^T: each K operand read once for all of the wave's row tiles ----
@@ -203,27 +247,29 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a, int nsub) {
             s[m][n][i] = (key < k_hi && key <= key_lim[m]) ? s[m][n][i] : -INFINITY;
           }
       }
-      float mx = fmaxf(fmaxf(fmaxf(s[m][0][0], s[m][0][1]), fmaxf(s[m][0][2], s[m][0][3])),
-                       fmaxf(fmaxf(s[m][1][0], s[m][1][1]), fmaxf(s[m][1][2], s[m][1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // the running maximum is kept on raw scores (sc > 0 keeps their order)
-      if (__ballot(mx * sc - m_ref[m] * sc > LAZY) != 0) {  // also the first visible key of a row
-        const float m_new = fmaxf(m_ref[m], mx);
+      // the lane's own maximum; the row's (over its 4 lanes) is formed only when some lane
+      // of the wave passes its row's threshold (also the first visible key of a row)
+      const float mx = fmaxf(fmaxf(fmaxf(s[m][0][0], s[m][0][1]), fmaxf(s[m][0][2], s[m][0][3])),
+                             fmaxf(fmaxf(s[m][1][0], s[m][1][1]), fmaxf(s[m][1][2], s[m][1][3])));
+      if (__ballot(mx > thr[m]) != 0) {
+        const float rmx = row_max4(mx);
+        const float m_new = fmaxf(m_ref[m], rmx);
         const float alpha = m_ref[m] == -INFINITY ? 0.f : exp2_hw(m_ref[m] * sc - m_new * sc);
         m_ref[m] = m_new;
-        l_run[m] *= alpha;
+        mb[m] = m_new == -INFINITY ? 0.f : m_new * sc;
+        thr[m] = m_new + lazy_raw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lsum[m][i] *= alpha;
 #pragma unroll
         for (int md = 0; md < MD; ++md)
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[m][md][i] *= alpha;
       }
-      const float mb = m_ref[m] == -INFINITY ? 0.f : m_ref[m] * sc;
       float p[2][4];
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[n][i] = exp2_hw(fmaf(s[m][n][i], sc, -mb));
+        for (int i = 0; i < 4; ++i) p[n][i] = exp2_hw(fmaf(s[m][n][i], sc, -mb[m]));
       // P^T operand: k-slot g4*8 + j  <->  key g4*4 + j (j < 4), 16 + g4*4 + (j-4) (j >= 4)
       uint4 pw;
       pw.x = f32x2_to_bf16x2(p[0][0], p[0][1]);
@@ -231,12 +277,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a, int nsub) {
       pw.z = f32x2_to_bf16x2(p[1][0], p[1][1]);
       pw.w = f32x2_to_bf16x2(p[1][2], p[1][3]);
       Pf[m] = __builtin_bit_cast(bf16x8_t, pw);
-      // the denominator sums the same rounded probabilities that weight V, so the output is
-      // a weighted mean whatever the rounding (with a stale reference maximum no weight is
-      // exactly 1)
-      auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
-      auto hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
-      l_run[m] += ((lo(pw.x) + hi(pw.x)) + (lo(pw.y) + hi(pw.y))) + ((lo(pw.z) + hi(pw.z)) + (lo(pw.w) + hi(pw.w)));
+      lsum[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, Pf[m], lsum[m], 0, 0, 0);
     }
     // ---- O^T += V^T P^T: each V^T operand read once for all row tiles ----
 #pragma unroll
@@ -300,9 +341,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma(AttnK a, int nsub) {
 
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {
-    // row totals: the 4 lane groups of a row hold partial sums
-    float l_row = l_run[m] + __shfl_xor(l_run[m], 16);
-    l_row += __shfl_xor(l_row, 32);
+    const float l_row = lsum[m][0];  // every lane of a row holds the row's total
     if (!row_ok[m]) continue;
     const int64_t orow = (int64_t)(q0 + t_of[m]) * hq_n + hq_of[m];
     if (a.splits == 1) {
@@ -431,11 +470,20 @@ __global__ __launch_bounds__(256) void attn_combine(AttnK a) {
 }
 
 template <typename T, int D>
-hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, hipStream_t s) {
-  const int nq_blocks = (int)((r.total_q + RPW - 1) / RPW);
+hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, bool host, hipStream_t s) {
+  // float32: Q and the local K rotated into the workspace; bf16: the local K only, and the
+  // cos / sin table from which the attention kernel rotates Q as it loads it
+  const int nq_blocks = sizeof(T) == 4 ? (int)((r.total_q + RPW - 1) / RPW) : 0;
   const int nk_blocks = (int)((r.total_kv + RPW - 1) / RPW);
   if (nq_blocks + nk_blocks > 0) {
     hipLaunchKernelGGL((rope_local<T, D>), dim3(nq_blocks + nk_blocks), dim3(256), 0, s, k, nq_blocks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (sizeof(T) == 2 && r.total_q > 0) {
+    const int64_t n = k.n_pos * (D / 2);
+    hipLaunchKernelGGL((rope_table<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float*)k.rtab,
+                       k.n_pos, k.rope_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -447,16 +495,17 @@ hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, hipStream_t s) {
     return hipGetLastError();
   } else {
     const int G = r.hq / r.h_kv;
-    const int brows = attn_rows_per_block(r.max_q_len, G);
+    const int brows = attn_fwd_rows(r.max_q_len, G, host);
     const int rblocks = (r.max_q_len * G + brows - 1) / brows;
     const int nsub = rblocks * k.splits;
     const int n_pairs = r.n_queries * r.h_kv;
     const dim3 grid((unsigned)(((n_pairs + 7) / 8) * 8 * nsub));
-    // 16-row tiles: two per wave (each K / V operand serves both) from 32 rows up
+    // 16-row tiles: two per wave (each K / V operand serves both) from 128 rows; below, fewer
+    // threads would each stage more of a tile, and the registers would not fit
     switch (brows) {
       case 16: hipLaunchKernelGGL((attn_mfma<D, 1, 1>), grid, dim3(64), 0, s, k, nsub); break;
-      case 32: hipLaunchKernelGGL((attn_mfma<D, 1, 2>), grid, dim3(64), 0, s, k, nsub); break;
-      case 64: hipLaunchKernelGGL((attn_mfma<D, 2, 2>), grid, dim3(128), 0, s, k, nsub); break;
+      case 32: hipLaunchKernelGGL((attn_mfma<D, 2, 1>), grid, dim3(128), 0, s, k, nsub); break;
+      case 64: hipLaunchKernelGGL((attn_mfma<D, 4, 1>), grid, dim3(256), 0, s, k, nsub); break;
       case 128: hipLaunchKernelGGL((attn_mfma<D, 4, 2>), grid, dim3(256), 0, s, k, nsub); break;
       default: hipLaunchKernelGGL((attn_mfma<D, 8, 2>), grid, dim3(512), 0, s, k, nsub); break;
     }
@@ -480,8 +529,20 @@ int attn_rows_per_block(int max_q_len, int G) {
   return rows;
 }
 
+// Query rows per forward workgroup.  With K-bar / V-bar in device memory, up to 128 (4 waves
+// of two 16-row tiles), so that two workgroups share a CU and the barriers of one overlap
+// the math of the other; the row blocks of one (query, kv head) run on one XCD, whose L2
+// serves the second block the rows the first read from HBM.  Over the host link every row
+// is read once: one block holds all the rows of a (query, kv head), up to 256.
+int attn_fwd_rows(int max_q_len, int G, bool host) {
+  const int rows = attn_rows_per_block(max_q_len, G);
+  return host || rows < 128 ? rows : 128;
+}
+
 // Key splits per (query, kv head): enough workgroups in flight to keep the host link or HBM
-// busy (about 64), bounded so the partial results stay small.
+// busy (about 64), bounded so the partial results stay small.  Counted on row blocks of up
+// to 256 rows whatever the placement, so that a bank in host memory and one in HBM split
+// the keys alike and give the same bits (waves hold the same 32 rows in both).
 int attn_splits(int n_queries, int max_q_len, int hq, int h_kv) {
   const int G = hq / h_kv;
   const int rows = attn_rows_per_block(max_q_len, G);
@@ -493,11 +554,18 @@ int attn_splits(int n_queries, int max_q_len, int hq, int h_kv) {
   return (int)s;
 }
 
+// Positions a query's rows and local keys can take: below keff + Lkv <= 1024 + total_kv.
+static int64_t attn_max_positions(int64_t total_kv, int k) { return (int64_t)k + total_kv; }
+
+// Workspace: float32 [rotated Q][rotated local K]; bf16 [rotated local K][cos / sin table]
+// [per-split partial outputs][per-split (max, sum)].
 size_t attn_workspace_bytes(int dtype, int n_queries, int64_t total_q, int64_t total_kv,
                             int max_q_len, int hq, int h_kv, int d) {
   const size_t esz = dtype == 0 ? 4 : 2;
-  size_t bytes = align256((size_t)total_q * hq * d * esz) + align256((size_t)total_kv * h_kv * d * esz);
+  size_t bytes = align256((size_t)total_kv * h_kv * d * esz);
+  if (dtype == 0) bytes += align256((size_t)total_q * hq * d * esz);
   if (dtype == 1) {
+    bytes += align256((size_t)attn_max_positions(total_kv, 1024) * d * 4);
     const int s = attn_splits(n_queries, max_q_len, hq, h_kv);
     if (s > 1) {
       bytes += align256((size_t)s * total_q * hq * d * 4);
@@ -530,10 +598,23 @@ hipError_t launch_sparse_attn(const AttnArgs& r, hipStream_t s) {
   k.lse = r.lse;
   const size_t esz = r.dtype == 0 ? 4 : 2;
   char* ws = (char*)r.workspace;
-  k.Qrot = ws;
-  ws += align256((size_t)r.total_q * r.hq * r.d * esz);
   k.Krot = ws;
   ws += align256((size_t)r.total_kv * r.h_kv * r.d * esz);
+  if (r.dtype == 0) {
+    k.Qrot = ws;
+    ws += align256((size_t)r.total_q * r.hq * r.d * esz);
+  } else {
+    k.n_pos = attn_max_positions(r.total_kv, r.k);
+    k.rtab = (const float*)ws;
+    ws += align256((size_t)attn_max_positions(r.total_kv, 1024) * r.d * 4);
+  }
+  // K-bar / V-bar in host memory (pinned): read over the host link, once per row
+  bool host = false;
+  if (r.dtype == 1) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, r.Kbar) == hipSuccess) host = at.type == hipMemoryTypeHost;
+    else (void)hipGetLastError();  // not a HIP allocation: nothing to record
+  }
   k.splits = r.dtype == 1 ? attn_splits(r.n_queries, r.max_q_len, r.hq, r.h_kv) : 1;
   if (k.splits > 1) {
     k.part_o = (float*)ws;
@@ -542,15 +623,15 @@ hipError_t launch_sparse_attn(const AttnArgs& r, hipStream_t s) {
   }
   if (r.dtype == 0) {
     switch (r.d) {
-      case 32: return launch_attn_t<float, 32>(r, k, s);
-      case 64: return launch_attn_t<float, 64>(r, k, s);
-      default: return launch_attn_t<float, 128>(r, k, s);
+      case 32: return launch_attn_t<float, 32>(r, k, host, s);
+      case 64: return launch_attn_t<float, 64>(r, k, host, s);
+      default: return launch_attn_t<float, 128>(r, k, host, s);
     }
   }
   switch (r.d) {
-    case 32: return launch_attn_t<bf16_t, 32>(r, k, s);
-    case 64: return launch_attn_t<bf16_t, 64>(r, k, s);
-    default: return launch_attn_t<bf16_t, 128>(r, k, s);
+    case 32: return launch_attn_t<bf16_t, 32>(r, k, host, s);
+    case 64: return launch_attn_t<bf16_t, 64>(r, k, host, s);
+    default: return launch_attn_t<bf16_t, 128>(r, k, host, s);
   }
 }
 

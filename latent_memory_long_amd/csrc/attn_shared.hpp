@@ -31,6 +31,8 @@ struct AttnK {
   float* part_ml;
   int splits;
   float* lse;  // optional per-row log-sum-exp output (natural log)
+  const float* rtab;  // rope_table of n_pos positions (bf16 forward: Q is rotated in place)
+  int64_t n_pos;
 };
 
 __device__ __forceinline__ int find_query(const int32_t* off, int n, int64_t row) {
@@ -49,6 +51,26 @@ __device__ __forceinline__ int count_valid_ids(const int32_t* ids, int k) {
 }
 
 // ---- global RoPE of the local context --------------------------------------------------
+// One rotation pair (x_i, x_{i+d/2}) by the angle with cosine c and sine s, with the
+// roundings written out, so that every kernel that rotates gets the same bits.
+__device__ __forceinline__ float rot_lo(float lo, float hi, float c, float s) { return fmaf(lo, c, -(hi * s)); }
+__device__ __forceinline__ float rot_hi(float lo, float hi, float c, float s) { return fmaf(hi, c, lo * s); }
+
+// cos and sin of p * theta_i for positions p < n_pos and pairs i < D/2, the angles in double
+// precision (theta_i = base^(-2i/D)), rounded to float: cos at [p][i], sin at
+// [n_pos + p][i].
+template <int D>
+__global__ __launch_bounds__(256) void rope_table(float* tab, int64_t n_pos, float rope_base) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n_pos * (D / 2)) return;
+  const int64_t p = e / (D / 2);
+  const int i = (int)(e % (D / 2));
+  const double th = pow((double)rope_base, -2.0 * (double)i / (double)D);
+  double sn, cs;
+  sincos((double)p * th, &sn, &cs);
+  tab[e] = (float)cs;
+  tab[n_pos * (D / 2) + e] = (float)sn;
+}
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
   __shared__ float cs_tab[RPW][D / 2], sn_tab[RPW][D / 2];
@@ -99,8 +121,8 @@ __global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float c = cs_tab[rr][i0 + q], s = sn_tab[rr][i0 + q];
-      o_lo[q] = lo[q] * c - hi[q] * s;
-      o_hi[q] = hi[q] * c + lo[q] * s;
+      o_lo[q] = rot_lo(lo[q], hi[q], c, s);
+      o_hi[q] = rot_hi(lo[q], hi[q], c, s);
     }
     T* o = dst + (r * heads + h) * D;
     Elem<T>::store4(o + i0, o_lo);
