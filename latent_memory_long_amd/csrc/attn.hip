@@ -39,16 +39,24 @@
 namespace msa {
 namespace {
 
-// Key -> source row of a query's keys [rows of the selected documents in rank order ;
-// local rows], as a table in LDS for TCH consecutive keys of the workgroup's range (a
-// chunk): entry >= 0 is a bank row, ~entry a local row.  Two chunk slots alternate.  The
-// lookups are branch-free (binary lifting over the document starts, keff <= 1024), so no
-// control flow sits between the loads in flight.
+// Key -> source of a query's keys [rows of the selected documents in rank order ; local
+// rows], as tables in LDS for TCH consecutive keys of the workgroup's range (a chunk): the
+// element offset of the key's row of kv head g from K-bar and from V-bar (a local row's
+// offset reaches the local K / V through the distance between the two allocations).  Two
+// chunk slots alternate.  Lookups are branch-free (binary lifting over the document starts,
+// keff <= 1024), so no control flow sits between the loads in flight.
 constexpr int TCH = 16 * KT;
 
-template <int THREADS>
-__device__ __forceinline__ void fwd_build_chunk(int* tab, int tid, int64_t key0, const int64_t* mstart,
-                                                const int64_t* mpre, int keff, int64_t M, int kv0) {
+// 16 bytes as a native vector (a struct copy such as HIP's uint4 would go through memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int THREADS>
+__device__ __forceinline__ void fwd_build_chunk(int64_t* tk, int64_t* tv, int tid, int64_t key0,
+                                                const int64_t* mstart, const int64_t* mpre, int keff, int64_t M,
+                                                int kv0, const AttnK& a, int g) {
+  // local K / V relative to K-bar / V-bar, in elements (all are 2-byte aligned)
+  const int64_t dk = ((int64_t)(uintptr_t)a.Krot - (int64_t)(uintptr_t)a.Kbar) / 2;
+  const int64_t dv = ((int64_t)(uintptr_t)a.Vloc - (int64_t)(uintptr_t)a.Vbar) / 2;
   for (int i = tid; i < TCH; i += THREADS) {
     const int64_t key = key0 + i;
     int lo = 0;  // largest rank t <= keff with mpre[t] <= key (mpre[keff] = M)
@@ -57,27 +65,29 @@ __device__ __forceinline__ void fwd_build_chunk(int* tab, int tid, int64_t key0,
       const int t = min(lo + step, keff);
       lo = mpre[t] <= key ? t : lo;
     }
-    tab[i] = lo < keff ? (int)(mstart[lo] + (key - mpre[lo])) : ~(int)(kv0 + (key - M));
+    const bool bank = lo < keff;
+    const int64_t row = bank ? mstart[lo] + (key - mpre[lo]) : kv0 + (key - M);
+    const int64_t off = (row * a.h_kv + g) * D;
+    tk[i] = bank ? off : dk + off;
+    tv[i] = bank ? off : dv + off;
   }
 }
 
-// One 32-key tile of K and V for kv head g into registers (tile offset rel from the range
-// start k_lo).  The loads are unconditional -- keys past the range re-read its last key and
-// are zeroed when the tile is written to LDS -- so that the wait for the oldest tile of the
-// ring can count the younger tiles' loads as still in flight.
+// One 32-key tile of K and V into registers (tile offset rel from the range start k_lo);
+// kb / vb point at the thread's 8 elements of K-bar / V-bar row 0.  The loads are
+// unconditional -- keys past the range re-read its last key (V zeroed when the tile is
+// written to LDS) -- so that the wait for the oldest tile of the ring can count the younger
+// tiles' loads as still in flight.
 template <int D, int THREADS, int UPK>
-__device__ __forceinline__ void fwd_fetch(const AttnK& a, int g, int tid, int rel, int n_keys, const int* ktab,
-                                          uint4 (&st)[2 * UPK]) {
-  constexpr int UPR = D / 8;
+__device__ __forceinline__ void fwd_fetch(const bf16_t* const (&kb)[UPK], const bf16_t* const (&vb)[UPK],
+                                          const int (&kr)[UPK], int rel, int n_keys, const int64_t* tk,
+                                          const int64_t* tv, u32x4 (&st)[2 * UPK]) {
 #pragma unroll
   for (int j = 0; j < UPK; ++j) {
-    const int u = min(tid + j * THREADS, KT * UPR - 1);  // threads past the tile repeat its last unit
-    const int kc = min(rel + u / UPR, n_keys - 1);
-    const int v = ktab[(((unsigned)kc / TCH) & 1) * TCH + (unsigned)kc % TCH];
-    const bool bank = v >= 0;
-    const int64_t off = ((int64_t)(bank ? v : ~v) * a.h_kv + g) * D + (u % UPR) * 8;
-    st[j] = *reinterpret_cast<const uint4*>((const bf16_t*)(bank ? a.Kbar : a.Krot) + off);
-    st[UPK + j] = *reinterpret_cast<const uint4*>((const bf16_t*)(bank ? a.Vbar : a.Vloc) + off);
+    const int kc = min(rel + kr[j], n_keys - 1);
+    const int e = kc & (2 * TCH - 1);  // chunk slot (kc / TCH) & 1, entry kc % TCH
+    st[j] = *reinterpret_cast<const u32x4*>(kb[j] + tk[e]);
+    st[UPK + j] = *reinterpret_cast<const u32x4*>(vb[j] + tv[e]);
   }
 }
 
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ __align__(16) bf16_t Vs[2][KT * KSTR];
   __shared__ int64_t mstart[1025], mpre[1025];
   __shared__ __align__(16) bf16_t sink[8];
-  __shared__ int ktab[2 * TCH];
+  __shared__ int64_t tabk[2 * TCH], tabv[2 * TCH];
   __shared__ int sh_keff;
   __shared__ int64_t sh_M;
 
@@ -155,15 +165,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // this wave's rows: MTW 16-row tiles from wr0; a wave with none skips the math
   const int wr0 = rb + w * MTW * 16;
   const bool wave_rows = wr0 < nrows;
-  // every key below this one is visible to every row of the wave
-  const int64_t key_lim_w = M + (int64_t)(Lkv - Lq + min(wr0, nrows - 1) / G);
+  // Keys relative to k_lo (int: fewer than 2^31 keys).  Every key up to lim_w is visible to
+  // every row of the wave; lim_r[m] is the lane's row's last visible key.
+  const int n_keys = (int)max(k_hi - k_lo, (int64_t)0);
+  const int lim_w = (int)(M + (Lkv - Lq) + min(wr0, nrows - 1) / G - k_lo);
 
   // this lane's query rows (one per row tile; B operands of S^T) and causal limits.  Q is
   // rotated here to its global position keff + (Lkv - Lq) + t: each lane also loads the
   // pair partners (d +- D/2) of its 8 elements and takes cos / sin from the table.
   int t_of[MTW], hq_of[MTW];
   bool row_ok[MTW];
-  int64_t key_lim[MTW];
+  int lim_r[MTW];
   bf16x8_t Qf[MTW][KK];
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     row_ok[m] = row < nrows;
     t_of[m] = row_ok[m] ? row / G : 0;
     hq_of[m] = g * G + (row_ok[m] ? row % G : 0);
-    key_lim[m] = M + (int64_t)(Lkv - Lq + t_of[m]);  // last visible key index
+    lim_r[m] = (int)(M + (Lkv - Lq) + t_of[m] - k_lo);
     const bf16_t* qp = (const bf16_t*)a.Q + ((int64_t)(q0 + t_of[m]) * hq_n + hq_of[m]) * D;
     const int64_t pos = (int64_t)keff + (Lkv - Lq) + t_of[m];
 #pragma unroll
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const float lazy_raw = LAZY / sc;  // the threshold in raw score units (sc > 0)
 
-  auto tile_math = [&](int buf, int64_t kt) __attribute__((always_inline)) {
+  auto tile_math = [&](int buf, int rel) __attribute__((always_inline)) {
     // ---- S^T = K Q^T: each K operand read once for all of the wave's row tiles ----
     f32x4_t s[MTW][2];
 #pragma unroll
@@ -233,25 +245,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int m = 0; m < MTW; ++m) s[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw, Qf[m][kk], s[m][n], 0, 0, 0);
       }
-    // lane holds S[row cl of tile m][key kt + n*16 + g4*4 + i]
-    const bool masked = kt + KT > k_hi || kt + KT - 1 > key_lim_w;  // uniform
+    // lane holds S[row cl of tile m][key rel + n*16 + g4*4 + i]; keys relative to k_lo
+    const bool masked = rel + KT > n_keys || rel + KT - 1 > lim_w;  // uniform
     bf16x8_t Pf[MTW];
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       if (masked) {
+        // key visible: below the range end and at most the row's causal limit
+        const int lim = min(n_keys - 1, lim_r[m]) - rel - g4 * 4;
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t key = kt + n * 16 + g4 * 4 + i;
-            s[m][n][i] = (key < k_hi && key <= key_lim[m]) ? s[m][n][i] : -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i) s[m][n][i] = n * 16 + i <= lim ? s[m][n][i] : -INFINITY;
       }
-      // the lane's own maximum; the row's (over its 4 lanes) is formed only when some lane
-      // of the wave passes its row's threshold (also the first visible key of a row)
-      const float mx = fmaxf(fmaxf(fmaxf(s[m][0][0], s[m][0][1]), fmaxf(s[m][0][2], s[m][0][3])),
-                             fmaxf(fmaxf(s[m][1][0], s[m][1][1]), fmaxf(s[m][1][2], s[m][1][3])));
-      if (__ballot(mx > thr[m]) != 0) {
+      // Does any score pass its row's threshold (also the first visible key of a row)?  Only
+      // then is the row's maximum (over its 4 lanes) formed and the reference moved.
+      const float t = thr[m];
+      const bool over = (s[m][0][0] > t) | (s[m][0][1] > t) | (s[m][0][2] > t) | (s[m][0][3] > t) |
+                        (s[m][1][0] > t) | (s[m][1][1] > t) | (s[m][1][2] > t) | (s[m][1][3] > t);
+      if (__ballot(over) != 0) {
+        const float mx = fmaxf(fmaxf(fmaxf(s[m][0][0], s[m][0][1]), fmaxf(s[m][0][2], s[m][0][3])),
+                               fmaxf(fmaxf(s[m][1][0], s[m][1][1]), fmaxf(s[m][1][2], s[m][1][3])));
         const float rmx = row_max4(mx);
         const float m_new = fmaxf(m_ref[m], rmx);
         const float alpha = m_ref[m] == -INFINITY ? 0.f : exp2_hw(m_ref[m] * sc - m_new * sc);
@@ -295,15 +309,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // ---- the key loop: gathers RING tiles ahead of the math; one barrier per tile ----
   // A tile's LDS buffer alternates; a wave writes tile i's buffer only after every wave has
   // passed tile i-1's barrier, hence finished tile i-2's math on that buffer.
-  if (k_lo < k_hi) {  // uniform; an empty key split still writes its (empty) partial rows
-    const int n_keys = (int)(k_hi - k_lo);  // < 2^31: bank rows and local rows are int32
-    fwd_build_chunk<THREADS>(ktab, tid, k_lo, mstart, mpre, keff, M, kv0);
-    __syncthreads();
-    uint4 st[RING][2 * UPK];
+  if (n_keys > 0) {  // uniform; an empty key split still writes its (empty) partial rows
+    // this thread's units of a tile: key kr[j] of the tile, elements e0 .. e0 + 7
+    const bf16_t* kb[UPK];
+    const bf16_t* vb[UPK];
+    int kr[UPK];
 #pragma unroll
-    for (int r = 0; r < RING; ++r) fwd_fetch<D, THREADS, UPK>(a, g, tid, r * KT, n_keys, ktab, st[r]);
+    for (int j = 0; j < UPK; ++j) {
+      const int u = min(tid + j * THREADS, KT * (D / 8) - 1);  // threads past the tile repeat its last unit
+      kr[j] = u / (D / 8);
+      kb[j] = (const bf16_t*)a.Kbar + (u % (D / 8)) * 8;
+      vb[j] = (const bf16_t*)a.Vbar + (u % (D / 8)) * 8;
+    }
+    fwd_build_chunk<D, THREADS>(tabk, tabv, tid, k_lo, mstart, mpre, keff, M, kv0, a, g);
+    __syncthreads();
+    u32x4 st[RING][2 * UPK];
+#pragma unroll
+    for (int r = 0; r < RING; ++r) fwd_fetch<D, THREADS, UPK>(kb, vb, kr, r * KT, n_keys, tabk, tabv, st[r]);
     // chunk 1 goes to the other slot; its first use comes many barriers later
-    fwd_build_chunk<THREADS>(ktab + TCH, tid, k_lo + TCH, mstart, mpre, keff, M, kv0);
+    fwd_build_chunk<D, THREADS>(tabk + TCH, tabv + TCH, tid, k_lo + TCH, mstart, mpre, keff, M, kv0, a, g);
     for (int t0 = 0; t0 < n_keys; t0 += RING * KT) {
 #pragma unroll
       for (int r = 0; r < RING; ++r) {
@@ -313,28 +337,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int j = 0; j < UPK; ++j) {
           // without branches (a branch here would make the compiler drain the ring): units
-          // past the tile go to a sink
+          // past the tile go to a sink.  V of keys past the range is zeroed (their
+          // probabilities are 0, and 0 * V must stay 0); their scores are masked.
           const int u = tid + j * THREADS;
           const bool unit = (KT * (D / 8)) % THREADS == 0 || u < KT * (D / 8);
-          const int kr = u / (D / 8), e0 = (u % (D / 8)) * 8;
-          const uint32_t in = rel + kr < n_keys ? ~0u : 0u;  // keys past the range: zeros
-          const uint4 kv = st[r][j], vv = st[r][UPK + j];
-          *reinterpret_cast<uint4*>(unit ? &Kd[kr * KSTR + e0] : &sink[0]) =
-              make_uint4(kv.x & in, kv.y & in, kv.z & in, kv.w & in);
-          *reinterpret_cast<uint4*>(unit ? &Vd[kr * KSTR + e0] : &sink[0]) =
-              make_uint4(vv.x & in, vv.y & in, vv.z & in, vv.w & in);
+          const int e0 = (u % (D / 8)) * 8;
+          const uint32_t in = rel + kr[j] < n_keys ? ~0u : 0u;
+          *reinterpret_cast<u32x4*>(unit ? &Kd[kr[j] * KSTR + e0] : &sink[0]) = st[r][j];
+          *reinterpret_cast<u32x4*>(unit ? &Vd[kr[j] * KSTR + e0] : &sink[0]) = st[r][UPK + j] & in;
         }
         __syncthreads();
         const int relf = rel + RING * KT;  // the tile fetched now
-        fwd_fetch<D, THREADS, UPK>(a, g, tid, relf, n_keys, ktab, st[r]);
+        fwd_fetch<D, THREADS, UPK>(kb, vb, kr, relf, n_keys, tabk, tabv, st[r]);
         // entering chunk c: chunk c+1 replaces chunk c-1, whose last fetch came before the
         // barrier above (uniform branch, LDS only)
-        if (relf % TCH == 0 && relf + TCH < n_keys)
-          fwd_build_chunk<THREADS>(ktab + ((relf / TCH + 1) & 1) * TCH, tid, k_lo + relf + TCH, mstart, mpre, keff,
-                                   M, kv0);
+        if (relf % TCH == 0 && relf + TCH < n_keys) {
+          const int slot = ((relf / TCH + 1) & 1) * TCH;
+          fwd_build_chunk<D, THREADS>(tabk + slot, tabv + slot, tid, k_lo + relf + TCH, mstart, mpre, keff, M, kv0,
+                                      a, g);
+        }
         // the ring runs in whole groups of RING tiles, with no exit inside a group (an exit
         // there makes the compiler drain the ring): tiles past the range only skip the math
-        if (wave_rows && rel < n_keys) tile_math(r & 1, k_lo + rel);
+        if (wave_rows && rel < n_keys) tile_math(r & 1, rel);
       }
     }
   }
