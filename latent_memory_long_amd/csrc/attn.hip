@@ -495,8 +495,16 @@ __global__ __launch_bounds__(256) void attn_combine(AttnK a) {
 
 template <typename T, int D>
 hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, bool host, hipStream_t s) {
-  // float32: Q and the local K rotated into the workspace; bf16: the local K only, and the
-  // cos / sin table from which the attention kernel rotates Q as it loads it
+  if (r.total_q == 0) return hipSuccess;  // no rows: nothing reads the rotated local K
+  // float32: Q and the local K rotated into the workspace; bf16: the cos / sin table, then
+  // the local K rotated with it (the attention kernel rotates Q with it as it loads it)
+  if (sizeof(T) == 2) {
+    const int64_t n = k.n_pos * (D / 2);
+    hipLaunchKernelGGL((rope_table<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float*)k.rtab,
+                       k.n_pos, k.rope_base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int nq_blocks = sizeof(T) == 4 ? (int)((r.total_q + RPW - 1) / RPW) : 0;
   const int nk_blocks = (int)((r.total_kv + RPW - 1) / RPW);
   if (nq_blocks + nk_blocks > 0) {
@@ -504,14 +512,6 @@ hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, bool host, hipStream_t s) 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (sizeof(T) == 2 && r.total_q > 0) {
-    const int64_t n = k.n_pos * (D / 2);
-    hipLaunchKernelGGL((rope_table<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float*)k.rtab,
-                       k.n_pos, k.rope_base);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (r.total_q == 0) return hipSuccess;
   if constexpr (sizeof(T) == 4) {
     k.splits = 1;
     dim3 grid((unsigned)((r.max_q_len * r.hq + 63) / 64), (unsigned)r.n_queries);

@@ -31,7 +31,8 @@ struct AttnK {
   float* part_ml;
   int splits;
   float* lse;  // optional per-row log-sum-exp output (natural log)
-  const float* rtab;  // rope_table of n_pos positions (bf16 forward: Q is rotated in place)
+  const float* rtab;  // rope_table of n_pos positions, or null (bf16 forward: Q is rotated in
+                      // the attention kernel, local K by rope_local, both from this table)
   int64_t n_pos;
 };
 
@@ -100,6 +101,12 @@ __global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
   __syncthreads();
   for (int e = tid; e < RPW * (D / 2); e += blockDim.x) {
     const int rr = e / (D / 2), i = e % (D / 2);
+    if (a.rtab != nullptr) {  // the values of rope_table, already computed
+      const int64_t p = row_pos[rr] >= 0 ? row_pos[rr] : 0;
+      cs_tab[rr][i] = a.rtab[p * (D / 2) + i];
+      sn_tab[rr][i] = a.rtab[(a.n_pos + p) * (D / 2) + i];
+      continue;
+    }
     const double th = pow((double)a.rope_base, -2.0 * (double)i / (double)D);
     double sn = 0.0, cs = 1.0;
     if (row_pos[rr] >= 0) sincos((double)row_pos[rr] * th, &sn, &cs);
