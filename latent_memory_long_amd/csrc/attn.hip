@@ -245,12 +245,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int m = 0; m < MTW; ++m) s[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw, Qf[m][kk], s[m][n], 0, 0, 0);
       }
-    // lane holds S[row cl of tile m][key rel + n*16 + g4*4 + i]; keys relative to k_lo
-    const bool masked = rel + KT > n_keys || rel + KT - 1 > lim_w;  // uniform
-    bf16x8_t Pf[MTW];
+    // lane holds S[row cl of tile m][key rel + n*16 + g4*4 + i]; keys relative to k_lo.
+    // At most two uniform branches per tile, both rare (the masks near the end of the range
+    // and the moves of the reference maximum), so that the exponentials of one row tile and
+    // the products of the other share one block the scheduler can interleave.
+    if (rel + KT > n_keys || rel + KT - 1 > lim_w) {  // uniform
 #pragma unroll
-    for (int m = 0; m < MTW; ++m) {
-      if (masked) {
+      for (int m = 0; m < MTW; ++m) {
         // key visible: below the range end and at most the row's causal limit
         const int lim = min(n_keys - 1, lim_r[m]) - rel - g4 * 4;
 #pragma unroll
@@ -258,12 +259,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[m][n][i] = n * 16 + i <= lim ? s[m][n][i] : -INFINITY;
       }
-      // Does any score pass its row's threshold (also the first visible key of a row)?  Only
-      // then is the row's maximum (over its 4 lanes) formed and the reference moved.
+    }
+    // Does any score pass its row's threshold (also the first visible key of a row)?  Only
+    // then are the rows' maxima (over their 4 lanes) formed and the references moved.
+    bool over = false;
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
       const float t = thr[m];
-      const bool over = (s[m][0][0] > t) | (s[m][0][1] > t) | (s[m][0][2] > t) | (s[m][0][3] > t) |
-                        (s[m][1][0] > t) | (s[m][1][1] > t) | (s[m][1][2] > t) | (s[m][1][3] > t);
-      if (__ballot(over) != 0) {
+      over |= (s[m][0][0] > t) | (s[m][0][1] > t) | (s[m][0][2] > t) | (s[m][0][3] > t) |
+              (s[m][1][0] > t) | (s[m][1][1] > t) | (s[m][1][2] > t) | (s[m][1][3] > t);
+    }
+    if (__ballot(over) != 0) {
+#pragma unroll
+      for (int m = 0; m < MTW; ++m) {
         const float mx = fmaxf(fmaxf(fmaxf(s[m][0][0], s[m][0][1]), fmaxf(s[m][0][2], s[m][0][3])),
                                fmaxf(fmaxf(s[m][1][0], s[m][1][1]), fmaxf(s[m][1][2], s[m][1][3])));
         const float rmx = row_max4(mx);
@@ -279,6 +287,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[m][md][i] *= alpha;
       }
+    }
+    bf16x8_t Pf[MTW];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
       float p[2][4];
 #pragma unroll
       for (int n = 0; n < 2; ++n)
