@@ -15,6 +15,10 @@
 //  * route_bwd_pair: one wave per (query, document): the maximising row, its token, the key
 //    gradient (added atomically: a row can be the maximiser for several queries), and a
 //    record (t*, row, per-head cosine and 1/|k|) for the query gradient;
+//  * bf16 banks with d = 128 and 4 or 8 heads: route_bwd_doc_b16 (one workgroup per
+//    document: every query's maximising row and token, the records, and the rows' key
+//    gradients added once per distinct row in a fixed order, without atomics) and
+//    route_bwd_dq_b16 (16-byte gathers, several matches in flight);
 //  * route_bwd_dq: one workgroup per (query, token) (strided when a query is longer than the
 //    grid): gathers the records that name the
 //    token (filtered a block of documents at a time through LDS) and writes its gradient
@@ -203,8 +207,265 @@ __global__ __launch_bounds__(DQ_THREADS) void route_bwd_dq(RouteBwdK a) {
   }
 }
 
+// ---- bf16, d = 128, 4 or 8 heads: all heads of a pair at once --------------------------
+// A lane holds EPL consecutive elements of one head (LPH lanes per head): 16-byte loads of
+// the query row and of the tiled key row, per-head sums over the head's lanes.
+
+// Sum over the LPH lanes of each head, returned to every lane of the head.
+template <int LPH>
+__device__ __forceinline__ float head_sum(float v) {
+  v = group_sum_last<LPH>(v);
+  return __shfl(v, (int)(threadIdx.x & 63) | (LPH - 1), 64);
+}
+
+// One document's share of the router's backward (a bank row belongs to one document, so
+// the workgroup owns its rows' key gradients):
+//  1. for each query, the maximising row (the first with the largest row score, 16 lanes
+//     per query) and its first maximising token;
+//  2. the queries with a gradient ordered by (row, query);
+//  3. in that order, per record: the per-head cosine and 1/|k| (the record the query
+//     gradient reads) and the key-gradient contribution, summed in registers over the
+//     records of one row and added to the row once with a plain read-modify-write.
+// A thread holds 8 consecutive elements of a row (16 threads per head).  The summation
+// order is fixed: the result does not depend on scheduling.
+template <int H>
+__global__ __launch_bounds__(H * 16) void route_bwd_doc_b16(RouteBwdK a) {
+  constexpr int D = 128, NE = H * D, NT = H * 16, QPASS = NT / 16;  // queries per pass
+  __shared__ int q_c[64], q_t[64], q_order[64];  // row (relative to the document), token
+  __shared__ float q_g[64];
+  __shared__ int n_valid;
+  const int d = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, sub = tid & 15;
+  const int e0 = tid * 8, h = e0 / D;
+  const bf16_t* K = (const bf16_t*)a.Krb;
+  const int64_t c0 = a.chunk_off[d];
+  const int nc = (int)(a.chunk_off[d + 1] - c0);
+  for (int b0 = 0; b0 < a.n_queries; b0 += 64) {
+    // ---- 1. maximising row and token of each query of the chunk ----
+    for (int qi = tid / 16; qi < 64; qi += QPASS) {
+      const int b = b0 + qi;
+      const bool inq = b < a.n_queries;
+      const int bb = inq ? b : a.n_queries - 1;  // addresses stay in bounds
+      const int64_t rec = (int64_t)bb * a.n_docs + d;
+      const int Lq = a.q_off[bb + 1] - a.q_off[bb];
+      const float gd = a.dD[rec];
+      float best = -INFINITY;
+      int bc = nc;
+      if (inq && gd != 0.f && Lq > 0) {
+        const float* rs = a.row_scores + (int64_t)bb * a.n_chunks + c0;
+        for (int c = sub; c < nc; c += 16) {
+          const float v = rs[c];
+          if (v > best) { best = v; bc = c; }  // c ascending: a tie keeps the first
+        }
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(best, o, 16);
+        const int oc = __shfl_xor(bc, o, 16);
+        if (ov > best || (ov == best && oc < bc)) { best = ov; bc = oc; }
+      }
+      if (sub == 0) {
+        const bool v = inq && bc < nc;  // else no gradient (an empty query or document, g = 0)
+        q_c[qi] = v ? bc : -1;
+        q_t[qi] = v ? a.row_arg[(int64_t)bb * a.n_chunks + c0 + bc] : 0;
+        q_g[qi] = gd / (float)H;
+        if (inq && !v) a.tstar[rec] = -1;
+      }
+    }
+    __syncthreads();
+    // ---- 2. the records with a gradient, ordered by (row, query) ----
+    if (tid < 64) {
+      const int c = q_c[lane];
+      const int key = c >= 0 ? c : INT_MAX;
+      int rank = 0;
+      for (int o = 0; o < 64; ++o) {
+        const int ko = __shfl(key, o, 64);
+        rank += (ko < key || (ko == key && o < lane)) ? 1 : 0;
+      }
+      if (c >= 0) q_order[rank] = lane;
+      const int nv = __popcll(__ballot(c >= 0));
+      if (lane == 0) n_valid = nv;
+    }
+    __syncthreads();
+    // ---- 3. records and key gradients ----
+    const int nv = n_valid;  // q_order[0 .. nv-1]; none read past them
+    float acc[8], y[8];
+    float ik_row = 0.f;  // 1/|k| of the current row's head (0 for a zero vector)
+    int row = -1;
+    auto flush = [&]() __attribute__((always_inline)) {
+      float* dk = a.dKrb + (c0 + row) * NE + e0;  // row-major, added to
+      const float4 u0 = *reinterpret_cast<const float4*>(dk), u1 = *reinterpret_cast<const float4*>(dk + 4);
+      *reinterpret_cast<float4*>(dk) = make_float4(u0.x + acc[0], u0.y + acc[1], u0.z + acc[2], u0.w + acc[3]);
+      *reinterpret_cast<float4*>(dk + 4) = make_float4(u1.x + acc[4], u1.y + acc[5], u1.z + acc[6], u1.w + acc[7]);
+    };
+    for (int r = 0; r < nv; ++r) {
+      const int qi = q_order[r];
+      const int b = b0 + qi, c = q_c[qi], t = q_t[qi];
+      const int64_t rec = (int64_t)b * a.n_docs + d;
+      if (c != row) {  // uniform: the next row
+        if (row >= 0) flush();
+        row = c;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        unpack8(*reinterpret_cast<const uint4*>(K + kr_tiled<D>(c0 + c, e0, H)), y);
+        float kn = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kn += y[i] * y[i];
+        kn = head_sum<16>(kn);
+        ik_row = kn > 0.f ? 1.f / sqrtf(kn) : 0.f;
+      }
+      float x[8];
+      unpack8(*reinterpret_cast<const uint4*>((const bf16_t*)a.Qr + (int64_t)(a.q_off[b] + t) * NE + e0), x);
+      float dot = 0.f, qn = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dot += x[i] * y[i];
+        qn += x[i] * x[i];
+      }
+      dot = head_sum<16>(dot);
+      qn = head_sum<16>(qn);
+      const bool ok = qn > 0.f && ik_row > 0.f;  // no gradient for a head with a zero vector
+      const float iq = ok ? 1.f / sqrtf(qn) : 0.f, ik = ok ? ik_row : 0.f;
+      const float co = dot * iq * ik;
+      if (sub == 0) {
+        a.cosv[rec * H + h] = co;
+        a.kinv[rec * H + h] = ik;
+      }
+      if (tid == 0) {
+        a.tstar[rec] = t;
+        a.cstar[rec] = c0 + c;
+      }
+      const float w = q_g[qi] * ik;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += w * (x[i] * iq - co * y[i] * ik);
+    }
+    if (row >= 0) flush();
+    __syncthreads();  // the chunk's arrays are rewritten for the next chunk of queries
+  }
+}
+
+// The query gradient of one token: its matches (documents whose maximum sits on it) are
+// taken PAR at a time by PAR thread groups, each thread holding 8 consecutive elements of
+// the token's row; the groups' partial sums are combined in group order, so the summation
+// order is fixed.
+template <int H>
+__global__ __launch_bounds__(DQ_THREADS) void route_bwd_dq_b16(RouteBwdK a) {
+  constexpr int D = 128, NE = H * D, TPM = NE / 8, PAR = DQ_THREADS / TPM;
+  static_assert(TPM * PAR == DQ_THREADS, "thread groups must tile the workgroup");
+  __shared__ int match[DQ_BLOCK];
+  __shared__ int wave_hits[DQ_THREADS / 64];
+  __shared__ float part1[PAR > 1 ? PAR - 1 : 1][NE];
+  __shared__ float part2[PAR > 1 ? PAR - 1 : 1][H];
+  const int b = blockIdx.y;
+  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int grp = tid / TPM, e0 = (tid % TPM) * 8, h = e0 / D;
+  const bf16_t* K = (const bf16_t*)a.Krb;
+  for (int t = blockIdx.x; t < Lq; t += gridDim.x) {
+    float acc1[8], acc2 = 0.f;  // sum of g * k / |k|, sum of g * cos (the thread's head)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc1[i] = 0.f;
+    const int32_t* ts = a.tstar + (int64_t)b * a.n_docs;
+    for (int d0 = 0; d0 < a.n_docs; d0 += DQ_BLOCK) {
+      // the block's documents whose maximum sits on token t, listed in document order
+      const int dd = d0 + tid;
+      const bool hit = dd < a.n_docs && ts[dd] == t;
+      const uint64_t bal = __ballot(hit);
+      if (lane == 0) wave_hits[wv] = __popcll(bal);
+      __syncthreads();
+      int base = 0, nm = 0;
+#pragma unroll
+      for (int i = 0; i < DQ_THREADS / 64; ++i) {
+        base += (i < wv) ? wave_hits[i] : 0;
+        nm += wave_hits[i];
+      }
+      if (hit) match[base + __popcll(bal & ((1ull << lane) - 1))] = dd;
+      __syncthreads();
+      // group grp takes matches grp, grp + PAR, ..., two at a time (both loads in flight)
+      int m = grp;
+      for (; m + PAR < nm; m += 2 * PAR) {
+        const int64_t r0 = (int64_t)b * a.n_docs + match[m], r1 = (int64_t)b * a.n_docs + match[m + PAR];
+        const int64_t k0 = a.cstar[r0], k1 = a.cstar[r1];
+        const float g0 = a.dD[r0], g1 = a.dD[r1];
+        const float w0 = g0 * a.kinv[r0 * H + h], w1 = g1 * a.kinv[r1 * H + h];
+        const float c0v = g0 * a.cosv[r0 * H + h], c1v = g1 * a.cosv[r1 * H + h];
+        const uint4 v0 = *reinterpret_cast<const uint4*>(K + kr_tiled<D>(k0, e0, H));
+        const uint4 v1 = *reinterpret_cast<const uint4*>(K + kr_tiled<D>(k1, e0, H));
+        float y0[8], y1[8];
+        unpack8(v0, y0);
+        unpack8(v1, y1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc1[i] += w0 * y0[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc1[i] += w1 * y1[i];
+        acc2 += c0v;
+        acc2 += c1v;
+      }
+      if (m < nm) {
+        const int64_t r0 = (int64_t)b * a.n_docs + match[m];
+        const int64_t k0 = a.cstar[r0];
+        const float g0 = a.dD[r0];
+        float y0[8];
+        unpack8(*reinterpret_cast<const uint4*>(K + kr_tiled<D>(k0, e0, H)), y0);
+        const float w0 = g0 * a.kinv[r0 * H + h];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc1[i] += w0 * y0[i];
+        acc2 += g0 * a.cosv[r0 * H + h];
+      }
+      __syncthreads();
+    }
+    // combine the groups in order: group 0 adds groups 1 .. PAR-1
+    if constexpr (PAR > 1) {
+      if (grp > 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part1[grp - 1][e0 + i] = acc1[i];
+        if (e0 % D == 0) part2[grp - 1][h] = acc2;
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int p = 0; p < PAR - 1; ++p) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc1[i] += part1[p][e0 + i];
+          acc2 += part2[p][h];
+        }
+      }
+    }
+    if (grp == 0) {
+      const bf16_t* q = (const bf16_t*)a.Qr + (int64_t)(q0 + t) * NE + e0;
+      float x[8];
+      unpack8(*reinterpret_cast<const uint4*>(q), x);
+      float qn = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qn += x[i] * x[i];
+      qn = head_sum<D / 8 < 64 ? D / 8 : 64>(qn);  // the 16 threads of the head (within a wave)
+      float* dq = a.dQr + (int64_t)(q0 + t) * NE + e0;
+      const float iq = qn > 0.f ? 1.f / sqrtf(qn) : 0.f;
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = qn > 0.f ? (acc1[i] - acc2 * x[i] * iq) * iq / (float)H : 0.f;
+      *reinterpret_cast<float4*>(dq) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(dq + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
+    __syncthreads();  // the partial-sum buffers are rewritten for the next token
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_t(const RouteBwdArgs& r, const RouteBwdK& k, hipStream_t s) {
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    if (r.h_r == 4 || r.h_r == 8) {
+      dim3 g2((unsigned)(r.max_q_len < 1024 ? r.max_q_len : 1024), (unsigned)r.n_queries);
+      if (r.h_r == 8) {
+        hipLaunchKernelGGL((route_bwd_doc_b16<8>), dim3((unsigned)r.n_docs), dim3(128), 0, s, k);
+        hipLaunchKernelGGL((route_bwd_dq_b16<8>), g2, dim3(DQ_THREADS), 0, s, k);
+      } else {
+        hipLaunchKernelGGL((route_bwd_doc_b16<4>), dim3((unsigned)r.n_docs), dim3(64), 0, s, k);
+        hipLaunchKernelGGL((route_bwd_dq_b16<4>), g2, dim3(DQ_THREADS), 0, s, k);
+      }
+      return hipGetLastError();
+    }
+  }
   dim3 g1((unsigned)((r.n_docs + 3) / 4), (unsigned)r.n_queries);
   hipLaunchKernelGGL((route_bwd_pair<T, D>), g1, dim3(256), 0, s, k);
   dim3 g2((unsigned)(r.max_q_len < 1024 ? r.max_q_len : 1024), (unsigned)r.n_queries);
