@@ -39,58 +39,6 @@
 namespace msa {
 namespace {
 
-// Key -> source of a query's keys [rows of the selected documents in rank order ; local
-// rows], as tables in LDS for TCH consecutive keys of the workgroup's range (a chunk): the
-// element offset of the key's row of kv head g from K-bar and from V-bar (a local row's
-// offset reaches the local K / V through the distance between the two allocations).  Two
-// chunk slots alternate.  Lookups are branch-free (binary lifting over the document starts,
-// keff <= 1024), so no control flow sits between the loads in flight.
-constexpr int TCH = 16 * KT;
-
-// 16 bytes as a native vector (a struct copy such as HIP's uint4 would go through memory)
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-template <int D, int THREADS>
-__device__ __forceinline__ void fwd_build_chunk(int64_t* tk, int64_t* tv, int tid, int64_t key0,
-                                                const int64_t* mstart, const int64_t* mpre, int keff, int64_t M,
-                                                int kv0, const AttnK& a, int g) {
-  // local K / V relative to K-bar / V-bar, in elements (all are 2-byte aligned)
-  const int64_t dk = ((int64_t)(uintptr_t)a.Krot - (int64_t)(uintptr_t)a.Kbar) / 2;
-  const int64_t dv = ((int64_t)(uintptr_t)a.Vloc - (int64_t)(uintptr_t)a.Vbar) / 2;
-  for (int i = tid; i < TCH; i += THREADS) {
-    const int64_t key = key0 + i;
-    int lo = 0;  // largest rank t <= keff with mpre[t] <= key (mpre[keff] = M)
-#pragma unroll
-    for (int step = 1024; step > 0; step >>= 1) {
-      const int t = min(lo + step, keff);
-      lo = mpre[t] <= key ? t : lo;
-    }
-    const bool bank = lo < keff;
-    const int64_t row = bank ? mstart[lo] + (key - mpre[lo]) : kv0 + (key - M);
-    const int64_t off = (row * a.h_kv + g) * D;
-    tk[i] = bank ? off : dk + off;
-    tv[i] = bank ? off : dv + off;
-  }
-}
-
-// One 32-key tile of K and V into registers (tile offset rel from the range start k_lo);
-// kb / vb point at the thread's 8 elements of K-bar / V-bar row 0.  The loads are
-// unconditional -- keys past the range re-read its last key (V zeroed when the tile is
-// written to LDS) -- so that the wait for the oldest tile of the ring can count the younger
-// tiles' loads as still in flight.
-template <int D, int THREADS, int UPK>
-__device__ __forceinline__ void fwd_fetch(const bf16_t* const (&kb)[UPK], const bf16_t* const (&vb)[UPK],
-                                          const int (&kr)[UPK], int rel, int n_keys, const int64_t* tk,
-                                          const int64_t* tv, u32x4 (&st)[2 * UPK]) {
-#pragma unroll
-  for (int j = 0; j < UPK; ++j) {
-    const int kc = min(rel + kr[j], n_keys - 1);
-    const int e = kc & (2 * TCH - 1);  // chunk slot (kc / TCH) & 1, entry kc % TCH
-    st[j] = *reinterpret_cast<const u32x4*>(kb[j] + tk[e]);
-    st[UPK + j] = *reinterpret_cast<const u32x4*>(vb[j] + tv[e]);
-  }
-}
-
 // Maximum over the four lanes cl, cl + 16, cl + 32, cl + 48 (the 16-lane rows of a wave):
 // gfx950's permlane swaps exchange odd and even rows, then the two halves, so each lane
 // holds its own value in one result and its partner's in the other.
@@ -318,62 +266,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
-  // ---- the key loop: gathers RING tiles ahead of the math; one barrier per tile ----
-  // A tile's LDS buffer alternates; a wave writes tile i's buffer only after every wave has
-  // passed tile i-1's barrier, hence finished tile i-2's math on that buffer.
-  if (n_keys > 0) {  // uniform; an empty key split still writes its (empty) partial rows
-    // this thread's units of a tile: key kr[j] of the tile, elements e0 .. e0 + 7
-    const bf16_t* kb[UPK];
-    const bf16_t* vb[UPK];
-    int kr[UPK];
-#pragma unroll
-    for (int j = 0; j < UPK; ++j) {
-      const int u = min(tid + j * THREADS, KT * (D / 8) - 1);  // threads past the tile repeat its last unit
-      kr[j] = u / (D / 8);
-      kb[j] = (const bf16_t*)a.Kbar + (u % (D / 8)) * 8;
-      vb[j] = (const bf16_t*)a.Vbar + (u % (D / 8)) * 8;
-    }
-    fwd_build_chunk<D, THREADS>(tabk, tabv, tid, k_lo, mstart, mpre, keff, M, kv0, a, g);
-    __syncthreads();
-    u32x4 st[RING][2 * UPK];
-#pragma unroll
-    for (int r = 0; r < RING; ++r) fwd_fetch<D, THREADS, UPK>(kb, vb, kr, r * KT, n_keys, tabk, tabv, st[r]);
-    // chunk 1 goes to the other slot; its first use comes many barriers later
-    fwd_build_chunk<D, THREADS>(tabk + TCH, tabv + TCH, tid, k_lo + TCH, mstart, mpre, keff, M, kv0, a, g);
-    for (int t0 = 0; t0 < n_keys; t0 += RING * KT) {
-#pragma unroll
-      for (int r = 0; r < RING; ++r) {
-        const int rel = t0 + r * KT;  // this tile's first key, relative to k_lo
-        bf16_t* Kd = Ks[r & 1];
-        bf16_t* Vd = Vs[r & 1];
-#pragma unroll
-        for (int j = 0; j < UPK; ++j) {
-          // without branches (a branch here would make the compiler drain the ring): units
-          // past the tile go to a sink.  V of keys past the range is zeroed (their
-          // probabilities are 0, and 0 * V must stay 0); their scores are masked.
-          const int u = tid + j * THREADS;
-          const bool unit = (KT * (D / 8)) % THREADS == 0 || u < KT * (D / 8);
-          const int e0 = (u % (D / 8)) * 8;
-          const uint32_t in = rel + kr[j] < n_keys ? ~0u : 0u;
-          *reinterpret_cast<u32x4*>(unit ? &Kd[kr[j] * KSTR + e0] : &sink[0]) = st[r][j];
-          *reinterpret_cast<u32x4*>(unit ? &Vd[kr[j] * KSTR + e0] : &sink[0]) = st[r][UPK + j] & in;
-        }
-        __syncthreads();
-        const int relf = rel + RING * KT;  // the tile fetched now
-        fwd_fetch<D, THREADS, UPK>(kb, vb, kr, relf, n_keys, tabk, tabv, st[r]);
-        // entering chunk c: chunk c+1 replaces chunk c-1, whose last fetch came before the
-        // barrier above (uniform branch, LDS only)
-        if (relf % TCH == 0 && relf + TCH < n_keys) {
-          const int slot = ((relf / TCH + 1) & 1) * TCH;
-          fwd_build_chunk<D, THREADS>(tabk + slot, tabv + slot, tid, k_lo + relf + TCH, mstart, mpre, keff, M, kv0,
-                                      a, g);
-        }
-        // the ring runs in whole groups of RING tiles, with no exit inside a group (an exit
-        // there makes the compiler drain the ring): tiles past the range only skip the math
-        if (wave_rows && rel < n_keys) tile_math(r & 1, rel);
-      }
-    }
-  }
+  // ---- the key loop (an empty key split still writes its empty partial rows) ----
+  key_loop<RING, D, THREADS, KSTR, true>(a, g, tid, k_lo, n_keys, mstart, mpre, keff, M, kv0, tabk, tabv, Ks[0], Ks[1],
+                                         Vs[0], Vs[1], sink, [&](int buf, int rel) __attribute__((always_inline)) {
+                                           if (wave_rows) tile_math(buf, rel);
+                                         });
 
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {

@@ -13,7 +13,8 @@
 //
 // Kernels (bf16 inputs, float32 gradients, MFMA with float32 accumulation):
 //  * rope_local (shared with the forward): rotated Q and local K into the workspace.
-//  * bwd_dq: one workgroup per (query, kv head, block of query rows), like the forward.
+//  * bwd_dq: one workgroup per (query, kv head, block of query rows), with the forward's key
+//    loop (attn_shared.hpp's key_loop).
 //    Unless the forward's per-row log-sum-exp is passed in, a first pass over the key tiles
 //    recomputes it; the second computes S^T = K Q~^T, P^T, dP^T = V dO^T and dS^T in
 //    registers and accumulates dQ~^T = K^T dS^T, reading K^T straight from the row-major
@@ -65,11 +66,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
   constexpr int MD = D / 16;
   constexpr int KSTR = D + 16;  // 32 bytes of padding: row and transposed reads are conflict-free
   constexpr int THREADS = 64 * NW;
-  constexpr int UPT = 2 * tile_upk<D, THREADS>();
+  constexpr int UPK = (KT * (D / 8) + THREADS - 1) / THREADS;  // 16-byte units per thread per tile
+  constexpr int RING = UPK == 1 ? 4 : 2;                       // tiles in flight
   constexpr int ROWS = NW * MTW * 16;
   __shared__ __align__(16) bf16_t Ks[2][KT * KSTR];
   __shared__ __align__(16) bf16_t Vs[2][KT * KSTR];
   __shared__ int64_t mstart[1025], mpre[1025];
+  __shared__ int64_t tabk[2 * TCH], tabv[2 * TCH];
+  __shared__ __align__(16) bf16_t sink[8];
   __shared__ int sh_keff;
   __shared__ int64_t sh_M;
 
@@ -132,19 +136,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
     drow[m] = dsum;
   }
 
-  TileSrc ts;
-  ts.Kb = (const bf16_t*)a.Kbar;
-  ts.Vb = (const bf16_t*)a.Vbar;
-  ts.Kr = (const bf16_t*)a.Krot;
-  ts.Vl = (const bf16_t*)a.Vloc;
-  ts.mstart = mstart;
-  ts.mpre = mpre;
-  ts.keff = keff;
-  ts.hkv = a.h_kv;
-  ts.g = g;
-  ts.kv0 = kv0;
-  ts.M = M;
-  ts.k_hi = k_hi;
 
   // the smallest causal limit over the block's rows (its first row's)
   const int64_t key_lim_min = M + (int64_t)(Lkv - Lq + rb / G);
@@ -180,7 +171,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
     float m_run[MTW], l_run[MTW];
 #pragma unroll
     for (int m = 0; m < MTW; ++m) { m_run[m] = -INFINITY; l_run[m] = 0.f; }
-    auto lse_math = [&](int buf, int64_t kt) __attribute__((always_inline)) {
+    auto lse_math = [&](int buf, int kt) __attribute__((always_inline)) {
 #pragma unroll
       for (int m = 0; m < MTW; ++m) {
         float s[2][4];
@@ -204,7 +195,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
         }
       }
     };
-    tile_pipeline<(UPT <= 4 ? TILE_RING : 2), D, THREADS, UPT, KSTR, false>(ts, tid, 0, k_hi, Ks[0], Ks[1], Vs[0], Vs[1], lse_math);
+    key_loop<RING, D, THREADS, KSTR, false>(a, g, tid, 0, (int)k_hi, mstart, mpre, keff, M, kv0, tabk, tabv, Ks[0],
+                                            Ks[1], Vs[0], Vs[1], sink, lse_math);
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       float l = l_run[m] + __shfl_xor(l_run[m], 16);
@@ -234,7 +226,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
   for (int m = 0; m < MTW; ++m)
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[m][md] = {0.f, 0.f, 0.f, 0.f};
-  auto dq_math = [&](int buf, int64_t kt) __attribute__((always_inline)) {
+  auto dq_math = [&](int buf, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       float s[2][4];
@@ -272,7 +264,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
       }
     }
   };
-  tile_pipeline<(UPT <= 4 ? TILE_RING : 2), D, THREADS, UPT, KSTR, true>(ts, tid, 0, k_hi, Ks[0], Ks[1], Vs[0], Vs[1], dq_math);
+  key_loop<RING, D, THREADS, KSTR, true>(a, g, tid, 0, (int)k_hi, mstart, mpre, keff, M, kv0, tabk, tabv, Ks[0], Ks[1],
+                                         Vs[0], Vs[1], sink, dq_math);
 
   // lane holds dQ~^T[d = md*16 + g4*4 + i][row cl]; natural-scale gradient = scale * acc
 #pragma unroll

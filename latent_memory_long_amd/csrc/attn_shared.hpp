@@ -1,6 +1,6 @@
 // Pieces shared by the sparse-attention forward (attn.hip) and backward (attn_bwd.hip):
 // the kernel argument block, the global RoPE of the local context, the memory map of a
-// query's selected documents and the staging of 32-key tiles.
+// query's selected documents and the key loop that stages 32-key tiles.
 #pragma once
 
 #include <math.h>
@@ -177,16 +177,6 @@ __device__ __forceinline__ MemMap build_memmap(const int32_t* ids, int k, const 
   return {keff, run};
 }
 
-// Staging of one 32-key tile, K and V row-major.  Key index -> source row: a bank row of
-// the selected document of rank r (mpre[r] <= key < mpre[r+1]) while key < M, else local
-// row key - M.
-struct TileSrc {
-  const bf16_t *Kb, *Vb, *Kr, *Vl;
-  const int64_t *mstart, *mpre;
-  int keff, hkv, g, kv0;
-  int64_t M, k_hi;
-};
-
 // Source row of key `key` of a query; returns the row's element offset for kv head g and
 // whether it is a bank row.
 __device__ __forceinline__ int64_t key_row(const int64_t* mstart, const int64_t* mpre, int keff, int64_t M,
@@ -207,76 +197,114 @@ __device__ __forceinline__ int64_t key_row(const int64_t* mstart, const int64_t*
   return (row * hkv + g) * D;
 }
 
-// 16-byte K units of a tile per thread; stage slot j < UPK holds K unit tid + j*THREADS,
-// slot UPK + j the V unit of the same key and elements, so each key's row is located once.
+// Key -> source of a query's keys [rows of the selected documents in rank order ; local
+// rows], as tables in LDS for TCH consecutive keys of a workgroup's range (a chunk): the
+// element offset of the key's row of kv head g from K-bar and from V-bar (a local row's
+// offset reaches the rotated local K / the local V through the distance between the two
+// allocations).  Two chunk slots alternate.  Lookups are branch-free (binary lifting over
+// the document starts, keff <= 1024), so no control flow sits between the loads in flight.
+constexpr int TCH = 16 * KT;
+
+// 16 bytes as a native vector (a struct copy such as HIP's uint4 would go through memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int D, int THREADS>
-constexpr int tile_upk() { return (KT * (D / 8) + THREADS - 1) / THREADS; }
-
-template <int D, int THREADS, int UPT, bool WITHV>
-__device__ __forceinline__ void tile_fetch(const TileSrc ts, int tid, int64_t kt, uint4 (&stage)[UPT]) {
-  constexpr int UPR = D / 8;
-  constexpr int UPK = tile_upk<D, THREADS>();
-  static_assert(UPT >= (WITHV ? 2 : 1) * UPK, "stage too small");
+__device__ __forceinline__ void build_key_chunk(int64_t* tk, int64_t* tv, int tid, int64_t key0,
+                                                const int64_t* mstart, const int64_t* mpre, int keff, int64_t M,
+                                                int kv0, const AttnK& a, int g) {
+  // local K / V relative to K-bar / V-bar, in elements (all are 2-byte aligned)
+  const int64_t dk = ((int64_t)(uintptr_t)a.Krot - (int64_t)(uintptr_t)a.Kbar) / 2;
+  const int64_t dv = ((int64_t)(uintptr_t)a.Vloc - (int64_t)(uintptr_t)a.Vbar) / 2;
+  for (int i = tid; i < TCH; i += THREADS) {
+    const int64_t key = key0 + i;
+    int lo = 0;  // largest rank t <= keff with mpre[t] <= key (mpre[keff] = M)
 #pragma unroll
-  for (int j = 0; j < UPK; ++j) {
-    const int u = tid + j * THREADS;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-    if (u < KT * UPR) {
-      const int kr = u / UPR, e0 = (u % UPR) * 8;
-      const int64_t key = kt + kr;
-      if (key < ts.k_hi) {
-        bool bank;
-        int64_t row;
-        const int64_t off = key_row(ts.mstart, ts.mpre, ts.keff, ts.M, key, ts.kv0, ts.hkv, ts.g, D, bank, row) + e0;
-        kv = *reinterpret_cast<const uint4*>((bank ? ts.Kb : ts.Kr) + off);
-        if (WITHV) vv = *reinterpret_cast<const uint4*>((bank ? ts.Vb : ts.Vl) + off);
-      }
+    for (int step = 1024; step > 0; step >>= 1) {
+      const int t = min(lo + step, keff);
+      lo = mpre[t] <= key ? t : lo;
     }
-    stage[j] = kv;
-    if (WITHV) stage[UPK + j] = vv;
+    const bool bank = lo < keff;
+    const int64_t row = bank ? mstart[lo] + (key - mpre[lo]) : kv0 + (key - M);
+    const int64_t off = (row * a.h_kv + g) * D;
+    tk[i] = bank ? off : dk + off;
+    tv[i] = bank ? off : dv + off;
   }
 }
 
-template <int D, int THREADS, int UPT, int KSTR, bool WITHV>
-__device__ __forceinline__ void tile_commit(int tid, const uint4 (&stage)[UPT], bf16_t* Ks, bf16_t* Vs) {
-  constexpr int UPR = D / 8;
-  constexpr int UPK = tile_upk<D, THREADS>();
-#pragma unroll
-  for (int j = 0; j < UPK; ++j) {
-    const int u = tid + j * THREADS;
-    if (u < KT * UPR) {
-      const int kr = u / UPR, e0 = (u % UPR) * 8;
-      *reinterpret_cast<uint4*>(&Ks[kr * KSTR + e0]) = stage[j];
-      if (WITHV) *reinterpret_cast<uint4*>(&Vs[kr * KSTR + e0]) = stage[UPK + j];
-    }
-  }
-}
-
-// The key loop of the attention kernels: tiles k_lo, k_lo + KT, ... below k_hi are gathered
-// into a ring of RING register stages, RING tiles ahead of their use, and written to the LDS
-// buffer of their parity just before their math (RING even: a tile's buffer alternates).
-// One barrier per tile: a wave writes tile i's buffer only after every wave has passed tile
-// i-1's barrier, hence finished tile i-2's math on that buffer.  (The barrier waits for the
-// LDS traffic only; the gathers of the tiles ahead stay in flight across it.)
-constexpr int TILE_RING = 4;
-
-template <int RING, int D, int THREADS, int UPT, int KSTR, bool WITHV, typename F>
-__device__ __forceinline__ void tile_pipeline(const TileSrc& ts, int tid, int64_t k_lo, int64_t k_hi,
-                                              bf16_t* Ks0, bf16_t* Ks1, bf16_t* Vs0, bf16_t* Vs1, F&& math) {
+// The key loop of the attention kernels over keys [k_lo, k_lo + n_keys) of one (query, kv
+// head): 32-key tiles of K (and V) gathered into a ring of RING register stages, RING tiles
+// ahead of their use, written to the LDS buffers of their parity, then math(buf, rel) for
+// each tile (rel: the tile's first key relative to k_lo; called by every wave).  One
+// barrier per tile: a wave writes tile i's buffer only after every wave has passed tile
+// i-1's barrier, hence finished tile i-2's math on that buffer.  The loads are
+// unconditional -- keys past the range re-read its last key (V zeroed when the tile is
+// written to LDS) -- and the ring runs in whole groups with no exit inside one, so the
+// wait for the oldest tile can count the younger tiles' loads as still in flight.  The
+// offset tables are rebuilt a chunk ahead: entering chunk c, chunk c+1 replaces chunk
+// c-1, whose last lookup came before that tile's barrier.
+template <int RING, int D, int THREADS, int KSTR, bool WITHV, typename F>
+__device__ __forceinline__ void key_loop(const AttnK& a, int g, int tid, int64_t k_lo, int n_keys,
+                                         const int64_t* mstart, const int64_t* mpre, int keff, int64_t M, int kv0,
+                                         int64_t* tabk, int64_t* tabv, bf16_t* Ks0, bf16_t* Ks1, bf16_t* Vs0,
+                                         bf16_t* Vs1, bf16_t* sink, F&& math) {
   static_assert(RING % 2 == 0, "tiles alternate between two LDS buffers");
-  uint4 st[RING][UPT];
+  constexpr int UPR = D / 8;                                // 16-byte units per key row
+  constexpr int UPK = (KT * UPR + THREADS - 1) / THREADS;  // units per thread per tile
+  constexpr int NS = WITHV ? 2 * UPK : UPK;
+  if (n_keys <= 0) return;  // uniform
+  // this thread's units of a tile: key kr[j] of the tile, elements e0[j] .. + 7; units past
+  // the tile go to a sink (no branch: one here would make the compiler drain the ring)
+  int kr[UPK], e0[UPK], ko[UPK];
+  bool unit[UPK];
 #pragma unroll
-  for (int r = 0; r < RING; ++r)
-    if (k_lo + r * KT < k_hi) tile_fetch<D, THREADS, UPT, WITHV>(ts, tid, k_lo + r * KT, st[r]);
-  for (int64_t k0 = k_lo; k0 < k_hi; k0 += RING * KT) {
+  for (int j = 0; j < UPK; ++j) {
+    const int u = min(tid + j * THREADS, KT * UPR - 1);  // threads past the tile repeat its last unit
+    kr[j] = u / UPR;
+    e0[j] = (u % UPR) * 8;
+    ko[j] = kr[j] * KSTR + e0[j];
+    unit[j] = (KT * UPR) % THREADS == 0 || tid + j * THREADS < KT * UPR;
+  }
+  const bf16_t* kb = (const bf16_t*)a.Kbar;
+  const bf16_t* vb = (const bf16_t*)a.Vbar;
+  auto fetch = [&](int rel, u32x4 (&st)[NS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < UPK; ++j) {
+      const int kc = min(rel + kr[j], n_keys - 1);
+      const int e = kc & (2 * TCH - 1);  // chunk slot (kc / TCH) & 1, entry kc % TCH
+      st[j] = *reinterpret_cast<const u32x4*>(kb + (tabk[e] + e0[j]));
+      if (WITHV) st[UPK + j] = *reinterpret_cast<const u32x4*>(vb + (tabv[e] + e0[j]));
+    }
+  };
+  build_key_chunk<D, THREADS>(tabk, tabv, tid, k_lo, mstart, mpre, keff, M, kv0, a, g);
+  __syncthreads();
+  u32x4 st[RING][NS];
+#pragma unroll
+  for (int r = 0; r < RING; ++r) fetch(r * KT, st[r]);
+  // chunk 1 goes to the other slot; its first use comes many barriers later
+  build_key_chunk<D, THREADS>(tabk + TCH, tabv + TCH, tid, k_lo + TCH, mstart, mpre, keff, M, kv0, a, g);
+  for (int t0 = 0; t0 < n_keys; t0 += RING * KT) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
-      const int64_t kt = k0 + r * KT;
-      if (kt >= k_hi) break;  // uniform
-      tile_commit<D, THREADS, UPT, KSTR, WITHV>(tid, st[r], (r & 1) ? Ks1 : Ks0, (r & 1) ? Vs1 : Vs0);
+      const int rel = t0 + r * KT;  // this tile's first key, relative to k_lo
+      bf16_t* Kd = (r & 1) ? Ks1 : Ks0;
+      bf16_t* Vd = (r & 1) ? Vs1 : Vs0;
+#pragma unroll
+      for (int j = 0; j < UPK; ++j) {
+        *reinterpret_cast<u32x4*>(unit[j] ? Kd + ko[j] : sink) = st[r][j];
+        if (WITHV) {  // V of keys past the range: zeros (probability 0 times V must stay 0)
+          const uint32_t in = rel + kr[j] < n_keys ? ~0u : 0u;
+          *reinterpret_cast<u32x4*>(unit[j] ? Vd + ko[j] : sink) = st[r][UPK + j] & in;
+        }
+      }
       __syncthreads();
-      if (kt + RING * KT < k_hi) tile_fetch<D, THREADS, UPT, WITHV>(ts, tid, kt + RING * KT, st[r]);
-      math(r & 1, kt);
+      const int relf = rel + RING * KT;  // the tile fetched now
+      fetch(relf, st[r]);
+      if (relf % TCH == 0 && relf + TCH < n_keys) {  // uniform branch, LDS only
+        const int slot = ((relf / TCH + 1) & 1) * TCH;
+        build_key_chunk<D, THREADS>(tabk + slot, tabv + slot, tid, k_lo + relf + TCH, mstart, mpre, keff, M, kv0, a,
+                                    g);
+      }
+      if (rel < n_keys) math(r & 1, rel);  // tiles past the range only skip the math
     }
   }
 }
