@@ -49,17 +49,6 @@ __device__ __forceinline__ float row_max4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Workgroup -> (kv pair, row block, key split).  Workgroups reach the eight XCDs round-robin
-// in linear order; the row blocks and splits of one (query, kv head) pair are placed on one
-// XCD back to back, so the selected K-bar / V-bar rows that all of them gather come from HBM
-// once and from that XCD's L2 after.
-__device__ __forceinline__ bool fwd_place(int n_pairs, int nsub, int& pair, int& sub) {
-  const int L = (int)blockIdx.x;
-  pair = (L >> 3) / nsub * 8 + (L & 7);
-  sub = (L >> 3) % nsub;
-  return pair < n_pairs;
-}
-
 template <int D, int NW, int MTW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma(AttnK a, int nsub) {
   constexpr int KK = D / 32;
@@ -83,7 +72,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ int64_t sh_M;
 
   int pair, sub;
-  if (!fwd_place(a.n_queries * a.h_kv, nsub, pair, sub)) return;
+  if (!place_pair(a.n_queries * a.h_kv, nsub, pair, sub)) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int cl = lane & 15, g4 = lane >> 4;
   const int b = pair / a.h_kv, g = pair % a.h_kv;

@@ -60,7 +60,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 template <int D, int NW, int MTW>
-__global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq(BwdK bk, int nsub) {
   const AttnK& a = bk.f;
   constexpr int KK = D / 32;
   constexpr int MD = D / 16;
@@ -77,15 +77,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
   __shared__ int sh_keff;
   __shared__ int64_t sh_M;
 
+  int pair, sub;
+  if (!place_pair(a.n_queries * a.h_kv, nsub, pair, sub)) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int cl = lane & 15, g4 = lane >> 4;
-  const int b = blockIdx.z, g = blockIdx.y;
+  const int b = pair / a.h_kv, g = pair % a.h_kv;
   const int G = a.hq / a.h_kv;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int kv0 = a.kv_off[b], Lkv = a.kv_off[b + 1] - kv0;
   const int nrows = Lq * G;
-  const int rb = blockIdx.x * ROWS;
+  const int rb = sub * ROWS;
   if (rb >= nrows) return;
+  // this wave's rows: MTW 16-row tiles; a wave with none skips the math
+  const bool wave_rows = rb + w * MTW * 16 < nrows;
 
   if (w == 0) {
     MemMap mm = build_memmap(a.ids + (int64_t)b * a.k, a.k, a.chunk_off, mstart, mpre);
@@ -140,28 +144,36 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
   // the smallest causal limit over the block's rows (its first row's)
   const int64_t key_lim_min = M + (int64_t)(Lkv - Lq + rb / G);
 
-  // S^T for row tile m and key tile kt from Ks: s[n][i] = logit (log2 units) of key
-  // kt + n*16 + g4*4 + i for row cl, -inf where not visible.  A tile whose keys every row
-  // of the block sees skips the masks.
-  auto logits = [&](const bf16_t* ks, int m, int64_t kt, float (&s)[2][4]) __attribute__((always_inline)) {
+  // S^T of key tile kt for every row tile of the wave (each K operand read once for all):
+  // s[m][n][i] = logit (log2 units) of key kt + n*16 + g4*4 + i for row cl of tile m, -inf
+  // where not visible.  A tile whose keys every row of the block sees skips the masks.
+  auto logits = [&](const bf16_t* ks, int kt, float (&s)[MTW][2][4]) __attribute__((always_inline)) {
+    f32x4_t acc[MTW][2];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) acc[m][0] = acc[m][1] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const bf16x8_t kw =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&ks[(n * 16 + cl) * KSTR + kk * 32 + g4 * 8]));
+#pragma unroll
+        for (int m = 0; m < MTW; ++m) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw, Qf[m][kk], acc[m][n], 0, 0, 0);
+      }
     const bool full = kt + KT <= k_hi && kt + KT - 1 <= key_lim_min && rb + ROWS <= nrows;
     // limits relative to kt, clamped into int range: visible iff rel < hi_rel && rel <= lim_rel
     const int hi_rel = (int)(k_hi - kt < KT ? k_hi - kt : KT);
-    const int64_t lr = key_lim[m] - kt;
-    const int lim_rel = row_ok[m] ? (int)(lr < -1 ? -1 : (lr > KT ? KT : lr)) : -1;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MTW; ++m) {
+      const int64_t lr = key_lim[m] - kt;
+      const int lim_rel = row_ok[m] ? (int)(lr < -1 ? -1 : (lr > KT ? KT : lr)) : -1;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(&ks[(n * 16 + cl) * KSTR + kk * 32 + g4 * 8]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), Qf[m][kk], acc, 0, 0, 0);
-      }
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rel = n * 16 + g4 * 4 + i;
-        s[n][i] = (full || (rel < hi_rel && rel <= lim_rel)) ? acc[i] * sl2 : -INFINITY;
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int rel = n * 16 + g4 * 4 + i;
+          s[m][n][i] = (full || (rel < hi_rel && rel <= lim_rel)) ? acc[m][n][i] * sl2 : -INFINITY;
+        }
     }
   };
 
@@ -172,15 +184,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
 #pragma unroll
     for (int m = 0; m < MTW; ++m) { m_run[m] = -INFINITY; l_run[m] = 0.f; }
     auto lse_math = [&](int buf, int kt) __attribute__((always_inline)) {
+      if (!wave_rows) return;
+      float s[MTW][2][4];
+      logits(Ks[buf], kt, s);
 #pragma unroll
       for (int m = 0; m < MTW; ++m) {
-        float s[2][4];
-        logits(Ks[buf], m, kt, s);
         float mx = -INFINITY;
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[n][i]);
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[m][n][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run[m], mx);
@@ -189,7 +202,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
 #pragma unroll
           for (int n = 0; n < 2; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ps += exp2_hw(s[n][i] - m_new);
+            for (int i = 0; i < 4; ++i) ps += exp2_hw(s[m][n][i] - m_new);
           l_run[m] = l_run[m] * exp2_hw(m_run[m] - m_new) + ps;
           m_run[m] = m_new;
         }
@@ -220,48 +233,56 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq(BwdK bk) {
     }
   }
 
-  // ---- pass 2: dQ~^T = K^T dS^T ----
+  // ---- pass 2: dQ~^T = K^T dS^T (K, V and K^T operands read once for all row tiles) ----
   f32x4_t acc[MTW][MD];
 #pragma unroll
   for (int m = 0; m < MTW; ++m)
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[m][md] = {0.f, 0.f, 0.f, 0.f};
   auto dq_math = [&](int buf, int kt) __attribute__((always_inline)) {
+    if (!wave_rows) return;
+    float s[MTW][2][4];
+    logits(Ks[buf], kt, s);
+    f32x4_t dp[MTW][2];
 #pragma unroll
-    for (int m = 0; m < MTW; ++m) {
-      float s[2][4];
-      logits(Ks[buf], m, kt, s);
-      float ds[2][4];
+    for (int m = 0; m < MTW; ++m) dp[m][0] = dp[m][1] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
+        const bf16x8_t vw =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&Vs[buf][(n * 16 + cl) * KSTR + kk * 32 + g4 * 8]));
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const uint4 vw = *reinterpret_cast<const uint4*>(&Vs[buf][(n * 16 + cl) * KSTR + kk * 32 + g4 * 8]);
-          dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), dOf[m][kk], dp, 0, 0, 0);
-        }
+        for (int m = 0; m < MTW; ++m) dp[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vw, dOf[m][kk], dp[m][n], 0, 0, 0);
+      }
+    bf16x8_t dSf[MTW];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      float ds[2][4];
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2_hw(s[n][i] - lse[m]);  // 0 where not visible (s = -inf)
-          ds[n][i] = p * (dp[i] - drow[m]);
+          const float p = exp2_hw(s[m][n][i] - lse[m]);  // 0 where not visible (s = -inf)
+          ds[n][i] = p * (dp[m][n][i] - drow[m]);
         }
-      }
       // dS^T operand: k-slot g4*8 + j <-> key g4*4 + j (j < 4), 16 + g4*4 + (j-4) (j >= 4)
       uint4 pw;
       pw.x = pack_bf16x2(ds[0][0], ds[0][1]);
       pw.y = pack_bf16x2(ds[0][2], ds[0][3]);
       pw.z = pack_bf16x2(ds[1][0], ds[1][1]);
       pw.w = pack_bf16x2(ds[1][2], ds[1][3]);
-      const bf16x8_t dSf = __builtin_bit_cast(bf16x8_t, pw);
+      dSf[m] = __builtin_bit_cast(bf16x8_t, pw);
+    }
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        // A operand K^T: element md*16 + cl over keys g4*4 .. +3 and 16 + g4*4 .. +3
-        const bf16_t* kr = &Ks[buf][(g4 * 4 + (cl >> 2)) * KSTR + md * 16 + (cl & 3) * 4];
-        const uint2 k0 = lds_read_tr16(kr);
-        const uint2 k1 = lds_read_tr16(kr + 16 * KSTR);
-        const bf16x8_t Kf = __builtin_bit_cast(bf16x8_t, make_uint4(k0.x, k0.y, k1.x, k1.y));
-        acc[m][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf, dSf, acc[m][md], 0, 0, 0);
-      }
+    for (int md = 0; md < MD; ++md) {
+      // A operand K^T: element md*16 + cl over keys g4*4 .. +3 and 16 + g4*4 .. +3
+      const bf16_t* kr = &Ks[buf][(g4 * 4 + (cl >> 2)) * KSTR + md * 16 + (cl & 3) * 4];
+      const uint2 k0 = lds_read_tr16(kr);
+      const uint2 k1 = lds_read_tr16(kr + 16 * KSTR);
+      const bf16x8_t Kf = __builtin_bit_cast(bf16x8_t, make_uint4(k0.x, k0.y, k1.x, k1.y));
+#pragma unroll
+      for (int m = 0; m < MTW; ++m) acc[m][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kf, dSf[m], acc[m][md], 0, 0, 0);
     }
   };
   key_loop<RING, D, THREADS, KSTR, true>(a, g, tid, 0, (int)k_hi, mstart, mpre, keff, M, kv0, tabk, tabv, Ks[0], Ks[1],
@@ -611,12 +632,15 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
   const int rows = min(attn_rows_per_block(f.max_q_len, G), 128);
   const int rblocks = (f.max_q_len * G + rows - 1) / rows;
   if (rblocks > 0) {
-    dim3 grid((unsigned)rblocks, (unsigned)f.h_kv, (unsigned)f.n_queries);
+    // the row blocks of a (query, kv head) on one XCD (place_pair); two 16-row tiles per
+    // wave at 128 rows, so each K / V operand read serves both
+    const int n_pairs = f.n_queries * f.h_kv;
+    const dim3 grid((unsigned)(((n_pairs + 7) / 8) * 8 * rblocks));
     switch (rows) {
-      case 16: hipLaunchKernelGGL((bwd_dq<D, 1, 1>), grid, dim3(64), 0, s, k); break;
-      case 32: hipLaunchKernelGGL((bwd_dq<D, 2, 1>), grid, dim3(128), 0, s, k); break;
-      case 64: hipLaunchKernelGGL((bwd_dq<D, 4, 1>), grid, dim3(256), 0, s, k); break;
-      default: hipLaunchKernelGGL((bwd_dq<D, 8, 1>), grid, dim3(512), 0, s, k); break;
+      case 16: hipLaunchKernelGGL((bwd_dq<D, 1, 1>), grid, dim3(64), 0, s, k, rblocks); break;
+      case 32: hipLaunchKernelGGL((bwd_dq<D, 2, 1>), grid, dim3(128), 0, s, k, rblocks); break;
+      case 64: hipLaunchKernelGGL((bwd_dq<D, 4, 1>), grid, dim3(256), 0, s, k, rblocks); break;
+      default: hipLaunchKernelGGL((bwd_dq<D, 4, 2>), grid, dim3(256), 0, s, k, rblocks); break;
     }
   }
   dim3 gkv((unsigned)k.kblocks, (unsigned)f.h_kv, (unsigned)f.n_queries);

@@ -137,6 +137,18 @@ __global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
   }
 }
 
+// Workgroup -> (kv pair, sub-block) of a 1-D grid of ceil(n_pairs / 8) * 8 * nsub
+// workgroups.  Workgroups reach the eight XCDs round-robin in linear order; the nsub
+// sub-blocks (row blocks, key splits) of one (query, kv head) pair are placed on one XCD
+// back to back, so the selected K-bar / V-bar rows that all of them gather come from HBM
+// once and from that XCD's L2 after.  False for the padding workgroups.
+__device__ __forceinline__ bool place_pair(int n_pairs, int nsub, int& pair, int& sub) {
+  const int L = (int)blockIdx.x;
+  pair = (L >> 3) / nsub * 8 + (L & 7);
+  sub = (L >> 3) % nsub;
+  return pair < n_pairs;
+}
+
 // Memory layout of one query: the selected documents' bank rows in rank order.
 struct MemMap {
   int keff;
