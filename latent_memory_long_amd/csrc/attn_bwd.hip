@@ -322,9 +322,11 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
   __shared__ int sh_keff;
   __shared__ int64_t sh_M;
 
+  int pair, kblock;
+  if (!place_pair(a.n_queries * a.h_kv, bk.kblocks, pair, kblock)) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int cl = lane & 15, g4 = lane >> 4;
-  const int b = blockIdx.z, g = blockIdx.y;
+  const int b = pair / a.h_kv, g = pair % a.h_kv;
   const int G = a.hq / a.h_kv;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int kv0 = a.kv_off[b], Lkv = a.kv_off[b + 1] - kv0;
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
   const int64_t M = sh_M;
   const int64_t NK = M + Lkv;
   const int64_t nchunk = (NK + KEYS - 1) / KEYS;
-  const int64_t c0 = nchunk * blockIdx.x / bk.kblocks, c1 = nchunk * (blockIdx.x + 1) / bk.kblocks;
+  const int64_t c0 = nchunk * kblock / bk.kblocks, c1 = nchunk * (kblock + 1) / bk.kblocks;
   const float sl2 = a.scale_log2;
   const bf16_t* Kb = (const bf16_t*)a.Kbar;
   const bf16_t* Vb = (const bf16_t*)a.Vbar;
@@ -643,7 +645,10 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
       default: hipLaunchKernelGGL((bwd_dq<D, 4, 2>), grid, dim3(256), 0, s, k, rblocks); break;
     }
   }
-  dim3 gkv((unsigned)k.kblocks, (unsigned)f.h_kv, (unsigned)f.n_queries);
+  // the key blocks of a (query, kv head) on one XCD (place_pair): they all stream the pair's
+  // query rows, which that XCD's L2 then holds
+  const int n_pairs = f.n_queries * f.h_kv;
+  const dim3 gkv((unsigned)(((n_pairs + 7) / 8) * 8 * k.kblocks));
   hipLaunchKernelGGL((bwd_dkv<D>), gkv, dim3(64 * DKV_NW), 0, s, k);
   if (nq_blocks + nk_blocks > 0)
     hipLaunchKernelGGL((rope_unrotate<D>), dim3(nq_blocks + nk_blocks), dim3(256), 0, s, k.f, r.dQ, r.dKloc,
