@@ -59,7 +59,11 @@ typedef enum {
   MSA_ERR_IO = 5           /* a bank file could not be written, read or verified     */
 } msa_status;
 
-typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+/* Element type of the tensors.  The type is a plain 32-bit integer rather than an enum so
+ * that any value a caller passes is well defined in C++ and reaches argument validation,
+ * which rejects values other than these two with MSA_ERR_UNSUPPORTED. */
+enum { MSA_F32 = 0, MSA_BF16 = 1 };
+typedef int32_t msa_dtype;
 
 /* Which tensors msa_pool rotates with document-wise RoPE.  The default reading rotates
  * K only (keys carry positions; V and the routing keys Kr are left as they are). */

@@ -15,7 +15,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmsa.so")
+# MSA_LIBRARY names another build of the same library (the host-sanitizer build of the
+# tests); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP, MSA_ERR_IO = range(6)
 MSA_F32, MSA_BF16 = 0, 1
