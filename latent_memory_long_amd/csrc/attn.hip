@@ -125,25 +125,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int64_t pos = (int64_t)keff + (Lkv - Lq) + t_of[m];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int d0 = kk * 32 + g4 * 8;                 // first of the lane's 8 elements
-      const bool low = d0 < D / 2;                     // x_i (else x_{i+D/2})
-      const int i0 = low ? d0 : d0 - D / 2;            // first pair index
-      float x[8], y[8], o[8];
-      Elem<bf16_t>::load8(qp + d0, x);
-      Elem<bf16_t>::load8(qp + (low ? d0 + D / 2 : i0), y);
-      const float* cp = a.rtab + pos * (D / 2) + i0;
-      const float* sp = cp + a.n_pos * (D / 2);
-      const float4 c0 = *reinterpret_cast<const float4*>(cp), c1 = *reinterpret_cast<const float4*>(cp + 4);
-      const float4 s0 = *reinterpret_cast<const float4*>(sp), s1 = *reinterpret_cast<const float4*>(sp + 4);
-      const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = low ? rot_lo(x[j], y[j], c[j], sn[j]) : rot_hi(y[j], x[j], c[j], sn[j]);
-      uint4 w;
-      w.x = f32x2_to_bf16x2(o[0], o[1]);
-      w.y = f32x2_to_bf16x2(o[2], o[3]);
-      w.z = f32x2_to_bf16x2(o[4], o[5]);
-      w.w = f32x2_to_bf16x2(o[6], o[7]);
+      const uint4 w = rope_load8<D>(qp, kk * 32 + g4 * 8, pos, a.rtab, a.n_pos);
       Qf[m][kk] = __builtin_bit_cast(bf16x8_t, row_ok[m] ? w : make_uint4(0, 0, 0, 0));
     }
   }

@@ -12,7 +12,8 @@
 // bank-shaped arrays (a row chosen by several queries collects every query's share).
 //
 // Kernels (bf16 inputs, float32 gradients, MFMA with float32 accumulation):
-//  * rope_local (shared with the forward): rotated Q and local K into the workspace.
+//  * rope_table and rope_local (shared with the forward): the cos / sin table of every
+//    position in use, and Q and the local K rotated with it into the workspace.
 //  * bwd_dq: one workgroup per (query, kv head, block of query rows), with the forward's key
 //    loop (attn_shared.hpp's key_loop).
 //    Unless the forward's per-row log-sum-exp is passed in, a first pass over the key tiles
@@ -26,7 +27,9 @@
 //    every lane with probabilities of one key over 4 rows of each 16-row half, which are the
 //    A operand of the 16x16x32 products dV += P^T dO and dK += dS^T Q~; their B operands are
 //    read transposed from the row-major stage.
-//  * rope_unrotate: turns dQ and the local dK back to the un-rotated inputs, in place.
+//  The gradients of the un-rotated Q and local K are turned back by the same angles in the
+//  epilogues of bwd_dq and bwd_dkv, where each lane holds both elements of every rotation
+//  pair it writes.
 #include <math.h>
 
 #include "attn_shared.hpp"
@@ -37,7 +40,7 @@ namespace msa {
 namespace {
 
 struct BwdK {
-  AttnK f;         // forward arguments; f.Qrot / f.Krot are the rotated copies
+  AttnK f;         // forward arguments; f.Qrot / f.Krot are the rotated copies, f.rtab the cos / sin table
   const void* O;   // forward output [total_q, hq, D]
   const void* dO;  // [total_q, hq, D]
   float* dQ;       // [total_q, hq, D]
@@ -288,15 +291,33 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   key_loop<RING, D, THREADS, KSTR, true>(a, g, tid, 0, (int)k_hi, mstart, mpre, keff, M, kv0, tabk, tabv, Ks[0], Ks[1],
                                          Vs[0], Vs[1], sink, dq_math);
 
-  // lane holds dQ~^T[d = md*16 + g4*4 + i][row cl]; natural-scale gradient = scale * acc
+  // lane holds dQ~^T[d = md*16 + g4*4 + i][row cl] for every md, so both elements of each
+  // rotation pair (d, d + D/2); the gradient of the un-rotated Q is the natural-scale
+  // gradient scale * acc turned back by the row's angle
 #pragma unroll
   for (int m = 0; m < MTW; ++m) {
     if (!row_ok[m]) continue;
+    const int64_t pos = (int64_t)keff + (Lkv - Lq) + t_of[m];
     float* o = bk.dQ + ((int64_t)(q0 + t_of[m]) * a.hq + hq_of[m]) * D + g4 * 4;
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
-      *reinterpret_cast<float4*>(o + md * 16) = make_float4(acc[m][md][0] * bk.scale, acc[m][md][1] * bk.scale,
-                                                           acc[m][md][2] * bk.scale, acc[m][md][3] * bk.scale);
+    for (int md = 0; md < MD / 2; ++md) {
+      const int i0 = md * 16 + g4 * 4;  // pair index of the lane's first element
+      const float4 c4 = *reinterpret_cast<const float4*>(a.rtab + pos * (D / 2) + i0);
+      const float4 s4 = *reinterpret_cast<const float4*>(a.rtab + (a.n_pos + pos) * (D / 2) + i0);
+      const float c[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+      float lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // rotation by the negative angle
+        const float x = acc[m][md][i] * bk.scale, y = acc[m][md + MD / 2][i] * bk.scale;
+        lo[i] = rot_lo(x, y, c[i], -sn[i]);
+        hi[i] = rot_hi(x, y, c[i], -sn[i]);
+      }
+      *reinterpret_cast<float4*>(o + md * 16) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+      *reinterpret_cast<float4*>(o + (md + MD / 2) * 16) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+      // a compiler-only fence: the next pair group's table loads are not hoisted above it,
+      // so their registers are taken only as the accumulators above are freed
+      __asm__ volatile("" ::: "memory");
+    }
   }
 }
 
@@ -512,76 +533,29 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
         bool bank;
         int64_t row;
         const int64_t off = key_row(mstart, mpre, keff, M, key, kv0, a.h_kv, g, D, bank, row) + cl;
+        if (bank) {
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const float gk = dK[nt][md][i] * bk.scale, gv = dV[nt][md][i];
-          if (bank) {
-            atomicAdd(bk.dKb + off + md * 16, gk);
-            atomicAdd(bk.dVb + off + md * 16, gv);
-          } else {
-            bk.dKl[off + md * 16] = gk;
-            bk.dVl[off + md * 16] = gv;
+          for (int md = 0; md < MD; ++md) {
+            atomicAdd(bk.dKb + off + md * 16, dK[nt][md][i] * bk.scale);
+            atomicAdd(bk.dVb + off + md * 16, dV[nt][md][i]);
           }
+        } else {
+          // a local key: the lane holds both elements of each rotation pair (md, md + MD/2);
+          // the un-rotated gradient turns back by the key's angle (position keff + index)
+          const int64_t pos = (int64_t)keff + (key - M);
+#pragma unroll
+          for (int md = 0; md < MD / 2; ++md) {
+            const float c = a.rtab[pos * (D / 2) + md * 16 + cl];
+            const float sn = a.rtab[(a.n_pos + pos) * (D / 2) + md * 16 + cl];
+            const float x = dK[nt][md][i] * bk.scale, y = dK[nt][md + MD / 2][i] * bk.scale;
+            bk.dKl[off + md * 16] = rot_lo(x, y, c, -sn);
+            bk.dKl[off + (md + MD / 2) * 16] = rot_hi(x, y, c, -sn);
+          }
+#pragma unroll
+          for (int md = 0; md < MD; ++md) bk.dVl[off + md * 16] = dV[nt][md][i];
         }
       }
     }
-  }
-}
-
-// ---- turning the gradients of the rotated Q and local K back, in place ---------------
-template <int D>
-__global__ __launch_bounds__(256) void rope_unrotate(AttnK a, float* dQ, float* dKl, int nq_blocks) {
-  __shared__ float cs_tab[RPW][D / 2], sn_tab[RPW][D / 2];
-  __shared__ int64_t row_pos[RPW];
-  const bool is_q = blockIdx.x < (unsigned)nq_blocks;
-  const int64_t r0 = (int64_t)(is_q ? blockIdx.x : blockIdx.x - nq_blocks) * RPW;
-  const int64_t total = is_q ? a.total_q : a.total_kv;
-  const int heads = is_q ? a.hq : a.h_kv;
-  float* x = is_q ? dQ : dKl;
-  const int32_t* off = is_q ? a.q_off : a.kv_off;
-  const int tid = threadIdx.x;
-  if (tid < RPW) {
-    const int64_t r = r0 + tid;
-    int64_t pos = -1;
-    if (r < total) {
-      const int b = find_query(off, a.n_queries, r);
-      const int keff = count_valid_ids(a.ids + (int64_t)b * a.k, a.k);
-      const int64_t Lq = a.q_off[b + 1] - a.q_off[b];
-      const int64_t Lkv = a.kv_off[b + 1] - a.kv_off[b];
-      pos = is_q ? keff + (Lkv - Lq) + (r - off[b]) : keff + (r - off[b]);
-    }
-    row_pos[tid] = pos;
-  }
-  __syncthreads();
-  for (int e = tid; e < RPW * (D / 2); e += blockDim.x) {
-    const int rr = e / (D / 2), i = e % (D / 2);
-    const double th = pow((double)a.rope_base, -2.0 * (double)i / (double)D);
-    double sn = 0.0, cs = 1.0;
-    if (row_pos[rr] >= 0) sincos((double)row_pos[rr] * th, &sn, &cs);
-    cs_tab[rr][i] = (float)cs;
-    sn_tab[rr][i] = (float)sn;
-  }
-  __syncthreads();
-  const int units = RPW * heads * (D / 8);
-  for (int u = tid; u < units; u += blockDim.x) {
-    const int rr = u / (heads * (D / 8));
-    const int rem = u % (heads * (D / 8));
-    const int h = rem / (D / 8), i0 = (rem % (D / 8)) * 4;
-    const int64_t r = r0 + rr;
-    if (r >= total) continue;
-    float* p = x + (r * heads + h) * D;
-    const float4 lo = *reinterpret_cast<const float4*>(p + i0);
-    const float4 hi = *reinterpret_cast<const float4*>(p + i0 + D / 2);
-    const float l[4] = {lo.x, lo.y, lo.z, lo.w}, hh[4] = {hi.x, hi.y, hi.z, hi.w};
-    float ol[4], oh[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {  // rotation by the negative angle
-      const float c = cs_tab[rr][i0 + q], s = sn_tab[rr][i0 + q];
-      ol[q] = l[q] * c + hh[q] * s;
-      oh[q] = hh[q] * c - l[q] * s;
-    }
-    *reinterpret_cast<float4*>(p + i0) = make_float4(ol[0], ol[1], ol[2], ol[3]);
-    *reinterpret_cast<float4*>(p + i0 + D / 2) = make_float4(oh[0], oh[1], oh[2], oh[3]);
   }
 }
 
@@ -612,6 +586,10 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
   ws += align256((size_t)f.total_q * f.hq * D * 2);
   k.f.Krot = ws;
   ws += align256((size_t)f.total_kv * f.h_kv * D * 2);
+  // cos / sin of every position a row or local key can take (< k + total_kv)
+  k.f.n_pos = (int64_t)f.k + f.total_kv;
+  k.f.rtab = (const float*)ws;
+  ws += align256((size_t)(1024 + f.total_kv) * D * 4);
   k.lse = (float*)ws;
   ws += align256((size_t)f.total_q * f.hq * 4);
   k.drow = (float*)ws;
@@ -626,6 +604,13 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
   k.scale = scale;
   k.kblocks = 16;
 
+  {
+    const int64_t n = k.f.n_pos * (D / 2);
+    hipLaunchKernelGGL((rope_table<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float*)k.f.rtab,
+                       k.f.n_pos, k.f.rope_base);
+  }
+  // Q and the local K rotated once per row with the table: bwd_dkv reads every query row
+  // once per key block, so rotating them in the kernels would repeat the work many times
   const int nq_blocks = (int)((f.total_q + RPW - 1) / RPW);
   const int nk_blocks = (int)((f.total_kv + RPW - 1) / RPW);
   if (nq_blocks + nk_blocks > 0)
@@ -650,17 +635,15 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
   const int n_pairs = f.n_queries * f.h_kv;
   const dim3 gkv((unsigned)(((n_pairs + 7) / 8) * 8 * k.kblocks));
   hipLaunchKernelGGL((bwd_dkv<D>), gkv, dim3(64 * DKV_NW), 0, s, k);
-  if (nq_blocks + nk_blocks > 0)
-    hipLaunchKernelGGL((rope_unrotate<D>), dim3(nq_blocks + nk_blocks), dim3(256), 0, s, k.f, r.dQ, r.dKloc,
-                       nq_blocks);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(int64_t total_q, int64_t total_kv, int hq, int h_kv, int d) {
+  // rotated Q and local K, the cos / sin table (k <= 1024), per-row log-sum-exp and rowsum(dO O)
   return align256((size_t)total_q * hq * d * 2) + align256((size_t)total_kv * h_kv * d * 2) +
-         2 * align256((size_t)total_q * hq * 4);
+         align256((size_t)(1024 + total_kv) * d * 4) + 2 * align256((size_t)total_q * hq * 4);
 }
 
 hipError_t launch_sparse_attn_backward(const AttnBwdArgs& r, hipStream_t s) {

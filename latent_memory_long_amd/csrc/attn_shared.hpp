@@ -72,6 +72,33 @@ __global__ __launch_bounds__(256) void rope_table(float* tab, int64_t n_pos, flo
   tab[e] = (float)cs;
   tab[n_pos * (D / 2) + e] = (float)sn;
 }
+
+
+// Elements d0 .. d0+7 of a bf16 row rotated to position pos with the rope_table values,
+// as one bf16 MFMA operand: the lane also loads the pair partners (d +- D/2) of its 8
+// elements.  The same roundings as rope_local (rot_lo / rot_hi), then one rounding to bf16.
+template <int D>
+__device__ __forceinline__ uint4 rope_load8(const bf16_t* row, int d0, int64_t pos, const float* tab, int64_t n_pos) {
+  const bool low = d0 < D / 2;           // x_i (else x_{i+D/2})
+  const int i0 = low ? d0 : d0 - D / 2;  // first pair index
+  float x[8], y[8], o[8];
+  Elem<bf16_t>::load8(row + d0, x);
+  Elem<bf16_t>::load8(row + (low ? d0 + D / 2 : i0), y);
+  const float* cp = tab + pos * (D / 2) + i0;
+  const float* sp = cp + n_pos * (D / 2);
+  const float4 c0 = *reinterpret_cast<const float4*>(cp), c1 = *reinterpret_cast<const float4*>(cp + 4);
+  const float4 s0 = *reinterpret_cast<const float4*>(sp), s1 = *reinterpret_cast<const float4*>(sp + 4);
+  const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = low ? rot_lo(x[j], y[j], c[j], sn[j]) : rot_hi(y[j], x[j], c[j], sn[j]);
+  uint4 w;
+  w.x = f32x2_to_bf16x2(o[0], o[1]);
+  w.y = f32x2_to_bf16x2(o[2], o[3]);
+  w.z = f32x2_to_bf16x2(o[4], o[5]);
+  w.w = f32x2_to_bf16x2(o[6], o[7]);
+  return w;
+}
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
   __shared__ float cs_tab[RPW][D / 2], sn_tab[RPW][D / 2];

@@ -195,7 +195,8 @@ def test_workspace_sizes():
     assert a >= 64 * 32 * 128 * 2 + 64 * 8 * 128 * 2
     assert m.msa_sparse_attn_workspace(1, 1, 64, 64, 64, 30, 8, 128) == 0
     b = m.msa_sparse_attn_backward_workspace(64, 64, 32, 8, 128)
-    assert b >= 64 * 32 * 128 * 2 + 64 * 8 * 128 * 2 + 2 * 64 * 32 * 4
+    # rotated Q and local K, the cos / sin table of up to 1024 + total_kv positions, two floats per row
+    assert b >= 64 * 32 * 128 * 2 + 64 * 8 * 128 * 2 + (1024 + 64) * 128 * 4 + 2 * 64 * 32 * 4
     assert m.msa_sparse_attn_backward_workspace(64, 64, 32, 8, 32) == 0
     c = m.msa_route_backward_workspace(2, 10, 20, 4)
     assert c >= 2 * 10 * 4 + 2 * 2 * 20 * 4 + 2 * 10 * (4 + 8) + 2 * 2 * 10 * 4 * 4
