@@ -373,7 +373,18 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
   const bf16_t* dOg = (const bf16_t*)bk.dO;
 
   // Stage `st` (query rows st*32 .. +31, row = t*G + j for token t and query head g*G + j)
-  // is read into registers one stage ahead and written to LDS buffer st & 1.
+  // is read into registers one stage ahead and written to LDS buffer st & 1.  A thread's
+  // rows advance by DKV_RS from stage to stage, so their (t, j) = (row / G, row % G) are
+  // stepped rather than divided out: fq / fr for the next stage, slot UPT for the row of
+  // the log-sum-exp and rowsum(dO O) (threads below DKV_RS), reset for every key chunk.
+  const int step_q = DKV_RS / G, step_r = DKV_RS % G;
+  int fq0[UPT + 1], fr0[UPT + 1], fq[UPT + 1], fr[UPT + 1];
+#pragma unroll
+  for (int j = 0; j <= UPT; ++j) {
+    const int rr = j < UPT ? (tid + j * THREADS) / UPR : tid;
+    fq0[j] = rr / G;
+    fr0[j] = rr % G;
+  }
   uint4 pq[UPT], pd[UPT];
   float pl = INFINITY, pr = 0.f;
   auto fetch = [&](int st) __attribute__((always_inline)) {
@@ -384,7 +395,7 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
       const int row = st * DKV_RS + rr;
       pq[j] = pd[j] = make_uint4(0, 0, 0, 0);
       if ((UNITS % THREADS == 0 || u < UNITS) && row < nrows) {
-        const int64_t ro = ((int64_t)(q0 + row / G) * a.hq + g * G + row % G) * D + e0;
+        const int64_t ro = (int64_t)((q0 + fq[j]) * a.hq + g * G + fr[j]) * D + e0;
         pq[j] = *reinterpret_cast<const uint4*>(Qg + ro);
         pd[j] = *reinterpret_cast<const uint4*>(dOg + ro);
       }
@@ -394,9 +405,18 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
       pl = INFINITY;  // rows past the end: P = 0
       pr = 0.f;
       if (row < nrows) {
-        const int64_t orow = (int64_t)(q0 + row / G) * a.hq + g * G + row % G;
+        const int64_t orow = (int64_t)(q0 + fq[UPT]) * a.hq + g * G + fr[UPT];
         pl = bk.lse[orow];
         pr = bk.drow[orow];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j <= UPT; ++j) {
+      fq[j] += step_q;
+      fr[j] += step_r;
+      if (fr[j] >= G) {
+        fr[j] -= G;
+        ++fq[j];
       }
     }
   };
@@ -456,6 +476,11 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
 #pragma unroll
       for (int md = 0; md < MD; ++md) dK[nt][md] = dV[nt][md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+#pragma unroll
+    for (int j = 0; j <= UPT; ++j) {
+      fq[j] = fq0[j];
+      fr[j] = fr0[j];
+    }
     if (nst > 0) fetch(0);
     for (int st = 0; st < nst; ++st) {
       const int buf = st & 1;
@@ -491,9 +516,10 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
 #pragma unroll
         for (int nt = 0; nt < DKV_NT; ++nt) {
           float p[4], dsv[4];
+          const int vis = rowmin[nt] - row0;  // element i is visible when i >= vis
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p[i] = row0 + i >= rowmin[nt] ? exp2_hw(fmaf(sacc[nt][i], sl2, -Lr[i])) : 0.f;
+            p[i] = i >= vis ? exp2_hw(fmaf(sacc[nt][i], sl2, -Lr[i])) : 0.f;
             dsv[i] = p[i] * (dpacc[nt][i] - Rr[i]);
           }
           pw[nt][sub * 2] = pack_bf16x2(p[0], p[1]);
