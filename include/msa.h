@@ -267,9 +267,11 @@ size_t msa_route_backward_workspace(int32_t n_queries, int32_t n_docs, int64_t n
  *   Heads with a zero vector get nothing; a query with no tokens gets nothing.  When two
  *   pairs tie the choice follows the forward kernel's float32 scores, so a near-tie can
  *   resolve differently from a float64 computation.  Row gradients shared by several
- *   queries are added atomically (their last bits can vary from run to run).
+ *   queries are summed in a fixed order for bf16 banks of 4 or 8 heads of dim 128, and
+ *   added atomically otherwise (their last bits can then vary from run to run).
  *   workspace  msa_route_backward_workspace() bytes, 256-byte aligned: the scan's document
- *              and row scores plus one record per (query, document).
+ *              and row scores plus one record per (query, document); with 4 or 8 routing
+ *              heads each record also keeps its maximising bank row (h_r * 256 bytes).
  *   Supported: as msa_route_scan (d in {32, 64, 128}; h_r in [1, 16]).
  */
 msa_status msa_route_backward(msa_dtype dtype, int32_t n_queries, int64_t total_q,

@@ -18,7 +18,8 @@
 //  * bf16 banks with d = 128 and 4 or 8 heads: route_bwd_doc_b16 (one workgroup per
 //    document: every query's maximising row and token, the records, and the rows' key
 //    gradients added once per distinct row in a fixed order, without atomics) and
-//    route_bwd_dq_b16 (16-byte gathers, several matches in flight);
+//    route_bwd_dq_b16 (each record's row, which the per-document kernel writes contiguously
+//    to the workspace, read with 16-byte loads, several matches in flight);
 //  * route_bwd_dq: one workgroup per (query, token) (strided when a query is longer than the
 //    grid): gathers the records that name the
 //    token (filtered a block of documents at a time through LDS) and writes its gradient
@@ -45,6 +46,7 @@ struct RouteBwdK {
   int64_t* cstar;           // [B, N]: maximising row
   float* cosv;              // [B, N, H]
   float* kinv;              // [B, N, H]: 1/|k| (0 when either vector is zero)
+  bf16_t* krec;             // [B, N, H * 128] (bf16 banks of 4 or 8 heads): the record's row
   int64_t n_chunks;
   int n_docs, n_queries, H;
 };
@@ -290,6 +292,7 @@ __global__ __launch_bounds__(H * 16) void route_bwd_doc_b16(RouteBwdK a) {
     // ---- 3. records and key gradients ----
     const int nv = n_valid;  // q_order[0 .. nv-1]; none read past them
     float acc[8], y[8];
+    uint4 yraw = make_uint4(0, 0, 0, 0);  // the thread's 16 bytes of the current row
     float ik_row = 0.f;  // 1/|k| of the current row's head (0 for a zero vector)
     int row = -1;
     auto flush = [&]() __attribute__((always_inline)) {
@@ -307,7 +310,8 @@ __global__ __launch_bounds__(H * 16) void route_bwd_doc_b16(RouteBwdK a) {
         row = c;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-        unpack8(*reinterpret_cast<const uint4*>(K + kr_tiled<D>(c0 + c, e0, H)), y);
+        yraw = *reinterpret_cast<const uint4*>(K + kr_tiled<D>(c0 + c, e0, H));
+        unpack8(yraw, y);
         float kn = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) kn += y[i] * y[i];
@@ -335,6 +339,9 @@ __global__ __launch_bounds__(H * 16) void route_bwd_doc_b16(RouteBwdK a) {
         a.tstar[rec] = t;
         a.cstar[rec] = c0 + c;
       }
+      // the record's row, contiguous, for the query gradient (which would otherwise gather
+      // it from the tiled layout at a 128-byte line per 16-byte piece)
+      *reinterpret_cast<uint4*>(a.krec + rec * NE + e0) = yraw;
       const float w = q_g[qi] * ik;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += w * (x[i] * iq - co * y[i] * ik);
@@ -360,7 +367,6 @@ __global__ __launch_bounds__(DQ_THREADS) void route_bwd_dq_b16(RouteBwdK a) {
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int grp = tid / TPM, e0 = (tid % TPM) * 8, h = e0 / D;
-  const bf16_t* K = (const bf16_t*)a.Krb;
   for (int t = blockIdx.x; t < Lq; t += gridDim.x) {
     float acc1[8], acc2 = 0.f;  // sum of g * k / |k|, sum of g * cos (the thread's head)
 #pragma unroll
@@ -385,12 +391,11 @@ __global__ __launch_bounds__(DQ_THREADS) void route_bwd_dq_b16(RouteBwdK a) {
       int m = grp;
       for (; m + PAR < nm; m += 2 * PAR) {
         const int64_t r0 = (int64_t)b * a.n_docs + match[m], r1 = (int64_t)b * a.n_docs + match[m + PAR];
-        const int64_t k0 = a.cstar[r0], k1 = a.cstar[r1];
         const float g0 = a.dD[r0], g1 = a.dD[r1];
         const float w0 = g0 * a.kinv[r0 * H + h], w1 = g1 * a.kinv[r1 * H + h];
         const float c0v = g0 * a.cosv[r0 * H + h], c1v = g1 * a.cosv[r1 * H + h];
-        const uint4 v0 = *reinterpret_cast<const uint4*>(K + kr_tiled<D>(k0, e0, H));
-        const uint4 v1 = *reinterpret_cast<const uint4*>(K + kr_tiled<D>(k1, e0, H));
+        const uint4 v0 = *reinterpret_cast<const uint4*>(a.krec + r0 * NE + e0);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(a.krec + r1 * NE + e0);
         float y0[8], y1[8];
         unpack8(v0, y0);
         unpack8(v1, y1);
@@ -403,10 +408,9 @@ __global__ __launch_bounds__(DQ_THREADS) void route_bwd_dq_b16(RouteBwdK a) {
       }
       if (m < nm) {
         const int64_t r0 = (int64_t)b * a.n_docs + match[m];
-        const int64_t k0 = a.cstar[r0];
         const float g0 = a.dD[r0];
         float y0[8];
-        unpack8(*reinterpret_cast<const uint4*>(K + kr_tiled<D>(k0, e0, H)), y0);
+        unpack8(*reinterpret_cast<const uint4*>(a.krec + r0 * NE + e0), y0);
         const float w0 = g0 * a.kinv[r0 * H + h];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc1[i] += w0 * y0[i];
@@ -475,10 +479,14 @@ hipError_t launch_t(const RouteBwdArgs& r, const RouteBwdK& k, hipStream_t s) {
 
 }  // namespace
 
+// Bytes per record of the record rows kept for the query gradient: 4 or 8 routing heads
+// (bf16 banks of dim 128 take the per-document kernels), 0 otherwise.
+static size_t krec_bytes(int h_r) { return (h_r == 4 || h_r == 8) ? (size_t)h_r * 128 * 2 : 0; }
+
 size_t route_bwd_workspace_bytes(int n_queries, int n_docs, int64_t n_chunks, int h_r) {
   const size_t bn = (size_t)n_queries * n_docs;
   return align256(bn * 4) + 2 * align256((size_t)n_queries * n_chunks * 4) + align256(bn * 4) +
-         align256(bn * 8) + 2 * align256(bn * h_r * 4);
+         align256(bn * 8) + 2 * align256(bn * h_r * 4) + align256(bn * krec_bytes(h_r));
 }
 
 hipError_t launch_route_backward(const RouteBwdArgs& r, hipStream_t s) {
@@ -498,6 +506,8 @@ hipError_t launch_route_backward(const RouteBwdArgs& r, hipStream_t s) {
   k.cosv = (float*)ws;
   ws += align256(bn * r.h_r * 4);
   k.kinv = (float*)ws;
+  ws += align256(bn * r.h_r * 4);
+  k.krec = krec_bytes(r.h_r) ? (bf16_t*)ws : nullptr;
   const float* row_scores = rows;
   const int32_t* row_arg = rarg;
   if (r.row_scores != nullptr) {
