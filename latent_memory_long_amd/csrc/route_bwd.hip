@@ -301,16 +301,36 @@ __global__ __launch_bounds__(H * 16) void route_bwd_doc_b16(RouteBwdK a) {
       *reinterpret_cast<float4*>(dk) = make_float4(u0.x + acc[0], u0.y + acc[1], u0.z + acc[2], u0.w + acc[3]);
       *reinterpret_cast<float4*>(dk + 4) = make_float4(u1.x + acc[4], u1.y + acc[5], u1.z + acc[6], u1.w + acc[7]);
     };
+    // The next record's query slice (and its row's key slice when the row changes) is
+    // loaded while the current record is computed: records are a chain of dependent loads.
+    auto qslice = [&](int qi) __attribute__((always_inline)) {
+      return *reinterpret_cast<const uint4*>((const bf16_t*)a.Qr + (int64_t)(a.q_off[b0 + qi] + q_t[qi]) * NE + e0);
+    };
+    auto kslice = [&](int c) __attribute__((always_inline)) {
+      return *reinterpret_cast<const uint4*>(K + kr_tiled<D>(c0 + c, e0, H));
+    };
+    uint4 xnext = make_uint4(0, 0, 0, 0), ynext = xnext;
+    if (nv > 0) {
+      xnext = qslice(q_order[0]);
+      ynext = kslice(q_c[q_order[0]]);
+    }
     for (int r = 0; r < nv; ++r) {
       const int qi = q_order[r];
       const int b = b0 + qi, c = q_c[qi], t = q_t[qi];
       const int64_t rec = (int64_t)b * a.n_docs + d;
+      const uint4 xraw = xnext, ycur = ynext;
+      if (r + 1 < nv) {  // uniform
+        const int qn1 = q_order[r + 1];
+        xnext = qslice(qn1);
+        const int c1 = q_c[qn1];
+        if (c1 != c) ynext = kslice(c1);  // uniform
+      }
       if (c != row) {  // uniform: the next row
         if (row >= 0) flush();
         row = c;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-        yraw = *reinterpret_cast<const uint4*>(K + kr_tiled<D>(c0 + c, e0, H));
+        yraw = ycur;
         unpack8(yraw, y);
         float kn = 0.f;
 #pragma unroll
@@ -319,7 +339,7 @@ __global__ __launch_bounds__(H * 16) void route_bwd_doc_b16(RouteBwdK a) {
         ik_row = kn > 0.f ? 1.f / sqrtf(kn) : 0.f;
       }
       float x[8];
-      unpack8(*reinterpret_cast<const uint4*>((const bf16_t*)a.Qr + (int64_t)(a.q_off[b] + t) * NE + e0), x);
+      unpack8(xraw, x);
       float dot = 0.f, qn = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
