@@ -529,26 +529,31 @@ def main():
     pre = [(q["Qr"][:Lq].contiguous(), q["Q"][:Lq].contiguous(), q["Kloc"][:Lq].contiguous(),
             q["Vloc"][:Lq].contiguous()) for q in qs]
 
-    def run(n_slots, steps, sync_each=False):
+    def run(n_slots, steps, sync_each=False, instrument=True):
         """`steps` timed steps, query i on stream i mod n_slots (default priority).  With one
         slot the queries run one at a time.  With several, queries are in flight together
         as concurrent requests are on a serving GPU: one query's top-k and host-link-bound
         attention overlap other queries' HBM-bound scans, and scans overlap one another.
-        Per-step events are recorded on the step's own stream."""
+        Per-step events are recorded on the step's own stream; without `instrument` a step
+        records none (each event leaves the GPU idle for a few microseconds)."""
         streams = [torch.cuda.current_stream()] if n_slots == 1 else [torch.cuda.Stream() for _ in range(n_slots)]
         slots = [slot_buffers() for _ in range(n_slots)]
 
         def step(i, ev):
             Qr, Q, Kl, Vl = pre[i % len(pre)]
             st, b = streams[i % n_slots], slots[i % n_slots]
-            ev[0].record(st)
+            if ev is not None:
+                ev[0].record(st)
             M.msa_route_scan(Qr, q_off, Lq, Krb, coff_d, out=b["ds"], stream=st)
-            ev[1].record(st)
+            if ev is not None:
+                ev[1].record(st)
             M.msa_topk(b["ds"], k, out=(b["ids"], b["sc"]), workspace=b["tws"], stream=st)
-            ev[2].record(st)
+            if ev is not None:
+                ev[2].record(st)
             M.msa_sparse_attn(Q, Kl, Vl, q_off, kv_off, Lq, b["ids"], coff_d, Kb, Vb, rope_base=sh.rope_base,
                               out=b["out"], workspace=b["ws"], stream=st)
-            ev[3].record(st)
+            if ev is not None:
+                ev[3].record(st)
 
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         wev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -565,14 +570,18 @@ def main():
             return host
         t0 = time.perf_counter()
         for i in range(steps):
-            step(i, evs[i])
+            step(i, evs[i] if instrument else None)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return wall, evs, slots[(steps - 1) % n_slots]["ids"]
 
     log(f"timing {args.steps} steps, one query at a time")
-    wall, evs, ids = run(1, args.steps)
+    # per-step events: the latencies, the phase split and the scan's roofline
+    wall_ev, evs, ids = run(1, args.steps)
     host_sync_ms = run(1, min(args.steps, 50), sync_each=True)
+    # the same steps back to back without per-step events: the throughput (`value`)
+    log(f"timing {args.steps} steps without per-step events")
+    wall, _, _ = run(1, args.steps, instrument=False)
     serving = None
     if args.inflight > 1:
         log(f"serving throughput: {args.steps} steps with {args.inflight} queries in flight")
@@ -590,6 +599,7 @@ def main():
     attn_ms = [e[2].elapsed_time(e[3]) for e in evs]
     step_ms = [e[0].elapsed_time(e[3]) for e in evs]
     ms_per_step = wall / args.steps * 1e3
+    ms_per_step_events = wall_ev / args.steps * 1e3
 
     # roofline of the scan kernel: algorithmic bytes per launch / its average duration
     scan_bytes = C * sh.h_r * sh.d * 2 + Lq * sh.h_r * sh.d * 2 + (N + 1) * 8 + N * 4
@@ -684,7 +694,8 @@ def main():
                        "route_attend_p90": round(pct(step_ms, 90), 4),
                        "scan_p50": round(pct(scan_ms, 50), 4), "topk_p50": round(pct(topk_ms, 50), 4),
                        "attend_p50": round(pct(attn_ms, 50), 4),
-                       "route_attend_host_sync_p50": round(pct(host_sync_ms, 50), 4)},
+                       "route_attend_host_sync_p50": round(pct(host_sync_ms, 50), 4),
+                       "ms_per_step_with_step_events": round(ms_per_step_events, 4)},
         "serving": serving,
         "roofline": {"kernel": SCAN_KERNEL, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

@@ -378,16 +378,19 @@ hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, bool host, hipStream_t s) 
   if (r.total_q == 0) return hipSuccess;  // no rows: nothing reads the rotated local K
   // float32: Q and the local K rotated into the workspace; bf16: the cos / sin table, then
   // the local K rotated with it (the attention kernel rotates Q with it as it loads it)
-  if (sizeof(T) == 2) {
-    const int64_t n = k.n_pos * (D / 2);
-    hipLaunchKernelGGL((rope_table<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float*)k.rtab,
-                       k.n_pos, k.rope_base);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const int nq_blocks = sizeof(T) == 4 ? (int)((r.total_q + RPW - 1) / RPW) : 0;
   const int nk_blocks = (int)((r.total_kv + RPW - 1) / RPW);
-  if (nq_blocks + nk_blocks > 0) {
+  if constexpr (sizeof(T) == 2) {
+    // one launch: the local K rotated (blocks 0 .. nk_blocks-1) and the table written
+    AttnK kp = k;
+    kp.rtab = nullptr;
+    const int64_t n = k.n_pos * (D / 2);
+    const int tab_blocks = (int)((n + 255) / 256);
+    hipLaunchKernelGGL((rope_prep<D>), dim3((unsigned)(nk_blocks + tab_blocks)), dim3(256), 0, s, kp, 0, nk_blocks,
+                       (float*)k.rtab);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (nq_blocks + nk_blocks > 0) {
     hipLaunchKernelGGL((rope_local<T, D>), dim3(nq_blocks + nk_blocks), dim3(256), 0, s, k, nq_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -630,17 +630,18 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
   k.scale = scale;
   k.kblocks = 16;
 
+  // Q and the local K rotated once per row, and the table written, in one launch: bwd_dkv
+  // reads every query row once per key block, so rotating them in the kernels would repeat
+  // the work many times
   {
-    const int64_t n = k.f.n_pos * (D / 2);
-    hipLaunchKernelGGL((rope_table<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float*)k.f.rtab,
-                       k.f.n_pos, k.f.rope_base);
+    const int nq_blocks = (int)((f.total_q + RPW - 1) / RPW);
+    const int nk_blocks = (int)((f.total_kv + RPW - 1) / RPW);
+    AttnK kp = k.f;
+    kp.rtab = nullptr;
+    const int tab_blocks = (int)((k.f.n_pos * (D / 2) + 255) / 256);
+    hipLaunchKernelGGL((rope_prep<D>), dim3((unsigned)(nq_blocks + nk_blocks + tab_blocks)), dim3(256), 0, s, kp,
+                       nq_blocks, nq_blocks + nk_blocks, (float*)k.f.rtab);
   }
-  // Q and the local K rotated once per row with the table: bwd_dkv reads every query row
-  // once per key block, so rotating them in the kernels would repeat the work many times
-  const int nq_blocks = (int)((f.total_q + RPW - 1) / RPW);
-  const int nk_blocks = (int)((f.total_kv + RPW - 1) / RPW);
-  if (nq_blocks + nk_blocks > 0)
-    hipLaunchKernelGGL((rope_local<bf16_t, D>), dim3(nq_blocks + nk_blocks), dim3(256), 0, s, k.f, nq_blocks);
   const int G = f.hq / f.h_kv;
   const int rows = min(attn_rows_per_block(f.max_q_len, G), 128);
   const int rblocks = (f.max_q_len * G + rows - 1) / rows;

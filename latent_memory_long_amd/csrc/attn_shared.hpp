@@ -61,8 +61,7 @@ __device__ __forceinline__ float rot_hi(float lo, float hi, float c, float s) { 
 // precision (theta_i = base^(-2i/D)), rounded to float: cos at [p][i], sin at
 // [n_pos + p][i].
 template <int D>
-__global__ __launch_bounds__(256) void rope_table(float* tab, int64_t n_pos, float rope_base) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void rope_table_entry(float* tab, int64_t n_pos, float rope_base, int64_t e) {
   if (e >= n_pos * (D / 2)) return;
   const int64_t p = e / (D / 2);
   const int i = (int)(e % (D / 2));
@@ -71,6 +70,10 @@ __global__ __launch_bounds__(256) void rope_table(float* tab, int64_t n_pos, flo
   sincos((double)p * th, &sn, &cs);
   tab[e] = (float)cs;
   tab[n_pos * (D / 2) + e] = (float)sn;
+}
+template <int D>
+__global__ __launch_bounds__(256) void rope_table(float* tab, int64_t n_pos, float rope_base) {
+  rope_table_entry<D>(tab, n_pos, rope_base, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 
@@ -99,13 +102,14 @@ __device__ __forceinline__ uint4 rope_load8(const bf16_t* row, int d0, int64_t p
   w.w = f32x2_to_bf16x2(o[6], o[7]);
   return w;
 }
+// Block blk of rope_local: RPW rows of Q (blk < nq_blocks) or of the local K.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
+__device__ __forceinline__ void rope_local_rows(const AttnK& a, int nq_blocks, int blk) {
   __shared__ float cs_tab[RPW][D / 2], sn_tab[RPW][D / 2];
   __shared__ int row_q[RPW];
   __shared__ int64_t row_pos[RPW];
-  const bool is_q = blockIdx.x < (unsigned)nq_blocks;
-  const int64_t r0 = (int64_t)(is_q ? blockIdx.x : blockIdx.x - nq_blocks) * RPW;
+  const bool is_q = blk < nq_blocks;
+  const int64_t r0 = (int64_t)(is_q ? blk : blk - nq_blocks) * RPW;
   const int64_t total = is_q ? a.total_q : a.total_kv;
   const int heads = is_q ? a.hq : a.h_kv;
   const T* src = (const T*)(is_q ? a.Q : a.Kloc);
@@ -162,6 +166,22 @@ __global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
     Elem<T>::store4(o + i0, o_lo);
     Elem<T>::store4(o + i0 + D / 2, o_hi);
   }
+}
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_local(AttnK a, int nq_blocks) {
+  rope_local_rows<T, D>(a, nq_blocks, blockIdx.x);
+}
+
+// The bf16 RoPE set-up in one launch: blocks below n_rot rotate rows as rope_local does
+// (a.rtab must be null: they take their own angles, the same double-precision values the
+// table holds), the others write the cos / sin table of a.n_pos positions into tab.
+template <int D>
+__global__ __launch_bounds__(256) void rope_prep(AttnK a, int nq_blocks, int n_rot, float* tab) {
+  if ((int)blockIdx.x < n_rot) {  // uniform over the block
+    rope_local_rows<bf16_t, D>(a, nq_blocks, blockIdx.x);
+    return;
+  }
+  rope_table_entry<D>(tab, a.n_pos, a.rope_base, (int64_t)(blockIdx.x - n_rot) * blockDim.x + threadIdx.x);
 }
 
 // Workgroup -> (kv pair, sub-block) of a 1-D grid of ceil(n_pairs / 8) * 8 * nsub
