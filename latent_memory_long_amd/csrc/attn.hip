@@ -28,7 +28,8 @@
 //    query row, which are exactly the P^T operand of O^T = V^T * P^T, so probabilities
 //    never leave registers; V^T comes from the row-major tile through gfx950's
 //    transposing LDS load, and each K / V operand read serves both row tiles of a wave.
-//  * attn_valu (float32): one thread per (query row, head), plain online softmax.
+//  * attn_valu (float32): one wave per (query token, kv head, up to 4 query heads), 16 lanes
+//    per head, online softmax in float32.
 //  * attn_combine: merges the per-split (max, sum, unnormalised output) triples.
 #include <math.h>
 
@@ -274,40 +275,46 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ---- float32 path: one thread per (query row, head) ----------------------------------
+// float32 inputs: one wave per (query token, kv head, block of up to 4 of the group's query
+// heads).  16 lanes per query head hold D/16 elements of its rotated row and of its output;
+// every key row is read once per wave (the four 16-lane groups read the same addresses),
+// each dot product is reduced across its 16 lanes, and the online softmax runs in float32,
+// replicated on the 16 lanes of a head.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_valu(AttnK a) {
+__global__ __launch_bounds__(64) void attn_valu(AttnK a, int hblocks) {
+  constexpr int E = D / 16;  // elements per lane
   const int b = blockIdx.y;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int kv0 = a.kv_off[b], Lkv = a.kv_off[b + 1] - kv0;
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= Lq * a.hq) return;
-  const int t = r / a.hq, hq = r % a.hq;
-  const int g = hq / (a.hq / a.h_kv);
-  const T* Qr = (const T*)a.Qrot + ((int64_t)(q0 + t) * a.hq + hq) * D;
-  float q[D], acc[D];
+  const int G = a.hq / a.h_kv;
+  const int x = blockIdx.x;
+  const int hb = x % hblocks, g = (x / hblocks) % a.h_kv, t = x / (hblocks * a.h_kv);
+  if (t >= Lq) return;  // uniform
+  const int lane = threadIdx.x, li = lane & 15;
+  const int j = hb * 4 + (lane >> 4);  // query head within the group
+  const bool row_ok = j < G;
+  const int hq = g * G + (row_ok ? j : 0);
+  const int e0 = li * E;
+  const T* Qr = (const T*)a.Qrot + ((int64_t)(q0 + t) * a.hq + hq) * D + e0;
+  float q[E], acc[E];
 #pragma unroll
-  for (int e = 0; e < D; e += 8) Elem<T>::load8(Qr + e, q + e);
-#pragma unroll
-  for (int e = 0; e < D; ++e) acc[e] = 0.f;
+  for (int e = 0; e < E; ++e) {
+    q[e] = row_ok ? (float)Qr[e] : 0.f;
+    acc[e] = 0.f;
+  }
   float m = -INFINITY, l = 0.f;
-  auto visit = [&](const T* kp, const T* vp) {
-    float kv[8], dot = 0.f;
+  auto visit = [&](const T* kp, const T* vp) __attribute__((always_inline)) {
+    float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < D; e += 8) {
-      Elem<T>::load8(kp + e, kv);
+    for (int e = 0; e < E; ++e) dot = fmaf(q[e], (float)kp[e0 + e], dot);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) dot += q[e + x] * kv[x];
-    }
+    for (int o = 8; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 16);
     const float s = dot * a.scale_log2;
     const float mn = fmaxf(m, s);
     const float al = exp2f(m - mn), p = exp2f(s - mn);
     l = l * al + p;
 #pragma unroll
-    for (int e = 0; e < D; e += 8) {
-      Elem<T>::load8(vp + e, kv);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) acc[e + x] = acc[e + x] * al + p * kv[x];
-    }
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(acc[e], al, p * (float)vp[e0 + e]);
     m = mn;
   };
   const int32_t* ids = a.ids + (int64_t)b * a.k;
@@ -321,18 +328,15 @@ __global__ __launch_bounds__(64) void attn_valu(AttnK a) {
   }
   const T* Kr = (const T*)a.Krot;
   const T* Vl = (const T*)a.Vloc;
-  for (int j = 0; j <= Lkv - Lq + t; ++j)
-    visit(Kr + ((int64_t)(kv0 + j) * a.h_kv + g) * D, Vl + ((int64_t)(kv0 + j) * a.h_kv + g) * D);
-  T* o = (T*)a.O + ((int64_t)(q0 + t) * a.hq + hq) * D;
-  if (a.lse != nullptr) a.lse[(int64_t)(q0 + t) * a.hq + hq] = l > 0.f ? (m + log2f(l)) * LN2 : -INFINITY;
+  for (int jj = 0; jj <= Lkv - Lq + t; ++jj)
+    visit(Kr + ((int64_t)(kv0 + jj) * a.h_kv + g) * D, Vl + ((int64_t)(kv0 + jj) * a.h_kv + g) * D);
+  if (!row_ok) return;
+  const int64_t orow = (int64_t)(q0 + t) * a.hq + hq;
+  if (a.lse != nullptr && li == 0) a.lse[orow] = l > 0.f ? (m + log2f(l)) * LN2 : -INFINITY;
   const float inv = 1.0f / l;
+  T* o = (T*)a.O + orow * D + e0;
 #pragma unroll
-  for (int e = 0; e < D; e += 8) {
-    float f[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) f[x] = acc[e + x] * inv;
-    Elem<T>::store8(o + e, f);
-  }
+  for (int e = 0; e < E; ++e) o[e] = (T)(acc[e] * inv);
 }
 
 // ---- merge of key splits -------------------------------------------------------------
@@ -397,8 +401,9 @@ hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, bool host, hipStream_t s) 
   }
   if constexpr (sizeof(T) == 4) {
     k.splits = 1;
-    dim3 grid((unsigned)((r.max_q_len * r.hq + 63) / 64), (unsigned)r.n_queries);
-    hipLaunchKernelGGL((attn_valu<T, D>), grid, dim3(64), 0, s, k);
+    const int G = r.hq / r.h_kv, hblocks = (G + 3) / 4;
+    dim3 grid((unsigned)((int64_t)r.max_q_len * r.h_kv * hblocks), (unsigned)r.n_queries);
+    hipLaunchKernelGGL((attn_valu<T, D>), grid, dim3(64), 0, s, k, hblocks);
     return hipGetLastError();
   } else {
     const int G = r.hq / r.h_kv;
