@@ -409,6 +409,10 @@ size_t msa_sparse_attn_backward_workspace(int64_t total_q, int64_t total_kv, int
  *   Supported: dtype MSA_BF16; d in {64, 128}; 1 <= k <= 1024.  Products in bf16 on MFMA,
  *   sums and softmax statistics in float32.  Kbar/Vbar may be pinned host memory
  *   (kv_source 1); the gradient arrays are device memory.
+ *   Streams: with lse given, the key-side gradients run on a second stream that the library
+ *   keeps per device (created on the first such call made outside graph capture), forked
+ *   from `stream` and joined back to it with events, so the call still completes in order
+ *   on `stream` and can be captured in a graph.
  */
 msa_status msa_sparse_attn_backward(msa_dtype dtype, int32_t n_queries, int64_t total_q,
                                     int64_t total_kv, const int32_t* q_off, const int32_t* kv_off,

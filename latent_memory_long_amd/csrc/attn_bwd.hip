@@ -32,6 +32,8 @@
 //  pair it writes.
 #include <math.h>
 
+#include <mutex>
+
 #include "attn_shared.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -120,27 +122,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int64_t ro = ((int64_t)(q0 + t_of[m]) * a.hq + hq_of[m]) * D + g4 * 8;
     const bf16_t* qp = (const bf16_t*)a.Qrot + ro;
     const bf16_t* dp = (const bf16_t*)bk.dO + ro;
-    const bf16_t* op = (const bf16_t*)bk.O + ro;
-    float dsum = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      uint4 qv = make_uint4(0, 0, 0, 0), dv = qv, ov = qv;
+      uint4 qv = make_uint4(0, 0, 0, 0), dv = qv;
       if (row_ok[m]) {
         qv = *reinterpret_cast<const uint4*>(qp + kk * 32);
         dv = *reinterpret_cast<const uint4*>(dp + kk * 32);
-        ov = *reinterpret_cast<const uint4*>(op + kk * 32);
       }
       Qf[m][kk] = __builtin_bit_cast(bf16x8_t, qv);
       dOf[m][kk] = __builtin_bit_cast(bf16x8_t, dv);
-      float x[8], y[8];
-      unpack8(dv, x);
-      unpack8(ov, y);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dsum += x[e] * y[e];
     }
-    dsum += __shfl_xor(dsum, 16);
-    dsum += __shfl_xor(dsum, 32);
-    drow[m] = dsum;
+    // rowsum(dO * O), from bwd_rows
+    drow[m] = row_ok[m] ? bk.drow[(int64_t)(q0 + t_of[m]) * a.hq + hq_of[m]] : 0.f;
   }
 
 
@@ -227,12 +220,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       lse[m] = v > -INFINITY ? v * LOG2E : INFINITY;
     }
   }
+  if (bk.lse_in == nullptr) {  // else bwd_rows has written the log2-unit copy for bwd_dkv
 #pragma unroll
-  for (int m = 0; m < MTW; ++m) {
-    if (row_ok[m] && g4 == 0) {
-      const int64_t orow = (int64_t)(q0 + t_of[m]) * a.hq + hq_of[m];
-      bk.lse[orow] = lse[m];
-      bk.drow[orow] = drow[m];
+    for (int m = 0; m < MTW; ++m) {
+      if (row_ok[m] && g4 == 0) bk.lse[(int64_t)(q0 + t_of[m]) * a.hq + hq_of[m]] = lse[m];
     }
   }
 
@@ -320,6 +311,57 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   }
 }
+
+// ---- row statistics ahead of both gradient kernels ------------------------------------
+// rowsum(dO * O) of every (token, query head) row and, when the forward's log-sum-exp is
+// given, its copy in log2 units: after this launch bwd_dq and bwd_dkv depend on nothing of
+// each other.  Lane (cl, g4) of a wave sums elements kk*32 + g4*8 .. +7 of row cl, then the
+// four lanes of the row are added (the order the values were first summed in).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rows(BwdK bk, int64_t n_rows) {
+  constexpr int KK = D / 32;
+  const int lane = threadIdx.x & 63, cl = lane & 15, g4 = lane >> 4;
+  const int64_t orow = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + cl;
+  const bool ok = orow < n_rows;
+  const int64_t ro = (ok ? orow : 0) * D + g4 * 8;
+  const bf16_t* dp = (const bf16_t*)bk.dO + ro;
+  const bf16_t* op = (const bf16_t*)bk.O + ro;
+  float dsum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    uint4 dv = make_uint4(0, 0, 0, 0), ov = dv;
+    if (ok) {
+      dv = *reinterpret_cast<const uint4*>(dp + kk * 32);
+      ov = *reinterpret_cast<const uint4*>(op + kk * 32);
+    }
+    float x[8], y[8];
+    unpack8(dv, x);
+    unpack8(ov, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum += x[e] * y[e];
+  }
+  dsum += __shfl_xor(dsum, 16);
+  dsum += __shfl_xor(dsum, 32);
+  if (ok && g4 == 0) {
+    bk.drow[orow] = dsum;
+    if (bk.lse_in != nullptr) {
+      const float v = bk.lse_in[orow];
+      bk.lse[orow] = v > -INFINITY ? v * LOG2E : INFINITY;
+    }
+  }
+}
+
+// A second stream per device, for running bwd_dkv beside bwd_dq: created once (default
+// priority, non-blocking), with the two events that fork it from and join it to the
+// caller's stream.  The fork / join sequence is enqueued under a lock, so that calls from
+// several host threads do not interleave their uses of the events.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int MAX_DEVICES = 64;
+SideStream g_side[MAX_DEVICES];
+std::mutex g_side_mu;
 
 // ---- dK and dV --------------------------------------------------------------------------
 constexpr int DKV_NW = 4;   // waves per workgroup
@@ -642,26 +684,76 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
     hipLaunchKernelGGL((rope_prep<D>), dim3((unsigned)(nq_blocks + nk_blocks + tab_blocks)), dim3(256), 0, s, kp,
                        nq_blocks, nq_blocks + nk_blocks, (float*)k.f.rtab);
   }
+  {
+    const int64_t n_rows = f.total_q * f.hq;
+    if (n_rows > 0)
+      hipLaunchKernelGGL((bwd_rows<D>), dim3((unsigned)((n_rows + 63) / 64)), dim3(256), 0, s, k, n_rows);
+  }
   const int G = f.hq / f.h_kv;
   const int rows = min(attn_rows_per_block(f.max_q_len, G), 128);
   const int rblocks = (f.max_q_len * G + rows - 1) / rows;
-  if (rblocks > 0) {
+  const int n_pairs = f.n_queries * f.h_kv;
+  auto launch_dq = [&](hipStream_t st) {
+    if (rblocks <= 0) return;
     // the row blocks of a (query, kv head) on one XCD (place_pair); two 16-row tiles per
     // wave at 128 rows, so each K / V operand read serves both
-    const int n_pairs = f.n_queries * f.h_kv;
     const dim3 grid((unsigned)(((n_pairs + 7) / 8) * 8 * rblocks));
     switch (rows) {
-      case 16: hipLaunchKernelGGL((bwd_dq<D, 1, 1>), grid, dim3(64), 0, s, k, rblocks); break;
-      case 32: hipLaunchKernelGGL((bwd_dq<D, 2, 1>), grid, dim3(128), 0, s, k, rblocks); break;
-      case 64: hipLaunchKernelGGL((bwd_dq<D, 4, 1>), grid, dim3(256), 0, s, k, rblocks); break;
-      default: hipLaunchKernelGGL((bwd_dq<D, 4, 2>), grid, dim3(256), 0, s, k, rblocks); break;
+      case 16: hipLaunchKernelGGL((bwd_dq<D, 1, 1>), grid, dim3(64), 0, st, k, rblocks); break;
+      case 32: hipLaunchKernelGGL((bwd_dq<D, 2, 1>), grid, dim3(128), 0, st, k, rblocks); break;
+      case 64: hipLaunchKernelGGL((bwd_dq<D, 4, 1>), grid, dim3(256), 0, st, k, rblocks); break;
+      default: hipLaunchKernelGGL((bwd_dq<D, 4, 2>), grid, dim3(256), 0, st, k, rblocks); break;
+    }
+  };
+  auto launch_dkv = [&](hipStream_t st) {
+    // the key blocks of a (query, kv head) on one XCD (place_pair): they all stream the
+    // pair's query rows, which that XCD's L2 then holds
+    const dim3 gkv((unsigned)(((n_pairs + 7) / 8) * 8 * k.kblocks));
+    hipLaunchKernelGGL((bwd_dkv<D>), gkv, dim3(64 * DKV_NW), 0, st, k);
+  };
+  // With the forward's log-sum-exp the two gradient kernels are independent: bwd_dkv runs
+  // on the side stream beside bwd_dq, whose workgroups then fill each other's idle issue
+  // slots and tails.  Without it bwd_dq computes the log-sum-exp that bwd_dkv reads.
+  int dev = -1;
+  SideStream* side = nullptr;
+  if (r.lse != nullptr && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < MAX_DEVICES) side = &g_side[dev];
+  if (side != nullptr) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    // created outside any graph capture only (a first call under capture runs in order)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (side->s == nullptr && hipStreamIsCapturing(s, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+      hipStream_t st;
+      hipEvent_t e0, e1;
+      if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess) {
+        if (hipEventCreateWithFlags(&e0, hipEventDisableTiming) == hipSuccess) {
+          if (hipEventCreateWithFlags(&e1, hipEventDisableTiming) == hipSuccess) {
+            side->s = st;
+            side->fork = e0;
+            side->join = e1;
+          } else {
+            (void)hipEventDestroy(e0);
+            (void)hipStreamDestroy(st);
+          }
+        } else {
+          (void)hipStreamDestroy(st);
+        }
+      }
+      (void)hipGetLastError();
+    }
+    if (side->s != nullptr) {
+      hipError_t e = hipEventRecord(side->fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+      if (e != hipSuccess) return e;
+      launch_dkv(side->s);
+      launch_dq(s);
+      e = hipEventRecord(side->join, side->s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+      if (e != hipSuccess) return e;
+      return hipGetLastError();
     }
   }
-  // the key blocks of a (query, kv head) on one XCD (place_pair): they all stream the pair's
-  // query rows, which that XCD's L2 then holds
-  const int n_pairs = f.n_queries * f.h_kv;
-  const dim3 gkv((unsigned)(((n_pairs + 7) / 8) * 8 * k.kblocks));
-  hipLaunchKernelGGL((bwd_dkv<D>), gkv, dim3(64 * DKV_NW), 0, s, k);
+  launch_dq(s);
+  launch_dkv(s);
   return hipGetLastError();
 }
 
