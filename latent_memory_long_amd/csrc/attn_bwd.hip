@@ -518,13 +518,28 @@ __global__ __launch_bounds__(64 * DKV_NW) void bwd_dkv(BwdK bk) {
 #pragma unroll
       for (int md = 0; md < MD; ++md) dK[nt][md] = dV[nt][md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // Stages before the one holding the chunk's first visible row are skipped: a local key i
+    // is hidden from the rows of tokens below i - (Lkv - Lq), and the chunk's first key has
+    // the smallest such bound (bank keys see every row).  The thread's row indices start
+    // at that stage.
+    int st_first = 0;
+    {
+      const int64_t tmin0 = (c * KEYS - M) - (Lkv - Lq);
+      if (c * KEYS >= M && tmin0 > 0) st_first = (int)min((int64_t)nst, tmin0 * G / DKV_RS);
+    }
 #pragma unroll
     for (int j = 0; j <= UPT; ++j) {
-      fq[j] = fq0[j];
-      fr[j] = fr0[j];
+      if (st_first == 0) {
+        fq[j] = fq0[j];
+        fr[j] = fr0[j];
+      } else {
+        const int rr = j < UPT ? (tid + j * THREADS) / UPR : tid;
+        fq[j] = (st_first * DKV_RS + rr) / G;
+        fr[j] = (st_first * DKV_RS + rr) % G;
+      }
     }
-    if (nst > 0) fetch(0);
-    for (int st = 0; st < nst; ++st) {
+    if (st_first < nst) fetch(st_first);
+    for (int st = st_first; st < nst; ++st) {
       const int buf = st & 1;
       commit(buf);
       __syncthreads();  // stage st is visible, and every wave is done with stage st-2 (this buffer)
