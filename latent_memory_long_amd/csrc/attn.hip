@@ -12,10 +12,11 @@
 // local states and the top-k memory.
 //
 // Kernels:
-//  * rope_local: rotates the local K (and for float32 also Q) at their global positions
-//    (k_eff + local index) into the workspace, angles in double precision, once per row.
-//  * rope_table (bf16): cos / sin of every position a row or local key can take, from
-//    double-precision angles; attn_mfma rotates Q with it while loading its operands.
+//  * rope_local (float32): rotates Q and the local K at their global positions (k_eff +
+//    local index) into the workspace, angles in double precision, once per row.
+//  * rope_prep (bf16): in one launch, the cos / sin table of every position a row or local
+//    key can take (double-precision angles) and the local K rotated the same way;
+//    attn_mfma rotates Q with the table while loading its operands.
 //  * attn_mfma (bf16): one workgroup per (query, kv head, block of query rows, key split);
 //    each wave holds one or two 16-row tiles of query rows, so each staged K/V tile serves
 //    every row of the block.  The key sequence is [rows of the selected documents in rank
