@@ -26,9 +26,9 @@
 //  * v_mfma_f32_16x16x32_bf16 products (exact bf16 products, float32 sums) are scaled by
 //    rs and cs in float32 and summed over heads in registers, as a pipeline over heads
 //    (one head's products, the next head's LDS reads and the previous head's scaling in
-//    flight together): no head exchange through LDS.  The tile's maximum
-//    over its valid query rows is folded into a running maximum per bank row while the
-//    tiles belong to one query.
+//    flight together): no head exchange through LDS.  Each lane folds the maximum of its
+//    four query rows of the tile into a running maximum while the tiles belong to one
+//    query; the lanes of a bank row are combined once per query.
 //  * When the query changes, each bank row's maximum is reduced over the rows of its
 //    document inside the wave (a segmented max over lanes) and merged into the document
 //    score with an integer atomic max/min on the float bits, after a fill of -inf.  The
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
   __shared__ __align__(16) bf16_t Abuf[2][SQ * RS];
   __shared__ __align__(16) float rsb[2][H][SQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
   const int cl = lane & 15, g = lane >> 4;
   const int64_t C = a.n_chunks;
   const int64_t base = (int64_t)blockIdx.x * BROWS + w * (BNT * 16);
@@ -168,37 +168,53 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
   }
 
   // ---- query stages ----
-  // Chunk i of a thread is 16 bytes of row (tid + i * BTHREADS) / CPR of the stage: the
-  // first CPT / 2 chunks lie in rows 0..15 (the first tile), the others in rows 16..31.
-  // A row past its query's end re-reads the tile's last row: its scores are masked out
-  // before any maximum.
-  static_assert(BTHREADS % CPR == 0 && CPT % 2 == 0, "a chunk index must pick one tile");
-  uint4 stage_regs[CPT];
-  auto load_stage = [&](const Tile& t0, const Tile& t1) __attribute__((always_inline)) {
+  // Wave w stages rows w*4 .. w*4+3 of the stage (all heads), so its rows lie in one tile
+  // (waves 0..3: the first, 4..7: the second).  Load i of a lane holds 16 bytes of the
+  // (row, head) pair p = (i / 2) * 8 + lane / 8 of the wave: its chunk (lane & 7) + 8 (i & 1).
+  // The eight lanes of a pair and the lane's two loads of it cover the pair's 256 bytes,
+  // so every load instruction reads eight whole 128-byte lines, and a pair's squared norm
+  // is summed in the lane and over eight lanes.  A row past its query's end re-reads the
+  // tile's last row: its scores are masked out before any maximum.
+  static_assert(BWAVES * 4 == SQ && CPT * 64 == 4 * H * 16 && CPT % 4 == 0, "stage split");
+  // The stage is loaded and committed in two halves (the wave's rows w*4, w*4+1, then
+  // w*4+2, w*4+3): each half's loads are in flight during one tile's products, and only
+  // half the stage occupies registers at a time.
+  constexpr int CPH = CPT / 2;  // loads per half
+  uint4 stage_regs[CPH];
+  auto load_half = [&](const Tile& t0, const Tile& t1, int half) __attribute__((always_inline)) {
+    const Tile& t = (w < BWAVES / 2) ? t0 : t1;  // uniform
+    if (t.b >= a.n_queries) return;              // uniform: no such tile
+    const char* tb = reinterpret_cast<const char*>(a.Qr + (int64_t)(t.off + t.t0) * HD);  // uniform
+    const int last = t.lq - t.t0 - 1;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const Tile& t = (i < CPT / 2) ? t0 : t1;
-      if (t.b >= a.n_queries) continue;  // uniform: no such tile
-      const int q = tid + i * BTHREADS;
-      const int row = (q / CPR) & 15, cr = q % CPR;
-      const char* tb = reinterpret_cast<const char*>(a.Qr + (int64_t)(t.off + t.t0) * HD);  // uniform
-      const uint32_t off = (uint32_t)(min(row, t.lq - t.t0 - 1) * (HD * 2) + cr * 16);
-      stage_regs[i] = *reinterpret_cast<const uint4*>(tb + off);
+    for (int k = 0; k < CPH; ++k) {
+      const int i = half * CPH + k;
+      const int p = (i / 2) * 8 + (lane >> 3);
+      const int row = (w * 4 + p / H) & 15, head = p % H, chunk = (lane & 7) + 8 * (i & 1);
+      const uint32_t off = (uint32_t)(min(row, last) * (HD * 2) + head * (BD * 2) + chunk * 16);
+      stage_regs[k] = *reinterpret_cast<const uint4*>(tb + off);
     }
   };
-  auto commit_stage = [&](int buf) __attribute__((always_inline)) {
+  auto commit_half = [&](int buf, int half) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int q = tid + i * BTHREADS;
-      const int row = q / CPR, cr = q % CPR;
-      const uint4 v = stage_regs[i];
-      *reinterpret_cast<uint4*>(&Abuf[buf][row * RS + cr * 8]) = v;
-      float ss = dot2_bf16(v.x, v.x, 0.f);
-      ss = dot2_bf16(v.y, v.y, ss);
-      ss = dot2_bf16(v.z, v.z, ss);
-      ss = dot2_bf16(v.w, v.w, ss);
-      ss = group_sum_last<16>(ss);  // the 16 chunks of one (row, head)
-      if ((lane & 15) == 15) rsb[buf][cr / (BD / 8)][row] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) / (float)H : 0.f;
+    for (int k = 0; k < CPH; k += 2) {
+      const int i = half * CPH + k;
+      const int p = (i / 2) * 8 + (lane >> 3);
+      const int row = w * 4 + p / H, head = p % H, chunk = lane & 7;
+      bf16_t* dst = &Abuf[buf][row * RS + head * BD + chunk * 8];
+      const uint4 v0 = stage_regs[k], v1 = stage_regs[k + 1];
+      *reinterpret_cast<uint4*>(dst) = v0;
+      *reinterpret_cast<uint4*>(dst + 64) = v1;
+      float ss = dot2_bf16(v0.x, v0.x, 0.f);
+      ss = dot2_bf16(v0.y, v0.y, ss);
+      ss = dot2_bf16(v0.z, v0.z, ss);
+      ss = dot2_bf16(v0.w, v0.w, ss);
+      ss = dot2_bf16(v1.x, v1.x, ss);
+      ss = dot2_bf16(v1.y, v1.y, ss);
+      ss = dot2_bf16(v1.z, v1.z, ss);
+      ss = dot2_bf16(v1.w, v1.w, ss);
+      ss = group_sum_last<8>(ss);  // the eight lanes of the pair
+      if ((lane & 7) == 7) rsb[buf][head][row] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) / (float)H : 0.f;
     }
   };
 
@@ -211,7 +227,30 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
     run_arg[j] = 0;
   }
 
+  // Each lane's running maximum covers its own four rows of every tile; the four lane
+  // groups of a column are combined once per query, here.  ARG keeps the first token: a
+  // lane's tokens rise with its rows and tiles, and equal maxima take the smaller token.
   auto flush = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < BNT; ++j) {
+      float x = run[j];
+      int xi = run_arg[j];
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float ox = __shfl_xor(x, o, 64);
+        if constexpr (ARG) {
+          const int oi = __shfl_xor(xi, o, 64);
+          if (ox > x || (ox == x && oi < xi)) {
+            x = ox;
+            xi = oi;
+          }
+        } else {
+          x = fmaxf(x, ox);
+        }
+      }
+      run[j] = x;
+      run_arg[j] = xi;
+    }
     if constexpr (ARG) {
 #pragma unroll
       for (int j = 0; j < BNT; ++j) {
@@ -249,79 +288,87 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
     for (int j = 0; j < BNT; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tot[j][i] = 0.f;
-    // Software pipeline over heads: head h's products run while head h + 1's operands
-    // load from LDS and head h - 1's products are scaled into the total.
-    bf16x8_t A[2][KS];
-    float4 r4[2];
+    // Software pipeline over heads: head h's products run while head h + 2's operands
+    // load from LDS and head h - 1's products are scaled into the total (a ring of three
+    // operand slots; head h - 1's slot takes head h + 2's operands once its products are
+    // issued, so its row scales are copied out first).
+    bf16x8_t A[3][KS];
+    float4 r4[3];
     f32x4_t acc[2][BNT];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) A[0][ks] = *reinterpret_cast<const bf16x8_t*>(arow + ks * 32);
-    r4[0] = *reinterpret_cast<const float4*>(rrow);
+    for (int h = 0; h < 2 && h < H; ++h) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) A[h][ks] = *reinterpret_cast<const bf16x8_t*>(arow + h * BD + ks * 32);
+      r4[h] = *reinterpret_cast<const float4*>(rrow + h * SQ);
+    }
 #pragma unroll
     for (int h = 0; h <= H; ++h) {
-      const int cur = h & 1, prv = cur ^ 1;
-      const float4 rr = r4[prv];  // head h - 1's row scales, read before the slot refills
-      if (h + 1 < H) {
+      const int cur = h % 3, prv = (h + 2) % 3;
+      const int ac = h & 1, ap = ac ^ 1;
+      const float4 rr = r4[prv];  // head h - 1's row scales
+      if (h + 2 < H) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          A[prv][ks] = *reinterpret_cast<const bf16x8_t*>(arow + (h + 1) * BD + ks * 32);
-        r4[prv] = *reinterpret_cast<const float4*>(rrow + (h + 1) * SQ);
+          A[prv][ks] = *reinterpret_cast<const bf16x8_t*>(arow + (h + 2) * BD + ks * 32);
+        r4[prv] = *reinterpret_cast<const float4*>(rrow + (h + 2) * SQ);
       }
       if (h < H) {
 #pragma unroll
         for (int j = 0; j < BNT; ++j) {
-          acc[cur][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          acc[ac][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            acc[cur][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[cur][ks], Bt[j][h][ks], acc[cur][j], 0, 0, 0);
+            acc[ac][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[cur][ks], Bt[j][h][ks], acc[ac][j], 0, 0, 0);
         }
       }
       if (h > 0) {
 #pragma unroll
         for (int j = 0; j < BNT; ++j) {
           const float c = cs[j][h - 1];
-          tot[j][0] += acc[prv][j][0] * rr.x * c;
-          tot[j][1] += acc[prv][j][1] * rr.y * c;
-          tot[j][2] += acc[prv][j][2] * rr.z * c;
-          tot[j][3] += acc[prv][j][3] * rr.w * c;
+          tot[j][0] += acc[ap][j][0] * rr.x * c;
+          tot[j][1] += acc[ap][j][1] * rr.y * c;
+          tot[j][2] += acc[ap][j][2] * rr.z * c;
+          tot[j][3] += acc[ap][j][3] * rr.w * c;
         }
       }
     }
-    // max over the tile's valid query rows (rows g*4 + i of column cl)
+    // this lane's maximum over its four rows g*4 + i of the tile, past the query's end
+    // masked (only a query's last tile has such rows: a uniform branch)
     const int nv = t.lq - t.t0;
     float m[BNT];
     int mi[BNT];  // ARG: the first row reaching it
 #pragma unroll
     for (int j = 0; j < BNT; ++j) {
-      float x = -INFINITY;
+      float x = tot[j][0];
       int xi = 0;
+      if (nv >= 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (ARG) {
-          if (g * 4 + i < nv && tot[j][i] > x) {
-            x = tot[j][i];
-            xi = g * 4 + i;
-          }
-        } else {
-          x = (g * 4 + i < nv) ? fmaxf(x, tot[j][i]) : x;
-        }
-      }
-      if constexpr (ARG) {
-#pragma unroll
-        for (int o = 16; o <= 32; o <<= 1) {
-          const float ox = __shfl_xor(x, o, 64);
-          const int oi = __shfl_xor(xi, o, 64);
-          if (ox > x || (ox == x && oi < xi)) {
-            x = ox;
-            xi = oi;
+        for (int i = 1; i < 4; ++i) {
+          if (ARG) {
+            if (tot[j][i] > x) {
+              x = tot[j][i];
+              xi = i;
+            }
+          } else {
+            x = fmaxf(x, tot[j][i]);
           }
         }
       } else {
-        x = fmaxf(x, __shfl_xor(x, 16, 64));
-        x = fmaxf(x, __shfl_xor(x, 32, 64));
+        x = (g * 4 < nv) ? x : -INFINITY;
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+          if (ARG) {
+            if (g * 4 + i < nv && tot[j][i] > x) {
+              x = tot[j][i];
+              xi = i;
+            }
+          } else {
+            x = (g * 4 + i < nv) ? fmaxf(x, tot[j][i]) : x;
+          }
+        }
       }
       m[j] = x;
-      mi[j] = t.t0 + xi;
+      mi[j] = t.t0 + g * 4 + xi;
     }
     if (t.b != run_b) {
       if (run_b >= 0) flush();
@@ -349,20 +396,25 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
   Tile t0 = query_start(a, 0);
   Tile t1 = next_tile(a, t0);
   if (t0.b >= a.n_queries) return;  // no query has tokens (uniform over the grid)
-  load_stage(t0, t1);
-  commit_stage(0);
+  load_half(t0, t1, 0);
+  commit_half(0, 0);
+  load_half(t0, t1, 1);
+  commit_half(0, 1);
   __syncthreads();
   int cur = 0;
   while (t0.b < a.n_queries) {
     const Tile n0 = next_tile(a, t1);
     const Tile n1 = next_tile(a, n0);
     const bool more = n0.b < a.n_queries;
-    if (more) load_stage(n0, n1);  // in flight during the products
-    if (has_rows) {
-      compute_tile(t0, cur, 0);
-      if (t1.b < a.n_queries) compute_tile(t1, cur, 1);
+    // the other buffer is free: every wave finished the previous stage before the barrier
+    if (more) load_half(n0, n1, 0);  // in flight during the first tile's products
+    if (has_rows) compute_tile(t0, cur, 0);
+    if (more) {
+      commit_half(cur ^ 1, 0);
+      load_half(n0, n1, 1);  // in flight during the second tile's products
     }
-    if (more) commit_stage(cur ^ 1);
+    if (has_rows && t1.b < a.n_queries) compute_tile(t1, cur, 1);
+    if (more) commit_half(cur ^ 1, 1);
     __syncthreads();
     t0 = n0;
     t1 = n1;
