@@ -257,14 +257,18 @@ def plant_needles(wl: Workload, n_docs: int, qr_prefill: torch.Tensor):
 
 
 def gen_pooled_bank(wl: Workload, chunk_off: np.ndarray, device, kv_device=None,
-                    slice_rows: int = 1 << 16):
+                    slice_rows: int = 1 << 16, needle_dirs: Optional[torch.Tensor] = None,
+                    needle_ids: Optional[np.ndarray] = None, krbar_only: bool = False):
     """A bank drawn directly at chunk level (for banks whose token states exceed memory).
 
     Row c of document d is mu_d + 0.125 * eps with mu_d ~ N(0, doc_offset_std^2) per
     document and tensor and eps ~ N(0, 1) per element: 0.125 = 1/sqrt(64) is the spread
     of the mean of a full chunk of unit-variance tokens.  ``chunk_off`` ([N+1]) gives each
     document's rows.  Krbar is placed on ``device``; Kbar / Vbar on ``kv_device``
-    ("cpu-pinned" for page-locked host memory, else a torch device).
+    ("cpu-pinned" for page-locked host memory, else a torch device), or not drawn at all
+    with ``krbar_only`` (then None).  Needle documents get the Krbar offset
+    a * needle_dirs[h] instead of mu_d, with a chosen as in ``gen_token_states``: a row
+    then makes cosine ``needle_cos`` with that direction, a^2 / (a^2 + D/64) = needle_cos^2.
     """
     sh = wl.shape
     N = len(chunk_off) - 1
@@ -273,11 +277,17 @@ def gen_pooled_bank(wl: Workload, chunk_off: np.ndarray, device, kv_device=None,
     counts = torch.as_tensor(np.diff(chunk_off), device=device)
     doc_of_row = torch.repeat_interleave(torch.arange(N, device=device), counts)
     kv_device = device if kv_device is None else kv_device
-    out = {}
-    for name, heads, where in (("Krbar", sh.h_r, device), ("Kbar", sh.h_kv, kv_device),
-                               ("Vbar", sh.h_kv, kv_device)):
+    out = {"Kbar": None, "Vbar": None}
+    tensors = (("Krbar", sh.h_r, device),) if krbar_only else (
+        ("Krbar", sh.h_r, device), ("Kbar", sh.h_kv, kv_device), ("Vbar", sh.h_kv, kv_device))
+    for name, heads, where in tensors:
         mu = torch.randn((N, heads, sh.d), generator=torch_gen(device, wl.seed, name),
                          device=device, dtype=torch.float32) * wl.doc_offset_std
+        if name == "Krbar" and needle_ids is not None and len(needle_ids):
+            c2 = wl.needle_cos ** 2
+            a = math.sqrt(c2 * (sh.d / sh.chunk) / (1.0 - c2))
+            ids_t = torch.as_tensor(needle_ids, device=device, dtype=torch.long)
+            mu[ids_t] = a * needle_dirs.to(device=device, dtype=torch.float32)[None]
         g = torch_gen(device, wl.seed + 500, name)
         if where == "cpu-pinned":
             X = torch.empty((C, heads, sh.d), dtype=dt, pin_memory=True)

@@ -6,7 +6,7 @@ group by group, and the top-k set with the oracle's full ranking.  Pooled rows a
 compared for sampled documents (pooling 10M tokens in float64 would take minutes), and
 attention for every query.  Exact properties are checked as well: the top-k is the
 (score desc, id asc) order of the GPU's own document scores, and planted needles are
-recalled.
+recalled (10M-token bank, and the 100M-token bank's routing keys).
 """
 import gc
 
@@ -226,6 +226,33 @@ def test_bank100m_host_full():
                             [0, r + 1], np.arange(len(sel), dtype=np.int32)[None], coff_c, kb, vb, sh.rope_base)
         e = assert_attn_close(out1, ref, "bf16", f"decode step {s}")
         say(f"  decode step {s}: attention max abs err {e:.3g}")
+
+
+def test_bank100m_needles():
+    # the headline bank (routing keys only) with five needle documents whose rows make cosine
+    # 0.9 with the query's mean routing direction: all five are routed into the top-16, and
+    # their scores and those of sampled documents agree with the oracle
+    say("case full-size bank100m with 5 planted needles: recall and sampled scores")
+    wl = W.workload("bank100m_host", needles=5)
+    sh = wl.shape
+    lens = W.doc_lengths(wl)
+    off = W.token_offsets(lens)
+    coff = M.msa_chunk_offsets(off, sh.chunk)
+    q = W.gen_queries(wl, DEV)
+    Lq = int(q["q_len"][0])
+    needles, dirs = W.plant_needles(wl, len(lens), q["Qr"][:Lq])
+    Krb_rows, _, _ = W.gen_pooled_bank(wl, coff, DEV, needle_dirs=dirs, needle_ids=needles, krbar_only=True)
+    Qr, q_off, ids, sc, ds = run_route(q, coff, as_keys(Krb_rows), wl.k)
+    ids_h = ids.cpu().numpy()[0]
+    assert_topk_consistent(ids_h, sc[0], ds[0], wl.k, "bank100m needles")
+    docs = sample_docs(len(lens), 4, extra=needles)
+    Qh = f64(Qr[:Lq])
+    o = np.array([O.doc_scores_one(Qh, f64(Krb_rows[int(coff[d]):int(coff[d + 1])]), [0, int(coff[d + 1] - coff[d])])[0]
+                  for d in docs])
+    err = assert_scores_close(ds[0][docs], o, "bf16", "bank100m needles: sampled document scores")
+    recalled = set(int(x) for x in needles) & set(int(x) for x in ids_h)
+    say(f"  bank100m: needles {list(needles)} recalled {len(recalled)}/5; {len(docs)} scores, max rel err {err:.3g}")
+    assert len(recalled) == len(needles)
 
 
 def test_batch32_bank10m_full():
