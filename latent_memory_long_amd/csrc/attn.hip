@@ -386,14 +386,7 @@ hipError_t launch_attn_t(const AttnArgs& r, AttnK& k, bool host, hipStream_t s) 
   const int nq_blocks = sizeof(T) == 4 ? (int)((r.total_q + RPW - 1) / RPW) : 0;
   const int nk_blocks = (int)((r.total_kv + RPW - 1) / RPW);
   if constexpr (sizeof(T) == 2) {
-    // one launch: the local K rotated (blocks 0 .. nk_blocks-1) and the table written
-    AttnK kp = k;
-    kp.rtab = nullptr;
-    const int64_t n = k.n_pos * (D / 2);
-    const int tab_blocks = (int)((n + 255) / 256);
-    hipLaunchKernelGGL((rope_prep<D>), dim3((unsigned)(nk_blocks + tab_blocks)), dim3(256), 0, s, kp, 0, nk_blocks,
-                       (float*)k.rtab);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_rope_setup<D>(k, 0, nk_blocks, s);
     if (e != hipSuccess) return e;
   } else if (nq_blocks + nk_blocks > 0) {
     hipLaunchKernelGGL((rope_local<T, D>), dim3(nq_blocks + nk_blocks), dim3(256), 0, s, k, nq_blocks);

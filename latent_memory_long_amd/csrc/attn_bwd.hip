@@ -693,11 +693,8 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
   {
     const int nq_blocks = (int)((f.total_q + RPW - 1) / RPW);
     const int nk_blocks = (int)((f.total_kv + RPW - 1) / RPW);
-    AttnK kp = k.f;
-    kp.rtab = nullptr;
-    const int tab_blocks = (int)((k.f.n_pos * (D / 2) + 255) / 256);
-    hipLaunchKernelGGL((rope_prep<D>), dim3((unsigned)(nq_blocks + nk_blocks + tab_blocks)), dim3(256), 0, s, kp,
-                       nq_blocks, nq_blocks + nk_blocks, (float*)k.f.rtab);
+    const hipError_t e = launch_rope_setup<D>(k.f, nq_blocks, nq_blocks + nk_blocks, s);
+    if (e != hipSuccess) return e;
   }
   {
     const int64_t n_rows = f.total_q * f.hq;

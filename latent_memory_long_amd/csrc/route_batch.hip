@@ -195,7 +195,8 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
       stage_regs[k] = *reinterpret_cast<const uint4*>(tb + off);
     }
   };
-  auto commit_half = [&](int buf, int half) __attribute__((always_inline)) {
+  auto commit_half = [&](const Tile& t0, const Tile& t1, int buf, int half) __attribute__((always_inline)) {
+    if (((w < BWAVES / 2) ? t0 : t1).b >= a.n_queries) return;  // uniform: nothing was loaded
 #pragma unroll
     for (int k = 0; k < CPH; k += 2) {
       const int i = half * CPH + k;
@@ -397,9 +398,9 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
   Tile t1 = next_tile(a, t0);
   if (t0.b >= a.n_queries) return;  // no query has tokens (uniform over the grid)
   load_half(t0, t1, 0);
-  commit_half(0, 0);
+  commit_half(t0, t1, 0, 0);
   load_half(t0, t1, 1);
-  commit_half(0, 1);
+  commit_half(t0, t1, 0, 1);
   __syncthreads();
   int cur = 0;
   while (t0.b < a.n_queries) {
@@ -410,11 +411,11 @@ __global__ __launch_bounds__(BTHREADS) void route_scan_batch(BatchK a) {
     if (more) load_half(n0, n1, 0);  // in flight during the first tile's products
     if (has_rows) compute_tile(t0, cur, 0);
     if (more) {
-      commit_half(cur ^ 1, 0);
+      commit_half(n0, n1, cur ^ 1, 0);
       load_half(n0, n1, 1);  // in flight during the second tile's products
     }
     if (has_rows && t1.b < a.n_queries) compute_tile(t1, cur, 1);
-    if (more) commit_half(cur ^ 1, 1);
+    if (more) commit_half(n0, n1, cur ^ 1, 1);
     __syncthreads();
     t0 = n0;
     t1 = n1;
