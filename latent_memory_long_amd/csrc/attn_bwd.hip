@@ -12,8 +12,10 @@
 // bank-shaped arrays (a row chosen by several queries collects every query's share).
 //
 // Kernels (bf16 inputs, float32 gradients, MFMA with float32 accumulation):
-//  * rope_table and rope_local (shared with the forward): the cos / sin table of every
-//    position in use, and Q and the local K rotated with it into the workspace.
+//  * rope_table (shared with the forward): the cos / sin table of every position in use.
+//  * bwd_prep: in one launch, Q and the local K rotated with the table into the workspace
+//    (rope_local's blocks) and, in the other blocks, every row's rowsum(dO O) and its
+//    log-sum-exp in log2 units (the row statistics, below).
 //  * bwd_dq: one workgroup per (query, kv head, block of query rows), with the forward's key
 //    loop (attn_shared.hpp's key_loop).
 //    Unless the forward's per-row log-sum-exp is passed in, a first pass over the key tiles
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       Qf[m][kk] = __builtin_bit_cast(bf16x8_t, qv);
       dOf[m][kk] = __builtin_bit_cast(bf16x8_t, dv);
     }
-    // rowsum(dO * O), from bwd_rows
+    // rowsum(dO * O), from bwd_prep's row statistics
     drow[m] = row_ok[m] ? bk.drow[(int64_t)(q0 + t_of[m]) * a.hq + hq_of[m]] : 0.f;
   }
 
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       lse[m] = v > -INFINITY ? v * LOG2E : INFINITY;
     }
   }
-  if (bk.lse_in == nullptr) {  // else bwd_rows has written the log2-unit copy for bwd_dkv
+  if (bk.lse_in == nullptr) {  // else bwd_prep has written the log2-unit copy for bwd_dkv
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       if (row_ok[m] && g4 == 0) bk.lse[(int64_t)(q0 + t_of[m]) * a.hq + hq_of[m]] = lse[m];
@@ -314,14 +316,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // ---- row statistics ahead of both gradient kernels ------------------------------------
 // rowsum(dO * O) of every (token, query head) row and, when the forward's log-sum-exp is
-// given, its copy in log2 units: after this launch bwd_dq and bwd_dkv depend on nothing of
-// each other.  Lane (cl, g4) of a wave sums elements kk*32 + g4*8 .. +7 of row cl, then the
+// given, its copy in log2 units: after them bwd_dq and bwd_dkv depend on nothing of each
+// other.  Block blk covers rows blk*64 .. +63.  Lane (cl, g4) of a wave sums elements kk*32 + g4*8 .. +7 of row cl, then the
 // four lanes of the row are added (the order the values were first summed in).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_rows(BwdK bk, int64_t n_rows) {
+__device__ __forceinline__ void bwd_rows_block(const BwdK& bk, int64_t n_rows, int64_t blk) {
   constexpr int KK = D / 32;
   const int lane = threadIdx.x & 63, cl = lane & 15, g4 = lane >> 4;
-  const int64_t orow = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + cl;
+  const int64_t orow = (blk * 4 + (threadIdx.x >> 6)) * 16 + cl;
   const bool ok = orow < n_rows;
   const int64_t ro = (ok ? orow : 0) * D + g4 * 8;
   const bf16_t* dp = (const bf16_t*)bk.dO + ro;
@@ -349,6 +351,17 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdK bk, int64_t n_rows) {
       bk.lse[orow] = v > -INFINITY ? v * LOG2E : INFINITY;
     }
   }
+}
+
+// The backward's set-up in one launch (the cos / sin table already written): blocks below
+// n_rot rotate Q and the local K as rope_local does, the others compute the row statistics.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep(BwdK bk, int nq_blocks, int n_rot, int64_t n_rows) {
+  if ((int)blockIdx.x < n_rot) {  // uniform over the block
+    rope_local_rows<bf16_t, D>(bk.f, nq_blocks, blockIdx.x);
+    return;
+  }
+  bwd_rows_block<D>(bk, n_rows, (int64_t)blockIdx.x - n_rot);
 }
 
 // A second stream per device, for running bwd_dkv beside bwd_dq: created once (default
@@ -693,13 +706,18 @@ hipError_t launch_bwd_t(const AttnBwdArgs& r, hipStream_t s) {
   {
     const int nq_blocks = (int)((f.total_q + RPW - 1) / RPW);
     const int nk_blocks = (int)((f.total_kv + RPW - 1) / RPW);
-    const hipError_t e = launch_rope_setup<D>(k.f, nq_blocks, nq_blocks + nk_blocks, s);
-    if (e != hipSuccess) return e;
-  }
-  {
     const int64_t n_rows = f.total_q * f.hq;
-    if (n_rows > 0)
-      hipLaunchKernelGGL((bwd_rows<D>), dim3((unsigned)((n_rows + 63) / 64)), dim3(256), 0, s, k, n_rows);
+    const int tab_blocks = (int)((k.f.n_pos * (D / 2) + 255) / 256);
+    hipLaunchKernelGGL((rope_table<D>), dim3((unsigned)tab_blocks), dim3(256), 0, s, (float*)k.f.rtab, k.f.n_pos,
+                       k.f.rope_base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t blocks = nq_blocks + nk_blocks + (n_rows + 63) / 64;
+    if (blocks > 0)
+      hipLaunchKernelGGL((bwd_prep<D>), dim3((unsigned)blocks), dim3(256), 0, s, k, nq_blocks, nq_blocks + nk_blocks,
+                         n_rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   const int G = f.hq / f.h_kv;
   const int rows = min(attn_rows_per_block(f.max_q_len, G), 128);
