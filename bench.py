@@ -465,6 +465,26 @@ def cpu_pool_sample(n_docs=64):
                       f"thread (the oracle's pooling loops over chunks in Python), {t:.1f} s"}
 
 
+def batch_scan_only(dev, n):
+    """The batched router scan of the 32-query batch, n launches over the 10M-token bank drawn
+    already pooled: a short program for hardware counter runs of that one kernel."""
+    wl = W.workload("batch32_bank10m")
+    sh = wl.shape
+    lens = W.doc_lengths(wl)
+    coff = M.msa_chunk_offsets(W.token_offsets(lens), sh.chunk)
+    Krb, Kb, Vb = W.gen_pooled_bank(wl, coff, dev, krbar_only=True)
+    Krb = M.RouteKeys.from_rows(Krb)
+    q = W.gen_queries(wl, dev)
+    q_len = q["q_len"]
+    q_off = torch.tensor(np.concatenate([[0], np.cumsum(q_len)]).astype(np.int32), device=dev)
+    ds = torch.empty((len(q_len), len(lens)), dtype=torch.float32, device=dev)
+    coff_d = torch.tensor(coff, device=dev)
+    for _ in range(n):
+        M.msa_route_scan(q["Qr"], q_off, int(q_len.max()), Krb, coff_d, out=ds)
+    torch.cuda.synchronize()
+    log(f"batched scan: {n} launches")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -482,7 +502,13 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device 3 times: a kernel of known traffic "
                          "against which hardware byte counters are scaled")
+    ap.add_argument("--batch-scan-launches", type=int, default=0, metavar="N",
+                    help="only launch the 32-query batched scan N times over the 10M-token bank drawn "
+                         "pooled (for counter runs), then exit")
     args = ap.parse_args()
+    if args.batch_scan_launches:
+        batch_scan_only(torch.device("cuda:0"), args.batch_scan_launches)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "sharded multi-GPU path.", file=sys.stderr)
