@@ -332,16 +332,42 @@ __global__ __launch_bounds__(TK_THREADS) void topk_reg(TopkArgs a, unsigned long
   }
 }
 
-// Merge of the slices' candidates: the k best composites of n_slices * k, sorted.
+// Merge of the slices' candidates: the k best composites of n_slices * k, sorted.  The
+// composites of distinct documents are distinct, so up to RANK_MAX candidates are placed by
+// rank (the number of larger candidates) after one barrier; more go through a bitonic sort.
+// Every valid document's composite is nonzero and at least min(k, n_docs) of them are
+// candidates, so the zero padding of short slices only takes ranks past the valid ones.
+constexpr int RANK_MAX = 512;
 __global__ __launch_bounds__(TK_THREADS) void topk_merge(TopkArgs a, int n_slices,
                                                          const unsigned long long* cand) {
   __shared__ unsigned long long buf[MERGE_MAX];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int total = n_slices * a.k;
+  const int keff = min(a.k, a.n_docs);
+  const unsigned long long* c = cand + (int64_t)b * total;
+  int32_t* ids = a.ids + (int64_t)b * a.k;
+  float* scores = a.scores + (int64_t)b * a.k;
+  if (total <= RANK_MAX) {
+    for (int i = tid; i < total; i += TK_THREADS) buf[i] = c[i];
+    __syncthreads();
+    for (int i = tid; i < total; i += TK_THREADS) {
+      const unsigned long long x = buf[i];
+      int r = 0;
+      for (int j = 0; j < total; ++j) r += buf[j] > x;
+      if (r < keff) {
+        ids[r] = (int32_t)(~(uint32_t)(x & 0xffffffffull));
+        scores[r] = key_score((uint32_t)(x >> 32));
+      }
+    }
+    for (int r = keff + tid; r < a.k; r += TK_THREADS) {
+      ids[r] = -1;
+      scores[r] = -INFINITY;
+    }
+    return;
+  }
   int n2 = 1;
   while (n2 < total) n2 <<= 1;
-  const unsigned long long* c = cand + (int64_t)b * total;
   for (int i = tid; i < n2; i += TK_THREADS) buf[i] = (i < total) ? c[i] : 0ull;
   __syncthreads();
   for (int k2 = 2; k2 <= n2; k2 <<= 1) {
@@ -357,15 +383,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge(TopkArgs a, int n_slice
       __syncthreads();
     }
   }
-  const int keff = min(a.k, a.n_docs);
   for (int r = tid; r < a.k; r += TK_THREADS) {
     if (r < keff) {
       const unsigned long long v = buf[r];
-      a.ids[(int64_t)b * a.k + r] = (int32_t)(~(uint32_t)(v & 0xffffffffull));
-      a.scores[(int64_t)b * a.k + r] = key_score((uint32_t)(v >> 32));
+      ids[r] = (int32_t)(~(uint32_t)(v & 0xffffffffull));
+      scores[r] = key_score((uint32_t)(v >> 32));
     } else {
-      a.ids[(int64_t)b * a.k + r] = -1;
-      a.scores[(int64_t)b * a.k + r] = -INFINITY;
+      ids[r] = -1;
+      scores[r] = -INFINITY;
     }
   }
 }
