@@ -101,6 +101,11 @@ def _check(grads, ref, what):
         assert err <= GRAD_RTOL * top + GRAD_ATOL, f"{what} {n}: max err {err:.3g} vs max {top:.3g}"
 
 
+_MAXK_RNG = np.random.default_rng(101)
+_MAXK_COUNTS = [int(x) for x in _MAXK_RNG.integers(1, 3, size=1100)]
+_MAXK_IDS = [[int(x) for x in _MAXK_RNG.choice(1100, size=1024, replace=False)],
+             [int(x) for x in _MAXK_RNG.choice(1100, size=924, replace=False)] + [-1] * 100]
+
 CASES = [
     # name, q_lens, extra kv (decode cache), hq, h_kv, d, chunk counts per doc, ids per query
     ("prefill64_gqa4_d128", [64], [0], 32, 8, 128, [3, 17, 1, 40, 9, 2], [[3, 1, 4, 0]]),
@@ -115,6 +120,10 @@ CASES = [
     # and the log-sum-exp straight from the attention kernel instead of the split merge
     ("batch8_unsplit", [12, 3, 20, 7, 1, 16, 9, 5], [0, 4, 0, 2, 30, 0, 1, 0], 32, 8, 128,
      [3, 8, 1, 5, 12, 2, 6], [[0, 4], [2, 1], [6, 5], [3, -1], [4, 0], [1, 2], [5, 6], [0, 3]]),
+    # k = 1024, the largest the library takes: 1,100 documents of one or two rows, the two
+    # queries sharing many of them (their rows' gradients collect both shares); the second
+    # leaves its last 100 slots unused
+    ("k1024_max", [7, 3], [2, 0], 8, 2, 64, _MAXK_COUNTS, _MAXK_IDS),
 ]
 
 

@@ -496,6 +496,35 @@ def test_attention(case):
         assert torch.equal(out_h, out) and torch.equal(out_2, out)
 
 
+def test_attention_max_k():
+    # k = 1024, the largest the library takes: 1,100 documents of one or two rows, so every
+    # query's memory spans over a thousand documents (the document table is built 64 ids at a
+    # time, and a key's document is found through all eleven lifting steps); the second query
+    # leaves its last 100 slots unused, as msa_route_topk does when fewer documents qualify
+    say("case attention k = 1024")
+    rng = np.random.default_rng(95)
+    counts = rng.integers(1, 3, size=1100)
+    coff, Kb = random_bank(counts, 2, 64, "bf16", 96, doc_std=1.0)
+    _, Vb = random_bank(counts, 2, 64, "bf16", 97, doc_std=1.0)
+    k = 1024
+    ids = np.full((2, k), -1, dtype=np.int32)
+    ids[0] = rng.choice(len(counts), size=k, replace=False)
+    ids[1, :k - 100] = rng.choice(len(counts), size=k - 100, replace=False)
+    q_lens, kv_lens = [12, 5], [14, 5]
+    Q = _cpu_randn((sum(q_lens), 8, 64), 98).to(torch.bfloat16)
+    Kl = _cpu_randn((sum(kv_lens), 2, 64), 99).to(torch.bfloat16)
+    Vl = _cpu_randn((sum(kv_lens), 2, 64), 100).to(torch.bfloat16)
+    q_off = np.concatenate([[0], np.cumsum(q_lens)])
+    kv_off = np.concatenate([[0], np.cumsum(kv_lens)])
+    out = M.msa_sparse_attn(Q.to(DEV), Kl.to(DEV), Vl.to(DEV), torch.tensor(q_off, dtype=torch.int32, device=DEV),
+                            torch.tensor(kv_off, dtype=torch.int32, device=DEV), max(q_lens),
+                            torch.tensor(ids, device=DEV), torch.tensor(coff, device=DEV), Kb, Vb, rope_base=1e6)
+    torch.cuda.synchronize()
+    ref = O.sparse_attn(f64(Q), f64(Kl), f64(Vl), q_off, kv_off, ids, coff, f64(Kb), f64(Vb), 1e6)
+    err = assert_attn_close(out, ref, "bf16", "k = 1024")
+    say(f"  max abs err {err:.3g}")
+
+
 def test_attention_scale_argument():
     say("case attention explicit scale")
     coff, Kb = random_bank([3, 2], 2, 64, "bf16", 90)
