@@ -79,6 +79,8 @@ def _check_lse(lse, Q, Kl, Kb, q_off, kv_off, ids, coff, d):
     qn = np.linalg.norm(f64(Q), axis=-1)
     G = Q.shape[1] // Kl.shape[1]
     for b in range(len(q_off) - 1):
+        if q_off[b + 1] == q_off[b]:
+            continue  # a query without tokens has no rows
         rows = [r for dd in ids[b] if dd >= 0 for r in range(int(coff[dd]), int(coff[dd + 1]))]
         kn = np.linalg.norm(f64(Kl)[kv_off[b]:kv_off[b + 1]], axis=-1).max(axis=0)
         if rows:
@@ -124,6 +126,8 @@ CASES = [
     # queries sharing many of them (their rows' gradients collect both shares); the second
     # leaves its last 100 slots unused
     ("k1024_max", [7, 3], [2, 0], 8, 2, 64, _MAXK_COUNTS, _MAXK_IDS),
+    # a query with no tokens between two others: its local keys get zero gradients
+    ("empty_query", [5, 0, 7], [0, 2, 1], 8, 2, 64, [3, 2, 4, 1], [[0, 2], [1, 3], [3, -1]]),
 ]
 
 

@@ -456,6 +456,8 @@ ATTN_CASES = [
     ("rows64_d128", "bf16", 32, 8, 128, [16, 3], 2, 6),
     ("rows128_d128", "bf16", 32, 8, 128, [32, 7], 0, 6),
     ("d32", "bf16", 4, 2, 32, [9], 0, 3),
+    # a query with no tokens (two local keys, nothing attends) between two others
+    ("empty_query", "bf16", 8, 2, 64, [5, 0, 7], 2, 4),
     ("fp32_tiny", "f32", 4, 2, 32, [8, 3], 2, 2),
     ("fp32_d128", "f32", 8, 2, 128, [5], 1, 3),
 ]
