@@ -196,14 +196,41 @@ __device__ __forceinline__ unsigned long long wave_bitonic_desc(unsigned long lo
 // Top-k of documents [blockIdx.x * SLICE, ...) of query blockIdx.y.  With cand == null the
 // slice is the whole query and the result goes to ids / scores; otherwise the slice's
 // best min(k, slice) composites (key << 32 | ~id, zero-padded to k) go to cand.
+// Exclusive prefix sum over the workgroup in thread order with one barrier: each thread adds
+// the totals of the waves before its own.  *total gets the sum.  wsum is written before the
+// barrier and read after it, so callers alternate two buffers between successive calls.
+__device__ __forceinline__ uint32_t block_excl_scan1(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < TK_WAVES; ++i) {
+    const uint32_t t = wsum[i];
+    before += i < w ? t : 0u;
+    all += t;
+  }
+  *total = all;
+  return before + x - v;
+}
+
 template <int KPT>
 __global__ __launch_bounds__(TK_THREADS) void topk_reg(TopkArgs a, unsigned long long* cand) {
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t wsum[TK_WAVES];
+  __shared__ uint32_t wsc[2][TK_WAVES];  // the radix passes' scans, alternating by pass
+  __shared__ uint32_t wao[2][TK_WAVES];  // the AND / OR of each wave's keys
   __shared__ unsigned long long sel[1024];
-  __shared__ uint32_t sh_digit, sh_above, sh_cnt, sh_bucket;
+  __shared__ uint32_t sh_digit[2], sh_above[2], sh_bucket[2], sh_cnt;
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.y;
   const int id0 = blockIdx.x * KPT * TK_THREADS;  // first document of the slice
   const int N = min(a.n_docs - id0, KPT * TK_THREADS);
@@ -218,8 +245,26 @@ __global__ __launch_bounds__(TK_THREADS) void topk_reg(TopkArgs a, unsigned long
     key[j] = (i < N) ? score_key(sb[i]) : 0u;
     if (i < N) { kand &= key[j]; kor |= key[j]; }
   }
-  kand = block_and_or(kand, true, wsum);
-  kor = block_and_or(kor, false, wsum);
+  // The AND and OR of all keys, the histogram cleared and the selection counter reset,
+  // behind one barrier.
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kand &= __shfl_xor(kand, o);
+    kor |= __shfl_xor(kor, o);
+  }
+  if (lane == 0) {
+    wao[0][w] = kand;
+    wao[1][w] = kor;
+  }
+  hist[2 * tid] = 0u;
+  hist[2 * tid + 1] = 0u;
+  if (tid == 0) sh_cnt = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TK_WAVES; ++i) {
+    kand &= wao[0][i];
+    kor |= wao[1][i];
+  }
   const uint32_t diff = kand ^ kor;
   int hi_bit = diff ? 31 - __clz(diff) : -1;      // highest bit on which keys differ
   uint32_t pmask = hi_bit >= 31 ? 0u : ~((2u << hi_bit) - 1u);
@@ -227,12 +272,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_reg(TopkArgs a, unsigned long
   uint32_t prefix = kand & pmask;                 // bits shared by every key
   uint32_t remaining = (uint32_t)keff;
   uint32_t bucket = (uint32_t)N;                  // keys whose determined bits equal prefix
+  // Each pass: histogram of the next digit (barrier), a one-barrier scan of it, the digit
+  // holding the k-th key published (barrier).  A thread reads only its own two bins and
+  // clears them for the next pass right after, and the published digit alternates between
+  // two slots, so three barriers a pass suffice.
+  int pass = 0;
   while (hi_bit >= 0 && bucket != remaining) {
     const int bits = min(11, hi_bit + 1);
     const int shift = hi_bit + 1 - bits;
     const uint32_t nb = 1u << bits, dmask = nb - 1u;
-    for (uint32_t i = tid; i < nb; i += TK_THREADS) hist[i] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int i = tid + j * TK_THREADS;
@@ -243,25 +291,26 @@ __global__ __launch_bounds__(TK_THREADS) void topk_reg(TopkArgs a, unsigned long
     const int j0 = (int)nb - 1 - 2 * tid;
     const uint32_t h0 = (j0 >= 0) ? hist[j0] : 0u;
     const uint32_t h1 = (j0 >= 1) ? hist[j0 - 1] : 0u;
+    if (j0 >= 0) hist[j0] = 0u;
+    if (j0 >= 1) hist[j0 - 1] = 0u;
+    const int ps = pass & 1;
     uint32_t tot;
-    const uint32_t excl = block_excl_scan(h0 + h1, wsum, &tot);
+    const uint32_t excl = block_excl_scan1(h0 + h1, wsc[ps], &tot);
     if (excl < remaining && excl + h0 + h1 >= remaining) {
-      if (excl + h0 >= remaining) { sh_digit = (uint32_t)j0; sh_above = excl; sh_bucket = h0; }
-      else { sh_digit = (uint32_t)(j0 - 1); sh_above = excl + h0; sh_bucket = h1; }
+      if (excl + h0 >= remaining) { sh_digit[ps] = (uint32_t)j0; sh_above[ps] = excl; sh_bucket[ps] = h0; }
+      else { sh_digit[ps] = (uint32_t)(j0 - 1); sh_above[ps] = excl + h0; sh_bucket[ps] = h1; }
     }
     __syncthreads();
-    remaining -= sh_above;
-    bucket = sh_bucket;
-    prefix |= sh_digit << shift;
+    remaining -= sh_above[ps];
+    bucket = sh_bucket[ps];
+    prefix |= sh_digit[ps] << shift;
     pmask |= dmask << shift;
     hi_bit = shift - 1;
-    __syncthreads();
+    ++pass;
   }
   // Selected: keys whose determined bits exceed prefix, plus `remaining` keys equal to it
   // on those bits (all of them when bucket == remaining, else the lowest ids).
   const bool take_all = bucket == remaining;
-  if (tid == 0) sh_cnt = 0u;
-  __syncthreads();
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = tid + j * TK_THREADS;
