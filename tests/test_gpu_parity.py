@@ -545,7 +545,10 @@ def test_attention_scale_argument():
 
 # ------------------------------------------------------------------------------ steps alone
 
-@pytest.mark.parametrize("n,k", [(1, 1), (5, 8), (1000, 16), (47_000, 16), (100_003, 32), (5000, 1024)])
+# (65_536, 64): 8 slices x 64 = 512 candidates, the largest merge placed by rank;
+# (100_003, 64): 832 candidates, merged by the bitonic sort
+@pytest.mark.parametrize("n,k", [(1, 1), (5, 8), (1000, 16), (47_000, 16), (100_003, 32), (5000, 1024),
+                                 (65_536, 64), (100_003, 64)])
 def test_topk_alone_exact(n, k):
     say(f"case top-k alone n={n} k={k}")
     rng = np.random.default_rng(n + k)
@@ -564,6 +567,24 @@ def test_topk_alone_exact(n, k):
         assert np.array_equal(ids[b, :keff], order), f"row {b}"
         assert np.array_equal(top[b, :keff], np.where(sc[b][order] == 0, 0.0, sc[b][order]))
         assert np.all(ids[b, keff:] == -1)
+
+
+@pytest.mark.parametrize("n,k", [(8192, 16), (47_000, 16), (30_000, 100)])
+def test_topk_narrow_band(n, k):
+    # continuous scores inside a narrow band share their sign, exponent and leading mantissa
+    # bits, so the radix select starts below them and needs several passes; exact against a
+    # sort of the same float32 values
+    say(f"case top-k narrow band n={n} k={k}")
+    rng = np.random.default_rng(n + 3 * k)
+    sc = (0.3 + 1e-4 * rng.random((2, n))).astype(np.float32)
+    sc[1, ::7] = np.float32(0.3)  # a tie run at the band's low edge
+    ids, top = M.msa_topk(torch.tensor(sc, device=DEV), k)
+    torch.cuda.synchronize()
+    ids, top = ids.cpu().numpy(), top.cpu().numpy()
+    for b in range(2):
+        order = np.lexsort((np.arange(n), -sc[b].astype(np.float64)))[:k]
+        assert np.array_equal(ids[b], order), f"row {b}"
+        assert np.array_equal(top[b], sc[b][order])
 
 
 def test_route_scan_alone_and_empty_query():
